@@ -1,0 +1,226 @@
+"""fp64 CPU oracle for the selective scan (S6) and the SSD chunked form.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import this package; the GPU path never does,
+and it shares no code with it.
+
+* ``selective_scan`` / ``ssd`` run the plain recurrence in C (``ssm_oracle.c``),
+  one independent row per thread task.  Discretisation per the tildalice.io
+  review "Mamba 논문 리뷰" (section 이산화): Abar = exp(delta*A),
+  Bbar = (delta*A)^-1 (exp(delta*A) - 1) delta*B; recurrence h_t = Abar h_{t-1}
+  + Bbar x_t; readout y_t = C_t h_t, plus D x_t (yongggg.tistory.com review,
+  State Space Model section) and the SiLU(z) gate (tildalice.io, Mamba block).
+* ``ssd_chunked`` (numpy, fp64) takes the steps of the SSD tiling algorithm of
+  the obsidian-dorae222 "Mamba-2" page (section SSD 타일링 알고리즘) in order --
+  chunk cumulative decay, chunk states, state passing, chunk scan -- and returns
+  every intermediate so that each GPU step can be checked on its own.  It is
+  pinned to the recurrence by the tests (any chunk size gives the same y).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB = os.path.join(_HERE, "libssm_oracle.so")
+
+MUTATIONS = {
+    1: "skip term D*x dropped",
+    2: "sign of the exponent flipped",
+    3: "B and C swapped",
+    4: "x read one step late",
+    5: "Euler Bbar used in place of ZOH",
+    6: "readout uses the wrong state index",
+    7: "gate sigmoid(z) in place of SiLU(z)",
+}
+
+
+def build(force: bool = False) -> str:
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+                               "-std=c11", _SRC, "-o", tmp, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_selective_scan.restype = ci
+        lib.oracle_selective_scan.argtypes = [i64, i64, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                              vp, vp, ci, ci]
+        lib.oracle_ssd.restype = ci
+        lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp,
+                                   vp, ci, ci]
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    """Host threads the oracle uses: every core in this process's affinity mask."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _io(a, io):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.uint16 if io == "bf16" else np.float32)
+
+
+def selective_scan(inp: dict, io: str, euler: bool = False, h0=None, rows=None, nthreads=None, mutation=0):
+    """Reference scan.
+
+    inp: x, delta (batch, L, D); A (D, N) fp32; B, C (batch, L, N); optional
+    D (D,) fp32 and z (batch, L, D).  bf16 tensors are uint16 bit patterns.
+    h0: optional (batch, D, N).  rows: optional flat ids b*D + d.
+    Returns (y, h_last): (batch, L, D) and (batch, D, N) float64, or
+    (nrows, L) and (nrows, N) when rows is given.
+    """
+    x, dl, B, C, z = (_io(inp.get(k), io) for k in ("x", "delta", "B", "C", "z"))
+    A, Dk = _c(inp["A"], np.float32), _c(inp.get("D"), np.float32)
+    batch, L, D = x.shape
+    N = A.shape[1]
+    assert dl.shape == x.shape and B.shape == (batch, L, N) and C.shape == (batch, L, N) and A.shape == (D, N)
+    h0c = _c(h0, np.float64)
+    if h0c is not None:
+        assert h0c.shape == (batch, D, N)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nr = batch * D if r is None else len(r)
+    y = np.empty((nr, L), np.float64)
+    hl = np.empty((nr, N), np.float64)
+    rc = _load().oracle_selective_scan(batch, L, D, N, 1 if io == "bf16" else 0, 1 if euler else 0, _ptr(x),
+                                       _ptr(dl), _ptr(A), _ptr(B), _ptr(C), _ptr(Dk), _ptr(z), _ptr(h0c), _ptr(r),
+                                       nr, _ptr(y), _ptr(hl), nthreads or threads(), mutation)
+    if rc != 0:
+        raise ValueError("oracle_selective_scan rejected its arguments")
+    if r is None:
+        return y.reshape(batch, D, L).transpose(0, 2, 1).copy(), hl.reshape(batch, D, N)
+    return y, hl
+
+
+def ssd(inp: dict, io: str, ngroups: int = 1, euler: bool = False, h0=None, rows=None, nthreads=None,
+        mutation=0):
+    """Reference SSD as the expanded scan.
+
+    inp: x (batch, L, H, P); delta (batch, L, H); A (H,) fp32; B, C
+    (batch, L, G, N); optional D (H,) fp32.  h0: optional (batch, H, P, N).
+    rows: optional flat ids b*H*P + h*P + p.
+    Returns (y, h_last): (batch, L, H, P) and (batch, H, P, N), or row-major
+    (nrows, L) and (nrows, N) when rows is given.
+    """
+    x, dl, B, C = (_io(inp.get(k), io) for k in ("x", "delta", "B", "C"))
+    A, Dk = _c(inp["A"], np.float32), _c(inp.get("D"), np.float32)
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert G == ngroups and dl.shape == (batch, L, H) and A.shape == (H,) and C.shape == B.shape
+    h0c = _c(h0, np.float64)
+    if h0c is not None:
+        assert h0c.shape == (batch, H, P, N)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nr = batch * H * P if r is None else len(r)
+    y = np.empty((nr, L), np.float64)
+    hl = np.empty((nr, N), np.float64)
+    rc = _load().oracle_ssd(batch, L, H, P, N, G, 1 if io == "bf16" else 0, 1 if euler else 0, _ptr(x), _ptr(dl),
+                            _ptr(A), _ptr(B), _ptr(C), _ptr(Dk), _ptr(h0c), _ptr(r), nr, _ptr(y), _ptr(hl),
+                            nthreads or threads(), mutation)
+    if rc != 0:
+        raise ValueError("oracle_ssd rejected its arguments")
+    if r is None:
+        return (y.reshape(batch, H, P, L).transpose(0, 3, 1, 2).copy(), hl.reshape(batch, H, P, N))
+    return y, hl
+
+
+def _f64(a, io):
+    if a is None:
+        return None
+    if io == "bf16":
+        return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(a, np.float32).astype(np.float64)
+
+
+def ssd_chunked(inp: dict, io: str, chunk: int, ngroups: int = 1, euler: bool = False, h0=None):
+    """The SSD tiling algorithm, fp64, with every intermediate.
+
+    Steps (obsidian-dorae222 "Mamba-2", SSD 타일링 알고리즘; the inter-chunk
+    term read as the decay-weighted sum over the chunk, the only reading under
+    which the result equals the semiseparable form y = M x):
+      1. a_t = delta_t * A_h; A_cum = inclusive cumulative sum of a inside each
+         chunk; beta_t = expm1(a_t)/A_h (ZOH; delta_t if A_h = 0) or delta_t.
+      2. chunk state: S_loc[c] = sum_j exp(A_cum_end - A_cum_j) beta_j x_j B_j^T
+      3. state passing: S_in[0] = h0 or 0, S_in[c+1] = exp(A_cum_end[c]) S_in[c] + S_loc[c]
+      4. chunk scan: y_i = sum_{j<=i in chunk} exp(A_cum_i - A_cum_j) (C_i . B_j) beta_j x_j
+                          + exp(A_cum_i) S_in[c] C_i + D_h x_i
+    The last chunk may be shorter than `chunk`.
+    Returns dict with y (batch, L, H, P), A_cum (batch, H, L), beta (batch, H, L),
+    S_loc (batch, nc, H, P, N), S_in (batch, nc, H, P, N), h_last (batch, H, P, N).
+    """
+    x = _f64(inp["x"], io)
+    dl = _f64(inp["delta"], io)
+    B = _f64(inp["B"], io)
+    C = _f64(inp["C"], io)
+    A = np.asarray(inp["A"], np.float32).astype(np.float64)
+    Dk = None if inp.get("D") is None else np.asarray(inp["D"], np.float32).astype(np.float64)
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    hpg = H // ngroups
+    gidx = np.arange(H) // hpg
+    Bh = B[:, :, gidx, :]  # (batch, L, H, N)
+    Ch = C[:, :, gidx, :]
+    a = dl * A[None, None, :]  # (batch, L, H)
+    if euler:
+        beta = dl.copy()
+    else:
+        with np.errstate(divide="ignore", invalid="ignore"):
+            beta = np.where(A[None, None, :] != 0, np.expm1(a) / np.where(A == 0, 1.0, A)[None, None, :], dl)
+    nc = (L + chunk - 1) // chunk
+    A_cum = np.empty((batch, L, H))
+    for c in range(nc):
+        s, e = c * chunk, min(L, (c + 1) * chunk)
+        A_cum[:, s:e] = np.cumsum(a[:, s:e], axis=1)
+    S_loc = np.zeros((batch, nc, H, P, N))
+    S_in = np.zeros((batch, nc, H, P, N))
+    y = np.zeros((batch, L, H, P))
+    state = np.zeros((batch, H, P, N)) if h0 is None else np.asarray(h0, np.float64).copy()
+    for c in range(nc):
+        s, e = c * chunk, min(L, (c + 1) * chunk)
+        Ac = A_cum[:, s:e]                      # (b, q, h)
+        Aend = Ac[:, -1]                        # (b, h)
+        w = np.exp(Aend[:, None, :] - Ac) * beta[:, s:e]          # (b, q, h)
+        S_loc[:, c] = np.einsum("bqh,bqhp,bqhn->bhpn", w, x[:, s:e], Bh[:, s:e])
+        S_in[:, c] = state
+        state = np.exp(Aend)[:, :, None, None] * state + S_loc[:, c]
+        # chunk scan
+        q = e - s
+        diff = Ac[:, :, None, :] - Ac[:, None, :, :]              # (b, i, j, h)
+        causal = np.tril(np.ones((q, q), bool))[None, :, :, None]
+        Lmask = np.where(causal, np.exp(np.where(causal, diff, 0.0)), 0.0)
+        CB = np.einsum("bihn,bjhn->bijh", Ch[:, s:e], Bh[:, s:e])
+        Wij = Lmask * CB * beta[:, None, s:e, :]                  # (b, i, j, h)
+        y_intra = np.einsum("bijh,bjhp->bihp", Wij, x[:, s:e])
+        y_inter = np.exp(Ac)[..., None] * np.einsum("bhpn,bihn->bihp", S_in[:, c], Ch[:, s:e])
+        y[:, s:e] = y_intra + y_inter
+        if Dk is not None:
+            y[:, s:e] += Dk[None, None, :, None] * x[:, s:e]
+    return {"y": y, "A_cum": A_cum.transpose(0, 2, 1).copy(), "beta": beta.transpose(0, 2, 1).copy(),
+            "S_loc": S_loc, "S_in": S_in, "h_last": state}

@@ -1,0 +1,229 @@
+"""Seeded synthetic inputs for the selective scan and the SSD chunked form.
+
+Used by the GPU parity tests, by ``bench.py`` and by the CPU oracle's tests.
+This module draws numbers and rounds them to storage types; it computes no
+part of the scan itself.  Every value is a pure function of
+(seed, stream id, flat index) -- see ``synth.c`` -- so any slice can be
+regenerated independently.
+
+bf16 tensors are returned as ``numpy.uint16`` bit patterns; fp32 as float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_LIB = os.path.join(_HERE, "libsynth.so")
+
+NORMAL, UNIFORM, SOFTPLUS_NORMAL, NEG_EXP_UNIFORM, NEG_IDX, CONST = range(6)
+
+# Stream ids: one per tensor role, so tensors never share random numbers.
+STREAM = {"x": 1, "delta": 2, "A": 3, "B": 4, "C": 5, "D": 6, "z": 7, "h0": 8}
+
+
+def build(force: bool = False) -> str:
+    """Compile libsynth.so with gcc (host code only)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c11", _SRC, "-o", tmp, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        lib.synth_fill.restype = ctypes.c_int
+        lib.synth_fill.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_double, ctypes.c_double, ctypes.c_int64, ctypes.c_uint64,
+                                   ctypes.c_uint64, ctypes.c_int]
+        lib.synth_raw.restype = None
+        lib.synth_raw.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64]
+        lib.synth_key.restype = ctypes.c_uint64
+        lib.synth_key.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        lib.synth_f32_to_bf16.restype = ctypes.c_uint16
+        lib.synth_f32_to_bf16.argtypes = [ctypes.c_float]
+        _lib = lib
+    return _lib
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+@dataclass(frozen=True)
+class Dist:
+    kind: int
+    p0: float = 0.0
+    p1: float = 1.0
+    period: int = 1
+
+
+def fill(shape, dist: Dist, dtype: str, seed: int, stream: int, start: int = 0) -> np.ndarray:
+    """Elements start..start+prod(shape) of a stream, reshaped.  dtype: 'f32' or 'bf16'."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    if n:
+        _load().synth_fill(out.ctypes.data, n, start, 1 if dtype == "bf16" else 0, dist.kind, dist.p0, dist.p1,
+                           dist.period, seed, stream, _threads())
+    return out.reshape(shape)
+
+
+def raw(n: int, start: int, seed: int, stream: int) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint64)
+    _load().synth_raw(out.ctypes.data, n, start, seed, stream)
+    return out
+
+
+def f32_to_bf16_bits(v: float) -> int:
+    return int(_load().synth_f32_to_bf16(float(v)))
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_to_f32(a).astype(np.float64) if dtype == "bf16" else a.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Workload recipes
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class ScanSpec:
+    """Selective scan problem: x, delta, z, y (batch, L, D); B, C (batch, L, N);
+    A (D, N); D (D)."""
+    name: str
+    batch: int
+    seqlen: int
+    dim: int
+    dstate: int
+    io: str  # 'f32' or 'bf16'
+    has_z: bool
+    has_D: bool
+    A: Dist
+    delta: Dist
+    euler: bool = False
+    x: Dist = Dist(NORMAL, 0.0, 1.0)
+    B: Dist = Dist(NORMAL, 0.0, 1.0)
+    C: Dist = Dist(NORMAL, 0.0, 1.0)
+    z: Dist = Dist(NORMAL, 0.0, 1.0)
+    Dskip: Dist = Dist(NORMAL, 0.0, 1.0)
+
+    @property
+    def tc(self) -> int:
+        return self.batch * self.seqlen * self.dim
+
+    def algorithmic_bytes(self) -> int:
+        """Each input read once, y written once; B and C once per token."""
+        e = 2 if self.io == "bf16" else 4
+        per_tc = e * (3 + (1 if self.has_z else 0))  # x, delta, [z], y
+        per_tok = 2 * self.dstate * e  # B, C
+        return self.tc * per_tc + self.batch * self.seqlen * per_tok + self.dim * self.dstate * 4 + \
+            (self.dim * 4 if self.has_D else 0)
+
+
+@dataclass(frozen=True)
+class SSDSpec:
+    """SSD (scalar A per head) problem: x, y (batch, L, H, P); delta (batch, L, H);
+    A (H); B, C (batch, L, G, N); D (H)."""
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int
+    chunk: int
+    io: str
+    has_D: bool
+    A: Dist
+    delta: Dist
+    euler: bool = False
+    x: Dist = Dist(NORMAL, 0.0, 1.0)
+    B: Dist = Dist(NORMAL, 0.0, 1.0)
+    C: Dist = Dist(NORMAL, 0.0, 1.0)
+    Dskip: Dist = Dist(NORMAL, 0.0, 1.0)
+
+
+# The five workloads: a tiny fp32 scan, a Mamba-130M-shaped layer, a
+# Mamba-2.8B-shaped layer, a 1M-token fp32 scan and a Mamba-2 (2.7B-shaped)
+# SSD layer.
+TINY = ScanSpec("tiny_b1_l64_d4_n4_f32", 1, 64, 4, 4, "f32", False, True,
+                A=Dist(NEG_EXP_UNIFORM, -1.0, 1.0), delta=Dist(SOFTPLUS_NORMAL, -2.0, 1.0))
+MAMBA130M = ScanSpec("mamba130m_b8_l2048_d1536_n16_bf16", 8, 2048, 1536, 16, "bf16", True, True,
+                     A=Dist(NEG_IDX, period=16), delta=Dist(SOFTPLUS_NORMAL, -3.0, 1.0))
+MAMBA2_8B = ScanSpec("mamba2.8b_b4_l4096_d5120_n16_bf16", 4, 4096, 5120, 16, "bf16", True, True,
+                     A=Dist(NEG_IDX, period=16), delta=Dist(SOFTPLUS_NORMAL, -3.0, 1.0))
+LONG1M = ScanSpec("long1m_b1_l1048576_d1536_n16_f32", 1, 1 << 20, 1536, 16, "f32", False, False,
+                  A=Dist(NEG_IDX, period=16), delta=Dist(SOFTPLUS_NORMAL, -4.0, 1.0))
+SSD2_7B = SSDSpec("ssd2.7b_b4_l4096_h80_p64_n64_g1_q256_bf16", 4, 4096, 80, 64, 64, 1, 256, "bf16", True,
+                  A=Dist(NEG_EXP_UNIFORM, 0.0, 2.7), delta=Dist(SOFTPLUS_NORMAL, -3.0, 1.0))
+
+SCAN_CONFIGS = {s.name: s for s in (TINY, MAMBA130M, MAMBA2_8B, LONG1M)}
+
+
+def scan_spec(base: ScanSpec, **kw) -> ScanSpec:
+    """Same distributions as `base`, other sizes/flags."""
+    if "name" not in kw:
+        kw["name"] = base.name + "_" + "_".join("%s%s" % (k, v) for k, v in sorted(kw.items()))
+    return replace(base, **kw)
+
+
+def ssd_spec(base: SSDSpec, **kw) -> SSDSpec:
+    if "name" not in kw:
+        kw["name"] = base.name + "_" + "_".join("%s%s" % (k, v) for k, v in sorted(kw.items()))
+    return replace(base, **kw)
+
+
+def scan_inputs(s: ScanSpec, seed: int = 0) -> dict:
+    """Host arrays for a scan problem.  Keys: x, delta, A, B, C, D, z (absent if off)."""
+    io = s.io
+    out = {
+        "x": fill((s.batch, s.seqlen, s.dim), s.x, io, seed, STREAM["x"]),
+        "delta": fill((s.batch, s.seqlen, s.dim), s.delta, io, seed, STREAM["delta"]),
+        "A": fill((s.dim, s.dstate), s.A, "f32", seed, STREAM["A"]),
+        "B": fill((s.batch, s.seqlen, s.dstate), s.B, io, seed, STREAM["B"]),
+        "C": fill((s.batch, s.seqlen, s.dstate), s.C, io, seed, STREAM["C"]),
+    }
+    if s.has_D:
+        out["D"] = fill((s.dim,), s.Dskip, "f32", seed, STREAM["D"])
+    if s.has_z:
+        out["z"] = fill((s.batch, s.seqlen, s.dim), s.z, io, seed, STREAM["z"])
+    return out
+
+
+def ssd_inputs(s: SSDSpec, seed: int = 0) -> dict:
+    io = s.io
+    out = {
+        "x": fill((s.batch, s.seqlen, s.nheads, s.headdim), s.x, io, seed, STREAM["x"]),
+        "delta": fill((s.batch, s.seqlen, s.nheads), s.delta, io, seed, STREAM["delta"]),
+        "A": fill((s.nheads,), s.A, "f32", seed, STREAM["A"]),
+        "B": fill((s.batch, s.seqlen, s.ngroups, s.dstate), s.B, io, seed, STREAM["B"]),
+        "C": fill((s.batch, s.seqlen, s.ngroups, s.dstate), s.C, io, seed, STREAM["C"]),
+    }
+    if s.has_D:
+        out["D"] = fill((s.nheads,), s.Dskip, "f32", seed, STREAM["D"])
+    return out
+
+
+def state_input(shape, seed: int = 0) -> np.ndarray:
+    """An fp32 initial state h0, N(0,1)."""
+    return fill(shape, Dist(NORMAL, 0.0, 1.0), "f32", seed, STREAM["h0"])
