@@ -1,0 +1,209 @@
+/*
+ * ssm.h -- C ABI of libssm: the selective state-space scan (S6) and its
+ * Mamba-2 SSD chunked form, forward pass, on AMD Instinct MI355X (gfx950).
+ *
+ * The operations (pages cited by title and section):
+ *
+ *  Selective scan -- "Mamba 논문 리뷰: 선형 시간복잡도로 Transformer에 도전하는
+ *  Selective State Space Model" (tildalice.io), sections 이산화, Selection
+ *  Mechanism, 하드웨어 인식 병렬 알고리즘 and the SelectiveSSM listing; the skip
+ *  term D from "[yongggg's] Mamba ... (Review)", section State Space Model.
+ *  For every batch element b and channel d, with N-wide state h:
+ *      u        = delta[b,t,d] * A[d,n]
+ *      Abar     = exp(u)
+ *      Bbar     = (exp(u) - 1) / A[d,n] * B[b,t,n]     (zero-order hold;
+ *                 delta*B[b,t,n] when A[d,n] == 0)
+ *               | delta[b,t,d] * B[b,t,n]               (SSM_DISC_EULER)
+ *      h[n]     = Abar * h[n] + Bbar * x[b,t,d]          h starts at h0 or 0
+ *      y[b,t,d] = (sum_n C[b,t,n] h[n] + D[d] x[b,t,d]) * silu(z[b,t,d])
+ *  silu(v) = v / (1 + exp(-v)).  D and z are optional (SSM_HAS_D, SSM_HAS_Z).
+ *  delta is taken as given (already positive); A is real, normally negative.
+ *
+ *  SSD -- "Mamba-2: 상태 공간 기반 시퀀스 모델" (obsidian-dorae222), sections
+ *  1-세미분리 행렬, SSM-Attention 동치성 and SSD 타일링 알고리즘: the same
+ *  recurrence with one scalar A per head, computed by chunks of `chunk` steps:
+ *  inside a chunk y = (L o C B^T)(beta x) (L the decay mask), across chunks the
+ *  state is passed on; every channel (h, p) of head h shares delta[b,t,h],
+ *  A[h] and the B, C of the head's group g = h / (nheads / ngroups).
+ *
+ * Conventions
+ *  - Shapes are outermost first; strides are in ELEMENTS and must be >= 0
+ *    (0 = broadcast).  Unless stated, the innermost dimension of x, delta, z,
+ *    y must have stride 1 (SSM_ERR_STRIDE otherwise).
+ *  - Ownership: the caller owns every buffer, the workspace included.  The
+ *    library never allocates, frees, retains pointers or synchronises.  Work
+ *    is enqueued on `hip_stream` (a hipStream_t, NULL = default stream) and
+ *    the call returns at once; buffers must stay alive until the stream has
+ *    run it.  Descriptors are read during the call only.
+ *  - Errors: every entry point returns an ssm_status.  All checks except
+ *    SSM_ERR_HIP happen on the host before any HIP call, so a rejected call
+ *    has no side effects.  Values are never inspected: NaN/Inf propagate.
+ *  - Thread safety: no mutable global state; calls may come from any thread.
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+#define SSM_MAX_DIMS 5
+#define SSM_SCAN_MAX_DSTATE 64 /* selective scan: N <= 64 */
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  SSM_ERR_SHAPE = 2,       /* sizes <= 0 or tensor shape != required shape    */
+  SSM_ERR_DTYPE = 3,       /* dtype not allowed for that tensor                */
+  SSM_ERR_STRIDE = 4,      /* negative stride, or innermost stride != 1       */
+  SSM_ERR_ALIGN = 5,       /* base pointer not aligned to its element size    */
+  SSM_ERR_ALIAS = 6,       /* an output overlaps an input or another output   */
+  SSM_ERR_UNSUPPORTED = 7, /* valid but not implemented (e.g. N > 64)         */
+  SSM_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than required         */
+  SSM_ERR_HIP = 9          /* a HIP call failed; see ssm_last_hip_error()     */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1, SSM_F16 = 2 /* reserved */ } ssm_dtype;
+
+typedef struct {
+  int32_t dtype; /* ssm_dtype */
+  int32_t ndim;
+  int64_t shape[SSM_MAX_DIMS];
+  int64_t stride[SSM_MAX_DIMS]; /* elements */
+} ssm_tensor_desc;
+
+/* descriptor flags */
+#define SSM_HAS_Z 1u       /* gate y by silu(z)                  (scan only) */
+#define SSM_HAS_D 2u       /* add D * x                                       */
+#define SSM_DISC_EULER 4u  /* Bbar = delta * B instead of zero-order hold     */
+#define SSM_HAS_H0 8u      /* start from h0 instead of 0                      */
+#define SSM_WANT_HLAST 16u /* write the final state to h_last                 */
+
+/* ------------------------------------------------------------------ scan */
+
+/* Selective scan problem.  Required tensors (shape, dtype):
+ *   x, delta : (batch, seqlen, dim)  io          innermost stride 1
+ *   z        : (batch, seqlen, dim)  io          if SSM_HAS_Z, innermost stride 1
+ *   y        : (batch, seqlen, dim)  io or F32   innermost stride 1
+ *   B, C     : (batch, seqlen, dstate) io        any strides
+ *   A        : (dim, dstate)  F32                any strides (0 = shared)
+ *   D        : (dim)          F32                if SSM_HAS_D, any stride
+ *   h0       : (batch, dim, dstate) F32 contiguous   if SSM_HAS_H0
+ *   h_last   : (batch, dim, dstate) F32 contiguous   if SSM_WANT_HLAST
+ * io is SSM_F32 or SSM_BF16 and is the same for x, delta, z, B, C.
+ * Descriptors of tensors a flag turns off are ignored. */
+typedef struct {
+  int64_t batch, seqlen, dim, dstate;
+  uint32_t flags;
+  ssm_tensor_desc x, delta, A, B, C, D, z, y, h0, h_last;
+} ssm_scan_desc;
+
+typedef struct {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;   /* NULL unless SSM_HAS_D      */
+  const void* z;    /* NULL unless SSM_HAS_Z      */
+  void* y;
+  const float* h0;  /* NULL unless SSM_HAS_H0     */
+  float* h_last;    /* NULL unless SSM_WANT_HLAST */
+} ssm_scan_ptrs;
+
+/* ------------------------------------------------------------------- SSD */
+
+/* SSD problem.  Required tensors (shape, dtype), all innermost stride 1:
+ *   x, y     : (batch, seqlen, nheads, headdim)   BF16 (y may be F32)
+ *   delta    : (batch, seqlen, nheads)            BF16
+ *   B, C     : (batch, seqlen, ngroups, dstate)   BF16
+ *   A        : (nheads)  F32, any stride
+ *   D        : (nheads)  F32, any stride          if SSM_HAS_D (one skip weight per head)
+ *   h0       : (batch, nheads, headdim, dstate) F32 contiguous  if SSM_HAS_H0
+ *   h_last   : (batch, nheads, headdim, dstate) F32 contiguous  if SSM_WANT_HLAST
+ * Supported: headdim == 64, dstate == 64, chunk in {64, 128, 256},
+ * nheads % ngroups == 0; seqlen need not be a multiple of chunk (the last
+ * chunk is shorter).  SSM_HAS_Z is not accepted. */
+typedef struct {
+  int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+  uint32_t flags;
+  ssm_tensor_desc x, delta, A, B, C, D, y, h0, h_last;
+} ssm_ssd_desc;
+
+typedef struct {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;  /* NULL unless SSM_HAS_D      */
+  void* y;
+  const float* h0; /* NULL unless SSM_HAS_H0     */
+  float* h_last;   /* NULL unless SSM_WANT_HLAST */
+} ssm_ssd_ptrs;
+
+/* --------------------------------------------------------------- entries */
+
+/* SSM_ABI_VERSION of the library that is loaded. */
+int ssm_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* ssm_status_string(ssm_status s);
+
+/* hipError_t of the last SSM_ERR_HIP returned on this thread (0 if none). */
+int ssm_last_hip_error(void);
+
+/* Bytes of device workspace ssm_selective_scan_fwd needs for `d` (may be 0).
+ * Depends only on the descriptor. */
+ssm_status ssm_selective_scan_workspace_size(const ssm_scan_desc* d, size_t* bytes);
+
+/* Selective scan forward (definition at the top of this file).  `workspace`
+ * is device memory of at least the queried size, 256-byte aligned (may be
+ * NULL when the size is 0); its contents need not be initialised and are
+ * overwritten.  Outputs: y, and h_last if SSM_WANT_HLAST. */
+ssm_status ssm_selective_scan_fwd(const ssm_scan_desc* d, const ssm_scan_ptrs* p, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of device workspace ssm_ssd_chunk_fwd needs for `d`. */
+ssm_status ssm_ssd_chunk_workspace_size(const ssm_ssd_desc* d, size_t* bytes);
+
+/* SSD forward: the four steps below in order on `hip_stream`, with their
+ * intermediates placed in `workspace` (256-byte aligned). */
+ssm_status ssm_ssd_chunk_fwd(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, void* workspace, size_t workspace_bytes,
+                             void* hip_stream);
+
+/* The four SSD steps, each one kernel launch, exposed so that each can be
+ * checked and timed on its own.  nchunks = ceil(seqlen / chunk); Lp =
+ * nchunks * chunk.  Intermediates are contiguous device buffers:
+ *   A_cum  : (batch, nheads, Lp) F32  -- inclusive cumulative sum of
+ *            delta*A inside each chunk (entries past seqlen unspecified)
+ *   beta   : (batch, nheads, Lp) F32  -- expm1(delta*A)/A (delta if A == 0),
+ *            or delta with SSM_DISC_EULER
+ *   states : (batch, nchunks, nheads, headdim, dstate) F32 -- state each
+ *            chunk builds from zero: sum_j exp(A_cum_end - A_cum_j) beta_j x_j B_j^T
+ *   S_in   : (batch, nchunks, nheads, headdim, dstate) BF16 -- state entering
+ *            each chunk, rounded to bf16 as the chunk-scan operand
+ * Step 1 (s1): A_cum, beta from delta and A.
+ * Step 2 (s2): states from x, B, A_cum, beta (bf16 matrix cores, fp32 sums).
+ * Step 3 (s3): S_in[0] = h0 or 0; S_in[c+1] = exp(A_cum_end[c]) S_in[c] + states[c]
+ *              (fp32 recurrence); h_last if SSM_WANT_HLAST.
+ * Step 4 (s4): y = (L o C B^T)(beta x) + diag(exp(A_cum)) C S_in^T + D x
+ *              with L_ij = exp(A_cum_i - A_cum_j) for j <= i, else 0. */
+ssm_status ssm_ssd_chunk_cumsum(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, float* A_cum, float* beta,
+                                void* hip_stream);
+ssm_status ssm_ssd_chunk_state(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, const float* A_cum,
+                               const float* beta, float* states, void* hip_stream);
+ssm_status ssm_ssd_state_passing(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, const float* A_cum,
+                                 const float* states, void* S_in, void* hip_stream);
+ssm_status ssm_ssd_chunk_scan(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, const float* A_cum, const float* beta,
+                              const void* S_in, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H */

@@ -1,0 +1,289 @@
+"""Python binding of libssm (include/ssm.h): the selective scan (S6) and the
+Mamba-2 SSD chunked form on MI355X.
+
+Argument marshalling only: every step of the computation runs in the gfx950
+kernels of ``libssm.so``.  PyTorch supplies device memory and the current HIP
+stream.  There is no CPU fallback: if the library is missing this module
+raises on import.  Build it with ``python -m selective_state_space_60_amd.build``
+or ``__graft_entry__.build()``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssm.so")
+
+SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_STRIDE, SSM_ERR_ALIGN, SSM_ERR_ALIAS, \
+    SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE, SSM_ERR_HIP = range(10)
+SSM_F32, SSM_BF16, SSM_F16 = 0, 1, 2
+SSM_HAS_Z, SSM_HAS_D, SSM_DISC_EULER, SSM_HAS_H0, SSM_WANT_HLAST = 1, 2, 4, 8, 16
+MAX_DIMS = 5
+
+# Every function include/ssm.h declares.
+EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_hip_error", "ssm_selective_scan_workspace_size",
+           "ssm_selective_scan_fwd", "ssm_ssd_chunk_workspace_size", "ssm_ssd_chunk_fwd", "ssm_ssd_chunk_cumsum",
+           "ssm_ssd_chunk_state", "ssm_ssd_state_passing", "ssm_ssd_chunk_scan")
+
+
+class TensorDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32), ("shape", ctypes.c_int64 * MAX_DIMS),
+                ("stride", ctypes.c_int64 * MAX_DIMS)]
+
+
+_SCAN_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "h0", "h_last")
+_SSD_T = ("x", "delta", "A", "B", "C", "D", "y", "h0", "h_last")
+
+
+class ScanDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("flags", ctypes.c_uint32)] + [(n, TensorDesc) for n in _SCAN_T]
+
+
+class ScanPtrs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _SCAN_T]
+
+
+class SSDDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("flags", ctypes.c_uint32)] + [(n, TensorDesc) for n in _SSD_T]
+
+
+class SSDPtrs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _SSD_T]
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().ssm_status_string(status).decode()
+        if status == SSM_ERR_HIP:
+            msg += " (hipError_t %d)" % lib().ssm_last_hip_error()
+        super().__init__("%s: %s" % (where, msg))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libssm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libssm.so is not built (run __graft_entry__.build()): " + LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, vp, sz = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t
+        L.ssm_abi_version.restype = ctypes.c_int
+        L.ssm_status_string.restype = ctypes.c_char_p
+        L.ssm_status_string.argtypes = [ctypes.c_int]
+        L.ssm_last_hip_error.restype = ctypes.c_int
+        L.ssm_selective_scan_workspace_size.argtypes = [P(ScanDesc), P(sz)]
+        L.ssm_selective_scan_fwd.argtypes = [P(ScanDesc), P(ScanPtrs), vp, sz, vp]
+        L.ssm_ssd_chunk_workspace_size.argtypes = [P(SSDDesc), P(sz)]
+        L.ssm_ssd_chunk_fwd.argtypes = [P(SSDDesc), P(SSDPtrs), vp, sz, vp]
+        L.ssm_ssd_chunk_cumsum.argtypes = [P(SSDDesc), P(SSDPtrs), vp, vp, vp]
+        L.ssm_ssd_chunk_state.argtypes = [P(SSDDesc), P(SSDPtrs), vp, vp, vp, vp]
+        L.ssm_ssd_state_passing.argtypes = [P(SSDDesc), P(SSDPtrs), vp, vp, vp, vp]
+        L.ssm_ssd_chunk_scan.argtypes = [P(SSDDesc), P(SSDPtrs), vp, vp, vp, vp]
+        for name in EXPORTS[3:]:
+            getattr(L, name).restype = ctypes.c_int
+        if L.ssm_abi_version() != 1:
+            raise ImportError("libssm ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().ssm_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().ssm_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != SSM_OK:
+        raise SSMError(status, where)
+
+
+_DT = {torch.float32: SSM_F32, torch.bfloat16: SSM_BF16, torch.float16: SSM_F16}
+
+
+def tensor_desc(t) -> TensorDesc:
+    d = TensorDesc()
+    if t is None:
+        return d
+    d.dtype = _DT.get(t.dtype, -1)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _workspace(nbytes: int, device):
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# -------------------------------------------------------------------- scan
+
+def scan_desc(x, delta, A, B, C, D=None, z=None, y=None, h0=None, h_last=None, euler=False) -> ScanDesc:
+    d = ScanDesc()
+    d.batch, d.seqlen, d.dim = x.shape
+    d.dstate = A.shape[-1]
+    d.flags = ((SSM_HAS_Z if z is not None else 0) | (SSM_HAS_D if D is not None else 0) |
+               (SSM_DISC_EULER if euler else 0) | (SSM_HAS_H0 if h0 is not None else 0) |
+               (SSM_WANT_HLAST if h_last is not None else 0))
+    for name, t in zip(_SCAN_T, (x, delta, A, B, C, D, z, y, h0, h_last)):
+        setattr(d, name, tensor_desc(t))
+    return d
+
+
+def scan_ptrs(x, delta, A, B, C, D=None, z=None, y=None, h0=None, h_last=None) -> ScanPtrs:
+    p = ScanPtrs()
+    for name, t in zip(_SCAN_T, (x, delta, A, B, C, D, z, y, h0, h_last)):
+        setattr(p, name, _p(t))
+    return p
+
+
+def selective_scan_workspace_size(desc: ScanDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().ssm_selective_scan_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "ssm_selective_scan_workspace_size")
+    return n.value
+
+
+def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, euler=False, want_hlast=False,
+                       y_dtype=None, y=None, stream=None):
+    """y = selective scan of x (see include/ssm.h).  Returns (y, h_last or None).
+
+    x, delta, z: (batch, L, dim); B, C: (batch, L, dstate); A: (dim, dstate)
+    fp32; D: (dim,) fp32; h0: (batch, dim, dstate) fp32.  x/delta/z/B/C are all
+    fp32 or all bf16; y defaults to x's dtype."""
+    if y is None:
+        y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
+    h_last = torch.empty((x.shape[0], x.shape[2], A.shape[-1]), dtype=torch.float32,
+                         device=x.device) if want_hlast else None
+    desc = scan_desc(x, delta, A, B, C, D, z, y, h0, h_last, euler)
+    ptrs = scan_ptrs(x, delta, A, B, C, D, z, y, h0, h_last)
+    nbytes = selective_scan_workspace_size(desc)
+    ws = _workspace(nbytes, x.device)
+    _check(lib().ssm_selective_scan_fwd(ctypes.byref(desc), ctypes.byref(ptrs), _p(ws), nbytes, _stream(stream)),
+           "ssm_selective_scan_fwd")
+    return y, h_last
+
+
+# --------------------------------------------------------------------- SSD
+
+def ssd_desc(x, delta, A, B, C, chunk, D=None, y=None, h0=None, h_last=None, euler=False) -> SSDDesc:
+    d = SSDDesc()
+    d.batch, d.seqlen, d.nheads, d.headdim = x.shape
+    d.ngroups, d.dstate = B.shape[2], B.shape[3]
+    d.chunk = chunk
+    d.flags = ((SSM_HAS_D if D is not None else 0) | (SSM_DISC_EULER if euler else 0) |
+               (SSM_HAS_H0 if h0 is not None else 0) | (SSM_WANT_HLAST if h_last is not None else 0))
+    for name, t in zip(_SSD_T, (x, delta, A, B, C, D, y, h0, h_last)):
+        setattr(d, name, tensor_desc(t))
+    if y is None:  # steps that do not write y still need a valid descriptor shape
+        d.y = tensor_desc(x)
+    return d
+
+
+def ssd_ptrs(x, delta, A, B, C, D=None, y=None, h0=None, h_last=None) -> SSDPtrs:
+    p = SSDPtrs()
+    for name, t in zip(_SSD_T, (x, delta, A, B, C, D, y, h0, h_last)):
+        setattr(p, name, _p(t))
+    return p
+
+
+def ssd_chunk_workspace_size(desc: SSDDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().ssm_ssd_chunk_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "ssm_ssd_chunk_workspace_size")
+    return n.value
+
+
+def ssd_chunk_fwd(x, delta, A, B, C, chunk, D=None, h0=None, euler=False, want_hlast=False, y_dtype=None,
+                  y=None, stream=None):
+    """SSD forward (see include/ssm.h).  x: (batch, L, H, P) bf16; delta
+    (batch, L, H) bf16; A (H,) fp32; B, C (batch, L, G, N) bf16; D (H,) fp32;
+    h0 (batch, H, P, N) fp32.  Returns (y, h_last or None)."""
+    if y is None:
+        y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
+    h_last = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]), dtype=torch.float32,
+                         device=x.device) if want_hlast else None
+    desc = ssd_desc(x, delta, A, B, C, chunk, D, y, h0, h_last, euler)
+    ptrs = ssd_ptrs(x, delta, A, B, C, D, y, h0, h_last)
+    nbytes = ssd_chunk_workspace_size(desc)
+    ws = _workspace(nbytes, x.device)
+    _check(lib().ssm_ssd_chunk_fwd(ctypes.byref(desc), ctypes.byref(ptrs), _p(ws), nbytes, _stream(stream)),
+           "ssm_ssd_chunk_fwd")
+    return y, h_last
+
+
+def _ssd_shapes(x, B, chunk):
+    batch, L, H, P = x.shape
+    N = B.shape[3]
+    nc = (L + chunk - 1) // chunk
+    return batch, H, P, N, nc, nc * chunk
+
+
+def ssd_chunk_cumsum(x, delta, A, B, C, chunk, euler=False, stream=None):
+    """Step 1: (A_cum, beta), each (batch, H, nchunks*chunk) fp32."""
+    batch, H, P, N, nc, Lp = _ssd_shapes(x, B, chunk)
+    A_cum = torch.empty((batch, H, Lp), dtype=torch.float32, device=x.device)
+    beta = torch.empty_like(A_cum)
+    desc = ssd_desc(x, delta, A, B, C, chunk, euler=euler)
+    _check(lib().ssm_ssd_chunk_cumsum(ctypes.byref(desc), ctypes.byref(ssd_ptrs(x, delta, A, B, C)), _p(A_cum),
+                                      _p(beta), _stream(stream)), "ssm_ssd_chunk_cumsum")
+    return A_cum, beta
+
+
+def ssd_chunk_state(x, delta, A, B, C, chunk, A_cum, beta, euler=False, stream=None):
+    """Step 2: chunk-local states (batch, nchunks, H, P, N) fp32."""
+    batch, H, P, N, nc, Lp = _ssd_shapes(x, B, chunk)
+    states = torch.empty((batch, nc, H, P, N), dtype=torch.float32, device=x.device)
+    desc = ssd_desc(x, delta, A, B, C, chunk, euler=euler)
+    _check(lib().ssm_ssd_chunk_state(ctypes.byref(desc), ctypes.byref(ssd_ptrs(x, delta, A, B, C)), _p(A_cum),
+                                     _p(beta), _p(states), _stream(stream)), "ssm_ssd_chunk_state")
+    return states
+
+
+def ssd_state_passing(x, delta, A, B, C, chunk, A_cum, states, h0=None, want_hlast=False, euler=False,
+                      stream=None):
+    """Step 3: (S_in (batch, nchunks, H, P, N) bf16, h_last or None)."""
+    batch, H, P, N, nc, Lp = _ssd_shapes(x, B, chunk)
+    S_in = torch.empty((batch, nc, H, P, N), dtype=torch.bfloat16, device=x.device)
+    h_last = torch.empty((batch, H, P, N), dtype=torch.float32, device=x.device) if want_hlast else None
+    desc = ssd_desc(x, delta, A, B, C, chunk, h0=h0, h_last=h_last, euler=euler)
+    ptrs = ssd_ptrs(x, delta, A, B, C, h0=h0, h_last=h_last)
+    _check(lib().ssm_ssd_state_passing(ctypes.byref(desc), ctypes.byref(ptrs), _p(A_cum), _p(states), _p(S_in),
+                                       _stream(stream)), "ssm_ssd_state_passing")
+    return S_in, h_last
+
+
+def ssd_chunk_scan(x, delta, A, B, C, chunk, A_cum, beta, S_in, D=None, euler=False, y_dtype=None, y=None,
+                   stream=None):
+    """Step 4: y (batch, L, H, P)."""
+    if y is None:
+        y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
+    desc = ssd_desc(x, delta, A, B, C, chunk, D=D, y=y, euler=euler)
+    ptrs = ssd_ptrs(x, delta, A, B, C, D=D, y=y)
+    _check(lib().ssm_ssd_chunk_scan(ctypes.byref(desc), ctypes.byref(ptrs), _p(A_cum), _p(beta), _p(S_in),
+                                    _stream(stream)), "ssm_ssd_chunk_scan")
+    return y

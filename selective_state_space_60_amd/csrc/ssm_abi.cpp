@@ -1,0 +1,448 @@
+// Host side of libssm: descriptor validation, workspace planning and
+// dispatch to the gfx950 kernels.  Every check runs before any HIP call, so a
+// rejected call has no side effects (and the checks run without a GPU).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/ssm.h"
+#include "ssm_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr uint32_t kScanFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_WANT_HLAST;
+constexpr uint32_t kSSDFlags = SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_WANT_HLAST;
+constexpr int kSimds = 256 * 4;  // MI355X: 256 compute units x 4 SIMDs
+
+int64_t esize(int32_t dt) { return dt == SSM_BF16 || dt == SSM_F16 ? 2 : 4; }
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+  bool valid = false;
+};
+
+Span span_of(const ssm_tensor_desc& t, const void* ptr) {
+  Span s;
+  if (!ptr) return s;
+  int64_t last = 0;
+  for (int i = 0; i < t.ndim; ++i) last += (t.shape[i] - 1) * t.stride[i];
+  s.lo = (uintptr_t)ptr;
+  s.hi = s.lo + (uintptr_t)((last + 1) * esize(t.dtype));
+  s.valid = true;
+  return s;
+}
+
+bool overlap(const Span& a, const Span& b) { return a.valid && b.valid && a.lo < b.hi && b.lo < a.hi; }
+
+// Shape, dtype and stride checks of one tensor.
+ssm_status check_tensor(const ssm_tensor_desc& t, int ndim, const int64_t* shape, bool dtype_ok, bool inner_unit,
+                        bool contiguous) {
+  if (!dtype_ok) return SSM_ERR_DTYPE;
+  if (t.ndim != ndim) return SSM_ERR_SHAPE;
+  for (int i = 0; i < ndim; ++i)
+    if (t.shape[i] != shape[i]) return SSM_ERR_SHAPE;
+  for (int i = 0; i < ndim; ++i)
+    if (t.stride[i] < 0) return SSM_ERR_STRIDE;
+  if (inner_unit && t.stride[ndim - 1] != 1 && t.shape[ndim - 1] > 1) return SSM_ERR_STRIDE;
+  if (contiguous) {
+    int64_t expect = 1;
+    for (int i = ndim - 1; i >= 0; --i) {
+      if (t.shape[i] > 1 && t.stride[i] != expect) return SSM_ERR_STRIDE;
+      expect *= t.shape[i];
+    }
+  }
+  return SSM_OK;
+}
+
+// An output must not write one element twice: with dimensions sorted by
+// stride, each stride must be at least the extent of the smaller ones.
+bool non_overlapping(const ssm_tensor_desc& t) {
+  int idx[SSM_MAX_DIMS];
+  int n = 0;
+  for (int i = 0; i < t.ndim; ++i)
+    if (t.shape[i] > 1) idx[n++] = i;
+  std::sort(idx, idx + n, [&](int a, int b) { return t.stride[a] < t.stride[b]; });
+  int64_t extent = 1;
+  for (int k = 0; k < n; ++k) {
+    if (t.stride[idx[k]] < extent) return false;
+    extent = t.stride[idx[k]] * (t.shape[idx[k]] - 1) + extent;
+  }
+  return true;
+}
+
+bool aligned(const void* p, int64_t bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
+
+int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
+
+// ------------------------------------------------------------------ scan
+
+struct ScanPlan {
+  int n_seg = 1;
+  int64_t seg_len = 0;
+  int64_t ws_H = 0, ws_S = 0, ws_hin = 0, ws_total = 0;
+};
+
+// Split the sequence only when batch x channels cannot give every SIMD work.
+ScanPlan plan_scan(const ssm_scan_desc& d) {
+  ScanPlan pl;
+  const int64_t blocks = d.batch * ((d.dim + ssm::kScanChannelsPerBlock - 1) / ssm::kScanChannelsPerBlock);
+  const int64_t waves = blocks * (ssm::kScanThreads / 64);
+  int64_t n_seg = 1;
+  if (waves < kSimds) {
+    n_seg = std::max<int64_t>(1, (3 * kSimds + waves / 2) / waves);
+    n_seg = std::min<int64_t>(n_seg, std::max<int64_t>(1, d.seqlen / 2048));
+  }
+  int64_t seg_len = (d.seqlen + n_seg - 1) / n_seg;
+  seg_len = (seg_len + ssm::kScanTileSteps - 1) / ssm::kScanTileSteps * ssm::kScanTileSteps;
+  n_seg = (d.seqlen + seg_len - 1) / seg_len;
+  pl.n_seg = (int)n_seg;
+  pl.seg_len = seg_len;
+  if (n_seg > 1) {
+    pl.ws_H = round256(d.batch * (n_seg - 1) * d.dim * d.dstate * 4);
+    pl.ws_S = round256(d.batch * (n_seg - 1) * d.dim * 4);
+    pl.ws_hin = round256(d.batch * n_seg * d.dim * d.dstate * 4);
+  }
+  pl.ws_total = pl.ws_H + pl.ws_S + pl.ws_hin;
+  return pl;
+}
+
+ssm_status validate_scan_desc(const ssm_scan_desc* d) {
+  if (!d) return SSM_ERR_NULL;
+  if (d->batch <= 0 || d->seqlen <= 0 || d->dim <= 0 || d->dstate <= 0) return SSM_ERR_SHAPE;
+  if (d->flags & ~kScanFlags) return SSM_ERR_UNSUPPORTED;
+  if (d->dstate > SSM_SCAN_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
+  const int32_t io = d->x.dtype;
+  if (io == SSM_F16) return SSM_ERR_UNSUPPORTED;
+  const bool io_ok = io == SSM_F32 || io == SSM_BF16;
+  const int64_t bld[3] = {d->batch, d->seqlen, d->dim};
+  const int64_t bln[3] = {d->batch, d->seqlen, d->dstate};
+  const int64_t dn[2] = {d->dim, d->dstate};
+  const int64_t dd[1] = {d->dim};
+  const int64_t bdn[3] = {d->batch, d->dim, d->dstate};
+  ssm_status s;
+  if ((s = check_tensor(d->x, 3, bld, io_ok, true, false))) return s;
+  if ((s = check_tensor(d->delta, 3, bld, d->delta.dtype == io, true, false))) return s;
+  if ((s = check_tensor(d->B, 3, bln, d->B.dtype == io, false, false))) return s;
+  if ((s = check_tensor(d->C, 3, bln, d->C.dtype == io, false, false))) return s;
+  if ((s = check_tensor(d->A, 2, dn, d->A.dtype == SSM_F32, false, false))) return s;
+  if ((s = check_tensor(d->y, 3, bld, d->y.dtype == io || d->y.dtype == SSM_F32, true, false))) return s;
+  if (!non_overlapping(d->y)) return SSM_ERR_STRIDE;
+  if (d->flags & SSM_HAS_Z)
+    if ((s = check_tensor(d->z, 3, bld, d->z.dtype == io, true, false))) return s;
+  if (d->flags & SSM_HAS_D)
+    if ((s = check_tensor(d->D, 1, dd, d->D.dtype == SSM_F32, false, false))) return s;
+  if (d->flags & SSM_HAS_H0)
+    if ((s = check_tensor(d->h0, 3, bdn, d->h0.dtype == SSM_F32, false, true))) return s;
+  if (d->flags & SSM_WANT_HLAST)
+    if ((s = check_tensor(d->h_last, 3, bdn, d->h_last.dtype == SSM_F32, false, true))) return s;
+  return SSM_OK;
+}
+
+ssm_status validate_scan_ptrs(const ssm_scan_desc* d, const ssm_scan_ptrs* p) {
+  if (!p) return SSM_ERR_NULL;
+  const uint32_t f = d->flags;
+  if (!p->x || !p->delta || !p->A || !p->B || !p->C || !p->y) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_Z) && !p->z) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_D) && !p->D) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_H0) && !p->h0) return SSM_ERR_NULL;
+  if ((f & SSM_WANT_HLAST) && !p->h_last) return SSM_ERR_NULL;
+  const int64_t io = esize(d->x.dtype);
+  if (!aligned(p->x, io) || !aligned(p->delta, io) || !aligned(p->B, io) || !aligned(p->C, io) ||
+      !aligned(p->A, 4) || !aligned(p->y, esize(d->y.dtype)))
+    return SSM_ERR_ALIGN;
+  if (((f & SSM_HAS_Z) && !aligned(p->z, io)) || ((f & SSM_HAS_D) && !aligned(p->D, 4)) ||
+      ((f & SSM_HAS_H0) && !aligned(p->h0, 4)) || ((f & SSM_WANT_HLAST) && !aligned(p->h_last, 4)))
+    return SSM_ERR_ALIGN;
+  const Span ins[] = {span_of(d->x, p->x),
+                      span_of(d->delta, p->delta),
+                      span_of(d->A, p->A),
+                      span_of(d->B, p->B),
+                      span_of(d->C, p->C),
+                      (f & SSM_HAS_D) ? span_of(d->D, p->D) : Span(),
+                      (f & SSM_HAS_Z) ? span_of(d->z, p->z) : Span(),
+                      (f & SSM_HAS_H0) ? span_of(d->h0, p->h0) : Span()};
+  const Span ys = span_of(d->y, p->y);
+  const Span hl = (f & SSM_WANT_HLAST) ? span_of(d->h_last, p->h_last) : Span();
+  for (const Span& s : ins)
+    if (overlap(ys, s) || overlap(hl, s)) return SSM_ERR_ALIAS;
+  if (overlap(ys, hl)) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
+// ------------------------------------------------------------------- SSD
+
+struct SSDPlan {
+  int64_t nchunks = 0, Lp = 0;
+  int64_t ws_acum = 0, ws_beta = 0, ws_states = 0, ws_sin = 0, ws_total = 0;
+};
+
+SSDPlan plan_ssd(const ssm_ssd_desc& d) {
+  SSDPlan pl;
+  pl.nchunks = (d.seqlen + d.chunk - 1) / d.chunk;
+  pl.Lp = pl.nchunks * d.chunk;
+  pl.ws_acum = round256(d.batch * d.nheads * pl.Lp * 4);
+  pl.ws_beta = pl.ws_acum;
+  pl.ws_states = round256(d.batch * pl.nchunks * d.nheads * d.headdim * d.dstate * 4);
+  pl.ws_sin = round256(d.batch * pl.nchunks * d.nheads * d.headdim * d.dstate * 2);
+  pl.ws_total = pl.ws_acum + pl.ws_beta + pl.ws_states + pl.ws_sin;
+  return pl;
+}
+
+ssm_status validate_ssd_desc(const ssm_ssd_desc* d) {
+  if (!d) return SSM_ERR_NULL;
+  if (d->batch <= 0 || d->seqlen <= 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0 ||
+      d->chunk <= 0)
+    return SSM_ERR_SHAPE;
+  if (d->nheads % d->ngroups) return SSM_ERR_SHAPE;
+  if (d->flags & ~kSSDFlags) return SSM_ERR_UNSUPPORTED;
+  if (d->headdim != 64 || d->dstate != 64 || (d->chunk != 64 && d->chunk != 128 && d->chunk != 256))
+    return SSM_ERR_UNSUPPORTED;
+  if (d->x.dtype == SSM_F32 || d->x.dtype == SSM_F16) return SSM_ERR_UNSUPPORTED;
+  const int64_t blhp[4] = {d->batch, d->seqlen, d->nheads, d->headdim};
+  const int64_t blh[3] = {d->batch, d->seqlen, d->nheads};
+  const int64_t blgn[4] = {d->batch, d->seqlen, d->ngroups, d->dstate};
+  const int64_t h1[1] = {d->nheads};
+  const int64_t bhpn[4] = {d->batch, d->nheads, d->headdim, d->dstate};
+  ssm_status s;
+  if ((s = check_tensor(d->x, 4, blhp, d->x.dtype == SSM_BF16, true, false))) return s;
+  if ((s = check_tensor(d->delta, 3, blh, d->delta.dtype == SSM_BF16, true, false))) return s;
+  if ((s = check_tensor(d->B, 4, blgn, d->B.dtype == SSM_BF16, true, false))) return s;
+  if ((s = check_tensor(d->C, 4, blgn, d->C.dtype == SSM_BF16, true, false))) return s;
+  if ((s = check_tensor(d->A, 1, h1, d->A.dtype == SSM_F32, false, false))) return s;
+  if ((s = check_tensor(d->y, 4, blhp, d->y.dtype == SSM_BF16 || d->y.dtype == SSM_F32, true, false))) return s;
+  if (!non_overlapping(d->y)) return SSM_ERR_STRIDE;
+  if (d->flags & SSM_HAS_D)
+    if ((s = check_tensor(d->D, 1, h1, d->D.dtype == SSM_F32, false, false))) return s;
+  if (d->flags & SSM_HAS_H0)
+    if ((s = check_tensor(d->h0, 4, bhpn, d->h0.dtype == SSM_F32, false, true))) return s;
+  if (d->flags & SSM_WANT_HLAST)
+    if ((s = check_tensor(d->h_last, 4, bhpn, d->h_last.dtype == SSM_F32, false, true))) return s;
+  return SSM_OK;
+}
+
+// Which pointers a step reads or writes.
+enum : unsigned { kNeedX = 1, kNeedDelta = 2, kNeedB = 4, kNeedC = 8, kNeedY = 16, kNeedAll = 31 };
+
+ssm_status validate_ssd_ptrs(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, unsigned need) {
+  if (!p) return SSM_ERR_NULL;
+  const uint32_t f = d->flags;
+  if (!p->A) return SSM_ERR_NULL;
+  if (((need & kNeedX) && !p->x) || ((need & kNeedDelta) && !p->delta) || ((need & kNeedB) && !p->B) ||
+      ((need & kNeedC) && !p->C) || ((need & kNeedY) && !p->y))
+    return SSM_ERR_NULL;
+  if ((need & kNeedY) && (f & SSM_HAS_D) && !p->D) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_H0) && !p->h0) return SSM_ERR_NULL;
+  if ((f & SSM_WANT_HLAST) && !p->h_last) return SSM_ERR_NULL;
+  if ((p->x && !aligned(p->x, 2)) || (p->delta && !aligned(p->delta, 2)) || (p->B && !aligned(p->B, 2)) ||
+      (p->C && !aligned(p->C, 2)) || !aligned(p->A, 4) || (p->y && !aligned(p->y, esize(d->y.dtype))) ||
+      (p->D && !aligned(p->D, 4)) || (p->h0 && !aligned(p->h0, 4)) || (p->h_last && !aligned(p->h_last, 4)))
+    return SSM_ERR_ALIGN;
+  const Span ins[] = {span_of(d->x, p->x),
+                      span_of(d->delta, p->delta),
+                      span_of(d->A, p->A),
+                      span_of(d->B, p->B),
+                      span_of(d->C, p->C),
+                      (f & SSM_HAS_D) ? span_of(d->D, p->D) : Span(),
+                      (f & SSM_HAS_H0) ? span_of(d->h0, p->h0) : Span()};
+  const Span ys = (need & kNeedY) ? span_of(d->y, p->y) : Span();
+  const Span hl = (f & SSM_WANT_HLAST) ? span_of(d->h_last, p->h_last) : Span();
+  for (const Span& s : ins)
+    if (overlap(ys, s) || overlap(hl, s)) return SSM_ERR_ALIAS;
+  if (overlap(ys, hl)) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
+ssm::SSDParams make_ssd_params(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, const SSDPlan& pl) {
+  ssm::SSDParams q;
+  std::memset(&q, 0, sizeof(q));
+  q.x = p->x; q.delta = p->delta; q.A = p->A; q.B = p->B; q.C = p->C;
+  q.Dskip = (d->flags & SSM_HAS_D) ? p->D : nullptr;
+  q.y = p->y;
+  q.h0 = (d->flags & SSM_HAS_H0) ? p->h0 : nullptr;
+  q.h_last = (d->flags & SSM_WANT_HLAST) ? p->h_last : nullptr;
+  q.batch = d->batch; q.L = d->seqlen; q.H = d->nheads; q.P = d->headdim; q.N = d->dstate;
+  q.G = d->ngroups; q.Q = d->chunk; q.nchunks = pl.nchunks; q.Lp = pl.Lp;
+  q.xs_b = d->x.stride[0]; q.xs_t = d->x.stride[1]; q.xs_h = d->x.stride[2];
+  q.ds_b = d->delta.stride[0]; q.ds_t = d->delta.stride[1]; q.ds_h = d->delta.stride[2];
+  q.Bs_b = d->B.stride[0]; q.Bs_t = d->B.stride[1]; q.Bs_g = d->B.stride[2];
+  q.Cs_b = d->C.stride[0]; q.Cs_t = d->C.stride[1]; q.Cs_g = d->C.stride[2];
+  q.ys_b = d->y.stride[0]; q.ys_t = d->y.stride[1]; q.ys_h = d->y.stride[2];
+  q.As_h = d->A.stride[0];
+  q.Ds_h = (d->flags & SSM_HAS_D) ? d->D.stride[0] : 0;
+  q.euler = (d->flags & SSM_DISC_EULER) ? 1 : 0;
+  q.y_f32 = d->y.dtype == SSM_F32;
+  return q;
+}
+
+ssm_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return SSM_OK;
+  g_last_hip_error = (int)e;
+  return SSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_string(ssm_status s) {
+  switch (s) {
+    case SSM_OK: return "SSM_OK";
+    case SSM_ERR_NULL: return "SSM_ERR_NULL: a required pointer is NULL";
+    case SSM_ERR_SHAPE: return "SSM_ERR_SHAPE: a size is <= 0 or a tensor shape does not match";
+    case SSM_ERR_DTYPE: return "SSM_ERR_DTYPE: dtype not allowed for this tensor";
+    case SSM_ERR_STRIDE: return "SSM_ERR_STRIDE: negative, non-unit innermost or self-overlapping strides";
+    case SSM_ERR_ALIGN: return "SSM_ERR_ALIGN: pointer not aligned";
+    case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps another tensor";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: valid but not implemented";
+    case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing or too small";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP: a HIP call failed";
+  }
+  return "unknown ssm_status";
+}
+
+int ssm_last_hip_error(void) { return g_last_hip_error; }
+
+ssm_status ssm_selective_scan_workspace_size(const ssm_scan_desc* d, size_t* bytes) {
+  if (!bytes) return SSM_ERR_NULL;
+  ssm_status s = validate_scan_desc(d);
+  if (s) return s;
+  *bytes = (size_t)plan_scan(*d).ws_total;
+  return SSM_OK;
+}
+
+ssm_status ssm_selective_scan_fwd(const ssm_scan_desc* d, const ssm_scan_ptrs* p, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream) {
+  ssm_status s = validate_scan_desc(d);
+  if (s) return s;
+  if ((s = validate_scan_ptrs(d, p))) return s;
+  const ScanPlan pl = plan_scan(*d);
+  if (pl.ws_total > 0) {
+    if (!workspace || workspace_bytes < (size_t)pl.ws_total) return SSM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SSM_ERR_ALIGN;
+  }
+  ssm::ScanParams q;
+  std::memset(&q, 0, sizeof(q));
+  const uint32_t f = d->flags;
+  q.x = p->x; q.delta = p->delta; q.z = (f & SSM_HAS_Z) ? p->z : nullptr; q.y = p->y;
+  q.B = p->B; q.C = p->C; q.A = p->A; q.Dskip = (f & SSM_HAS_D) ? p->D : nullptr;
+  q.h0 = (f & SSM_HAS_H0) ? p->h0 : nullptr;
+  q.h_last = (f & SSM_WANT_HLAST) ? p->h_last : nullptr;
+  q.batch = d->batch; q.L = d->seqlen; q.D = d->dim; q.N = d->dstate;
+  q.xs_b = d->x.stride[0]; q.xs_t = d->x.stride[1];
+  q.ds_b = d->delta.stride[0]; q.ds_t = d->delta.stride[1];
+  if (f & SSM_HAS_Z) { q.zs_b = d->z.stride[0]; q.zs_t = d->z.stride[1]; }
+  q.ys_b = d->y.stride[0]; q.ys_t = d->y.stride[1];
+  q.Bs_b = d->B.stride[0]; q.Bs_t = d->B.stride[1]; q.Bs_n = d->B.stride[2];
+  q.Cs_b = d->C.stride[0]; q.Cs_t = d->C.stride[1]; q.Cs_n = d->C.stride[2];
+  q.As_d = d->A.stride[0]; q.As_n = d->A.stride[1];
+  q.Ds_d = (f & SSM_HAS_D) ? d->D.stride[0] : 0;
+  q.flags = f;
+  q.io_bf16 = d->x.dtype == SSM_BF16;
+  q.y_f32 = d->y.dtype == SSM_F32;
+  q.n_seg = pl.n_seg;
+  q.seg_len = pl.seg_len;
+  if (pl.n_seg > 1) {
+    char* w = (char*)workspace;
+    q.agg_H = (float*)w;
+    q.agg_S = (float*)(w + pl.ws_H);
+    q.h_in = (float*)(w + pl.ws_H + pl.ws_S);
+  }
+  return hip_status(ssm::launch_selective_scan(q, (hipStream_t)hip_stream));
+}
+
+ssm_status ssm_ssd_chunk_workspace_size(const ssm_ssd_desc* d, size_t* bytes) {
+  if (!bytes) return SSM_ERR_NULL;
+  ssm_status s = validate_ssd_desc(d);
+  if (s) return s;
+  *bytes = (size_t)plan_ssd(*d).ws_total;
+  return SSM_OK;
+}
+
+ssm_status ssm_ssd_chunk_fwd(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, void* workspace, size_t workspace_bytes,
+                             void* hip_stream) {
+  ssm_status s = validate_ssd_desc(d);
+  if (s) return s;
+  if ((s = validate_ssd_ptrs(d, p, kNeedAll))) return s;
+  const SSDPlan pl = plan_ssd(*d);
+  if (!workspace || workspace_bytes < (size_t)pl.ws_total) return SSM_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return SSM_ERR_ALIGN;
+  ssm::SSDParams q = make_ssd_params(d, p, pl);
+  char* w = (char*)workspace;
+  q.A_cum = (float*)w;
+  q.beta = (float*)(w + pl.ws_acum);
+  q.states = (float*)(w + pl.ws_acum + pl.ws_beta);
+  q.S_in = (void*)(w + pl.ws_acum + pl.ws_beta + pl.ws_states);
+  hipStream_t st = (hipStream_t)hip_stream;
+  hipError_t e;
+  if ((e = ssm::launch_ssd_chunk_cumsum(q, st)) != hipSuccess) return hip_status(e);
+  if ((e = ssm::launch_ssd_chunk_state(q, st)) != hipSuccess) return hip_status(e);
+  if ((e = ssm::launch_ssd_state_passing(q, st)) != hipSuccess) return hip_status(e);
+  return hip_status(ssm::launch_ssd_chunk_scan(q, st));
+}
+
+ssm_status ssm_ssd_chunk_cumsum(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, float* A_cum, float* beta,
+                                void* hip_stream) {
+  ssm_status s = validate_ssd_desc(d);
+  if (s) return s;
+  if ((s = validate_ssd_ptrs(d, p, kNeedDelta))) return s;
+  if (!A_cum || !beta) return SSM_ERR_NULL;
+  if (!aligned(A_cum, 4) || !aligned(beta, 4)) return SSM_ERR_ALIGN;
+  const SSDPlan pl = plan_ssd(*d);
+  ssm::SSDParams q = make_ssd_params(d, p, pl);
+  q.A_cum = A_cum;
+  q.beta = beta;
+  return hip_status(ssm::launch_ssd_chunk_cumsum(q, (hipStream_t)hip_stream));
+}
+
+ssm_status ssm_ssd_chunk_state(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, const float* A_cum,
+                               const float* beta, float* states, void* hip_stream) {
+  ssm_status s = validate_ssd_desc(d);
+  if (s) return s;
+  if ((s = validate_ssd_ptrs(d, p, kNeedX | kNeedB))) return s;
+  if (!A_cum || !beta || !states) return SSM_ERR_NULL;
+  if (!aligned(A_cum, 4) || !aligned(beta, 4) || !aligned(states, 16)) return SSM_ERR_ALIGN;
+  const SSDPlan pl = plan_ssd(*d);
+  ssm::SSDParams q = make_ssd_params(d, p, pl);
+  q.A_cum = (float*)A_cum;
+  q.beta = (float*)beta;
+  q.states = states;
+  return hip_status(ssm::launch_ssd_chunk_state(q, (hipStream_t)hip_stream));
+}
+
+ssm_status ssm_ssd_state_passing(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, const float* A_cum,
+                                 const float* states, void* S_in, void* hip_stream) {
+  ssm_status s = validate_ssd_desc(d);
+  if (s) return s;
+  if ((s = validate_ssd_ptrs(d, p, 0))) return s;
+  if (!A_cum || !states || !S_in) return SSM_ERR_NULL;
+  if (!aligned(A_cum, 4) || !aligned(states, 16) || !aligned(S_in, 16)) return SSM_ERR_ALIGN;
+  const SSDPlan pl = plan_ssd(*d);
+  ssm::SSDParams q = make_ssd_params(d, p, pl);
+  q.A_cum = (float*)A_cum;
+  q.states = (float*)states;
+  q.S_in = S_in;
+  return hip_status(ssm::launch_ssd_state_passing(q, (hipStream_t)hip_stream));
+}
+
+ssm_status ssm_ssd_chunk_scan(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, const float* A_cum, const float* beta,
+                              const void* S_in, void* hip_stream) {
+  ssm_status s = validate_ssd_desc(d);
+  if (s) return s;
+  if ((s = validate_ssd_ptrs(d, p, kNeedX | kNeedB | kNeedC | kNeedY))) return s;
+  if (!A_cum || !beta || !S_in) return SSM_ERR_NULL;
+  if (!aligned(A_cum, 4) || !aligned(beta, 4) || !aligned(S_in, 16)) return SSM_ERR_ALIGN;
+  const SSDPlan pl = plan_ssd(*d);
+  ssm::SSDParams q = make_ssd_params(d, p, pl);
+  q.A_cum = (float*)A_cum;
+  q.beta = (float*)beta;
+  q.S_in = (void*)S_in;
+  return hip_status(ssm::launch_ssd_chunk_scan(q, (hipStream_t)hip_stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal declarations shared by the host dispatch (ssm_abi.cpp) and the
+// gfx950 kernels (scan_fwd.hip, ssd_fwd.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// ----------------------------------------------------------- selective scan
+struct ScanParams {
+  const void* x;
+  const void* delta;
+  const void* z;
+  void* y;
+  const void* B;
+  const void* C;
+  const float* A;
+  const float* Dskip;
+  const float* h0;
+  float* h_last;
+  int64_t batch, L, D, N;
+  int64_t xs_b, xs_t, ds_b, ds_t, zs_b, zs_t, ys_b, ys_t;  // element strides
+  int64_t Bs_b, Bs_t, Bs_n, Cs_b, Cs_t, Cs_n;
+  int64_t As_d, As_n, Ds_d;
+  uint32_t flags;
+  int io_bf16;  // x, delta, z, B, C are bf16 (1) or fp32 (0)
+  int y_f32;    // y stored as fp32 (1) or in the io type (0)
+  // Sequence split: segment s covers [s*seg_len, min(L, (s+1)*seg_len)).
+  int n_seg;
+  int64_t seg_len;
+  float* agg_H;  // (batch, n_seg-1, D, N): end state of segment s scanned from 0
+  float* agg_S;  // (batch, n_seg-1, D): sum of delta over segment s
+  float* h_in;   // (batch, n_seg, D, N): state entering segment s
+};
+
+// Tiling of the scan kernels (also used by the host planner).
+constexpr int kScanLanesPerChannel = 8;
+constexpr int kScanChannelsPerBlock = 32;
+constexpr int kScanTileSteps = 32;
+constexpr int kScanThreads = kScanLanesPerChannel * kScanChannelsPerBlock;
+
+hipError_t launch_selective_scan(const ScanParams& p, hipStream_t stream);
+
+// ---------------------------------------------------------------------- SSD
+struct SSDParams {
+  const void* x;      // (batch, L, H, P) bf16
+  const void* delta;  // (batch, L, H) bf16
+  const float* A;     // (H)
+  const void* B;      // (batch, L, G, N) bf16
+  const void* C;
+  const float* Dskip;  // (H) or null
+  void* y;             // (batch, L, H, P) bf16 or fp32
+  const float* h0;     // (batch, H, P, N) or null
+  float* h_last;       // (batch, H, P, N) or null
+  int64_t batch, L, H, P, N, G, Q, nchunks, Lp;
+  int64_t xs_b, xs_t, xs_h;  // x strides (p stride 1)
+  int64_t ds_b, ds_t, ds_h;  // delta strides
+  int64_t Bs_b, Bs_t, Bs_g, Cs_b, Cs_t, Cs_g;  // B, C strides (n stride 1)
+  int64_t ys_b, ys_t, ys_h;
+  int64_t As_h, Ds_h;
+  int euler;
+  int y_f32;
+  float* A_cum;   // (batch, H, Lp)
+  float* beta;    // (batch, H, Lp)
+  float* states;  // (batch, nchunks, H, P, N)
+  void* S_in;     // (batch, nchunks, H, P, N) bf16
+};
+
+hipError_t launch_ssd_chunk_cumsum(const SSDParams& p, hipStream_t stream);
+hipError_t launch_ssd_chunk_state(const SSDParams& p, hipStream_t stream);
+hipError_t launch_ssd_state_passing(const SSDParams& p, hipStream_t stream);
+hipError_t launch_ssd_chunk_scan(const SSDParams& p, hipStream_t stream);
+
+}  // namespace ssm

@@ -1,0 +1,47 @@
+"""Helpers shared by the GPU parity tests: upload the seeded host inputs,
+run the HIP path through the C ABI, and compare with the oracle."""
+import os
+import sys
+
+import numpy as np
+import torch
+
+import synth
+
+FP32_TOL = {"rel_l2": 1e-5, "max_abs": 1e-4}
+BF16_TOL = {"rel_l2": 2e-2}
+
+
+def dev_tensor(a: np.ndarray, io: str) -> torch.Tensor:
+    if io == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def metrics(got: np.ndarray, ref: np.ndarray) -> dict:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    diff = got - ref
+    return {"rel_l2": float(np.linalg.norm(diff) / max(1e-300, np.linalg.norm(ref))),
+            "max_abs": float(np.max(np.abs(diff))) if diff.size else 0.0,
+            "nan": int(np.isnan(got).sum())}
+
+
+def assert_close(got, ref, io: str, what: str = ""):
+    m = metrics(got, ref)
+    tol = FP32_TOL if io == "f32" else BF16_TOL
+    print("%s %s" % (what, m), flush=True)
+    assert m["nan"] == 0, (what, m)
+    for k, v in tol.items():
+        assert m[k] <= v, (what, k, m, tol)
+    return m
+
+
+def banner(msg: str):
+    """Name the case on stdout before any GPU work (visible if the box dies)."""
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
