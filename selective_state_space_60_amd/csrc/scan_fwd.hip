@@ -6,31 +6,37 @@
 //   Abar = exp(delta*A),  Bbar = (exp(delta*A) - 1)/A * B   (zero-order hold)
 //   h_t = Abar h_{t-1} + Bbar x_t,   y_t = (C_t . h_t + D x_t) * silu(z_t)
 // The pages' recipe -- discretise, scan and multiply by C in one kernel, with
-// no (batch, L, D, N) tensor in HBM -- is kept; the blocking is MI355X's own:
+// no (batch, L, D, N) tensor in HBM -- is kept; the blocking is MI355X's own.
 //
-//  * A 256-thread workgroup owns 32 channels of one batch row and one stretch
-//    of the sequence.  Each channel is spread over 8 lanes; a lane keeps N/8
-//    states in registers for the whole walk, so the N-wide state never leaves
-//    the register file.
-//  * The sequence is walked in tiles of 32 steps.  x, delta, z (32 x 32) and
-//    B, C (32 x N) of the next tile are fetched with coalesced loads into
-//    registers while the current tile is being scanned, then converted to fp32
-//    and staged in LDS.  Each lane reads its channel's delta/x and its states'
-//    B/C from LDS (broadcast reads).
-//  * Per step and state: u = delta*A*log2(e) (1 mul), Abar = v_exp_f32(u)
-//    (a half-rate transcendental on gfx950), c = Abar/A - 1/A (1 fma),
-//    h = Abar*h + c*(B*x) (3 ops), y += C*h (1 fma).  The 8 lanes of a channel
-//    add their partial readouts with three DPP adds.
-//  * The readout sums of a tile go to LDS; the whole workgroup then applies
-//    the D skip and the SiLU(z) gate, rounds to the output type and writes the
-//    tile with coalesced stores.
-//  * When the batch x channel count alone cannot fill the 1024 SIMDs (long,
-//    narrow problems), the sequence is cut into segments: (1) every segment
-//    but the last is scanned from h = 0 for its end state and its sum of
-//    delta, (2) a small kernel chains those into the state entering each
-//    segment, (3) every segment is scanned again from that state and writes y.
-//    This is the associative combine of (Abar, Bbar x) pairs (tildalice.io,
-//    병렬 스캔) applied at segment granularity.
+// On gfx950 this path is bound by VALU issue, not by HBM: every state of every
+// token*channel costs one v_exp_f32 (half rate) and six fp32 ops, against ~8
+// bytes of HBM traffic per token*channel.  The layout therefore aims at full
+// VALU occupancy and balance across the 1024 SIMDs:
+//
+//  * A 256-thread workgroup owns 16 channels of one batch row and one stretch
+//    of the sequence.  Each channel is spread over 16 lanes; a lane keeps
+//    N/16 states in registers for the whole walk (one state at N = 16), so the
+//    N-wide state never leaves the register file.  With 16 lanes per channel a
+//    wide layer gives thousands of equal waves, and the Mamba-2.8B layer
+//    (4 x 5120 channels) gives exactly five per SIMD.
+//  * The sequence is walked in tiles of 32 steps.  x, delta, z (32 x 16) and
+//    B, C (32 x N) of the next tile are fetched into registers while the
+//    current tile is scanned, then converted to fp32 and staged in LDS as
+//    (delta, x) and (B, C) pairs, so a lane reads each step's operands with two
+//    8-byte LDS reads (broadcast across the lanes that share them).
+//  * Per step and state: u = delta*A*log2(e), Abar = v_exp_f32(u),
+//    c = Abar/A - 1/A (one fma with a precomputed 1/A), h = Abar*h + c*(B*x),
+//    partial readout C*h -- no cross-lane traffic inside the recurrence.
+//  * Each lane writes its partial readout to LDS; after the tile, the
+//    workgroup sums the 16 partials of each (step, channel), adds D*x, applies
+//    SiLU(z), rounds to the output type and stores.
+//  * When batch x channels cannot fill the GPU (long, narrow problems), the
+//    sequence is cut into segments: (1) each segment but the last is scanned
+//    from h = 0 for its end state and its sum of delta, (2) a small kernel
+//    chains those into the state entering each segment (the associative
+//    combine of (Abar, Bbar x) pairs -- tildalice.io, 병렬 스캔 -- at segment
+//    granularity), (3) every segment is scanned from its entering state and
+//    writes y.
 #include <hip/hip_runtime.h>
 
 #include "ssm_internal.h"
@@ -38,132 +44,283 @@
 namespace ssm {
 namespace {
 
-constexpr int G = kScanLanesPerChannel;
-constexpr int CH = kScanChannelsPerBlock;
-constexpr int TT = kScanTileSteps;
-constexpr int NT = kScanThreads;
+constexpr int G = kScanLanesPerChannel;    // 16 lanes per channel
+constexpr int CH = kScanChannelsPerBlock;  // 16 channels per workgroup
+constexpr int TT = kScanTileSteps;         // 32 steps per tile
+constexpr int NT = kScanThreads;           // 256 threads
+constexpr int EPT = TT * CH / NT;          // x/delta/z elements per thread per tile (2)
 constexpr float kLog2e = 1.4426950408889634f;
+
+static_assert(G == 16 && CH * G == NT && EPT == 2, "tiling");
 
 enum : uint32_t { kHasZ = 1u, kHasD = 2u, kEuler = 4u, kHasH0 = 8u, kWantHLast = 16u };
 
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-template <bool BF16>
-__device__ __forceinline__ float ld_io(const void* p, int64_t i) {
-  if constexpr (BF16) return bf2f(((const uint16_t*)p)[i]);
-  else return ((const float*)p)[i];
-}
-
-// Sum over the 8 lanes of a channel (lanes 8k..8k+7): xor-1, xor-2 within
-// quads, then the two quads of each 8-lane half-row.
-__device__ __forceinline__ float sum8(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-  return v;
-}
-
-// Logical block index -> (dblk, seg, b), with blocks of neighbouring
-// channels placed on the same XCD (the hardware deals consecutive block ids
-// round-robin over the 8 XCDs), so that the 128-byte lines two blocks share
-// are fetched into one L2.
+// Logical block index with blocks of neighbouring channels placed on the same
+// XCD (the hardware deals consecutive block ids round-robin over the 8 XCDs),
+// so the cache lines several blocks share are fetched into one L2.
 __device__ __forceinline__ int64_t logical_block(int64_t nblocks_padded) {
-  int64_t i = blockIdx.x;
+  const int64_t i = blockIdx.x;
   return (i & 7) * (nblocks_padded >> 3) + (i >> 3);
 }
 
+constexpr int TP = TT + 2;  // time pitch of the time-major LDS arrays (keeps 16-byte alignment)
+
+// Finalize ownership: wave w finalizes the channels it scans (64/G of them);
+// lane -> channel fin_channel, step pair fin_pair.
+__device__ __forceinline__ int fin_channel(int tid) { return (tid / 64) * (64 / G) + (tid % (64 / G)); }
+__device__ __forceinline__ int fin_pair(int tid) { return (tid % 64) / (64 / G); }
+
 template <int KS>
 struct alignas(16) ScanSmem {
-  float x[2][TT][CH];
-  float dl[2][TT][CH];
-  float z[2][TT][CH];
-  float Bt[2][TT][G * KS];
-  float Ct[2][TT][G * KS];
-  float ysum[TT][CH];
+  float2 dx[2][CH][TP];      // (delta, x), time-major per channel
+  float2 bc[2][G * KS][TP];  // (B_n, C_n), time-major per state
+  float2 z[TT / 2][CH];      // (z_t, z_t+1) of the finalizing thread's channel
   float Dk[CH];
   int any_zero_A;
 };
 
-// Registers holding one tile's global loads while the previous tile is scanned.
-template <int KS>
-struct TileRegs {
-  float x[4], dl[4], z[4];
-  float B[KS], C[KS];
+// Per-lane partial readouts of one tile, as (step 2u, step 2u+1) pairs, in an
+// LDS array of its own so the compiler can move operand reads of later steps
+// above these stores.  Each wave owns a region: row sg (the state lane),
+// column tp*CPW + c (step pair, channel of the wave).  A row holds 64 pairs
+// (512 bytes) plus 16 bytes of padding: the finalize's loads read one row (512
+// contiguous bytes) and the compute loop's stores (16 rows x 32 bytes) land
+// on staggered banks.  (A 32-byte pad would make the stores conflict-free but
+// push the workgroup past the LDS size that lets three share a compute unit.)
+constexpr int CPW = 64 / G;            // channels per wave (4)
+constexpr int PROW = (TT / 2) * CPW + 2;  // row pitch in float2
+struct alignas(16) PartSmem {
+  float2 part[NT / 64][G][PROW];
 };
 
+// One tile's global loads, held as raw bits until store_tile: the loads are
+// issued two tiles ahead of use, and converting or masking the values at load
+// time would force the wave to wait for them right away.  Out-of-range
+// elements are loaded from a valid address (offset 0) and zeroed on store.
+template <bool BF16, int KS>
+struct TileRegs {
+  static constexpr int W = BF16 ? 1 : 2;  // dwords per two channels
+  uint32_t x[W], dl[W];                  // channels c0, c0+1 of one step
+  uint32_t z[2];                         // steps 2*fin_pair, +1 of channel fin_channel
+  static constexpr int BW = BF16 ? KS : 2 * KS;  // dwords holding this thread's 2*KS B (or C) values
+  uint32_t B[BW], C[BW];
+  uint8_t row_ok, dleft, z_ok, bc_ok;    // validity, applied on store
+};
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t ld_raw(const void* p, int64_t i) {
+  if constexpr (BF16) return ((const uint16_t*)p)[i];
+  else return ((const uint32_t*)p)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ float raw2f(uint32_t v) {
+  if constexpr (BF16) return __uint_as_float(v << 16);
+  else return __uint_as_float(v);
+}
+
+// Two consecutive channels at element offset `off` (VEC: one 4/8-byte load).
 template <bool BF16, bool VEC>
-__device__ __forceinline__ void load4(const void* base, int64_t off, bool row_ok, int dleft, float out[4]) {
-  // 4 consecutive channels starting at element `off`; dleft = channels left in D.
-  if (VEC && row_ok && dleft >= 4) {
-    if constexpr (BF16) {
-      uint2 v = *(const uint2*)((const uint16_t*)base + off);
-      out[0] = bf2f(v.x & 0xFFFF); out[1] = bf2f(v.x >> 16);
-      out[2] = bf2f(v.y & 0xFFFF); out[3] = bf2f(v.y >> 16);
-    } else {
-      float4 v = *(const float4*)((const float*)base + off);
-      out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+__device__ __forceinline__ void load2_raw(const void* base, int64_t off, bool ok2, bool ok0, bool ok1,
+                                          uint32_t (&w)[BF16 ? 1 : 2]) {
+  if (VEC) {
+    const int64_t o = ok2 ? off : 0;
+    if constexpr (BF16) w[0] = *(const uint32_t*)((const uint16_t*)base + o);
+    else {
+      const uint2 v = *(const uint2*)((const float*)base + o);
+      w[0] = v.x;
+      w[1] = v.y;
     }
   } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = (row_ok && j < dleft) ? ld_io<BF16>(base, off + j) : 0.f;
+    const uint32_t a = ld_raw<BF16>(base, ok0 ? off : 0);
+    const uint32_t c = ld_raw<BF16>(base, ok1 ? off + 1 : 0);
+    if constexpr (BF16) w[0] = a | (c << 16);
+    else {
+      w[0] = a;
+      w[1] = c;
+    }
   }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float2 unpack2(const uint32_t (&w)[BF16 ? 1 : 2]) {
+  if constexpr (BF16) return make_float2(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u));
+  else return make_float2(__uint_as_float(w[0]), __uint_as_float(w[1]));
+}
+
+// Per-thread element offsets of tile 0 and their per-tile increments.
+struct LoadPlan {
+  int64_t x, dl, z, B, C;  // offsets of this thread's first element in tile 0
+  int64_t bB, bC;          // batch offsets of B and C (general-stride path)
+  int64_t sx, sdl, sz, sbc;  // per-tile increments
+  int row, zt, dleft;        // step of the x/delta row; first z step; channels left (0..2)
+  bool full;                 // all CH channels of the block exist (uniform)
+  bool zc_ok;
+  bool bc_contig;            // B and C rows contiguous with N == G*KS (uniform)
+};
+
+template <int KS>
+__device__ __forceinline__ LoadPlan make_plan(const ScanParams& p, int64_t b, int64_t d0, int64_t t_begin) {
+  const int tid = threadIdx.x;
+  LoadPlan q;
+  q.row = tid / (CH / EPT);
+  const int c0 = (tid % (CH / EPT)) * EPT;
+  const int64_t left = p.D - (d0 + c0);
+  q.dleft = left >= 2 ? 2 : (left <= 0 ? 0 : (int)left);
+  q.full = d0 + CH <= p.D;
+  q.x = b * p.xs_b + (t_begin + q.row) * p.xs_t + d0 + c0;
+  q.dl = b * p.ds_b + (t_begin + q.row) * p.ds_t + d0 + c0;
+  q.sx = TT * p.xs_t;
+  q.sdl = TT * p.ds_t;
+  const int zc = fin_channel(tid);
+  q.zt = 2 * fin_pair(tid);
+  q.zc_ok = d0 + zc < p.D;
+  q.z = b * p.zs_b + (t_begin + q.zt) * p.zs_t + d0 + zc;
+  q.sz = TT * p.zs_t;
+  const int64_t esz = p.io_bf16 ? 2 : 4;
+  q.bc_contig = p.N == G * KS && p.Bs_n == 1 && p.Cs_n == 1 && p.Bs_t == p.N && p.Cs_t == p.N &&
+                p.Bs_b % (2 * KS) == 0 && p.Cs_b % (2 * KS) == 0 && (uintptr_t)p.B % (2 * KS * esz) == 0 &&
+                (uintptr_t)p.C % (2 * KS * esz) == 0;
+  q.bB = b * p.Bs_b;
+  q.bC = b * p.Cs_b;
+  q.B = b * p.Bs_b + t_begin * p.N + tid * 2 * KS;
+  q.C = b * p.Cs_b + t_begin * p.N + tid * 2 * KS;
+  q.sbc = TT * p.N;
+  return q;
 }
 
 template <bool BF16, bool VEC, int KS, bool WANT_Z>
-__device__ __forceinline__ void load_tile(const ScanParams& p, int64_t b, int64_t d0, int64_t t0, int64_t t_end,
-                                          TileRegs<KS>& r) {
+__device__ __forceinline__ void load_tile(const ScanParams& p, const LoadPlan& q, int64_t k, int64_t t0,
+                                          int64_t t_end, TileRegs<BF16, KS>& r) {
   const int tid = threadIdx.x;
-  const int row = tid >> 3, c0 = (tid & 7) * 4;
-  const int64_t t = t0 + row;
-  const bool row_ok = t < t_end;
-  const int dleft = (int)(p.D - (d0 + c0));
-  load4<BF16, VEC>(p.x, b * p.xs_b + t * p.xs_t + d0 + c0, row_ok, dleft, r.x);
-  load4<BF16, VEC>(p.delta, b * p.ds_b + t * p.ds_t + d0 + c0, row_ok, dleft, r.dl);
-  if (WANT_Z) load4<BF16, VEC>(p.z, b * p.zs_b + t * p.zs_t + d0 + c0, row_ok, dleft, r.z);
-  // B, C tile: TT x (G*KS) values, KS per thread.
+  const bool row_ok = t0 + q.row < t_end;
+  r.row_ok = row_ok;
+  r.dleft = (uint8_t)q.dleft;
+  const int64_t ox = q.x + k * q.sx, od = q.dl + k * q.sdl;
+  if (VEC && q.full) {
+    // whole block present: one paired load per tensor; rows past the end read offset 0
+    load2_raw<BF16, true>(p.x, row_ok ? ox : 0, true, true, true, r.x);
+    load2_raw<BF16, true>(p.delta, row_ok ? od : 0, true, true, true, r.dl);
+  } else {
+    const bool ok0 = row_ok && q.dleft > 0, ok1 = row_ok && q.dleft > 1;
+    load2_raw<BF16, false>(p.x, ox, false, ok0, ok1, r.x);
+    load2_raw<BF16, false>(p.delta, od, false, ok0, ok1, r.dl);
+  }
+  if (WANT_Z) {
+    // z is read only by the finalize, in its own thread mapping (channel
+    // fin_channel, steps 2*fin_pair and +1), so it needs a single LDS buffer.
+    const int64_t oz = q.z + k * q.sz;
+    const bool z0 = q.zc_ok && t0 + q.zt < t_end, z1 = q.zc_ok && t0 + q.zt + 1 < t_end;
+    r.z_ok = (uint8_t)((z0 ? 1 : 0) | (z1 ? 2 : 0));
+    r.z[0] = ld_raw<BF16>(p.z, z0 ? oz : 0);
+    r.z[1] = ld_raw<BF16>(p.z, z1 ? oz + p.zs_t : 0);
+  }
+  // B, C tile: TT x (G*KS) values, 2*KS consecutive ones per thread.
+  const int e0 = tid * 2 * KS;
+  const int rr = e0 / (G * KS);
+  const bool rows_ok = t0 + rr < t_end;
+  if (q.bc_contig) {
+    // 2*KS consecutive values per thread: one vector load each for B and C
+    const int64_t ob = rows_ok ? q.B + k * q.sbc : 0, oc = rows_ok ? q.C + k * q.sbc : 0;
+    constexpr int BW = TileRegs<BF16, KS>::BW;
+    const uint32_t* pb = (const uint32_t*)((const char*)p.B + ob * (BF16 ? 2 : 4));
+    const uint32_t* pc = (const uint32_t*)((const char*)p.C + oc * (BF16 ? 2 : 4));
+    if constexpr (BW == 1) {
+      r.B[0] = pb[0];
+      r.C[0] = pc[0];
+    } else if constexpr (BW == 2) {
+      const uint2 vb = *(const uint2*)pb, vc = *(const uint2*)pc;
+      r.B[0] = vb.x; r.B[1] = vb.y; r.C[0] = vc.x; r.C[1] = vc.y;
+    } else {
 #pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    const int e = tid * KS + k;
-    const int rr = e / (G * KS), n = e % (G * KS);
-    const int64_t tt = t0 + rr;
-    const bool ok = tt < t_end && n < p.N;
-    r.B[k] = ok ? ld_io<BF16>(p.B, b * p.Bs_b + tt * p.Bs_t + n * p.Bs_n) : 0.f;
-    r.C[k] = ok ? ld_io<BF16>(p.C, b * p.Cs_b + tt * p.Cs_t + n * p.Cs_n) : 0.f;
+      for (int j = 0; j < BW; j += 4) {
+        const uint4 vb = *(const uint4*)(pb + j), vc = *(const uint4*)(pc + j);
+        r.B[j] = vb.x; r.B[j + 1] = vb.y; r.B[j + 2] = vb.z; r.B[j + 3] = vb.w;
+        r.C[j] = vc.x; r.C[j + 1] = vc.y; r.C[j + 2] = vc.z; r.C[j + 3] = vc.w;
+      }
+    }
+    r.bc_ok = rows_ok ? (uint8_t)((1 << (2 * KS)) - 1) : 0;
+  } else {
+    // general strides: element loads (values packed as in the vector path)
+    uint8_t bc_ok = 0;
+#pragma unroll
+    for (int j = 0; j < TileRegs<BF16, KS>::BW; ++j) { r.B[j] = 0; r.C[j] = 0; }
+#pragma unroll
+    for (int j = 0; j < 2 * KS; ++j) {
+      const int e = e0 + j;
+      const int rj = e / (G * KS), n = e % (G * KS);
+      const int64_t tt = t0 + rj;
+      const bool ok = tt < t_end && n < p.N;
+      bc_ok |= (uint8_t)(ok ? 1 << j : 0);
+      const uint32_t vb = ld_raw<BF16>(p.B, ok ? q.bB + tt * p.Bs_t + n * p.Bs_n : 0);
+      const uint32_t vc = ld_raw<BF16>(p.C, ok ? q.bC + tt * p.Cs_t + n * p.Cs_n : 0);
+      if constexpr (BF16) {
+        r.B[j / 2] |= vb << (16 * (j % 2));
+        r.C[j / 2] |= vc << (16 * (j % 2));
+      } else {
+        r.B[j] = vb;
+        r.C[j] = vc;
+      }
+    }
+    r.bc_ok = bc_ok;
   }
 }
 
-template <int KS, bool WANT_Z>
-__device__ __forceinline__ void store_tile(ScanSmem<KS>& s, int buf, const TileRegs<KS>& r) {
+// z goes to its own single buffer: each thread writes only the entries its
+// own finalize reads, after that finalize.
+template <bool BF16, int KS>
+__device__ __forceinline__ void store_z(ScanSmem<KS>& s, const TileRegs<BF16, KS>& r) {
+  const float z0 = (r.z_ok & 1) ? raw2f<BF16>(r.z[0]) : 0.f;
+  const float z1 = (r.z_ok & 2) ? raw2f<BF16>(r.z[1]) : 0.f;
+  s.z[fin_pair(threadIdx.x)][fin_channel(threadIdx.x)] = make_float2(z0, z1);
+}
+
+template <bool BF16, int KS>
+__device__ __forceinline__ void store_tile(ScanSmem<KS>& s, int buf, const TileRegs<BF16, KS>& r) {
   const int tid = threadIdx.x;
-  const int row = tid >> 3, c0 = (tid & 7) * 4;
-  *(float4*)&s.x[buf][row][c0] = make_float4(r.x[0], r.x[1], r.x[2], r.x[3]);
-  *(float4*)&s.dl[buf][row][c0] = make_float4(r.dl[0], r.dl[1], r.dl[2], r.dl[3]);
-  if (WANT_Z) *(float4*)&s.z[buf][row][c0] = make_float4(r.z[0], r.z[1], r.z[2], r.z[3]);
+  const int row = tid / (CH / EPT), c0 = (tid % (CH / EPT)) * EPT;
+  float2 xv = unpack2<BF16>(r.x), dv = unpack2<BF16>(r.dl);
+  if (!r.row_ok || r.dleft < 2) {
+    xv.y = 0.f;
+    dv.y = 0.f;
+    if (!r.row_ok || r.dleft < 1) {
+      xv.x = 0.f;
+      dv.x = 0.f;
+    }
+  }
+  s.dx[buf][c0][row] = make_float2(dv.x, xv.x);
+  s.dx[buf][c0 + 1][row] = make_float2(dv.y, xv.y);
 #pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    const int e = threadIdx.x * KS + k;
-    (&s.Bt[buf][0][0])[e] = r.B[k];
-    (&s.Ct[buf][0][0])[e] = r.C[k];
+  for (int k = 0; k < 2 * KS; ++k) {
+    const int e = tid * 2 * KS + k;
+    const bool ok = (r.bc_ok >> k) & 1;
+    uint32_t vb, vc;
+    if constexpr (BF16) {
+      vb = (r.B[k / 2] >> (16 * (k % 2))) & 0xFFFFu;
+      vc = (r.C[k / 2] >> (16 * (k % 2))) & 0xFFFFu;
+    } else {
+      vb = r.B[k];
+      vc = r.C[k];
+    }
+    s.bc[buf][e % (G * KS)][e / (G * KS)] = make_float2(ok ? raw2f<BF16>(vb) : 0.f, ok ? raw2f<BF16>(vc) : 0.f);
   }
 }
 
-// Discretisation + state update for one step of one lane's KS states.
-// DISC: 0 = zero-order hold with A != 0, 1 = zero-order hold allowing A == 0,
-// 2 = Bbar = delta*B.   Returns the lane's partial readout sum_k C_k h_k.
+// One step of one lane's KS states.  DISC: 0 = zero-order hold with A != 0,
+// 1 = zero-order hold allowing A == 0 (limit delta*B), 2 = Bbar = delta*B.
 template <int KS, int DISC, bool READOUT>
 __device__ __forceinline__ float step(float (&h)[KS], const float (&A2)[KS], const float (&iA)[KS],
-                                      const float (&ez)[KS], float dt, float xt, const float* Bv,
-                                      const float* Cv) {
+                                      const float (&ez)[KS], float dt, float xt, const float* Bv, const float* Cv) {
   float yp = 0.f;
-  const float dtx = dt * xt;
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
     const float Ab = __builtin_amdgcn_exp2f(dt * A2[k]);
     if constexpr (DISC == 2) {
-      h[k] = __builtin_fmaf(Ab, h[k], Bv[k] * dtx);
+      h[k] = __builtin_fmaf(Ab, h[k], Bv[k] * (dt * xt));
     } else {
-      // (Abar - 1)/A as Abar*(1/A) - 1/A in one rounding; for A == 0 the
+      // (Abar - 1)/A as Abar*(1/A) - 1/A with one rounding; for A == 0 the
       // factor is 0 and ez*delta supplies the limit delta.
       float c = __builtin_fmaf(Ab, iA[k], -iA[k]);
       if constexpr (DISC == 1) c = __builtin_fmaf(ez[k], dt, c);
@@ -174,45 +331,113 @@ __device__ __forceinline__ float step(float (&h)[KS], const float (&A2)[KS], con
   return yp;
 }
 
-// Scan one tile of `nt` steps held in LDS buffer `buf`.
-template <int KS, int DISC, bool READOUT>
-__device__ __forceinline__ void scan_tile(ScanSmem<KS>& s, int buf, int nt, float (&h)[KS], const float (&A2)[KS],
-                                          const float (&iA)[KS], const float (&ez)[KS], float& sum_dt) {
-  const int tid = threadIdx.x;
-  const int ch = tid >> 3, sg = tid & 7;
-  auto one = [&](int t) {
-    const float dt = s.dl[buf][t][ch];
-    const float xt = s.x[buf][t][ch];
-    float Bv[KS], Cv[KS];
+constexpr int UB = 8;  // steps per register block
+
+// Operands of UB steps for one lane: (delta, x) and, per state, (B, C).
+template <int KS>
+struct StepOps {
+  float4 dx[UB / 2];
+  float4 bc[UB / 2][KS];
+};
+
+template <int KS>
+__device__ __forceinline__ void read_block(const ScanSmem<KS>& s, int buf, int t0, int ch, int sg, StepOps<KS>& o) {
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      Bv[k] = s.Bt[buf][t][sg * KS + k];
-      if (READOUT) Cv[k] = s.Ct[buf][t][sg * KS + k];
-    }
-    float yp = step<KS, DISC, READOUT>(h, A2, iA, ez, dt, xt, Bv, Cv);
-    if (READOUT) {
-      yp = sum8(yp);
-      if (sg == (t & 7)) s.ysum[t][ch] = yp;
-    } else {
-      sum_dt += dt;
-    }
-  };
-  if (nt == TT) {
-#pragma unroll 4
-    for (int t = 0; t < TT; ++t) one(t);
-  } else {
-    for (int t = 0; t < nt; ++t) one(t);
+  for (int u = 0; u < UB / 2; ++u) {
+    o.dx[u] = *(const float4*)&s.dx[buf][ch][t0 + 2 * u];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) o.bc[u][k] = *(const float4*)&s.bc[buf][sg * KS + k][t0 + 2 * u];
   }
 }
 
-// MODE 0: write y (and h_last / use h_in).  MODE 1: segment aggregates only.
+// Scan one tile of `nt` steps held in LDS buffer `buf`.  Full tiles run in
+// blocks of UB steps whose operands are read from LDS one block ahead.
+template <int KS, int DISC, bool READOUT>
+__device__ __forceinline__ void scan_tile(const ScanSmem<KS>& s, PartSmem& ps, int buf, int nt, float (&h)[KS],
+                                          const float (&A2)[KS], const float (&iA)[KS], const float (&ez)[KS],
+                                          float& sum_dt) {
+  const int tid = threadIdx.x;
+  const int ch = tid / G, sg = tid % G;
+  if (nt == TT) {
+    StepOps<KS> o[2];
+    read_block<KS>(s, buf, 0, ch, sg, o[0]);
+#pragma unroll
+    for (int blk = 0; blk < TT / UB; ++blk) {
+      if (blk + 1 < TT / UB) read_block<KS>(s, buf, (blk + 1) * UB, ch, sg, o[(blk + 1) & 1]);
+      const StepOps<KS>& c = o[blk & 1];
+#pragma unroll
+      for (int u = 0; u < UB / 2; ++u) {
+        float B0[KS], C0[KS], B1[KS], C1[KS];
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          B0[k] = c.bc[u][k].x; C0[k] = c.bc[u][k].y; B1[k] = c.bc[u][k].z; C1[k] = c.bc[u][k].w;
+        }
+        const float y0 = step<KS, DISC, READOUT>(h, A2, iA, ez, c.dx[u].x, c.dx[u].y, B0, C0);
+        const float y1 = step<KS, DISC, READOUT>(h, A2, iA, ez, c.dx[u].z, c.dx[u].w, B1, C1);
+        if (READOUT) ps.part[tid / 64][sg][(blk * (UB / 2) + u) * CPW + ch % CPW] = make_float2(y0, y1);
+        else sum_dt += c.dx[u].x + c.dx[u].z;
+      }
+    }
+  } else {
+    for (int t = 0; t < nt; ++t) {
+      const float2 dx = s.dx[buf][ch][t];
+      float Bv[KS], Cv[KS];
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const float2 v = s.bc[buf][sg * KS + k][t];
+        Bv[k] = v.x;
+        Cv[k] = v.y;
+      }
+      const float yp = step<KS, DISC, READOUT>(h, A2, iA, ez, dx.x, dx.y, Bv, Cv);
+      if (READOUT) ((float*)&ps.part[tid / 64][sg][(t >> 1) * CPW + ch % CPW])[t & 1] = yp;
+      else sum_dt += dx.x;
+    }
+  }
+}
+
+// Finalize a tile: y = (sum of the 16 partials + D x) * silu(z).  Each wave
+// finalizes the 4 channels it scanned (its partials are wave-private, so no
+// workgroup barrier is needed): lane -> channel 4*wave + lane % 4, steps
+// 2*(lane / 4) and +1, i.e. lane = column tp*CPW + c of the partial rows.
+template <bool BF16, bool VEC, int KS>
+__device__ __forceinline__ void finalize_tile(const ScanParams& p, const ScanSmem<KS>& s, const PartSmem& ps, int buf,
+                                              int nt, int64_t b, int64_t d0, int64_t t0, bool want_z) {
+  const int tid = threadIdx.x;
+  const int c = fin_channel(tid), tp = fin_pair(tid);
+  const float2* pp = &ps.part[tid / 64][0][tp * CPW + c % CPW];
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    const float2 v = pp[q * PROW];  // (y_t, y_t+1) of state lane q
+    a0 += v.x;
+    a1 += v.y;
+  }
+  const int dleft = (int)(p.D - (d0 + c));
+  if (dleft <= 0) return;
+  const float acc[2] = {a0, a1};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 2 * tp + j;
+    if (row >= nt) break;
+    float v = __builtin_fmaf(s.Dk[c], s.dx[buf][c][row].y, acc[j]);
+    if (want_z) {
+      const float zf = j ? s.z[tp][c].y : s.z[tp][c].x;
+      v *= zf * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zf * kLog2e));
+    }
+    const int64_t off = b * p.ys_b + (t0 + row) * p.ys_t + d0 + c;
+    if (p.y_f32 || !BF16) ((float*)p.y)[off] = v;
+    else ((uint16_t*)p.y)[off] = f2bf(v);
+  }
+}
+
+// MODE 0: write y (and h_last / start from h_in).  MODE 1: segment aggregates.
 template <bool BF16, bool VEC, int KS, int MODE>
 __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, int64_t nseg_run,
                                                   int64_t nblocks_padded) {
   __shared__ ScanSmem<KS> s;
-  constexpr int NP = G * KS;
+  __shared__ PartSmem ps;
   const int tid = threadIdx.x;
-  const int ch = tid >> 3, sg = tid & 7;
+  const int ch = tid / G, sg = tid % G;
 
   const int64_t lb = logical_block(nblocks_padded);
   if (lb >= n_dblk * nseg_run * p.batch) return;
@@ -256,89 +481,61 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   if (tid < CH) s.Dk[tid] = (MODE == 0 && (p.flags & kHasD) && d0 + tid < p.D) ? p.Dskip[(d0 + tid) * p.Ds_d] : 0.f;
   __syncthreads();
   if (zero_A) s.any_zero_A = 1;
+
+  // Global loads run two tiles ahead of use: r0/r1 hold tiles k with k & 1 == 0/1.
+  TileRegs<BF16, KS> r0, r1;
+  const int64_t ntiles = (t_end - t_begin + TT - 1) / TT;
+  const LoadPlan lp = make_plan<KS>(p, b, d0, t_begin);
+  auto load = [&](int64_t k, TileRegs<BF16, KS>& r) {
+    if (want_z) load_tile<BF16, VEC, KS, true>(p, lp, k, t_begin + k * TT, t_end, r);
+    else load_tile<BF16, VEC, KS, false>(p, lp, k, t_begin + k * TT, t_end, r);
+  };
+  auto store = [&](int buf, const TileRegs<BF16, KS>& r) {
+    if (want_z) {
+      store_tile<BF16, KS>(s, buf, r);
+      store_z<BF16, KS>(s, r);
+    } else {
+      store_tile<BF16, KS>(s, buf, r);
+    }
+  };
+  load(0, r0);
+  store(0, r0);
+  if (ntiles > 1) load(1, r1);
+  if (ntiles > 2) load(2, r0);
   __syncthreads();
   const int disc = (p.flags & kEuler) ? 2 : (s.any_zero_A ? 1 : 0);
 
-  TileRegs<KS> r;
-  const int64_t ntiles = (t_end - t_begin + TT - 1) / TT;
-  if (want_z) load_tile<BF16, VEC, KS, true>(p, b, d0, t_begin, t_end, r);
-  else load_tile<BF16, VEC, KS, false>(p, b, d0, t_begin, t_end, r);
-  if (want_z) store_tile<KS, true>(s, 0, r);
-  else store_tile<KS, false>(s, 0, r);
-  __syncthreads();
-
   float sum_dt = 0.f;
-  for (int64_t it = 0; it < ntiles; ++it) {
+  // One tile: scan it, finalize it, stage tile it+1 (held in rn) and refill
+  // rn with tile it+3.
+  auto body = [&](int64_t it, TileRegs<BF16, KS>& rn) {
     const int buf = (int)(it & 1);
     const int64_t t0 = t_begin + it * TT;
     const int nt = (int)((t_end - t0) < TT ? (t_end - t0) : TT);
-    const bool more = it + 1 < ntiles;
-    if (more) {
-      if (want_z) load_tile<BF16, VEC, KS, true>(p, b, d0, t0 + TT, t_end, r);
-      else load_tile<BF16, VEC, KS, false>(p, b, d0, t0 + TT, t_end, r);
-    }
     if (MODE == 0) {
-      if (disc == 0) scan_tile<KS, 0, true>(s, buf, nt, h, A2, iA, ez, sum_dt);
-      else if (disc == 1) scan_tile<KS, 1, true>(s, buf, nt, h, A2, iA, ez, sum_dt);
-      else scan_tile<KS, 2, true>(s, buf, nt, h, A2, iA, ez, sum_dt);
-      __syncthreads();
-      // Finalize the tile: y = (ysum + D x) * silu(z), 4 channels per thread.
-      const int row = tid >> 3, c0 = (tid & 7) * 4;
-      const int64_t t = t0 + row;
-      if (row < nt) {
-        float yv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float v = __builtin_fmaf(s.Dk[c0 + j], s.x[buf][row][c0 + j], s.ysum[row][c0 + j]);
-          if (want_z) {
-            const float zf = s.z[buf][row][c0 + j];
-            v *= zf * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zf * kLog2e));
-          }
-          yv[j] = v;
-        }
-        const int dleft = (int)(p.D - (d0 + c0));
-        const int64_t off = b * p.ys_b + t * p.ys_t + d0 + c0;
-        if (p.y_f32) {
-          float* yp = (float*)p.y;
-          if (VEC && dleft >= 4) *(float4*)(yp + off) = make_float4(yv[0], yv[1], yv[2], yv[3]);
-          else
-            for (int j = 0; j < 4; ++j)
-              if (j < dleft) yp[off + j] = yv[j];
-        } else if (BF16) {
-          uint16_t* yp = (uint16_t*)p.y;
-          if (VEC && dleft >= 4) {
-            uint2 v;
-            v.x = (uint32_t)f2bf(yv[0]) | ((uint32_t)f2bf(yv[1]) << 16);
-            v.y = (uint32_t)f2bf(yv[2]) | ((uint32_t)f2bf(yv[3]) << 16);
-            *(uint2*)(yp + off) = v;
-          } else {
-            for (int j = 0; j < 4; ++j)
-              if (j < dleft) yp[off + j] = f2bf(yv[j]);
-          }
-        } else {
-          float* yp = (float*)p.y;
-          if (VEC && dleft >= 4) *(float4*)(yp + off) = make_float4(yv[0], yv[1], yv[2], yv[3]);
-          else
-            for (int j = 0; j < 4; ++j)
-              if (j < dleft) yp[off + j] = yv[j];
-        }
-      }
+      if (disc == 0) scan_tile<KS, 0, true>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
+      else if (disc == 1) scan_tile<KS, 1, true>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
+      else scan_tile<KS, 2, true>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
+      finalize_tile<BF16, VEC, KS>(p, s, ps, buf, nt, b, d0, t0, want_z);
     } else {
-      if (disc == 0) scan_tile<KS, 0, false>(s, buf, nt, h, A2, iA, ez, sum_dt);
-      else if (disc == 1) scan_tile<KS, 1, false>(s, buf, nt, h, A2, iA, ez, sum_dt);
-      else scan_tile<KS, 2, false>(s, buf, nt, h, A2, iA, ez, sum_dt);
+      if (disc == 0) scan_tile<KS, 0, false>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
+      else if (disc == 1) scan_tile<KS, 1, false>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
+      else scan_tile<KS, 2, false>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
     }
-    if (more) {
-      if (want_z) store_tile<KS, true>(s, buf ^ 1, r);
-      else store_tile<KS, false>(s, buf ^ 1, r);
+    if (it + 1 < ntiles) {
+      store(buf ^ 1, rn);
+      if (it + 3 < ntiles) load(it + 3, rn);
     }
     __syncthreads();
+  };
+  for (int64_t it = 0; it < ntiles; it += 2) {
+    body(it, r1);
+    if (it + 1 < ntiles) body(it + 1, r0);
   }
 
   if (!d_ok) return;
   if (MODE == 0) {
-    const bool last = seg == p.n_seg - 1;
-    if (last && (p.flags & kWantHLast)) {
+    if (seg == p.n_seg - 1 && (p.flags & kWantHLast)) {
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
         const int n = sg * KS + k;
@@ -393,21 +590,20 @@ template <bool BF16, bool VEC>
 hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
   if (p.N <= G * 1) return launch_ks<BF16, VEC, 1>(p, stream);
   if (p.N <= G * 2) return launch_ks<BF16, VEC, 2>(p, stream);
-  if (p.N <= G * 4) return launch_ks<BF16, VEC, 4>(p, stream);
-  return launch_ks<BF16, VEC, 8>(p, stream);
+  return launch_ks<BF16, VEC, 4>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_selective_scan(const ScanParams& p, hipStream_t stream) {
-  // Vector tile loads/stores need 4 consecutive channels to be 8-byte (bf16)
-  // or 16-byte (fp32) aligned for every (b, t).
+  // Paired tile loads/stores need two consecutive channels aligned to their
+  // combined size for every (b, t).
   const int64_t e = p.io_bf16 ? 2 : 4;
   const int64_t ye = p.y_f32 ? 4 : e;
   auto al = [](const void* q, int64_t bytes) { return q == nullptr || ((uintptr_t)q % (uintptr_t)bytes) == 0; };
-  bool vec = al(p.x, 4 * e) && al(p.delta, 4 * e) && al(p.y, 4 * ye) && p.xs_b % 4 == 0 && p.xs_t % 4 == 0 &&
-             p.ds_b % 4 == 0 && p.ds_t % 4 == 0 && p.ys_b % 4 == 0 && p.ys_t % 4 == 0;
-  if (p.flags & kHasZ) vec = vec && al(p.z, 4 * e) && p.zs_b % 4 == 0 && p.zs_t % 4 == 0;
+  bool vec = al(p.x, 2 * e) && al(p.delta, 2 * e) && al(p.y, 2 * ye) && p.xs_b % 2 == 0 && p.xs_t % 2 == 0 &&
+             p.ds_b % 2 == 0 && p.ds_t % 2 == 0 && p.ys_b % 2 == 0 && p.ys_t % 2 == 0;
+  if (p.flags & kHasZ) vec = vec && al(p.z, 2 * e) && p.zs_b % 2 == 0 && p.zs_t % 2 == 0;
   if (p.io_bf16) return vec ? launch_io<true, true>(p, stream) : launch_io<true, false>(p, stream);
   return vec ? launch_io<false, true>(p, stream) : launch_io<false, false>(p, stream);
 }

@@ -35,8 +35,8 @@ struct ScanParams {
 };
 
 // Tiling of the scan kernels (also used by the host planner).
-constexpr int kScanLanesPerChannel = 8;
-constexpr int kScanChannelsPerBlock = 32;
+constexpr int kScanLanesPerChannel = 16;
+constexpr int kScanChannelsPerBlock = 16;
 constexpr int kScanTileSteps = 32;
 constexpr int kScanThreads = kScanLanesPerChannel * kScanChannelsPerBlock;
 
