@@ -127,7 +127,9 @@ typedef struct {
  *   h_last   : (batch, nheads, headdim, dstate) F32 contiguous  if SSM_WANT_HLAST
  * Supported: headdim == 64, dstate == 64, chunk in {64, 128, 256},
  * nheads % ngroups == 0; seqlen need not be a multiple of chunk (the last
- * chunk is shorter).  SSM_HAS_Z is not accepted. */
+ * chunk is shorter).  SSM_HAS_Z is not accepted.  Every (batch, step, head or
+ * group) row of x, B, C and y, and h0 / h_last, must start 16-byte aligned
+ * (SSM_ERR_ALIGN otherwise). */
 typedef struct {
   int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
   uint32_t flags;

@@ -1,11 +1,421 @@
-// SSD chunked forward for gfx950 (placeholder until the kernels land).
+// Mamba-2 SSD (structured state-space duality) chunked forward for gfx950.
+//
+// What is computed ("Mamba-2: 상태 공간 기반 시퀀스 모델", obsidian-dorae222:
+// 1-세미분리 행렬, SSM-Attention 동치성, SSD 타일링 알고리즘): the selective
+// recurrence with one scalar A per head, h_t = exp(delta_t A) h_{t-1} +
+// beta_t x_t B_t^T (beta_t = (exp(delta_t A) - 1)/A, the zero-order hold of the
+// Mamba review on tildalice.io, section 이산화; delta_t with the simplified
+// discretisation), y_t = h_t C_t + D x_t, evaluated by chunks of Q steps:
+//
+//   s1 chunk_cumsum : A_cum = per-chunk inclusive cumsum of delta*A; beta.
+//   s2 chunk_state  : S_loc[c] = sum_j exp(A_cum_end - A_cum_j) beta_j x_j B_j^T
+//                     -- a (P x Q)(Q x N) product on bf16 matrix cores.
+//   s3 state_passing: S_in[c+1] = exp(A_cum_end[c]) S_in[c] + S_loc[c] (fp32).
+//   s4 chunk_scan   : Y = (L o C B^T)(beta x) + diag(exp(A_cum)) C S_in^T + D x,
+//                     L_ij = exp(A_cum_i - A_cum_j) for j <= i -- two products
+//                     per 32-step block on bf16 matrix cores.
+//
+// The pages' inter-chunk formula is read as the decay-weighted sum over the
+// chunk (the only reading under which the chunked result equals the
+// semiseparable form y = M x), and B in M is the discretised B (beta B).
+//
+// Matrix-core layout (v_mfma_f32_16x16x32_bf16, checked on the device): lane l
+// supplies A[l%16][8*(l/16) + i] and B[8*(l/16) + i][l%16], i = 0..7, and
+// receives D[4*(l/16) + r][l%16], r = 0..3.  The contraction index of both
+// products of s2 and of the second product of s4 is time, the slowest index of
+// x and B in memory, so those operands are staged transposed in LDS.  The
+// first product of s4 is formed as G^T = B_J C_I^T so that its output layout
+// (4 consecutive j per lane) feeds the second product directly, with the
+// contraction slots permuted the same way in both operands.
 #include <hip/hip_runtime.h>
 
 #include "ssm_internal.h"
 
 namespace ssm {
-hipError_t launch_ssd_chunk_cumsum(const SSDParams&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_ssd_chunk_state(const SSDParams&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_ssd_state_passing(const SSDParams&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_ssd_chunk_scan(const SSDParams&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ------------------------------------------------------------ s1 cumsum
+
+constexpr int kCumHeads = 16;  // heads per block; 16 threads per head
+
+template <int Q>
+__global__ __launch_bounds__(256) void chunk_cumsum_kernel(SSDParams p) {
+  constexpr int RUN = Q / 16;  // steps per thread
+  __shared__ float sa[kCumHeads][Q + 1];
+  __shared__ float sbeta[kCumHeads][Q + 1];
+  __shared__ float spart[kCumHeads][17];
+  const int64_t nhb = (p.H + kCumHeads - 1) / kCumHeads;
+  int64_t bid = blockIdx.x;
+  const int64_t hb = bid % nhb;
+  bid /= nhb;
+  const int64_t c = bid % p.nchunks, b = bid / p.nchunks;
+  const int tid = threadIdx.x;
+  // a = delta*A and beta for every (head, step) of the chunk; steps past L
+  // get a = 0 (A_cum stays flat) and beta = 0 (no input).
+  for (int e = tid; e < Q * kCumHeads; e += 256) {
+    const int t = e / kCumHeads, hh = e % kCumHeads;
+    const int64_t h = hb * kCumHeads + hh, tg = c * Q + t;
+    float a = 0.f, bt = 0.f;
+    if (h < p.H && tg < p.L) {
+      const float dt = bf2f(((const uint16_t*)p.delta)[b * p.ds_b + tg * p.ds_t + h * p.ds_h]);
+      const float A = p.A[h * p.As_h];
+      a = dt * A;
+      bt = p.euler ? dt : (A != 0.f ? expm1f(a) / A : dt);
+    }
+    sa[hh][t] = a;
+    sbeta[hh][t] = bt;
+  }
+  __syncthreads();
+  const int hh = tid / 16, j = tid % 16;
+  float loc[RUN];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < RUN; ++k) {
+    s += sa[hh][j * RUN + k];
+    loc[k] = s;
+  }
+  spart[hh][j] = s;
+  __syncthreads();
+  float off = 0.f;
+  for (int k = 0; k < j; ++k) off += spart[hh][k];
+  const int64_t h = hb * kCumHeads + hh;
+  if (h < p.H) {
+    float* dst = p.A_cum + (b * p.H + h) * p.Lp + c * Q + j * RUN;
+    float* dbt = p.beta + (b * p.H + h) * p.Lp + c * Q + j * RUN;
+#pragma unroll
+    for (int k = 0; k < RUN; ++k) {
+      dst[k] = loc[k] + off;
+      dbt[k] = sbeta[hh][j * RUN + k];
+    }
+  }
+}
+
+// Stage rows [0, nj) of a time-major (Q x 64) bf16 tile into LDS transposed,
+// dst[col][j] (row pitch `pitch` elements), optionally scaled by scale[j]
+// (fp32), rounding to bf16.  Row j is at src + (t0 + j) * row_stride; rows at
+// or past L are zero.  Two rows x 8 columns per task: two 16-byte loads, eight
+// 4-byte LDS stores of (row j, row j+1) pairs.
+__device__ __forceinline__ void stage_transposed(uint16_t* dst, int pitch, const uint16_t* src, int64_t row_stride,
+                                                 int64_t t0, int64_t L, int nj, const float* scale) {
+  for (int task = threadIdx.x; task < (nj / 2) * 8; task += blockDim.x) {
+    const int j = 2 * (task / 8), cb = (task % 8) * 8;
+    uint4 r0 = make_uint4(0, 0, 0, 0), r1 = make_uint4(0, 0, 0, 0);
+    if (t0 + j < L) r0 = *(const uint4*)(src + (t0 + j) * row_stride + cb);
+    if (t0 + j + 1 < L) r1 = *(const uint4*)(src + (t0 + j + 1) * row_stride + cb);
+    const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w}, w1[4] = {r1.x, r1.y, r1.z, r1.w};
+    if (scale) {
+      const float s0 = scale[j], s1 = scale[j + 1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v0 = __uint_as_float((i & 1) ? (w0[i / 2] & 0xFFFF0000u) : (w0[i / 2] << 16)) * s0;
+        const float v1 = __uint_as_float((i & 1) ? (w1[i / 2] & 0xFFFF0000u) : (w1[i / 2] << 16)) * s1;
+        *(uint32_t*)(dst + (cb + i) * pitch + j) = pack2(v0, v1);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t a = (i & 1) ? (w0[i / 2] >> 16) : (w0[i / 2] & 0xFFFFu);
+        const uint32_t c = (i & 1) ? (w1[i / 2] >> 16) : (w1[i / 2] & 0xFFFFu);
+        *(uint32_t*)(dst + (cb + i) * pitch + j) = a | (c << 16);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------- s2 chunk state
+
+template <int Q>
+__global__ __launch_bounds__(256) void chunk_state_kernel(SSDParams p) {
+  constexpr int PITCH = Q + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t xT[64][PITCH];  // (x * w)^T: [p][j]
+  __shared__ __attribute__((aligned(16))) uint16_t bT[64][PITCH];  // B^T: [n][j]
+  __shared__ float w[Q];
+  int64_t bid = blockIdx.x;
+  const int64_t h = bid % p.H;
+  bid /= p.H;
+  const int64_t c = bid % p.nchunks, b = bid / p.nchunks;
+  const int64_t g = h / (p.H / p.G);
+  const int tid = threadIdx.x;
+  const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + c * Q;
+  const float* be = p.beta + (b * p.H + h) * p.Lp + c * Q;
+  const float a_end = Ac[Q - 1];
+  for (int t = tid; t < Q; t += 256) w[t] = __builtin_amdgcn_exp2f((a_end - Ac[t]) * kLog2e) * be[t];
+  __syncthreads();
+  stage_transposed(&xT[0][0], PITCH, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, c * Q, p.L, Q, w);
+  stage_transposed(&bT[0][0], PITCH, (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g, p.Bs_t, c * Q, p.L, Q,
+                   nullptr);
+  __syncthreads();
+  const int wv = tid / 64, l = tid % 64, lr = l % 16, lq = l / 16;
+  f32x4 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < Q / 32; ++ks) {
+    const bf16x8 a = as_bf16x8(*(const uint4*)&xT[16 * wv + lr][32 * ks + 8 * lq]);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const bf16x8 bb = as_bf16x8(*(const uint4*)&bT[16 * nt + lr][32 * ks + 8 * lq]);
+      acc[nt] = mfma(a, bb, acc[nt]);
+    }
+  }
+  float* dst = p.states + (((b * p.nchunks + c) * p.H + h) * 64) * 64;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(16 * wv + 4 * lq + r) * 64 + 16 * nt + lr] = acc[nt][r];
+}
+
+// ---------------------------------------------------- s3 state passing
+
+__global__ __launch_bounds__(256) void state_passing_kernel(SSDParams p) {
+  // block = (b, h, quarter of the P*N = 4096 entries); 4 entries per thread
+  int64_t bid = blockIdx.x;
+  const int q = (int)(bid % 4);
+  bid /= 4;
+  const int64_t h = bid % p.H, b = bid / p.H;
+  const int e0 = q * 1024 + threadIdx.x * 4;
+  float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (p.h0) S = *(const float4*)(p.h0 + (b * p.H + h) * 4096 + e0);
+  const float* Ac = p.A_cum + (b * p.H + h) * p.Lp;
+  const int64_t cstride = p.H * 4096;
+  const float* st = p.states + (b * p.nchunks * p.H + h) * 4096 + e0;
+  uint16_t* sin = (uint16_t*)p.S_in + (b * p.nchunks * p.H + h) * 4096 + e0;
+  float4 nxt = *(const float4*)st;
+  for (int64_t c = 0; c < p.nchunks; ++c) {
+    const float4 cur = nxt;
+    if (c + 1 < p.nchunks) nxt = *(const float4*)(st + (c + 1) * cstride);
+    *(uint2*)(sin + c * cstride) = make_uint2(pack2(S.x, S.y), pack2(S.z, S.w));
+    const float dec = __builtin_amdgcn_exp2f(Ac[c * p.Q + p.Q - 1] * kLog2e);
+    S.x = __builtin_fmaf(dec, S.x, cur.x);
+    S.y = __builtin_fmaf(dec, S.y, cur.y);
+    S.z = __builtin_fmaf(dec, S.z, cur.z);
+    S.w = __builtin_fmaf(dec, S.w, cur.w);
+  }
+  if (p.h_last) *(float4*)(p.h_last + (b * p.H + h) * 4096 + e0) = S;
+}
+
+// ------------------------------------------------------- s4 chunk scan
+
+// Block = (b, chunk c, head h, row tile it) with RW rows; wave wv owns SPW
+// strips of 16 rows: i0 = RW*it + 16*(SPW*wv + s).  Accumulators hold
+// Y^T[p][i]: lane -> p = 16*mt + 4*(l/16) + r, i = i0 + l%16.
+template <int Q, int RW>
+__global__ __launch_bounds__(256) void chunk_scan_kernel(SSDParams p) {
+  constexpr int SPW = RW / 64;
+  constexpr int PX = Q + 8;   // xT pitch
+  constexpr int PB = 64 + 8;  // Bs pitch
+  constexpr int NIT = Q / RW;
+  __shared__ __attribute__((aligned(16))) uint16_t xT[64][PX];  // (beta x)^T: [p][j]
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][PB];   // B rows: [j][n]
+  __shared__ float A2[Q];                                      // A_cum * log2(e)
+  __shared__ float tj[Q];                                      // exp(A_cum[j|31] - A_cum[j])
+  __shared__ float bj[Q];                                      // beta
+
+  int64_t bid = blockIdx.x;
+  const int it = (int)(bid % NIT);
+  bid /= NIT;
+  const int64_t h = bid % p.H;
+  bid /= p.H;
+  const int64_t c = bid % p.nchunks, b = bid / p.nchunks;
+  const int64_t g = h / (p.H / p.G);
+  const int tid = threadIdx.x;
+  const int nj = RW * (it + 1);  // steps j < nj feed these rows
+  const int64_t t0 = c * Q;
+
+  const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
+  const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
+  for (int t = tid; t < nj; t += 256) {
+    A2[t] = Ac[t] * kLog2e;
+    bj[t] = be[t];
+  }
+  __syncthreads();
+  for (int t = tid; t < nj; t += 256) tj[t] = __builtin_amdgcn_exp2f(A2[t | 31] - A2[t]);
+  stage_transposed(&xT[0][0], PX, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L, nj, bj);
+  {
+    const uint16_t* src = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
+    for (int task = tid; task < nj * 8; task += 256) {
+      const int j = task / 8, cb = (task % 8) * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (t0 + j < p.L) v = *(const uint4*)(src + (t0 + j) * p.Bs_t + cb);
+      *(uint4*)&Bs[j][cb] = v;
+    }
+  }
+  __syncthreads();
+
+  const int wv = tid / 64, l = tid % 64, lr = l % 16, lq = l / 16;
+  const int i00 = RW * it + 16 * SPW * wv;  // first row of the wave's strips
+  // C operand of each strip: C[i][32*ks + 8*lq .. +7]
+  bf16x8 Cop[SPW][2];
+  const uint16_t* Cb = (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g;
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int64_t ti = t0 + i00 + 16 * s + lr;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (ti < p.L) v = *(const uint4*)(Cb + ti * p.Cs_t + 32 * ks + 8 * lq);
+      Cop[s][ks] = as_bf16x8(v);
+    }
+  }
+  f32x4 acc[SPW][4];
+  // inter-chunk term: Y^T[p][i] = exp(A_cum_i) sum_n S_in[p][n] C[i][n]
+  {
+    const uint16_t* Sp = (const uint16_t*)p.S_in + ((b * p.nchunks + c) * p.H + h) * 4096;
+    bf16x8 aS[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) aS[mt][ks] = as_bf16x8(*(const uint4*)(Sp + (16 * mt + lr) * 64 + 32 * ks + 8 * lq));
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      const float ei = __builtin_amdgcn_exp2f(A2[i00 + 16 * s + lr]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+        a = mfma(aS[mt][0], Cop[s][0], a);
+        a = mfma(aS[mt][1], Cop[s][1], a);
+        acc[s][mt] = a * ei;
+      }
+    }
+  }
+  // intra-chunk term over 32-step blocks jb <= the wave's diagonal block
+  const int jb_diag = i00 / 32;
+  for (int jb = 0; jb <= jb_diag; ++jb) {
+    const int j0 = 32 * jb;
+    // A operands of G^T = B_J C_I^T: B rows j0 + 16*jt + lr
+    bf16x8 aB[2][2];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) aB[jt][ks] = as_bf16x8(*(const uint4*)&Bs[j0 + 16 * jt + lr][32 * ks + 8 * lq]);
+    // A operands of Y^T += X~^T G^T: rows p, contraction slots in G^T's layout
+    bf16x8 aX[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint2 lo = *(const uint2*)&xT[16 * mt + lr][j0 + 4 * lq];
+      const uint2 hi = *(const uint2*)&xT[16 * mt + lr][j0 + 16 + 4 * lq];
+      aX[mt] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    }
+    float tjv[8];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tjv[4 * jt + r] = tj[j0 + 16 * jt + 4 * lq + r];
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      const int i = i00 + 16 * s + lr;
+      f32x4 gt[2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+        a = mfma(aB[jt][0], Cop[s][0], a);
+        a = mfma(aB[jt][1], Cop[s][1], a);
+        gt[jt] = a;  // G^T[j0 + 16*jt + 4*lq + r][i]
+      }
+      float v[8];
+      if (jb < jb_diag) {
+        // every j of the block precedes every row of the strip:
+        // exp(A_i - A_j) = exp(A_i - A_m) exp(A_m - A_j), m = j0 + 31, both <= 1
+        const float vi = __builtin_amdgcn_exp2f(A2[i] - A2[j0 + 31]);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[4 * jt + r] = gt[jt][r] * (tjv[4 * jt + r] * vi);
+      } else {
+        const float ai = A2[i];
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = j0 + 16 * jt + 4 * lq + r;
+            const float d = j <= i ? ai - A2[j] : 0.f;
+            const float e = __builtin_amdgcn_exp2f(d);
+            v[4 * jt + r] = j <= i ? gt[jt][r] * e : 0.f;
+          }
+      }
+      const bf16x8 bop = as_bf16x8(make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]),
+                                              pack2(v[6], v[7])));
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[s][mt] = mfma(aX[mt], bop, acc[s][mt]);
+    }
+  }
+  // epilogue: + D x, store y[i][p0..p0+3]
+  const float Dh = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int64_t ti = t0 + i00 + 16 * s + lr;
+    if (ti >= p.L) continue;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int p0 = 16 * mt + 4 * lq;
+      float o[4] = {acc[s][mt][0], acc[s][mt][1], acc[s][mt][2], acc[s][mt][3]};
+      if (p.Dskip) {
+        const uint2 xv = *(const uint2*)((const uint16_t*)p.x + b * p.xs_b + ti * p.xs_t + h * p.xs_h + p0);
+        o[0] = __builtin_fmaf(Dh, __uint_as_float(xv.x << 16), o[0]);
+        o[1] = __builtin_fmaf(Dh, __uint_as_float(xv.x & 0xFFFF0000u), o[1]);
+        o[2] = __builtin_fmaf(Dh, __uint_as_float(xv.y << 16), o[2]);
+        o[3] = __builtin_fmaf(Dh, __uint_as_float(xv.y & 0xFFFF0000u), o[3]);
+      }
+      const int64_t off = b * p.ys_b + ti * p.ys_t + h * p.ys_h + p0;
+      if (p.y_f32) *(float4*)((float*)p.y + off) = make_float4(o[0], o[1], o[2], o[3]);
+      else *(uint2*)((uint16_t*)p.y + off) = make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ssd_chunk_cumsum(const SSDParams& p, hipStream_t stream) {
+  const unsigned nb = (unsigned)(p.batch * p.nchunks * ((p.H + kCumHeads - 1) / kCumHeads));
+  if (p.Q == 64) hipLaunchKernelGGL(chunk_cumsum_kernel<64>, dim3(nb), dim3(256), 0, stream, p);
+  else if (p.Q == 128) hipLaunchKernelGGL(chunk_cumsum_kernel<128>, dim3(nb), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(chunk_cumsum_kernel<256>, dim3(nb), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_ssd_chunk_state(const SSDParams& p, hipStream_t stream) {
+  const unsigned nb = (unsigned)(p.batch * p.nchunks * p.H);
+  if (p.Q == 64) hipLaunchKernelGGL(chunk_state_kernel<64>, dim3(nb), dim3(256), 0, stream, p);
+  else if (p.Q == 128) hipLaunchKernelGGL(chunk_state_kernel<128>, dim3(nb), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(chunk_state_kernel<256>, dim3(nb), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_ssd_state_passing(const SSDParams& p, hipStream_t stream) {
+  const unsigned nb = (unsigned)(p.batch * p.H * 4);
+  hipLaunchKernelGGL(state_passing_kernel, dim3(nb), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_ssd_chunk_scan(const SSDParams& p, hipStream_t stream) {
+  if (p.Q == 64) {
+    hipLaunchKernelGGL((chunk_scan_kernel<64, 64>), dim3((unsigned)(p.batch * p.nchunks * p.H)), dim3(256), 0,
+                       stream, p);
+  } else if (p.Q == 128) {
+    hipLaunchKernelGGL((chunk_scan_kernel<128, 128>), dim3((unsigned)(p.batch * p.nchunks * p.H)), dim3(256), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((chunk_scan_kernel<256, 128>), dim3((unsigned)(p.batch * p.nchunks * p.H * 2)), dim3(256),
+                       0, stream, p);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace ssm

@@ -227,6 +227,17 @@ ssm_status validate_ssd_desc(const ssm_ssd_desc* d) {
 // Which pointers a step reads or writes.
 enum : unsigned { kNeedX = 1, kNeedDelta = 2, kNeedB = 4, kNeedC = 8, kNeedY = 16, kNeedAll = 31 };
 
+// The SSD kernels move whole 16-byte groups of a row (8 bf16 / 4 fp32): each
+// (batch, step, head or group) row must start 16-byte aligned.
+bool rows_aligned16(const ssm_tensor_desc& t, const void* ptr, int outer_dims) {
+  if (!ptr) return true;
+  const int64_t e = esize(t.dtype);
+  if ((uintptr_t)ptr % 16) return false;
+  for (int i = 0; i < outer_dims; ++i)
+    if (t.shape[i] > 1 && (t.stride[i] * e) % 16) return false;
+  return true;
+}
+
 ssm_status validate_ssd_ptrs(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, unsigned need) {
   if (!p) return SSM_ERR_NULL;
   const uint32_t f = d->flags;
@@ -240,6 +251,12 @@ ssm_status validate_ssd_ptrs(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, unsig
   if ((p->x && !aligned(p->x, 2)) || (p->delta && !aligned(p->delta, 2)) || (p->B && !aligned(p->B, 2)) ||
       (p->C && !aligned(p->C, 2)) || !aligned(p->A, 4) || (p->y && !aligned(p->y, esize(d->y.dtype))) ||
       (p->D && !aligned(p->D, 4)) || (p->h0 && !aligned(p->h0, 4)) || (p->h_last && !aligned(p->h_last, 4)))
+    return SSM_ERR_ALIGN;
+  if (!rows_aligned16(d->x, (need & kNeedX) ? p->x : nullptr, 3) ||
+      !rows_aligned16(d->B, (need & kNeedB) ? p->B : nullptr, 3) ||
+      !rows_aligned16(d->C, (need & kNeedC) ? p->C : nullptr, 3) ||
+      !rows_aligned16(d->y, (need & kNeedY) ? p->y : nullptr, 3) || (p->h0 && !aligned(p->h0, 16)) ||
+      (p->h_last && !aligned(p->h_last, 16)))
     return SSM_ERR_ALIGN;
   const Span ins[] = {span_of(d->x, p->x),
                       span_of(d->delta, p->delta),
