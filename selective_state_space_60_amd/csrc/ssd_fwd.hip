@@ -57,7 +57,8 @@ constexpr int kCumHeads = 16;  // heads per block; 16 threads per head
 
 template <int Q>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(SSDParams p) {
-  constexpr int RUN = Q / 16;  // steps per thread
+  constexpr int RUN = Q / 16;                  // steps per thread in the scan phase
+  constexpr int NLD = Q * kCumHeads / 256;     // delta loads per thread
   __shared__ float sa[kCumHeads][Q + 1];
   __shared__ float sbeta[kCumHeads][Q + 1];
   __shared__ float spart[kCumHeads][17];
@@ -68,13 +69,25 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(SSDParams p) {
   const int64_t c = bid % p.nchunks, b = bid / p.nchunks;
   const int tid = threadIdx.x;
   // a = delta*A and beta for every (head, step) of the chunk; steps past L
-  // get a = 0 (A_cum stays flat) and beta = 0 (no input).
-  for (int e = tid; e < Q * kCumHeads; e += 256) {
+  // get a = 0 (A_cum stays flat) and beta = 0 (no input).  All loads are
+  // issued before any is used (out-of-range ones read a valid element).
+  uint16_t raw[NLD];
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int e = tid + 256 * u;
+    const int t = e / kCumHeads, hh = e % kCumHeads;
+    const int64_t h = hb * kCumHeads + hh, tg = c * Q + t;
+    const bool ok = h < p.H && tg < p.L;
+    raw[u] = ((const uint16_t*)p.delta)[ok ? b * p.ds_b + tg * p.ds_t + h * p.ds_h : 0];
+  }
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int e = tid + 256 * u;
     const int t = e / kCumHeads, hh = e % kCumHeads;
     const int64_t h = hb * kCumHeads + hh, tg = c * Q + t;
     float a = 0.f, bt = 0.f;
     if (h < p.H && tg < p.L) {
-      const float dt = bf2f(((const uint16_t*)p.delta)[b * p.ds_b + tg * p.ds_t + h * p.ds_h]);
+      const float dt = bf2f(raw[u]);
       const float A = p.A[h * p.As_h];
       a = dt * A;
       bt = p.euler ? dt : (A != 0.f ? expm1f(a) / A : dt);
@@ -107,32 +120,72 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(SSDParams p) {
   }
 }
 
-// Stage rows [0, nj) of a time-major (Q x 64) bf16 tile into LDS transposed,
-// dst[col][j] (row pitch `pitch` elements), optionally scaled by scale[j]
-// (fp32), rounding to bf16.  Row j is at src + (t0 + j) * row_stride; rows at
-// or past L are zero.  Two rows x 8 columns per task: two 16-byte loads, eight
-// 4-byte LDS stores of (row j, row j+1) pairs.
-__device__ __forceinline__ void stage_transposed(uint16_t* dst, int pitch, const uint16_t* src, int64_t row_stride,
-                                                 int64_t t0, int64_t L, int nj, const float* scale) {
-  for (int task = threadIdx.x; task < (nj / 2) * 8; task += blockDim.x) {
-    const int j = 2 * (task / 8), cb = (task % 8) * 8;
-    uint4 r0 = make_uint4(0, 0, 0, 0), r1 = make_uint4(0, 0, 0, 0);
-    if (t0 + j < L) r0 = *(const uint4*)(src + (t0 + j) * row_stride + cb);
-    if (t0 + j + 1 < L) r1 = *(const uint4*)(src + (t0 + j + 1) * row_stride + cb);
-    const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w}, w1[4] = {r1.x, r1.y, r1.z, r1.w};
+// Global loads of a time-major (ROWS x 64) bf16 tile for staging it
+// transposed in LDS, all issued before any is used.  A task is (row pair jp,
+// 8-column block cb).  Two task maps: ROWMAJ (t -> jp = t / 8, cb = 8*(t % 8))
+// gives coalesced global loads (8 lanes read one 128-byte row); COLMAJ
+// (t -> jp = t % (ROWS/2), cb = 8*(t / (ROWS/2))) makes the transposed LDS
+// stores of a wave land on consecutive dwords.  NTH threads, NT = 4*ROWS/NTH
+// tasks each.  Rows at or past L read row L-1 (a valid address) and are
+// zeroed when written to LDS.
+template <int ROWS, int NTH>
+struct PairLoads {
+  static constexpr int NT = 4 * ROWS / NTH;
+  uint4 r0[NT], r1[NT];
+};
+
+template <int ROWS, bool COLMAJ>
+__device__ __forceinline__ void pair_task(int task, int& j, int& cb) {
+  if (COLMAJ) {
+    j = 2 * (task % (ROWS / 2));
+    cb = 8 * (task / (ROWS / 2));
+  } else {
+    j = 2 * (task / 8);
+    cb = 8 * (task % 8);
+  }
+}
+
+template <int ROWS, int NTH, bool COLMAJ>
+__device__ __forceinline__ void load_pairs(PairLoads<ROWS, NTH>& ld, const uint16_t* src, int64_t row_stride,
+                                           int64_t t0, int64_t L) {
+#pragma unroll
+  for (int u = 0; u < PairLoads<ROWS, NTH>::NT; ++u) {
+    const int task = threadIdx.x + NTH * u;
+    int j, cb;
+    pair_task<ROWS, COLMAJ>(task, j, cb);
+    const int64_t ta = t0 + j < L ? t0 + j : L - 1, tb = t0 + j + 1 < L ? t0 + j + 1 : L - 1;
+    ld.r0[u] = *(const uint4*)(src + ta * row_stride + cb);
+    ld.r1[u] = *(const uint4*)(src + tb * row_stride + cb);
+  }
+}
+
+// Write the loaded pairs to LDS transposed, dst[col][j] (row pitch `pitch`),
+// optionally scaled by scale[j] (fp32) and rounded to bf16.
+template <int ROWS, int NTH, bool COLMAJ>
+__device__ __forceinline__ void store_pairs_transposed(const PairLoads<ROWS, NTH>& ld, uint16_t* dst, int pitch,
+                                                       int64_t t0, int64_t L, const float* scale) {
+#pragma unroll
+  for (int u = 0; u < PairLoads<ROWS, NTH>::NT; ++u) {
+    const int task = threadIdx.x + NTH * u;
+    int j, cb;
+    pair_task<ROWS, COLMAJ>(task, j, cb);
+    const bool ok0 = t0 + j < L, ok1 = t0 + j + 1 < L;
+    const uint32_t w0[4] = {ld.r0[u].x, ld.r0[u].y, ld.r0[u].z, ld.r0[u].w};
+    const uint32_t w1[4] = {ld.r1[u].x, ld.r1[u].y, ld.r1[u].z, ld.r1[u].w};
     if (scale) {
       const float s0 = scale[j], s1 = scale[j + 1];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float v0 = __uint_as_float((i & 1) ? (w0[i / 2] & 0xFFFF0000u) : (w0[i / 2] << 16)) * s0;
-        const float v1 = __uint_as_float((i & 1) ? (w1[i / 2] & 0xFFFF0000u) : (w1[i / 2] << 16)) * s1;
+        // padding rows are zeroed as data, not through the scale (0 * inf)
+        const float v0 = ok0 ? __uint_as_float((i & 1) ? (w0[i / 2] & 0xFFFF0000u) : (w0[i / 2] << 16)) * s0 : 0.f;
+        const float v1 = ok1 ? __uint_as_float((i & 1) ? (w1[i / 2] & 0xFFFF0000u) : (w1[i / 2] << 16)) * s1 : 0.f;
         *(uint32_t*)(dst + (cb + i) * pitch + j) = pack2(v0, v1);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t a = (i & 1) ? (w0[i / 2] >> 16) : (w0[i / 2] & 0xFFFFu);
-        const uint32_t c = (i & 1) ? (w1[i / 2] >> 16) : (w1[i / 2] & 0xFFFFu);
+        const uint32_t a = ok0 ? ((i & 1) ? (w0[i / 2] >> 16) : (w0[i / 2] & 0xFFFFu)) : 0u;
+        const uint32_t c = ok1 ? ((i & 1) ? (w1[i / 2] >> 16) : (w1[i / 2] & 0xFFFFu)) : 0u;
         *(uint32_t*)(dst + (cb + i) * pitch + j) = a | (c << 16);
       }
     }
@@ -140,6 +193,9 @@ __device__ __forceinline__ void stage_transposed(uint16_t* dst, int pitch, const
 }
 
 // ------------------------------------------------------- s2 chunk state
+
+constexpr bool kStateColMaj = false;  // staging task map of chunk_state
+constexpr bool kScanColMaj = false;   // staging task map of chunk_scan
 
 template <int Q>
 __global__ __launch_bounds__(256) void chunk_state_kernel(SSDParams p) {
@@ -153,14 +209,17 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(SSDParams p) {
   const int64_t c = bid % p.nchunks, b = bid / p.nchunks;
   const int64_t g = h / (p.H / p.G);
   const int tid = threadIdx.x;
-  const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + c * Q;
-  const float* be = p.beta + (b * p.H + h) * p.Lp + c * Q;
+  const int64_t t0 = c * Q;
+  PairLoads<Q, 256> lx, lb;
+  load_pairs<Q, 256, kStateColMaj>(lx, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
+  load_pairs<Q, 256, kStateColMaj>(lb, (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g, p.Bs_t, t0, p.L);
+  const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
+  const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
   const float a_end = Ac[Q - 1];
   for (int t = tid; t < Q; t += 256) w[t] = __builtin_amdgcn_exp2f((a_end - Ac[t]) * kLog2e) * be[t];
   __syncthreads();
-  stage_transposed(&xT[0][0], PITCH, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, c * Q, p.L, Q, w);
-  stage_transposed(&bT[0][0], PITCH, (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g, p.Bs_t, c * Q, p.L, Q,
-                   nullptr);
+  store_pairs_transposed<Q, 256, kStateColMaj>(lx, &xT[0][0], PITCH, t0, p.L, w);
+  store_pairs_transposed<Q, 256, kStateColMaj>(lb, &bT[0][0], PITCH, t0, p.L, nullptr);
   __syncthreads();
   const int wv = tid / 64, l = tid % 64, lr = l % 16, lq = l / 16;
   f32x4 acc[4];
@@ -213,15 +272,17 @@ __global__ __launch_bounds__(256) void state_passing_kernel(SSDParams p) {
 
 // ------------------------------------------------------- s4 chunk scan
 
-// Block = (b, chunk c, head h, row tile it) with RW rows; wave wv owns SPW
-// strips of 16 rows: i0 = RW*it + 16*(SPW*wv + s).  Accumulators hold
-// Y^T[p][i]: lane -> p = 16*mt + 4*(l/16) + r, i = i0 + l%16.
-template <int Q, int RW>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(SSDParams p) {
-  constexpr int SPW = RW / 64;
-  constexpr int PX = Q + 8;   // xT pitch
-  constexpr int PB = 64 + 8;  // Bs pitch
-  constexpr int NIT = Q / RW;
+// Block = (b, chunk c, head h) with Q/32 waves; wave wv owns the two 16-row
+// strips k = wv and k = Q/16 - 1 - wv, which balances the causal work.
+// Accumulators hold Y^T[p][i]: lane -> p = 16*mt + 4*(l/16) + r,
+// i = 16*k + l%16.
+template <int Q>
+__global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
+  constexpr int NTH = 2 * Q;     // threads
+  constexpr int NSTRIP = Q / 16;
+  constexpr int PX = Q + 8;      // xT pitch
+  constexpr int PB = 64 + 8;     // Bs pitch
+  constexpr int NTB = Q * 8 / NTH;  // B (row, 8 columns) tasks per thread
   __shared__ __attribute__((aligned(16))) uint16_t xT[64][PX];  // (beta x)^T: [p][j]
   __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][PB];   // B rows: [j][n]
   __shared__ float A2[Q];                                      // A_cum * log2(e)
@@ -229,75 +290,66 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(SSDParams p) {
   __shared__ float bj[Q];                                      // beta
 
   int64_t bid = blockIdx.x;
-  const int it = (int)(bid % NIT);
-  bid /= NIT;
   const int64_t h = bid % p.H;
   bid /= p.H;
   const int64_t c = bid % p.nchunks, b = bid / p.nchunks;
   const int64_t g = h / (p.H / p.G);
   const int tid = threadIdx.x;
-  const int nj = RW * (it + 1);  // steps j < nj feed these rows
   const int64_t t0 = c * Q;
+  // wave index as a scalar, so branches on it are uniform
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64), l = tid % 64, lr = l % 16, lq = l / 16;
+  const int kst[2] = {wv, NSTRIP - 1 - wv};
 
+  // --- issue the staging loads and the C operands before using any
+  PairLoads<Q, NTH> lx;
+  load_pairs<Q, NTH, kScanColMaj>(lx, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
+  uint4 rb[NTB];
+  const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
+#pragma unroll
+  for (int u = 0; u < NTB; ++u) {
+    const int task = tid + NTH * u;
+    const int j = task / 8, cb = (task % 8) * 8;
+    const int64_t tr = t0 + j < p.L ? t0 + j : p.L - 1;
+    rb[u] = *(const uint4*)(Bsrc + tr * p.Bs_t + cb);
+  }
+  bf16x8 Cop[2][2];  // C operand of each strip: C[i][32*ks + 8*lq .. +7]
+  const uint16_t* Cb = (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int64_t ti = t0 + 16 * kst[s] + lr;
+    const int64_t tr = ti < p.L ? ti : p.L - 1;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) Cop[s][ks] = as_bf16x8(*(const uint4*)(Cb + tr * p.Cs_t + 32 * ks + 8 * lq));
+  }
   const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
   const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
-  for (int t = tid; t < nj; t += 256) {
+  for (int t = tid; t < Q; t += NTH) {
     A2[t] = Ac[t] * kLog2e;
     bj[t] = be[t];
   }
   __syncthreads();
-  for (int t = tid; t < nj; t += 256) tj[t] = __builtin_amdgcn_exp2f(A2[t | 31] - A2[t]);
-  stage_transposed(&xT[0][0], PX, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L, nj, bj);
-  {
-    const uint16_t* src = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
-    for (int task = tid; task < nj * 8; task += 256) {
-      const int j = task / 8, cb = (task % 8) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t0 + j < p.L) v = *(const uint4*)(src + (t0 + j) * p.Bs_t + cb);
-      *(uint4*)&Bs[j][cb] = v;
-    }
+  for (int t = tid; t < Q; t += NTH) tj[t] = __builtin_amdgcn_exp2f(A2[t | 31] - A2[t]);
+  store_pairs_transposed<Q, NTH, kScanColMaj>(lx, &xT[0][0], PX, t0, p.L, bj);
+#pragma unroll
+  for (int u = 0; u < NTB; ++u) {
+    const int task = tid + NTH * u;
+    const int j = task / 8, cb = (task % 8) * 8;
+    *(uint4*)&Bs[j][cb] = t0 + j < p.L ? rb[u] : make_uint4(0, 0, 0, 0);
   }
+  // C rows past L must not contribute
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    if (t0 + 16 * kst[s] + lr >= p.L) Cop[s][0] = Cop[s][1] = as_bf16x8(make_uint4(0, 0, 0, 0));
   __syncthreads();
 
-  const int wv = tid / 64, l = tid % 64, lr = l % 16, lq = l / 16;
-  const int i00 = RW * it + 16 * SPW * wv;  // first row of the wave's strips
-  // C operand of each strip: C[i][32*ks + 8*lq .. +7]
-  bf16x8 Cop[SPW][2];
-  const uint16_t* Cb = (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g;
+  f32x4 acc[2][4];
 #pragma unroll
-  for (int s = 0; s < SPW; ++s) {
-    const int64_t ti = t0 + i00 + 16 * s + lr;
+  for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (ti < p.L) v = *(const uint4*)(Cb + ti * p.Cs_t + 32 * ks + 8 * lq);
-      Cop[s][ks] = as_bf16x8(v);
-    }
-  }
-  f32x4 acc[SPW][4];
-  // inter-chunk term: Y^T[p][i] = exp(A_cum_i) sum_n S_in[p][n] C[i][n]
-  {
-    const uint16_t* Sp = (const uint16_t*)p.S_in + ((b * p.nchunks + c) * p.H + h) * 4096;
-    bf16x8 aS[4][2];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) aS[mt][ks] = as_bf16x8(*(const uint4*)(Sp + (16 * mt + lr) * 64 + 32 * ks + 8 * lq));
-#pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      const float ei = __builtin_amdgcn_exp2f(A2[i00 + 16 * s + lr]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-        a = mfma(aS[mt][0], Cop[s][0], a);
-        a = mfma(aS[mt][1], Cop[s][1], a);
-        acc[s][mt] = a * ei;
-      }
-    }
-  }
-  // intra-chunk term over 32-step blocks jb <= the wave's diagonal block
-  const int jb_diag = i00 / 32;
-  for (int jb = 0; jb <= jb_diag; ++jb) {
+    for (int mt = 0; mt < 4; ++mt) acc[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // intra-chunk term over 32-step blocks jb up to the later strip's diagonal
+  const int jb_last = (16 * kst[1]) / 32;
+  for (int jb = 0; jb <= jb_last; ++jb) {
     const int j0 = 32 * jb;
     // A operands of G^T = B_J C_I^T: B rows j0 + 16*jt + lr
     bf16x8 aB[2][2];
@@ -313,14 +365,12 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(SSDParams p) {
       const uint2 hi = *(const uint2*)&xT[16 * mt + lr][j0 + 16 + 4 * lq];
       aX[mt] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
     }
-    float tjv[8];
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) tjv[4 * jt + r] = tj[j0 + 16 * jt + 4 * lq + r];
-#pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      const int i = i00 + 16 * s + lr;
+    for (int s = 0; s < 2; ++s) {
+      const int i0 = 16 * kst[s];
+      const int diag = i0 / 32;
+      if (jb > diag) continue;  // wave-uniform
+      const int i = i0 + lr;
       f32x4 gt[2];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
@@ -330,25 +380,32 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(SSDParams p) {
         gt[jt] = a;  // G^T[j0 + 16*jt + 4*lq + r][i]
       }
       float v[8];
-      if (jb < jb_diag) {
+      if (jb < diag) {
         // every j of the block precedes every row of the strip:
         // exp(A_i - A_j) = exp(A_i - A_m) exp(A_m - A_j), m = j0 + 31, both <= 1
         const float vi = __builtin_amdgcn_exp2f(A2[i] - A2[j0 + 31]);
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[4 * jt + r] = gt[jt][r] * (tjv[4 * jt + r] * vi);
+        for (int jt = 0; jt < 2; ++jt) {
+          const float4 t4 = *(const float4*)&tj[j0 + 16 * jt + 4 * lq];
+          v[4 * jt + 0] = gt[jt][0] * (t4.x * vi);
+          v[4 * jt + 1] = gt[jt][1] * (t4.y * vi);
+          v[4 * jt + 2] = gt[jt][2] * (t4.z * vi);
+          v[4 * jt + 3] = gt[jt][3] * (t4.w * vi);
+        }
       } else {
         const float ai = A2[i];
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+        for (int jt = 0; jt < 2; ++jt) {
+          const float4 a4 = *(const float4*)&A2[j0 + 16 * jt + 4 * lq];
+          const float aj[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = j0 + 16 * jt + 4 * lq + r;
-            const float d = j <= i ? ai - A2[j] : 0.f;
+            const float d = j <= i ? ai - aj[r] : 0.f;
             const float e = __builtin_amdgcn_exp2f(d);
             v[4 * jt + r] = j <= i ? gt[jt][r] * e : 0.f;
           }
+        }
       }
       const bf16x8 bop = as_bf16x8(make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]),
                                               pack2(v[6], v[7])));
@@ -356,22 +413,46 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(SSDParams p) {
       for (int mt = 0; mt < 4; ++mt) acc[s][mt] = mfma(aX[mt], bop, acc[s][mt]);
     }
   }
+  // inter-chunk term: Y^T[p][i] += exp(A_cum_i) sum_n S_in[p][n] C[i][n]
+  {
+    const uint16_t* Sp = (const uint16_t*)p.S_in + ((b * p.nchunks + c) * p.H + h) * 4096;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const bf16x8 a0 = as_bf16x8(*(const uint4*)(Sp + (16 * mt + lr) * 64 + 8 * lq));
+      const bf16x8 a1 = as_bf16x8(*(const uint4*)(Sp + (16 * mt + lr) * 64 + 32 + 8 * lq));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+        a = mfma(a0, Cop[s][0], a);
+        a = mfma(a1, Cop[s][1], a);
+        const float ei = __builtin_amdgcn_exp2f(A2[16 * kst[s] + lr]);
+        acc[s][mt] += a * ei;
+      }
+    }
+  }
   // epilogue: + D x, store y[i][p0..p0+3]
   const float Dh = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
 #pragma unroll
-  for (int s = 0; s < SPW; ++s) {
-    const int64_t ti = t0 + i00 + 16 * s + lr;
-    if (ti >= p.L) continue;
+  for (int s = 0; s < 2; ++s) {
+    const int64_t ti = t0 + 16 * kst[s] + lr;
+    const bool ok = ti < p.L;
+    const int64_t tr = ok ? ti : p.L - 1;
+    uint2 xv[4];
+    if (p.Dskip) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        xv[mt] = *(const uint2*)((const uint16_t*)p.x + b * p.xs_b + tr * p.xs_t + h * p.xs_h + 16 * mt + 4 * lq);
+    }
+    if (!ok) continue;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int p0 = 16 * mt + 4 * lq;
       float o[4] = {acc[s][mt][0], acc[s][mt][1], acc[s][mt][2], acc[s][mt][3]};
       if (p.Dskip) {
-        const uint2 xv = *(const uint2*)((const uint16_t*)p.x + b * p.xs_b + ti * p.xs_t + h * p.xs_h + p0);
-        o[0] = __builtin_fmaf(Dh, __uint_as_float(xv.x << 16), o[0]);
-        o[1] = __builtin_fmaf(Dh, __uint_as_float(xv.x & 0xFFFF0000u), o[1]);
-        o[2] = __builtin_fmaf(Dh, __uint_as_float(xv.y << 16), o[2]);
-        o[3] = __builtin_fmaf(Dh, __uint_as_float(xv.y & 0xFFFF0000u), o[3]);
+        o[0] = __builtin_fmaf(Dh, __uint_as_float(xv[mt].x << 16), o[0]);
+        o[1] = __builtin_fmaf(Dh, __uint_as_float(xv[mt].x & 0xFFFF0000u), o[1]);
+        o[2] = __builtin_fmaf(Dh, __uint_as_float(xv[mt].y << 16), o[2]);
+        o[3] = __builtin_fmaf(Dh, __uint_as_float(xv[mt].y & 0xFFFF0000u), o[3]);
       }
       const int64_t off = b * p.ys_b + ti * p.ys_t + h * p.ys_h + p0;
       if (p.y_f32) *(float4*)((float*)p.y + off) = make_float4(o[0], o[1], o[2], o[3]);
@@ -405,16 +486,10 @@ hipError_t launch_ssd_state_passing(const SSDParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_ssd_chunk_scan(const SSDParams& p, hipStream_t stream) {
-  if (p.Q == 64) {
-    hipLaunchKernelGGL((chunk_scan_kernel<64, 64>), dim3((unsigned)(p.batch * p.nchunks * p.H)), dim3(256), 0,
-                       stream, p);
-  } else if (p.Q == 128) {
-    hipLaunchKernelGGL((chunk_scan_kernel<128, 128>), dim3((unsigned)(p.batch * p.nchunks * p.H)), dim3(256), 0,
-                       stream, p);
-  } else {
-    hipLaunchKernelGGL((chunk_scan_kernel<256, 128>), dim3((unsigned)(p.batch * p.nchunks * p.H * 2)), dim3(256),
-                       0, stream, p);
-  }
+  const unsigned nb = (unsigned)(p.batch * p.nchunks * p.H);
+  if (p.Q == 64) hipLaunchKernelGGL(chunk_scan_kernel<64>, dim3(nb), dim3(128), 0, stream, p);
+  else if (p.Q == 128) hipLaunchKernelGGL(chunk_scan_kernel<128>, dim3(nb), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(chunk_scan_kernel<256>, dim3(nb), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
