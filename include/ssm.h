@@ -95,7 +95,10 @@ typedef struct {
  *   h0       : (batch, dim, dstate) F32 contiguous   if SSM_HAS_H0
  *   h_last   : (batch, dim, dstate) F32 contiguous   if SSM_WANT_HLAST
  * io is SSM_F32 or SSM_BF16 and is the same for x, delta, z, B, C.
- * Descriptors of tensors a flag turns off are ignored. */
+ * Descriptors of tensors a flag turns off are ignored.
+ * Limit: for x, delta, z, y, (16 * stride[1] + 16 * stride[2]) elements, and
+ * for B, C, (16 * stride[1] + dstate * stride[2]) elements, must span less
+ * than 2 GiB (SSM_ERR_UNSUPPORTED otherwise). */
 typedef struct {
   int64_t batch, seqlen, dim, dstate;
   uint32_t flags;

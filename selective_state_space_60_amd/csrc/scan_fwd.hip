@@ -9,27 +9,37 @@
 // no (batch, L, D, N) tensor in HBM -- is kept; the blocking is MI355X's own.
 //
 // On gfx950 this path is bound by VALU issue, not by HBM: every state of every
-// token*channel costs one v_exp_f32 (half rate) and six fp32 ops, against ~8
-// bytes of HBM traffic per token*channel.  The layout therefore aims at full
-// VALU occupancy and balance across the 1024 SIMDs:
+// token*channel costs one v_exp_f32 (half rate) and several fp32 ops, against
+// ~8 bytes of HBM traffic per token*channel.  Everything else is arranged to
+// add as few vector instructions as possible on top of that:
 //
 //  * A 256-thread workgroup owns 16 channels of one batch row and one stretch
 //    of the sequence.  Each channel is spread over 16 lanes; a lane keeps
 //    N/16 states in registers for the whole walk (one state at N = 16), so the
 //    N-wide state never leaves the register file.  With 16 lanes per channel a
-//    wide layer gives thousands of equal waves, and the Mamba-2.8B layer
-//    (4 x 5120 channels) gives exactly five per SIMD.
-//  * The sequence is walked in tiles of 32 steps.  x, delta, z (32 x 16) and
-//    B, C (32 x N) of the next tile are fetched into registers while the
-//    current tile is scanned, then converted to fp32 and staged in LDS as
-//    (delta, x) and (B, C) pairs, so a lane reads each step's operands with two
-//    8-byte LDS reads (broadcast across the lanes that share them).
-//  * Per step and state: u = delta*A*log2(e), Abar = v_exp_f32(u),
-//    c = Abar/A - 1/A (one fma with a precomputed 1/A), h = Abar*h + c*(B*x),
-//    partial readout C*h -- no cross-lane traffic inside the recurrence.
-//  * Each lane writes its partial readout to LDS; after the tile, the
-//    workgroup sums the 16 partials of each (step, channel), adds D*x, applies
-//    SiLU(z), rounds to the output type and stores.
+//    wide layer gives thousands of equal waves.
+//  * The sequence is walked in tiles of 16 steps.  x, delta (16 x 16 each),
+//    B, C (16 x N) and z of tile k+2 are fetched into registers with buffer
+//    loads while tile k is scanned.  All per-tile address arithmetic is
+//    scalar: each lane's byte offset inside a tile is fixed and the buffer
+//    base advances in SGPRs; in the last tile of a stretch the descriptor's
+//    range ends at the last element that belongs to it, so reads of rows past
+//    the end return zero without touching memory.  Tile
+//    k+1 is then converted and staged in LDS as (delta, x) and (B, C) pairs,
+//    so a lane reads the operands of two steps with two 16-byte LDS reads.
+//  * Per step and state, with A != 0 and one state per lane, the kernel
+//    carries g = A*h instead of h:  g_t = Abar*(g_{t-1} + B x) - B x, the
+//    zero-order-hold update multiplied through by A.  That is one exp2, one
+//    multiply for delta*A*log2(e), one for B*x, an add and an fma; the factor
+//    1/A moves out of the recurrence into the readout sum below.  Workgroups
+//    with several states per lane, with A == 0 somewhere (limit delta*B), or
+//    with the simplified discretisation (Bbar = delta*B) carry h itself.
+//  * Each lane writes its partial readout (C*g, or C.h over its states) to
+//    LDS; after every tile each wave sums, for the 4 channels it scans, the 16
+//    partials of each (step, channel) -- weighted by 1/A of the state in the g
+//    form -- adds D*x, applies SiLU(z) (z is loaded straight into the summing
+//    lane's registers), rounds to the output type and stores.  The partials
+//    are wave-private, so this needs no workgroup barrier.
 //  * When batch x channels cannot fill the GPU (long, narrow problems), the
 //    sequence is cut into segments: (1) each segment but the last is scanned
 //    from h = 0 for its end state and its sum of delta, (2) a small kernel
@@ -46,16 +56,25 @@ namespace {
 
 constexpr int G = kScanLanesPerChannel;    // 16 lanes per channel
 constexpr int CH = kScanChannelsPerBlock;  // 16 channels per workgroup
-constexpr int TT = kScanTileSteps;         // 32 steps per tile
+constexpr int TT = kScanTileSteps;         // 16 steps per tile
 constexpr int NT = kScanThreads;           // 256 threads
-constexpr int EPT = TT * CH / NT;          // x/delta/z elements per thread per tile (2)
+constexpr int CPW = 64 / G;                // channels per wave (4)
+constexpr int UB = 4;                      // steps per register block
+constexpr int TP = TT + 2;                 // time pitch (float2) of the staged tiles; even keeps 16-byte reads aligned
+constexpr int PN = TT * CPW + 4;           // pitch (floats) of one state's row of partials
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // buffer descriptor word 3 for raw (unformatted) access on gfx9
 
-static_assert(G == 16 && CH * G == NT && EPT == 2, "tiling");
+static_assert(G == 16 && CH * G == NT && TT * CH == NT && TT * CPW == 64 && UB == 4, "tiling");
 
 enum : uint32_t { kHasZ = 1u, kHasD = 2u, kEuler = 4u, kHasH0 = 8u, kWantHLast = 16u };
 
-__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// Update forms (uniform per workgroup):
+//   kFormG     : g = A*h, zero-order hold, A != 0 everywhere, one state per lane
+//   kFormH     : h, zero-order hold, A != 0
+//   kFormHZero : h, zero-order hold, some A == 0 (limit delta*B)
+//   kFormEuler : h, Bbar = delta*B
+enum Form : int { kFormG = 0, kFormH = 1, kFormHZero = 2, kFormEuler = 3 };
 
 // Logical block index with blocks of neighbouring channels placed on the same
 // XCD (the hardware deals consecutive block ids round-robin over the 8 XCDs),
@@ -65,54 +84,28 @@ __device__ __forceinline__ int64_t logical_block(int64_t nblocks_padded) {
   return (i & 7) * (nblocks_padded >> 3) + (i >> 3);
 }
 
-constexpr int TP = TT + 2;  // time pitch of the time-major LDS arrays (keeps 16-byte alignment)
-
-// Finalize ownership: wave w finalizes the channels it scans (64/G of them);
-// lane -> channel fin_channel, step pair fin_pair.
-__device__ __forceinline__ int fin_channel(int tid) { return (tid / 64) * (64 / G) + (tid % (64 / G)); }
-__device__ __forceinline__ int fin_pair(int tid) { return (tid % 64) / (64 / G); }
-
-template <int KS>
-struct alignas(16) ScanSmem {
-  float2 dx[2][CH][TP];      // (delta, x), time-major per channel
-  float2 bc[2][G * KS][TP];  // (B_n, C_n), time-major per state
-  float2 z[TT / 2][CH];      // (z_t, z_t+1) of the finalizing thread's channel
-  float Dk[CH];
-  int any_zero_A;
+// A wave-uniform walk over a tensor: the address of the current tile's first
+// element (b, t0, d0), the bytes from one tile to the next, and the byte
+// range of the stretch's last tile (up to and including its last element).
+// Accesses go through a raw buffer descriptor at that address; reads at or
+// beyond the range return zero and touch no memory.
+struct Span {
+  const char* p;
+  int32_t step;
+  uint32_t last_range;
 };
 
-// Per-lane partial readouts of one tile, as (step 2u, step 2u+1) pairs, in an
-// LDS array of its own so the compiler can move operand reads of later steps
-// above these stores.  Each wave owns a region: row sg (the state lane),
-// column tp*CPW + c (step pair, channel of the wave).  A row holds 64 pairs
-// (512 bytes) plus 16 bytes of padding: the finalize's loads read one row (512
-// contiguous bytes) and the compute loop's stores (16 rows x 32 bytes) land
-// on staggered banks.  (A 32-byte pad would make the stores conflict-free but
-// push the workgroup past the LDS size that lets three share a compute unit.)
-constexpr int CPW = 64 / G;            // channels per wave (4)
-constexpr int PROW = (TT / 2) * CPW + 2;  // row pitch in float2
-struct alignas(16) PartSmem {
-  float2 part[NT / 64][G][PROW];
-};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const Span& s, bool last) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)s.p, (short)0, (int)(last ? s.last_range : 0xFFFFFFFFu),
+                                           (int)kRsrcWord3);
+}
 
-// One tile's global loads, held as raw bits until store_tile: the loads are
-// issued two tiles ahead of use, and converting or masking the values at load
-// time would force the wave to wait for them right away.  Out-of-range
-// elements are loaded from a valid address (offset 0) and zeroed on store.
-template <bool BF16, int KS>
-struct TileRegs {
-  static constexpr int W = BF16 ? 1 : 2;  // dwords per two channels
-  uint32_t x[W], dl[W];                  // channels c0, c0+1 of one step
-  uint32_t z[2];                         // steps 2*fin_pair, +1 of channel fin_channel
-  static constexpr int BW = BF16 ? KS : 2 * KS;  // dwords holding this thread's 2*KS B (or C) values
-  uint32_t B[BW], C[BW];
-  uint8_t row_ok, dleft, z_ok, bc_ok;    // validity, applied on store
-};
+__device__ __forceinline__ void advance(Span& s) { s.p += s.step; }
 
 template <bool BF16>
-__device__ __forceinline__ uint32_t ld_raw(const void* p, int64_t i) {
-  if constexpr (BF16) return ((const uint16_t*)p)[i];
-  else return ((const uint32_t*)p)[i];
+__device__ __forceinline__ uint32_t bload(const Span& s, bool last, uint32_t voff) {
+  if constexpr (BF16) return __builtin_amdgcn_raw_buffer_load_b16(rsrc(s, last), (int)voff, 0, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b32(rsrc(s, last), (int)voff, 0, 0);
 }
 
 template <bool BF16>
@@ -121,323 +114,244 @@ __device__ __forceinline__ float raw2f(uint32_t v) {
   else return __uint_as_float(v);
 }
 
-// Two consecutive channels at element offset `off` (VEC: one 4/8-byte load).
-template <bool BF16, bool VEC>
-__device__ __forceinline__ void load2_raw(const void* base, int64_t off, bool ok2, bool ok0, bool ok1,
-                                          uint32_t (&w)[BF16 ? 1 : 2]) {
-  if (VEC) {
-    const int64_t o = ok2 ? off : 0;
-    if constexpr (BF16) w[0] = *(const uint32_t*)((const uint16_t*)base + o);
-    else {
-      const uint2 v = *(const uint2*)((const float*)base + o);
-      w[0] = v.x;
-      w[1] = v.y;
-    }
-  } else {
-    const uint32_t a = ld_raw<BF16>(base, ok0 ? off : 0);
-    const uint32_t c = ld_raw<BF16>(base, ok1 ? off + 1 : 0);
-    if constexpr (BF16) w[0] = a | (c << 16);
-    else {
-      w[0] = a;
-      w[1] = c;
-    }
-  }
-}
-
-template <bool BF16>
-__device__ __forceinline__ float2 unpack2(const uint32_t (&w)[BF16 ? 1 : 2]) {
-  if constexpr (BF16) return make_float2(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u));
-  else return make_float2(__uint_as_float(w[0]), __uint_as_float(w[1]));
-}
-
-// Per-thread element offsets of tile 0 and their per-tile increments.
-struct LoadPlan {
-  int64_t x, dl, z, B, C;  // offsets of this thread's first element in tile 0
-  int64_t bB, bC;          // batch offsets of B and C (general-stride path)
-  int64_t sx, sdl, sz, sbc;  // per-tile increments
-  int row, zt, dleft;        // step of the x/delta row; first z step; channels left (0..2)
-  bool full;                 // all CH channels of the block exist (uniform)
-  bool zc_ok;
-  bool bc_contig;            // B and C rows contiguous with N == G*KS (uniform)
+template <int KS>
+struct alignas(16) ScanSmem {
+  float2 dx[2][CH][TP];      // (delta, x), time-major per channel
+  float2 bc[2][G * KS][TP];  // (B_n, C_n), time-major per state
+  // Partial readouts, wave-private: part[wave][state lane][16*(t/4) + 4*channel of wave + t%4]
+  float part[NT / 64][G][PN];
 };
 
+// One tile's global loads, held as raw bits until they are staged: they are
+// issued two tiles ahead of use, and converting them at load time would make
+// the wave wait for them right away.
 template <int KS>
-__device__ __forceinline__ LoadPlan make_plan(const ScanParams& p, int64_t b, int64_t d0, int64_t t_begin) {
-  const int tid = threadIdx.x;
-  LoadPlan q;
-  q.row = tid / (CH / EPT);
-  const int c0 = (tid % (CH / EPT)) * EPT;
-  const int64_t left = p.D - (d0 + c0);
-  q.dleft = left >= 2 ? 2 : (left <= 0 ? 0 : (int)left);
-  q.full = d0 + CH <= p.D;
-  q.x = b * p.xs_b + (t_begin + q.row) * p.xs_t + d0 + c0;
-  q.dl = b * p.ds_b + (t_begin + q.row) * p.ds_t + d0 + c0;
-  q.sx = TT * p.xs_t;
-  q.sdl = TT * p.ds_t;
-  const int zc = fin_channel(tid);
-  q.zt = 2 * fin_pair(tid);
-  q.zc_ok = d0 + zc < p.D;
-  q.z = b * p.zs_b + (t_begin + q.zt) * p.zs_t + d0 + zc;
-  q.sz = TT * p.zs_t;
-  const int64_t esz = p.io_bf16 ? 2 : 4;
-  q.bc_contig = p.N == G * KS && p.Bs_n == 1 && p.Cs_n == 1 && p.Bs_t == p.N && p.Cs_t == p.N &&
-                p.Bs_b % (2 * KS) == 0 && p.Cs_b % (2 * KS) == 0 && (uintptr_t)p.B % (2 * KS * esz) == 0 &&
-                (uintptr_t)p.C % (2 * KS * esz) == 0;
-  q.bB = b * p.Bs_b;
-  q.bC = b * p.Cs_b;
-  q.B = b * p.Bs_b + t_begin * p.N + tid * 2 * KS;
-  q.C = b * p.Cs_b + t_begin * p.N + tid * 2 * KS;
-  q.sbc = TT * p.N;
-  return q;
-}
+struct Raw {
+  uint32_t x, dl, z;
+  uint32_t B[KS], C[KS];
+};
 
-template <bool BF16, bool VEC, int KS, bool WANT_Z>
-__device__ __forceinline__ void load_tile(const ScanParams& p, const LoadPlan& q, int64_t k, int64_t t0,
-                                          int64_t t_end, TileRegs<BF16, KS>& r) {
-  const int tid = threadIdx.x;
-  const bool row_ok = t0 + q.row < t_end;
-  r.row_ok = row_ok;
-  r.dleft = (uint8_t)q.dleft;
-  const int64_t ox = q.x + k * q.sx, od = q.dl + k * q.sdl;
-  if (VEC && q.full) {
-    // whole block present: one paired load per tensor; rows past the end read offset 0
-    load2_raw<BF16, true>(p.x, row_ok ? ox : 0, true, true, true, r.x);
-    load2_raw<BF16, true>(p.delta, row_ok ? od : 0, true, true, true, r.dl);
-  } else {
-    const bool ok0 = row_ok && q.dleft > 0, ok1 = row_ok && q.dleft > 1;
-    load2_raw<BF16, false>(p.x, ox, false, ok0, ok1, r.x);
-    load2_raw<BF16, false>(p.delta, od, false, ok0, ok1, r.dl);
-  }
-  if (WANT_Z) {
-    // z is read only by the finalize, in its own thread mapping (channel
-    // fin_channel, steps 2*fin_pair and +1), so it needs a single LDS buffer.
-    const int64_t oz = q.z + k * q.sz;
-    const bool z0 = q.zc_ok && t0 + q.zt < t_end, z1 = q.zc_ok && t0 + q.zt + 1 < t_end;
-    r.z_ok = (uint8_t)((z0 ? 1 : 0) | (z1 ? 2 : 0));
-    r.z[0] = ld_raw<BF16>(p.z, z0 ? oz : 0);
-    r.z[1] = ld_raw<BF16>(p.z, z1 ? oz + p.zs_t : 0);
-  }
-  // B, C tile: TT x (G*KS) values, 2*KS consecutive ones per thread.
-  const int e0 = tid * 2 * KS;
-  const int rr = e0 / (G * KS);
-  const bool rows_ok = t0 + rr < t_end;
-  if (q.bc_contig) {
-    // 2*KS consecutive values per thread: one vector load each for B and C
-    const int64_t ob = rows_ok ? q.B + k * q.sbc : 0, oc = rows_ok ? q.C + k * q.sbc : 0;
-    constexpr int BW = TileRegs<BF16, KS>::BW;
-    const uint32_t* pb = (const uint32_t*)((const char*)p.B + ob * (BF16 ? 2 : 4));
-    const uint32_t* pc = (const uint32_t*)((const char*)p.C + oc * (BF16 ? 2 : 4));
-    if constexpr (BW == 1) {
-      r.B[0] = pb[0];
-      r.C[0] = pc[0];
-    } else if constexpr (BW == 2) {
-      const uint2 vb = *(const uint2*)pb, vc = *(const uint2*)pc;
-      r.B[0] = vb.x; r.B[1] = vb.y; r.C[0] = vc.x; r.C[1] = vc.y;
-    } else {
-#pragma unroll
-      for (int j = 0; j < BW; j += 4) {
-        const uint4 vb = *(const uint4*)(pb + j), vc = *(const uint4*)(pc + j);
-        r.B[j] = vb.x; r.B[j + 1] = vb.y; r.B[j + 2] = vb.z; r.B[j + 3] = vb.w;
-        r.C[j] = vc.x; r.C[j + 1] = vc.y; r.C[j + 2] = vc.z; r.C[j + 3] = vc.w;
-      }
-    }
-    r.bc_ok = rows_ok ? (uint8_t)((1 << (2 * KS)) - 1) : 0;
-  } else {
-    // general strides: element loads (values packed as in the vector path)
-    uint8_t bc_ok = 0;
-#pragma unroll
-    for (int j = 0; j < TileRegs<BF16, KS>::BW; ++j) { r.B[j] = 0; r.C[j] = 0; }
-#pragma unroll
-    for (int j = 0; j < 2 * KS; ++j) {
-      const int e = e0 + j;
-      const int rj = e / (G * KS), n = e % (G * KS);
-      const int64_t tt = t0 + rj;
-      const bool ok = tt < t_end && n < p.N;
-      bc_ok |= (uint8_t)(ok ? 1 << j : 0);
-      const uint32_t vb = ld_raw<BF16>(p.B, ok ? q.bB + tt * p.Bs_t + n * p.Bs_n : 0);
-      const uint32_t vc = ld_raw<BF16>(p.C, ok ? q.bC + tt * p.Cs_t + n * p.Cs_n : 0);
-      if constexpr (BF16) {
-        r.B[j / 2] |= vb << (16 * (j % 2));
-        r.C[j / 2] |= vc << (16 * (j % 2));
-      } else {
-        r.B[j] = vb;
-        r.C[j] = vc;
-      }
-    }
-    r.bc_ok = bc_ok;
-  }
-}
+// Per-lane byte offsets inside a tile (fixed for the whole walk).
+template <int KS>
+struct Offs {
+  uint32_t x, dl, z, y;
+  uint32_t B[KS], C[KS];
+  bool bc_ok[KS];  // the staged state exists (n < N)
+};
 
-// z goes to its own single buffer: each thread writes only the entries its
-// own finalize reads, after that finalize.
-template <bool BF16, int KS>
-__device__ __forceinline__ void store_z(ScanSmem<KS>& s, const TileRegs<BF16, KS>& r) {
-  const float z0 = (r.z_ok & 1) ? raw2f<BF16>(r.z[0]) : 0.f;
-  const float z1 = (r.z_ok & 2) ? raw2f<BF16>(r.z[1]) : 0.f;
-  s.z[fin_pair(threadIdx.x)][fin_channel(threadIdx.x)] = make_float2(z0, z1);
-}
-
-template <bool BF16, int KS>
-__device__ __forceinline__ void store_tile(ScanSmem<KS>& s, int buf, const TileRegs<BF16, KS>& r) {
-  const int tid = threadIdx.x;
-  const int row = tid / (CH / EPT), c0 = (tid % (CH / EPT)) * EPT;
-  float2 xv = unpack2<BF16>(r.x), dv = unpack2<BF16>(r.dl);
-  if (!r.row_ok || r.dleft < 2) {
-    xv.y = 0.f;
-    dv.y = 0.f;
-    if (!r.row_ok || r.dleft < 1) {
-      xv.x = 0.f;
-      dv.x = 0.f;
-    }
-  }
-  s.dx[buf][c0][row] = make_float2(dv.x, xv.x);
-  s.dx[buf][c0 + 1][row] = make_float2(dv.y, xv.y);
-#pragma unroll
-  for (int k = 0; k < 2 * KS; ++k) {
-    const int e = tid * 2 * KS + k;
-    const bool ok = (r.bc_ok >> k) & 1;
-    uint32_t vb, vc;
-    if constexpr (BF16) {
-      vb = (r.B[k / 2] >> (16 * (k % 2))) & 0xFFFFu;
-      vc = (r.C[k / 2] >> (16 * (k % 2))) & 0xFFFFu;
-    } else {
-      vb = r.B[k];
-      vc = r.C[k];
-    }
-    s.bc[buf][e % (G * KS)][e / (G * KS)] = make_float2(ok ? raw2f<BF16>(vb) : 0.f, ok ? raw2f<BF16>(vc) : 0.f);
-  }
-}
-
-// One step of one lane's KS states.  DISC: 0 = zero-order hold with A != 0,
-// 1 = zero-order hold allowing A == 0 (limit delta*B), 2 = Bbar = delta*B.
-template <int KS, int DISC, bool READOUT>
+// One step of one lane's KS states; returns the lane's partial readout.
+template <int KS, int FORM, bool READOUT>
 __device__ __forceinline__ float step(float (&h)[KS], const float (&A2)[KS], const float (&iA)[KS],
-                                      const float (&ez)[KS], float dt, float xt, const float* Bv, const float* Cv) {
+                                      const float (&ez)[KS], float dt, float xt, const float (&Bv)[KS],
+                                      const float (&Cv)[KS]) {
   float yp = 0.f;
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
     const float Ab = __builtin_amdgcn_exp2f(dt * A2[k]);
-    if constexpr (DISC == 2) {
+    if constexpr (FORM == kFormG) {
+      const float q = Bv[k] * xt;
+      h[k] = __builtin_fmaf(Ab, h[k] + q, -q);
+    } else if constexpr (FORM == kFormEuler) {
       h[k] = __builtin_fmaf(Ab, h[k], Bv[k] * (dt * xt));
     } else {
-      // (Abar - 1)/A as Abar*(1/A) - 1/A with one rounding; for A == 0 the
+      // (Abar - 1)/A as Abar*(1/A) - 1/A with one rounding; with A == 0 the
       // factor is 0 and ez*delta supplies the limit delta.
       float c = __builtin_fmaf(Ab, iA[k], -iA[k]);
-      if constexpr (DISC == 1) c = __builtin_fmaf(ez[k], dt, c);
+      if constexpr (FORM == kFormHZero) c = __builtin_fmaf(ez[k], dt, c);
       h[k] = __builtin_fmaf(Ab, h[k], c * (Bv[k] * xt));
     }
-    if constexpr (READOUT) yp = __builtin_fmaf(Cv[k], h[k], yp);
+    if constexpr (READOUT) yp = k == 0 ? Cv[k] * h[k] : __builtin_fmaf(Cv[k], h[k], yp);
   }
   return yp;
 }
 
-constexpr int UB = 8;  // steps per register block
-
-// Operands of UB steps for one lane: (delta, x) and, per state, (B, C).
 template <int KS>
 struct StepOps {
-  float4 dx[UB / 2];
-  float4 bc[UB / 2][KS];
+  float4 dx[UB / 2];      // (delta_t, x_t, delta_t+1, x_t+1)
+  float4 bc[UB / 2][KS];  // (B_t, C_t, B_t+1, C_t+1) per state
 };
 
 template <int KS>
-__device__ __forceinline__ void read_block(const ScanSmem<KS>& s, int buf, int t0, int ch, int sg, StepOps<KS>& o) {
+__device__ __forceinline__ void read_block(const ScanSmem<KS>& s, int buf, int t0, int chb, int sg, StepOps<KS>& o) {
 #pragma unroll
   for (int u = 0; u < UB / 2; ++u) {
-    o.dx[u] = *(const float4*)&s.dx[buf][ch][t0 + 2 * u];
+    o.dx[u] = *(const float4*)&s.dx[buf][chb][t0 + 2 * u];
 #pragma unroll
     for (int k = 0; k < KS; ++k) o.bc[u][k] = *(const float4*)&s.bc[buf][sg * KS + k][t0 + 2 * u];
   }
 }
 
-// Scan one tile of `nt` steps held in LDS buffer `buf`.  Full tiles run in
-// blocks of UB steps whose operands are read from LDS one block ahead.
-template <int KS, int DISC, bool READOUT>
-__device__ __forceinline__ void scan_tile(const ScanSmem<KS>& s, PartSmem& ps, int buf, int nt, float (&h)[KS],
+// Everything one workgroup needs while walking its stretch of the sequence.
+template <int KS>
+struct Walk {
+  Span x, dl, z, B, C;  // load heads (advance as tiles are loaded)
+  Span y;               // store head (advances as tiles are finalized)
+  Offs<KS> o;
+  int ntiles;           // tiles in the stretch
+  int last_rows;        // rows of the last tile that belong to the stretch (1..TT)
+  int st_t;      // staging: step of this thread's x/delta/B/C elements
+  int fin_t;     // finalize: step and channel (within the block) of this lane
+  int fin_c;
+  bool fin_ok;   // the finalize channel exists
+  bool y_f32;
+};
+
+template <bool BF16, int KS, bool WANT_Z>
+__device__ __forceinline__ void load_tile(Walk<KS>& w, int it, Raw<KS>& r) {
+  const bool last = it == w.ntiles - 1;
+  r.x = bload<BF16>(w.x, last, w.o.x);
+  r.dl = bload<BF16>(w.dl, last, w.o.dl);
+  if constexpr (WANT_Z) r.z = bload<BF16>(w.z, last, w.o.z);
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    r.B[k] = bload<BF16>(w.B, last, w.o.B[k]);
+    r.C[k] = bload<BF16>(w.C, last, w.o.C[k]);
+  }
+  advance(w.x);
+  advance(w.dl);
+  if constexpr (WANT_Z) advance(w.z);
+  advance(w.B);
+  advance(w.C);
+}
+
+// Stage tile `it` (raw registers r) into LDS buffer `buf`.  Rows at or past
+// the end of the stretch are zeroed: delta = x = 0 leaves every state
+// unchanged, so a partial last tile is scanned like a full one.
+template <bool BF16, int KS>
+__device__ __forceinline__ void stage_tile(ScanSmem<KS>& s, int buf, const Walk<KS>& w, int it, const Raw<KS>& r) {
+  const int tid = threadIdx.x;
+  float dt = raw2f<BF16>(r.dl), xv = raw2f<BF16>(r.x);
+  float Bv[KS], Cv[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    Bv[k] = w.o.bc_ok[k] ? raw2f<BF16>(r.B[k]) : 0.f;
+    Cv[k] = w.o.bc_ok[k] ? raw2f<BF16>(r.C[k]) : 0.f;
+  }
+  if (it == w.ntiles - 1) {  // uniform: only the last tile
+    const bool ok = w.st_t < w.last_rows;
+    dt = ok ? dt : 0.f;
+    xv = ok ? xv : 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      Bv[k] = ok ? Bv[k] : 0.f;
+      Cv[k] = ok ? Cv[k] : 0.f;
+    }
+  }
+  s.dx[buf][tid % CH][w.st_t] = make_float2(dt, xv);
+#pragma unroll
+  for (int k = 0; k < KS; ++k) s.bc[buf][(tid % G) + G * k][w.st_t] = make_float2(Bv[k], Cv[k]);
+}
+
+// Scan one tile from LDS buffer `buf`, in blocks of UB steps whose operands
+// are read one block ahead.  prow: this lane's row of partials.
+template <int KS, int FORM, bool READOUT>
+__device__ __forceinline__ void scan_tile(const ScanSmem<KS>& s, float* prow, int buf, float (&h)[KS],
                                           const float (&A2)[KS], const float (&iA)[KS], const float (&ez)[KS],
                                           float& sum_dt) {
   const int tid = threadIdx.x;
-  const int ch = tid / G, sg = tid % G;
-  if (nt == TT) {
-    StepOps<KS> o[2];
-    read_block<KS>(s, buf, 0, ch, sg, o[0]);
+  const int chb = tid / G, sg = tid % G;
+  StepOps<KS> o[2];
+  read_block<KS>(s, buf, 0, chb, sg, o[0]);
 #pragma unroll
-    for (int blk = 0; blk < TT / UB; ++blk) {
-      if (blk + 1 < TT / UB) read_block<KS>(s, buf, (blk + 1) * UB, ch, sg, o[(blk + 1) & 1]);
-      const StepOps<KS>& c = o[blk & 1];
+  for (int blk = 0; blk < TT / UB; ++blk) {
+    if (blk + 1 < TT / UB) read_block<KS>(s, buf, (blk + 1) * UB, chb, sg, o[(blk + 1) & 1]);
+    const StepOps<KS>& c = o[blk & 1];
+    float yp[UB];
 #pragma unroll
-      for (int u = 0; u < UB / 2; ++u) {
-        float B0[KS], C0[KS], B1[KS], C1[KS];
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          B0[k] = c.bc[u][k].x; C0[k] = c.bc[u][k].y; B1[k] = c.bc[u][k].z; C1[k] = c.bc[u][k].w;
-        }
-        const float y0 = step<KS, DISC, READOUT>(h, A2, iA, ez, c.dx[u].x, c.dx[u].y, B0, C0);
-        const float y1 = step<KS, DISC, READOUT>(h, A2, iA, ez, c.dx[u].z, c.dx[u].w, B1, C1);
-        if (READOUT) ps.part[tid / 64][sg][(blk * (UB / 2) + u) * CPW + ch % CPW] = make_float2(y0, y1);
-        else sum_dt += c.dx[u].x + c.dx[u].z;
-      }
-    }
-  } else {
-    for (int t = 0; t < nt; ++t) {
-      const float2 dx = s.dx[buf][ch][t];
-      float Bv[KS], Cv[KS];
+    for (int u = 0; u < UB / 2; ++u) {
+      float B0[KS], C0[KS], B1[KS], C1[KS];
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        const float2 v = s.bc[buf][sg * KS + k][t];
-        Bv[k] = v.x;
-        Cv[k] = v.y;
+        B0[k] = c.bc[u][k].x; C0[k] = c.bc[u][k].y; B1[k] = c.bc[u][k].z; C1[k] = c.bc[u][k].w;
       }
-      const float yp = step<KS, DISC, READOUT>(h, A2, iA, ez, dx.x, dx.y, Bv, Cv);
-      if (READOUT) ((float*)&ps.part[tid / 64][sg][(t >> 1) * CPW + ch % CPW])[t & 1] = yp;
-      else sum_dt += dx.x;
+      yp[2 * u] = step<KS, FORM, READOUT>(h, A2, iA, ez, c.dx[u].x, c.dx[u].y, B0, C0);
+      yp[2 * u + 1] = step<KS, FORM, READOUT>(h, A2, iA, ez, c.dx[u].z, c.dx[u].w, B1, C1);
+      if (!READOUT) sum_dt += c.dx[u].x + c.dx[u].z;
     }
+    // partials of steps 4*blk .. 4*blk+3 of this lane's channel: one 16-byte store
+    if (READOUT) *(float4*)&prow[blk * (UB * CPW)] = make_float4(yp[0], yp[1], yp[2], yp[3]);
   }
 }
 
-// Finalize a tile: y = (sum of the 16 partials + D x) * silu(z).  Each wave
-// finalizes the 4 channels it scanned (its partials are wave-private, so no
-// workgroup barrier is needed): lane -> channel 4*wave + lane % 4, steps
-// 2*(lane / 4) and +1, i.e. lane = column tp*CPW + c of the partial rows.
-template <bool BF16, bool VEC, int KS>
-__device__ __forceinline__ void finalize_tile(const ScanParams& p, const ScanSmem<KS>& s, const PartSmem& ps, int buf,
-                                              int nt, int64_t b, int64_t d0, int64_t t0, bool want_z) {
-  const int tid = threadIdx.x;
-  const int c = fin_channel(tid), tp = fin_pair(tid);
-  const float2* pp = &ps.part[tid / 64][0][tp * CPW + c % CPW];
-  float a0 = 0.f, a1 = 0.f;
+// Finalize a tile: y = (sum_n w_n partial_n + D x) * silu(z), w_n = 1/A_n in
+// the g form, else 1.  Lane l of a wave takes step l/4 of channel l%4 of the
+// wave; pcol points at that (step, channel) in state row 0 of the partials.
+template <bool BF16, int KS, int FORM>
+__device__ __forceinline__ void finalize_tile(const ScanSmem<KS>& s, const float* pcol, int buf, Walk<KS>& w,
+                                              int it, const float (&fA)[G], float Dk, uint32_t zraw,
+                                              bool want_z) {
+  float acc = 0.f;
 #pragma unroll
-  for (int q = 0; q < G; ++q) {
-    const float2 v = pp[q * PROW];  // (y_t, y_t+1) of state lane q
-    a0 += v.x;
-    a1 += v.y;
+  for (int n = 0; n < G; ++n) {
+    const float v = pcol[n * PN];
+    if constexpr (FORM == kFormG) acc = __builtin_fmaf(fA[n], v, acc);
+    else acc += v;
   }
-  const int dleft = (int)(p.D - (d0 + c));
-  if (dleft <= 0) return;
-  const float acc[2] = {a0, a1};
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 2 * tp + j;
-    if (row >= nt) break;
-    float v = __builtin_fmaf(s.Dk[c], s.dx[buf][c][row].y, acc[j]);
-    if (want_z) {
-      const float zf = j ? s.z[tp][c].y : s.z[tp][c].x;
-      v *= zf * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zf * kLog2e));
+  const bool row_ok = it < w.ntiles - 1 || w.fin_t < w.last_rows;
+  float v = __builtin_fmaf(Dk, s.dx[buf][w.fin_c][w.fin_t].y, acc);
+  if (want_z) {
+    const float zf = raw2f<BF16>(zraw);
+    v *= zf * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zf * kLog2e));
+  }
+  if (row_ok && w.fin_ok) {
+    if (w.y_f32 || !BF16)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc(w.y, false), (int)w.o.y, 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rsrc(w.y, false), (int)w.o.y,
+                                            0, 0);
+  }
+  advance(w.y);
+}
+
+// The walk over the stretch, for one update form.  MODE 0 writes y;
+// MODE 1 only carries the state (from 0) and the sum of delta.
+template <bool BF16, int KS, int MODE, int FORM>
+__device__ __forceinline__ void walk(ScanSmem<KS>& s, Walk<KS>& w, float (&h)[KS], const float (&A2)[KS],
+                                     const float (&iA)[KS], const float (&ez)[KS], const float (&fA)[G], float Dk,
+                                     bool want_z, float& sum_dt) {
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64;
+  float* prow = &s.part[wave][lane % G][CPW * (lane / G)];
+  const float* pcol = &s.part[wave][0][16 * (lane / 16) + 4 * (lane % 4) + (lane / 4) % 4];
+  // Loads run two tiles ahead of use: ra/rb hold the tiles with it & 1 == 0/1.
+  Raw<KS> ra, rb;
+  auto load = [&](int it, Raw<KS>& r) {
+    if (want_z) load_tile<BF16, KS, true>(w, it, r);
+    else load_tile<BF16, KS, false>(w, it, r);
+  };
+  load(0, ra);
+  stage_tile<BF16, KS>(s, 0, w, 0, ra);
+  uint32_t z_cur = ra.z;
+  if (w.ntiles > 1) load(1, rb);
+  if (w.ntiles > 2) load(2, ra);
+  __syncthreads();
+  // One tile: scan it, finalize it, stage tile it+1 (held in rn) and refill
+  // rn with tile it+3.
+  auto body = [&](int it, Raw<KS>& rn) {
+    const int buf = (int)(it & 1);
+    scan_tile<KS, FORM, MODE == 0>(s, prow, buf, h, A2, iA, ez, sum_dt);
+    if (MODE == 0) finalize_tile<BF16, KS, FORM>(s, pcol, buf, w, it, fA, Dk, z_cur, want_z);
+    if (it + 1 < w.ntiles) {
+      z_cur = rn.z;
+      stage_tile<BF16, KS>(s, buf ^ 1, w, it + 1, rn);
+      if (it + 3 < w.ntiles) load(it + 3, rn);
     }
-    const int64_t off = b * p.ys_b + (t0 + row) * p.ys_t + d0 + c;
-    if (p.y_f32 || !BF16) ((float*)p.y)[off] = v;
-    else ((uint16_t*)p.y)[off] = f2bf(v);
+    __syncthreads();
+  };
+  for (int it = 0; it < w.ntiles; it += 2) {
+    body(it, rb);
+    if (it + 1 < w.ntiles) body(it + 1, ra);
   }
 }
 
 // MODE 0: write y (and h_last / start from h_in).  MODE 1: segment aggregates.
-template <bool BF16, bool VEC, int KS, int MODE>
+template <bool BF16, int KS, int MODE>
 __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, int64_t nseg_run,
                                                   int64_t nblocks_padded) {
   __shared__ ScanSmem<KS> s;
-  __shared__ PartSmem ps;
   const int tid = threadIdx.x;
-  const int ch = tid / G, sg = tid % G;
+  const int wave = tid / 64, lane = tid % 64;
+  const int chb = tid / G, sg = tid % G;
 
   const int64_t lb = logical_block(nblocks_padded);
   if (lb >= n_dblk * nseg_run * p.batch) return;
@@ -445,14 +359,20 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   const int64_t seg = (lb / n_dblk) % nseg_run;
   const int64_t b = lb / (n_dblk * nseg_run);
   const int64_t d0 = dblk * CH;
-  const int64_t d = d0 + ch;
+  const int64_t d = d0 + chb;
   const bool d_ok = d < p.D;
+  const bool want_z = MODE == 0 && (p.flags & kHasZ);
+  const int64_t esz = BF16 ? 2 : 4;
+
+  Walk<KS> w;
   const int64_t t_begin = seg * p.seg_len;
   const int64_t t_end = (t_begin + p.seg_len < p.L) ? t_begin + p.seg_len : p.L;
-  const bool want_z = MODE == 0 && (p.flags & kHasZ);
+  w.ntiles = (int)((t_end - t_begin + TT - 1) / TT);
+  w.last_rows = (int)(t_end - t_begin - (int64_t)(w.ntiles - 1) * TT);
+  w.y_f32 = p.y_f32 != 0;
 
-  // Per-lane constants: log2(e)*A, 1/A, (A == 0) for this lane's KS states.
-  float A2[KS], iA[KS], ez[KS], h[KS];
+  // Per-lane constants: A, log2(e)*A, 1/A and (A == 0) for this lane's KS states.
+  float Av[KS], A2[KS], iA[KS], ez[KS], h[KS];
   int zero_A = 0;
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
@@ -460,6 +380,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
     float a = -1.f;  // padding states (n >= N) and channels (d >= D): any A != 0, B = C = 0
     if (d_ok && n < p.N) a = p.A[d * p.As_d + n * p.As_n];
     zero_A |= (a == 0.f);
+    Av[k] = a;
     A2[k] = a * kLog2e;
     iA[k] = a != 0.f ? 1.f / a : 0.f;
     ez[k] = a == 0.f ? 1.f : 0.f;
@@ -477,60 +398,87 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
       }
     }
   }
-  if (tid == 0) s.any_zero_A = 0;
-  if (tid < CH) s.Dk[tid] = (MODE == 0 && (p.flags & kHasD) && d0 + tid < p.D) ? p.Dskip[(d0 + tid) * p.Ds_d] : 0.f;
-  __syncthreads();
-  if (zero_A) s.any_zero_A = 1;
+  const bool any_zero_A = __syncthreads_or(zero_A) != 0;
 
-  // Global loads run two tiles ahead of use: r0/r1 hold tiles k with k & 1 == 0/1.
-  TileRegs<BF16, KS> r0, r1;
-  const int64_t ntiles = (t_end - t_begin + TT - 1) / TT;
-  const LoadPlan lp = make_plan<KS>(p, b, d0, t_begin);
-  auto load = [&](int64_t k, TileRegs<BF16, KS>& r) {
-    if (want_z) load_tile<BF16, VEC, KS, true>(p, lp, k, t_begin + k * TT, t_end, r);
-    else load_tile<BF16, VEC, KS, false>(p, lp, k, t_begin + k * TT, t_end, r);
-  };
-  auto store = [&](int buf, const TileRegs<BF16, KS>& r) {
-    if (want_z) {
-      store_tile<BF16, KS>(s, buf, r);
-      store_z<BF16, KS>(s, r);
-    } else {
-      store_tile<BF16, KS>(s, buf, r);
-    }
-  };
-  load(0, r0);
-  store(0, r0);
-  if (ntiles > 1) load(1, r1);
-  if (ntiles > 2) load(2, r0);
-  __syncthreads();
-  const int disc = (p.flags & kEuler) ? 2 : (s.any_zero_A ? 1 : 0);
+  // Finalize lane: step lane/4 of channel 4*wave + lane%4.
+  w.fin_t = lane / 4;
+  w.fin_c = CPW * wave + lane % 4;
+  const int64_t df = d0 + w.fin_c;
+  w.fin_ok = df < p.D;
+  float Dk = 0.f;
+  if (MODE == 0 && (p.flags & kHasD) && w.fin_ok) Dk = p.Dskip[df * p.Ds_d];
 
+  // Streams: each starts at element (b, t_begin, d0) (state 0 for B, C) and
+  // advances one tile of rows at a time.  The last tile's range ends at its
+  // last row's last element (channel D-1 or state N-1): lanes of rows past
+  // the stretch, or of channels / states past the end of the tensor's last
+  // row, read zeros.  (Rows past the stretch inside the tensor may also be
+  // read; stage_tile discards them.)
+  const int rows_last = w.last_rows;
+  auto span = [&](const void* base, int64_t sb, int64_t st, int64_t sw, int64_t width, int64_t e, int64_t inner) {
+    Span sp;
+    sp.p = (const char*)base + (b * sb + t_begin * st + inner) * e;
+    sp.step = (int32_t)(TT * st * e);
+    sp.last_range = (uint32_t)(((rows_last - 1) * st + (width - 1) * sw + 1) * e);
+    return sp;
+  };
+  w.x = span(p.x, p.xs_b, p.xs_t, 1, p.D - d0, esz, d0);
+  w.dl = span(p.delta, p.ds_b, p.ds_t, 1, p.D - d0, esz, d0);
+  w.z = want_z ? span(p.z, p.zs_b, p.zs_t, 1, p.D - d0, esz, d0) : w.x;
+  w.B = span(p.B, p.Bs_b, p.Bs_t, p.Bs_n, p.N, esz, 0);
+  w.C = span(p.C, p.Cs_b, p.Cs_t, p.Cs_n, p.N, esz, 0);
+  const int64_t yesz = (p.y_f32 || !BF16) ? 4 : 2;
+  w.y = MODE == 0 ? span(p.y, p.ys_b, p.ys_t, 1, p.D - d0, yesz, d0) : w.x;
+
+  // Staging: thread tid loads step tid/16 of channel tid%16 (x, delta) and,
+  // for B and C, state tid%16 + 16k of step tid/16 (states >= N read state 0
+  // and are zeroed when staged).
+  w.st_t = tid / CH;
+  const int64_t stc = tid % CH;
+  w.o.x = (uint32_t)((w.st_t * p.xs_t + stc) * esz);
+  w.o.dl = (uint32_t)((w.st_t * p.ds_t + stc) * esz);
+  w.o.z = want_z ? (uint32_t)((w.fin_t * p.zs_t + w.fin_c) * esz) : 0u;
+  w.o.y = MODE == 0 ? (uint32_t)((w.fin_t * p.ys_t + w.fin_c) * yesz) : 0u;
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const int n = (tid % G) + G * k;
+    w.o.bc_ok[k] = n < p.N;
+    const int64_t nn = n < p.N ? n : 0;
+    w.o.B[k] = (uint32_t)((w.st_t * p.Bs_t + nn * p.Bs_n) * esz);
+    w.o.C[k] = (uint32_t)((w.st_t * p.Cs_t + nn * p.Cs_n) * esz);
+  }
+
+  int form;
+  if (p.flags & kEuler) form = kFormEuler;
+  else if (any_zero_A) form = kFormHZero;
+  else form = (KS == 1) ? kFormG : kFormH;
+
+  float fA[G];
+#pragma unroll
+  for (int n = 0; n < G; ++n) fA[n] = 1.f;
   float sum_dt = 0.f;
-  // One tile: scan it, finalize it, stage tile it+1 (held in rn) and refill
-  // rn with tile it+3.
-  auto body = [&](int64_t it, TileRegs<BF16, KS>& rn) {
-    const int buf = (int)(it & 1);
-    const int64_t t0 = t_begin + it * TT;
-    const int nt = (int)((t_end - t0) < TT ? (t_end - t0) : TT);
+  if (KS == 1 && form == kFormG) {
+    // g form: the finalize weighs the partial of state n by 1/A of the finalize
+    // lane's channel.
     if (MODE == 0) {
-      if (disc == 0) scan_tile<KS, 0, true>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
-      else if (disc == 1) scan_tile<KS, 1, true>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
-      else scan_tile<KS, 2, true>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
-      finalize_tile<BF16, VEC, KS>(p, s, ps, buf, nt, b, d0, t0, want_z);
-    } else {
-      if (disc == 0) scan_tile<KS, 0, false>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
-      else if (disc == 1) scan_tile<KS, 1, false>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
-      else scan_tile<KS, 2, false>(s, ps, buf, nt, h, A2, iA, ez, sum_dt);
+#pragma unroll
+      for (int n = 0; n < G; ++n) {
+        float a = -1.f;
+        if (w.fin_ok && n < p.N) a = p.A[df * p.As_d + n * p.As_n];
+        fA[n] = 1.f / a;
+      }
     }
-    if (it + 1 < ntiles) {
-      store(buf ^ 1, rn);
-      if (it + 3 < ntiles) load(it + 3, rn);
-    }
-    __syncthreads();
-  };
-  for (int64_t it = 0; it < ntiles; it += 2) {
-    body(it, r1);
-    if (it + 1 < ntiles) body(it + 1, r0);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) h[k] *= Av[k];  // g = A h
+    walk<BF16, KS, MODE, kFormG>(s, w, h, A2, iA, ez, fA, Dk, want_z, sum_dt);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) h[k] *= iA[k];  // h = g / A
+  } else if (form == kFormEuler) {
+    walk<BF16, KS, MODE, kFormEuler>(s, w, h, A2, iA, ez, fA, Dk, want_z, sum_dt);
+  } else if (form == kFormHZero) {
+    walk<BF16, KS, MODE, kFormHZero>(s, w, h, A2, iA, ez, fA, Dk, want_z, sum_dt);
+  } else {
+    walk<BF16, KS, MODE, kFormH>(s, w, h, A2, iA, ez, fA, Dk, want_z, sum_dt);
   }
 
   if (!d_ok) return;
@@ -569,43 +517,34 @@ __global__ __launch_bounds__(256) void scan_combine_kernel(ScanParams p) {
   }
 }
 
-template <bool BF16, bool VEC, int KS>
+template <bool BF16, int KS>
 hipError_t launch_ks(const ScanParams& p, hipStream_t stream) {
   const int64_t n_dblk = (p.D + CH - 1) / CH;
   auto padded = [](int64_t n) { return (n + 7) / 8 * 8; };
   if (p.n_seg > 1) {
     const int64_t nb = n_dblk * (p.n_seg - 1) * p.batch;
-    hipLaunchKernelGGL((scan_kernel<BF16, VEC, KS, 1>), dim3((unsigned)padded(nb)), dim3(NT), 0, stream, p, n_dblk,
+    hipLaunchKernelGGL((scan_kernel<BF16, KS, 1>), dim3((unsigned)padded(nb)), dim3(NT), 0, stream, p, n_dblk,
                        (int64_t)(p.n_seg - 1), padded(nb));
     const int64_t ncomb = p.batch * p.D * p.N;
     hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((ncomb + 255) / 256)), dim3(256), 0, stream, p);
   }
   const int64_t nb = n_dblk * p.n_seg * p.batch;
-  hipLaunchKernelGGL((scan_kernel<BF16, VEC, KS, 0>), dim3((unsigned)padded(nb)), dim3(NT), 0, stream, p, n_dblk,
+  hipLaunchKernelGGL((scan_kernel<BF16, KS, 0>), dim3((unsigned)padded(nb)), dim3(NT), 0, stream, p, n_dblk,
                      (int64_t)p.n_seg, padded(nb));
   return hipGetLastError();
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16>
 hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
-  if (p.N <= G * 1) return launch_ks<BF16, VEC, 1>(p, stream);
-  if (p.N <= G * 2) return launch_ks<BF16, VEC, 2>(p, stream);
-  return launch_ks<BF16, VEC, 4>(p, stream);
+  if (p.N <= G * 1) return launch_ks<BF16, 1>(p, stream);
+  if (p.N <= G * 2) return launch_ks<BF16, 2>(p, stream);
+  return launch_ks<BF16, 4>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_selective_scan(const ScanParams& p, hipStream_t stream) {
-  // Paired tile loads/stores need two consecutive channels aligned to their
-  // combined size for every (b, t).
-  const int64_t e = p.io_bf16 ? 2 : 4;
-  const int64_t ye = p.y_f32 ? 4 : e;
-  auto al = [](const void* q, int64_t bytes) { return q == nullptr || ((uintptr_t)q % (uintptr_t)bytes) == 0; };
-  bool vec = al(p.x, 2 * e) && al(p.delta, 2 * e) && al(p.y, 2 * ye) && p.xs_b % 2 == 0 && p.xs_t % 2 == 0 &&
-             p.ds_b % 2 == 0 && p.ds_t % 2 == 0 && p.ys_b % 2 == 0 && p.ys_t % 2 == 0;
-  if (p.flags & kHasZ) vec = vec && al(p.z, 2 * e) && p.zs_b % 2 == 0 && p.zs_t % 2 == 0;
-  if (p.io_bf16) return vec ? launch_io<true, true>(p, stream) : launch_io<true, false>(p, stream);
-  return vec ? launch_io<false, true>(p, stream) : launch_io<false, false>(p, stream);
+  return p.io_bf16 ? launch_io<true>(p, stream) : launch_io<false>(p, stream);
 }
 
 }  // namespace ssm

@@ -93,7 +93,7 @@ ScanPlan plan_scan(const ssm_scan_desc& d) {
   const int64_t waves = blocks * (ssm::kScanThreads / 64);
   int64_t n_seg = 1;
   if (waves < kSimds) {
-    n_seg = std::max<int64_t>(1, (3 * kSimds + waves / 2) / waves);
+    n_seg = std::max<int64_t>(1, (5 * kSimds + waves / 2) / waves);
     n_seg = std::min<int64_t>(n_seg, std::max<int64_t>(1, d.seqlen / 2048));
   }
   int64_t seg_len = (d.seqlen + n_seg - 1) / n_seg;
@@ -139,6 +139,17 @@ ssm_status validate_scan_desc(const ssm_scan_desc* d) {
     if ((s = check_tensor(d->h0, 3, bdn, d->h0.dtype == SSM_F32, false, true))) return s;
   if (d->flags & SSM_WANT_HLAST)
     if ((s = check_tensor(d->h_last, 3, bdn, d->h_last.dtype == SSM_F32, false, true))) return s;
+  // The kernel addresses one tile of rows (and, for B and C, all N states of
+  // a row) with 32-bit byte offsets from the tile's first element.
+  const int64_t e = esize(io), ey = esize(d->y.dtype);
+  const int64_t rows = ssm::kScanTileSteps;
+  auto fits = [&](const ssm_tensor_desc& t, int64_t width, int64_t es) {
+    return (rows * t.stride[1] + width * t.stride[2]) * es < ((int64_t)1 << 31);
+  };
+  if (!fits(d->x, ssm::kScanChannelsPerBlock, e) || !fits(d->delta, ssm::kScanChannelsPerBlock, e) ||
+      !fits(d->y, ssm::kScanChannelsPerBlock, ey) || !fits(d->B, d->dstate, e) || !fits(d->C, d->dstate, e) ||
+      ((d->flags & SSM_HAS_Z) && !fits(d->z, ssm::kScanChannelsPerBlock, e)))
+    return SSM_ERR_UNSUPPORTED;
   return SSM_OK;
 }
 

@@ -37,7 +37,7 @@ struct ScanParams {
 // Tiling of the scan kernels (also used by the host planner).
 constexpr int kScanLanesPerChannel = 16;
 constexpr int kScanChannelsPerBlock = 16;
-constexpr int kScanTileSteps = 32;
+constexpr int kScanTileSteps = 16;
 constexpr int kScanThreads = kScanLanesPerChannel * kScanChannelsPerBlock;
 
 hipError_t launch_selective_scan(const ScanParams& p, hipStream_t stream);
