@@ -8,38 +8,44 @@
 // The pages' recipe -- discretise, scan and multiply by C in one kernel, with
 // no (batch, L, D, N) tensor in HBM -- is kept; the blocking is MI355X's own.
 //
-// On gfx950 this path is bound by VALU issue, not by HBM: every state of every
-// token*channel costs one v_exp_f32 (half rate) and several fp32 ops, against
-// ~8 bytes of HBM traffic per token*channel.  Everything else is arranged to
-// add as few vector instructions as possible on top of that:
+// On gfx950 this path is bound by VALU issue and LDS bandwidth, not by HBM:
+// every state of every token*channel costs one v_exp_f32 (half rate) and
+// several fp32 ops, against ~8 bytes of HBM traffic per token*channel.
+// Everything else is arranged to add as little as possible on top:
 //
 //  * A 256-thread workgroup owns 16 channels of one batch row and one stretch
-//    of the sequence.  Each channel is spread over 16 lanes; a lane keeps
+//    of the sequence.  Each channel is one 16-lane row of a wave; a lane keeps
 //    N/16 states in registers for the whole walk (one state at N = 16), so the
 //    N-wide state never leaves the register file.  With 16 lanes per channel a
 //    wide layer gives thousands of equal waves.
-//  * The sequence is walked in tiles of 16 steps.  x, delta (16 x 16 each),
-//    B, C (16 x N) and z of tile k+2 are fetched into registers with buffer
-//    loads while tile k is scanned.  All per-tile address arithmetic is
-//    scalar: each lane's byte offset inside a tile is fixed and the buffer
-//    base advances in SGPRs; in the last tile of a stretch the descriptor's
-//    range ends at the last element that belongs to it, so reads of rows past
-//    the end return zero without touching memory.  Tile
-//    k+1 is then converted and staged in LDS as (delta, x) and (B, C) pairs,
-//    so a lane reads the operands of two steps with two 16-byte LDS reads.
+//  * The sequence is walked in tiles of 16 steps, and lane j of a channel's
+//    row also holds step j of the tile: its delta, x and z.  A step broadcasts
+//    delta and x from that lane to the row with a DPP row broadcast folded
+//    into the multiply that consumes them, so they cost no extra instruction
+//    and no LDS traffic.  B and C (16 x N per tile, shared by the 16 channels)
+//    are staged in LDS as (B, C) pairs; a lane reads two steps' worth with one
+//    16-byte read.
+//  * Global memory is touched in whole rows of the workgroup's 16 channels
+//    (32 bytes in bf16): thread (t, c) = (tid/16, tid%16) loads x, delta, z
+//    of step t, channel c and stores y the same way; a small LDS transpose
+//    hands them to and from the lanes that hold them.  Loads run two tiles
+//    ahead, into registers, as buffer loads: each lane's byte offset inside a
+//    tile is fixed and the buffer base advances in SGPRs; in the last tile of
+//    a stretch the descriptor's range ends at the last element that belongs
+//    to it, so reads past the end return zero without touching memory.
 //  * Per step and state, with A != 0 and one state per lane, the kernel
 //    carries g = A*h instead of h:  g_t = Abar*(g_{t-1} + B x) - B x, the
-//    zero-order-hold update multiplied through by A.  That is one exp2, one
-//    multiply for delta*A*log2(e), one for B*x, an add and an fma; the factor
-//    1/A moves out of the recurrence into the readout sum below.  Workgroups
-//    with several states per lane, with A == 0 somewhere (limit delta*B), or
-//    with the simplified discretisation (Bbar = delta*B) carry h itself.
+//    zero-order-hold update multiplied through by A.  That is one exp2, two
+//    multiplies (delta*A*log2(e) and B*x), an add and an fma; the factor 1/A
+//    moves out of the recurrence into the readout sum.  Workgroups with
+//    several states per lane, with A == 0 somewhere (limit delta*B), or with
+//    the simplified discretisation (Bbar = delta*B) carry h itself.
 //  * Each lane writes its partial readout (C*g, or C.h over its states) to
-//    LDS; after every tile each wave sums, for the 4 channels it scans, the 16
-//    partials of each (step, channel) -- weighted by 1/A of the state in the g
-//    form -- adds D*x, applies SiLU(z) (z is loaded straight into the summing
-//    lane's registers), rounds to the output type and stores.  The partials
-//    are wave-private, so this needs no workgroup barrier.
+//    LDS; after every tile lane j of a channel's row sums the 16 partials of
+//    step j -- weighted by 1/A of the state in the g form -- adds D*x and
+//    applies SiLU(z).  The partials are wave-private, so this needs no
+//    workgroup barrier; the results go through LDS to the row-wise stores of
+//    the next tile.
 //  * When batch x channels cannot fill the GPU (long, narrow problems), the
 //    sequence is cut into segments: (1) each segment but the last is scanned
 //    from h = 0 for its end state and its sum of delta, (2) a small kernel
@@ -54,18 +60,18 @@
 namespace ssm {
 namespace {
 
-constexpr int G = kScanLanesPerChannel;    // 16 lanes per channel
+constexpr int G = kScanLanesPerChannel;    // 16 lanes per channel (one DPP row)
 constexpr int CH = kScanChannelsPerBlock;  // 16 channels per workgroup
-constexpr int TT = kScanTileSteps;         // 16 steps per tile
+constexpr int TT = kScanTileSteps;         // 16 steps per tile (one per lane of a row)
 constexpr int NT = kScanThreads;           // 256 threads
-constexpr int CPW = 64 / G;                // channels per wave (4)
 constexpr int UB = 4;                      // steps per register block
-constexpr int TP = TT + 2;                 // time pitch (float2) of the staged tiles; even keeps 16-byte reads aligned
-constexpr int PN = TT * CPW + 4;           // pitch (floats) of one state's row of partials
+constexpr int TP = TT + 2;                 // time pitch (float2) of the staged B/C; even keeps 16-byte reads aligned
+constexpr int PN = TT * (64 / G) + 4;      // pitch (floats) of one state's row of partials
+constexpr int HP = TT + 1;                 // pitch of the per-channel step arrays of the LDS transpose
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // buffer descriptor word 3 for raw (unformatted) access on gfx9
 
-static_assert(G == 16 && CH * G == NT && TT * CH == NT && TT * CPW == 64 && UB == 4, "tiling");
+static_assert(G == 16 && TT == G && CH * G == NT && UB == 4, "tiling");
 
 enum : uint32_t { kHasZ = 1u, kHasD = 2u, kEuler = 4u, kHasH0 = 8u, kWantHLast = 16u };
 
@@ -82,6 +88,12 @@ enum Form : int { kFormG = 0, kFormH = 1, kFormHZero = 2, kFormEuler = 3 };
 __device__ __forceinline__ int64_t logical_block(int64_t nblocks_padded) {
   const int64_t i = blockIdx.x;
   return (i & 7) * (nblocks_padded >> 3) + (i >> 3);
+}
+
+// Value of lane T of this lane's 16-lane row (DPP row broadcast).
+template <int T>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + T, 0xF, 0xF, true));
 }
 
 // A wave-uniform walk over a tensor: the address of the current tile's first
@@ -116,19 +128,27 @@ __device__ __forceinline__ float raw2f(uint32_t v) {
 
 template <int KS>
 struct alignas(16) ScanSmem {
-  float2 dx[2][CH][TP];      // (delta, x), time-major per channel
-  float2 bc[2][G * KS][TP];  // (B_n, C_n), time-major per state
-  // Partial readouts, wave-private: part[wave][state lane][16*(t/4) + 4*channel of wave + t%4]
+  float2 bc[2][G * KS][TP];  // (B_n, C_n), time-major per state, double-buffered
+  // Partial readouts, wave-private: part[wave][state lane][16*(channel of wave) + step]
   float part[NT / 64][G][PN];
+  float2 hx[2][CH][HP];      // (delta, x) per channel and step, double-buffered
+  uint32_t hz[2][CH][HP];    // z (raw bits)
+  float yb[2][CH][HP];       // finalized y, stored row-wise one tile later
 };
 
-// One tile's global loads, held as raw bits until they are staged: they are
-// issued two tiles ahead of use, and converting them at load time would make
-// the wave wait for them right away.
+// One tile's global loads, held as raw bits until the tile is staged: they
+// are issued two tiles ahead of use, and converting them at load time would
+// make the wave wait for them right away.
 template <int KS>
 struct Raw {
   uint32_t x, dl, z;
   uint32_t B[KS], C[KS];
+};
+
+// The current tile's per-channel values held by this lane (step lane%16).
+struct Hold {
+  float dt, x, xs;  // delta, x, and the value broadcast as x (x, or delta*x in the Euler form)
+  uint32_t z;       // raw bits
 };
 
 // Per-lane byte offsets inside a tile (fixed for the whole walk).
@@ -139,48 +159,6 @@ struct Offs {
   bool bc_ok[KS];  // the staged state exists (n < N)
 };
 
-// One step of one lane's KS states; returns the lane's partial readout.
-template <int KS, int FORM, bool READOUT>
-__device__ __forceinline__ float step(float (&h)[KS], const float (&A2)[KS], const float (&iA)[KS],
-                                      const float (&ez)[KS], float dt, float xt, const float (&Bv)[KS],
-                                      const float (&Cv)[KS]) {
-  float yp = 0.f;
-#pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    const float Ab = __builtin_amdgcn_exp2f(dt * A2[k]);
-    if constexpr (FORM == kFormG) {
-      const float q = Bv[k] * xt;
-      h[k] = __builtin_fmaf(Ab, h[k] + q, -q);
-    } else if constexpr (FORM == kFormEuler) {
-      h[k] = __builtin_fmaf(Ab, h[k], Bv[k] * (dt * xt));
-    } else {
-      // (Abar - 1)/A as Abar*(1/A) - 1/A with one rounding; with A == 0 the
-      // factor is 0 and ez*delta supplies the limit delta.
-      float c = __builtin_fmaf(Ab, iA[k], -iA[k]);
-      if constexpr (FORM == kFormHZero) c = __builtin_fmaf(ez[k], dt, c);
-      h[k] = __builtin_fmaf(Ab, h[k], c * (Bv[k] * xt));
-    }
-    if constexpr (READOUT) yp = k == 0 ? Cv[k] * h[k] : __builtin_fmaf(Cv[k], h[k], yp);
-  }
-  return yp;
-}
-
-template <int KS>
-struct StepOps {
-  float4 dx[UB / 2];      // (delta_t, x_t, delta_t+1, x_t+1)
-  float4 bc[UB / 2][KS];  // (B_t, C_t, B_t+1, C_t+1) per state
-};
-
-template <int KS>
-__device__ __forceinline__ void read_block(const ScanSmem<KS>& s, int buf, int t0, int chb, int sg, StepOps<KS>& o) {
-#pragma unroll
-  for (int u = 0; u < UB / 2; ++u) {
-    o.dx[u] = *(const float4*)&s.dx[buf][chb][t0 + 2 * u];
-#pragma unroll
-    for (int k = 0; k < KS; ++k) o.bc[u][k] = *(const float4*)&s.bc[buf][sg * KS + k][t0 + 2 * u];
-  }
-}
-
 // Everything one workgroup needs while walking its stretch of the sequence.
 template <int KS>
 struct Walk {
@@ -189,11 +167,17 @@ struct Walk {
   Offs<KS> o;
   int ntiles;           // tiles in the stretch
   int last_rows;        // rows of the last tile that belong to the stretch (1..TT)
-  int st_t;      // staging: step of this thread's x/delta/B/C elements
-  int fin_t;     // finalize: step and channel (within the block) of this lane
-  int fin_c;
-  bool fin_ok;   // the finalize channel exists
+  int st_t;             // row-wise role: step (tid/16) of this thread's loads and stores
+  bool st_ch_ok;        // row-wise role: channel tid%16 exists
   bool y_f32;
+};
+
+// Per-lane constants of this lane's KS states.
+template <int KS>
+struct Lane {
+  float A2[KS];  // log2(e) * A
+  float iA[KS];  // 1/A (0 where A == 0)
+  float ez[KS];  // 1 where A == 0, else 0
 };
 
 template <bool BF16, int KS, bool WANT_Z>
@@ -214,9 +198,10 @@ __device__ __forceinline__ void load_tile(Walk<KS>& w, int it, Raw<KS>& r) {
   advance(w.C);
 }
 
-// Stage tile `it` (raw registers r) into LDS buffer `buf`.  Rows at or past
-// the end of the stretch are zeroed: delta = x = 0 leaves every state
-// unchanged, so a partial last tile is scanned like a full one.
+// Make tile `it` (raw registers r) current: B/C into LDS buffer `buf`, this
+// lane's step into registers.  Rows at or past the end of the stretch are
+// zeroed: delta = x = 0 leaves every state unchanged, so a partial last tile
+// is scanned like a full one.
 template <bool BF16, int KS>
 __device__ __forceinline__ void stage_tile(ScanSmem<KS>& s, int buf, const Walk<KS>& w, int it, const Raw<KS>& r) {
   const int tid = threadIdx.x;
@@ -228,58 +213,96 @@ __device__ __forceinline__ void stage_tile(ScanSmem<KS>& s, int buf, const Walk<
     Cv[k] = w.o.bc_ok[k] ? raw2f<BF16>(r.C[k]) : 0.f;
   }
   if (it == w.ntiles - 1) {  // uniform: only the last tile
-    const bool ok = w.st_t < w.last_rows;
-    dt = ok ? dt : 0.f;
-    xv = ok ? xv : 0.f;
+    const bool st_ok = w.st_t < w.last_rows;
+    dt = st_ok ? dt : 0.f;
+    xv = st_ok ? xv : 0.f;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      Bv[k] = ok ? Bv[k] : 0.f;
-      Cv[k] = ok ? Cv[k] : 0.f;
+      Bv[k] = st_ok ? Bv[k] : 0.f;
+      Cv[k] = st_ok ? Cv[k] : 0.f;
     }
   }
-  s.dx[buf][tid % CH][w.st_t] = make_float2(dt, xv);
 #pragma unroll
   for (int k = 0; k < KS; ++k) s.bc[buf][(tid % G) + G * k][w.st_t] = make_float2(Bv[k], Cv[k]);
+  s.hx[buf][tid % G][w.st_t] = make_float2(dt, xv);
+  s.hz[buf][tid % G][w.st_t] = r.z;
 }
 
-// Scan one tile from LDS buffer `buf`, in blocks of UB steps whose operands
-// are read one block ahead.  prow: this lane's row of partials.
-template <int KS, int FORM, bool READOUT>
-__device__ __forceinline__ void scan_tile(const ScanSmem<KS>& s, float* prow, int buf, float (&h)[KS],
-                                          const float (&A2)[KS], const float (&iA)[KS], const float (&ez)[KS],
-                                          float& sum_dt) {
+// This lane's step (lane%16) of its channel (tid/16) for the tile in `buf`.
+template <int KS, int FORM>
+__device__ __forceinline__ void take_hold(const ScanSmem<KS>& s, int buf, bool want_z, Hold& hd) {
   const int tid = threadIdx.x;
-  const int chb = tid / G, sg = tid % G;
-  StepOps<KS> o[2];
-  read_block<KS>(s, buf, 0, chb, sg, o[0]);
+  const float2 v = s.hx[buf][tid / G][tid % G];
+  hd.dt = v.x;
+  hd.x = v.y;
+  hd.xs = FORM == kFormEuler ? v.x * v.y : v.y;
+  hd.z = want_z ? s.hz[buf][tid / G][tid % G] : 0u;
+}
+
+// One step (step T of the tile) of one lane's KS states; returns the lane's
+// partial readout.  delta and x come from lane T of the row.  No implicit
+// fusing of multiplies into adds here: that would turn the broadcast
+// multiplies into fmas, which cannot take the DPP operand.
+template <int KS, int FORM, bool READOUT, int T>
+__device__ __forceinline__ float step(float (&h)[KS], const Lane<KS>& ln, const Hold& hd, const float4 (&bc)[KS],
+                                      bool hi) {
+#pragma clang fp contract(off)
+  float yp = 0.f;
 #pragma unroll
-  for (int blk = 0; blk < TT / UB; ++blk) {
-    if (blk + 1 < TT / UB) read_block<KS>(s, buf, (blk + 1) * UB, chb, sg, o[(blk + 1) & 1]);
-    const StepOps<KS>& c = o[blk & 1];
-    float yp[UB];
-#pragma unroll
-    for (int u = 0; u < UB / 2; ++u) {
-      float B0[KS], C0[KS], B1[KS], C1[KS];
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        B0[k] = c.bc[u][k].x; C0[k] = c.bc[u][k].y; B1[k] = c.bc[u][k].z; C1[k] = c.bc[u][k].w;
-      }
-      yp[2 * u] = step<KS, FORM, READOUT>(h, A2, iA, ez, c.dx[u].x, c.dx[u].y, B0, C0);
-      yp[2 * u + 1] = step<KS, FORM, READOUT>(h, A2, iA, ez, c.dx[u].z, c.dx[u].w, B1, C1);
-      if (!READOUT) sum_dt += c.dx[u].x + c.dx[u].z;
+  for (int k = 0; k < KS; ++k) {
+    const float Bv = hi ? bc[k].z : bc[k].x;
+    const float Cv = hi ? bc[k].w : bc[k].y;
+    const float Ab = __builtin_amdgcn_exp2f(row_bcast<T>(hd.dt) * ln.A2[k]);
+    const float q = row_bcast<T>(hd.xs) * Bv;  // B*x (B*delta*x in the Euler form)
+    if constexpr (FORM == kFormG) {
+      h[k] = __builtin_fmaf(Ab, h[k] + q, -q);
+    } else if constexpr (FORM == kFormEuler) {
+      h[k] = __builtin_fmaf(Ab, h[k], q);
+    } else {
+      // (Abar - 1)/A as Abar*(1/A) - 1/A with one rounding; with A == 0 the
+      // factor is 0 and ez*delta supplies the limit delta.
+      float c = __builtin_fmaf(Ab, ln.iA[k], -ln.iA[k]);
+      if constexpr (FORM == kFormHZero) c = __builtin_fmaf(ln.ez[k], row_bcast<T>(hd.dt), c);
+      h[k] = __builtin_fmaf(Ab, h[k], c * q);
     }
-    // partials of steps 4*blk .. 4*blk+3 of this lane's channel: one 16-byte store
-    if (READOUT) *(float4*)&prow[blk * (UB * CPW)] = make_float4(yp[0], yp[1], yp[2], yp[3]);
+    if constexpr (READOUT) yp = k == 0 ? Cv * h[k] : __builtin_fmaf(Cv, h[k], yp);
+  }
+  return yp;
+}
+
+// B/C of steps t0 .. t0+3 for this lane's states: o[u][k] = (B_t, C_t, B_t+1, C_t+1), t = t0 + 2u.
+template <int KS>
+__device__ __forceinline__ void read_block(const ScanSmem<KS>& s, int buf, int t0, int sg, float4 (&o)[2][KS]) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int k = 0; k < KS; ++k) o[u][k] = *(const float4*)&s.bc[buf][sg * KS + k][t0 + 2 * u];
+}
+
+// Blocks BLK.. of one tile: operands of block BLK+1 are read while block BLK
+// is scanned.  prow: this lane's row of partials (column 16*channel).
+template <int KS, int FORM, bool READOUT, int BLK>
+__device__ __forceinline__ void scan_blocks(const ScanSmem<KS>& s, float* prow, int buf, int sg, float (&h)[KS],
+                                            const Lane<KS>& ln, const Hold& hd, float4 (&o)[2][2][KS]) {
+  if constexpr (BLK < TT / UB) {
+    if constexpr (BLK + 1 < TT / UB) read_block<KS>(s, buf, (BLK + 1) * UB, sg, o[(BLK + 1) & 1]);
+    const float4(&c)[2][KS] = o[BLK & 1];
+    float yp[UB];
+    yp[0] = step<KS, FORM, READOUT, UB * BLK + 0>(h, ln, hd, c[0], false);
+    yp[1] = step<KS, FORM, READOUT, UB * BLK + 1>(h, ln, hd, c[0], true);
+    yp[2] = step<KS, FORM, READOUT, UB * BLK + 2>(h, ln, hd, c[1], false);
+    yp[3] = step<KS, FORM, READOUT, UB * BLK + 3>(h, ln, hd, c[1], true);
+    if (READOUT) *(float4*)&prow[UB * BLK] = make_float4(yp[0], yp[1], yp[2], yp[3]);
+    scan_blocks<KS, FORM, READOUT, BLK + 1>(s, prow, buf, sg, h, ln, hd, o);
   }
 }
 
-// Finalize a tile: y = (sum_n w_n partial_n + D x) * silu(z), w_n = 1/A_n in
-// the g form, else 1.  Lane l of a wave takes step l/4 of channel l%4 of the
-// wave; pcol points at that (step, channel) in state row 0 of the partials.
+// Finalize a tile: lane j of the row takes step j: y = (sum_n w_n partial_n +
+// D x) * silu(z), w_n = 1/A_n in the g form, else 1.  pcol: the lane's
+// (channel, step) column in state row 0 of the partials.
 template <bool BF16, int KS, int FORM>
-__device__ __forceinline__ void finalize_tile(const ScanSmem<KS>& s, const float* pcol, int buf, Walk<KS>& w,
-                                              int it, const float (&fA)[G], float Dk, uint32_t zraw,
-                                              bool want_z) {
+__device__ __forceinline__ void finalize_tile(ScanSmem<KS>& s, int buf, const float* pcol, const float (&fA)[G],
+                                              float Dk, const Hold& hd, bool want_z) {
   float acc = 0.f;
 #pragma unroll
   for (int n = 0; n < G; ++n) {
@@ -287,13 +310,21 @@ __device__ __forceinline__ void finalize_tile(const ScanSmem<KS>& s, const float
     if constexpr (FORM == kFormG) acc = __builtin_fmaf(fA[n], v, acc);
     else acc += v;
   }
-  const bool row_ok = it < w.ntiles - 1 || w.fin_t < w.last_rows;
-  float v = __builtin_fmaf(Dk, s.dx[buf][w.fin_c][w.fin_t].y, acc);
+  float v = __builtin_fmaf(Dk, hd.x, acc);
   if (want_z) {
-    const float zf = raw2f<BF16>(zraw);
+    const float zf = raw2f<BF16>(hd.z);
     v *= zf * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zf * kLog2e));
   }
-  if (row_ok && w.fin_ok) {
+  s.yb[buf][threadIdx.x / G][threadIdx.x % G] = v;
+}
+
+// Store tile `it` (finalized into yb[buf] before the last barrier) row-wise:
+// thread (t, c) = (tid/16, tid%16) stores step t of channel c.
+template <bool BF16, int KS>
+__device__ __forceinline__ void store_y(const ScanSmem<KS>& s, int buf, Walk<KS>& w, int it) {
+  const float v = s.yb[buf][threadIdx.x % G][w.st_t];
+  const bool row_ok = it < w.ntiles - 1 || w.st_t < w.last_rows;
+  if (row_ok && w.st_ch_ok) {
     if (w.y_f32 || !BF16)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc(w.y, false), (int)w.o.y, 0, 0);
     else
@@ -304,35 +335,43 @@ __device__ __forceinline__ void finalize_tile(const ScanSmem<KS>& s, const float
 }
 
 // The walk over the stretch, for one update form.  MODE 0 writes y;
-// MODE 1 only carries the state (from 0) and the sum of delta.
+// MODE 1 only carries the state (from 0) and this lane's share of the sum of
+// delta (the steps it holds).
 template <bool BF16, int KS, int MODE, int FORM>
-__device__ __forceinline__ void walk(ScanSmem<KS>& s, Walk<KS>& w, float (&h)[KS], const float (&A2)[KS],
-                                     const float (&iA)[KS], const float (&ez)[KS], const float (&fA)[G], float Dk,
-                                     bool want_z, float& sum_dt) {
+__device__ __forceinline__ void walk(ScanSmem<KS>& s, Walk<KS>& w, float (&h)[KS], const Lane<KS>& ln,
+                                     const float (&fA)[G], float Dk, bool want_z, float& sum_dt) {
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
-  float* prow = &s.part[wave][lane % G][CPW * (lane / G)];
-  const float* pcol = &s.part[wave][0][16 * (lane / 16) + 4 * (lane % 4) + (lane / 4) % 4];
+  const int wave = tid / 64, lane = tid % 64, sg = tid % G;
+  float* prow = &s.part[wave][sg][G * (lane / G)];
+  const float* pcol = &s.part[wave][0][lane];
   // Loads run two tiles ahead of use: ra/rb hold the tiles with it & 1 == 0/1.
   Raw<KS> ra, rb;
+  Hold hd;
   auto load = [&](int it, Raw<KS>& r) {
     if (want_z) load_tile<BF16, KS, true>(w, it, r);
     else load_tile<BF16, KS, false>(w, it, r);
   };
   load(0, ra);
   stage_tile<BF16, KS>(s, 0, w, 0, ra);
-  uint32_t z_cur = ra.z;
   if (w.ntiles > 1) load(1, rb);
   if (w.ntiles > 2) load(2, ra);
   __syncthreads();
-  // One tile: scan it, finalize it, stage tile it+1 (held in rn) and refill
-  // rn with tile it+3.
+  // One tile: take this lane's step, scan, finalize into yb, store the
+  // previous tile's y, stage tile it+1 (held in rn) and refill rn with tile
+  // it+3.
   auto body = [&](int it, Raw<KS>& rn) {
-    const int buf = (int)(it & 1);
-    scan_tile<KS, FORM, MODE == 0>(s, prow, buf, h, A2, iA, ez, sum_dt);
-    if (MODE == 0) finalize_tile<BF16, KS, FORM>(s, pcol, buf, w, it, fA, Dk, z_cur, want_z);
+    const int buf = it & 1;
+    take_hold<KS, FORM>(s, buf, want_z, hd);
+    float4 o[2][2][KS];
+    read_block<KS>(s, buf, 0, sg, o[0]);
+    scan_blocks<KS, FORM, MODE == 0, 0>(s, prow, buf, sg, h, ln, hd, o);
+    if (MODE == 0) {
+      finalize_tile<BF16, KS, FORM>(s, buf, pcol, fA, Dk, hd, want_z);
+      if (it > 0) store_y<BF16, KS>(s, buf ^ 1, w, it - 1);
+    } else {
+      sum_dt += hd.dt;
+    }
     if (it + 1 < w.ntiles) {
-      z_cur = rn.z;
       stage_tile<BF16, KS>(s, buf ^ 1, w, it + 1, rn);
       if (it + 3 < w.ntiles) load(it + 3, rn);
     }
@@ -342,6 +381,7 @@ __device__ __forceinline__ void walk(ScanSmem<KS>& s, Walk<KS>& w, float (&h)[KS
     body(it, rb);
     if (it + 1 < w.ntiles) body(it + 1, ra);
   }
+  if (MODE == 0) store_y<BF16, KS>(s, (w.ntiles - 1) & 1, w, w.ntiles - 1);
 }
 
 // MODE 0: write y (and h_last / start from h_in).  MODE 1: segment aggregates.
@@ -350,7 +390,6 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
                                                   int64_t nblocks_padded) {
   __shared__ ScanSmem<KS> s;
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
   const int chb = tid / G, sg = tid % G;
 
   const int64_t lb = logical_block(nblocks_padded);
@@ -359,7 +398,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   const int64_t seg = (lb / n_dblk) % nseg_run;
   const int64_t b = lb / (n_dblk * nseg_run);
   const int64_t d0 = dblk * CH;
-  const int64_t d = d0 + chb;
+  const int64_t d = d0 + chb;  // this lane's channel (scan and finalize)
   const bool d_ok = d < p.D;
   const bool want_z = MODE == 0 && (p.flags & kHasZ);
   const int64_t esz = BF16 ? 2 : 4;
@@ -371,8 +410,9 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   w.last_rows = (int)(t_end - t_begin - (int64_t)(w.ntiles - 1) * TT);
   w.y_f32 = p.y_f32 != 0;
 
-  // Per-lane constants: A, log2(e)*A, 1/A and (A == 0) for this lane's KS states.
-  float Av[KS], A2[KS], iA[KS], ez[KS], h[KS];
+  // Per-lane constants of this lane's KS states.
+  Lane<KS> ln;
+  float Av[KS], h[KS];
   int zero_A = 0;
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
@@ -381,9 +421,9 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
     if (d_ok && n < p.N) a = p.A[d * p.As_d + n * p.As_n];
     zero_A |= (a == 0.f);
     Av[k] = a;
-    A2[k] = a * kLog2e;
-    iA[k] = a != 0.f ? 1.f / a : 0.f;
-    ez[k] = a == 0.f ? 1.f : 0.f;
+    ln.A2[k] = a * kLog2e;
+    ln.iA[k] = a != 0.f ? 1.f / a : 0.f;
+    ln.ez[k] = a == 0.f ? 1.f : 0.f;
     h[k] = 0.f;
   }
   if (MODE == 0) {
@@ -400,13 +440,8 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   }
   const bool any_zero_A = __syncthreads_or(zero_A) != 0;
 
-  // Finalize lane: step lane/4 of channel 4*wave + lane%4.
-  w.fin_t = lane / 4;
-  w.fin_c = CPW * wave + lane % 4;
-  const int64_t df = d0 + w.fin_c;
-  w.fin_ok = df < p.D;
   float Dk = 0.f;
-  if (MODE == 0 && (p.flags & kHasD) && w.fin_ok) Dk = p.Dskip[df * p.Ds_d];
+  if (MODE == 0 && (p.flags & kHasD) && d_ok) Dk = p.Dskip[d * p.Ds_d];
 
   // Streams: each starts at element (b, t_begin, d0) (state 0 for B, C) and
   // advances one tile of rows at a time.  The last tile's range ends at its
@@ -414,7 +449,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   // the stretch, or of channels / states past the end of the tensor's last
   // row, read zeros.  (Rows past the stretch inside the tensor may also be
   // read; stage_tile discards them.)
-  const int rows_last = w.last_rows;
+  const int64_t rows_last = w.last_rows;
   auto span = [&](const void* base, int64_t sb, int64_t st, int64_t sw, int64_t width, int64_t e, int64_t inner) {
     Span sp;
     sp.p = (const char*)base + (b * sb + t_begin * st + inner) * e;
@@ -430,18 +465,18 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   const int64_t yesz = (p.y_f32 || !BF16) ? 4 : 2;
   w.y = MODE == 0 ? span(p.y, p.ys_b, p.ys_t, 1, p.D - d0, yesz, d0) : w.x;
 
-  // Staging: thread tid loads step tid/16 of channel tid%16 (x, delta) and,
-  // for B and C, state tid%16 + 16k of step tid/16 (states >= N read state 0
-  // and are zeroed when staged).
-  w.st_t = tid / CH;
-  const int64_t stc = tid % CH;
-  w.o.x = (uint32_t)((w.st_t * p.xs_t + stc) * esz);
-  w.o.dl = (uint32_t)((w.st_t * p.ds_t + stc) * esz);
-  w.o.z = want_z ? (uint32_t)((w.fin_t * p.zs_t + w.fin_c) * esz) : 0u;
-  w.o.y = MODE == 0 ? (uint32_t)((w.fin_t * p.ys_t + w.fin_c) * yesz) : 0u;
+  // Row-wise role: thread (t, c) = (tid/16, tid%16) loads x, delta, z of
+  // step t, channel c and stores y the same way; for B and C it loads state
+  // c + 16k of step t (states >= N read state 0 and are zeroed when staged).
+  w.st_t = tid / G;
+  w.st_ch_ok = d0 + sg < p.D;
+  w.o.x = (uint32_t)((w.st_t * p.xs_t + sg) * esz);
+  w.o.dl = (uint32_t)((w.st_t * p.ds_t + sg) * esz);
+  w.o.z = want_z ? (uint32_t)((w.st_t * p.zs_t + sg) * esz) : 0u;
+  w.o.y = MODE == 0 ? (uint32_t)((w.st_t * p.ys_t + sg) * yesz) : 0u;
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
-    const int n = (tid % G) + G * k;
+    const int n = sg + G * k;
     w.o.bc_ok[k] = n < p.N;
     const int64_t nn = n < p.N ? n : 0;
     w.o.B[k] = (uint32_t)((w.st_t * p.Bs_t + nn * p.Bs_n) * esz);
@@ -458,29 +493,33 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   for (int n = 0; n < G; ++n) fA[n] = 1.f;
   float sum_dt = 0.f;
   if (KS == 1 && form == kFormG) {
-    // g form: the finalize weighs the partial of state n by 1/A of the finalize
-    // lane's channel.
+    // g form: the finalize weighs the partial of state n by 1/A of the lane's channel.
     if (MODE == 0) {
 #pragma unroll
       for (int n = 0; n < G; ++n) {
         float a = -1.f;
-        if (w.fin_ok && n < p.N) a = p.A[df * p.As_d + n * p.As_n];
+        if (d_ok && n < p.N) a = p.A[d * p.As_d + n * p.As_n];
         fA[n] = 1.f / a;
       }
     }
 #pragma unroll
     for (int k = 0; k < KS; ++k) h[k] *= Av[k];  // g = A h
-    walk<BF16, KS, MODE, kFormG>(s, w, h, A2, iA, ez, fA, Dk, want_z, sum_dt);
+    walk<BF16, KS, MODE, kFormG>(s, w, h, ln, fA, Dk, want_z, sum_dt);
 #pragma unroll
-    for (int k = 0; k < KS; ++k) h[k] *= iA[k];  // h = g / A
+    for (int k = 0; k < KS; ++k) h[k] *= ln.iA[k];  // h = g / A
   } else if (form == kFormEuler) {
-    walk<BF16, KS, MODE, kFormEuler>(s, w, h, A2, iA, ez, fA, Dk, want_z, sum_dt);
+    walk<BF16, KS, MODE, kFormEuler>(s, w, h, ln, fA, Dk, want_z, sum_dt);
   } else if (form == kFormHZero) {
-    walk<BF16, KS, MODE, kFormHZero>(s, w, h, A2, iA, ez, fA, Dk, want_z, sum_dt);
+    walk<BF16, KS, MODE, kFormHZero>(s, w, h, ln, fA, Dk, want_z, sum_dt);
   } else {
-    walk<BF16, KS, MODE, kFormH>(s, w, h, A2, iA, ez, fA, Dk, want_z, sum_dt);
+    walk<BF16, KS, MODE, kFormH>(s, w, h, ln, fA, Dk, want_z, sum_dt);
   }
 
+  if (MODE == 1) {
+    // the row's 16 lanes each summed the steps they hold
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) sum_dt += __shfl_xor(sum_dt, m, G);
+  }
   if (!d_ok) return;
   if (MODE == 0) {
     if (seg == p.n_seg - 1 && (p.flags & kWantHLast)) {
