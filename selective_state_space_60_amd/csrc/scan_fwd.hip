@@ -25,14 +25,16 @@
 //    and no LDS traffic.  B and C (16 x N per tile, shared by the 16 channels)
 //    are staged in LDS as (B, C) pairs; a lane reads two steps' worth with one
 //    16-byte read.
-//  * Global memory is touched in whole rows of the workgroup's 16 channels
-//    (32 bytes in bf16): thread (t, c) = (tid/16, tid%16) loads x, delta, z
-//    of step t, channel c and stores y the same way; a small LDS transpose
-//    hands them to and from the lanes that hold them.  Loads run two tiles
-//    ahead, into registers, as buffer loads: each lane's byte offset inside a
-//    tile is fixed and the buffer base advances in SGPRs; in the last tile of
-//    a stretch the descriptor's range ends at the last element that belongs
-//    to it, so reads past the end return zero without touching memory.
+//  * Global memory is read and written in whole tiles: when the layout allows
+//    (rows aligned to 4 elements), each wave loads one or two of the tile's
+//    16 x 16 pieces -- x, delta, z, and 16 states of B or C -- with one 8- or
+//    16-byte load per lane, two tiles ahead of use, and one wave stores y the
+//    same way; an LDS transpose hands the values to and from the lanes that
+//    hold them.  Other layouts load element by element, one tile ahead.
+//    Loads are buffer loads: each lane's byte offset inside a tile is fixed
+//    and the buffer base advances in SGPRs; in the last tile of a stretch the
+//    descriptor's range ends at the last element that belongs to it, so reads
+//    past the end return zero without touching memory.
 //  * Per step and state, with A != 0 and one state per lane, the kernel
 //    carries g = A*h instead of h:  g_t = Abar*(g_{t-1} + B x) - B x, the
 //    zero-order-hold update multiplied through by A.  That is one exp2, two
@@ -44,8 +46,8 @@
 //    LDS; after every tile lane j of a channel's row sums the 16 partials of
 //    step j -- weighted by 1/A of the state in the g form -- adds D*x and
 //    applies SiLU(z).  The partials are wave-private, so this needs no
-//    workgroup barrier; the results go through LDS to the row-wise stores of
-//    the next tile.
+//    workgroup barrier; the results go through LDS to the stores of the next
+//    tile.
 //  * When batch x channels cannot fill the GPU (long, narrow problems), the
 //    sequence is cut into segments: (1) each segment but the last is scanned
 //    from h = 0 for its end state and its sum of delta, (2) a small kernel
@@ -71,9 +73,12 @@ constexpr int HP = TT + 1;                 // pitch of the per-channel step arra
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // buffer descriptor word 3 for raw (unformatted) access on gfx9
 
-static_assert(G == 16 && TT == G && CH * G == NT && UB == 4, "tiling");
+static_assert(G == 16 && TT == G && CH == 16 && CH * G == NT && UB == 4, "tiling");
 
 enum : uint32_t { kHasZ = 1u, kHasD = 2u, kEuler = 4u, kHasH0 = 8u, kWantHLast = 16u };
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Update forms (uniform per workgroup):
 //   kFormG     : g = A*h, zero-order hold, A != 0 everywhere, one state per lane
@@ -97,27 +102,48 @@ __device__ __forceinline__ float row_bcast(float v) {
 }
 
 // A wave-uniform walk over a tensor: the address of the current tile's first
-// element (b, t0, d0), the bytes from one tile to the next, and the byte
-// range of the stretch's last tile (up to and including its last element).
-// Accesses go through a raw buffer descriptor at that address; reads at or
-// beyond the range return zero and touch no memory.
+// element, the bytes from one tile to the next, and the descriptor range for
+// the tiles before the last (all of memory, or 0 for an unused stream) and
+// for the last tile (up to and including its last element).  Accesses go
+// through a raw buffer descriptor at that address; reads at or beyond the
+// range return zero and touch no memory.
 struct Span {
   const char* p;
   int32_t step;
+  uint32_t full_range;
   uint32_t last_range;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const Span& s, bool last) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)s.p, (short)0, (int)(last ? s.last_range : 0xFFFFFFFFu),
-                                           (int)kRsrcWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const Span& s, uint32_t range) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)s.p, (short)0, (int)range, (int)kRsrcWord3);
 }
 
 __device__ __forceinline__ void advance(Span& s) { s.p += s.step; }
 
-template <bool BF16>
-__device__ __forceinline__ uint32_t bload(const Span& s, bool last, uint32_t voff) {
-  if constexpr (BF16) return __builtin_amdgcn_raw_buffer_load_b16(rsrc(s, last), (int)voff, 0, 0);
-  else return __builtin_amdgcn_raw_buffer_load_b32(rsrc(s, last), (int)voff, 0, 0);
+// Geometry of a workgroup's stretch, in tiles.
+struct Tiles {
+  int ntiles;     // tiles that hold rows of the stretch
+  int last_rows;  // rows of the last of them that belong to it (1..TT)
+  // Descriptor range for tile `it` (tiles past the stretch read nothing).
+  __device__ __forceinline__ uint32_t range(const Span& s, int it) const {
+    return it < ntiles - 1 ? s.full_range : (it == ntiles - 1 ? s.last_range : 0u);
+  }
+  __device__ __forceinline__ bool row_ok(int it, int r) const {
+    return it < ntiles - 1 || (it == ntiles - 1 && r < last_rows);
+  }
+};
+
+// A span over rows of a tensor starting at element offset `off`: `st` is the
+// row stride, the last tile's range ends at element (rows_last - 1, width - 1)
+// of the span (elements of a row `sw` apart).
+__device__ __forceinline__ Span make_span(const void* base, int64_t off, int64_t st, int64_t sw, int64_t width,
+                                          int64_t e, int rows_last, bool live) {
+  Span sp;
+  sp.p = (const char*)base + off * e;
+  sp.step = (int32_t)(TT * st * e);
+  sp.full_range = live ? 0xFFFFFFFFu : 0u;
+  sp.last_range = live && width > 0 ? (uint32_t)(((int64_t)(rows_last - 1) * st + (width - 1) * sw + 1) * e) : 0u;
+  return sp;
 }
 
 template <bool BF16>
@@ -131,45 +157,212 @@ struct alignas(16) ScanSmem {
   float2 bc[2][G * KS][TP];  // (B_n, C_n), time-major per state, double-buffered
   // Partial readouts, wave-private: part[wave][state lane][16*(channel of wave) + step]
   float part[NT / 64][G][PN];
-  float2 hx[2][CH][HP];      // (delta, x) per channel and step, double-buffered
-  uint32_t hz[2][CH][HP];    // z (raw bits)
-  float yb[2][CH][HP];       // finalized y, stored row-wise one tile later
+  float2 hx[2][CH][HP];  // (delta, x) per channel and step, double-buffered
+  float hz[2][CH][HP];   // z
+  float yb[2][CH][HP];   // finalized y, stored one tile later
 };
 
-// One tile's global loads, held as raw bits until the tile is staged: they
-// are issued two tiles ahead of use, and converting them at load time would
-// make the wave wait for them right away.
-template <int KS>
-struct Raw {
-  uint32_t x, dl, z;
-  uint32_t B[KS], C[KS];
+// ---------------------------------------------------------------- loaders
+//
+// A loader moves one tile of x, delta, z, B, C from global memory into LDS
+// (load: into registers, `kDepth` tiles ahead; stage: registers -> LDS) and
+// y from LDS to global memory.  Rows past the stretch are staged as zeros:
+// delta = x = 0 leaves every state unchanged, so a partial last tile (and
+// the padding tile that evens out the two-ahead loop) is scanned like a full
+// one.
+
+// Element-wise loader for any layout: thread (t, c) = (tid/16, tid%16) loads
+// x, delta, z of step t, channel c and states c + 16k of B and C, and stores
+// y of step t, channel c.
+template <bool BF16, int KS>
+struct ElemLoader {
+  static constexpr int kDepth = 1;
+  struct Set {
+    uint32_t x, dl, z;
+    uint32_t B[KS], C[KS];
+  };
+  Span x, dl, z, B, C, y;
+  uint32_t ox, odl, oz, oy, oB[KS], oC[KS];
+  bool bc_ok[KS];  // state c + 16k exists
+  bool ch_ok;      // channel c exists
+  bool y_f32;
+  int t;
+
+  __device__ __forceinline__ uint32_t ld(const Span& s, uint32_t range, uint32_t voff) const {
+    if constexpr (BF16) return __builtin_amdgcn_raw_buffer_load_b16(rsrc(s, range), (int)voff, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(rsrc(s, range), (int)voff, 0, 0);
+  }
+
+  __device__ __forceinline__ void load(const Tiles& tl, int it, Set& r) {
+    r.x = ld(x, tl.range(x, it), ox);
+    r.dl = ld(dl, tl.range(dl, it), odl);
+    r.z = ld(z, tl.range(z, it), oz);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      r.B[k] = ld(B, tl.range(B, it), oB[k]);
+      r.C[k] = ld(C, tl.range(C, it), oC[k]);
+    }
+    advance(x);
+    advance(dl);
+    advance(z);
+    advance(B);
+    advance(C);
+  }
+
+  __device__ __forceinline__ void stage(ScanSmem<KS>& s, const Tiles& tl, int buf, int it, const Set& r) const {
+    const int c = threadIdx.x % G;
+    const bool ok = tl.row_ok(it, t);
+    const float dt = raw2f<BF16>(r.dl), xv = raw2f<BF16>(r.x);
+    s.hx[buf][c][t] = make_float2(ok ? dt : 0.f, ok ? xv : 0.f);
+    s.hz[buf][c][t] = raw2f<BF16>(r.z);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const bool okk = ok && bc_ok[k];
+      s.bc[buf][c + G * k][t] = make_float2(okk ? raw2f<BF16>(r.B[k]) : 0.f, okk ? raw2f<BF16>(r.C[k]) : 0.f);
+    }
+  }
+
+  __device__ __forceinline__ void store_y(const ScanSmem<KS>& s, const Tiles& tl, int buf, int it) {
+    const int c = threadIdx.x % G;
+    const float v = s.yb[buf][c][t];
+    if (tl.row_ok(it, t) && ch_ok) {
+      if (y_f32 || !BF16)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc(y, 0xFFFFFFFFu), (int)oy, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rsrc(y, 0xFFFFFFFFu),
+                                              (int)oy, 0, 0);
+    }
+    advance(y);
+  }
 };
+
+// Tile-piece loader for layouts whose rows are aligned to 4 elements (x,
+// delta, z, y with D % 4 == 0; B, C contiguous over states with N % 4 == 0).
+// The tile is cut into 16 x 16 pieces -- x, delta, z, then B and C in groups
+// of 16 states -- dealt round-robin to the 4 waves; lane (r, q) = (lane/4,
+// lane%4) of a wave loads row r, elements 4q..4q+3 of each of its pieces.
+// Wave 3 also stores y.
+template <bool BF16, int KS>
+struct VecLoader {
+  static constexpr int kDepth = 2;
+  static constexpr int kPieces = 3 + 2 * KS;
+  static constexpr int kSlots = (kPieces + 3) / 4;
+  static constexpr int kYWave = 3;
+  using Word = typename std::conditional<BF16, u32x2, u32x4>::type;  // 4 elements
+  struct Set {
+    Word v[kSlots];
+  };
+  Span sp[kSlots];
+  bool used[kSlots];     // the slot holds a piece
+  uint32_t voff[kSlots];  // byte offset of this lane's 4 elements in the piece
+  // Where the slot's 4 elements go in LDS: element i of tile buffer `buf` at
+  // dst[j] + buf * dbuf[j] + i * dpitch[j] (floats); elements i >= nok[j]
+  // (states past N) are staged as zeros.
+  float* dst[kSlots];
+  int dbuf[kSlots], dpitch[kSlots], nok[kSlots];
+  Span y;
+  uint32_t oy;
+  bool y_ok;  // this lane's 4 channels exist
+  bool y_f32;
+  int r, q;
+
+  __device__ __forceinline__ Word ld(const Span& s, uint32_t range, uint32_t off) const {
+    if constexpr (BF16) return __builtin_amdgcn_raw_buffer_load_b64(rsrc(s, range), (int)off, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b128(rsrc(s, range), (int)off, 0, 0);
+  }
+
+  __device__ __forceinline__ void load(const Tiles& tl, int it, Set& st) {
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      st.v[j] = ld(sp[j], tl.range(sp[j], it), voff[j]);
+      advance(sp[j]);
+    }
+  }
+
+  __device__ __forceinline__ static void unpack(const Word& w, float (&e)[4]) {
+    if constexpr (BF16) {
+      e[0] = __uint_as_float(w.x << 16);
+      e[1] = __uint_as_float(w.x & 0xFFFF0000u);
+      e[2] = __uint_as_float(w.y << 16);
+      e[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    } else {
+      e[0] = __uint_as_float(w.x);
+      e[1] = __uint_as_float(w.y);
+      e[2] = __uint_as_float(w.z);
+      e[3] = __uint_as_float(w.w);
+    }
+  }
+
+  __device__ __forceinline__ void stage(ScanSmem<KS>& s, const Tiles& tl, int buf, int it, const Set& st) const {
+    const bool ok = tl.row_ok(it, r);
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      if (!used[j]) continue;
+      float e[4];
+      unpack(st.v[j], e);
+      float* d = dst[j] + buf * dbuf[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i * dpitch[j]] = ok && i < nok[j] ? e[i] : 0.f;
+    }
+  }
+
+  // Set slot j up for piece `kd` (see VecLoader); `s` gives the LDS layout.
+  __device__ __forceinline__ void place(ScanSmem<KS>& s, int j, int kd, int n_states) {
+    used[j] = kd < kPieces;
+    nok[j] = 4;
+    if (kd == 0 || kd == 1) {
+      dst[j] = kd == 0 ? &s.hx[0][4 * q][r].y : &s.hx[0][4 * q][r].x;
+      dpitch[j] = 2 * HP;
+      dbuf[j] = 2 * CH * HP;
+    } else if (kd == 2) {
+      dst[j] = &s.hz[0][4 * q][r];
+      dpitch[j] = HP;
+      dbuf[j] = CH * HP;
+    } else {
+      const bool isC = kd >= 3 + KS;
+      const int n0 = 16 * (kd - 3 - (isC ? KS : 0)) + 4 * q;
+      const int nk = n0 < G * KS ? n0 : 0;
+      dst[j] = isC ? &s.bc[0][nk][r].y : &s.bc[0][nk][r].x;
+      dpitch[j] = 2 * TP;
+      dbuf[j] = 2 * G * KS * TP;
+      const int left = n_states - n0;
+      nok[j] = left < 0 ? 0 : (left > 4 ? 4 : left);
+    }
+  }
+
+  __device__ __forceinline__ void store_y(const ScanSmem<KS>& s, const Tiles& tl, int buf, int it) {
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x / 64) == kYWave) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = s.yb[buf][4 * q + i][r];
+      if (tl.row_ok(it, r) && y_ok) {
+        if (y_f32 || !BF16) {
+          u32x4 w;
+          w.x = __float_as_uint(v[0]);
+          w.y = __float_as_uint(v[1]);
+          w.z = __float_as_uint(v[2]);
+          w.w = __float_as_uint(v[3]);
+          __builtin_amdgcn_raw_buffer_store_b128(w, rsrc(y, 0xFFFFFFFFu), (int)oy, 0, 0);
+        } else {
+          u32x2 w;
+          w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+          w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(w, rsrc(y, 0xFFFFFFFFu), (int)oy, 0, 0);
+        }
+      }
+    }
+    advance(y);
+  }
+};
+
+// ------------------------------------------------------------- the scan
 
 // The current tile's per-channel values held by this lane (step lane%16).
 struct Hold {
   float dt, x, xs;  // delta, x, and the value broadcast as x (x, or delta*x in the Euler form)
-  uint32_t z;       // raw bits
-};
-
-// Per-lane byte offsets inside a tile (fixed for the whole walk).
-template <int KS>
-struct Offs {
-  uint32_t x, dl, z, y;
-  uint32_t B[KS], C[KS];
-  bool bc_ok[KS];  // the staged state exists (n < N)
-};
-
-// Everything one workgroup needs while walking its stretch of the sequence.
-template <int KS>
-struct Walk {
-  Span x, dl, z, B, C;  // load heads (advance as tiles are loaded)
-  Span y;               // store head (advances as tiles are finalized)
-  Offs<KS> o;
-  int ntiles;           // tiles in the stretch
-  int last_rows;        // rows of the last tile that belong to the stretch (1..TT)
-  int st_t;             // row-wise role: step (tid/16) of this thread's loads and stores
-  bool st_ch_ok;        // row-wise role: channel tid%16 exists
-  bool y_f32;
+  float z;
 };
 
 // Per-lane constants of this lane's KS states.
@@ -180,54 +373,6 @@ struct Lane {
   float ez[KS];  // 1 where A == 0, else 0
 };
 
-template <bool BF16, int KS, bool WANT_Z>
-__device__ __forceinline__ void load_tile(Walk<KS>& w, int it, Raw<KS>& r) {
-  const bool last = it == w.ntiles - 1;
-  r.x = bload<BF16>(w.x, last, w.o.x);
-  r.dl = bload<BF16>(w.dl, last, w.o.dl);
-  if constexpr (WANT_Z) r.z = bload<BF16>(w.z, last, w.o.z);
-#pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    r.B[k] = bload<BF16>(w.B, last, w.o.B[k]);
-    r.C[k] = bload<BF16>(w.C, last, w.o.C[k]);
-  }
-  advance(w.x);
-  advance(w.dl);
-  if constexpr (WANT_Z) advance(w.z);
-  advance(w.B);
-  advance(w.C);
-}
-
-// Make tile `it` (raw registers r) current: B/C into LDS buffer `buf`, this
-// lane's step into registers.  Rows at or past the end of the stretch are
-// zeroed: delta = x = 0 leaves every state unchanged, so a partial last tile
-// is scanned like a full one.
-template <bool BF16, int KS>
-__device__ __forceinline__ void stage_tile(ScanSmem<KS>& s, int buf, const Walk<KS>& w, int it, const Raw<KS>& r) {
-  const int tid = threadIdx.x;
-  float dt = raw2f<BF16>(r.dl), xv = raw2f<BF16>(r.x);
-  float Bv[KS], Cv[KS];
-#pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    Bv[k] = w.o.bc_ok[k] ? raw2f<BF16>(r.B[k]) : 0.f;
-    Cv[k] = w.o.bc_ok[k] ? raw2f<BF16>(r.C[k]) : 0.f;
-  }
-  if (it == w.ntiles - 1) {  // uniform: only the last tile
-    const bool st_ok = w.st_t < w.last_rows;
-    dt = st_ok ? dt : 0.f;
-    xv = st_ok ? xv : 0.f;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      Bv[k] = st_ok ? Bv[k] : 0.f;
-      Cv[k] = st_ok ? Cv[k] : 0.f;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < KS; ++k) s.bc[buf][(tid % G) + G * k][w.st_t] = make_float2(Bv[k], Cv[k]);
-  s.hx[buf][tid % G][w.st_t] = make_float2(dt, xv);
-  s.hz[buf][tid % G][w.st_t] = r.z;
-}
-
 // This lane's step (lane%16) of its channel (tid/16) for the tile in `buf`.
 template <int KS, int FORM>
 __device__ __forceinline__ void take_hold(const ScanSmem<KS>& s, int buf, bool want_z, Hold& hd) {
@@ -236,7 +381,7 @@ __device__ __forceinline__ void take_hold(const ScanSmem<KS>& s, int buf, bool w
   hd.dt = v.x;
   hd.x = v.y;
   hd.xs = FORM == kFormEuler ? v.x * v.y : v.y;
-  hd.z = want_z ? s.hz[buf][tid / G][tid % G] : 0u;
+  hd.z = want_z ? s.hz[buf][tid / G][tid % G] : 0.f;
 }
 
 // One step (step T of the tile) of one lane's KS states; returns the lane's
@@ -298,9 +443,9 @@ __device__ __forceinline__ void scan_blocks(const ScanSmem<KS>& s, float* prow, 
 }
 
 // Finalize a tile: lane j of the row takes step j: y = (sum_n w_n partial_n +
-// D x) * silu(z), w_n = 1/A_n in the g form, else 1.  pcol: the lane's
-// (channel, step) column in state row 0 of the partials.
-template <bool BF16, int KS, int FORM>
+// D x) * silu(z), w_n = 1/A_n in the g form, else 1, into yb[buf].  pcol: the
+// lane's (channel, step) column in state row 0 of the partials.
+template <int KS, int FORM>
 __device__ __forceinline__ void finalize_tile(ScanSmem<KS>& s, int buf, const float* pcol, const float (&fA)[G],
                                               float Dk, const Hold& hd, bool want_z) {
   float acc = 0.f;
@@ -311,85 +456,72 @@ __device__ __forceinline__ void finalize_tile(ScanSmem<KS>& s, int buf, const fl
     else acc += v;
   }
   float v = __builtin_fmaf(Dk, hd.x, acc);
-  if (want_z) {
-    const float zf = raw2f<BF16>(hd.z);
-    v *= zf * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zf * kLog2e));
-  }
+  if (want_z) v *= hd.z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-hd.z * kLog2e));
   s.yb[buf][threadIdx.x / G][threadIdx.x % G] = v;
-}
-
-// Store tile `it` (finalized into yb[buf] before the last barrier) row-wise:
-// thread (t, c) = (tid/16, tid%16) stores step t of channel c.
-template <bool BF16, int KS>
-__device__ __forceinline__ void store_y(const ScanSmem<KS>& s, int buf, Walk<KS>& w, int it) {
-  const float v = s.yb[buf][threadIdx.x % G][w.st_t];
-  const bool row_ok = it < w.ntiles - 1 || w.st_t < w.last_rows;
-  if (row_ok && w.st_ch_ok) {
-    if (w.y_f32 || !BF16)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc(w.y, false), (int)w.o.y, 0, 0);
-    else
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rsrc(w.y, false), (int)w.o.y,
-                                            0, 0);
-  }
-  advance(w.y);
 }
 
 // The walk over the stretch, for one update form.  MODE 0 writes y;
 // MODE 1 only carries the state (from 0) and this lane's share of the sum of
 // delta (the steps it holds).
-template <bool BF16, int KS, int MODE, int FORM>
-__device__ __forceinline__ void walk(ScanSmem<KS>& s, Walk<KS>& w, float (&h)[KS], const Lane<KS>& ln,
+template <class L, int KS, int MODE, int FORM>
+__device__ __forceinline__ void walk(ScanSmem<KS>& s, L& ld, const Tiles& tl, float (&h)[KS], const Lane<KS>& ln,
                                      const float (&fA)[G], float Dk, bool want_z, float& sum_dt) {
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, sg = tid % G;
   float* prow = &s.part[wave][sg][G * (lane / G)];
   const float* pcol = &s.part[wave][0][lane];
-  // Loads run two tiles ahead of use: ra/rb hold the tiles with it & 1 == 0/1.
-  Raw<KS> ra, rb;
+  typename L::Set ra, rb;
   Hold hd;
-  auto load = [&](int it, Raw<KS>& r) {
-    if (want_z) load_tile<BF16, KS, true>(w, it, r);
-    else load_tile<BF16, KS, false>(w, it, r);
-  };
-  load(0, ra);
-  stage_tile<BF16, KS>(s, 0, w, 0, ra);
-  if (w.ntiles > 1) load(1, rb);
-  if (w.ntiles > 2) load(2, ra);
+  // Tiles walked: with two tiles in flight the loop is unrolled by two, so
+  // the count is evened out with an all-padding tile.
+  const int nrun = L::kDepth == 2 ? (tl.ntiles + 1) & ~1 : tl.ntiles;
+  ld.load(tl, 0, ra);
+  ld.stage(s, tl, 0, 0, ra);
+  if constexpr (L::kDepth == 2) {
+    ld.load(tl, 1, rb);
+    ld.load(tl, 2, ra);
+  } else {
+    ld.load(tl, 1, ra);
+  }
   __syncthreads();
   // One tile: take this lane's step, scan, finalize into yb, store the
-  // previous tile's y, stage tile it+1 (held in rn) and refill rn with tile
-  // it+3.
-  auto body = [&](int it, Raw<KS>& rn) {
+  // previous tile's y, stage tile it+1 (held in rn) and refill rn.  Loads
+  // are issued whatever `it` (past the stretch they read nothing): a branch
+  // around them would make the compiler wait for them at once.
+  auto body = [&](int it, typename L::Set& rn) {
     const int buf = it & 1;
     take_hold<KS, FORM>(s, buf, want_z, hd);
     float4 o[2][2][KS];
     read_block<KS>(s, buf, 0, sg, o[0]);
     scan_blocks<KS, FORM, MODE == 0, 0>(s, prow, buf, sg, h, ln, hd, o);
     if (MODE == 0) {
-      finalize_tile<BF16, KS, FORM>(s, buf, pcol, fA, Dk, hd, want_z);
-      if (it > 0) store_y<BF16, KS>(s, buf ^ 1, w, it - 1);
+      finalize_tile<KS, FORM>(s, buf, pcol, fA, Dk, hd, want_z);
+      if (it > 0) ld.store_y(s, tl, buf ^ 1, it - 1);
     } else {
       sum_dt += hd.dt;
     }
-    if (it + 1 < w.ntiles) {
-      stage_tile<BF16, KS>(s, buf ^ 1, w, it + 1, rn);
-      if (it + 3 < w.ntiles) load(it + 3, rn);
-    }
+    if (it + 1 < nrun) ld.stage(s, tl, buf ^ 1, it + 1, rn);
+    ld.load(tl, it + 1 + L::kDepth, rn);
     __syncthreads();
   };
-  for (int it = 0; it < w.ntiles; it += 2) {
-    body(it, rb);
-    if (it + 1 < w.ntiles) body(it + 1, ra);
+  if constexpr (L::kDepth == 2) {
+    for (int it = 0; it < nrun; it += 2) {
+      body(it, rb);
+      body(it + 1, ra);
+    }
+  } else {
+    for (int it = 0; it < nrun; ++it) body(it, ra);
   }
-  if (MODE == 0) store_y<BF16, KS>(s, (w.ntiles - 1) & 1, w, w.ntiles - 1);
+  if (MODE == 0) ld.store_y(s, tl, (nrun - 1) & 1, nrun - 1);
 }
 
 // MODE 0: write y (and h_last / start from h_in).  MODE 1: segment aggregates.
-template <bool BF16, int KS, int MODE>
+template <bool BF16, bool VEC, int KS, int MODE>
 __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, int64_t nseg_run,
                                                   int64_t nblocks_padded) {
   __shared__ ScanSmem<KS> s;
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;  // wave: uniform (SGPR)
   const int chb = tid / G, sg = tid % G;
 
   const int64_t lb = logical_block(nblocks_padded);
@@ -402,13 +534,13 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   const bool d_ok = d < p.D;
   const bool want_z = MODE == 0 && (p.flags & kHasZ);
   const int64_t esz = BF16 ? 2 : 4;
+  const int64_t yesz = (p.y_f32 || !BF16) ? 4 : 2;
 
-  Walk<KS> w;
   const int64_t t_begin = seg * p.seg_len;
   const int64_t t_end = (t_begin + p.seg_len < p.L) ? t_begin + p.seg_len : p.L;
-  w.ntiles = (int)((t_end - t_begin + TT - 1) / TT);
-  w.last_rows = (int)(t_end - t_begin - (int64_t)(w.ntiles - 1) * TT);
-  w.y_f32 = p.y_f32 != 0;
+  Tiles tl;
+  tl.ntiles = (int)((t_end - t_begin + TT - 1) / TT);
+  tl.last_rows = (int)(t_end - t_begin - (int64_t)(tl.ntiles - 1) * TT);
 
   // Per-lane constants of this lane's KS states.
   Lane<KS> ln;
@@ -443,44 +575,63 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   float Dk = 0.f;
   if (MODE == 0 && (p.flags & kHasD) && d_ok) Dk = p.Dskip[d * p.Ds_d];
 
-  // Streams: each starts at element (b, t_begin, d0) (state 0 for B, C) and
-  // advances one tile of rows at a time.  The last tile's range ends at its
-  // last row's last element (channel D-1 or state N-1): lanes of rows past
-  // the stretch, or of channels / states past the end of the tensor's last
-  // row, read zeros.  (Rows past the stretch inside the tensor may also be
-  // read; stage_tile discards them.)
-  const int64_t rows_last = w.last_rows;
-  auto span = [&](const void* base, int64_t sb, int64_t st, int64_t sw, int64_t width, int64_t e, int64_t inner) {
-    Span sp;
-    sp.p = (const char*)base + (b * sb + t_begin * st + inner) * e;
-    sp.step = (int32_t)(TT * st * e);
-    sp.last_range = (uint32_t)(((rows_last - 1) * st + (width - 1) * sw + 1) * e);
-    return sp;
-  };
-  w.x = span(p.x, p.xs_b, p.xs_t, 1, p.D - d0, esz, d0);
-  w.dl = span(p.delta, p.ds_b, p.ds_t, 1, p.D - d0, esz, d0);
-  w.z = want_z ? span(p.z, p.zs_b, p.zs_t, 1, p.D - d0, esz, d0) : w.x;
-  w.B = span(p.B, p.Bs_b, p.Bs_t, p.Bs_n, p.N, esz, 0);
-  w.C = span(p.C, p.Cs_b, p.Cs_t, p.Cs_n, p.N, esz, 0);
-  const int64_t yesz = (p.y_f32 || !BF16) ? 4 : 2;
-  w.y = MODE == 0 ? span(p.y, p.ys_b, p.ys_t, 1, p.D - d0, yesz, d0) : w.x;
-
-  // Row-wise role: thread (t, c) = (tid/16, tid%16) loads x, delta, z of
-  // step t, channel c and stores y the same way; for B and C it loads state
-  // c + 16k of step t (states >= N read state 0 and are zeroed when staged).
-  w.st_t = tid / G;
-  w.st_ch_ok = d0 + sg < p.D;
-  w.o.x = (uint32_t)((w.st_t * p.xs_t + sg) * esz);
-  w.o.dl = (uint32_t)((w.st_t * p.ds_t + sg) * esz);
-  w.o.z = want_z ? (uint32_t)((w.st_t * p.zs_t + sg) * esz) : 0u;
-  w.o.y = MODE == 0 ? (uint32_t)((w.st_t * p.ys_t + sg) * yesz) : 0u;
+  // Streams: each starts at row t_begin of batch row b and advances one tile
+  // of rows at a time.  The last tile's range ends at its last row's last
+  // element (channel D-1 or state N-1 of the span): lanes of rows past the
+  // stretch, or of channels / states past the end of the tensor's last row,
+  // read zeros.  (Rows past the stretch inside the tensor may also be read;
+  // the loaders stage them as zeros.)
+  const int rows_last = tl.last_rows;
+  typename std::conditional<VEC, VecLoader<BF16, KS>, ElemLoader<BF16, KS>>::type ld;
+  if constexpr (VEC) {
+    ld.r = lane / 4;
+    ld.q = lane % 4;
+    ld.y_f32 = p.y_f32 != 0;
 #pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    const int n = sg + G * k;
-    w.o.bc_ok[k] = n < p.N;
-    const int64_t nn = n < p.N ? n : 0;
-    w.o.B[k] = (uint32_t)((w.st_t * p.Bs_t + nn * p.Bs_n) * esz);
-    w.o.C[k] = (uint32_t)((w.st_t * p.Cs_t + nn * p.Cs_n) * esz);
+    for (int j = 0; j < ld.kSlots; ++j) {
+      const int kd = wave + 4 * j;
+      ld.place(s, j, kd, (int)p.N);
+      const void* base = p.x;
+      int64_t sb = 0, st = 0, col0 = 0, width = 0;
+      bool live = kd < ld.kPieces;
+      if (kd == 0) { base = p.x; sb = p.xs_b; st = p.xs_t; col0 = d0; width = p.D - d0; }
+      else if (kd == 1) { base = p.delta; sb = p.ds_b; st = p.ds_t; col0 = d0; width = p.D - d0; }
+      else if (kd == 2) { base = want_z ? p.z : p.x; sb = p.zs_b; st = p.zs_t; col0 = d0; width = p.D - d0; live = want_z; }
+      else if (kd < 3 + KS) { base = p.B; sb = p.Bs_b; st = p.Bs_t; col0 = 16 * (kd - 3); width = p.N - col0; }
+      else if (kd < ld.kPieces) { base = p.C; sb = p.Cs_b; st = p.Cs_t; col0 = 16 * (kd - 3 - KS); width = p.N - col0; }
+      width = width < 16 ? width : 16;
+      live = live && width > 0;
+      ld.sp[j] = make_span(base, b * sb + t_begin * st + col0, st, 1, width, esz, rows_last, live);
+      ld.voff[j] = (uint32_t)((ld.r * st + 4 * ld.q) * esz);
+    }
+    ld.y = make_span(MODE == 0 ? p.y : p.x, b * p.ys_b + t_begin * p.ys_t + d0, p.ys_t, 1, p.D - d0, yesz,
+                     rows_last, MODE == 0);
+    ld.oy = (uint32_t)((ld.r * p.ys_t + 4 * ld.q) * yesz);
+    ld.y_ok = d0 + 4 * ld.q < p.D;
+  } else {
+    ld.t = tid / G;
+    ld.ch_ok = d0 + sg < p.D;
+    ld.y_f32 = p.y_f32 != 0;
+    ld.x = make_span(p.x, b * p.xs_b + t_begin * p.xs_t + d0, p.xs_t, 1, p.D - d0, esz, rows_last, true);
+    ld.dl = make_span(p.delta, b * p.ds_b + t_begin * p.ds_t + d0, p.ds_t, 1, p.D - d0, esz, rows_last, true);
+    ld.z = make_span(want_z ? p.z : p.x, b * p.zs_b + t_begin * p.zs_t + d0, p.zs_t, 1, p.D - d0, esz, rows_last,
+                     want_z);
+    ld.B = make_span(p.B, b * p.Bs_b + t_begin * p.Bs_t, p.Bs_t, p.Bs_n, p.N, esz, rows_last, true);
+    ld.C = make_span(p.C, b * p.Cs_b + t_begin * p.Cs_t, p.Cs_t, p.Cs_n, p.N, esz, rows_last, true);
+    ld.y = make_span(MODE == 0 ? p.y : p.x, b * p.ys_b + t_begin * p.ys_t + d0, p.ys_t, 1, p.D - d0, yesz,
+                     rows_last, MODE == 0);
+    ld.ox = (uint32_t)((ld.t * p.xs_t + sg) * esz);
+    ld.odl = (uint32_t)((ld.t * p.ds_t + sg) * esz);
+    ld.oz = (uint32_t)((ld.t * p.zs_t + sg) * esz);
+    ld.oy = (uint32_t)((ld.t * p.ys_t + sg) * yesz);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const int n = sg + G * k;
+      ld.bc_ok[k] = n < p.N;
+      const int64_t nn = n < p.N ? n : 0;
+      ld.oB[k] = (uint32_t)((ld.t * p.Bs_t + nn * p.Bs_n) * esz);
+      ld.oC[k] = (uint32_t)((ld.t * p.Cs_t + nn * p.Cs_n) * esz);
+    }
   }
 
   int form;
@@ -504,15 +655,15 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
     }
 #pragma unroll
     for (int k = 0; k < KS; ++k) h[k] *= Av[k];  // g = A h
-    walk<BF16, KS, MODE, kFormG>(s, w, h, ln, fA, Dk, want_z, sum_dt);
+    walk<decltype(ld), KS, MODE, kFormG>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt);
 #pragma unroll
     for (int k = 0; k < KS; ++k) h[k] *= ln.iA[k];  // h = g / A
   } else if (form == kFormEuler) {
-    walk<BF16, KS, MODE, kFormEuler>(s, w, h, ln, fA, Dk, want_z, sum_dt);
+    walk<decltype(ld), KS, MODE, kFormEuler>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt);
   } else if (form == kFormHZero) {
-    walk<BF16, KS, MODE, kFormHZero>(s, w, h, ln, fA, Dk, want_z, sum_dt);
+    walk<decltype(ld), KS, MODE, kFormHZero>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt);
   } else {
-    walk<BF16, KS, MODE, kFormH>(s, w, h, ln, fA, Dk, want_z, sum_dt);
+    walk<decltype(ld), KS, MODE, kFormH>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt);
   }
 
   if (MODE == 1) {
@@ -556,34 +707,45 @@ __global__ __launch_bounds__(256) void scan_combine_kernel(ScanParams p) {
   }
 }
 
-template <bool BF16, int KS>
+template <bool BF16, bool VEC, int KS>
 hipError_t launch_ks(const ScanParams& p, hipStream_t stream) {
   const int64_t n_dblk = (p.D + CH - 1) / CH;
   auto padded = [](int64_t n) { return (n + 7) / 8 * 8; };
   if (p.n_seg > 1) {
     const int64_t nb = n_dblk * (p.n_seg - 1) * p.batch;
-    hipLaunchKernelGGL((scan_kernel<BF16, KS, 1>), dim3((unsigned)padded(nb)), dim3(NT), 0, stream, p, n_dblk,
+    hipLaunchKernelGGL((scan_kernel<BF16, VEC, KS, 1>), dim3((unsigned)padded(nb)), dim3(NT), 0, stream, p, n_dblk,
                        (int64_t)(p.n_seg - 1), padded(nb));
     const int64_t ncomb = p.batch * p.D * p.N;
     hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((ncomb + 255) / 256)), dim3(256), 0, stream, p);
   }
   const int64_t nb = n_dblk * p.n_seg * p.batch;
-  hipLaunchKernelGGL((scan_kernel<BF16, KS, 0>), dim3((unsigned)padded(nb)), dim3(NT), 0, stream, p, n_dblk,
+  hipLaunchKernelGGL((scan_kernel<BF16, VEC, KS, 0>), dim3((unsigned)padded(nb)), dim3(NT), 0, stream, p, n_dblk,
                      (int64_t)p.n_seg, padded(nb));
   return hipGetLastError();
 }
 
-template <bool BF16>
+template <bool BF16, bool VEC>
 hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
-  if (p.N <= G * 1) return launch_ks<BF16, 1>(p, stream);
-  if (p.N <= G * 2) return launch_ks<BF16, 2>(p, stream);
-  return launch_ks<BF16, 4>(p, stream);
+  if (p.N <= G * 1) return launch_ks<BF16, VEC, 1>(p, stream);
+  if (p.N <= G * 2) return launch_ks<BF16, VEC, 2>(p, stream);
+  return launch_ks<BF16, VEC, 4>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_selective_scan(const ScanParams& p, hipStream_t stream) {
-  return p.io_bf16 ? launch_io<true>(p, stream) : launch_io<false>(p, stream);
+  // Tile pieces load 4 consecutive elements per lane: every row of x, delta,
+  // z, y must start 4-element aligned, and B, C must be contiguous over states.
+  const int64_t e = p.io_bf16 ? 2 : 4;
+  const int64_t ye = (p.y_f32 || !p.io_bf16) ? 4 : 2;
+  auto al = [](const void* q, int64_t bytes) { return q == nullptr || ((uintptr_t)q % (uintptr_t)bytes) == 0; };
+  bool vec = p.D % 4 == 0 && p.N % 4 == 0 && al(p.x, 4 * e) && al(p.delta, 4 * e) && al(p.y, 4 * ye) &&
+             al(p.B, 4 * e) && al(p.C, 4 * e) && p.xs_b % 4 == 0 && p.xs_t % 4 == 0 && p.ds_b % 4 == 0 &&
+             p.ds_t % 4 == 0 && p.ys_b % 4 == 0 && p.ys_t % 4 == 0 && p.Bs_n == 1 && p.Cs_n == 1 &&
+             p.Bs_b % 4 == 0 && p.Bs_t % 4 == 0 && p.Cs_b % 4 == 0 && p.Cs_t % 4 == 0;
+  if (p.flags & kHasZ) vec = vec && al(p.z, 4 * e) && p.zs_b % 4 == 0 && p.zs_t % 4 == 0;
+  if (p.io_bf16) return vec ? launch_io<true, true>(p, stream) : launch_io<true, false>(p, stream);
+  return vec ? launch_io<false, true>(p, stream) : launch_io<false, false>(p, stream);
 }
 
 }  // namespace ssm
