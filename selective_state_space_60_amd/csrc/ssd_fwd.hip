@@ -288,6 +288,10 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
   __shared__ float A2[Q];                                      // A_cum * log2(e)
   __shared__ float tj[Q];                                      // exp(A_cum[j|31] - A_cum[j])
   __shared__ float bj[Q];                                      // beta
+  // S_in (64 x 64 bf16), row p in 8 chunks of 8 values; chunk q of row p is
+  // stored at chunk q ^ (p % 8) so the inter-chunk reads (16 rows, one chunk)
+  // spread over the banks.
+  __shared__ __attribute__((aligned(16))) uint4 Ss[64][8];
 
   int64_t bid = blockIdx.x;
   const int64_t h = bid % p.H;
@@ -321,6 +325,11 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) Cop[s][ks] = as_bf16x8(*(const uint4*)(Cb + tr * p.Cs_t + 32 * ks + 8 * lq));
   }
+  // S_in of this (chunk, head): 512 16-byte pieces
+  const uint16_t* Sp = (const uint16_t*)p.S_in + ((b * p.nchunks + c) * p.H + h) * 4096;
+  uint4 rs[512 / NTH];
+#pragma unroll
+  for (int u = 0; u < 512 / NTH; ++u) rs[u] = *(const uint4*)(Sp + 8 * (tid + NTH * u));
   const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
   const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
   for (int t = tid; t < Q; t += NTH) {
@@ -328,6 +337,11 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
     bj[t] = be[t];
   }
   __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 512 / NTH; ++u) {
+    const int e = tid + NTH * u, row = e / 8, cq = e % 8;
+    Ss[row][cq ^ (row % 8)] = rs[u];
+  }
   for (int t = tid; t < Q; t += NTH) tj[t] = __builtin_amdgcn_exp2f(A2[t | 31] - A2[t]);
   store_pairs_transposed<Q, NTH, kScanColMaj>(lx, &xT[0][0], PX, t0, p.L, bj);
 #pragma unroll
@@ -413,13 +427,25 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
       for (int mt = 0; mt < 4; ++mt) acc[s][mt] = mfma(aX[mt], bop, acc[s][mt]);
     }
   }
+  // x rows of the epilogue (D x), loaded now so the inter-chunk term hides their latency
+  const float Dh = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
+  uint2 xv[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int64_t ti = t0 + 16 * kst[s] + lr;
+    const int64_t tr = ti < p.L ? ti : p.L - 1;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      xv[s][mt] = p.Dskip ? *(const uint2*)((const uint16_t*)p.x + b * p.xs_b + tr * p.xs_t + h * p.xs_h + 16 * mt + 4 * lq)
+                          : make_uint2(0, 0);
+  }
   // inter-chunk term: Y^T[p][i] += exp(A_cum_i) sum_n S_in[p][n] C[i][n]
   {
-    const uint16_t* Sp = (const uint16_t*)p.S_in + ((b * p.nchunks + c) * p.H + h) * 4096;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const bf16x8 a0 = as_bf16x8(*(const uint4*)(Sp + (16 * mt + lr) * 64 + 8 * lq));
-      const bf16x8 a1 = as_bf16x8(*(const uint4*)(Sp + (16 * mt + lr) * 64 + 32 + 8 * lq));
+      const int row = 16 * mt + lr;
+      const bf16x8 a0 = as_bf16x8(Ss[row][lq ^ (row % 8)]);
+      const bf16x8 a1 = as_bf16x8(Ss[row][(lq + 4) ^ (row % 8)]);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -431,28 +457,19 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
     }
   }
   // epilogue: + D x, store y[i][p0..p0+3]
-  const float Dh = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int64_t ti = t0 + 16 * kst[s] + lr;
-    const bool ok = ti < p.L;
-    const int64_t tr = ok ? ti : p.L - 1;
-    uint2 xv[4];
-    if (p.Dskip) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        xv[mt] = *(const uint2*)((const uint16_t*)p.x + b * p.xs_b + tr * p.xs_t + h * p.xs_h + 16 * mt + 4 * lq);
-    }
-    if (!ok) continue;
+    if (ti >= p.L) continue;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int p0 = 16 * mt + 4 * lq;
       float o[4] = {acc[s][mt][0], acc[s][mt][1], acc[s][mt][2], acc[s][mt][3]};
       if (p.Dskip) {
-        o[0] = __builtin_fmaf(Dh, __uint_as_float(xv[mt].x << 16), o[0]);
-        o[1] = __builtin_fmaf(Dh, __uint_as_float(xv[mt].x & 0xFFFF0000u), o[1]);
-        o[2] = __builtin_fmaf(Dh, __uint_as_float(xv[mt].y << 16), o[2]);
-        o[3] = __builtin_fmaf(Dh, __uint_as_float(xv[mt].y & 0xFFFF0000u), o[3]);
+        o[0] = __builtin_fmaf(Dh, __uint_as_float(xv[s][mt].x << 16), o[0]);
+        o[1] = __builtin_fmaf(Dh, __uint_as_float(xv[s][mt].x & 0xFFFF0000u), o[1]);
+        o[2] = __builtin_fmaf(Dh, __uint_as_float(xv[s][mt].y << 16), o[2]);
+        o[3] = __builtin_fmaf(Dh, __uint_as_float(xv[s][mt].y & 0xFFFF0000u), o[3]);
       }
       const int64_t off = b * p.ys_b + ti * p.ys_t + h * p.ys_h + p0;
       if (p.y_f32) *(float4*)((float*)p.y + off) = make_float4(o[0], o[1], o[2], o[3]);
