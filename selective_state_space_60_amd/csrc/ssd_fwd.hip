@@ -36,6 +36,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -195,7 +197,6 @@ __device__ __forceinline__ void store_pairs_transposed(const PairLoads<ROWS, NTH
 // ------------------------------------------------------- s2 chunk state
 
 constexpr bool kStateColMaj = false;  // staging task map of chunk_state
-constexpr bool kScanColMaj = false;   // staging task map of chunk_scan
 
 template <int Q>
 __global__ __launch_bounds__(256) void chunk_state_kernel(SSDParams p) {
@@ -276,18 +277,26 @@ __global__ __launch_bounds__(256) void state_passing_kernel(SSDParams p) {
 // strips k = wv and k = Q/16 - 1 - wv, which balances the causal work.
 // Accumulators hold Y^T[p][i]: lane -> p = 16*mt + 4*(l/16) + r,
 // i = 16*k + l%16.
+//
+// x is staged in LDS as it is laid out in memory (row j = step, 64 values p)
+// and read as the A operand of Y^T += X^T G'^T with the LDS transpose read
+// (ds_read_b64_tr_b16): within each group of 16 lanes, output lane m, slot i
+// receives element m%4 of the 4 values read by lane 4i + m/4 (checked on the
+// device).  Lane (g, 4a + b) of group g therefore reads x[j0 + 4g + a][16mt +
+// 4b .. +3], and output lane (g, m) gets x[j0 + 4g + i][16mt + m], i = 0..3:
+// four consecutive steps of one p, the contraction slots G'^T's layout needs.
+// beta_j is applied to G' (it multiplies the decay factor of column j).
 template <int Q>
 __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
-  constexpr int NTH = 2 * Q;     // threads
+  constexpr int NTH = 2 * Q;        // threads
   constexpr int NSTRIP = Q / 16;
-  constexpr int PX = Q + 8;      // xT pitch
-  constexpr int PB = 64 + 8;     // Bs pitch
-  constexpr int NTB = Q * 8 / NTH;  // B (row, 8 columns) tasks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t xT[64][PX];  // (beta x)^T: [p][j]
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][PB];   // B rows: [j][n]
-  __shared__ float A2[Q];                                      // A_cum * log2(e)
-  __shared__ float tj[Q];                                      // exp(A_cum[j|31] - A_cum[j])
-  __shared__ float bj[Q];                                      // beta
+  constexpr int PR = 64 + 4;        // row pitch (bf16) of the staged x and B rows
+  constexpr int NTX = Q * 8 / NTH;  // (row, 8 values) pieces of x and of B per thread
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][PR];  // x rows: [j][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][PR];  // B rows: [j][n]
+  __shared__ float A2[Q];                                     // A_cum * log2(e)
+  __shared__ float tb[Q];                                     // exp(A_cum[j|31] - A_cum[j]) * beta_j
+  __shared__ float bj[Q];                                     // beta
   // S_in (64 x 64 bf16), row p in 8 chunks of 8 values; chunk q of row p is
   // stored at chunk q ^ (p % 8) so the inter-chunk reads (16 rows, one chunk)
   // spread over the banks.
@@ -305,15 +314,15 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
   const int kst[2] = {wv, NSTRIP - 1 - wv};
 
   // --- issue the staging loads and the C operands before using any
-  PairLoads<Q, NTH> lx;
-  load_pairs<Q, NTH, kScanColMaj>(lx, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
-  uint4 rb[NTB];
+  uint4 rx[NTX], rb[NTX];
+  const uint16_t* Xsrc = (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h;
   const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
 #pragma unroll
-  for (int u = 0; u < NTB; ++u) {
+  for (int u = 0; u < NTX; ++u) {
     const int task = tid + NTH * u;
     const int j = task / 8, cb = (task % 8) * 8;
     const int64_t tr = t0 + j < p.L ? t0 + j : p.L - 1;
+    rx[u] = *(const uint4*)(Xsrc + tr * p.xs_t + cb);
     rb[u] = *(const uint4*)(Bsrc + tr * p.Bs_t + cb);
   }
   bf16x8 Cop[2][2];  // C operand of each strip: C[i][32*ks + 8*lq .. +7]
@@ -337,18 +346,20 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
     bj[t] = be[t];
   }
   __syncthreads();
+  for (int t = tid; t < Q; t += NTH) tb[t] = __builtin_amdgcn_exp2f(A2[t | 31] - A2[t]) * bj[t];
+  // rows at or past L hold zeros
+#pragma unroll
+  for (int u = 0; u < NTX; ++u) {
+    const int task = tid + NTH * u;
+    const int j = task / 8, cb = (task % 8) * 8;
+    const bool ok = t0 + j < p.L;
+    *(uint4*)&Xs[j][cb] = ok ? rx[u] : make_uint4(0, 0, 0, 0);
+    *(uint4*)&Bs[j][cb] = ok ? rb[u] : make_uint4(0, 0, 0, 0);
+  }
 #pragma unroll
   for (int u = 0; u < 512 / NTH; ++u) {
     const int e = tid + NTH * u, row = e / 8, cq = e % 8;
     Ss[row][cq ^ (row % 8)] = rs[u];
-  }
-  for (int t = tid; t < Q; t += NTH) tj[t] = __builtin_amdgcn_exp2f(A2[t | 31] - A2[t]);
-  store_pairs_transposed<Q, NTH, kScanColMaj>(lx, &xT[0][0], PX, t0, p.L, bj);
-#pragma unroll
-  for (int u = 0; u < NTB; ++u) {
-    const int task = tid + NTH * u;
-    const int j = task / 8, cb = (task % 8) * 8;
-    *(uint4*)&Bs[j][cb] = t0 + j < p.L ? rb[u] : make_uint4(0, 0, 0, 0);
   }
   // C rows past L must not contribute
 #pragma unroll
@@ -361,6 +372,8 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // transpose-read address of this lane: row 4*lq + (lr / 4), values 4*(lr % 4) .. +3 of a 16-wide p block
+  const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
   // intra-chunk term over 32-step blocks jb up to the later strip's diagonal
   const int jb_last = (16 * kst[1]) / 32;
   for (int jb = 0; jb <= jb_last; ++jb) {
@@ -371,13 +384,14 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) aB[jt][ks] = as_bf16x8(*(const uint4*)&Bs[j0 + 16 * jt + lr][32 * ks + 8 * lq]);
-    // A operands of Y^T += X~^T G^T: rows p, contraction slots in G^T's layout
+    // A operands of Y^T += X^T G'^T: rows p, contraction slots in G^T's layout
     bf16x8 aX[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const uint2 lo = *(const uint2*)&xT[16 * mt + lr][j0 + 4 * lq];
-      const uint2 hi = *(const uint2*)&xT[16 * mt + lr][j0 + 16 + 4 * lq];
-      aX[mt] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Xs[j0 + tr_row][16 * mt + tr_col]);
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Xs[j0 + 16 + tr_row][16 * mt + tr_col]);
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      aX[mt] = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -400,7 +414,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
         const float vi = __builtin_amdgcn_exp2f(A2[i] - A2[j0 + 31]);
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
-          const float4 t4 = *(const float4*)&tj[j0 + 16 * jt + 4 * lq];
+          const float4 t4 = *(const float4*)&tb[j0 + 16 * jt + 4 * lq];
           v[4 * jt + 0] = gt[jt][0] * (t4.x * vi);
           v[4 * jt + 1] = gt[jt][1] * (t4.y * vi);
           v[4 * jt + 2] = gt[jt][2] * (t4.z * vi);
@@ -411,13 +425,15 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
           const float4 a4 = *(const float4*)&A2[j0 + 16 * jt + 4 * lq];
+          const float4 b4 = *(const float4*)&bj[j0 + 16 * jt + 4 * lq];
           const float aj[4] = {a4.x, a4.y, a4.z, a4.w};
+          const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = j0 + 16 * jt + 4 * lq + r;
             const float d = j <= i ? ai - aj[r] : 0.f;
             const float e = __builtin_amdgcn_exp2f(d);
-            v[4 * jt + r] = j <= i ? gt[jt][r] * e : 0.f;
+            v[4 * jt + r] = j <= i ? gt[jt][r] * (e * bb[r]) : 0.f;
           }
         }
       }
@@ -427,50 +443,37 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
       for (int mt = 0; mt < 4; ++mt) acc[s][mt] = mfma(aX[mt], bop, acc[s][mt]);
     }
   }
-  // x rows of the epilogue (D x), loaded now so the inter-chunk term hides their latency
-  const float Dh = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
-  uint2 xv[2][4];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int64_t ti = t0 + 16 * kst[s] + lr;
-    const int64_t tr = ti < p.L ? ti : p.L - 1;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      xv[s][mt] = p.Dskip ? *(const uint2*)((const uint16_t*)p.x + b * p.xs_b + tr * p.xs_t + h * p.xs_h + 16 * mt + 4 * lq)
-                          : make_uint2(0, 0);
-  }
   // inter-chunk term: Y^T[p][i] += exp(A_cum_i) sum_n S_in[p][n] C[i][n]
-  {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int row = 16 * mt + lr;
-      const bf16x8 a0 = as_bf16x8(Ss[row][lq ^ (row % 8)]);
-      const bf16x8 a1 = as_bf16x8(Ss[row][(lq + 4) ^ (row % 8)]);
+  for (int mt = 0; mt < 4; ++mt) {
+    const int row = 16 * mt + lr;
+    const bf16x8 a0 = as_bf16x8(Ss[row][lq ^ (row % 8)]);
+    const bf16x8 a1 = as_bf16x8(Ss[row][(lq + 4) ^ (row % 8)]);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-        a = mfma(a0, Cop[s][0], a);
-        a = mfma(a1, Cop[s][1], a);
-        const float ei = __builtin_amdgcn_exp2f(A2[16 * kst[s] + lr]);
-        acc[s][mt] += a * ei;
-      }
+    for (int s = 0; s < 2; ++s) {
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+      a = mfma(a0, Cop[s][0], a);
+      a = mfma(a1, Cop[s][1], a);
+      const float ei = __builtin_amdgcn_exp2f(A2[16 * kst[s] + lr]);
+      acc[s][mt] += a * ei;
     }
   }
-  // epilogue: + D x, store y[i][p0..p0+3]
+  // epilogue: + D x (x from the staged rows), store y[i][p0..p0+3]
+  const float Dh = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int64_t ti = t0 + 16 * kst[s] + lr;
+    const int il = 16 * kst[s] + lr;
+    const int64_t ti = t0 + il;
     if (ti >= p.L) continue;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int p0 = 16 * mt + 4 * lq;
+      const uint2 xv = *(const uint2*)&Xs[il][p0];
       float o[4] = {acc[s][mt][0], acc[s][mt][1], acc[s][mt][2], acc[s][mt][3]};
-      if (p.Dskip) {
-        o[0] = __builtin_fmaf(Dh, __uint_as_float(xv[s][mt].x << 16), o[0]);
-        o[1] = __builtin_fmaf(Dh, __uint_as_float(xv[s][mt].x & 0xFFFF0000u), o[1]);
-        o[2] = __builtin_fmaf(Dh, __uint_as_float(xv[s][mt].y << 16), o[2]);
-        o[3] = __builtin_fmaf(Dh, __uint_as_float(xv[s][mt].y & 0xFFFF0000u), o[3]);
-      }
+      o[0] = __builtin_fmaf(Dh, __uint_as_float(xv.x << 16), o[0]);
+      o[1] = __builtin_fmaf(Dh, __uint_as_float(xv.x & 0xFFFF0000u), o[1]);
+      o[2] = __builtin_fmaf(Dh, __uint_as_float(xv.y << 16), o[2]);
+      o[3] = __builtin_fmaf(Dh, __uint_as_float(xv.y & 0xFFFF0000u), o[3]);
       const int64_t off = b * p.ys_b + ti * p.ys_t + h * p.ys_h + p0;
       if (p.y_f32) *(float4*)((float*)p.y + off) = make_float4(o[0], o[1], o[2], o[3]);
       else *(uint2*)((uint16_t*)p.y + off) = make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
