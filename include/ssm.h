@@ -183,7 +183,8 @@ ssm_status ssm_ssd_chunk_fwd(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, void*
 
 /* The four SSD steps, each one kernel launch, exposed so that each can be
  * checked and timed on its own.  nchunks = ceil(seqlen / chunk); Lp =
- * nchunks * chunk.  Intermediates are contiguous device buffers:
+ * nchunks * chunk.  Intermediates are contiguous device buffers, 16-byte
+ * aligned (SSM_ERR_ALIGN otherwise):
  *   A_cum  : (batch, nheads, Lp) F32  -- inclusive cumulative sum of
  *            delta*A inside each chunk (entries past seqlen unspecified)
  *   beta   : (batch, nheads, Lp) F32  -- expm1(delta*A)/A (delta if A == 0),

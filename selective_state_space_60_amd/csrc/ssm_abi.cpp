@@ -420,7 +420,7 @@ ssm_status ssm_ssd_chunk_cumsum(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, fl
   if (s) return s;
   if ((s = validate_ssd_ptrs(d, p, kNeedDelta))) return s;
   if (!A_cum || !beta) return SSM_ERR_NULL;
-  if (!aligned(A_cum, 4) || !aligned(beta, 4)) return SSM_ERR_ALIGN;
+  if (!aligned(A_cum, 16) || !aligned(beta, 16)) return SSM_ERR_ALIGN;
   const SSDPlan pl = plan_ssd(*d);
   ssm::SSDParams q = make_ssd_params(d, p, pl);
   q.A_cum = A_cum;
@@ -434,7 +434,7 @@ ssm_status ssm_ssd_chunk_state(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, con
   if (s) return s;
   if ((s = validate_ssd_ptrs(d, p, kNeedX | kNeedB))) return s;
   if (!A_cum || !beta || !states) return SSM_ERR_NULL;
-  if (!aligned(A_cum, 4) || !aligned(beta, 4) || !aligned(states, 16)) return SSM_ERR_ALIGN;
+  if (!aligned(A_cum, 16) || !aligned(beta, 16) || !aligned(states, 16)) return SSM_ERR_ALIGN;
   const SSDPlan pl = plan_ssd(*d);
   ssm::SSDParams q = make_ssd_params(d, p, pl);
   q.A_cum = (float*)A_cum;
@@ -449,7 +449,7 @@ ssm_status ssm_ssd_state_passing(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, c
   if (s) return s;
   if ((s = validate_ssd_ptrs(d, p, 0))) return s;
   if (!A_cum || !states || !S_in) return SSM_ERR_NULL;
-  if (!aligned(A_cum, 4) || !aligned(states, 16) || !aligned(S_in, 16)) return SSM_ERR_ALIGN;
+  if (!aligned(A_cum, 16) || !aligned(states, 16) || !aligned(S_in, 16)) return SSM_ERR_ALIGN;
   const SSDPlan pl = plan_ssd(*d);
   ssm::SSDParams q = make_ssd_params(d, p, pl);
   q.A_cum = (float*)A_cum;
@@ -464,7 +464,7 @@ ssm_status ssm_ssd_chunk_scan(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, cons
   if (s) return s;
   if ((s = validate_ssd_ptrs(d, p, kNeedX | kNeedB | kNeedC | kNeedY))) return s;
   if (!A_cum || !beta || !S_in) return SSM_ERR_NULL;
-  if (!aligned(A_cum, 4) || !aligned(beta, 4) || !aligned(S_in, 16)) return SSM_ERR_ALIGN;
+  if (!aligned(A_cum, 16) || !aligned(beta, 16) || !aligned(S_in, 16)) return SSM_ERR_ALIGN;
   const SSDPlan pl = plan_ssd(*d);
   ssm::SSDParams q = make_ssd_params(d, p, pl);
   q.A_cum = (float*)A_cum;
