@@ -148,124 +148,90 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(SSDParams p) {
   }
 }
 
-// Global loads of a time-major (ROWS x 64) bf16 tile for staging it
-// transposed in LDS, all issued before any is used.  A task is (row pair jp,
-// 8-column block cb).  Two task maps: ROWMAJ (t -> jp = t / 8, cb = 8*(t % 8))
-// gives coalesced global loads (8 lanes read one 128-byte row); COLMAJ
-// (t -> jp = t % (ROWS/2), cb = 8*(t / (ROWS/2))) makes the transposed LDS
-// stores of a wave land on consecutive dwords.  NTH threads, NT = 4*ROWS/NTH
-// tasks each.  Rows at or past L read row L-1 (a valid address) and are
-// zeroed when written to LDS.
-template <int ROWS, int NTH>
-struct PairLoads {
-  static constexpr int NT = 4 * ROWS / NTH;
-  uint4 r0[NT], r1[NT];
-};
-
-template <int ROWS, bool COLMAJ>
-__device__ __forceinline__ void pair_task(int task, int& j, int& cb) {
-  if (COLMAJ) {
-    j = 2 * (task % (ROWS / 2));
-    cb = 8 * (task / (ROWS / 2));
-  } else {
-    j = 2 * (task / 8);
-    cb = 8 * (task % 8);
-  }
-}
-
-template <int ROWS, int NTH, bool COLMAJ>
-__device__ __forceinline__ void load_pairs(PairLoads<ROWS, NTH>& ld, const uint16_t* src, int64_t row_stride,
-                                           int64_t t0, int64_t L) {
-#pragma unroll
-  for (int u = 0; u < PairLoads<ROWS, NTH>::NT; ++u) {
-    const int task = threadIdx.x + NTH * u;
-    int j, cb;
-    pair_task<ROWS, COLMAJ>(task, j, cb);
-    const int64_t ta = t0 + j < L ? t0 + j : L - 1, tb = t0 + j + 1 < L ? t0 + j + 1 : L - 1;
-    ld.r0[u] = *(const uint4*)(src + ta * row_stride + cb);
-    ld.r1[u] = *(const uint4*)(src + tb * row_stride + cb);
-  }
-}
-
-// Write the loaded pairs to LDS transposed, dst[col][j] (row pitch `pitch`),
-// optionally scaled by scale[j] (fp32) and rounded to bf16.
-template <int ROWS, int NTH, bool COLMAJ>
-__device__ __forceinline__ void store_pairs_transposed(const PairLoads<ROWS, NTH>& ld, uint16_t* dst, int pitch,
-                                                       int64_t t0, int64_t L, const float* scale) {
-#pragma unroll
-  for (int u = 0; u < PairLoads<ROWS, NTH>::NT; ++u) {
-    const int task = threadIdx.x + NTH * u;
-    int j, cb;
-    pair_task<ROWS, COLMAJ>(task, j, cb);
-    const bool ok0 = t0 + j < L, ok1 = t0 + j + 1 < L;
-    const uint32_t w0[4] = {ld.r0[u].x, ld.r0[u].y, ld.r0[u].z, ld.r0[u].w};
-    const uint32_t w1[4] = {ld.r1[u].x, ld.r1[u].y, ld.r1[u].z, ld.r1[u].w};
-    if (scale) {
-      const float s0 = scale[j], s1 = scale[j + 1];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // padding rows are zeroed as data, not through the scale (0 * inf)
-        const float v0 = ok0 ? __uint_as_float((i & 1) ? (w0[i / 2] & 0xFFFF0000u) : (w0[i / 2] << 16)) * s0 : 0.f;
-        const float v1 = ok1 ? __uint_as_float((i & 1) ? (w1[i / 2] & 0xFFFF0000u) : (w1[i / 2] << 16)) * s1 : 0.f;
-        *(uint32_t*)(dst + (cb + i) * pitch + j) = pack2(v0, v1);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t a = ok0 ? ((i & 1) ? (w0[i / 2] >> 16) : (w0[i / 2] & 0xFFFFu)) : 0u;
-        const uint32_t c = ok1 ? ((i & 1) ? (w1[i / 2] >> 16) : (w1[i / 2] & 0xFFFFu)) : 0u;
-        *(uint32_t*)(dst + (cb + i) * pitch + j) = a | (c << 16);
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------- s2 chunk state
 
-constexpr bool kStateColMaj = false;  // staging task map of chunk_state
+// Operand of a (16 x 32)-by-32 MFMA contraction over time read from a
+// row-major LDS tile rows[j][PR] (j = step) with the transpose read
+// ds_read_b64_tr_b16: within each group of 16 lanes, output lane m, slot i
+// receives element m%4 of the 4 values lane 4i + m/4 read (checked on the
+// device).  Lane (g, 4a + b) of group g reads rows j0 + 8g + a (and + 4) at
+// columns c0 + 4b .. +3, so output lane (g, m) gets rows j0 + 8g + 0..7 of
+// column c0 + m: the slots 8g + i of the A operand (row c0 + m) or of the B
+// operand (column c0 + m).
+template <int PR>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t (*rows)[PR], int j0, int c0, int lr, int lq) {
+  const int r = j0 + 8 * lq + lr / 4, col = c0 + 4 * (lr % 4);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&rows[r][col]);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&rows[r + 4][col]);
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  return as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+}
 
+// Block = (b, chunk c, head h), 8 waves.  S_loc[p][n] = sum_j (w_j x_j[p])
+// B_j[n], w_j = exp(A_cum_end - A_cum_j) beta_j: x rows are staged scaled by
+// w_j, B rows as they are; wave wv computes p-tile wv % 4 times n-tiles
+// 2*(wv/4) and +1, contracting over the Q steps in slices of 32.
 template <int Q>
-__global__ __launch_bounds__(256) void chunk_state_kernel(SSDParams p) {
-  constexpr int PITCH = Q + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t xT[64][PITCH];  // (x * w)^T: [p][j]
-  __shared__ __attribute__((aligned(16))) uint16_t bT[64][PITCH];  // B^T: [n][j]
+__global__ __launch_bounds__(512) void chunk_state_kernel(SSDParams p) {
+  constexpr int NTH = 512;
+  constexpr int PR = 64 + 4;        // row pitch (bf16)
+  constexpr int NTX = Q * 8 / NTH;  // (row, 8 values) pieces of x and of B per thread
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][PR];  // w_j x_j rows
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][PR];  // B rows
   __shared__ float w[Q];
-  int64_t bid = blockIdx.x;
-  const int64_t h = bid % p.H;
-  bid /= p.H;
-  const int64_t c = bid % p.nchunks, b = bid / p.nchunks;
+  int bid = (int)blockIdx.x;
+  const int64_t h = bid % (int)p.H;
+  bid /= (int)p.H;
+  const int64_t c = bid % (int)p.nchunks, b = bid / (int)p.nchunks;
   const int64_t g = h / (p.H / p.G);
   const int tid = threadIdx.x;
   const int64_t t0 = c * Q;
-  PairLoads<Q, 256> lx, lb;
-  load_pairs<Q, 256, kStateColMaj>(lx, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
-  load_pairs<Q, 256, kStateColMaj>(lb, (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g, p.Bs_t, t0, p.L);
+  uint4 rx[NTX], rb[NTX];
+  const uint16_t* Xsrc = (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h;
+  const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
+#pragma unroll
+  for (int u = 0; u < NTX; ++u) {
+    const int task = tid + NTH * u;
+    const int j = task / 8, cb = (task % 8) * 8;
+    const int64_t tr = t0 + j < p.L ? t0 + j : p.L - 1;
+    rx[u] = *(const uint4*)(Xsrc + tr * p.xs_t + cb);
+    rb[u] = *(const uint4*)(Bsrc + tr * p.Bs_t + cb);
+  }
   const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
   const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
   const float a_end = Ac[Q - 1];
-  for (int t = tid; t < Q; t += 256) w[t] = __builtin_amdgcn_exp2f((a_end - Ac[t]) * kLog2e) * be[t];
+  for (int t = tid; t < Q; t += NTH) w[t] = __builtin_amdgcn_exp2f((a_end - Ac[t]) * kLog2e) * be[t];
   __syncthreads();
-  store_pairs_transposed<Q, 256, kStateColMaj>(lx, &xT[0][0], PITCH, t0, p.L, w);
-  store_pairs_transposed<Q, 256, kStateColMaj>(lb, &bT[0][0], PITCH, t0, p.L, nullptr);
-  __syncthreads();
-  const int wv = tid / 64, l = tid % 64, lr = l % 16, lq = l / 16;
-  f32x4 acc[4];
+  // rows at or past L hold zeros (as data, not through w: 0 * inf)
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < NTX; ++u) {
+    const int task = tid + NTH * u;
+    const int j = task / 8, cb = (task % 8) * 8;
+    const bool ok = t0 + j < p.L;
+    const float wj = w[j];
+    const uint32_t v[4] = {rx[u].x, rx[u].y, rx[u].z, rx[u].w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[k] = ok ? pack2(__uint_as_float(v[k] << 16) * wj, __uint_as_float(v[k] & 0xFFFF0000u) * wj) : 0u;
+    *(uint4*)&Xs[j][cb] = make_uint4(o[0], o[1], o[2], o[3]);
+    *(uint4*)&Bs[j][cb] = ok ? rb[u] : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64), l = tid % 64, lr = l % 16, lq = l / 16;
+  const int pt = wv % 4, nt0 = 2 * (wv / 4);
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int ks = 0; ks < Q / 32; ++ks) {
-    const bf16x8 a = as_bf16x8(*(const uint4*)&xT[16 * wv + lr][32 * ks + 8 * lq]);
+    const bf16x8 a = tr_operand<PR>(Xs, 32 * ks, 16 * pt, lr, lq);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const bf16x8 bb = as_bf16x8(*(const uint4*)&bT[16 * nt + lr][32 * ks + 8 * lq]);
-      acc[nt] = mfma(a, bb, acc[nt]);
-    }
+    for (int k = 0; k < 2; ++k) acc[k] = mfma(a, tr_operand<PR>(Bs, 32 * ks, 16 * (nt0 + k), lr, lq), acc[k]);
   }
   float* dst = p.states + (((b * p.nchunks + c) * p.H + h) * 64) * 64;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int k = 0; k < 2; ++k)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(16 * wv + 4 * lq + r) * 64 + 16 * nt + lr] = acc[nt][r];
+    for (int r = 0; r < 4; ++r) dst[(16 * pt + 4 * lq + r) * 64 + 16 * (nt0 + k) + lr] = acc[k][r];
 }
 
 // ---------------------------------------------------- s3 state passing
@@ -519,9 +485,9 @@ hipError_t launch_ssd_chunk_cumsum(const SSDParams& p, hipStream_t stream) {
 
 hipError_t launch_ssd_chunk_state(const SSDParams& p, hipStream_t stream) {
   const unsigned nb = (unsigned)(p.batch * p.nchunks * p.H);
-  if (p.Q == 64) hipLaunchKernelGGL(chunk_state_kernel<64>, dim3(nb), dim3(256), 0, stream, p);
-  else if (p.Q == 128) hipLaunchKernelGGL(chunk_state_kernel<128>, dim3(nb), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(chunk_state_kernel<256>, dim3(nb), dim3(256), 0, stream, p);
+  if (p.Q == 64) hipLaunchKernelGGL(chunk_state_kernel<64>, dim3(nb), dim3(512), 0, stream, p);
+  else if (p.Q == 128) hipLaunchKernelGGL(chunk_state_kernel<128>, dim3(nb), dim3(512), 0, stream, p);
+  else hipLaunchKernelGGL(chunk_state_kernel<256>, dim3(nb), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
