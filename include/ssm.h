@@ -151,6 +151,46 @@ typedef struct {
   float* h_last;   /* NULL unless SSM_WANT_HLAST */
 } ssm_ssd_ptrs;
 
+/* ---------------------------------------------------------------- decode */
+
+/* One recurrent step (autoregressive decode): the recurrent mode of the
+ * discretised SSM ("Mamba 논문 리뷰 ...", tildalice.io, sections SSM의 이중 연산
+ * 모드, 추론 속도 and Mamba의 강점 / 고정 크기 상태로 효율적 추론: generation
+ * keeps only the fixed (dim x dstate) state).  For every batch element b and
+ * channel d,
+ *      state[b,d,n] <- Abar * state[b,d,n] + Bbar * x[b,d]      (in place)
+ *      y[b,d]        = (sum_n C[b,n] state[b,d,n] + D[d] x[b,d]) * silu(z[b,d])
+ * with Abar, Bbar as in the selective scan (delta[b,d], A[d,n], B[b,n]); it
+ * equals ssm_selective_scan_fwd with seqlen 1, h0 = h_last = state.
+ * Required tensors (shape, dtype):
+ *   x, delta : (batch, dim)  io           innermost stride 1
+ *   z        : (batch, dim)  io           if SSM_HAS_Z, innermost stride 1
+ *   y        : (batch, dim)  io or F32    innermost stride 1
+ *   B, C     : (batch, dstate) io         any strides
+ *   A        : (dim, dstate) F32          any strides (0 = shared)
+ *   D        : (dim) F32                  if SSM_HAS_D, any stride
+ *   state    : (batch, dim, dstate) F32 contiguous, read and overwritten
+ * Flags: SSM_HAS_Z, SSM_HAS_D, SSM_DISC_EULER (SSM_HAS_H0 / SSM_WANT_HLAST
+ * are not accepted: the state is both).  y and state may not overlap each
+ * other or any input.  dstate <= SSM_SCAN_MAX_DSTATE. */
+typedef struct {
+  int64_t batch, dim, dstate;
+  uint32_t flags;
+  ssm_tensor_desc x, delta, A, B, C, D, z, y, state;
+} ssm_update_desc;
+
+typedef struct {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;  /* NULL unless SSM_HAS_D */
+  const void* z;   /* NULL unless SSM_HAS_Z */
+  void* y;
+  float* state;
+} ssm_update_ptrs;
+
 /* --------------------------------------------------------------- entries */
 
 /* SSM_ABI_VERSION of the library that is loaded. */
@@ -207,6 +247,9 @@ ssm_status ssm_ssd_state_passing(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, c
                                  const float* states, void* S_in, void* hip_stream);
 ssm_status ssm_ssd_chunk_scan(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, const float* A_cum, const float* beta,
                               const void* S_in, void* hip_stream);
+
+/* One decode step (definition above ssm_update_desc).  No workspace. */
+ssm_status ssm_selective_state_update(const ssm_update_desc* d, const ssm_update_ptrs* p, void* hip_stream);
 
 #ifdef __cplusplus
 }

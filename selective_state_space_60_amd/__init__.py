@@ -26,7 +26,7 @@ MAX_DIMS = 5
 # Every function include/ssm.h declares.
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_hip_error", "ssm_selective_scan_workspace_size",
            "ssm_selective_scan_fwd", "ssm_ssd_chunk_workspace_size", "ssm_ssd_chunk_fwd", "ssm_ssd_chunk_cumsum",
-           "ssm_ssd_chunk_state", "ssm_ssd_state_passing", "ssm_ssd_chunk_scan")
+           "ssm_ssd_chunk_state", "ssm_ssd_state_passing", "ssm_ssd_chunk_scan", "ssm_selective_state_update")
 
 
 class TensorDesc(ctypes.Structure):
@@ -36,6 +36,7 @@ class TensorDesc(ctypes.Structure):
 
 _SCAN_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "h0", "h_last")
 _SSD_T = ("x", "delta", "A", "B", "C", "D", "y", "h0", "h_last")
+_UPD_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "state")
 
 
 class ScanDesc(ctypes.Structure):
@@ -55,6 +56,15 @@ class SSDDesc(ctypes.Structure):
 
 class SSDPtrs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _SSD_T]
+
+
+class UpdateDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("flags", ctypes.c_uint32)] + [(n, TensorDesc) for n in _UPD_T]
+
+
+class UpdatePtrs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _UPD_T]
 
 
 class SSMError(RuntimeError):
@@ -89,6 +99,7 @@ def lib() -> ctypes.CDLL:
         L.ssm_ssd_chunk_state.argtypes = [P(SSDDesc), P(SSDPtrs), vp, vp, vp, vp]
         L.ssm_ssd_state_passing.argtypes = [P(SSDDesc), P(SSDPtrs), vp, vp, vp, vp]
         L.ssm_ssd_chunk_scan.argtypes = [P(SSDDesc), P(SSDPtrs), vp, vp, vp, vp]
+        L.ssm_selective_state_update.argtypes = [P(UpdateDesc), P(UpdatePtrs), vp]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = ctypes.c_int
         if L.ssm_abi_version() != 1:
@@ -286,4 +297,38 @@ def ssd_chunk_scan(x, delta, A, B, C, chunk, A_cum, beta, S_in, D=None, euler=Fa
     ptrs = ssd_ptrs(x, delta, A, B, C, D=D, y=y)
     _check(lib().ssm_ssd_chunk_scan(ctypes.byref(desc), ctypes.byref(ptrs), _p(A_cum), _p(beta), _p(S_in),
                                     _stream(stream)), "ssm_ssd_chunk_scan")
+    return y
+
+
+# ------------------------------------------------------------------ decode
+
+def update_desc(x, delta, A, B, C, state, D=None, z=None, y=None, euler=False) -> UpdateDesc:
+    d = UpdateDesc()
+    d.batch, d.dim = x.shape
+    d.dstate = A.shape[-1]
+    d.flags = ((SSM_HAS_Z if z is not None else 0) | (SSM_HAS_D if D is not None else 0) |
+               (SSM_DISC_EULER if euler else 0))
+    for name, t in zip(_UPD_T, (x, delta, A, B, C, D, z, y, state)):
+        setattr(d, name, tensor_desc(t))
+    return d
+
+
+def update_ptrs(x, delta, A, B, C, state, D=None, z=None, y=None) -> UpdatePtrs:
+    p = UpdatePtrs()
+    for name, t in zip(_UPD_T, (x, delta, A, B, C, D, z, y, state)):
+        setattr(p, name, _p(t))
+    return p
+
+
+def selective_state_update(state, x, delta, A, B, C, D=None, z=None, euler=False, y_dtype=None, y=None,
+                           stream=None):
+    """One decode step (see include/ssm.h): advances ``state`` (batch, dim,
+    dstate) fp32 in place and returns y (batch, dim).  x, delta, z: (batch,
+    dim); B, C: (batch, dstate); A: (dim, dstate) fp32; D: (dim,) fp32."""
+    if y is None:
+        y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
+    desc = update_desc(x, delta, A, B, C, state, D, z, y, euler)
+    ptrs = update_ptrs(x, delta, A, B, C, state, D, z, y)
+    _check(lib().ssm_selective_state_update(ctypes.byref(desc), ctypes.byref(ptrs), _stream(stream)),
+           "ssm_selective_state_update")
     return y

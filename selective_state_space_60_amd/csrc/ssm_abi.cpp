@@ -16,6 +16,7 @@ thread_local int g_last_hip_error = 0;
 
 constexpr uint32_t kScanFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_WANT_HLAST;
 constexpr uint32_t kSSDFlags = SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_WANT_HLAST;
+constexpr uint32_t kUpdateFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER;
 constexpr int kSimds = 256 * 4;  // MI355X: 256 compute units x 4 SIMDs
 
 int64_t esize(int32_t dt) { return dt == SSM_BF16 || dt == SSM_F16 ? 2 : 4; }
@@ -306,6 +307,60 @@ ssm::SSDParams make_ssd_params(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, con
   return q;
 }
 
+// ---------------------------------------------------------------- decode
+
+ssm_status validate_update(const ssm_update_desc* d, const ssm_update_ptrs* p) {
+  if (!d || !p) return SSM_ERR_NULL;
+  if (d->batch <= 0 || d->dim <= 0 || d->dstate <= 0) return SSM_ERR_SHAPE;
+  if (d->flags & ~kUpdateFlags) return SSM_ERR_UNSUPPORTED;
+  if (d->dstate > SSM_SCAN_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
+  // one workgroup per (batch element, 16..256 channels): the grid is 1-D
+  if (d->dim > (1 << 30) || d->batch * ((d->dim + 15) / 16) >= ((int64_t)1 << 31)) return SSM_ERR_UNSUPPORTED;
+  const int32_t io = d->x.dtype;
+  if (io == SSM_F16) return SSM_ERR_UNSUPPORTED;
+  const bool io_ok = io == SSM_F32 || io == SSM_BF16;
+  const uint32_t f = d->flags;
+  const int64_t bd[2] = {d->batch, d->dim};
+  const int64_t bn[2] = {d->batch, d->dstate};
+  const int64_t dn[2] = {d->dim, d->dstate};
+  const int64_t dd[1] = {d->dim};
+  const int64_t bdn[3] = {d->batch, d->dim, d->dstate};
+  ssm_status s;
+  if ((s = check_tensor(d->x, 2, bd, io_ok, true, false))) return s;
+  if ((s = check_tensor(d->delta, 2, bd, d->delta.dtype == io, true, false))) return s;
+  if ((s = check_tensor(d->B, 2, bn, d->B.dtype == io, false, false))) return s;
+  if ((s = check_tensor(d->C, 2, bn, d->C.dtype == io, false, false))) return s;
+  if ((s = check_tensor(d->A, 2, dn, d->A.dtype == SSM_F32, false, false))) return s;
+  if ((s = check_tensor(d->y, 2, bd, d->y.dtype == io || d->y.dtype == SSM_F32, true, false))) return s;
+  if (!non_overlapping(d->y)) return SSM_ERR_STRIDE;
+  if ((s = check_tensor(d->state, 3, bdn, d->state.dtype == SSM_F32, false, true))) return s;
+  if (f & SSM_HAS_Z)
+    if ((s = check_tensor(d->z, 2, bd, d->z.dtype == io, true, false))) return s;
+  if (f & SSM_HAS_D)
+    if ((s = check_tensor(d->D, 1, dd, d->D.dtype == SSM_F32, false, false))) return s;
+  if (!p->x || !p->delta || !p->A || !p->B || !p->C || !p->y || !p->state) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_Z) && !p->z) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_D) && !p->D) return SSM_ERR_NULL;
+  const int64_t e = esize(io);
+  if (!aligned(p->x, e) || !aligned(p->delta, e) || !aligned(p->B, e) || !aligned(p->C, e) || !aligned(p->A, 4) ||
+      !aligned(p->y, esize(d->y.dtype)) || !aligned(p->state, 4))
+    return SSM_ERR_ALIGN;
+  if (((f & SSM_HAS_Z) && !aligned(p->z, e)) || ((f & SSM_HAS_D) && !aligned(p->D, 4))) return SSM_ERR_ALIGN;
+  const Span ins[] = {span_of(d->x, p->x),
+                      span_of(d->delta, p->delta),
+                      span_of(d->A, p->A),
+                      span_of(d->B, p->B),
+                      span_of(d->C, p->C),
+                      (f & SSM_HAS_D) ? span_of(d->D, p->D) : Span(),
+                      (f & SSM_HAS_Z) ? span_of(d->z, p->z) : Span()};
+  const Span ys = span_of(d->y, p->y);
+  const Span st = span_of(d->state, p->state);
+  for (const Span& sp : ins)
+    if (overlap(ys, sp) || overlap(st, sp)) return SSM_ERR_ALIAS;
+  if (overlap(ys, st)) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
 ssm_status hip_status(hipError_t e) {
   if (e == hipSuccess) return SSM_OK;
   g_last_hip_error = (int)e;
@@ -471,6 +526,27 @@ ssm_status ssm_ssd_chunk_scan(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, cons
   q.beta = (float*)beta;
   q.S_in = (void*)S_in;
   return hip_status(ssm::launch_ssd_chunk_scan(q, (hipStream_t)hip_stream));
+}
+
+ssm_status ssm_selective_state_update(const ssm_update_desc* d, const ssm_update_ptrs* p, void* hip_stream) {
+  ssm_status s = validate_update(d, p);
+  if (s) return s;
+  ssm::UpdateParams q;
+  std::memset(&q, 0, sizeof(q));
+  const uint32_t f = d->flags;
+  q.x = p->x; q.delta = p->delta; q.z = (f & SSM_HAS_Z) ? p->z : nullptr; q.y = p->y;
+  q.B = p->B; q.C = p->C; q.A = p->A; q.Dskip = (f & SSM_HAS_D) ? p->D : nullptr; q.state = p->state;
+  q.batch = d->batch; q.D = d->dim; q.N = d->dstate;
+  q.xs_b = d->x.stride[0]; q.ds_b = d->delta.stride[0];
+  q.zs_b = (f & SSM_HAS_Z) ? d->z.stride[0] : 0; q.ys_b = d->y.stride[0];
+  q.Bs_b = d->B.stride[0]; q.Bs_n = d->B.stride[1];
+  q.Cs_b = d->C.stride[0]; q.Cs_n = d->C.stride[1];
+  q.As_d = d->A.stride[0]; q.As_n = d->A.stride[1];
+  q.Ds_d = (f & SSM_HAS_D) ? d->D.stride[0] : 0;
+  q.euler = (f & SSM_DISC_EULER) ? 1 : 0;
+  q.io_bf16 = d->x.dtype == SSM_BF16;
+  q.y_f32 = d->y.dtype == SSM_F32;
+  return hip_status(ssm::launch_selective_state_update(q, (hipStream_t)hip_stream));
 }
 
 }  // extern "C"

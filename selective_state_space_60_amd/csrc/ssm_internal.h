@@ -42,6 +42,26 @@ constexpr int kScanThreads = kScanLanesPerChannel * kScanChannelsPerBlock;
 
 hipError_t launch_selective_scan(const ScanParams& p, hipStream_t stream);
 
+// ------------------------------------------------------------------- decode
+struct UpdateParams {
+  const void* x;      // (batch, D)
+  const void* delta;  // (batch, D)
+  const void* z;      // (batch, D) or null
+  void* y;            // (batch, D)
+  const void* B;      // (batch, N)
+  const void* C;
+  const float* A;      // (D, N)
+  const float* Dskip;  // (D) or null
+  float* state;        // (batch, D, N) contiguous
+  int64_t batch, D, N;
+  int64_t xs_b, ds_b, zs_b, ys_b, Bs_b, Bs_n, Cs_b, Cs_n, As_d, As_n, Ds_d;
+  int euler;
+  int io_bf16;
+  int y_f32;
+};
+
+hipError_t launch_selective_state_update(const UpdateParams& p, hipStream_t stream);
+
 // ---------------------------------------------------------------------- SSD
 struct SSDParams {
   const void* x;      // (batch, L, H, P) bf16

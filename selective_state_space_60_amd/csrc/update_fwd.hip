@@ -1,0 +1,280 @@
+// One recurrent (decode) step of the selective SSM for gfx950.
+//
+// The recurrent mode of the discretised model ("Mamba 논문 리뷰 ... Selective
+// State Space Model", tildalice.io: 이산화, SSM의 이중 연산 모드, 고정 크기 상태로
+// 효율적 추론): per batch element b and channel d the fixed-size state is
+// advanced by one step in place,
+//   h[n] <- exp(delta*A[n]) h[n] + Bbar[n] x,  Bbar = expm1(delta*A)/A * B
+//   (delta*B with the simplified discretisation), and
+//   y = (C . h + D x) * silu(z).
+// The step streams the fp32 state once through memory (8 bytes per state:
+// read and write); x, delta, z, y are one element per channel and B, C one
+// row per batch element.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace {
+
+constexpr int NT = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <bool BF16>
+__device__ __forceinline__ float ld(const void* p, int64_t i) {
+  if constexpr (BF16) return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
+  else return ((const float*)p)[i];
+}
+
+// Bbar / B for u = delta*A, given t = u / ln 2, e = exp(u) and ra = 1/A:
+// expm1(u)/A = delta * phi(u) with phi(u) = expm1(u)/u.  phi comes from its
+// Taylor polynomial (through u^5, evaluated in t) for |u| < 1/4, which also
+// covers A == 0, and (e - 1) * ra beyond, where the subtraction does not
+// cancel.  The simplified discretisation takes delta.
+template <bool EULER>
+__device__ __forceinline__ float bbar_coef(float t, float e, float dt, float ra) {
+  if constexpr (EULER) {
+    return dt;
+  } else {
+    constexpr float l1 = kLn2, l2 = l1 * kLn2, l3 = l2 * kLn2, l4 = l3 * kLn2, l5 = l4 * kLn2;
+    float q = l5 / 720.f;
+    q = __builtin_fmaf(q, t, l4 / 120.f);
+    q = __builtin_fmaf(q, t, l3 / 24.f);
+    q = __builtin_fmaf(q, t, l2 / 6.f);
+    q = __builtin_fmaf(q, t, l1 / 2.f);
+    q = __builtin_fmaf(q, t, 1.f);
+    float cs = dt * q, cb = (e - 1.f) * ra;
+    // both sides stay computed for every lane: a select, not a branch
+    asm volatile("" : "+v"(cs), "+v"(cb));
+    return fabsf(t) < 0.25f / kLn2 ? cs : cb;
+  }
+}
+
+__device__ __forceinline__ float gate(float v, float Dv, float x, float z, bool has_z) {
+  v = __builtin_fmaf(Dv, x, v);
+  return has_z ? v * (z * __builtin_amdgcn_rcpf(1.f + __expf(-z))) : v;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_y(const UpdateParams& p, int64_t b, int d, float v) {
+  if (p.y_f32 || !BF16) ((float*)p.y)[b * p.ys_b + d] = v;
+  else ((__bf16*)p.y)[b * p.ys_b + d] = (__bf16)v;
+}
+
+// ------------------------------------------------------------ vector path
+// Q lanes per channel, four consecutive states per lane, so a wave reads and
+// writes 1 KiB of contiguous state per instruction.  A workgroup owns 256/Q
+// channels and walks the batch (b = slot, slot + slots, ...) in a two-stage
+// software pipeline: the inputs of the next batch element are in flight
+// while the current one is computed and stored, so memory traffic and
+// arithmetic overlap inside every wave.  A, its reciprocal and D are read
+// once per workgroup.  Needs N % 4 == 0, 16-byte aligned rows of the state
+// and A, and rows of B and C aligned to four elements, each contiguous in n.
+struct Item {
+  float4 h;
+  float x, dt, z;
+  uint32_t bw[4], cw[4];  // B, C: bf16 pairs in [0..1], or fp32 in [0..3]
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_item(Item& it, const UpdateParams& p, int64_t b, int dd, int nn,
+                                          const void* zp, int64_t zsb) {
+  it.h = *(const float4*)(p.state + (b * p.D + dd) * p.N + nn);
+  it.x = ld<BF16>(p.x, b * p.xs_b + dd);
+  it.dt = ld<BF16>(p.delta, b * p.ds_b + dd);
+  it.z = ld<BF16>(zp, b * zsb + dd);
+  if constexpr (BF16) {
+    const uint2 bw = *(const uint2*)((const uint16_t*)p.B + b * p.Bs_b + nn);
+    const uint2 cw = *(const uint2*)((const uint16_t*)p.C + b * p.Cs_b + nn);
+    it.bw[0] = bw.x; it.bw[1] = bw.y; it.cw[0] = cw.x; it.cw[1] = cw.y;
+  } else {
+    const uint4 bw = *(const uint4*)((const float*)p.B + b * p.Bs_b + nn);
+    const uint4 cw = *(const uint4*)((const float*)p.C + b * p.Cs_b + nn);
+    it.bw[0] = bw.x; it.bw[1] = bw.y; it.bw[2] = bw.z; it.bw[3] = bw.w;
+    it.cw[0] = cw.x; it.cw[1] = cw.y; it.cw[2] = cw.z; it.cw[3] = cw.w;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float unpack(const uint32_t* w, int i) {
+  if constexpr (BF16) return __uint_as_float((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
+  else return __uint_as_float(w[i]);
+}
+
+template <bool BF16, int Q, bool EULER>
+__device__ __forceinline__ void process_item(const Item& it, const UpdateParams& p, int64_t b, int d, int n0,
+                                             bool ok, bool ch_ok, const float (&al2)[4], const float (&ra)[4],
+                                             float Dv, bool has_z) {
+  const float hin[4] = {it.h.x, it.h.y, it.h.z, it.h.w};
+  float hv[4];
+  float yp = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t = it.dt * al2[i];
+    const float e = __builtin_amdgcn_exp2f(t);
+    const float c = bbar_coef<EULER>(t, e, it.dt, ra[i]);
+    hv[i] = __builtin_fmaf(e, hin[i], c * (unpack<BF16>(it.bw, i) * it.x));
+    yp = __builtin_fmaf(unpack<BF16>(it.cw, i), hv[i], yp);
+  }
+  if (ok) *(float4*)(p.state + (b * p.D + d) * p.N + n0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+  if (!ok) yp = 0.f;
+#pragma unroll
+  for (int m = Q / 2; m >= 1; m >>= 1) yp += __shfl_xor(yp, m, Q);
+  if (n0 == 0 && ch_ok) store_y<BF16>(p, b, d, gate(yp, Dv, it.x, it.z, has_z));
+}
+
+template <bool BF16, int Q, bool EULER>
+__global__ __launch_bounds__(NT) void update_kernel(UpdateParams p, unsigned tiles) {
+  constexpr int CPB = NT / Q;  // channels per workgroup
+  const unsigned slots = gridDim.x / tiles;
+  const unsigned slot = blockIdx.x / tiles;  // first batch element (workgroup-uniform)
+  const int tile = (int)(blockIdx.x - slot * tiles);
+  const int tid = threadIdx.x;
+  const int n0 = 4 * (tid % Q);
+  const int d = tile * CPB + tid / Q;
+  const bool ch_ok = d < p.D;
+  const bool ok = ch_ok && n0 < (int)p.N;
+  const int dd = ch_ok ? d : 0;
+  const int nn = ok ? n0 : 0;
+  const int64_t batch = p.batch;
+  if ((int64_t)slot >= batch) return;  // whole workgroup
+
+  // optional inputs are read unconditionally (from x and A when absent) so
+  // that no load sits behind a branch
+  const bool has_z = p.z != nullptr;
+  const void* zp = has_z ? p.z : p.x;
+  const int64_t zsb = has_z ? p.zs_b : p.xs_b;
+  const float4 a4 = *(const float4*)(p.A + (int64_t)dd * p.As_d + nn);
+  const float Dl = *(p.Dskip ? p.Dskip + (int64_t)dd * p.Ds_d : p.A);
+  Item i0, i1;
+  int64_t b = slot;
+  load_item<BF16>(i0, p, b, dd, nn, zp, zsb);
+  const float Dv = p.Dskip ? Dl : 0.f;
+  const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+  float al2[4], ra[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    al2[i] = av[i] * kLog2e;
+    ra[i] = __builtin_amdgcn_rcpf(av[i]);
+  }
+  // the prefetch past the last element re-reads the current one (a cache hit)
+  while (true) {
+    int64_t bn = b + slots;
+    load_item<BF16>(i1, p, bn < batch ? bn : b, dd, nn, zp, zsb);
+    process_item<BF16, Q, EULER>(i0, p, b, d, n0, ok, ch_ok, al2, ra, Dv, has_z);
+    b = bn;
+    if (b >= batch) break;
+    bn = b + slots;
+    load_item<BF16>(i0, p, bn < batch ? bn : b, dd, nn, zp, zsb);
+    process_item<BF16, Q, EULER>(i1, p, b, d, n0, ok, ch_ok, al2, ra, Dv, has_z);
+    b = bn;
+    if (b >= batch) break;
+  }
+}
+
+// ----------------------------------------------------------- generic path
+// Any N and strides: 16 lanes per channel, lane j holds states j, j + 16, ...
+template <bool BF16, int KS, bool EULER>
+__global__ __launch_bounds__(NT) void update_kernel_any(UpdateParams p, unsigned tiles) {
+  constexpr int G = 16;
+  constexpr int CPB = NT / G;
+  const unsigned b32 = blockIdx.x / tiles;
+  const int tile = (int)(blockIdx.x - b32 * tiles);
+  const int64_t b = b32;
+  const int tid = threadIdx.x;
+  const int sg = tid % G;
+  const int d = tile * CPB + tid / G;
+  const bool ch_ok = d < p.D;
+  const int dd = ch_ok ? d : 0;
+  const int N = (int)p.N;
+  const bool has_z = p.z != nullptr;
+  const void* zp = has_z ? p.z : p.x;
+  const int64_t zsb = has_z ? p.zs_b : p.xs_b;
+  float* hrow = p.state + (b * p.D + dd) * p.N;
+  const float xv = ld<BF16>(p.x, b * p.xs_b + dd);
+  const float dt = ld<BF16>(p.delta, b * p.ds_b + dd);
+  const float zv = ld<BF16>(zp, b * zsb + dd);
+  const float Dl = *(p.Dskip ? p.Dskip + (int64_t)dd * p.Ds_d : p.A);
+  float a[KS], Bn[KS], Cn[KS], h[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const int n = sg + G * k;
+    const int nn = (ch_ok && n < N) ? n : 0;
+    a[k] = p.A[(int64_t)dd * p.As_d + (int64_t)nn * p.As_n];
+    Bn[k] = ld<BF16>(p.B, b * p.Bs_b + (int64_t)nn * p.Bs_n);
+    Cn[k] = ld<BF16>(p.C, b * p.Cs_b + (int64_t)nn * p.Cs_n);
+    h[k] = hrow[nn];
+  }
+  float yp = 0.f;
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const int n = sg + G * k;
+    const float t = dt * (a[k] * kLog2e);
+    const float e = __builtin_amdgcn_exp2f(t);
+    const float c = bbar_coef<EULER>(t, e, dt, __builtin_amdgcn_rcpf(a[k]));
+    const float hn = __builtin_fmaf(e, h[k], c * (Bn[k] * xv));
+    if (ch_ok && n < N) {
+      hrow[n] = hn;
+      yp = __builtin_fmaf(Cn[k], hn, yp);
+    }
+  }
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) yp += __shfl_xor(yp, m, G);
+  if (sg == 0 && ch_ok) store_y<BF16>(p, b, d, gate(yp, p.Dskip ? Dl : 0.f, xv, zv, has_z));
+}
+
+template <bool BF16, int Q>
+void launch_q(const UpdateParams& p, hipStream_t stream) {
+  // about four batch elements per workgroup, so the pipeline has depth
+  const unsigned tiles = (unsigned)((p.D + NT / Q - 1) / (NT / Q));
+  const unsigned slots = (unsigned)std::max<int64_t>(1, (p.batch + 3) / 4);
+  const dim3 grid(tiles * slots);
+  if (p.euler) hipLaunchKernelGGL((update_kernel<BF16, Q, true>), grid, dim3(NT), 0, stream, p, tiles);
+  else hipLaunchKernelGGL((update_kernel<BF16, Q, false>), grid, dim3(NT), 0, stream, p, tiles);
+}
+
+template <bool BF16, int KS>
+void launch_any(const UpdateParams& p, hipStream_t stream) {
+  const unsigned tiles = (unsigned)((p.D + 15) / 16);
+  const dim3 grid(tiles * (unsigned)p.batch);
+  if (p.euler) hipLaunchKernelGGL((update_kernel_any<BF16, KS, true>), grid, dim3(NT), 0, stream, p, tiles);
+  else hipLaunchKernelGGL((update_kernel_any<BF16, KS, false>), grid, dim3(NT), 0, stream, p, tiles);
+}
+
+template <bool BF16>
+hipError_t launch_io(const UpdateParams& p, hipStream_t stream) {
+  // vector path: 4 consecutive states per lane from contiguous, aligned rows
+  const int64_t e = BF16 ? 2 : 4;
+  const int64_t rowbytes = 4 * e;  // four B (or C) values
+  auto rows_ok = [&](const void* ptr, int64_t sb, int64_t sn, int64_t es, int64_t al) {
+    return sn == 1 && ((uintptr_t)ptr % al) == 0 && (sb * es) % al == 0;
+  };
+  const bool vec = p.N % 4 == 0 && ((uintptr_t)p.state % 16) == 0 && rows_ok(p.A, p.As_d, p.As_n, 4, 16) &&
+                   rows_ok(p.B, p.Bs_b, p.Bs_n, e, rowbytes) && rows_ok(p.C, p.Cs_b, p.Cs_n, e, rowbytes);
+  if (vec) {
+    const int q = (int)((p.N + 3) / 4);
+    if (q <= 1) launch_q<BF16, 1>(p, stream);
+    else if (q <= 2) launch_q<BF16, 2>(p, stream);
+    else if (q <= 4) launch_q<BF16, 4>(p, stream);
+    else if (q <= 8) launch_q<BF16, 8>(p, stream);
+    else launch_q<BF16, 16>(p, stream);
+  } else if (p.N <= 16) {
+    launch_any<BF16, 1>(p, stream);
+  } else if (p.N <= 32) {
+    launch_any<BF16, 2>(p, stream);
+  } else {
+    launch_any<BF16, 4>(p, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_selective_state_update(const UpdateParams& p, hipStream_t stream) {
+  return p.io_bf16 ? launch_io<true>(p, stream) : launch_io<false>(p, stream);
+}
+
+}  // namespace ssm

@@ -177,6 +177,11 @@ LONG1M = ScanSpec("long1m_b1_l1048576_d1536_n16_f32", 1, 1 << 20, 1536, 16, "f32
 SSD2_7B = SSDSpec("ssd2.7b_b4_l4096_h80_p64_n64_g1_q256_bf16", 4, 4096, 80, 64, 64, 1, 256, "bf16", True,
                   A=Dist(NEG_EXP_UNIFORM, 0.0, 2.7), delta=Dist(SOFTPLUS_NORMAL, -3.0, 1.0))
 
+# One decode step of the Mamba-2.8B-shaped layer for 64 concurrent sequences
+# (seqlen 1: the state (64, 5120, 16) fp32 is read and written in place).
+DECODE2_8B = ScanSpec("decode_mamba2.8b_b64_d5120_n16_bf16", 64, 1, 5120, 16, "bf16", True, True,
+                      A=Dist(NEG_IDX, period=16), delta=Dist(SOFTPLUS_NORMAL, -3.0, 1.0))
+
 SCAN_CONFIGS = {s.name: s for s in (TINY, MAMBA130M, MAMBA2_8B, LONG1M)}
 
 

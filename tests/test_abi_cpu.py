@@ -180,3 +180,50 @@ def test_ssd_workspace_size():
     want = 2 * 4 * 80 * 4096 * 4 + 4 * nc * 80 * 64 * 64 * 4 + 4 * nc * 80 * 64 * 64 * 2
     assert n == want
     assert ssm.lib().ssm_ssd_chunk_fwd(ctypes.byref(d), ctypes.byref(p), None, 0, None) == ssm.SSM_ERR_WORKSPACE
+
+
+def _upd(batch=3, D=8, N=16, io="bf16", flags=0, **over):
+    ts = {"x": T((batch, D), io, ptr=1 << 36), "delta": T((batch, D), io, ptr=2 << 36),
+          "A": T((D, N), ptr=3 << 36), "B": T((batch, N), io, ptr=4 << 36), "C": T((batch, N), io, ptr=5 << 36),
+          "D": T((D,), ptr=6 << 36), "z": T((batch, D), io, ptr=7 << 36), "y": T((batch, D), io, ptr=8 << 36),
+          "state": T((batch, D, N), ptr=9 << 36)}
+    ts.update(over)
+    d = ssm.UpdateDesc()
+    d.batch, d.dim, d.dstate, d.flags = batch, D, N, flags
+    p = ssm.UpdatePtrs()
+    for k, t in ts.items():
+        setattr(d, k, _td(t))
+        setattr(p, k, None if t is None else t.ptr)
+    return d, p
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda d, p: setattr(p, "state", None), ssm.SSM_ERR_NULL),
+    (lambda d, p: setattr(p, "z", None), ssm.SSM_ERR_NULL),
+    (lambda d, p: setattr(d, "batch", 0), ssm.SSM_ERR_SHAPE),
+    (lambda d, p: setattr(d, "dstate", 65), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: setattr(d, "flags", d.flags | ssm.SSM_HAS_H0), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: setattr(d, "flags", d.flags | ssm.SSM_WANT_HLAST), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: setattr(d.x, "dtype", 2), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: setattr(d.state, "dtype", 1), ssm.SSM_ERR_DTYPE),
+    (lambda d, p: setattr(d.C, "dtype", 0), ssm.SSM_ERR_DTYPE),
+    (lambda d, p: d.B.shape.__setitem__(1, 8), ssm.SSM_ERR_SHAPE),
+    (lambda d, p: setattr(d.x, "ndim", 3), ssm.SSM_ERR_SHAPE),
+    (lambda d, p: d.state.stride.__setitem__(2, 2), ssm.SSM_ERR_STRIDE),
+    (lambda d, p: d.z.stride.__setitem__(1, 2), ssm.SSM_ERR_STRIDE),
+    (lambda d, p: d.y.stride.__setitem__(0, 0), ssm.SSM_ERR_STRIDE),
+    (lambda d, p: setattr(p, "state", (9 << 36) + 2), ssm.SSM_ERR_ALIGN),
+    (lambda d, p: setattr(p, "y", p.x), ssm.SSM_ERR_ALIAS),
+    (lambda d, p: setattr(p, "state", p.A + 64), ssm.SSM_ERR_ALIAS),
+    (lambda d, p: setattr(p, "y", p.state + 4), ssm.SSM_ERR_ALIAS),
+])
+def test_update_validation(mutate, status):
+    d, p = _upd(flags=ssm.SSM_HAS_Z | ssm.SSM_HAS_D)
+    mutate(d, p)
+    assert ssm.lib().ssm_selective_state_update(ctypes.byref(d), ctypes.byref(p), None) == status
+
+
+def test_update_null_descriptor():
+    d, p = _upd()
+    assert ssm.lib().ssm_selective_state_update(None, ctypes.byref(p), None) == ssm.SSM_ERR_NULL
+    assert ssm.lib().ssm_selective_state_update(ctypes.byref(d), None, None) == ssm.SSM_ERR_NULL
