@@ -71,31 +71,58 @@ __device__ __forceinline__ void store_y(const UpdateParams& p, int64_t b, int d,
 // software pipeline: the inputs of the next batch element are in flight
 // while the current one is computed and stored, so memory traffic and
 // arithmetic overlap inside every wave.  A, its reciprocal and D are read
-// once per workgroup.  Needs N % 4 == 0, 16-byte aligned rows of the state
-// and A, and rows of B and C aligned to four elements, each contiguous in n.
+// once per workgroup.  All accesses are buffer loads and stores whose
+// per-lane byte offset is fixed for the workgroup and whose batch offset is
+// a scalar register, so walking the batch costs no vector instructions.
+// Needs N % 4 == 0, 16-byte aligned rows of the state and A, rows of B and C
+// aligned to four elements, each contiguous in n, and every tensor's byte
+// span below 2 GiB.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)0x7FFFFFFF, kRsrcWord3);
+}
+
 struct Item {
-  float4 h;
-  float x, dt, z;
+  uint4 h;
+  uint32_t x, dt, z;
   uint32_t bw[4], cw[4];  // B, C: bf16 pairs in [0..1], or fp32 in [0..3]
 };
 
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t st, x, dt, z, B, C;
+};
+
+// byte strides per batch element
+struct BStride {
+  uint32_t st, x, dt, z, B, C, y;
+};
+
 template <bool BF16>
-__device__ __forceinline__ void load_item(Item& it, const UpdateParams& p, int64_t b, int dd, int nn,
-                                          const void* zp, int64_t zsb) {
-  it.h = *(const float4*)(p.state + (b * p.D + dd) * p.N + nn);
-  it.x = ld<BF16>(p.x, b * p.xs_b + dd);
-  it.dt = ld<BF16>(p.delta, b * p.ds_b + dd);
-  it.z = ld<BF16>(zp, b * zsb + dd);
+__device__ __forceinline__ void load_item(Item& it, const Rsrc& r, const BStride& bs, uint32_t b, int vo_st,
+                                          int vo_ch, int vo_n) {
+  it.h = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.st, vo_st, (int)(b * bs.st), 0));
   if constexpr (BF16) {
-    const uint2 bw = *(const uint2*)((const uint16_t*)p.B + b * p.Bs_b + nn);
-    const uint2 cw = *(const uint2*)((const uint16_t*)p.C + b * p.Cs_b + nn);
-    it.bw[0] = bw.x; it.bw[1] = bw.y; it.cw[0] = cw.x; it.cw[1] = cw.y;
+    it.x = __builtin_amdgcn_raw_buffer_load_b16(r.x, vo_ch, (int)(b * bs.x), 0);
+    it.dt = __builtin_amdgcn_raw_buffer_load_b16(r.dt, vo_ch, (int)(b * bs.dt), 0);
+    it.z = __builtin_amdgcn_raw_buffer_load_b16(r.z, vo_ch, (int)(b * bs.z), 0);
+    const auto bw = __builtin_amdgcn_raw_buffer_load_b64(r.B, vo_n, (int)(b * bs.B), 0);
+    const auto cw = __builtin_amdgcn_raw_buffer_load_b64(r.C, vo_n, (int)(b * bs.C), 0);
+    it.bw[0] = bw[0]; it.bw[1] = bw[1]; it.cw[0] = cw[0]; it.cw[1] = cw[1];
   } else {
-    const uint4 bw = *(const uint4*)((const float*)p.B + b * p.Bs_b + nn);
-    const uint4 cw = *(const uint4*)((const float*)p.C + b * p.Cs_b + nn);
-    it.bw[0] = bw.x; it.bw[1] = bw.y; it.bw[2] = bw.z; it.bw[3] = bw.w;
-    it.cw[0] = cw.x; it.cw[1] = cw.y; it.cw[2] = cw.z; it.cw[3] = cw.w;
+    it.x = __builtin_amdgcn_raw_buffer_load_b32(r.x, vo_ch, (int)(b * bs.x), 0);
+    it.dt = __builtin_amdgcn_raw_buffer_load_b32(r.dt, vo_ch, (int)(b * bs.dt), 0);
+    it.z = __builtin_amdgcn_raw_buffer_load_b32(r.z, vo_ch, (int)(b * bs.z), 0);
+    const auto bw = __builtin_amdgcn_raw_buffer_load_b128(r.B, vo_n, (int)(b * bs.B), 0);
+    const auto cw = __builtin_amdgcn_raw_buffer_load_b128(r.C, vo_n, (int)(b * bs.C), 0);
+    it.bw[0] = bw[0]; it.bw[1] = bw[1]; it.bw[2] = bw[2]; it.bw[3] = bw[3];
+    it.cw[0] = cw[0]; it.cw[1] = cw[1]; it.cw[2] = cw[2]; it.cw[3] = cw[3];
   }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float scal(uint32_t w) {
+  return __uint_as_float(BF16 ? (w << 16) : w);
 }
 
 template <bool BF16>
@@ -104,31 +131,59 @@ __device__ __forceinline__ float unpack(const uint32_t* w, int i) {
   else return __uint_as_float(w[i]);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// sum over each aligned group of Q lanes (Q <= 16), the total in every lane
+template <int Q>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (Q >= 2) v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (Q >= 4) v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (Q >= 8) v = dpp_add<0x141>(v);  // row_half_mirror
+  if constexpr (Q >= 16) v = dpp_add<0x140>(v); // row_mirror
+  return v;
+}
+
 template <bool BF16, int Q, bool EULER>
-__device__ __forceinline__ void process_item(const Item& it, const UpdateParams& p, int64_t b, int d, int n0,
-                                             bool ok, bool ch_ok, const float (&al2)[4], const float (&ra)[4],
-                                             float Dv, bool has_z) {
-  const float hin[4] = {it.h.x, it.h.y, it.h.z, it.h.w};
+__device__ __forceinline__ void process_item(const Item& it, const UpdateParams& p, const Rsrc& r,
+                                             const BStride& bs, uint32_t b, int vo_st, int vo_y, bool ok,
+                                             bool y_lane, const float (&al2)[4], const float (&ra)[4], float Dv,
+                                             bool has_z) {
+  const float hin[4] = {__uint_as_float(it.h.x), __uint_as_float(it.h.y), __uint_as_float(it.h.z),
+                        __uint_as_float(it.h.w)};
+  const float xv = scal<BF16>(it.x), dt = scal<BF16>(it.dt);
   float hv[4];
   float yp = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float t = it.dt * al2[i];
+    const float t = dt * al2[i];
     const float e = __builtin_amdgcn_exp2f(t);
-    const float c = bbar_coef<EULER>(t, e, it.dt, ra[i]);
-    hv[i] = __builtin_fmaf(e, hin[i], c * (unpack<BF16>(it.bw, i) * it.x));
+    const float c = bbar_coef<EULER>(t, e, dt, ra[i]);
+    hv[i] = __builtin_fmaf(e, hin[i], c * (unpack<BF16>(it.bw, i) * xv));
     yp = __builtin_fmaf(unpack<BF16>(it.cw, i), hv[i], yp);
   }
-  if (ok) *(float4*)(p.state + (b * p.D + d) * p.N + n0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
-  if (!ok) yp = 0.f;
-#pragma unroll
-  for (int m = Q / 2; m >= 1; m >>= 1) yp += __shfl_xor(yp, m, Q);
-  if (n0 == 0 && ch_ok) store_y<BF16>(p, b, d, gate(yp, Dv, it.x, it.z, has_z));
+  if (ok) {
+    const uint4 w = {__float_as_uint(hv[0]), __float_as_uint(hv[1]), __float_as_uint(hv[2]), __float_as_uint(hv[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, w),
+                                           r.st, vo_st, (int)(b * bs.st), 0);
+  }
+  yp = group_sum<Q>(ok ? yp : 0.f);
+  const float v = gate(yp, Dv, xv, scal<BF16>(it.z), has_z);
+  if (y_lane) {
+    if (p.y_f32 || !BF16)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc(p.y), vo_y, (int)(b * bs.y), 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rsrc(p.y), vo_y,
+                                            (int)(b * bs.y), 0);
+  }
 }
 
 template <bool BF16, int Q, bool EULER>
 __global__ __launch_bounds__(NT) void update_kernel(UpdateParams p, unsigned tiles) {
   constexpr int CPB = NT / Q;  // channels per workgroup
+  constexpr int E = BF16 ? 2 : 4;
   const unsigned slots = gridDim.x / tiles;
   const unsigned slot = blockIdx.x / tiles;  // first batch element (workgroup-uniform)
   const int tile = (int)(blockIdx.x - slot * tiles);
@@ -139,37 +194,46 @@ __global__ __launch_bounds__(NT) void update_kernel(UpdateParams p, unsigned til
   const bool ok = ch_ok && n0 < (int)p.N;
   const int dd = ch_ok ? d : 0;
   const int nn = ok ? n0 : 0;
-  const int64_t batch = p.batch;
-  if ((int64_t)slot >= batch) return;  // whole workgroup
+  const uint32_t batch = (uint32_t)p.batch;
+  if (slot >= batch) return;  // whole workgroup
 
   // optional inputs are read unconditionally (from x and A when absent) so
   // that no load sits behind a branch
   const bool has_z = p.z != nullptr;
-  const void* zp = has_z ? p.z : p.x;
-  const int64_t zsb = has_z ? p.zs_b : p.xs_b;
-  const float4 a4 = *(const float4*)(p.A + (int64_t)dd * p.As_d + nn);
-  const float Dl = *(p.Dskip ? p.Dskip + (int64_t)dd * p.Ds_d : p.A);
+  const Rsrc r = {rsrc(p.state), rsrc(p.x), rsrc(p.delta), rsrc(has_z ? p.z : p.x), rsrc(p.B), rsrc(p.C)};
+  const BStride bs = {(uint32_t)(p.D * p.N * 4), (uint32_t)(p.xs_b * E), (uint32_t)(p.ds_b * E),
+                      (uint32_t)((has_z ? p.zs_b : p.xs_b) * E), (uint32_t)(p.Bs_b * E), (uint32_t)(p.Cs_b * E),
+                      (uint32_t)(p.ys_b * ((p.y_f32 || !BF16) ? 4 : 2))};
+  const int vo_st = (dd * (int)p.N + nn) * 4;
+  const int vo_ch = dd * E;
+  const int vo_n = nn * E;
+  const int vo_y = d * ((p.y_f32 || !BF16) ? 4 : 2);
+  const bool y_lane = n0 == 0 && ch_ok;
+  const auto a4 = __builtin_amdgcn_raw_buffer_load_b128(rsrc(p.A), (int)(dd * p.As_d + nn) * 4, 0, 0);
+  const float Dl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rsrc(p.Dskip ? p.Dskip : p.A),
+                                                 p.Dskip ? (int)(dd * p.Ds_d) * 4 : 0, 0, 0));
   Item i0, i1;
-  int64_t b = slot;
-  load_item<BF16>(i0, p, b, dd, nn, zp, zsb);
+  uint32_t b = slot;
+  load_item<BF16>(i0, r, bs, b, vo_st, vo_ch, vo_n);
   const float Dv = p.Dskip ? Dl : 0.f;
-  const float av[4] = {a4.x, a4.y, a4.z, a4.w};
   float al2[4], ra[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    al2[i] = av[i] * kLog2e;
-    ra[i] = __builtin_amdgcn_rcpf(av[i]);
+    const float av = __uint_as_float(a4[i]);
+    al2[i] = av * kLog2e;
+    ra[i] = __builtin_amdgcn_rcpf(av);
   }
   // the prefetch past the last element re-reads the current one (a cache hit)
   while (true) {
-    int64_t bn = b + slots;
-    load_item<BF16>(i1, p, bn < batch ? bn : b, dd, nn, zp, zsb);
-    process_item<BF16, Q, EULER>(i0, p, b, d, n0, ok, ch_ok, al2, ra, Dv, has_z);
+    uint32_t bn = b + slots;
+    load_item<BF16>(i1, r, bs, bn < batch ? bn : b, vo_st, vo_ch, vo_n);
+    process_item<BF16, Q, EULER>(i0, p, r, bs, b, vo_st, vo_y, ok, y_lane, al2, ra, Dv, has_z);
     b = bn;
     if (b >= batch) break;
     bn = b + slots;
-    load_item<BF16>(i0, p, bn < batch ? bn : b, dd, nn, zp, zsb);
-    process_item<BF16, Q, EULER>(i1, p, b, d, n0, ok, ch_ok, al2, ra, Dv, has_z);
+    load_item<BF16>(i0, r, bs, bn < batch ? bn : b, vo_st, vo_ch, vo_n);
+    process_item<BF16, Q, EULER>(i1, p, r, bs, b, vo_st, vo_y, ok, y_lane, al2, ra, Dv, has_z);
     b = bn;
     if (b >= batch) break;
   }
@@ -252,7 +316,16 @@ hipError_t launch_io(const UpdateParams& p, hipStream_t stream) {
   auto rows_ok = [&](const void* ptr, int64_t sb, int64_t sn, int64_t es, int64_t al) {
     return sn == 1 && ((uintptr_t)ptr % al) == 0 && (sb * es) % al == 0;
   };
-  const bool vec = p.N % 4 == 0 && ((uintptr_t)p.state % 16) == 0 && rows_ok(p.A, p.As_d, p.As_n, 4, 16) &&
+  // buffer offsets are 32-bit: every tensor must span less than 2 GiB
+  const int64_t ye = (p.y_f32 || !BF16) ? 4 : 2;
+  auto small = [&](int64_t last_elem, int64_t es) { return (last_elem + 1) * es < ((int64_t)1 << 31); };
+  const bool spans = small(p.batch * p.D * p.N - 1, 4) && small((p.batch - 1) * p.xs_b + p.D - 1, e) &&
+                     small((p.batch - 1) * p.ds_b + p.D - 1, e) &&
+                     (!p.z || small((p.batch - 1) * p.zs_b + p.D - 1, e)) &&
+                     small((p.batch - 1) * p.Bs_b + p.N - 1, e) && small((p.batch - 1) * p.Cs_b + p.N - 1, e) &&
+                     small((p.batch - 1) * p.ys_b + p.D - 1, ye) && small((p.D - 1) * p.As_d + p.N - 1, 4) &&
+                     (!p.Dskip || small((p.D - 1) * p.Ds_d, 4));
+  const bool vec = spans && p.N % 4 == 0 && ((uintptr_t)p.state % 16) == 0 && rows_ok(p.A, p.As_d, p.As_n, 4, 16) &&
                    rows_ok(p.B, p.Bs_b, p.Bs_n, e, rowbytes) && rows_ok(p.C, p.Cs_b, p.Cs_n, e, rowbytes);
   if (vec) {
     const int q = (int)((p.N + 3) / 4);
