@@ -15,6 +15,13 @@ and it shares no code with it.
   chunk cumulative decay, chunk states, state passing, chunk scan -- and returns
   every intermediate so that each GPU step can be checked on its own.  It is
   pinned to the recurrence by the tests (any chunk size gives the same y).
+* ``selective_scan(..., delta_softplus=True, delta_bias=b)`` first replaces
+  delta by softplus(delta + b) (tildalice.io SelectiveSSM listing: delta is
+  the softplus of its projection, which carries a bias).
+* ``causal_conv1d`` is the Mamba block's per-channel Conv1D of width k with
+  k - 1 steps of zero padding cut back to the first L outputs, then SiLU
+  (tildalice.io, Mamba 블록 아키텍처 and the SelectiveSSM listing), as a direct
+  sum in C.
 """
 from __future__ import annotations
 
@@ -58,7 +65,9 @@ def _load():
         vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.oracle_selective_scan.restype = ci
         lib.oracle_selective_scan.argtypes = [i64, i64, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
-                                              vp, vp, ci, ci]
+                                              vp, vp, ci, ci, ci, vp]
+        lib.oracle_causal_conv1d.restype = ci
+        lib.oracle_causal_conv1d.argtypes = [i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, ci]
         lib.oracle_ssd.restype = ci
         lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp,
                                    vp, ci, ci]
@@ -88,12 +97,15 @@ def _io(a, io):
     return np.ascontiguousarray(a, dtype=np.uint16 if io == "bf16" else np.float32)
 
 
-def selective_scan(inp: dict, io: str, euler: bool = False, h0=None, rows=None, nthreads=None, mutation=0):
+def selective_scan(inp: dict, io: str, euler: bool = False, h0=None, rows=None, nthreads=None, mutation=0,
+                   delta_softplus: bool = False, delta_bias=None):
     """Reference scan.
 
     inp: x, delta (batch, L, D); A (D, N) fp32; B, C (batch, L, N); optional
     D (D,) fp32 and z (batch, L, D).  bf16 tensors are uint16 bit patterns.
     h0: optional (batch, D, N).  rows: optional flat ids b*D + d.
+    delta_softplus: delta <- softplus(delta + delta_bias) (delta_bias (D,)
+    fp32, optional).
     Returns (y, h_last): (batch, L, D) and (batch, D, N) float64, or
     (nrows, L) and (nrows, N) when rows is given.
     """
@@ -111,7 +123,8 @@ def selective_scan(inp: dict, io: str, euler: bool = False, h0=None, rows=None, 
     hl = np.empty((nr, N), np.float64)
     rc = _load().oracle_selective_scan(batch, L, D, N, 1 if io == "bf16" else 0, 1 if euler else 0, _ptr(x),
                                        _ptr(dl), _ptr(A), _ptr(B), _ptr(C), _ptr(Dk), _ptr(z), _ptr(h0c), _ptr(r),
-                                       nr, _ptr(y), _ptr(hl), nthreads or threads(), mutation)
+                                       nr, _ptr(y), _ptr(hl), nthreads or threads(), mutation,
+                                       1 if delta_softplus else 0, _ptr(_c(delta_bias, np.float32)))
     if rc != 0:
         raise ValueError("oracle_selective_scan rejected its arguments")
     if r is None:
@@ -149,6 +162,30 @@ def ssd(inp: dict, io: str, ngroups: int = 1, euler: bool = False, h0=None, rows
     if r is None:
         return (y.reshape(batch, H, P, L).transpose(0, 3, 1, 2).copy(), hl.reshape(batch, H, P, N))
     return y, hl
+
+
+CONV_MUTATIONS = {1: "taps reversed", 2: "window one step late", 3: "sigmoid in place of SiLU"}
+
+
+def causal_conv1d(x, weight, io: str, bias=None, silu: bool = True, mutation: int = 0):
+    """Causal depthwise convolution (+ bias, + SiLU), fp64.
+
+    x: (batch, L, D) in the io dtype (bf16 as uint16 bit patterns); weight
+    (D, W) fp32; bias (D,) fp32 or None.  out[b,t,d] = bias[d] +
+    sum_k weight[d,k] x[b, t-(W-1)+k, d] with x = 0 before t = 0, then SiLU.
+    Returns (batch, L, D) float64.
+    """
+    xc = _io(x, io)
+    w = _c(weight, np.float32)
+    bc = _c(bias, np.float32)
+    batch, L, D = xc.shape
+    assert w.ndim == 2 and w.shape[0] == D and (bc is None or bc.shape == (D,))
+    out = np.empty((batch, L, D), np.float64)
+    rc = _load().oracle_causal_conv1d(batch, L, D, w.shape[1], 1 if io == "bf16" else 0, _ptr(xc), _ptr(w),
+                                      _ptr(bc), 1 if silu else 0, _ptr(out), mutation)
+    if rc != 0:
+        raise ValueError("oracle_causal_conv1d rejected its arguments")
+    return out
 
 
 def _f64(a, io):

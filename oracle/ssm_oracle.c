@@ -23,6 +23,14 @@
  *   matrix D feeds the input straight to the output):  y_t += D x_t
  *   Gate (tildalice.io, Mamba 블록 아키텍처 and the SelectiveSSM listing:
  *   the scan output is multiplied by SiLU(z)):  y_t *= z_t * sigmoid(z_t)
+ *   Optional step-size transform (same listing: delta is the softplus of a
+ *   projection, and its delta projection carries a bias):
+ *       delta_t <- softplus(delta_t + bias_d),  softplus(v) = log(1 + e^v)
+ *
+ * The causal depthwise convolution in front of the scan (tildalice.io, Mamba
+ * 블록 아키텍처 and the SelectiveSSM listing: a per-channel Conv1D of width k
+ * with k - 1 steps of zero padding, cut back to the first L outputs, then
+ * SiLU) is oracle_causal_conv1d below.
  *
  * The SSD form (obsidian-dorae222 "Mamba-2", sections on the semiseparable
  * matrix and SSD tiling) is the same recurrence with one scalar A per head:
@@ -52,12 +60,17 @@ static double rd(const void* p, int bf16, int64_t i) {
   return bf16 ? bf16_to_double(((const uint16_t*)p)[i]) : (double)((const float*)p)[i];
 }
 
+/* log(1 + e^v) without overflow or cancellation. */
+static double softplus(double v) { return v > 0 ? v + log1p(exp(-v)) : log1p(exp(v)); }
+
 /* One row of the scan.  All offsets/strides are in elements. */
 typedef struct {
   int64_t L, N;
   int bf16, euler, mutation;
   const void *x, *delta, *B, *C, *z;   /* io dtype */
   const float *A, *Dskip;              /* fp32 */
+  const float* dbias;                  /* delta bias (fp32), used with dsoftplus */
+  int dsoftplus;                       /* delta <- softplus(delta + dbias) */
   const double* h0;                    /* fp64, may be null */
   int64_t x_off, x_st;                 /* x[t] = x[x_off + t*x_st], same for z */
   int64_t d_off, d_st;                 /* delta[t] */
@@ -76,6 +89,7 @@ static void scan_row(const row_t* r, double* h) {
     if (r->mutation == 4 && t > 0) tx -= r->x_st;          /* off-by-one in time */
     double xt = rd(r->x, r->bf16, tx);
     double dt = rd(r->delta, r->bf16, r->d_off + t * r->d_st);
+    if (r->dsoftplus) dt = softplus(dt + (r->dbias ? (double)r->dbias[r->D_off] : 0.0));
     double y = 0.0;
     for (int64_t n = 0; n < N; ++n) {
       double a = (double)r->A[r->a_off + n * r->a_st];
@@ -116,6 +130,8 @@ typedef struct {
   int bf16, euler, mutation;
   const void *x, *delta, *B, *C, *z;
   const float *A, *Dskip;
+  const float* dbias;
+  int dsoftplus;
   const double* h0;
   const int64_t* rows;               /* flat row ids: b*D + d                */
   int64_t nrows;
@@ -131,7 +147,7 @@ static void make_row(const problem_t* p, int64_t r, row_t* rw) {
   rw->L = p->L; rw->N = p->N;
   rw->bf16 = p->bf16; rw->euler = p->euler; rw->mutation = p->mutation;
   rw->x = p->x; rw->delta = p->delta; rw->B = p->B; rw->C = p->C; rw->z = p->z;
-  rw->A = p->A; rw->Dskip = p->Dskip;
+  rw->A = p->A; rw->Dskip = p->Dskip; rw->dbias = p->dbias; rw->dsoftplus = p->dsoftplus;
   rw->h0 = p->h0 ? p->h0 + id * p->N : 0;
   rw->y = p->y + r * p->L;
   rw->h_last = p->h_last ? p->h_last + r * p->N : 0;
@@ -192,17 +208,20 @@ static int run(problem_t* p, int nthreads) {
  * Selective scan.  Contiguous inputs:
  *   x, delta, z: (batch, L, D)   B, C: (batch, L, N)   A: (D, N)   Dskip: (D)
  *   h0: (batch, D, N) fp64 or NULL.  Dskip / z NULL when off.
+ * dsoftplus: delta <- softplus(delta + dbias[d]) (dbias (D) fp32 or NULL = 0).
  * rows: flat ids b*D + d to compute (NULL = all batch*D rows, nrows = batch*D).
  * Outputs: y (nrows, L) and h_last (nrows, N) or NULL, fp64.
  */
 int oracle_selective_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int bf16, int euler,
                           const void* x, const void* delta, const float* A, const void* B, const void* C,
                           const float* Dskip, const void* z, const double* h0, const int64_t* rows,
-                          int64_t nrows, double* y, double* h_last, int nthreads, int mutation) {
+                          int64_t nrows, double* y, double* h_last, int nthreads, int mutation, int dsoftplus,
+                          const float* dbias) {
   problem_t p;
   memset(&p, 0, sizeof(p));
   p.kind = 0; p.batch = batch; p.L = L; p.D = D; p.N = N;
   p.bf16 = bf16; p.euler = euler; p.mutation = mutation;
+  p.dsoftplus = dsoftplus; p.dbias = dbias;
   p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = Dskip; p.z = z; p.h0 = h0;
   p.rows = rows; p.nrows = nrows; p.y = y; p.h_last = h_last;
   return run(&p, nthreads);
@@ -226,4 +245,34 @@ int oracle_ssd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_
   p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = Dskip; p.z = 0; p.h0 = h0;
   p.rows = rows; p.nrows = nrows; p.y = y; p.h_last = h_last;
   return run(&p, nthreads);
+}
+
+/*
+ * Causal depthwise convolution, per channel d of batch element b:
+ *     out[b,t,d] = bias[d] + sum_{k=0}^{W-1} w[d,k] * x[b, t - (W-1) + k, d]
+ * with x = 0 before t = 0 (the W - 1 steps of left padding of the page's
+ * Conv1D, whose output is cut back to the first L steps), then SiLU if silu:
+ * out <- out * sigmoid(out).  x: (batch, L, D) contiguous in the io dtype;
+ * w: (D, W) fp32; bias: (D) fp32 or NULL.  out: (batch, L, D) fp64.
+ * `mutation` (tests only): 1 taps reversed, 2 window one step late,
+ * 3 SiLU replaced by sigmoid.
+ */
+int oracle_causal_conv1d(int64_t batch, int64_t L, int64_t D, int64_t W, int bf16, const void* x, const float* w,
+                         const float* bias, int silu, double* out, int mutation) {
+  if (W < 1) return -1;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t t = 0; t < L; ++t)
+      for (int64_t d = 0; d < D; ++d) {
+        double acc = bias ? (double)bias[d] : 0.0;
+        for (int64_t k = 0; k < W; ++k) {
+          int64_t src = t - (W - 1) + k;
+          if (mutation == 2) src -= 1;
+          if (src < 0) continue;
+          double wk = (double)w[d * W + (mutation == 1 ? W - 1 - k : k)];
+          acc += wk * rd(x, bf16, (b * L + src) * D + d);
+        }
+        if (silu) acc = mutation == 3 ? 1.0 / (1.0 + exp(-acc)) : acc / (1.0 + exp(-acc));
+        out[(b * L + t) * D + d] = acc;
+      }
+  return 0;
 }
