@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 #define SSM_MAX_DIMS 5
 #define SSM_SCAN_MAX_DSTATE 64 /* selective scan: N <= 64 */
 
@@ -77,11 +77,15 @@ typedef struct {
 } ssm_tensor_desc;
 
 /* descriptor flags */
-#define SSM_HAS_Z 1u       /* gate y by silu(z)                  (scan only) */
+#define SSM_HAS_Z 1u       /* gate y by silu(z)               (scan, decode) */
 #define SSM_HAS_D 2u       /* add D * x                                       */
 #define SSM_DISC_EULER 4u  /* Bbar = delta * B instead of zero-order hold     */
 #define SSM_HAS_H0 8u      /* start from h0 instead of 0                      */
 #define SSM_WANT_HLAST 16u /* write the final state to h_last                 */
+#define SSM_DELTA_SOFTPLUS 32u /* delta <- softplus(delta [+ delta_bias[d]])  (scan, decode) */
+#define SSM_HAS_DELTA_BIAS 64u /* with SSM_DELTA_SOFTPLUS: add delta_bias first (scan, decode) */
+#define SSM_HAS_BIAS 128u      /* conv: add bias[d]                                   */
+#define SSM_SILU 256u          /* conv: apply SiLU to the output                      */
 
 /* ------------------------------------------------------------------ scan */
 
@@ -94,7 +98,13 @@ typedef struct {
  *   D        : (dim)          F32                if SSM_HAS_D, any stride
  *   h0       : (batch, dim, dstate) F32 contiguous   if SSM_HAS_H0
  *   h_last   : (batch, dim, dstate) F32 contiguous   if SSM_WANT_HLAST
+ *   delta_bias: (dim)         F32                if SSM_HAS_DELTA_BIAS, any stride
  * io is SSM_F32 or SSM_BF16 and is the same for x, delta, z, B, C.
+ * SSM_DELTA_SOFTPLUS: the step size used is softplus(delta + delta_bias[d])
+ * (softplus(v) = log(1 + e^v); delta_bias taken as 0 without
+ * SSM_HAS_DELTA_BIAS) -- the Mamba block computes delta as the softplus of a
+ * projection with a bias ("Mamba 논문 리뷰", tildalice.io, SelectiveSSM
+ * listing).
  * Descriptors of tensors a flag turns off are ignored.
  * Limit: for x, delta, z, y, (16 * stride[1] + 16 * stride[2]) elements, and
  * for B, C, (16 * stride[1] + dstate * stride[2]) elements, must span less
@@ -102,7 +112,7 @@ typedef struct {
 typedef struct {
   int64_t batch, seqlen, dim, dstate;
   uint32_t flags;
-  ssm_tensor_desc x, delta, A, B, C, D, z, y, h0, h_last;
+  ssm_tensor_desc x, delta, A, B, C, D, z, y, h0, h_last, delta_bias;
 } ssm_scan_desc;
 
 typedef struct {
@@ -116,6 +126,7 @@ typedef struct {
   void* y;
   const float* h0;  /* NULL unless SSM_HAS_H0     */
   float* h_last;    /* NULL unless SSM_WANT_HLAST */
+  const float* delta_bias; /* NULL unless SSM_HAS_DELTA_BIAS */
 } ssm_scan_ptrs;
 
 /* ------------------------------------------------------------------- SSD */
@@ -170,13 +181,15 @@ typedef struct {
  *   A        : (dim, dstate) F32          any strides (0 = shared)
  *   D        : (dim) F32                  if SSM_HAS_D, any stride
  *   state    : (batch, dim, dstate) F32 contiguous, read and overwritten
- * Flags: SSM_HAS_Z, SSM_HAS_D, SSM_DISC_EULER (SSM_HAS_H0 / SSM_WANT_HLAST
- * are not accepted: the state is both).  y and state may not overlap each
+ *   delta_bias: (dim) F32                 if SSM_HAS_DELTA_BIAS, any stride
+ * Flags: SSM_HAS_Z, SSM_HAS_D, SSM_DISC_EULER, SSM_DELTA_SOFTPLUS,
+ * SSM_HAS_DELTA_BIAS (as in the scan); SSM_HAS_H0 / SSM_WANT_HLAST are not
+ * accepted: the state is both.  y and state may not overlap each
  * other or any input.  dstate <= SSM_SCAN_MAX_DSTATE. */
 typedef struct {
   int64_t batch, dim, dstate;
   uint32_t flags;
-  ssm_tensor_desc x, delta, A, B, C, D, z, y, state;
+  ssm_tensor_desc x, delta, A, B, C, D, z, y, state, delta_bias;
 } ssm_update_desc;
 
 typedef struct {
@@ -189,7 +202,36 @@ typedef struct {
   const void* z;   /* NULL unless SSM_HAS_Z */
   void* y;
   float* state;
+  const float* delta_bias; /* NULL unless SSM_HAS_DELTA_BIAS */
 } ssm_update_ptrs;
+
+/* ------------------------------------------------------------------ conv */
+
+/* Causal depthwise convolution in front of the scan: the Mamba block's
+ * per-channel Conv1D of width k with k - 1 steps of zero padding, cut back to
+ * the first seqlen outputs, then SiLU ("Mamba 논문 리뷰", tildalice.io, Mamba
+ * 블록 아키텍처 and the SelectiveSSM listing).  For every b, t, d:
+ *     y[b,t,d] = bias[d] + sum_{k=0}^{width-1} weight[d,k] * x[b, t-width+1+k, d]
+ * with x = 0 before t = 0; then y <- y * sigmoid(y) if SSM_SILU.
+ * Required tensors (shape, dtype):
+ *   x      : (batch, seqlen, dim)  io (F32 or BF16)   innermost stride 1
+ *   y      : (batch, seqlen, dim)  io or F32           innermost stride 1
+ *   weight : (dim, width) F32                          any strides
+ *   bias   : (dim) F32            if SSM_HAS_BIAS,     any stride
+ * Flags: SSM_HAS_BIAS, SSM_SILU.  1 <= width <= 8.  y may not overlap x
+ * (the convolution is not computed in place) nor the weights. */
+typedef struct {
+  int64_t batch, seqlen, dim, width;
+  uint32_t flags;
+  ssm_tensor_desc x, weight, bias, y;
+} ssm_conv_desc;
+
+typedef struct {
+  const void* x;
+  const float* weight;
+  const float* bias; /* NULL unless SSM_HAS_BIAS */
+  void* y;
+} ssm_conv_ptrs;
 
 /* --------------------------------------------------------------- entries */
 
@@ -250,6 +292,10 @@ ssm_status ssm_ssd_chunk_scan(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, cons
 
 /* One decode step (definition above ssm_update_desc).  No workspace. */
 ssm_status ssm_selective_state_update(const ssm_update_desc* d, const ssm_update_ptrs* p, void* hip_stream);
+
+/* Causal depthwise convolution (+ bias, + SiLU) (definition above
+ * ssm_conv_desc).  No workspace. */
+ssm_status ssm_causal_conv1d_fwd(const ssm_conv_desc* d, const ssm_conv_ptrs* p, void* hip_stream);
 
 #ifdef __cplusplus
 }

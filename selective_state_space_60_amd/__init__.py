@@ -21,12 +21,15 @@ SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_STRIDE, SSM_ERR_ALIG
     SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE, SSM_ERR_HIP = range(10)
 SSM_F32, SSM_BF16, SSM_F16 = 0, 1, 2
 SSM_HAS_Z, SSM_HAS_D, SSM_DISC_EULER, SSM_HAS_H0, SSM_WANT_HLAST = 1, 2, 4, 8, 16
+SSM_DELTA_SOFTPLUS, SSM_HAS_DELTA_BIAS, SSM_HAS_BIAS, SSM_SILU = 32, 64, 128, 256
+ABI_VERSION = 2
 MAX_DIMS = 5
 
 # Every function include/ssm.h declares.
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_hip_error", "ssm_selective_scan_workspace_size",
            "ssm_selective_scan_fwd", "ssm_ssd_chunk_workspace_size", "ssm_ssd_chunk_fwd", "ssm_ssd_chunk_cumsum",
-           "ssm_ssd_chunk_state", "ssm_ssd_state_passing", "ssm_ssd_chunk_scan", "ssm_selective_state_update")
+           "ssm_ssd_chunk_state", "ssm_ssd_state_passing", "ssm_ssd_chunk_scan", "ssm_selective_state_update",
+           "ssm_causal_conv1d_fwd")
 
 
 class TensorDesc(ctypes.Structure):
@@ -34,9 +37,10 @@ class TensorDesc(ctypes.Structure):
                 ("stride", ctypes.c_int64 * MAX_DIMS)]
 
 
-_SCAN_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "h0", "h_last")
+_SCAN_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "h0", "h_last", "delta_bias")
 _SSD_T = ("x", "delta", "A", "B", "C", "D", "y", "h0", "h_last")
-_UPD_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "state")
+_UPD_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "state", "delta_bias")
+_CONV_T = ("x", "weight", "bias", "y")
 
 
 class ScanDesc(ctypes.Structure):
@@ -65,6 +69,15 @@ class UpdateDesc(ctypes.Structure):
 
 class UpdatePtrs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _UPD_T]
+
+
+class ConvDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("width", ctypes.c_int64), ("flags", ctypes.c_uint32)] + [(n, TensorDesc) for n in _CONV_T]
+
+
+class ConvPtrs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _CONV_T]
 
 
 class SSMError(RuntimeError):
@@ -100,9 +113,10 @@ def lib() -> ctypes.CDLL:
         L.ssm_ssd_state_passing.argtypes = [P(SSDDesc), P(SSDPtrs), vp, vp, vp, vp]
         L.ssm_ssd_chunk_scan.argtypes = [P(SSDDesc), P(SSDPtrs), vp, vp, vp, vp]
         L.ssm_selective_state_update.argtypes = [P(UpdateDesc), P(UpdatePtrs), vp]
+        L.ssm_causal_conv1d_fwd.argtypes = [P(ConvDesc), P(ConvPtrs), vp]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = ctypes.c_int
-        if L.ssm_abi_version() != 1:
+        if L.ssm_abi_version() != ABI_VERSION:
             raise ImportError("libssm ABI version mismatch")
         _lib = L
     return _lib
@@ -154,21 +168,28 @@ def _workspace(nbytes: int, device):
 
 # -------------------------------------------------------------------- scan
 
-def scan_desc(x, delta, A, B, C, D=None, z=None, y=None, h0=None, h_last=None, euler=False) -> ScanDesc:
+def _delta_flags(delta_softplus, delta_bias):
+    if delta_bias is not None and not delta_softplus:
+        raise ValueError("delta_bias is only used with delta_softplus=True")
+    return (SSM_DELTA_SOFTPLUS if delta_softplus else 0) | (SSM_HAS_DELTA_BIAS if delta_bias is not None else 0)
+
+
+def scan_desc(x, delta, A, B, C, D=None, z=None, y=None, h0=None, h_last=None, euler=False,
+              delta_softplus=False, delta_bias=None) -> ScanDesc:
     d = ScanDesc()
     d.batch, d.seqlen, d.dim = x.shape
     d.dstate = A.shape[-1]
     d.flags = ((SSM_HAS_Z if z is not None else 0) | (SSM_HAS_D if D is not None else 0) |
                (SSM_DISC_EULER if euler else 0) | (SSM_HAS_H0 if h0 is not None else 0) |
-               (SSM_WANT_HLAST if h_last is not None else 0))
-    for name, t in zip(_SCAN_T, (x, delta, A, B, C, D, z, y, h0, h_last)):
+               (SSM_WANT_HLAST if h_last is not None else 0) | _delta_flags(delta_softplus, delta_bias))
+    for name, t in zip(_SCAN_T, (x, delta, A, B, C, D, z, y, h0, h_last, delta_bias)):
         setattr(d, name, tensor_desc(t))
     return d
 
 
-def scan_ptrs(x, delta, A, B, C, D=None, z=None, y=None, h0=None, h_last=None) -> ScanPtrs:
+def scan_ptrs(x, delta, A, B, C, D=None, z=None, y=None, h0=None, h_last=None, delta_bias=None) -> ScanPtrs:
     p = ScanPtrs()
-    for name, t in zip(_SCAN_T, (x, delta, A, B, C, D, z, y, h0, h_last)):
+    for name, t in zip(_SCAN_T, (x, delta, A, B, C, D, z, y, h0, h_last, delta_bias)):
         setattr(p, name, _p(t))
     return p
 
@@ -181,18 +202,19 @@ def selective_scan_workspace_size(desc: ScanDesc) -> int:
 
 
 def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, euler=False, want_hlast=False,
-                       y_dtype=None, y=None, stream=None):
+                       y_dtype=None, y=None, stream=None, delta_softplus=False, delta_bias=None):
     """y = selective scan of x (see include/ssm.h).  Returns (y, h_last or None).
 
     x, delta, z: (batch, L, dim); B, C: (batch, L, dstate); A: (dim, dstate)
     fp32; D: (dim,) fp32; h0: (batch, dim, dstate) fp32.  x/delta/z/B/C are all
-    fp32 or all bf16; y defaults to x's dtype."""
+    fp32 or all bf16; y defaults to x's dtype.  delta_softplus: the step size
+    is softplus(delta + delta_bias) (delta_bias (dim,) fp32, optional)."""
     if y is None:
         y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
     h_last = torch.empty((x.shape[0], x.shape[2], A.shape[-1]), dtype=torch.float32,
                          device=x.device) if want_hlast else None
-    desc = scan_desc(x, delta, A, B, C, D, z, y, h0, h_last, euler)
-    ptrs = scan_ptrs(x, delta, A, B, C, D, z, y, h0, h_last)
+    desc = scan_desc(x, delta, A, B, C, D, z, y, h0, h_last, euler, delta_softplus, delta_bias)
+    ptrs = scan_ptrs(x, delta, A, B, C, D, z, y, h0, h_last, delta_bias)
     nbytes = selective_scan_workspace_size(desc)
     ws = _workspace(nbytes, x.device)
     _check(lib().ssm_selective_scan_fwd(ctypes.byref(desc), ctypes.byref(ptrs), _p(ws), nbytes, _stream(stream)),
@@ -302,33 +324,67 @@ def ssd_chunk_scan(x, delta, A, B, C, chunk, A_cum, beta, S_in, D=None, euler=Fa
 
 # ------------------------------------------------------------------ decode
 
-def update_desc(x, delta, A, B, C, state, D=None, z=None, y=None, euler=False) -> UpdateDesc:
+def update_desc(x, delta, A, B, C, state, D=None, z=None, y=None, euler=False, delta_softplus=False,
+                delta_bias=None) -> UpdateDesc:
     d = UpdateDesc()
     d.batch, d.dim = x.shape
     d.dstate = A.shape[-1]
     d.flags = ((SSM_HAS_Z if z is not None else 0) | (SSM_HAS_D if D is not None else 0) |
-               (SSM_DISC_EULER if euler else 0))
-    for name, t in zip(_UPD_T, (x, delta, A, B, C, D, z, y, state)):
+               (SSM_DISC_EULER if euler else 0) | _delta_flags(delta_softplus, delta_bias))
+    for name, t in zip(_UPD_T, (x, delta, A, B, C, D, z, y, state, delta_bias)):
         setattr(d, name, tensor_desc(t))
     return d
 
 
-def update_ptrs(x, delta, A, B, C, state, D=None, z=None, y=None) -> UpdatePtrs:
+def update_ptrs(x, delta, A, B, C, state, D=None, z=None, y=None, delta_bias=None) -> UpdatePtrs:
     p = UpdatePtrs()
-    for name, t in zip(_UPD_T, (x, delta, A, B, C, D, z, y, state)):
+    for name, t in zip(_UPD_T, (x, delta, A, B, C, D, z, y, state, delta_bias)):
         setattr(p, name, _p(t))
     return p
 
 
 def selective_state_update(state, x, delta, A, B, C, D=None, z=None, euler=False, y_dtype=None, y=None,
-                           stream=None):
+                           stream=None, delta_softplus=False, delta_bias=None):
     """One decode step (see include/ssm.h): advances ``state`` (batch, dim,
     dstate) fp32 in place and returns y (batch, dim).  x, delta, z: (batch,
-    dim); B, C: (batch, dstate); A: (dim, dstate) fp32; D: (dim,) fp32."""
+    dim); B, C: (batch, dstate); A: (dim, dstate) fp32; D: (dim,) fp32;
+    delta_softplus / delta_bias as in selective_scan_fwd."""
     if y is None:
         y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
-    desc = update_desc(x, delta, A, B, C, state, D, z, y, euler)
-    ptrs = update_ptrs(x, delta, A, B, C, state, D, z, y)
+    desc = update_desc(x, delta, A, B, C, state, D, z, y, euler, delta_softplus, delta_bias)
+    ptrs = update_ptrs(x, delta, A, B, C, state, D, z, y, delta_bias)
     _check(lib().ssm_selective_state_update(ctypes.byref(desc), ctypes.byref(ptrs), _stream(stream)),
            "ssm_selective_state_update")
+    return y
+
+
+# -------------------------------------------------------------------- conv
+
+def conv_desc(x, weight, bias=None, y=None, silu=True) -> ConvDesc:
+    d = ConvDesc()
+    d.batch, d.seqlen, d.dim = x.shape
+    d.width = weight.shape[-1]
+    d.flags = (SSM_HAS_BIAS if bias is not None else 0) | (SSM_SILU if silu else 0)
+    for name, t in zip(_CONV_T, (x, weight, bias, y)):
+        setattr(d, name, tensor_desc(t))
+    return d
+
+
+def conv_ptrs(x, weight, bias=None, y=None) -> ConvPtrs:
+    p = ConvPtrs()
+    for name, t in zip(_CONV_T, (x, weight, bias, y)):
+        setattr(p, name, _p(t))
+    return p
+
+
+def causal_conv1d(x, weight, bias=None, silu=True, y_dtype=None, y=None, stream=None):
+    """Causal depthwise convolution (+ bias, + SiLU) (see include/ssm.h).
+    x: (batch, L, dim) fp32 or bf16; weight: (dim, width) fp32, width <= 8;
+    bias: (dim,) fp32.  Returns y (batch, L, dim), x's dtype by default."""
+    if y is None:
+        y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
+    desc = conv_desc(x, weight, bias, y, silu)
+    ptrs = conv_ptrs(x, weight, bias, y)
+    _check(lib().ssm_causal_conv1d_fwd(ctypes.byref(desc), ctypes.byref(ptrs), _stream(stream)),
+           "ssm_causal_conv1d_fwd")
     return y

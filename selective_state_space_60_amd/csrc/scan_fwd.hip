@@ -373,14 +373,37 @@ struct Lane {
   float ez[KS];  // 1 where A == 0, else 0
 };
 
-// This lane's step (lane%16) of its channel (tid/16) for the tile in `buf`.
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|); log1p(w) is taken
+// as log(u) * w / (u - 1) with u = 1 + w (u - 1 is exact), which keeps its
+// relative accuracy for small w.
+__device__ __forceinline__ float softplus_f32(float v) {
+  constexpr float kLn2 = 0.6931471805599453f;
+  const float w = __builtin_amdgcn_exp2f(-fabsf(v) * kLog2e);
+  const float u = 1.f + w;
+  const float lp = u == 1.f ? w : (__builtin_amdgcn_logf(u) * kLn2) * (w * __builtin_amdgcn_rcpf(u - 1.f));
+  return fmaxf(v, 0.f) + lp;
+}
+
+// Step-size transform of a lane: delta <- softplus(delta + bias) on the
+// lane's steps inside the sequence; padding steps keep delta = 0 (no change
+// of the state).
+struct DeltaXform {
+  bool on;
+  float bias;
+};
+
+// This lane's step (lane%16) of its channel (tid/16) for the tile in `buf`;
+// `valid`: that step lies inside the stretch.
 template <int KS, int FORM>
-__device__ __forceinline__ void take_hold(const ScanSmem<KS>& s, int buf, bool want_z, Hold& hd) {
+__device__ __forceinline__ void take_hold(const ScanSmem<KS>& s, int buf, bool want_z, Hold& hd,
+                                          const DeltaXform& dx, bool valid) {
   const int tid = threadIdx.x;
   const float2 v = s.hx[buf][tid / G][tid % G];
-  hd.dt = v.x;
+  float dt = v.x;
+  if (dx.on) dt = valid ? softplus_f32(dt + dx.bias) : 0.f;
+  hd.dt = dt;
   hd.x = v.y;
-  hd.xs = FORM == kFormEuler ? v.x * v.y : v.y;
+  hd.xs = FORM == kFormEuler ? dt * v.y : v.y;
   hd.z = want_z ? s.hz[buf][tid / G][tid % G] : 0.f;
 }
 
@@ -465,7 +488,8 @@ __device__ __forceinline__ void finalize_tile(ScanSmem<KS>& s, int buf, const fl
 // delta (the steps it holds).
 template <class L, int KS, int MODE, int FORM>
 __device__ __forceinline__ void walk(ScanSmem<KS>& s, L& ld, const Tiles& tl, float (&h)[KS], const Lane<KS>& ln,
-                                     const float (&fA)[G], float Dk, bool want_z, float& sum_dt) {
+                                     const float (&fA)[G], float Dk, bool want_z, float& sum_dt,
+                                     const DeltaXform& dx) {
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, sg = tid % G;
   float* prow = &s.part[wave][sg][G * (lane / G)];
@@ -490,7 +514,8 @@ __device__ __forceinline__ void walk(ScanSmem<KS>& s, L& ld, const Tiles& tl, fl
   // around them would make the compiler wait for them at once.
   auto body = [&](int it, typename L::Set& rn) {
     const int buf = it & 1;
-    take_hold<KS, FORM>(s, buf, want_z, hd);
+    const int rows = it < tl.ntiles - 1 ? TT : (it == tl.ntiles - 1 ? tl.last_rows : 0);
+    take_hold<KS, FORM>(s, buf, want_z, hd, dx, sg < rows);
     float4 o[2][2][KS];
     read_block<KS>(s, buf, 0, sg, o[0]);
     scan_blocks<KS, FORM, MODE == 0, 0>(s, prow, buf, sg, h, ln, hd, o);
@@ -643,6 +668,9 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
 #pragma unroll
   for (int n = 0; n < G; ++n) fA[n] = 1.f;
   float sum_dt = 0.f;
+  DeltaXform dx;
+  dx.on = p.dsoftplus != 0;
+  dx.bias = (dx.on && p.dbias && d_ok) ? p.dbias[d * p.dbs_d] : 0.f;
   if (KS == 1 && form == kFormG) {
     // g form: the finalize weighs the partial of state n by 1/A of the lane's channel.
     if (MODE == 0) {
@@ -655,15 +683,15 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
     }
 #pragma unroll
     for (int k = 0; k < KS; ++k) h[k] *= Av[k];  // g = A h
-    walk<decltype(ld), KS, MODE, kFormG>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt);
+    walk<decltype(ld), KS, MODE, kFormG>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx);
 #pragma unroll
     for (int k = 0; k < KS; ++k) h[k] *= ln.iA[k];  // h = g / A
   } else if (form == kFormEuler) {
-    walk<decltype(ld), KS, MODE, kFormEuler>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt);
+    walk<decltype(ld), KS, MODE, kFormEuler>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx);
   } else if (form == kFormHZero) {
-    walk<decltype(ld), KS, MODE, kFormHZero>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt);
+    walk<decltype(ld), KS, MODE, kFormHZero>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx);
   } else {
-    walk<decltype(ld), KS, MODE, kFormH>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt);
+    walk<decltype(ld), KS, MODE, kFormH>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx);
   }
 
   if (MODE == 1) {

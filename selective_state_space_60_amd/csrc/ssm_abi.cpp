@@ -14,9 +14,11 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr uint32_t kScanFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_WANT_HLAST;
+constexpr uint32_t kScanFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_WANT_HLAST |
+                                SSM_DELTA_SOFTPLUS | SSM_HAS_DELTA_BIAS;
 constexpr uint32_t kSSDFlags = SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_WANT_HLAST;
-constexpr uint32_t kUpdateFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER;
+constexpr uint32_t kUpdateFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER | SSM_DELTA_SOFTPLUS | SSM_HAS_DELTA_BIAS;
+constexpr uint32_t kConvFlags = SSM_HAS_BIAS | SSM_SILU;
 constexpr int kSimds = 256 * 4;  // MI355X: 256 compute units x 4 SIMDs
 
 int64_t esize(int32_t dt) { return dt == SSM_BF16 || dt == SSM_F16 ? 2 : 4; }
@@ -115,6 +117,7 @@ ssm_status validate_scan_desc(const ssm_scan_desc* d) {
   if (!d) return SSM_ERR_NULL;
   if (d->batch <= 0 || d->seqlen <= 0 || d->dim <= 0 || d->dstate <= 0) return SSM_ERR_SHAPE;
   if (d->flags & ~kScanFlags) return SSM_ERR_UNSUPPORTED;
+  if ((d->flags & SSM_HAS_DELTA_BIAS) && !(d->flags & SSM_DELTA_SOFTPLUS)) return SSM_ERR_UNSUPPORTED;
   if (d->dstate > SSM_SCAN_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
   const int32_t io = d->x.dtype;
   if (io == SSM_F16) return SSM_ERR_UNSUPPORTED;
@@ -140,6 +143,8 @@ ssm_status validate_scan_desc(const ssm_scan_desc* d) {
     if ((s = check_tensor(d->h0, 3, bdn, d->h0.dtype == SSM_F32, false, true))) return s;
   if (d->flags & SSM_WANT_HLAST)
     if ((s = check_tensor(d->h_last, 3, bdn, d->h_last.dtype == SSM_F32, false, true))) return s;
+  if (d->flags & SSM_HAS_DELTA_BIAS)
+    if ((s = check_tensor(d->delta_bias, 1, dd, d->delta_bias.dtype == SSM_F32, false, false))) return s;
   // The kernel addresses one tile of rows (and, for B and C, all N states of
   // a row) with 32-bit byte offsets from the tile's first element.
   const int64_t e = esize(io), ey = esize(d->y.dtype);
@@ -162,6 +167,8 @@ ssm_status validate_scan_ptrs(const ssm_scan_desc* d, const ssm_scan_ptrs* p) {
   if ((f & SSM_HAS_D) && !p->D) return SSM_ERR_NULL;
   if ((f & SSM_HAS_H0) && !p->h0) return SSM_ERR_NULL;
   if ((f & SSM_WANT_HLAST) && !p->h_last) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_DELTA_BIAS) && !p->delta_bias) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_DELTA_BIAS) && !aligned(p->delta_bias, 4)) return SSM_ERR_ALIGN;
   const int64_t io = esize(d->x.dtype);
   if (!aligned(p->x, io) || !aligned(p->delta, io) || !aligned(p->B, io) || !aligned(p->C, io) ||
       !aligned(p->A, 4) || !aligned(p->y, esize(d->y.dtype)))
@@ -176,7 +183,8 @@ ssm_status validate_scan_ptrs(const ssm_scan_desc* d, const ssm_scan_ptrs* p) {
                       span_of(d->C, p->C),
                       (f & SSM_HAS_D) ? span_of(d->D, p->D) : Span(),
                       (f & SSM_HAS_Z) ? span_of(d->z, p->z) : Span(),
-                      (f & SSM_HAS_H0) ? span_of(d->h0, p->h0) : Span()};
+                      (f & SSM_HAS_H0) ? span_of(d->h0, p->h0) : Span(),
+                      (f & SSM_HAS_DELTA_BIAS) ? span_of(d->delta_bias, p->delta_bias) : Span()};
   const Span ys = span_of(d->y, p->y);
   const Span hl = (f & SSM_WANT_HLAST) ? span_of(d->h_last, p->h_last) : Span();
   for (const Span& s : ins)
@@ -313,6 +321,7 @@ ssm_status validate_update(const ssm_update_desc* d, const ssm_update_ptrs* p) {
   if (!d || !p) return SSM_ERR_NULL;
   if (d->batch <= 0 || d->dim <= 0 || d->dstate <= 0) return SSM_ERR_SHAPE;
   if (d->flags & ~kUpdateFlags) return SSM_ERR_UNSUPPORTED;
+  if ((d->flags & SSM_HAS_DELTA_BIAS) && !(d->flags & SSM_DELTA_SOFTPLUS)) return SSM_ERR_UNSUPPORTED;
   if (d->dstate > SSM_SCAN_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
   // one workgroup per (batch element, 16..256 channels): the grid is 1-D
   if (d->dim > (1 << 30) || d->batch * ((d->dim + 15) / 16) >= ((int64_t)1 << 31)) return SSM_ERR_UNSUPPORTED;
@@ -338,7 +347,11 @@ ssm_status validate_update(const ssm_update_desc* d, const ssm_update_ptrs* p) {
     if ((s = check_tensor(d->z, 2, bd, d->z.dtype == io, true, false))) return s;
   if (f & SSM_HAS_D)
     if ((s = check_tensor(d->D, 1, dd, d->D.dtype == SSM_F32, false, false))) return s;
+  if (f & SSM_HAS_DELTA_BIAS)
+    if ((s = check_tensor(d->delta_bias, 1, dd, d->delta_bias.dtype == SSM_F32, false, false))) return s;
   if (!p->x || !p->delta || !p->A || !p->B || !p->C || !p->y || !p->state) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_DELTA_BIAS) && (!p->delta_bias)) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_DELTA_BIAS) && !aligned(p->delta_bias, 4)) return SSM_ERR_ALIGN;
   if ((f & SSM_HAS_Z) && !p->z) return SSM_ERR_NULL;
   if ((f & SSM_HAS_D) && !p->D) return SSM_ERR_NULL;
   const int64_t e = esize(io);
@@ -352,12 +365,47 @@ ssm_status validate_update(const ssm_update_desc* d, const ssm_update_ptrs* p) {
                       span_of(d->B, p->B),
                       span_of(d->C, p->C),
                       (f & SSM_HAS_D) ? span_of(d->D, p->D) : Span(),
-                      (f & SSM_HAS_Z) ? span_of(d->z, p->z) : Span()};
+                      (f & SSM_HAS_Z) ? span_of(d->z, p->z) : Span(),
+                      (f & SSM_HAS_DELTA_BIAS) ? span_of(d->delta_bias, p->delta_bias) : Span()};
   const Span ys = span_of(d->y, p->y);
   const Span st = span_of(d->state, p->state);
   for (const Span& sp : ins)
     if (overlap(ys, sp) || overlap(st, sp)) return SSM_ERR_ALIAS;
   if (overlap(ys, st)) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
+// ------------------------------------------------------------------ conv
+
+ssm_status validate_conv(const ssm_conv_desc* d, const ssm_conv_ptrs* p) {
+  if (!d || !p) return SSM_ERR_NULL;
+  if (d->batch <= 0 || d->seqlen <= 0 || d->dim <= 0 || d->width <= 0) return SSM_ERR_SHAPE;
+  if (d->flags & ~kConvFlags) return SSM_ERR_UNSUPPORTED;
+  if (d->width > ssm::kConvMaxWidth) return SSM_ERR_UNSUPPORTED;
+  // grid: (channel blocks) x (32-step runs) x batch workgroups, 1-D
+  if (d->batch * ((d->seqlen + 31) / 32) * ((d->dim + 255) / 256) >= ((int64_t)1 << 31)) return SSM_ERR_UNSUPPORTED;
+  const int32_t io = d->x.dtype;
+  if (io == SSM_F16) return SSM_ERR_UNSUPPORTED;
+  const bool io_ok = io == SSM_F32 || io == SSM_BF16;
+  const uint32_t f = d->flags;
+  const int64_t bld[3] = {d->batch, d->seqlen, d->dim};
+  const int64_t dw[2] = {d->dim, d->width};
+  const int64_t dd[1] = {d->dim};
+  ssm_status s;
+  if ((s = check_tensor(d->x, 3, bld, io_ok, true, false))) return s;
+  if ((s = check_tensor(d->y, 3, bld, d->y.dtype == io || d->y.dtype == SSM_F32, true, false))) return s;
+  if (!non_overlapping(d->y)) return SSM_ERR_STRIDE;
+  if ((s = check_tensor(d->weight, 2, dw, d->weight.dtype == SSM_F32, false, false))) return s;
+  if (f & SSM_HAS_BIAS)
+    if ((s = check_tensor(d->bias, 1, dd, d->bias.dtype == SSM_F32, false, false))) return s;
+  if (!p->x || !p->weight || !p->y) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_BIAS) && !p->bias) return SSM_ERR_NULL;
+  if (!aligned(p->x, esize(io)) || !aligned(p->y, esize(d->y.dtype)) || !aligned(p->weight, 4)) return SSM_ERR_ALIGN;
+  if ((f & SSM_HAS_BIAS) && !aligned(p->bias, 4)) return SSM_ERR_ALIGN;
+  const Span ys = span_of(d->y, p->y);
+  if (overlap(ys, span_of(d->x, p->x)) || overlap(ys, span_of(d->weight, p->weight)) ||
+      ((f & SSM_HAS_BIAS) && overlap(ys, span_of(d->bias, p->bias))))
+    return SSM_ERR_ALIAS;
   return SSM_OK;
 }
 
@@ -428,6 +476,9 @@ ssm_status ssm_selective_scan_fwd(const ssm_scan_desc* d, const ssm_scan_ptrs* p
   q.flags = f;
   q.io_bf16 = d->x.dtype == SSM_BF16;
   q.y_f32 = d->y.dtype == SSM_F32;
+  q.dsoftplus = (f & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+  q.dbias = (f & SSM_HAS_DELTA_BIAS) ? p->delta_bias : nullptr;
+  q.dbs_d = (f & SSM_HAS_DELTA_BIAS) ? d->delta_bias.stride[0] : 0;
   q.n_seg = pl.n_seg;
   q.seg_len = pl.seg_len;
   if (pl.n_seg > 1) {
@@ -528,6 +579,23 @@ ssm_status ssm_ssd_chunk_scan(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, cons
   return hip_status(ssm::launch_ssd_chunk_scan(q, (hipStream_t)hip_stream));
 }
 
+ssm_status ssm_causal_conv1d_fwd(const ssm_conv_desc* d, const ssm_conv_ptrs* p, void* hip_stream) {
+  ssm_status s = validate_conv(d, p);
+  if (s) return s;
+  ssm::ConvParams q;
+  std::memset(&q, 0, sizeof(q));
+  q.x = p->x; q.w = p->weight; q.bias = (d->flags & SSM_HAS_BIAS) ? p->bias : nullptr; q.y = p->y;
+  q.batch = d->batch; q.L = d->seqlen; q.D = d->dim; q.W = d->width;
+  q.xs_b = d->x.stride[0]; q.xs_t = d->x.stride[1];
+  q.ys_b = d->y.stride[0]; q.ys_t = d->y.stride[1];
+  q.ws_d = d->weight.stride[0]; q.ws_k = d->weight.stride[1];
+  q.bs_d = (d->flags & SSM_HAS_BIAS) ? d->bias.stride[0] : 0;
+  q.io_bf16 = d->x.dtype == SSM_BF16;
+  q.y_f32 = d->y.dtype == SSM_F32;
+  q.silu = (d->flags & SSM_SILU) ? 1 : 0;
+  return hip_status(ssm::launch_causal_conv1d(q, (hipStream_t)hip_stream));
+}
+
 ssm_status ssm_selective_state_update(const ssm_update_desc* d, const ssm_update_ptrs* p, void* hip_stream) {
   ssm_status s = validate_update(d, p);
   if (s) return s;
@@ -546,6 +614,9 @@ ssm_status ssm_selective_state_update(const ssm_update_desc* d, const ssm_update
   q.euler = (f & SSM_DISC_EULER) ? 1 : 0;
   q.io_bf16 = d->x.dtype == SSM_BF16;
   q.y_f32 = d->y.dtype == SSM_F32;
+  q.dsoftplus = (f & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+  q.dbias = (f & SSM_HAS_DELTA_BIAS) ? p->delta_bias : nullptr;
+  q.dbs_d = (f & SSM_HAS_DELTA_BIAS) ? d->delta_bias.stride[0] : 0;
   return hip_status(ssm::launch_selective_state_update(q, (hipStream_t)hip_stream));
 }
 

@@ -32,6 +32,11 @@ struct ScanParams {
   float* agg_H;  // (batch, n_seg-1, D, N): end state of segment s scanned from 0
   float* agg_S;  // (batch, n_seg-1, D): sum of delta over segment s
   float* h_in;   // (batch, n_seg, D, N): state entering segment s
+  // Step-size transform: delta <- softplus(delta + dbias[d * dbs_d]) when
+  // dsoftplus (dbias may be null: bias 0).
+  const float* dbias;
+  int64_t dbs_d;
+  int dsoftplus;
 };
 
 // Tiling of the scan kernels (also used by the host planner).
@@ -58,9 +63,29 @@ struct UpdateParams {
   int euler;
   int io_bf16;
   int y_f32;
+  const float* dbias;  // delta <- softplus(delta + dbias[d * dbs_d]) when dsoftplus
+  int64_t dbs_d;
+  int dsoftplus;
 };
 
 hipError_t launch_selective_state_update(const UpdateParams& p, hipStream_t stream);
+
+// --------------------------------------------------------------------- conv
+struct ConvParams {
+  const void* x;       // (batch, L, D), innermost stride 1
+  const float* w;      // (D, W)
+  const float* bias;   // (D) or null
+  void* y;             // (batch, L, D), innermost stride 1
+  int64_t batch, L, D, W;
+  int64_t xs_b, xs_t, ys_b, ys_t, ws_d, ws_k, bs_d;  // element strides
+  int io_bf16;
+  int y_f32;
+  int silu;
+};
+
+constexpr int kConvMaxWidth = 8;
+
+hipError_t launch_causal_conv1d(const ConvParams& p, hipStream_t stream);
 
 // ---------------------------------------------------------------------- SSD
 struct SSDParams {

@@ -53,6 +53,15 @@ __device__ __forceinline__ float bbar_coef(float t, float e, float dt, float ra)
   }
 }
 
+// softplus(v) = max(v, 0) + log1p(e^-|v|), log1p(w) = log(u) * w / (u - 1),
+// u = 1 + w (u - 1 is exact).
+__device__ __forceinline__ float softplus_f32(float v) {
+  const float w = __builtin_amdgcn_exp2f(-fabsf(v) * kLog2e);
+  const float u = 1.f + w;
+  const float lp = u == 1.f ? w : (__builtin_amdgcn_logf(u) * kLn2) * (w * __builtin_amdgcn_rcpf(u - 1.f));
+  return fmaxf(v, 0.f) + lp;
+}
+
 __device__ __forceinline__ float gate(float v, float Dv, float x, float z, bool has_z) {
   v = __builtin_fmaf(Dv, x, v);
   return has_z ? v * (z * __builtin_amdgcn_rcpf(1.f + __expf(-z))) : v;
@@ -150,10 +159,12 @@ template <bool BF16, int Q, bool EULER>
 __device__ __forceinline__ void process_item(const Item& it, const UpdateParams& p, const Rsrc& r,
                                              const BStride& bs, uint32_t b, int vo_st, int vo_y, bool ok,
                                              bool y_lane, const float (&al2)[4], const float (&ra)[4], float Dv,
-                                             bool has_z) {
+                                             bool has_z, float dbias) {
   const float hin[4] = {__uint_as_float(it.h.x), __uint_as_float(it.h.y), __uint_as_float(it.h.z),
                         __uint_as_float(it.h.w)};
-  const float xv = scal<BF16>(it.x), dt = scal<BF16>(it.dt);
+  const float xv = scal<BF16>(it.x);
+  float dt = scal<BF16>(it.dt);
+  if (p.dsoftplus) dt = softplus_f32(dt + dbias);
   float hv[4];
   float yp = 0.f;
 #pragma unroll
@@ -213,10 +224,15 @@ __global__ __launch_bounds__(NT) void update_kernel(UpdateParams p, unsigned til
   const float Dl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                  rsrc(p.Dskip ? p.Dskip : p.A),
                                                  p.Dskip ? (int)(dd * p.Ds_d) * 4 : 0, 0, 0));
+  const bool has_db = p.dsoftplus && p.dbias;
+  const float dbl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  rsrc(has_db ? p.dbias : p.A), has_db ? (int)(dd * p.dbs_d) * 4 : 0,
+                                                  0, 0));
   Item i0, i1;
   uint32_t b = slot;
   load_item<BF16>(i0, r, bs, b, vo_st, vo_ch, vo_n);
   const float Dv = p.Dskip ? Dl : 0.f;
+  const float dbias = has_db ? dbl : 0.f;
   float al2[4], ra[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -228,12 +244,12 @@ __global__ __launch_bounds__(NT) void update_kernel(UpdateParams p, unsigned til
   while (true) {
     uint32_t bn = b + slots;
     load_item<BF16>(i1, r, bs, bn < batch ? bn : b, vo_st, vo_ch, vo_n);
-    process_item<BF16, Q, EULER>(i0, p, r, bs, b, vo_st, vo_y, ok, y_lane, al2, ra, Dv, has_z);
+    process_item<BF16, Q, EULER>(i0, p, r, bs, b, vo_st, vo_y, ok, y_lane, al2, ra, Dv, has_z, dbias);
     b = bn;
     if (b >= batch) break;
     bn = b + slots;
     load_item<BF16>(i0, r, bs, bn < batch ? bn : b, vo_st, vo_ch, vo_n);
-    process_item<BF16, Q, EULER>(i1, p, r, bs, b, vo_st, vo_y, ok, y_lane, al2, ra, Dv, has_z);
+    process_item<BF16, Q, EULER>(i1, p, r, bs, b, vo_st, vo_y, ok, y_lane, al2, ra, Dv, has_z, dbias);
     b = bn;
     if (b >= batch) break;
   }
@@ -259,8 +275,9 @@ __global__ __launch_bounds__(NT) void update_kernel_any(UpdateParams p, unsigned
   const int64_t zsb = has_z ? p.zs_b : p.xs_b;
   float* hrow = p.state + (b * p.D + dd) * p.N;
   const float xv = ld<BF16>(p.x, b * p.xs_b + dd);
-  const float dt = ld<BF16>(p.delta, b * p.ds_b + dd);
+  float dt = ld<BF16>(p.delta, b * p.ds_b + dd);
   const float zv = ld<BF16>(zp, b * zsb + dd);
+  if (p.dsoftplus) dt = softplus_f32(dt + (p.dbias ? p.dbias[(int64_t)dd * p.dbs_d] : 0.f));
   const float Dl = *(p.Dskip ? p.Dskip + (int64_t)dd * p.Ds_d : p.A);
   float a[KS], Bn[KS], Cn[KS], h[KS];
 #pragma unroll
@@ -324,7 +341,8 @@ hipError_t launch_io(const UpdateParams& p, hipStream_t stream) {
                      (!p.z || small((p.batch - 1) * p.zs_b + p.D - 1, e)) &&
                      small((p.batch - 1) * p.Bs_b + p.N - 1, e) && small((p.batch - 1) * p.Cs_b + p.N - 1, e) &&
                      small((p.batch - 1) * p.ys_b + p.D - 1, ye) && small((p.D - 1) * p.As_d + p.N - 1, 4) &&
-                     (!p.Dskip || small((p.D - 1) * p.Ds_d, 4));
+                     (!p.Dskip || small((p.D - 1) * p.Ds_d, 4)) &&
+                     (!(p.dsoftplus && p.dbias) || small((p.D - 1) * p.dbs_d, 4));
   const bool vec = spans && p.N % 4 == 0 && ((uintptr_t)p.state % 16) == 0 && rows_ok(p.A, p.As_d, p.As_n, 4, 16) &&
                    rows_ok(p.B, p.Bs_b, p.Bs_n, e, rowbytes) && rows_ok(p.C, p.Cs_b, p.Cs_n, e, rowbytes);
   if (vec) {

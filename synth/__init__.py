@@ -24,7 +24,8 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 NORMAL, UNIFORM, SOFTPLUS_NORMAL, NEG_EXP_UNIFORM, NEG_IDX, CONST = range(6)
 
 # Stream ids: one per tensor role, so tensors never share random numbers.
-STREAM = {"x": 1, "delta": 2, "A": 3, "B": 4, "C": 5, "D": 6, "z": 7, "h0": 8}
+STREAM = {"x": 1, "delta": 2, "A": 3, "B": 4, "C": 5, "D": 6, "z": 7, "h0": 8, "delta_bias": 9, "conv_w": 10,
+          "conv_b": 11}
 
 
 def build(force: bool = False) -> str:
@@ -141,6 +142,27 @@ class ScanSpec:
 
 
 @dataclass(frozen=True)
+class ConvSpec:
+    """Causal depthwise convolution: x, y (batch, L, D); weight (D, width); bias (D)."""
+    name: str
+    batch: int
+    seqlen: int
+    dim: int
+    width: int
+    io: str
+    has_bias: bool = True
+    silu: bool = True
+    x: Dist = Dist(NORMAL, 0.0, 1.0)
+    w: Dist = Dist(NORMAL, 0.0, 0.5)
+    b: Dist = Dist(NORMAL, 0.0, 1.0)
+
+    def algorithmic_bytes(self) -> int:
+        """x read once, y written once (io dtype); weights and bias once."""
+        e = 2 if self.io == "bf16" else 4
+        return 2 * e * self.batch * self.seqlen * self.dim + 4 * self.dim * (self.width + (1 if self.has_bias else 0))
+
+
+@dataclass(frozen=True)
 class SSDSpec:
     """SSD (scalar A per head) problem: x, y (batch, L, H, P); delta (batch, L, H);
     A (H); B, C (batch, L, G, N); D (H)."""
@@ -182,6 +204,9 @@ SSD2_7B = SSDSpec("ssd2.7b_b4_l4096_h80_p64_n64_g1_q256_bf16", 4, 4096, 80, 64, 
 DECODE2_8B = ScanSpec("decode_mamba2.8b_b64_d5120_n16_bf16", 64, 1, 5120, 16, "bf16", True, True,
                       A=Dist(NEG_IDX, period=16), delta=Dist(SOFTPLUS_NORMAL, -3.0, 1.0))
 
+# The Mamba-2.8B layer's Conv1D (width 4) in front of its scan.
+CONV2_8B = ConvSpec("conv_mamba2.8b_b4_l4096_d5120_w4_bf16", 4, 4096, 5120, 4, "bf16")
+
 SCAN_CONFIGS = {s.name: s for s in (TINY, MAMBA130M, MAMBA2_8B, LONG1M)}
 
 
@@ -213,6 +238,26 @@ def scan_inputs(s: ScanSpec, seed: int = 0) -> dict:
     if s.has_z:
         out["z"] = fill((s.batch, s.seqlen, s.dim), s.z, io, seed, STREAM["z"])
     return out
+
+
+def conv_spec(base: ConvSpec, **kw) -> ConvSpec:
+    if "name" not in kw:
+        kw["name"] = base.name + "_" + "_".join("%s%s" % (k, v) for k, v in sorted(kw.items()))
+    return replace(base, **kw)
+
+
+def conv_inputs(s: ConvSpec, seed: int = 0) -> dict:
+    """Host arrays: x (batch, L, D) io; weight (D, width) fp32; bias (D,) fp32 if on."""
+    out = {"x": fill((s.batch, s.seqlen, s.dim), s.x, s.io, seed, STREAM["x"]),
+           "weight": fill((s.dim, s.width), s.w, "f32", seed, STREAM["conv_w"])}
+    if s.has_bias:
+        out["bias"] = fill((s.dim,), s.b, "f32", seed, STREAM["conv_b"])
+    return out
+
+
+def delta_bias_input(dim: int, seed: int = 0, dist: Dist = Dist(NORMAL, -4.0, 1.0)) -> np.ndarray:
+    """A per-channel fp32 bias for the softplus step-size transform."""
+    return fill((dim,), dist, "f32", seed, STREAM["delta_bias"])
 
 
 def ssd_inputs(s: SSDSpec, seed: int = 0) -> dict:

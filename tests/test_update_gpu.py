@@ -200,3 +200,30 @@ def test_nan_stays_in_its_channel():
     assert np.all(np.isfinite(np.delete(y, 5, axis=2)))
     st = host_f64(state)
     assert np.all(np.isnan(st[0, 5])) and np.all(np.isfinite(np.delete(st, 5, axis=1)))
+
+
+@pytest.mark.parametrize("io,N,strided", [("f32", 16, False), ("bf16", 16, False), ("f32", 6, False),
+                                           ("bf16", 16, True)])
+def test_delta_softplus(io, N, strided):
+    """delta <- softplus(delta + bias), vector and generic paths, chained
+    steps against the oracle's scan with the same transform."""
+    base = synth.TINY if io == "f32" else synth.MAMBA130M
+    spec = synth.scan_spec(base, batch=3, seqlen=4, dim=72, dstate=N, io=io, has_z=True, has_D=True,
+                           A=synth.Dist(synth.NEG_EXP_UNIFORM, -1.0, 1.0), delta=synth.Dist(synth.NORMAL, 0.0, 1.0))
+    inp = synth.scan_inputs(spec, 15)
+    db = synth.delta_bias_input(72, 15)
+    h0 = synth.state_input((3, 72, N), 15)
+    banner("update softplus %s N%d strided%d" % (io, N, strided))
+    g = _upload(spec, inp)
+    A = g["A"].t().contiguous().t() if strided else g["A"]
+    state = torch.from_numpy(h0).cuda()
+    dbd = torch.from_numpy(db).cuda()
+    ys = []
+    for t in range(4):
+        ys.append(ssm.selective_state_update(state, g["x"][:, t], g["delta"][:, t], A, g["B"][:, t], g["C"][:, t],
+                                             D=g["D"], z=g["z"][:, t], y_dtype=torch.float32, delta_softplus=True,
+                                             delta_bias=dbd))
+    torch.cuda.synchronize()
+    yr, hr = oracle.selective_scan(inp, io, h0=h0.astype(np.float64), delta_softplus=True, delta_bias=db)
+    assert_close(np.stack([host_f64(v) for v in ys], axis=1), yr, "f32", "update softplus y")
+    assert_close(host_f64(state), hr, "f32", "update softplus state")
