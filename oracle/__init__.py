@@ -22,6 +22,11 @@ and it shares no code with it.
   k - 1 steps of zero padding cut back to the first L outputs, then SiLU
   (tildalice.io, Mamba 블록 아키텍처 and the SelectiveSSM listing), as a direct
   sum in C.
+* ``mamba_block`` composes one Mamba block in fp64 in the order of the block
+  figure and listing of the same page: in_proj, conv + SiLU, x_proj (B, C,
+  dt), dt_proj, the selective scan with softplus(delta + bias), the D skip and
+  the SiLU(z) gate, out_proj.  Matrix products are numpy's; the conv and the
+  scan are the functions above.
 """
 from __future__ import annotations
 
@@ -94,7 +99,11 @@ def _c(a, dtype):
 def _io(a, io):
     if a is None:
         return None
-    return np.ascontiguousarray(a, dtype=np.uint16 if io == "bf16" else np.float32)
+    return np.ascontiguousarray(a, dtype={"bf16": np.uint16, "f32": np.float32, "f64": np.float64}[io])
+
+
+def _mode(io):
+    return {"f32": 0, "bf16": 1, "f64": 2}[io]
 
 
 def selective_scan(inp: dict, io: str, euler: bool = False, h0=None, rows=None, nthreads=None, mutation=0,
@@ -121,7 +130,7 @@ def selective_scan(inp: dict, io: str, euler: bool = False, h0=None, rows=None, 
     nr = batch * D if r is None else len(r)
     y = np.empty((nr, L), np.float64)
     hl = np.empty((nr, N), np.float64)
-    rc = _load().oracle_selective_scan(batch, L, D, N, 1 if io == "bf16" else 0, 1 if euler else 0, _ptr(x),
+    rc = _load().oracle_selective_scan(batch, L, D, N, _mode(io), 1 if euler else 0, _ptr(x),
                                        _ptr(dl), _ptr(A), _ptr(B), _ptr(C), _ptr(Dk), _ptr(z), _ptr(h0c), _ptr(r),
                                        nr, _ptr(y), _ptr(hl), nthreads or threads(), mutation,
                                        1 if delta_softplus else 0, _ptr(_c(delta_bias, np.float32)))
@@ -154,7 +163,7 @@ def ssd(inp: dict, io: str, ngroups: int = 1, euler: bool = False, h0=None, rows
     nr = batch * H * P if r is None else len(r)
     y = np.empty((nr, L), np.float64)
     hl = np.empty((nr, N), np.float64)
-    rc = _load().oracle_ssd(batch, L, H, P, N, G, 1 if io == "bf16" else 0, 1 if euler else 0, _ptr(x), _ptr(dl),
+    rc = _load().oracle_ssd(batch, L, H, P, N, G, _mode(io), 1 if euler else 0, _ptr(x), _ptr(dl),
                             _ptr(A), _ptr(B), _ptr(C), _ptr(Dk), _ptr(h0c), _ptr(r), nr, _ptr(y), _ptr(hl),
                             nthreads or threads(), mutation)
     if rc != 0:
@@ -181,7 +190,7 @@ def causal_conv1d(x, weight, io: str, bias=None, silu: bool = True, mutation: in
     batch, L, D = xc.shape
     assert w.ndim == 2 and w.shape[0] == D and (bc is None or bc.shape == (D,))
     out = np.empty((batch, L, D), np.float64)
-    rc = _load().oracle_causal_conv1d(batch, L, D, w.shape[1], 1 if io == "bf16" else 0, _ptr(xc), _ptr(w),
+    rc = _load().oracle_causal_conv1d(batch, L, D, w.shape[1], _mode(io), _ptr(xc), _ptr(w),
                                       _ptr(bc), 1 if silu else 0, _ptr(out), mutation)
     if rc != 0:
         raise ValueError("oracle_causal_conv1d rejected its arguments")
@@ -261,3 +270,48 @@ def ssd_chunked(inp: dict, io: str, chunk: int, ngroups: int = 1, euler: bool = 
             y[:, s:e] += Dk[None, None, :, None] * x[:, s:e]
     return {"y": y, "A_cum": A_cum.transpose(0, 2, 1).copy(), "beta": beta.transpose(0, 2, 1).copy(),
             "S_loc": S_loc, "S_in": S_in, "h_last": state}
+
+
+BLOCK_MUTATIONS = {1: "x and z halves of in_proj swapped", 2: "B and C columns of x_proj swapped",
+                   3: "dt_proj bias dropped", 4: "conv output without SiLU"}
+
+
+def mamba_block(inp: dict, io: str, dstate: int, dt_rank: int, intermediates: bool = False, mutation: int = 0):
+    """One Mamba block forward in fp64.
+
+    inp (synth.block_inputs): u (batch, L, M); W_in (2E, M); conv_w (E, k),
+    conv_b (E); W_x (>= 2N + R, E) with rows B | C | dt (any further rows are
+    ignored); W_dt (E, R), b_dt (E); A (E, N); D (E); W_out (M, E).
+    Steps (tildalice.io "Mamba 논문 리뷰", Mamba 블록 아키텍처 and the
+    SelectiveSSM listing; delta is the softplus of dt_proj of the rank-R slice
+    of x_proj, with dt_proj's bias):
+        xz = u W_in^T;  x, z = xz[..., :E], xz[..., E:]
+        xc = silu(conv(x) + conv_b)
+        B, C, dt = split(xc W_x^T)
+        delta_raw = dt W_dt^T
+        y = scan(xc, softplus(delta_raw + b_dt), A, B, C) + D xc, times silu(z)
+        out = y W_out^T
+    Returns out (batch, L, M) float64 (and a dict of intermediates).
+    """
+    f = lambda k: _f64(inp[k], io)
+    u, W_in, W_x, W_dt, W_out = f("u"), f("W_in"), f("W_x"), f("W_dt"), f("W_out")
+    N, R = dstate, dt_rank
+    E = W_in.shape[0] // 2
+    xz = u @ W_in.T
+    x, z = xz[..., :E], xz[..., E:]
+    if mutation == 1:
+        x, z = z, x
+    xc = causal_conv1d(np.ascontiguousarray(x), inp["conv_w"], "f64", inp["conv_b"], silu=mutation != 4)
+    xd = xc @ W_x.T
+    Bm, Cm, dt = xd[..., :N], xd[..., N:2 * N], xd[..., 2 * N:2 * N + R]
+    if mutation == 2:
+        Bm, Cm = Cm, Bm
+    draw = dt @ W_dt.T
+    sc = {"x": xc, "delta": draw, "A": inp["A"], "B": np.ascontiguousarray(Bm), "C": np.ascontiguousarray(Cm),
+          "D": inp["D"], "z": np.ascontiguousarray(z)}
+    dbias = np.zeros_like(inp["b_dt"]) if mutation == 3 else inp["b_dt"]
+    y, _ = selective_scan(sc, "f64", delta_softplus=True, delta_bias=dbias)
+    out = y @ W_out.T
+    if intermediates:
+        return out, {"xz": xz, "xc": xc, "xd": xd, "delta_raw": draw, "y": y}
+    return out

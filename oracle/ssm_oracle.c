@@ -37,8 +37,8 @@
  * row (b, h, p) scans x[b,:,h,p] with delta[b,:,h], A[h] and the B, C of the
  * head's group.  The oracle computes it as exactly that expanded scan.
  *
- * All arithmetic is fp64 with exp/expm1 from libm.  Inputs stored as bf16 or
- * fp32 are widened exactly.  Rows are independent and are spread over threads.
+ * All arithmetic is fp64 with exp/expm1 from libm.  Inputs stored as bf16, fp32
+ * or fp64 are widened exactly.  Rows are independent and are spread over threads.
  *
  * `mutation` (tests only) plants a deliberate mistake so that the tests can
  * show their pins catch it; 0 means the definition above.
@@ -55,9 +55,11 @@ static double bf16_to_double(uint16_t b) {
   return (double)f;
 }
 
-/* Read element i of an input stored as bf16 bit patterns (bf16=1) or float32. */
-static double rd(const void* p, int bf16, int64_t i) {
-  return bf16 ? bf16_to_double(((const uint16_t*)p)[i]) : (double)((const float*)p)[i];
+/* Read element i of an input stored as float32 (mode 0), bf16 bit patterns
+ * (mode 1) or float64 (mode 2). */
+static double rd(const void* p, int mode, int64_t i) {
+  if (mode == 2) return ((const double*)p)[i];
+  return mode ? bf16_to_double(((const uint16_t*)p)[i]) : (double)((const float*)p)[i];
 }
 
 /* log(1 + e^v) without overflow or cancellation. */
@@ -66,7 +68,7 @@ static double softplus(double v) { return v > 0 ? v + log1p(exp(-v)) : log1p(exp
 /* One row of the scan.  All offsets/strides are in elements. */
 typedef struct {
   int64_t L, N;
-  int bf16, euler, mutation;
+  int io_mode, euler, mutation;
   const void *x, *delta, *B, *C, *z;   /* io dtype */
   const float *A, *Dskip;              /* fp32 */
   const float* dbias;                  /* delta bias (fp32), used with dsoftplus */
@@ -87,15 +89,15 @@ static void scan_row(const row_t* r, double* h) {
   for (int64_t t = 0; t < r->L; ++t) {
     int64_t tx = r->x_off + t * r->x_st;
     if (r->mutation == 4 && t > 0) tx -= r->x_st;          /* off-by-one in time */
-    double xt = rd(r->x, r->bf16, tx);
-    double dt = rd(r->delta, r->bf16, r->d_off + t * r->d_st);
+    double xt = rd(r->x, r->io_mode, tx);
+    double dt = rd(r->delta, r->io_mode, r->d_off + t * r->d_st);
     if (r->dsoftplus) dt = softplus(dt + (r->dbias ? (double)r->dbias[r->D_off] : 0.0));
     double y = 0.0;
     for (int64_t n = 0; n < N; ++n) {
       double a = (double)r->A[r->a_off + n * r->a_st];
       int64_t ib = r->bc_off + t * r->bc_st + n;
-      double Bn = rd(r->B, r->bf16, ib);
-      double Cn = rd(r->C, r->bf16, ib);
+      double Bn = rd(r->B, r->io_mode, ib);
+      double Cn = rd(r->C, r->io_mode, ib);
       if (r->mutation == 3) { double tmp = Bn; Bn = Cn; Cn = tmp; }   /* B and C swapped */
       double u = dt * a;
       if (r->mutation == 2) u = -u;                                  /* sign of the exponent */
@@ -109,7 +111,7 @@ static void scan_row(const row_t* r, double* h) {
     }
     if (r->Dskip && r->mutation != 1) y += (double)r->Dskip[r->D_off] * xt;   /* mutation 1: skip dropped */
     if (r->z) {
-      double zt = rd(r->z, r->bf16, tx);
+      double zt = rd(r->z, r->io_mode, tx);
       double g = zt / (1.0 + exp(-zt));
       if (r->mutation == 7) g = 1.0 / (1.0 + exp(-zt));            /* sigmoid instead of SiLU */
       y *= g;
@@ -127,7 +129,7 @@ typedef struct {
   /* shapes */
   int64_t batch, L, D, N;            /* scan: D channels; ssd: D = H*P      */
   int64_t H, P, G;                   /* ssd only                             */
-  int bf16, euler, mutation;
+  int io_mode, euler, mutation;
   const void *x, *delta, *B, *C, *z;
   const float *A, *Dskip;
   const float* dbias;
@@ -145,7 +147,7 @@ static void make_row(const problem_t* p, int64_t r, row_t* rw) {
   int64_t b = id / p->D, d = id % p->D;
   memset(rw, 0, sizeof(*rw));
   rw->L = p->L; rw->N = p->N;
-  rw->bf16 = p->bf16; rw->euler = p->euler; rw->mutation = p->mutation;
+  rw->io_mode = p->io_mode; rw->euler = p->euler; rw->mutation = p->mutation;
   rw->x = p->x; rw->delta = p->delta; rw->B = p->B; rw->C = p->C; rw->z = p->z;
   rw->A = p->A; rw->Dskip = p->Dskip; rw->dbias = p->dbias; rw->dsoftplus = p->dsoftplus;
   rw->h0 = p->h0 ? p->h0 + id * p->N : 0;
@@ -212,7 +214,7 @@ static int run(problem_t* p, int nthreads) {
  * rows: flat ids b*D + d to compute (NULL = all batch*D rows, nrows = batch*D).
  * Outputs: y (nrows, L) and h_last (nrows, N) or NULL, fp64.
  */
-int oracle_selective_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int bf16, int euler,
+int oracle_selective_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int io_mode, int euler,
                           const void* x, const void* delta, const float* A, const void* B, const void* C,
                           const float* Dskip, const void* z, const double* h0, const int64_t* rows,
                           int64_t nrows, double* y, double* h_last, int nthreads, int mutation, int dsoftplus,
@@ -220,7 +222,7 @@ int oracle_selective_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int bf
   problem_t p;
   memset(&p, 0, sizeof(p));
   p.kind = 0; p.batch = batch; p.L = L; p.D = D; p.N = N;
-  p.bf16 = bf16; p.euler = euler; p.mutation = mutation;
+  p.io_mode = io_mode; p.euler = euler; p.mutation = mutation;
   p.dsoftplus = dsoftplus; p.dbias = dbias;
   p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = Dskip; p.z = z; p.h0 = h0;
   p.rows = rows; p.nrows = nrows; p.y = y; p.h_last = h_last;
@@ -233,7 +235,7 @@ int oracle_selective_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int bf
  *   Dskip: (H) or NULL   h0: (batch, H, P, N) fp64 or NULL
  * rows: flat ids b*(H*P) + h*P + p.  Outputs y (nrows, L), h_last (nrows, N).
  */
-int oracle_ssd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int bf16, int euler,
+int oracle_ssd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int io_mode, int euler,
                const void* x, const void* delta, const float* A, const void* B, const void* C,
                const float* Dskip, const double* h0, const int64_t* rows, int64_t nrows, double* y,
                double* h_last, int nthreads, int mutation) {
@@ -241,7 +243,7 @@ int oracle_ssd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_
   problem_t p;
   memset(&p, 0, sizeof(p));
   p.kind = 1; p.batch = batch; p.L = L; p.D = H * P; p.N = N; p.H = H; p.P = P; p.G = G;
-  p.bf16 = bf16; p.euler = euler; p.mutation = mutation;
+  p.io_mode = io_mode; p.euler = euler; p.mutation = mutation;
   p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = Dskip; p.z = 0; p.h0 = h0;
   p.rows = rows; p.nrows = nrows; p.y = y; p.h_last = h_last;
   return run(&p, nthreads);
@@ -257,7 +259,7 @@ int oracle_ssd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_
  * `mutation` (tests only): 1 taps reversed, 2 window one step late,
  * 3 SiLU replaced by sigmoid.
  */
-int oracle_causal_conv1d(int64_t batch, int64_t L, int64_t D, int64_t W, int bf16, const void* x, const float* w,
+int oracle_causal_conv1d(int64_t batch, int64_t L, int64_t D, int64_t W, int io_mode, const void* x, const float* w,
                          const float* bias, int silu, double* out, int mutation) {
   if (W < 1) return -1;
   for (int64_t b = 0; b < batch; ++b)
@@ -269,7 +271,7 @@ int oracle_causal_conv1d(int64_t batch, int64_t L, int64_t D, int64_t W, int bf1
           if (mutation == 2) src -= 1;
           if (src < 0) continue;
           double wk = (double)w[d * W + (mutation == 1 ? W - 1 - k : k)];
-          acc += wk * rd(x, bf16, (b * L + src) * D + d);
+          acc += wk * rd(x, io_mode, (b * L + src) * D + d);
         }
         if (silu) acc = mutation == 3 ? 1.0 / (1.0 + exp(-acc)) : acc / (1.0 + exp(-acc));
         out[(b * L + t) * D + d] = acc;

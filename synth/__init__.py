@@ -25,7 +25,7 @@ NORMAL, UNIFORM, SOFTPLUS_NORMAL, NEG_EXP_UNIFORM, NEG_IDX, CONST = range(6)
 
 # Stream ids: one per tensor role, so tensors never share random numbers.
 STREAM = {"x": 1, "delta": 2, "A": 3, "B": 4, "C": 5, "D": 6, "z": 7, "h0": 8, "delta_bias": 9, "conv_w": 10,
-          "conv_b": 11}
+          "conv_b": 11, "w_in": 12, "w_x": 13, "w_dt": 14, "w_out": 15, "u": 16}
 
 
 def build(force: bool = False) -> str:
@@ -163,6 +163,33 @@ class ConvSpec:
 
 
 @dataclass(frozen=True)
+class BlockSpec:
+    """A Mamba block: u (batch, L, d_model) -> in_proj (2E) -> conv (width k)
+    + SiLU -> x_proj (B, C, dt of rank R) -> dt_proj (E) -> scan with
+    softplus(delta + b_dt), D skip and SiLU(z) gate -> out_proj (d_model)."""
+    name: str
+    batch: int
+    seqlen: int
+    d_model: int
+    d_inner: int
+    dstate: int
+    dt_rank: int
+    d_conv: int
+    io: str = "bf16"
+
+    @property
+    def xproj_width(self) -> int:
+        """B, C, dt columns of x_proj, padded with zero rows to a multiple of 8."""
+        w = 2 * self.dstate + self.dt_rank
+        return (w + 7) // 8 * 8
+
+    def gemm_flops(self) -> float:
+        t = self.batch * self.seqlen
+        E, M = self.d_inner, self.d_model
+        return 2.0 * t * (M * 2 * E + E * (2 * self.dstate + self.dt_rank) + self.dt_rank * E + E * M)
+
+
+@dataclass(frozen=True)
 class SSDSpec:
     """SSD (scalar A per head) problem: x, y (batch, L, H, P); delta (batch, L, H);
     A (H); B, C (batch, L, G, N); D (H)."""
@@ -203,6 +230,10 @@ SSD2_7B = SSDSpec("ssd2.7b_b4_l4096_h80_p64_n64_g1_q256_bf16", 4, 4096, 80, 64, 
 # (seqlen 1: the state (64, 5120, 16) fp32 is read and written in place).
 DECODE2_8B = ScanSpec("decode_mamba2.8b_b64_d5120_n16_bf16", 64, 1, 5120, 16, "bf16", True, True,
                       A=Dist(NEG_IDX, period=16), delta=Dist(SOFTPLUS_NORMAL, -3.0, 1.0))
+
+# One Mamba-2.8B-shaped block (d_model 2560, expand 2, N 16, conv width 4;
+# the rank of the step-size projection is 1, as in the block listing).
+BLOCK2_8B = BlockSpec("block_mamba2.8b_b4_l4096_dm2560_e5120_n16_r1", 4, 4096, 2560, 5120, 16, 1, 4)
 
 # The Mamba-2.8B layer's Conv1D (width 4) in front of its scan.
 CONV2_8B = ConvSpec("conv_mamba2.8b_b4_l4096_d5120_w4_bf16", 4, 4096, 5120, 4, "bf16")
@@ -253,6 +284,37 @@ def conv_inputs(s: ConvSpec, seed: int = 0) -> dict:
     if s.has_bias:
         out["bias"] = fill((s.dim,), s.b, "f32", seed, STREAM["conv_b"])
     return out
+
+
+def block_spec(base: BlockSpec, **kw) -> BlockSpec:
+    if "name" not in kw:
+        kw["name"] = base.name + "_" + "_".join("%s%s" % (k, v) for k, v in sorted(kw.items()))
+    return replace(base, **kw)
+
+
+def block_inputs(s: BlockSpec, seed: int = 0) -> dict:
+    """Input u and random-init weights of the block (projection weights in the
+    io dtype, (out, in) layout; the rest fp32):
+      W_in (2E, M) ~ N(0, 1/M); conv_w (E, k) ~ N(0, 1/4), conv_b ~ N(0, 1);
+      W_x (xproj_width, E) ~ N(0, 1/E), rows B | C | dt, zero padding rows;
+      W_dt (E, R) ~ N(0, 1/R); b_dt (E) ~ N(-4, 1) (softplus(-4) ~ 0.018);
+      A (E, N) = -(n+1); D (E) ~ N(0, 1); W_out (M, E) ~ N(0, 1/E).
+    """
+    M, E, N, R, io = s.d_model, s.d_inner, s.dstate, s.dt_rank, s.io
+    wx = fill((s.xproj_width, E), Dist(NORMAL, 0.0, E ** -0.5), io, seed, STREAM["w_x"])
+    wx[2 * N + R:] = 0
+    return {
+        "u": fill((s.batch, s.seqlen, M), Dist(NORMAL, 0.0, 1.0), io, seed, STREAM["u"]),
+        "W_in": fill((2 * E, M), Dist(NORMAL, 0.0, M ** -0.5), io, seed, STREAM["w_in"]),
+        "conv_w": fill((E, s.d_conv), Dist(NORMAL, 0.0, 0.5), "f32", seed, STREAM["conv_w"]),
+        "conv_b": fill((E,), Dist(NORMAL, 0.0, 1.0), "f32", seed, STREAM["conv_b"]),
+        "W_x": wx,
+        "W_dt": fill((E, R), Dist(NORMAL, 0.0, R ** -0.5), io, seed, STREAM["w_dt"]),
+        "b_dt": fill((E,), Dist(NORMAL, -4.0, 1.0), "f32", seed, STREAM["delta_bias"]),
+        "A": fill((E, N), Dist(NEG_IDX, period=N), "f32", seed, STREAM["A"]),
+        "D": fill((E,), Dist(NORMAL, 0.0, 1.0), "f32", seed, STREAM["D"]),
+        "W_out": fill((M, E), Dist(NORMAL, 0.0, E ** -0.5), io, seed, STREAM["w_out"]),
+    }
 
 
 def delta_bias_input(dim: int, seed: int = 0, dist: Dist = Dist(NORMAL, -4.0, 1.0)) -> np.ndarray:
