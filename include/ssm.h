@@ -219,7 +219,9 @@ typedef struct {
  *   weight : (dim, width) F32                          any strides
  *   bias   : (dim) F32            if SSM_HAS_BIAS,     any stride
  * Flags: SSM_HAS_BIAS, SSM_SILU.  1 <= width <= 8.  y may not overlap x
- * (the convolution is not computed in place) nor the weights. */
+ * (the convolution is not computed in place) nor the weights.
+ * Limit: 160 * max(x.stride[1], y.stride[1]) + 4096 must be below 2^29
+ * (SSM_ERR_UNSUPPORTED otherwise). */
 typedef struct {
   int64_t batch, seqlen, dim, width;
   uint32_t flags;

@@ -402,6 +402,10 @@ ssm_status validate_conv(const ssm_conv_desc* d, const ssm_conv_ptrs* p) {
   if ((f & SSM_HAS_BIAS) && !p->bias) return SSM_ERR_NULL;
   if (!aligned(p->x, esize(io)) || !aligned(p->y, esize(d->y.dtype)) || !aligned(p->weight, 4)) return SSM_ERR_ALIGN;
   if ((f & SSM_HAS_BIAS) && !aligned(p->bias, 4)) return SSM_ERR_ALIGN;
+  // the kernel addresses a run of 32 + width rows of 1024 channels with
+  // 32-bit byte offsets below 2^29
+  if ((32 + ssm::kConvMaxWidth) * std::max(d->x.stride[1], d->y.stride[1]) * 4 + 1024 * 4 >= ((int64_t)1 << 29))
+    return SSM_ERR_UNSUPPORTED;
   const Span ys = span_of(d->y, p->y);
   if (overlap(ys, span_of(d->x, p->x)) || overlap(ys, span_of(d->weight, p->weight)) ||
       ((f & SSM_HAS_BIAS) && overlap(ys, span_of(d->bias, p->bias))))
@@ -588,6 +592,9 @@ ssm_status ssm_causal_conv1d_fwd(const ssm_conv_desc* d, const ssm_conv_ptrs* p,
   q.batch = d->batch; q.L = d->seqlen; q.D = d->dim; q.W = d->width;
   q.xs_b = d->x.stride[0]; q.xs_t = d->x.stride[1];
   q.ys_b = d->y.stride[0]; q.ys_t = d->y.stride[1];
+  // the kernel drops stores past row L-1 by a range check that needs a row
+  // stride of at least dim; a single row's stride is arbitrary, so give it one
+  if (d->seqlen == 1) { q.xs_t = d->dim; q.ys_t = d->dim; }
   q.ws_d = d->weight.stride[0]; q.ws_k = d->weight.stride[1];
   q.bs_d = (d->flags & SSM_HAS_BIAS) ? d->bias.stride[0] : 0;
   q.io_bf16 = d->x.dtype == SSM_BF16;
