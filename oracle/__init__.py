@@ -18,6 +18,10 @@ and it shares no code with it.
 * ``selective_scan(..., delta_softplus=True, delta_bias=b)`` first replaces
   delta by softplus(delta + b) (tildalice.io SelectiveSSM listing: delta is
   the softplus of its projection, which carries a bias).
+* ``selective_scan_bwd`` is the reverse-mode derivative of ``selective_scan``
+  (the recomputation-based backward of tildalice.io 역전파 시 재계산 computes
+  the same numbers): the forward states of each row, then the adjoint
+  recurrence lam_t = C_t g_t + Abar_{t+1} lam_{t+1} backwards in time.
 * ``causal_conv1d`` is the Mamba block's per-channel Conv1D of width k with
   k - 1 steps of zero padding cut back to the first L outputs, then SiLU
   (tildalice.io, Mamba 블록 아키텍처 and the SelectiveSSM listing), as a direct
@@ -71,6 +75,9 @@ def _load():
         lib.oracle_selective_scan.restype = ci
         lib.oracle_selective_scan.argtypes = [i64, i64, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
                                               vp, vp, ci, ci, ci, vp]
+        lib.oracle_selective_scan_bwd.restype = ci
+        lib.oracle_selective_scan_bwd.argtypes = [i64, i64, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp, ci, vp, vp,
+                                                  ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci]
         lib.oracle_causal_conv1d.restype = ci
         lib.oracle_causal_conv1d.argtypes = [i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, ci]
         lib.oracle_ssd.restype = ci
@@ -171,6 +178,46 @@ def ssd(inp: dict, io: str, ngroups: int = 1, euler: bool = False, h0=None, rows
     if r is None:
         return (y.reshape(batch, H, P, L).transpose(0, 3, 1, 2).copy(), hl.reshape(batch, H, P, N))
     return y, hl
+
+
+BWD_MUTATIONS = {1: "adjoint carried without the decay Abar"}
+
+
+def selective_scan_bwd(inp: dict, io: str, dy, dy_io: str = None, euler: bool = False, h0=None,
+                       delta_softplus: bool = False, delta_bias=None, mutation: int = 0, nthreads=None) -> dict:
+    """Gradients of sum(dy * y) for y = selective_scan(inp, ...), fp64.
+
+    Same inputs as selective_scan; dy (batch, L, D) in dy_io (default io).
+    Returns dict: dx, ddelta (delta as passed in), dz (if z), dA, dB, dC, dD (if
+    D), ddelta_bias (if delta_softplus and delta_bias), dh0 (if h0).
+    """
+    x, dl, B, C, z = (_io(inp.get(k), io) for k in ("x", "delta", "B", "C", "z"))
+    A, Dk = _c(inp["A"], np.float32), _c(inp.get("D"), np.float32)
+    batch, L, D = x.shape
+    N = A.shape[1]
+    dyi = _io(dy, dy_io or io)
+    h0c = _c(h0, np.float64)
+    dbi = _c(delta_bias, np.float32)
+    out = {k: np.empty((batch, L, D)) for k in ("dx", "ddelta")}
+    out["dA"] = np.empty((D, N))
+    out["dB"], out["dC"] = np.empty((batch, L, N)), np.empty((batch, L, N))
+    if z is not None:
+        out["dz"] = np.empty((batch, L, D))
+    if Dk is not None:
+        out["dD"] = np.empty(D)
+    if delta_softplus and dbi is not None:
+        out["ddelta_bias"] = np.empty(D)
+    if h0c is not None:
+        out["dh0"] = np.empty((batch, D, N))
+    rc = _load().oracle_selective_scan_bwd(batch, L, D, N, _mode(io), 1 if euler else 0, _ptr(x), _ptr(dl), _ptr(A),
+                                           _ptr(B), _ptr(C), _ptr(Dk), _ptr(z), _ptr(h0c), 1 if delta_softplus else 0,
+                                           _ptr(dbi), _ptr(dyi), _mode(dy_io or io), _ptr(out["dx"]),
+                                           _ptr(out["ddelta"]), _ptr(out.get("dz")), _ptr(out["dA"]), _ptr(out["dB"]),
+                                           _ptr(out["dC"]), _ptr(out.get("dD")), _ptr(out.get("ddelta_bias")),
+                                           _ptr(out.get("dh0")), nthreads or threads(), mutation)
+    if rc != 0:
+        raise ValueError("oracle_selective_scan_bwd failed")
+    return out
 
 
 CONV_MUTATIONS = {1: "taps reversed", 2: "window one step late", 3: "sigmoid in place of SiLU"}

@@ -46,6 +46,7 @@
 #include <math.h>
 #include <pthread.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 static double bf16_to_double(uint16_t b) {
@@ -277,4 +278,173 @@ int oracle_causal_conv1d(int64_t batch, int64_t L, int64_t D, int64_t W, int io_
         out[(b * L + t) * D + d] = acc;
       }
   return 0;
+}
+
+/*
+ * Backward of the selective scan (reverse-mode derivative of oracle_selective_scan).
+ *
+ * Per row (b, d), with u_t = delta_t a_n, Abar = exp(u), c = expm1(u)/a
+ * (ZOH; delta when a = 0) or delta (Euler), h_t = Abar h_{t-1} + c B_t x_t,
+ * s_t = sum_n C_t h_t, o_t = s_t + D x_t, y_t = o_t silu(z_t):
+ *   g_t   = dy_t silu(z_t)           (dy_t without z)
+ *   dz_t  = dy_t o_t silu'(z_t),     silu'(v) = sig(v) (1 + v (1 - sig(v)))
+ *   dD   += g_t x_t
+ *   lam_t = C_t g_t + Abar_{t+1} lam_{t+1}       (adjoint of h_t; lam_L = 0)
+ *   dC_t += g_t h_t;   dB_t += lam_t c_t x_t
+ *   dx_t  = D g_t + sum_n lam_t c_t B_t
+ *   ddelta_t = sum_n lam_t (dAbar/ddelta h_{t-1} + dc/ddelta B_t x_t)
+ *   da_n += sum_t lam_t (dAbar/da h_{t-1} + dc/da B_t x_t)
+ *   dh0   = Abar_0 lam_0
+ * with dAbar/ddelta = a Abar, dAbar/da = delta Abar, and for ZOH dc/ddelta =
+ * Abar, dc/da = (delta Abar - c)/a (delta^2/2 at a = 0); Euler: 1 and 0.
+ * With dsoftplus the step size is delta = softplus(v), v = delta_in + bias:
+ * ddelta_in = ddelta sig(v), and dbias sums it over b and t.
+ * All inputs contiguous as in oracle_selective_scan.  Outputs fp64: dx,
+ * ddelta, dz (batch, L, D); dA (D, N); dB, dC (batch, L, N); dD, dbias (D);
+ * dh0 (batch, D, N).  dz / dD / dbias / dh0 may be NULL.  Single-threaded.
+ */
+static double sigm(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+typedef struct {
+  int64_t batch, L, D, N;
+  int io_mode, euler, dsoftplus, dy_mode, mutation;
+  const void *x, *delta, *B, *C, *z, *dy;
+  const float *A, *Dskip, *dbias_in;
+  const double* h0;
+  double *dx, *ddelta, *dz, *dA, *dD, *dbias, *dh0;
+  double *dB, *dC;   /* this worker's own accumulators, (batch, L, N) */
+  int64_t d_lo, d_hi; /* channels of this worker */
+  int status;
+} bwd_t;
+
+static void* bwd_worker(void* arg) {
+  bwd_t* w = (bwd_t*)arg;
+  const int64_t L = w->L, D = w->D, N = w->N;
+  double* hs = (double*)malloc(sizeof(double) * (size_t)(L + 1) * (size_t)N);
+  double* lam = (double*)malloc(sizeof(double) * (size_t)N);
+  if (!hs || !lam) { w->status = -1; free(hs); free(lam); return 0; }
+  for (int64_t d = w->d_lo; d < w->d_hi; ++d)
+    for (int64_t b = 0; b < w->batch; ++b) {
+      /* forward: hs[(t+1)*N + n] = h_t, hs[n] = h_{-1} */
+      for (int64_t n = 0; n < N; ++n) hs[n] = w->h0 ? w->h0[(b * D + d) * N + n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t ix = (b * L + t) * D + d;
+        double dt = rd(w->delta, w->io_mode, ix);
+        if (w->dsoftplus) dt = softplus(dt + (w->dbias_in ? (double)w->dbias_in[d] : 0.0));
+        const double xt = rd(w->x, w->io_mode, ix);
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = (double)w->A[d * N + n], u = dt * a;
+          const double c = w->euler ? dt : (a != 0.0 ? expm1(u) / a : dt);
+          hs[(t + 1) * N + n] = exp(u) * hs[t * N + n] + c * rd(w->B, w->io_mode, (b * L + t) * N + n) * xt;
+        }
+      }
+      /* reverse */
+      for (int64_t n = 0; n < N; ++n) lam[n] = 0.0;
+      const double Dd = w->Dskip ? (double)w->Dskip[d] : 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t ix = (b * L + t) * D + d;
+        const double vin = rd(w->delta, w->io_mode, ix);
+        double v = vin, dt = vin;
+        if (w->dsoftplus) { v = vin + (w->dbias_in ? (double)w->dbias_in[d] : 0.0); dt = softplus(v); }
+        const double xt = rd(w->x, w->io_mode, ix);
+        double s = 0.0;
+        for (int64_t n = 0; n < N; ++n) s += rd(w->C, w->io_mode, (b * L + t) * N + n) * hs[(t + 1) * N + n];
+        const double o = s + Dd * xt;
+        const double gy = rd(w->dy, w->dy_mode, ix);
+        double g = gy;
+        if (w->z) {
+          const double zt = rd(w->z, w->io_mode, ix), sg = sigm(zt);
+          g = gy * zt * sg;
+          w->dz[ix] = gy * o * sg * (1.0 + zt * (1.0 - sg));
+        }
+        if (w->dD) w->dD[d] += g * xt;
+        double gx = Dd * g, gdt = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const int64_t ib = (b * L + t) * N + n;
+          const double a = (double)w->A[d * N + n], u = dt * a, Ab = exp(u);
+          const double Bn = rd(w->B, w->io_mode, ib), Cn = rd(w->C, w->io_mode, ib);
+          const double c = w->euler ? dt : (a != 0.0 ? expm1(u) / a : dt);
+          const double hp = hs[t * N + n];
+          /* lam[n] holds Abar_{t+1} lam_{t+1} on entry */
+          const double l = Cn * g + lam[n];
+          w->dC[ib] += g * hs[(t + 1) * N + n];
+          w->dB[ib] += l * c * xt;
+          gx += l * c * Bn;
+          const double dc_ddt = w->euler ? 1.0 : Ab;
+          const double dc_da = w->euler ? 0.0 : (a != 0.0 ? (dt * Ab - c) / a : 0.5 * dt * dt);
+          gdt += l * (a * Ab * hp + dc_ddt * Bn * xt);
+          w->dA[d * N + n] += l * (dt * Ab * hp + dc_da * Bn * xt);
+          lam[n] = (w->mutation == 1 ? 1.0 : Ab) * l;   /* mutation 1: adjoint not decayed */
+        }
+        w->dx[ix] = gx;
+        if (w->dsoftplus) {
+          const double gv = gdt * sigm(v);
+          w->ddelta[ix] = gv;
+          if (w->dbias) w->dbias[d] += gv;
+        } else {
+          w->ddelta[ix] = gdt;
+        }
+      }
+      if (w->dh0)
+        for (int64_t n = 0; n < N; ++n) w->dh0[(b * D + d) * N + n] = lam[n];
+    }
+  free(lam);
+  free(hs);
+  w->status = 0;
+  return 0;
+}
+
+int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int io_mode, int euler,
+                              const void* x, const void* delta, const float* A, const void* B, const void* C,
+                              const float* Dskip, const void* z, const double* h0, int dsoftplus,
+                              const float* dbias_in, const void* dy, int dy_mode, double* dx, double* ddelta,
+                              double* dz, double* dA, double* dB, double* dC, double* dD, double* dbias,
+                              double* dh0, int nthreads, int mutation) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 64) nthreads = 64;
+  if (nthreads > D) nthreads = (int)D;
+  const size_t nbc = (size_t)(batch * L * N);
+  memset(dA, 0, sizeof(double) * (size_t)(D * N));
+  if (dD) memset(dD, 0, sizeof(double) * (size_t)D);
+  if (dbias) memset(dbias, 0, sizeof(double) * (size_t)D);
+  bwd_t w[64];
+  pthread_t th[64];
+  int started[64];
+  int rc = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    memset(&w[i], 0, sizeof(w[i]));
+    w[i].batch = batch; w[i].L = L; w[i].D = D; w[i].N = N;
+    w[i].io_mode = io_mode; w[i].euler = euler; w[i].dsoftplus = dsoftplus; w[i].dy_mode = dy_mode;
+    w[i].mutation = mutation;
+    w[i].x = x; w[i].delta = delta; w[i].B = B; w[i].C = C; w[i].z = z; w[i].dy = dy;
+    w[i].A = A; w[i].Dskip = Dskip; w[i].dbias_in = dbias_in; w[i].h0 = h0;
+    w[i].dx = dx; w[i].ddelta = ddelta; w[i].dz = dz; w[i].dA = dA; w[i].dD = dD; w[i].dbias = dbias;
+    w[i].dh0 = dh0;
+    w[i].dB = (double*)calloc(nbc, sizeof(double));
+    w[i].dC = (double*)calloc(nbc, sizeof(double));
+    w[i].d_lo = D * i / nthreads;
+    w[i].d_hi = D * (i + 1) / nthreads;
+    w[i].status = -1;
+    started[i] = 0;
+    if (!w[i].dB || !w[i].dC) rc = -1;
+  }
+  if (rc == 0) {
+    for (int i = 1; i < nthreads; ++i) started[i] = pthread_create(&th[i], 0, bwd_worker, &w[i]) == 0;
+    bwd_worker(&w[0]);
+    for (int i = 1; i < nthreads; ++i) {
+      if (started[i]) pthread_join(th[i], 0);
+      else bwd_worker(&w[i]);
+    }
+    /* dB, dC: sum of the workers' accumulators in worker order */
+    for (size_t j = 0; j < nbc; ++j) {
+      double sb = 0.0, sc = 0.0;
+      for (int i = 0; i < nthreads; ++i) { sb += w[i].dB[j]; sc += w[i].dC[j]; }
+      dB[j] = sb;
+      dC[j] = sc;
+    }
+    for (int i = 0; i < nthreads; ++i)
+      if (w[i].status) rc = -1;
+  }
+  for (int i = 0; i < nthreads; ++i) { free(w[i].dB); free(w[i].dC); }
+  return rc;
 }
