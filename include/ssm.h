@@ -129,6 +129,66 @@ typedef struct {
   const float* delta_bias; /* NULL unless SSM_HAS_DELTA_BIAS */
 } ssm_scan_ptrs;
 
+/* -------------------------------------------------------- scan backward */
+
+/* Backward of the selective scan with recomputation ("Mamba 논문 리뷰",
+ * tildalice.io, 하드웨어 인식 병렬 알고리즘 / 역전파 시 재계산: the states are not
+ * kept from the forward pass; the backward recomputes them).  Given the
+ * forward inputs and dy = dLoss/dy it writes the gradients of every input:
+ *   g_t   = dy_t silu(z_t) (dy_t without SSM_HAS_Z), dz_t = dy_t o_t silu'(z_t)
+ *           with o_t = C_t.h_t + D x_t
+ *   lam_t = C_t g_t + Abar_{t+1} lam_{t+1}        (adjoint of h_t, lam past the end = 0)
+ *   dx_t  = D g_t + sum_n lam_t Bbar_t;   dB_t += lam_t cbar_t x_t;   dC_t += g_t h_t
+ *   ddelta_t, dA: through Abar = exp(delta A) and Bbar = cbar B (cbar =
+ *   expm1(delta A)/A, or delta with SSM_DISC_EULER); dD += g_t x_t;
+ *   dh0 = Abar_0 lam_0; with SSM_DELTA_SOFTPLUS ddelta is taken through the
+ *   softplus (ddelta_in = ddelta * sigmoid(delta_in + bias)) and ddelta_bias
+ *   sums it over batch and time.
+ * Tensors (shape, dtype):
+ *   x, delta, z, h0, delta_bias, A, B, C, D : as in ssm_scan_desc
+ *   dy          : (batch, seqlen, dim)  io or F32   innermost stride 1
+ *   dx, ddelta  : (batch, seqlen, dim)  io or F32   innermost stride 1
+ *   dz          : (batch, seqlen, dim)  io or F32   if SSM_HAS_Z, innermost stride 1
+ *   dA          : (dim, dstate) F32 contiguous
+ *   dB, dC      : (batch, seqlen, dstate) F32 contiguous
+ *   dD          : (dim) F32 contiguous  if SSM_HAS_D
+ *   dh0         : (batch, dim, dstate) F32 contiguous   if SSM_HAS_H0
+ *   ddelta_bias : (dim) F32 contiguous  if SSM_HAS_DELTA_BIAS
+ * Flags as in the forward except SSM_WANT_HLAST (not accepted).  The sums
+ * over channels (dB, dC) and over batch and time (dA, dD, ddelta_bias) are
+ * formed from per-workgroup fp32 partial sums added in a fixed order, so the
+ * results are deterministic.  Outputs may not overlap inputs or each other.
+ * Workspace: ssm_selective_scan_bwd_workspace_size bytes (the state at every
+ * 16th step and the partial sums), 256-byte aligned. */
+typedef struct {
+  int64_t batch, seqlen, dim, dstate;
+  uint32_t flags;
+  ssm_tensor_desc x, delta, A, B, C, D, z, h0, delta_bias, dy;
+  ssm_tensor_desc dx, ddelta, dz, dA, dB, dC, dD, dh0, ddelta_bias;
+} ssm_scan_bwd_desc;
+
+typedef struct {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;          /* NULL unless SSM_HAS_D          */
+  const void* z;           /* NULL unless SSM_HAS_Z          */
+  const float* h0;         /* NULL unless SSM_HAS_H0         */
+  const float* delta_bias; /* NULL unless SSM_HAS_DELTA_BIAS */
+  const void* dy;
+  void* dx;
+  void* ddelta;
+  void* dz;                /* NULL unless SSM_HAS_Z          */
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;               /* NULL unless SSM_HAS_D          */
+  float* dh0;              /* NULL unless SSM_HAS_H0         */
+  float* ddelta_bias;      /* NULL unless SSM_HAS_DELTA_BIAS */
+} ssm_scan_bwd_ptrs;
+
 /* ------------------------------------------------------------------- SSD */
 
 /* SSD problem.  Required tensors (shape, dtype), all innermost stride 1:
@@ -294,6 +354,13 @@ ssm_status ssm_ssd_chunk_scan(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, cons
 
 /* One decode step (definition above ssm_update_desc).  No workspace. */
 ssm_status ssm_selective_state_update(const ssm_update_desc* d, const ssm_update_ptrs* p, void* hip_stream);
+
+/* Workspace bytes for ssm_selective_scan_bwd. */
+ssm_status ssm_selective_scan_bwd_workspace_size(const ssm_scan_bwd_desc* d, size_t* bytes);
+
+/* Backward of the selective scan (definition above ssm_scan_bwd_desc). */
+ssm_status ssm_selective_scan_bwd(const ssm_scan_bwd_desc* d, const ssm_scan_bwd_ptrs* p, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream);
 
 /* Causal depthwise convolution (+ bias, + SiLU) (definition above
  * ssm_conv_desc).  No workspace. */

@@ -29,7 +29,7 @@ MAX_DIMS = 5
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_hip_error", "ssm_selective_scan_workspace_size",
            "ssm_selective_scan_fwd", "ssm_ssd_chunk_workspace_size", "ssm_ssd_chunk_fwd", "ssm_ssd_chunk_cumsum",
            "ssm_ssd_chunk_state", "ssm_ssd_state_passing", "ssm_ssd_chunk_scan", "ssm_selective_state_update",
-           "ssm_causal_conv1d_fwd")
+           "ssm_causal_conv1d_fwd", "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd")
 
 
 class TensorDesc(ctypes.Structure):
@@ -41,6 +41,8 @@ _SCAN_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "h0", "h_last", "delta_bi
 _SSD_T = ("x", "delta", "A", "B", "C", "D", "y", "h0", "h_last")
 _UPD_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "state", "delta_bias")
 _CONV_T = ("x", "weight", "bias", "y")
+_BWD_IN = ("x", "delta", "A", "B", "C", "D", "z", "h0", "delta_bias", "dy")
+_BWD_OUT = ("dx", "ddelta", "dz", "dA", "dB", "dC", "dD", "dh0", "ddelta_bias")
 
 
 class ScanDesc(ctypes.Structure):
@@ -80,6 +82,15 @@ class ConvPtrs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _CONV_T]
 
 
+class ScanBwdDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("flags", ctypes.c_uint32)] + [(n, TensorDesc) for n in _BWD_IN + _BWD_OUT]
+
+
+class ScanBwdPtrs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _BWD_IN + _BWD_OUT]
+
+
 class SSMError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -114,6 +125,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_ssd_chunk_scan.argtypes = [P(SSDDesc), P(SSDPtrs), vp, vp, vp, vp]
         L.ssm_selective_state_update.argtypes = [P(UpdateDesc), P(UpdatePtrs), vp]
         L.ssm_causal_conv1d_fwd.argtypes = [P(ConvDesc), P(ConvPtrs), vp]
+        L.ssm_selective_scan_bwd_workspace_size.argtypes = [P(ScanBwdDesc), P(sz)]
+        L.ssm_selective_scan_bwd.argtypes = [P(ScanBwdDesc), P(ScanBwdPtrs), vp, sz, vp]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = ctypes.c_int
         if L.ssm_abi_version() != ABI_VERSION:
@@ -386,5 +399,44 @@ def causal_conv1d(x, weight, bias=None, silu=True, y_dtype=None, y=None, stream=
     desc = conv_desc(x, weight, bias, y, silu)
     ptrs = conv_ptrs(x, weight, bias, y)
     _check(lib().ssm_causal_conv1d_fwd(ctypes.byref(desc), ctypes.byref(ptrs), _stream(stream)),
-           "ssm_causal_conv1d_fwd")
+           "ssm_causal_conv1d_fwd", "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd")
     return y
+
+
+# ---------------------------------------------------------- scan backward
+
+def selective_scan_bwd(dy, x, delta, A, B, C, D=None, z=None, h0=None, euler=False, delta_softplus=False,
+                       delta_bias=None, grad_dtype=None, stream=None) -> dict:
+    """Gradients of sum(dy * y) for y = selective_scan_fwd(x, delta, A, B, C,
+    D, z, h0, euler, delta_softplus, delta_bias) (see include/ssm.h).
+
+    Returns a dict: dx, ddelta (grad_dtype, default x's dtype), dz (if z), dA
+    (dim, dstate), dB, dC (batch, L, dstate), dD (if D), dh0 (if h0),
+    ddelta_bias (if delta_bias); the last six fp32."""
+    gdt = grad_dtype or x.dtype
+    batch, L, dim = x.shape
+    N = A.shape[-1]
+    dev = x.device
+    f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty(x.shape, dtype=gdt, device=dev), "ddelta": torch.empty(x.shape, dtype=gdt, device=dev),
+           "dz": torch.empty(x.shape, dtype=gdt, device=dev) if z is not None else None,
+           "dA": f32(dim, N), "dB": f32(batch, L, N), "dC": f32(batch, L, N),
+           "dD": f32(dim) if D is not None else None, "dh0": f32(batch, dim, N) if h0 is not None else None,
+           "ddelta_bias": f32(dim) if delta_bias is not None else None}
+    ins = (x, delta, A, B, C, D, z, h0, delta_bias, dy)
+    d = ScanBwdDesc()
+    d.batch, d.seqlen, d.dim, d.dstate = batch, L, dim, N
+    d.flags = ((SSM_HAS_Z if z is not None else 0) | (SSM_HAS_D if D is not None else 0) |
+               (SSM_DISC_EULER if euler else 0) | (SSM_HAS_H0 if h0 is not None else 0) |
+               _delta_flags(delta_softplus, delta_bias))
+    p = ScanBwdPtrs()
+    for name, t in list(zip(_BWD_IN, ins)) + [(k, out[k]) for k in _BWD_OUT]:
+        setattr(d, name, tensor_desc(t))
+        setattr(p, name, _p(t))
+    n = ctypes.c_size_t()
+    _check(lib().ssm_selective_scan_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)),
+           "ssm_selective_scan_bwd_workspace_size")
+    ws = _workspace(n.value, dev)
+    _check(lib().ssm_selective_scan_bwd(ctypes.byref(d), ctypes.byref(p), _p(ws), n.value, _stream(stream)),
+           "ssm_selective_scan_bwd")
+    return {k: v for k, v in out.items() if v is not None}

@@ -19,6 +19,8 @@ constexpr uint32_t kScanFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER | SSM_HAS
 constexpr uint32_t kSSDFlags = SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_WANT_HLAST;
 constexpr uint32_t kUpdateFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER | SSM_DELTA_SOFTPLUS | SSM_HAS_DELTA_BIAS;
 constexpr uint32_t kConvFlags = SSM_HAS_BIAS | SSM_SILU;
+constexpr uint32_t kScanBwdFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_DELTA_SOFTPLUS |
+                                   SSM_HAS_DELTA_BIAS;
 constexpr int kSimds = 256 * 4;  // MI355X: 256 compute units x 4 SIMDs
 
 int64_t esize(int32_t dt) { return dt == SSM_BF16 || dt == SSM_F16 ? 2 : 4; }
@@ -375,6 +377,123 @@ ssm_status validate_update(const ssm_update_desc* d, const ssm_update_ptrs* p) {
   return SSM_OK;
 }
 
+// --------------------------------------------------------- scan backward
+
+struct BwdPlan {
+  int64_t ntiles = 0, n_dblk = 0;
+  int64_t ws_ckpt = 0, ws_pdB = 0, ws_pdA = 0, ws_pdD = 0, ws_total = 0;
+};
+
+BwdPlan plan_bwd(const ssm_scan_bwd_desc& d) {
+  BwdPlan pl;
+  pl.ntiles = (d.seqlen + 15) / 16;
+  pl.n_dblk = (d.dim + 15) / 16;
+  pl.ws_ckpt = round256(d.batch * pl.ntiles * d.dim * d.dstate * 4);
+  pl.ws_pdB = round256(pl.n_dblk * d.batch * d.seqlen * d.dstate * 4);
+  pl.ws_pdA = round256(d.batch * d.dim * d.dstate * 4);
+  pl.ws_pdD = round256(d.batch * d.dim * 4);
+  pl.ws_total = pl.ws_ckpt + 2 * pl.ws_pdB + pl.ws_pdA + 2 * pl.ws_pdD;
+  return pl;
+}
+
+ssm_status validate_bwd_desc(const ssm_scan_bwd_desc* d) {
+  if (!d) return SSM_ERR_NULL;
+  if (d->batch <= 0 || d->seqlen <= 0 || d->dim <= 0 || d->dstate <= 0) return SSM_ERR_SHAPE;
+  const uint32_t f = d->flags;
+  if (f & ~kScanBwdFlags) return SSM_ERR_UNSUPPORTED;
+  if ((f & SSM_HAS_DELTA_BIAS) && !(f & SSM_DELTA_SOFTPLUS)) return SSM_ERR_UNSUPPORTED;
+  if (d->dstate > SSM_SCAN_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
+  if (d->batch * ((d->dim + 15) / 16) >= ((int64_t)1 << 31)) return SSM_ERR_UNSUPPORTED;
+  const int32_t io = d->x.dtype;
+  if (io == SSM_F16) return SSM_ERR_UNSUPPORTED;
+  const bool io_ok = io == SSM_F32 || io == SSM_BF16;
+  auto out_ok = [&](int32_t dt) { return dt == io || dt == SSM_F32; };
+  const int64_t bld[3] = {d->batch, d->seqlen, d->dim};
+  const int64_t bln[3] = {d->batch, d->seqlen, d->dstate};
+  const int64_t dn[2] = {d->dim, d->dstate};
+  const int64_t dd[1] = {d->dim};
+  const int64_t bdn[3] = {d->batch, d->dim, d->dstate};
+  ssm_status s;
+  if ((s = check_tensor(d->x, 3, bld, io_ok, true, false))) return s;
+  if ((s = check_tensor(d->delta, 3, bld, d->delta.dtype == io, true, false))) return s;
+  if ((s = check_tensor(d->B, 3, bln, d->B.dtype == io, false, false))) return s;
+  if ((s = check_tensor(d->C, 3, bln, d->C.dtype == io, false, false))) return s;
+  if ((s = check_tensor(d->A, 2, dn, d->A.dtype == SSM_F32, false, false))) return s;
+  if ((s = check_tensor(d->dy, 3, bld, out_ok(d->dy.dtype), true, false))) return s;
+  if ((s = check_tensor(d->dx, 3, bld, out_ok(d->dx.dtype), true, false))) return s;
+  if ((s = check_tensor(d->ddelta, 3, bld, out_ok(d->ddelta.dtype), true, false))) return s;
+  if ((s = check_tensor(d->dA, 2, dn, d->dA.dtype == SSM_F32, false, true))) return s;
+  if ((s = check_tensor(d->dB, 3, bln, d->dB.dtype == SSM_F32, false, true))) return s;
+  if ((s = check_tensor(d->dC, 3, bln, d->dC.dtype == SSM_F32, false, true))) return s;
+  if (!non_overlapping(d->dx) || !non_overlapping(d->ddelta)) return SSM_ERR_STRIDE;
+  if (f & SSM_HAS_Z) {
+    if ((s = check_tensor(d->z, 3, bld, d->z.dtype == io, true, false))) return s;
+    if ((s = check_tensor(d->dz, 3, bld, out_ok(d->dz.dtype), true, false))) return s;
+    if (!non_overlapping(d->dz)) return SSM_ERR_STRIDE;
+  }
+  if (f & SSM_HAS_D) {
+    if ((s = check_tensor(d->D, 1, dd, d->D.dtype == SSM_F32, false, false))) return s;
+    if ((s = check_tensor(d->dD, 1, dd, d->dD.dtype == SSM_F32, false, true))) return s;
+  }
+  if (f & SSM_HAS_H0) {
+    if ((s = check_tensor(d->h0, 3, bdn, d->h0.dtype == SSM_F32, false, true))) return s;
+    if ((s = check_tensor(d->dh0, 3, bdn, d->dh0.dtype == SSM_F32, false, true))) return s;
+  }
+  if (f & SSM_HAS_DELTA_BIAS) {
+    if ((s = check_tensor(d->delta_bias, 1, dd, d->delta_bias.dtype == SSM_F32, false, false))) return s;
+    if ((s = check_tensor(d->ddelta_bias, 1, dd, d->ddelta_bias.dtype == SSM_F32, false, true))) return s;
+  }
+  return SSM_OK;
+}
+
+ssm_status validate_bwd_ptrs(const ssm_scan_bwd_desc* d, const ssm_scan_bwd_ptrs* p) {
+  if (!p) return SSM_ERR_NULL;
+  const uint32_t f = d->flags;
+  if (!p->x || !p->delta || !p->A || !p->B || !p->C || !p->dy || !p->dx || !p->ddelta || !p->dA || !p->dB ||
+      !p->dC)
+    return SSM_ERR_NULL;
+  if ((f & SSM_HAS_Z) && (!p->z || !p->dz)) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_D) && (!p->D || !p->dD)) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_H0) && (!p->h0 || !p->dh0)) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_DELTA_BIAS) && (!p->delta_bias || !p->ddelta_bias)) return SSM_ERR_NULL;
+  const int64_t e = esize(d->x.dtype);
+  if (!aligned(p->x, e) || !aligned(p->delta, e) || !aligned(p->B, e) || !aligned(p->C, e) || !aligned(p->A, 4) ||
+      !aligned(p->dy, esize(d->dy.dtype)) || !aligned(p->dx, esize(d->dx.dtype)) ||
+      !aligned(p->ddelta, esize(d->ddelta.dtype)) || !aligned(p->dA, 4) || !aligned(p->dB, 4) || !aligned(p->dC, 4))
+    return SSM_ERR_ALIGN;
+  if ((f & SSM_HAS_Z) && (!aligned(p->z, e) || !aligned(p->dz, esize(d->dz.dtype)))) return SSM_ERR_ALIGN;
+  if ((f & SSM_HAS_D) && (!aligned(p->D, 4) || !aligned(p->dD, 4))) return SSM_ERR_ALIGN;
+  if ((f & SSM_HAS_H0) && (!aligned(p->h0, 4) || !aligned(p->dh0, 4))) return SSM_ERR_ALIGN;
+  if ((f & SSM_HAS_DELTA_BIAS) && (!aligned(p->delta_bias, 4) || !aligned(p->ddelta_bias, 4))) return SSM_ERR_ALIGN;
+  const Span ins[] = {span_of(d->x, p->x),
+                      span_of(d->delta, p->delta),
+                      span_of(d->A, p->A),
+                      span_of(d->B, p->B),
+                      span_of(d->C, p->C),
+                      span_of(d->dy, p->dy),
+                      (f & SSM_HAS_D) ? span_of(d->D, p->D) : Span(),
+                      (f & SSM_HAS_Z) ? span_of(d->z, p->z) : Span(),
+                      (f & SSM_HAS_H0) ? span_of(d->h0, p->h0) : Span(),
+                      (f & SSM_HAS_DELTA_BIAS) ? span_of(d->delta_bias, p->delta_bias) : Span()};
+  const Span outs[] = {span_of(d->dx, p->dx),
+                       span_of(d->ddelta, p->ddelta),
+                       span_of(d->dA, p->dA),
+                       span_of(d->dB, p->dB),
+                       span_of(d->dC, p->dC),
+                       (f & SSM_HAS_Z) ? span_of(d->dz, p->dz) : Span(),
+                       (f & SSM_HAS_D) ? span_of(d->dD, p->dD) : Span(),
+                       (f & SSM_HAS_H0) ? span_of(d->dh0, p->dh0) : Span(),
+                       (f & SSM_HAS_DELTA_BIAS) ? span_of(d->ddelta_bias, p->ddelta_bias) : Span()};
+  const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
+  for (int i = 0; i < nout; ++i) {
+    for (const Span& sp : ins)
+      if (overlap(outs[i], sp)) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return SSM_ERR_ALIAS;
+  }
+  return SSM_OK;
+}
+
 // ------------------------------------------------------------------ conv
 
 ssm_status validate_conv(const ssm_conv_desc* d, const ssm_conv_ptrs* p) {
@@ -581,6 +700,66 @@ ssm_status ssm_ssd_chunk_scan(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, cons
   q.beta = (float*)beta;
   q.S_in = (void*)S_in;
   return hip_status(ssm::launch_ssd_chunk_scan(q, (hipStream_t)hip_stream));
+}
+
+ssm_status ssm_selective_scan_bwd_workspace_size(const ssm_scan_bwd_desc* d, size_t* bytes) {
+  if (!bytes) return SSM_ERR_NULL;
+  ssm_status s = validate_bwd_desc(d);
+  if (s) return s;
+  *bytes = (size_t)plan_bwd(*d).ws_total;
+  return SSM_OK;
+}
+
+ssm_status ssm_selective_scan_bwd(const ssm_scan_bwd_desc* d, const ssm_scan_bwd_ptrs* p, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream) {
+  ssm_status s = validate_bwd_desc(d);
+  if (s) return s;
+  if ((s = validate_bwd_ptrs(d, p))) return s;
+  const BwdPlan pl = plan_bwd(*d);
+  if (!workspace || workspace_bytes < (size_t)pl.ws_total) return SSM_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return SSM_ERR_ALIGN;
+  const uint32_t f = d->flags;
+  ssm::ScanBwdParams q;
+  std::memset(&q, 0, sizeof(q));
+  q.x = p->x; q.delta = p->delta; q.z = (f & SSM_HAS_Z) ? p->z : nullptr; q.dy = p->dy;
+  q.B = p->B; q.C = p->C; q.A = p->A; q.Dskip = (f & SSM_HAS_D) ? p->D : nullptr;
+  q.h0 = (f & SSM_HAS_H0) ? p->h0 : nullptr;
+  q.dbias = (f & SSM_HAS_DELTA_BIAS) ? p->delta_bias : nullptr;
+  q.dx = p->dx; q.ddelta = p->ddelta; q.dz = (f & SSM_HAS_Z) ? p->dz : nullptr;
+  q.dA = p->dA; q.dB = p->dB; q.dC = p->dC;
+  q.dD = (f & SSM_HAS_D) ? p->dD : nullptr;
+  q.dh0 = (f & SSM_HAS_H0) ? p->dh0 : nullptr;
+  q.ddbias = (f & SSM_HAS_DELTA_BIAS) ? p->ddelta_bias : nullptr;
+  char* w = (char*)workspace;
+  q.ckpt = (float*)w;
+  q.pdB = (float*)(w + pl.ws_ckpt);
+  q.pdC = (float*)(w + pl.ws_ckpt + pl.ws_pdB);
+  q.pdA = (float*)(w + pl.ws_ckpt + 2 * pl.ws_pdB);
+  q.pdD = (f & SSM_HAS_D) ? (float*)(w + pl.ws_ckpt + 2 * pl.ws_pdB + pl.ws_pdA) : nullptr;
+  q.pdbias = (f & SSM_HAS_DELTA_BIAS) ? (float*)(w + pl.ws_ckpt + 2 * pl.ws_pdB + pl.ws_pdA + pl.ws_pdD) : nullptr;
+  q.batch = d->batch; q.L = d->seqlen; q.D = d->dim; q.N = d->dstate;
+  q.xs_b = d->x.stride[0]; q.xs_t = d->x.stride[1];
+  q.ds_b = d->delta.stride[0]; q.ds_t = d->delta.stride[1];
+  if (f & SSM_HAS_Z) {
+    q.zs_b = d->z.stride[0]; q.zs_t = d->z.stride[1];
+    q.dzs_b = d->dz.stride[0]; q.dzs_t = d->dz.stride[1];
+    q.dz_f32 = d->dz.dtype == SSM_F32;
+  }
+  q.gs_b = d->dy.stride[0]; q.gs_t = d->dy.stride[1];
+  q.dxs_b = d->dx.stride[0]; q.dxs_t = d->dx.stride[1];
+  q.dds_b = d->ddelta.stride[0]; q.dds_t = d->ddelta.stride[1];
+  q.Bs_b = d->B.stride[0]; q.Bs_t = d->B.stride[1]; q.Bs_n = d->B.stride[2];
+  q.Cs_b = d->C.stride[0]; q.Cs_t = d->C.stride[1]; q.Cs_n = d->C.stride[2];
+  q.As_d = d->A.stride[0]; q.As_n = d->A.stride[1];
+  q.Ds_d = (f & SSM_HAS_D) ? d->D.stride[0] : 0;
+  q.dbs_d = (f & SSM_HAS_DELTA_BIAS) ? d->delta_bias.stride[0] : 0;
+  q.io_bf16 = d->x.dtype == SSM_BF16;
+  q.dy_f32 = d->dy.dtype == SSM_F32;
+  q.dx_f32 = d->dx.dtype == SSM_F32;
+  q.dd_f32 = d->ddelta.dtype == SSM_F32;
+  q.euler = (f & SSM_DISC_EULER) ? 1 : 0;
+  q.dsoftplus = (f & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+  return hip_status(ssm::launch_selective_scan_bwd(q, (hipStream_t)hip_stream));
 }
 
 ssm_status ssm_causal_conv1d_fwd(const ssm_conv_desc* d, const ssm_conv_ptrs* p, void* hip_stream) {

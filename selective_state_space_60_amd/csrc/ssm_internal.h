@@ -70,6 +70,47 @@ struct UpdateParams {
 
 hipError_t launch_selective_state_update(const UpdateParams& p, hipStream_t stream);
 
+// ------------------------------------------------------------ scan backward
+struct ScanBwdParams {
+  const void* x;
+  const void* delta;
+  const void* z;       // or null
+  const void* dy;
+  const void* B;
+  const void* C;
+  const float* A;
+  const float* Dskip;  // or null
+  const float* h0;     // or null
+  const float* dbias;  // or null
+  void* dx;
+  void* ddelta;
+  void* dz;            // or null
+  float* dA;           // (D, N)
+  float* dB;           // (batch, L, N)
+  float* dC;
+  float* dD;           // or null
+  float* dh0;          // or null
+  float* ddbias;       // or null
+  // workspace
+  float* ckpt;         // (batch, ntiles, D, N): state before each 16-step tile
+  float* pdB;          // (n_dblk, batch, L, N): sums over each workgroup's channels
+  float* pdC;
+  float* pdA;          // (batch, D, N): sums over time
+  float* pdD;          // (batch, D)
+  float* pdbias;       // (batch, D)
+  int64_t batch, L, D, N;
+  int64_t xs_b, xs_t, ds_b, ds_t, zs_b, zs_t, gs_b, gs_t;  // x, delta, z, dy
+  int64_t dxs_b, dxs_t, dds_b, dds_t, dzs_b, dzs_t;        // dx, ddelta, dz
+  int64_t Bs_b, Bs_t, Bs_n, Cs_b, Cs_t, Cs_n;
+  int64_t As_d, As_n, Ds_d, dbs_d;
+  int io_bf16;    // x, delta, z, B, C
+  int dy_f32;     // dy fp32 (1) or io (0)
+  int dx_f32, dd_f32, dz_f32;
+  int euler, dsoftplus;
+};
+
+hipError_t launch_selective_scan_bwd(const ScanBwdParams& p, hipStream_t stream);
+
 // --------------------------------------------------------------------- conv
 struct ConvParams {
   const void* x;       // (batch, L, D), innermost stride 1
