@@ -159,7 +159,8 @@ typedef struct {
  * formed from per-workgroup fp32 partial sums added in a fixed order, so the
  * results are deterministic.  Outputs may not overlap inputs or each other.
  * Workspace: ssm_selective_scan_bwd_workspace_size bytes (the state at every
- * 16th step and the partial sums), 256-byte aligned. */
+ * 16th step and the partial sums), 256-byte aligned.
+ * Limit: the forward's span limit, applied to x, delta, z, dy, B and C. */
 typedef struct {
   int64_t batch, seqlen, dim, dstate;
   uint32_t flags;

@@ -22,8 +22,8 @@
 //     the readout C.h, forms g_t and dz_t, then steps the adjoint back through
 //     the tile, accumulating dx and ddelta (sums over the lane's states, then
 //     over the row through LDS), dB and dC (sums over the workgroup's 16
-//     channels: DPP-free lane shuffles across the 4 rows of a wave, then
-//     LDS across the 4 waves) and dA, dD, ddelta_bias in registers.
+//     channels: cross-row lane swaps over the 4 rows of a wave, then LDS
+//     across the 4 waves) and dA, dD, ddelta_bias in registers.
 //  3. reduce kernels add the per-workgroup partial sums of dB, dC over the
 //     channel blocks and of dA, dD, ddelta_bias over the batch, in a fixed
 //     order.
@@ -73,6 +73,20 @@ __device__ __forceinline__ float softplus_f32(float v) {
   return fmaxf(v, 0.f) + lp;
 }
 
+// Sum over the 4 rows (16-lane groups) of the wave, in every lane.  gfx950's
+// permlane32 swap, given (v, v), returns v's lower half-wave in both halves of
+// one result and its upper half-wave in the other, so their sum adds the
+// halves; permlane16 swap does the same between neighbouring rows.  (Lane
+// layout checked on the device.)  VALU only: no LDS round trip.
+__device__ __forceinline__ float sum_rows(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float w = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const uint32_t uw = __float_as_uint(w);
+  const auto q = __builtin_amdgcn_permlane16_swap(uw, uw, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 template <int... S, class F>
 __device__ __forceinline__ void for_steps(std::integer_sequence<int, S...>, F&& f) {
   (f(std::integral_constant<int, S>{}), ...);
@@ -83,22 +97,23 @@ __device__ __forceinline__ void for_steps_rev(std::integer_sequence<int, S...>, 
   (f(std::integral_constant<int, TT - 1 - S>{}), ...);
 }
 
-// The per-channel, per-step values of one tile and the (B, C) pairs.
+static_assert(CH * TT == NT, "one (channel, step) of a tile per thread");
+
+// Update forms (uniform per workgroup): zero-order hold with A != 0, zero-order
+// hold with some A == 0 (limit delta), and the simplified Bbar = delta B.
+enum Form : int { kZoh = 0, kZohZero = 1, kEuler = 2 };
+
+// The (B, C) pairs of one tile, and per-lane sums of the backward.
 template <int KS>
-struct TileSmem {
-  float dt[CH][TP];   // step size used (after the softplus); 0 on padding steps
-  float dv[CH][TP];   // softplus argument delta + bias
-  float x[CH][TP];
-  float z[CH][TP];
-  float gy[CH][TP];   // dy
+struct BwdSmem {
   float2 bc[TT][G * KS];
+  float part[2][NT][TP];          // per-lane partial sums over states, by step
+  float red[4][TT][2][G * KS];    // per-wave sums of dB, dC over the wave's 4 channels
 };
 
 template <int KS>
-struct BwdSmem {
-  TileSmem<KS> t;
-  float part[2][NT][TP];          // per-lane partial sums over states, by step
-  float red[4][TT][2][G * KS];    // per-wave sums of dB, dC over the wave's 4 channels
+struct CkptSmem {
+  float2 bc[TT][G * KS];
 };
 
 // Lane constants of its KS states.
@@ -107,56 +122,135 @@ struct LaneA {
   float a[KS], A2[KS], iA[KS];
 };
 
-// Stage tile `it` of the workgroup's 16 channels into LDS (zeros past the
-// sequence and the channels; delta 0 there so the state does not change).
+// What a thread reads of one tile: step (tid % 16) of channel (tid / 16) --
+// the values its lane holds -- and KS (B, C) pairs for the shared staging.
+template <int KS>
+struct Fetch {
+  float x, dr, z, gy;
+  float B[KS], C[KS];
+};
+
+// One tensor walked tile by tile through a per-lane pointer (VGPRs: the
+// strides are needed only here, which keeps the scalar registers free).
+struct LanePtr {
+  const char* p;     // this lane's element in the current tile
+  int64_t step;      // bytes from one tile to the next
+  const char* safe;  // a valid element, read in place of one past the end
+};
+
+// (batch, L, width) tensor, element (b, t, col) at b*sb + t*st + col*sc:
+// lane reads step j, column col of tile `it`.
+__device__ __forceinline__ LanePtr lane_ptr(const void* p, int64_t es, int64_t b, int64_t sb, int64_t st, int64_t sc,
+                                            int64_t col, int j, int it) {
+  LanePtr r;
+  r.safe = (const char*)p;
+  r.step = TT * st * es;
+  r.p = (const char*)p + (b * sb + ((int64_t)it * TT + j) * st + col * sc) * es;
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float lload(const LanePtr& w, bool ok) {
+  const char* a = ok ? w.p : w.safe;
+  if constexpr (BF16) return __uint_as_float((uint32_t)(*(const uint16_t*)a) << 16);
+  else return *(const float*)a;
+}
+
+template <int KS>
+struct LanePtrs {
+  LanePtr x, dr, z, gy;
+  LanePtr B[KS], C[KS];
+};
+
+template <bool BF16, int KS>
+__device__ __forceinline__ LanePtrs<KS> lane_ptrs(const ScanBwdParams& p, int64_t b, int64_t d0, int it) {
+  const int tid = threadIdx.x;
+  const int j = tid % TT;
+  const int64_t d = d0 + tid / TT;
+  const int64_t e = BF16 ? 2 : 4;
+  LanePtrs<KS> w;
+  w.x = lane_ptr(p.x, e, b, p.xs_b, p.xs_t, 1, d, j, it);
+  w.dr = lane_ptr(p.delta, e, b, p.ds_b, p.ds_t, 1, d, j, it);
+  w.z = p.z ? lane_ptr(p.z, e, b, p.zs_b, p.zs_t, 1, d, j, it) : w.x;
+  w.gy = lane_ptr(p.dy, p.dy_f32 ? 4 : 2, b, p.gs_b, p.gs_t, 1, d, j, it);
+#pragma unroll
+  for (int r = 0; r < KS; ++r) {
+    const int i = tid + r * NT;
+    w.B[r] = lane_ptr(p.B, e, b, p.Bs_b, p.Bs_t, p.Bs_n, i % (G * KS), i / (G * KS), it);
+    w.C[r] = lane_ptr(p.C, e, b, p.Cs_b, p.Cs_t, p.Cs_n, i % (G * KS), i / (G * KS), it);
+  }
+  return w;
+}
+
+// Read tile `it` at the pointers, then move them `dir` tiles on.  Loads are
+// unconditional (steps, channels and states past the end read a valid
+// element, zeroed afterwards).
 template <bool BF16, int KS, bool FULL>
-__device__ __forceinline__ void stage_tile(TileSmem<KS>& s, const ScanBwdParams& p, int64_t b, int64_t d0, int it) {
+__device__ __forceinline__ Fetch<KS> fetch(const ScanBwdParams& p, LanePtrs<KS>& w, int64_t d0, int it, int dir) {
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)it * TT;
-  for (int i = tid; i < CH * TT; i += NT) {
-    const int c = i / TT, j = i % TT;
-    const int64_t t = t0 + j, d = d0 + c;
-    const bool ok = t < p.L && d < p.D;
-    const float xv = ok ? ld<BF16>(p.x, b * p.xs_b + t * p.xs_t + d) : 0.f;
-    const float raw = ok ? ld<BF16>(p.delta, b * p.ds_b + t * p.ds_t + d) : 0.f;
-    float dt = raw, v = raw;
-    if (p.dsoftplus) {
-      v = raw + ((p.dbias && d < p.D) ? p.dbias[d * p.dbs_d] : 0.f);
-      dt = ok ? softplus_f32(v) : 0.f;
-    }
-    s.x[c][j] = xv;
-    s.dt[c][j] = dt;
-    if constexpr (FULL) {
-      s.dv[c][j] = v;
-      s.z[c][j] = (ok && p.z) ? ld<BF16>(p.z, b * p.zs_b + t * p.zs_t + d) : 0.f;
-      const int64_t gi = b * p.gs_b + t * p.gs_t + d;
-      s.gy[c][j] = ok ? (p.dy_f32 ? ((const float*)p.dy)[gi] : ld<true>(p.dy, gi)) : 0.f;
-    }
+  const bool tile_ok = it >= 0;  // tile -1 (after the first) and tiles past the end read nothing
+  const bool ok = tile_ok && d0 + tid / TT < p.D && t0 + tid % TT < p.L;
+  Fetch<KS> f;
+  f.x = lload<BF16>(w.x, ok);
+  f.dr = lload<BF16>(w.dr, ok);
+  if constexpr (FULL) {
+    f.z = p.z ? lload<BF16>(w.z, ok) : 0.f;
+    f.gy = p.dy_f32 ? lload<false>(w.gy, ok) : lload<true>(w.gy, ok);
   }
-  for (int i = tid; i < TT * G * KS; i += NT) {
-    const int j = i / (G * KS), n = i % (G * KS);
-    const int64_t t = t0 + j;
-    const bool ok = t < p.L && n < p.N;
-    const float Bv = ok ? ld<BF16>(p.B, b * p.Bs_b + t * p.Bs_t + n * p.Bs_n) : 0.f;
-    const float Cv = (FULL && ok) ? ld<BF16>(p.C, b * p.Cs_b + t * p.Cs_t + n * p.Cs_n) : 0.f;
-    s.bc[j][n] = make_float2(Bv, Cv);
+  if (!ok) f.x = f.dr = f.z = f.gy = 0.f;
+  w.x.p += dir * w.x.step;
+  w.dr.p += dir * w.dr.step;
+  w.z.p += dir * w.z.step;
+  w.gy.p += dir * w.gy.step;
+#pragma unroll
+  for (int r = 0; r < KS; ++r) {
+    const int i = tid + r * NT;
+    const bool okb = tile_ok && i % (G * KS) < p.N && t0 + i / (G * KS) < p.L;
+    f.B[r] = lload<BF16>(w.B[r], okb);
+    f.C[r] = FULL ? lload<BF16>(w.C[r], okb) : 0.f;
+    if (!okb) f.B[r] = f.C[r] = 0.f;
+    w.B[r].p += dir * w.B[r].step;
+    w.C[r].p += dir * w.C[r].step;
+  }
+  return f;
+}
+
+template <int KS>
+__device__ __forceinline__ void put_bc(float2 (&bc)[TT][G * KS], const Fetch<KS>& f) {
+#pragma unroll
+  for (int r = 0; r < KS; ++r) {
+    const int i = threadIdx.x + r * NT;
+    bc[i / (G * KS)][i % (G * KS)] = make_float2(f.B[r], f.C[r]);
   }
 }
 
-// cbar for one state: expm1(u)/a as Abar/a - 1/a (delta where a == 0), or delta.
-__device__ __forceinline__ float cbar(float Ab, float a, float iA, float dt, bool euler) {
-  if (euler) return dt;
-  return a != 0.f ? __builtin_fmaf(Ab, iA, -iA) : dt;
+// The lane's step size for its step: softplus(delta + bias) inside the
+// sequence, 0 on padding steps (no change of the state).
+__device__ __forceinline__ float step_size(const ScanBwdParams& p, float raw, float bias, bool ok, float& v) {
+  v = raw + bias;
+  if (!p.dsoftplus) return raw;
+  return ok ? softplus_f32(v) : 0.f;
+}
+
+// cbar = Bbar / B for one state.
+template <int FORM>
+__device__ __forceinline__ float cbar(float Ab, float a, float iA, float dt) {
+  if constexpr (FORM == kEuler) return dt;
+  else if constexpr (FORM == kZoh) return __builtin_fmaf(Ab, iA, -iA);
+  else return a != 0.f ? __builtin_fmaf(Ab, iA, -iA) : dt;
 }
 
 template <bool BF16, int KS>
-__device__ __forceinline__ LaneA<KS> lane_a(const ScanBwdParams& p, int64_t d, int sg) {
+__device__ __forceinline__ LaneA<KS> lane_a(const ScanBwdParams& p, int64_t d, int sg, int& zero_a) {
   LaneA<KS> la;
+  zero_a = 0;
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
     const int n = sg * KS + k;
     float a = -1.f;  // padding states and channels: any A != 0 (B = C = 0 there)
     if (d < p.D && n < p.N) a = p.A[d * p.As_d + n * p.As_n];
+    zero_a |= a == 0.f;
     la.a[k] = a;
     la.A2[k] = a * kLog2e;
     la.iA[k] = a != 0.f ? 1.f / a : 0.f;
@@ -166,21 +260,15 @@ __device__ __forceinline__ LaneA<KS> lane_a(const ScanBwdParams& p, int64_t d, i
 
 // ---------------------------------------------------------- checkpoints
 
-template <bool BF16, int KS>
-__global__ __launch_bounds__(NT) void ckpt_kernel(ScanBwdParams p, int64_t n_dblk) {
-  __shared__ TileSmem<KS> s;
+template <bool BF16, int KS, int FORM>
+__device__ __forceinline__ void ckpt_walk(CkptSmem<KS>& s, const ScanBwdParams& p, int64_t b, int64_t d0,
+                                          const LaneA<KS>& la, float (&h)[KS]) {
   const int tid = threadIdx.x, c = tid / G, sg = tid % G;
-  const int64_t dblk = blockIdx.x % n_dblk, b = blockIdx.x / n_dblk;
-  const int64_t d0 = dblk * CH, d = d0 + c;
-  const bool euler = p.euler != 0;
-  const LaneA<KS> la = lane_a<BF16, KS>(p, d, sg);
+  const int64_t d = d0 + c;
   const int ntiles = (int)((p.L + TT - 1) / TT);
-  float h[KS];
-#pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    const int n = sg * KS + k;
-    h[k] = (p.h0 && d < p.D && n < p.N) ? p.h0[(b * p.D + d) * p.N + n] : 0.f;
-  }
+  const float bias = (p.dbias && d < p.D) ? p.dbias[d * p.dbs_d] : 0.f;
+  LanePtrs<KS> w = lane_ptrs<BF16, KS>(p, b, d0, 0);
+  Fetch<KS> cur = fetch<BF16, KS, false>(p, w, d0, 0, 1);
   for (int it = 0; it < ntiles; ++it) {
     if (d < p.D) {
       float* ck = p.ckpt + (((b * ntiles + it) * p.D + d) * p.N);
@@ -188,36 +276,60 @@ __global__ __launch_bounds__(NT) void ckpt_kernel(ScanBwdParams p, int64_t n_dbl
       for (int k = 0; k < KS; ++k)
         if (sg * KS + k < p.N) ck[sg * KS + k] = h[k];
     }
-    stage_tile<BF16, KS, false>(s, p, b, d0, it);
+    put_bc<KS>(s.bc, cur);
+    float v;
+    const float hdt = step_size(p, cur.dr, bias, (int64_t)it * TT + sg < p.L && d < p.D, v), hx = cur.x;
     __syncthreads();
-    const float hdt = s.dt[c][sg], hx = s.x[c][sg];
+    cur = fetch<BF16, KS, false>(p, w, d0, it + 1, 1);  // past the last tile: masked
     for_steps(std::make_integer_sequence<int, TT>{}, [&](auto S) {
+#pragma clang fp contract(off)
       constexpr int T = decltype(S)::value;
       const float dt = row_bcast<T>(hdt), xv = row_bcast<T>(hx);
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
         const float Ab = __builtin_amdgcn_exp2f(dt * la.A2[k]);
         const float Bv = s.bc[T][sg * KS + k].x;
-        h[k] = __builtin_fmaf(Ab, h[k], cbar(Ab, la.a[k], la.iA[k], dt, euler) * (Bv * xv));
+        h[k] = __builtin_fmaf(Ab, h[k], cbar<FORM>(Ab, la.a[k], la.iA[k], dt) * (Bv * xv));
       }
     });
     __syncthreads();
   }
 }
 
-// -------------------------------------------------------------- backward
-
-template <bool BF16, int KS>
-__global__ __launch_bounds__(NT) void bwd_kernel(ScanBwdParams p, int64_t n_dblk) {
-  __shared__ BwdSmem<KS> s;
+template <bool BF16, int KS, bool EULER>
+__global__ __launch_bounds__(NT) void ckpt_kernel(ScanBwdParams p, int64_t n_dblk) {
+  __shared__ CkptSmem<KS> s;
   const int tid = threadIdx.x, c = tid / G, sg = tid % G;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int64_t dblk = blockIdx.x % n_dblk, b = blockIdx.x / n_dblk;
   const int64_t d0 = dblk * CH, d = d0 + c;
+  int zero_a;
+  const LaneA<KS> la = lane_a<BF16, KS>(p, d, sg, zero_a);
+  float h[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const int n = sg * KS + k;
+    h[k] = (p.h0 && d < p.D && n < p.N) ? p.h0[(b * p.D + d) * p.N + n] : 0.f;
+  }
+  if constexpr (EULER) {
+    ckpt_walk<BF16, KS, kEuler>(s, p, b, d0, la, h);
+  } else {
+    if (__syncthreads_or(zero_a)) ckpt_walk<BF16, KS, kZohZero>(s, p, b, d0, la, h);
+    else ckpt_walk<BF16, KS, kZoh>(s, p, b, d0, la, h);
+  }
+}
+
+// -------------------------------------------------------------- backward
+
+template <bool BF16, int KS, int FORM>
+__device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p, int64_t b, int64_t dblk,
+                                         const LaneA<KS>& la) {
+  const int tid = threadIdx.x, c = tid / G, sg = tid % G;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int64_t d0 = dblk * CH, d = d0 + c;
   const bool d_ok = d < p.D;
-  const bool euler = p.euler != 0, has_z = p.z != nullptr;
-  const LaneA<KS> la = lane_a<BF16, KS>(p, d, sg);
+  const bool has_z = p.z != nullptr;
   const float Dk = (p.Dskip && d_ok) ? p.Dskip[d * p.Ds_d] : 0.f;
+  const float bias = (p.dbias && d_ok) ? p.dbias[d * p.dbs_d] : 0.f;
   const int ntiles = (int)((p.L + TT - 1) / TT);
   float carry[KS], dA[KS];
 #pragma unroll
@@ -225,95 +337,151 @@ __global__ __launch_bounds__(NT) void bwd_kernel(ScanBwdParams p, int64_t n_dblk
   float dD = 0.f, dbias = 0.f;  // this lane's steps of its channel
   float* prow = &s.part[0][tid][0];
 
-  for (int it = ntiles - 1; it >= 0; --it) {
-    const int64_t t0 = (int64_t)it * TT;
-    stage_tile<BF16, KS, true>(s.t, p, b, d0, it);
-    float h0t[KS];
+  // Per-lane pointers, set up once and moved one tile per iteration (the
+  // loop then needs no strides: fewer live scalar registers).
+  const int64_t dd = d_ok ? d : 0;
+  const float* ckp = p.ckpt + ((b * ntiles + (ntiles - 1)) * p.D + dd) * p.N;  // tile ntiles-1
+  const int64_t ck_step = p.D * p.N;
+  const int64_t e_dx = p.dx_f32 ? 4 : 2, e_dd = p.dd_f32 ? 4 : 2, e_dz = p.dz_f32 ? 4 : 2;
+  char* pdx = (char*)p.dx + (b * p.dxs_b + ((int64_t)(ntiles - 1) * TT + sg) * p.dxs_t + dd) * e_dx;
+  char* pdd = (char*)p.ddelta + (b * p.dds_b + ((int64_t)(ntiles - 1) * TT + sg) * p.dds_t + dd) * e_dd;
+  char* pdz = p.dz ? (char*)p.dz + (b * p.dzs_b + ((int64_t)(ntiles - 1) * TT + sg) * p.dzs_t + dd) * e_dz : nullptr;
+  const int64_t sdx = TT * p.dxs_t * e_dx, sdd = TT * p.dds_t * e_dd, sdz = TT * p.dzs_t * e_dz;
+  const bool dx_f32 = p.dx_f32, dd_f32 = p.dd_f32, dz_f32 = p.dz_f32;
+  // dB, dC partials: element (j, q, n) of a tile per thread (2 * KS of them)
+  constexpr int RED = TT * 2 * G * KS / NT;
+  static_assert(RED * NT == TT * 2 * G * KS, "whole tiles of dB, dC partials");
+  float* pred[RED];
+  bool red_n_ok[RED];
+  int red_j[RED];
+  const int64_t red_step = (int64_t)TT * p.N;
+#pragma unroll
+  for (int r = 0; r < RED; ++r) {
+    const int i = tid + r * NT;
+    const int j = i / (2 * G * KS), q = (i / (G * KS)) % 2, n = i % (G * KS);
+    red_j[r] = j;
+    red_n_ok[r] = n < p.N;
+    pred[r] = (q == 0 ? p.pdB : p.pdC) + ((dblk * p.batch + b) * p.L + (int64_t)(ntiles - 1) * TT + j) * p.N +
+              (n < p.N ? n : 0);
+  }
+  const int64_t L = p.L;
+  const int N = (int)p.N;
+  auto ckpt_of = [&](float (&h)[KS]) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       const int n = sg * KS + k;
-      h0t[k] = (d_ok && n < p.N) ? p.ckpt[((b * ntiles + it) * p.D + d) * p.N + n] : 0.f;
+      const bool ok = d_ok && n < N;
+      const float v = ckp[ok ? n : 0];
+      h[k] = ok ? v : 0.f;
     }
+  };
+  LanePtrs<KS> w = lane_ptrs<BF16, KS>(p, b, d0, ntiles - 1);
+  Fetch<KS> cur = fetch<BF16, KS, true>(p, w, d0, ntiles - 1, -1);
+  float h0n[KS];
+  ckpt_of(h0n);
+  for (int it = ntiles - 1; it >= 0; --it) {
+    const int64_t t0 = (int64_t)it * TT;
+    const bool j_ok = d_ok && t0 + sg < L;
+    put_bc<KS>(s.bc, cur);
+    float dv;
+    float hdt = step_size(p, cur.dr, bias, j_ok, dv), hx = cur.x;
+    const float zj = cur.z, gyj = cur.gy;
+    float h0t[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) h0t[k] = h0n[k];
     __syncthreads();
-    const float hdt = s.t.dt[c][sg], hx = s.t.x[c][sg];
+    // the previous tile's inputs are in flight during this tile
+    cur = fetch<BF16, KS, true>(p, w, d0, it - 1, -1);  // before the first tile: masked
+    if (it > 0) ckp -= ck_step;
+    ckpt_of(h0n);
 
-    // recompute the tile's states and the readout partials
-    float hh[TT][KS];
+    // recompute the tile's states (and Abar) and the readout partials
+    float hh[TT][KS], AA[TT][KS];
     {
       float h[KS];
 #pragma unroll
       for (int k = 0; k < KS; ++k) h[k] = h0t[k];
       for_steps(std::make_integer_sequence<int, TT>{}, [&](auto S) {
+#pragma clang fp contract(off)
         constexpr int T = decltype(S)::value;
         const float dt = row_bcast<T>(hdt), xv = row_bcast<T>(hx);
         float yp = 0.f;
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-          const float2 bcv = s.t.bc[T][sg * KS + k];
+          const float2 bcv = s.bc[T][sg * KS + k];
           const float Ab = __builtin_amdgcn_exp2f(dt * la.A2[k]);
-          h[k] = __builtin_fmaf(Ab, h[k], cbar(Ab, la.a[k], la.iA[k], dt, euler) * (bcv.x * xv));
+          h[k] = __builtin_fmaf(Ab, h[k], cbar<FORM>(Ab, la.a[k], la.iA[k], dt) * (bcv.x * xv));
           hh[T][k] = h[k];
+          AA[T][k] = Ab;
           yp = __builtin_fmaf(bcv.y, h[k], yp);
         }
         prow[T] = yp;
+        __builtin_amdgcn_sched_barrier(0);  // one step at a time: bounded live registers
       });
     }
     // lane sg takes step sg of its channel: o, g, dz
-    const int64_t tj = t0 + sg;
-    const bool j_ok = d_ok && tj < p.L;
     float o = 0.f;
 #pragma unroll
     for (int l = 0; l < G; ++l) o += s.part[0][c * G + l][sg];
-    const float xj = hx, zj = s.t.z[c][sg], gyj = s.t.gy[c][sg];
-    o = __builtin_fmaf(Dk, xj, o);
+    o = __builtin_fmaf(Dk, hx, o);
     float g = gyj;
     if (has_z) {
       const float sgm = sigmoid_f32(zj);
       g = gyj * zj * sgm;
       const float dz = gyj * o * sgm * __builtin_fmaf(zj, 1.f - sgm, 1.f);
-      if (j_ok) st(p.dz, b * p.dzs_b + tj * p.dzs_t + d, dz, p.dz_f32);
+      if (j_ok) st(pdz, 0, dz, dz_f32);
     }
-    dD = __builtin_fmaf(g, xj, dD);
+    dD = __builtin_fmaf(g, hx, dD);
+    // the reverse recomputes its per-step values instead of keeping the
+    // recompute phase's (fewer live registers)
+    asm volatile("" : "+v"(hdt), "+v"(hx));
 
     // reverse through the tile
     for_steps_rev(std::make_integer_sequence<int, TT>{}, [&](auto S) {
+#pragma clang fp contract(off)
       constexpr int T = decltype(S)::value;
       const float dt = row_bcast<T>(hdt), xv = row_bcast<T>(hx), gs = row_bcast<T>(g);
       float dxp = 0.f, dtp = 0.f;
       float vB[KS], vC[KS];
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        const float2 bcv = s.t.bc[T][sg * KS + k];
+        const float2 bcv = s.bc[T][sg * KS + k];
         const float a = la.a[k];
-        const float Ab = __builtin_amdgcn_exp2f(dt * la.A2[k]);
-        const float cb = cbar(Ab, a, la.iA[k], dt, euler);
+        const float Ab = AA[T][k];
+        const float cb = cbar<FORM>(Ab, a, la.iA[k], dt);
         const float hp = T > 0 ? hh[T > 0 ? T - 1 : 0][k] : h0t[k];
         const float l = __builtin_fmaf(bcv.y, gs, carry[k]);
         const float bx = bcv.x * xv;
         vC[k] = gs * hh[T][k];
-        vB[k] = l * cb * xv;
-        dxp = __builtin_fmaf(l * cb, bcv.x, dxp);
-        const float dc_ddt = euler ? 1.f : Ab;
-        const float dc_da = euler ? 0.f : (a != 0.f ? (dt * Ab - cb) * la.iA[k] : 0.5f * dt * dt);
-        dtp = __builtin_fmaf(l, __builtin_fmaf(a * Ab, hp, dc_ddt * bx), dtp);
-        dA[k] = __builtin_fmaf(l, __builtin_fmaf(dt * Ab, hp, dc_da * bx), dA[k]);
-        carry[k] = Ab * l;
+        const float lc = l * cb;
+        vB[k] = lc * xv;
+        dxp = __builtin_fmaf(lc, bcv.x, dxp);
+        const float la_ = Ab * l;  // Abar lam: the next (earlier) step's carry
+        if constexpr (FORM == kEuler) {
+          // dh/ddelta = a Abar h_{t-1} + B x;  dh/da = delta Abar h_{t-1}
+          dtp = __builtin_fmaf(la_, a * hp, __builtin_fmaf(l, bx, dtp));
+          dA[k] = __builtin_fmaf(la_, dt * hp, dA[k]);
+        } else {
+          // dh/ddelta = Abar (a h_{t-1} + B x);  dh/da = delta Abar h_{t-1} + dcbar/da B x,
+          // dcbar/da = (delta Abar - cbar)/a (delta^2/2 at a = 0)
+          dtp = __builtin_fmaf(la_, __builtin_fmaf(a, hp, bx), dtp);
+          float dc_da = __builtin_fmaf(dt, Ab, -cb) * la.iA[k];
+          if constexpr (FORM == kZohZero) dc_da = a != 0.f ? dc_da : 0.5f * dt * dt;
+          dA[k] = __builtin_fmaf(la_, dt * hp, __builtin_fmaf(l * dc_da, bx, dA[k]));
+        }
+        carry[k] = la_;
       }
       s.part[0][tid][T] = dxp;
       s.part[1][tid][T] = dtp;
-      // dB, dC: sum over the wave's 4 channels (rows), then one row writes
+      // dB, dC: sum over the wave's 4 channels (rows); every row then holds
+      // the sum and writes it to the same place (no divergent store, which
+      // would keep every step's sums live until after the loop)
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        float vb = vB[k], vc = vC[k];
-        vb += __shfl_xor(vb, 16);
-        vc += __shfl_xor(vc, 16);
-        vb += __shfl_xor(vb, 32);
-        vc += __shfl_xor(vc, 32);
-        if (lane < G) {
-          s.red[wave][T][0][sg * KS + k] = vb;
-          s.red[wave][T][1][sg * KS + k] = vc;
-        }
+        s.red[wave][T][0][sg * KS + k] = sum_rows(vB[k]);
+        s.red[wave][T][1][sg * KS + k] = sum_rows(vC[k]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     });
     // lane sg: dx and ddelta of step sg
     float dxs = 0.f, dts = 0.f;
@@ -324,24 +492,26 @@ __global__ __launch_bounds__(NT) void bwd_kernel(ScanBwdParams p, int64_t n_dblk
     }
     dxs = __builtin_fmaf(Dk, g, dxs);
     if (p.dsoftplus) {
-      dts *= sigmoid_f32(s.t.dv[c][sg]);
+      dts *= sigmoid_f32(dv);
       if (j_ok) dbias += dts;
     }
     if (j_ok) {
-      st(p.dx, b * p.dxs_b + tj * p.dxs_t + d, dxs, p.dx_f32);
-      st(p.ddelta, b * p.dds_b + tj * p.dds_t + d, dts, p.dd_f32);
+      st(pdx, 0, dxs, dx_f32);
+      st(pdd, 0, dts, dd_f32);
     }
     __syncthreads();
     // dB, dC of the tile: sum over the 4 waves, store the workgroup's partial
-    for (int i = tid; i < TT * 2 * G * KS; i += NT) {
+#pragma unroll
+    for (int r = 0; r < RED; ++r) {
+      const int i = tid + r * NT;
       const int j = i / (2 * G * KS), q = (i / (G * KS)) % 2, n = i % (G * KS);
-      const int64_t t = t0 + j;
-      if (t < p.L && n < p.N) {
-        const float v = s.red[0][j][q][n] + s.red[1][j][q][n] + s.red[2][j][q][n] + s.red[3][j][q][n];
-        float* dst = q == 0 ? p.pdB : p.pdC;
-        dst[((dblk * p.batch + b) * p.L + t) * p.N + n] = v;
-      }
+      const float v = s.red[0][j][q][n] + s.red[1][j][q][n] + s.red[2][j][q][n] + s.red[3][j][q][n];
+      if (t0 + red_j[r] < L && red_n_ok[r]) *pred[r] = v;
+      pred[r] -= red_step;
     }
+    pdx -= sdx;
+    pdd -= sdd;
+    if (pdz) pdz -= sdz;
     __syncthreads();
   }
   // per-channel and per-state sums of this batch row
@@ -367,6 +537,21 @@ __global__ __launch_bounds__(NT) void bwd_kernel(ScanBwdParams p, int64_t n_dblk
   }
 }
 
+template <bool BF16, int KS, bool EULER>
+__global__ __launch_bounds__(NT) void bwd_kernel(ScanBwdParams p, int64_t n_dblk) {
+  __shared__ BwdSmem<KS> s;
+  const int tid = threadIdx.x;
+  const int64_t dblk = blockIdx.x % n_dblk, b = blockIdx.x / n_dblk;
+  int zero_a;
+  const LaneA<KS> la = lane_a<BF16, KS>(p, dblk * CH + tid / G, tid % G, zero_a);
+  if constexpr (EULER) {
+    bwd_walk<BF16, KS, kEuler>(s, p, b, dblk, la);
+  } else {
+    if (__syncthreads_or(zero_a)) bwd_walk<BF16, KS, kZohZero>(s, p, b, dblk, la);
+    else bwd_walk<BF16, KS, kZoh>(s, p, b, dblk, la);
+  }
+}
+
 // dst[i] = sum_k src[k * stride + i], k = 0 .. parts-1 in order
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ src, float* __restrict__ dst,
                                                      int64_t count, int64_t parts, int64_t stride) {
@@ -386,8 +571,13 @@ template <bool BF16, int KS>
 void launch_ks(const ScanBwdParams& p, hipStream_t stream) {
   const int64_t n_dblk = (p.D + CH - 1) / CH;
   const dim3 grid((unsigned)(n_dblk * p.batch));
-  hipLaunchKernelGGL((ckpt_kernel<BF16, KS>), grid, dim3(NT), 0, stream, p, n_dblk);
-  hipLaunchKernelGGL((bwd_kernel<BF16, KS>), grid, dim3(NT), 0, stream, p, n_dblk);
+  if (p.euler) {
+    hipLaunchKernelGGL((ckpt_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk);
+    hipLaunchKernelGGL((bwd_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk);
+  } else {
+    hipLaunchKernelGGL((ckpt_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk);
+    hipLaunchKernelGGL((bwd_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk);
+  }
   const int64_t bln = p.batch * p.L * p.N;
   reduce(p.pdB, p.dB, bln, n_dblk, bln, stream);
   reduce(p.pdC, p.dC, bln, n_dblk, bln, stream);

@@ -443,6 +443,15 @@ ssm_status validate_bwd_desc(const ssm_scan_bwd_desc* d) {
     if ((s = check_tensor(d->delta_bias, 1, dd, d->delta_bias.dtype == SSM_F32, false, false))) return s;
     if ((s = check_tensor(d->ddelta_bias, 1, dd, d->ddelta_bias.dtype == SSM_F32, false, true))) return s;
   }
+  // The kernels address one 16-step tile of 16 channels (or of all dstate
+  // states of B and C) with 32-bit byte offsets.
+  const int64_t e = esize(io);
+  auto fits = [&](const ssm_tensor_desc& t, int64_t width, int64_t es) {
+    return (16 * t.stride[1] + width * t.stride[2]) * es < ((int64_t)1 << 31);
+  };
+  if (!fits(d->x, 16, e) || !fits(d->delta, 16, e) || !fits(d->dy, 16, esize(d->dy.dtype)) ||
+      !fits(d->B, d->dstate, e) || !fits(d->C, d->dstate, e) || ((f & SSM_HAS_Z) && !fits(d->z, 16, e)))
+    return SSM_ERR_UNSUPPORTED;
   return SSM_OK;
 }
 
