@@ -399,7 +399,7 @@ def causal_conv1d(x, weight, bias=None, silu=True, y_dtype=None, y=None, stream=
     desc = conv_desc(x, weight, bias, y, silu)
     ptrs = conv_ptrs(x, weight, bias, y)
     _check(lib().ssm_causal_conv1d_fwd(ctypes.byref(desc), ctypes.byref(ptrs), _stream(stream)),
-           "ssm_causal_conv1d_fwd", "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd")
+           "ssm_causal_conv1d_fwd")
     return y
 
 
