@@ -200,7 +200,8 @@ typedef struct {
  *   D        : (nheads)  F32, any stride          if SSM_HAS_D (one skip weight per head)
  *   h0       : (batch, nheads, headdim, dstate) F32 contiguous  if SSM_HAS_H0
  *   h_last   : (batch, nheads, headdim, dstate) F32 contiguous  if SSM_WANT_HLAST
- * Supported: headdim == 64, dstate == 64, chunk in {64, 128, 256},
+ * Supported: headdim == 64, dstate in {64, 128, 256}, chunk in {64, 128,
+ * 256} except dstate 256 with chunk 256 (its staging exceeds the LDS),
  * nheads % ngroups == 0; seqlen need not be a multiple of chunk (the last
  * chunk is shorter).  SSM_HAS_Z is not accepted.  Every (batch, step, head or
  * group) row of x, B, C and y, and h0 / h_last, must start 16-byte aligned

@@ -167,11 +167,12 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t (*rows)[PR], int j0,
   return as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
 }
 
-// Block = (b, chunk c, head h), 8 waves.  S_loc[p][n] = sum_j (w_j x_j[p])
-// B_j[n], w_j = exp(A_cum_end - A_cum_j) beta_j: x rows are staged scaled by
-// w_j, B rows as they are; wave wv computes p-tile wv % 4 times n-tiles
-// 2*(wv/4) and +1, contracting over the Q steps in slices of 32.
-template <int Q>
+// Block = (b, chunk c, head h, 64-wide block nbk of the N states), 8 waves.
+// S_loc[p][n] = sum_j (w_j x_j[p]) B_j[n], w_j = exp(A_cum_end - A_cum_j)
+// beta_j: x rows are staged scaled by w_j, the block's 64 columns of the B
+// rows as they are; wave wv computes p-tile wv % 4 times n-tiles 2*(wv/4) and
+// +1, contracting over the Q steps in slices of 32.
+template <int Q, int NB>
 __global__ __launch_bounds__(512) void chunk_state_kernel(SSDParams p) {
   constexpr int NTH = 512;
   constexpr int PR = 64 + 4;        // row pitch (bf16)
@@ -180,6 +181,8 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(SSDParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][PR];  // B rows
   __shared__ float w[Q];
   int bid = (int)blockIdx.x;
+  const int nbk = bid % NB;
+  bid /= NB;
   const int64_t h = bid % (int)p.H;
   bid /= (int)p.H;
   const int64_t c = bid % (int)p.nchunks, b = bid / (int)p.nchunks;
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(SSDParams p) {
   const int64_t t0 = c * Q;
   uint4 rx[NTX], rb[NTX];
   const uint16_t* Xsrc = (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h;
-  const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
+  const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g + 64 * nbk;
 #pragma unroll
   for (int u = 0; u < NTX; ++u) {
     const int task = tid + NTH * u;
@@ -227,28 +230,31 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(SSDParams p) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) acc[k] = mfma(a, tr_operand<PR>(Bs, 32 * ks, 16 * (nt0 + k), lr, lq), acc[k]);
   }
-  float* dst = p.states + (((b * p.nchunks + c) * p.H + h) * 64) * 64;
+  constexpr int N = 64 * NB;
+  float* dst = p.states + (((b * p.nchunks + c) * p.H + h) * 64) * N + 64 * nbk;
 #pragma unroll
   for (int k = 0; k < 2; ++k)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(16 * pt + 4 * lq + r) * 64 + 16 * (nt0 + k) + lr] = acc[k][r];
+    for (int r = 0; r < 4; ++r) dst[(16 * pt + 4 * lq + r) * N + 16 * (nt0 + k) + lr] = acc[k][r];
 }
 
 // ---------------------------------------------------- s3 state passing
 
 __global__ __launch_bounds__(256) void state_passing_kernel(SSDParams p) {
-  // block = (b, h, quarter of the P*N = 4096 entries); 4 entries per thread
+  // block = (b, h, 1024 of the P*N entries); 4 entries per thread
+  const int64_t E = 64 * p.N;  // entries of one (b, h) state
+  const int nq = (int)(E / 1024);
   int64_t bid = blockIdx.x;
-  const int q = (int)(bid % 4);
-  bid /= 4;
+  const int q = (int)(bid % nq);
+  bid /= nq;
   const int64_t h = bid % p.H, b = bid / p.H;
-  const int e0 = q * 1024 + threadIdx.x * 4;
+  const int64_t e0 = q * 1024 + threadIdx.x * 4;
   float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (p.h0) S = *(const float4*)(p.h0 + (b * p.H + h) * 4096 + e0);
+  if (p.h0) S = *(const float4*)(p.h0 + (b * p.H + h) * E + e0);
   const float* Ac = p.A_cum + (b * p.H + h) * p.Lp;
-  const int64_t cstride = p.H * 4096;
-  const float* st = p.states + (b * p.nchunks * p.H + h) * 4096 + e0;
-  uint16_t* sin = (uint16_t*)p.S_in + (b * p.nchunks * p.H + h) * 4096 + e0;
+  const int64_t cstride = p.H * E;
+  const float* st = p.states + (b * p.nchunks * p.H + h) * E + e0;
+  uint16_t* sin = (uint16_t*)p.S_in + (b * p.nchunks * p.H + h) * E + e0;
   float4 nxt = *(const float4*)st;
   for (int64_t c = 0; c < p.nchunks; ++c) {
     const float4 cur = nxt;
@@ -260,7 +266,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(SSDParams p) {
     S.z = __builtin_fmaf(dec, S.z, cur.z);
     S.w = __builtin_fmaf(dec, S.w, cur.w);
   }
-  if (p.h_last) *(float4*)(p.h_last + (b * p.H + h) * 4096 + e0) = S;
+  if (p.h_last) *(float4*)(p.h_last + (b * p.H + h) * E + e0) = S;
 }
 
 // ------------------------------------------------------- s4 chunk scan
@@ -278,21 +284,25 @@ __global__ __launch_bounds__(256) void state_passing_kernel(SSDParams p) {
 // 4b .. +3], and output lane (g, m) gets x[j0 + 4g + i][16mt + m], i = 0..3:
 // four consecutive steps of one p, the contraction slots G'^T's layout needs.
 // beta_j is applied to G' (it multiplies the decay factor of column j).
-template <int Q>
+template <int Q, int NB>
 __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
   constexpr int NTH = 2 * Q;        // threads
   constexpr int NSTRIP = Q / 16;
-  constexpr int PR = 64 + 4;        // row pitch (bf16) of the staged x and B rows
-  constexpr int NTX = Q * 8 / NTH;  // (row, 8 values) pieces of x and of B per thread
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][PR];  // x rows: [j][p]
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][PR];  // B rows: [j][n]
+  constexpr int N = 64 * NB;        // states
+  constexpr int KS = N / 32;        // 32-wide contraction slices over the states
+  constexpr int PR = 64 + 4;        // row pitch (bf16) of the staged x rows
+  constexpr int PRB = N + 4;        // row pitch (bf16) of the staged B rows
+  constexpr int NTX = Q * 8 / NTH;  // (row, 8 values) pieces of x per thread
+  constexpr int NTB = NTX * NB;     // pieces of B per thread
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][PR];   // x rows: [j][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][PRB];  // B rows: [j][n]
   __shared__ float A2[Q];                                     // A_cum * log2(e)
   __shared__ float tb[Q];                                     // exp(A_cum[j|31] - A_cum[j]) * beta_j
   __shared__ float bj[Q];                                     // beta
-  // S_in (64 x 64 bf16), row p in 8 chunks of 8 values; chunk q of row p is
+  // S_in (64 x N bf16), row p in N/8 chunks of 8 values; chunk q of row p is
   // stored at chunk q ^ (p % 8) so the inter-chunk reads (16 rows, one chunk)
   // spread over the banks.
-  __shared__ __attribute__((aligned(16))) uint4 Ss[64][8];
+  __shared__ __attribute__((aligned(16))) uint4 Ss[64][8 * NB];
 
   int64_t bid = blockIdx.x;
   const int64_t h = bid % p.H;
@@ -306,7 +316,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
   const int kst[2] = {wv, NSTRIP - 1 - wv};
 
   // --- issue the staging loads and the C operands before using any
-  uint4 rx[NTX], rb[NTX];
+  uint4 rx[NTX], rb[NTB];
   const uint16_t* Xsrc = (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h;
   const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
 #pragma unroll
@@ -315,22 +325,30 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
     const int j = task / 8, cb = (task % 8) * 8;
     const int64_t tr = t0 + j < p.L ? t0 + j : p.L - 1;
     rx[u] = *(const uint4*)(Xsrc + tr * p.xs_t + cb);
+  }
+#pragma unroll
+  for (int u = 0; u < NTB; ++u) {
+    const int task = tid + NTH * u;
+    const int j = task / (8 * NB), cb = (task % (8 * NB)) * 8;
+    const int64_t tr = t0 + j < p.L ? t0 + j : p.L - 1;
     rb[u] = *(const uint4*)(Bsrc + tr * p.Bs_t + cb);
   }
-  bf16x8 Cop[2][2];  // C operand of each strip: C[i][32*ks + 8*lq .. +7]
+  bf16x8 Cop[2][KS];  // C operand of each strip: C[i][32*ks + 8*lq .. +7]
   const uint16_t* Cb = (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int64_t ti = t0 + 16 * kst[s] + lr;
     const int64_t tr = ti < p.L ? ti : p.L - 1;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) Cop[s][ks] = as_bf16x8(*(const uint4*)(Cb + tr * p.Cs_t + 32 * ks + 8 * lq));
+    for (int ks = 0; ks < KS; ++ks) Cop[s][ks] = as_bf16x8(*(const uint4*)(Cb + tr * p.Cs_t + 32 * ks + 8 * lq));
   }
-  // S_in of this (chunk, head): 512 16-byte pieces
-  const uint16_t* Sp = (const uint16_t*)p.S_in + ((b * p.nchunks + c) * p.H + h) * 4096;
-  uint4 rs[512 / NTH];
+  // S_in of this (chunk, head): 512 * NB 16-byte pieces
+  constexpr int NS = 512 * NB / NTH;
+  static_assert(NS * NTH == 512 * NB, "whole S_in pieces per thread");
+  const uint16_t* Sp = (const uint16_t*)p.S_in + ((b * p.nchunks + c) * p.H + h) * (64 * N);
+  uint4 rs[NS];
 #pragma unroll
-  for (int u = 0; u < 512 / NTH; ++u) rs[u] = *(const uint4*)(Sp + 8 * (tid + NTH * u));
+  for (int u = 0; u < NS; ++u) rs[u] = *(const uint4*)(Sp + 8 * (tid + NTH * u));
   const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
   const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
   for (int t = tid; t < Q; t += NTH) {
@@ -346,17 +364,25 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
     const int j = task / 8, cb = (task % 8) * 8;
     const bool ok = t0 + j < p.L;
     *(uint4*)&Xs[j][cb] = ok ? rx[u] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < NTB; ++u) {
+    const int task = tid + NTH * u;
+    const int j = task / (8 * NB), cb = (task % (8 * NB)) * 8;
+    const bool ok = t0 + j < p.L;
     *(uint4*)&Bs[j][cb] = ok ? rb[u] : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int u = 0; u < 512 / NTH; ++u) {
-    const int e = tid + NTH * u, row = e / 8, cq = e % 8;
+  for (int u = 0; u < NS; ++u) {
+    const int e = tid + NTH * u, row = e / (8 * NB), cq = e % (8 * NB);
     Ss[row][cq ^ (row % 8)] = rs[u];
   }
   // C rows past L must not contribute
 #pragma unroll
   for (int s = 0; s < 2; ++s)
-    if (t0 + 16 * kst[s] + lr >= p.L) Cop[s][0] = Cop[s][1] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    if (t0 + 16 * kst[s] + lr >= p.L)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) Cop[s][ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
   __syncthreads();
 
   f32x4 acc[2][4];
@@ -370,12 +396,6 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
   const int jb_last = (16 * kst[1]) / 32;
   for (int jb = 0; jb <= jb_last; ++jb) {
     const int j0 = 32 * jb;
-    // A operands of G^T = B_J C_I^T: B rows j0 + 16*jt + lr
-    bf16x8 aB[2][2];
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) aB[jt][ks] = as_bf16x8(*(const uint4*)&Bs[j0 + 16 * jt + lr][32 * ks + 8 * lq]);
     // A operands of Y^T += X^T G'^T: rows p, contraction slots in G^T's layout
     bf16x8 aX[4];
 #pragma unroll
@@ -394,9 +414,11 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
       f32x4 gt[2];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
+        // A operands of G^T = B_J C_I^T: B rows j0 + 16*jt + lr, read per use
         f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-        a = mfma(aB[jt][0], Cop[s][0], a);
-        a = mfma(aB[jt][1], Cop[s][1], a);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          a = mfma(as_bf16x8(*(const uint4*)&Bs[j0 + 16 * jt + lr][32 * ks + 8 * lq]), Cop[s][ks], a);
         gt[jt] = a;  // G^T[j0 + 16*jt + 4*lq + r][i]
       }
       float v[8];
@@ -439,13 +461,14 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int row = 16 * mt + lr;
-    const bf16x8 a0 = as_bf16x8(Ss[row][lq ^ (row % 8)]);
-    const bf16x8 a1 = as_bf16x8(Ss[row][(lq + 4) ^ (row % 8)]);
+    bf16x8 aS[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) aS[ks] = as_bf16x8(Ss[row][(4 * ks + lq) ^ (row % 8)]);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-      a = mfma(a0, Cop[s][0], a);
-      a = mfma(a1, Cop[s][1], a);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) a = mfma(aS[ks], Cop[s][ks], a);
       const float ei = __builtin_amdgcn_exp2f(A2[16 * kst[s] + lr]);
       acc[s][mt] += a * ei;
     }
@@ -483,25 +506,43 @@ hipError_t launch_ssd_chunk_cumsum(const SSDParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int NB>
+void launch_state_nb(const SSDParams& p, hipStream_t stream) {
+  const unsigned nb = (unsigned)(p.batch * p.nchunks * p.H * NB);
+  if (p.Q == 64) hipLaunchKernelGGL((chunk_state_kernel<64, NB>), dim3(nb), dim3(512), 0, stream, p);
+  else if (p.Q == 128) hipLaunchKernelGGL((chunk_state_kernel<128, NB>), dim3(nb), dim3(512), 0, stream, p);
+  else hipLaunchKernelGGL((chunk_state_kernel<256, NB>), dim3(nb), dim3(512), 0, stream, p);
+}
+
 hipError_t launch_ssd_chunk_state(const SSDParams& p, hipStream_t stream) {
-  const unsigned nb = (unsigned)(p.batch * p.nchunks * p.H);
-  if (p.Q == 64) hipLaunchKernelGGL(chunk_state_kernel<64>, dim3(nb), dim3(512), 0, stream, p);
-  else if (p.Q == 128) hipLaunchKernelGGL(chunk_state_kernel<128>, dim3(nb), dim3(512), 0, stream, p);
-  else hipLaunchKernelGGL(chunk_state_kernel<256>, dim3(nb), dim3(512), 0, stream, p);
+  if (p.N == 64) launch_state_nb<1>(p, stream);
+  else if (p.N == 128) launch_state_nb<2>(p, stream);
+  else launch_state_nb<4>(p, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_ssd_state_passing(const SSDParams& p, hipStream_t stream) {
-  const unsigned nb = (unsigned)(p.batch * p.H * 4);
+  const unsigned nb = (unsigned)(p.batch * p.H * (64 * p.N / 1024));
   hipLaunchKernelGGL(state_passing_kernel, dim3(nb), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_ssd_chunk_scan(const SSDParams& p, hipStream_t stream) {
   const unsigned nb = (unsigned)(p.batch * p.nchunks * p.H);
-  if (p.Q == 64) hipLaunchKernelGGL(chunk_scan_kernel<64>, dim3(nb), dim3(128), 0, stream, p);
-  else if (p.Q == 128) hipLaunchKernelGGL(chunk_scan_kernel<128>, dim3(nb), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(chunk_scan_kernel<256>, dim3(nb), dim3(512), 0, stream, p);
+  // (chunk, states) pairs whose staging fits in LDS; the host rejects chunk
+  // 256 with 256 states
+  if (p.N == 64) {
+    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 1>), dim3(nb), dim3(128), 0, stream, p);
+    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 1>), dim3(nb), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_scan_kernel<256, 1>), dim3(nb), dim3(512), 0, stream, p);
+  } else if (p.N == 128) {
+    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 2>), dim3(nb), dim3(128), 0, stream, p);
+    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 2>), dim3(nb), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_scan_kernel<256, 2>), dim3(nb), dim3(512), 0, stream, p);
+  } else {
+    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 4>), dim3(nb), dim3(128), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_scan_kernel<128, 4>), dim3(nb), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

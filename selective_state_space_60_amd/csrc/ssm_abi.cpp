@@ -221,7 +221,8 @@ ssm_status validate_ssd_desc(const ssm_ssd_desc* d) {
     return SSM_ERR_SHAPE;
   if (d->nheads % d->ngroups) return SSM_ERR_SHAPE;
   if (d->flags & ~kSSDFlags) return SSM_ERR_UNSUPPORTED;
-  if (d->headdim != 64 || d->dstate != 64 || (d->chunk != 64 && d->chunk != 128 && d->chunk != 256))
+  if (d->headdim != 64 || (d->dstate != 64 && d->dstate != 128 && d->dstate != 256) ||
+      (d->chunk != 64 && d->chunk != 128 && d->chunk != 256) || (d->dstate == 256 && d->chunk == 256))
     return SSM_ERR_UNSUPPORTED;
   if (d->x.dtype == SSM_F32 || d->x.dtype == SSM_F16) return SSM_ERR_UNSUPPORTED;
   const int64_t blhp[4] = {d->batch, d->seqlen, d->nheads, d->headdim};

@@ -171,6 +171,9 @@ def _ssd(batch=1, L=100, H=4, P=64, N=64, G=1, Q=64, flags=0, **over):
 @pytest.mark.parametrize("mutate,status", [
     (lambda d, p: setattr(d, "chunk", 100), ssm.SSM_ERR_UNSUPPORTED),
     (lambda d, p: setattr(d, "headdim", 32), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: setattr(d, "dstate", 96), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: (setattr(d, "dstate", 256), setattr(d, "chunk", 256)), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: setattr(d, "dstate", 128), ssm.SSM_ERR_SHAPE),  # B, C, h0 still have 64 states
     (lambda d, p: setattr(d, "ngroups", 3), ssm.SSM_ERR_SHAPE),
     (lambda d, p: setattr(d, "flags", d.flags | ssm.SSM_HAS_Z), ssm.SSM_ERR_UNSUPPORTED),
     (lambda d, p: setattr(d.x, "dtype", 0), ssm.SSM_ERR_UNSUPPORTED),

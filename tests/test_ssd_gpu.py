@@ -151,3 +151,31 @@ def test_strided_heads_view():
     torch.cuda.synchronize()
     yr, _ = oracle.ssd(inp, "bf16")
     assert_close(host_f64(y), yr, "bf16", "ssd strided")
+
+
+@pytest.mark.parametrize("dstate,chunk", [(128, 64), (128, 128), (128, 256), (256, 64), (256, 128)])
+def test_larger_states(dstate, chunk):
+    """N = 128 and 256 states (every supported chunk size), ragged length,
+    grouped B/C, h0 and h_last, against the expanded recurrence."""
+    spec = small(seqlen=333, chunk=chunk, nheads=4, ngroups=2, dstate=dstate)
+    h0 = synth.state_input((2, 4, 64, dstate), 11)
+    _check(spec, 11, h0=h0)
+
+
+def test_larger_states_steps():
+    """Each step's intermediate against the chunked reference at N = 256."""
+    spec = small(seqlen=200, chunk=64, nheads=2, dstate=256)
+    inp = synth.ssd_inputs(spec, 12)
+    banner("ssd steps N256")
+    g = _upload(inp)
+    args = (g["x"], g["delta"], g["A"], g["B"], g["C"], spec.chunk)
+    A_cum, beta = ssm.ssd_chunk_cumsum(*args)
+    states = ssm.ssd_chunk_state(*args, A_cum, beta)
+    S_in, hl = ssm.ssd_state_passing(*args, A_cum, states, want_hlast=True)
+    y = ssm.ssd_chunk_scan(*args, A_cum, beta, S_in, D=g["D"])
+    torch.cuda.synchronize()
+    ref = oracle.ssd_chunked(inp, "bf16", spec.chunk)
+    assert_close(host_f64(states), ref["S_loc"], "bf16", "chunk states N256")
+    assert_close(host_f64(S_in), ref["S_in"], "bf16", "chunk-entry states N256")
+    assert_close(host_f64(hl), ref["h_last"], "bf16", "h_last N256")
+    assert_close(host_f64(y), ref["y"], "bf16", "y N256")
