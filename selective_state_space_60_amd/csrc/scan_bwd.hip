@@ -99,6 +99,15 @@ __device__ __forceinline__ void for_steps_rev(std::integer_sequence<int, S...>, 
 
 static_assert(CH * TT == NT, "one (channel, step) of a tile per thread");
 
+// Logical block index: the hardware deals consecutive block ids round-robin
+// over the 8 XCDs, each with its own L2.  A tile row of 16 channels is 32
+// bytes of a 128-byte line, so neighbouring channel blocks are put on the
+// same XCD, where they share each line's one fetch from HBM.
+__device__ __forceinline__ int64_t logical_block(int64_t nblocks_padded) {
+  const int64_t i = blockIdx.x;
+  return (i & 7) * (nblocks_padded >> 3) + (i >> 3);
+}
+
 // Update forms (uniform per workgroup): zero-order hold with A != 0, zero-order
 // hold with some A == 0 (limit delta), and the simplified Bbar = delta B.
 enum Form : int { kZoh = 0, kZohZero = 1, kEuler = 2 };
@@ -297,10 +306,12 @@ __device__ __forceinline__ void ckpt_walk(CkptSmem<KS>& s, const ScanBwdParams& 
 }
 
 template <bool BF16, int KS, bool EULER>
-__global__ __launch_bounds__(NT) void ckpt_kernel(ScanBwdParams p, int64_t n_dblk) {
+__global__ __launch_bounds__(NT) void ckpt_kernel(ScanBwdParams p, int64_t n_dblk, int64_t nblocks_padded) {
   __shared__ CkptSmem<KS> s;
   const int tid = threadIdx.x, c = tid / G, sg = tid % G;
-  const int64_t dblk = blockIdx.x % n_dblk, b = blockIdx.x / n_dblk;
+  const int64_t lb = logical_block(nblocks_padded);
+  if (lb >= n_dblk * p.batch) return;
+  const int64_t dblk = lb % n_dblk, b = lb / n_dblk;
   const int64_t d0 = dblk * CH, d = d0 + c;
   int zero_a;
   const LaneA<KS> la = lane_a<BF16, KS>(p, d, sg, zero_a);
@@ -538,10 +549,12 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
 }
 
 template <bool BF16, int KS, bool EULER>
-__global__ __launch_bounds__(NT) void bwd_kernel(ScanBwdParams p, int64_t n_dblk) {
+__global__ __launch_bounds__(NT) void bwd_kernel(ScanBwdParams p, int64_t n_dblk, int64_t nblocks_padded) {
   __shared__ BwdSmem<KS> s;
   const int tid = threadIdx.x;
-  const int64_t dblk = blockIdx.x % n_dblk, b = blockIdx.x / n_dblk;
+  const int64_t lb = logical_block(nblocks_padded);
+  if (lb >= n_dblk * p.batch) return;
+  const int64_t dblk = lb % n_dblk, b = lb / n_dblk;
   int zero_a;
   const LaneA<KS> la = lane_a<BF16, KS>(p, dblk * CH + tid / G, tid % G, zero_a);
   if constexpr (EULER) {
@@ -552,31 +565,94 @@ __global__ __launch_bounds__(NT) void bwd_kernel(ScanBwdParams p, int64_t n_dblk
   }
 }
 
-// dst[i] = sum_k src[k * stride + i], k = 0 .. parts-1 in order
-__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ src, float* __restrict__ dst,
-                                                     int64_t count, int64_t parts, int64_t stride) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= count) return;
-  float acc = 0.f;
-  for (int64_t k = 0; k < parts; ++k) acc += src[k * stride + i];
-  dst[i] = acc;
+// dst[i] = sum_k src[k * stride + i] over k = 0 .. parts-1, in a fixed order:
+// the RG waves of a workgroup each add one run of consecutive parts in order
+// (run r holds parts [r*parts/RG, (r+1)*parts/RG)), then the run sums are
+// added in run order.  V consecutive elements per lane (V = 4: 16-byte
+// loads, for 16-byte aligned buffers, count and stride).  RG loads in flight
+// per column keep the partial sums streaming from HBM.
+constexpr int RG = 4;
+
+template <int V>
+struct Vec {
+  float v[V];
+};
+
+template <int V>
+__device__ __forceinline__ Vec<V> vload(const float* p) {
+  Vec<V> r;
+  if constexpr (V == 4) {
+    const float4 q = *(const float4*)p;
+    r.v[0] = q.x, r.v[1] = q.y, r.v[2] = q.z, r.v[3] = q.w;
+  } else {
+    r.v[0] = *p;
+  }
+  return r;
+}
+
+template <int V>
+__global__ __launch_bounds__(64 * RG) void reduce_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                         int64_t count, int64_t parts, int64_t stride) {
+  __shared__ float run_sum[RG - 1][64 * V];
+  const int c = threadIdx.x % 64, r = threadIdx.x / 64;
+  const int64_t i = ((int64_t)blockIdx.x * 64 + c) * V;
+  const bool ok = i < count;
+  const int64_t k0 = r * parts / RG, k1 = (r + 1) * parts / RG;
+  float acc[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = 0.f;
+  if (ok) {
+    const float* q = src + k0 * stride + i;
+    int64_t k = k0;
+    for (; k + 4 <= k1; k += 4, q += 4 * stride) {
+      const Vec<V> a = vload<V>(q), b = vload<V>(q + stride), d = vload<V>(q + 2 * stride),
+                   e4 = vload<V>(q + 3 * stride);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = ((acc[e] + a.v[e]) + b.v[e] + d.v[e]) + e4.v[e];
+    }
+    for (; k < k1; ++k, q += stride) {
+      const Vec<V> a = vload<V>(q);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += a.v[e];
+    }
+  }
+  if (r > 0) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) run_sum[r - 1][c * V + e] = acc[e];
+  }
+  __syncthreads();
+  if (r == 0 && ok) {
+#pragma unroll
+    for (int g = 0; g < RG - 1; ++g)
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += run_sum[g][c * V + e];
+    if constexpr (V == 4) *(float4*)(dst + i) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    else dst[i] = acc[0];
+  }
 }
 
 void reduce(const float* src, float* dst, int64_t count, int64_t parts, int64_t stride, hipStream_t stream) {
-  const unsigned nb = (unsigned)((count + 255) / 256);
-  hipLaunchKernelGGL(reduce_kernel, dim3(nb), dim3(256), 0, stream, src, dst, count, parts, stride);
+  const bool v4 = count % 4 == 0 && stride % 4 == 0 && ((uintptr_t)src | (uintptr_t)dst) % 16 == 0;
+  if (v4) {
+    const unsigned nb = (unsigned)((count / 4 + 63) / 64);
+    hipLaunchKernelGGL(reduce_kernel<4>, dim3(nb), dim3(64 * RG), 0, stream, src, dst, count, parts, stride);
+  } else {
+    const unsigned nb = (unsigned)((count + 63) / 64);
+    hipLaunchKernelGGL(reduce_kernel<1>, dim3(nb), dim3(64 * RG), 0, stream, src, dst, count, parts, stride);
+  }
 }
 
 template <bool BF16, int KS>
 void launch_ks(const ScanBwdParams& p, hipStream_t stream) {
   const int64_t n_dblk = (p.D + CH - 1) / CH;
-  const dim3 grid((unsigned)(n_dblk * p.batch));
+  const int64_t npad = (n_dblk * p.batch + 7) / 8 * 8;  // blocks past the end exit at once
+  const dim3 grid((unsigned)npad);
   if (p.euler) {
-    hipLaunchKernelGGL((ckpt_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk);
-    hipLaunchKernelGGL((bwd_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk);
+    hipLaunchKernelGGL((ckpt_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
+    hipLaunchKernelGGL((bwd_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
   } else {
-    hipLaunchKernelGGL((ckpt_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk);
-    hipLaunchKernelGGL((bwd_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk);
+    hipLaunchKernelGGL((ckpt_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
+    hipLaunchKernelGGL((bwd_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
   }
   const int64_t bln = p.batch * p.L * p.N;
   reduce(p.pdB, p.dB, bln, n_dblk, bln, stream);
