@@ -73,17 +73,20 @@ __device__ __forceinline__ float softplus_f32(float v) {
   return fmaxf(v, 0.f) + lp;
 }
 
-// Sum over the 4 rows (16-lane groups) of the wave, in every lane.  gfx950's
-// permlane32 swap, given (v, v), returns v's lower half-wave in both halves of
-// one result and its upper half-wave in the other, so their sum adds the
-// halves; permlane16 swap does the same between neighbouring rows.  (Lane
-// layout checked on the device.)  VALU only: no LDS round trip.
-__device__ __forceinline__ float sum_rows(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const float w = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  const uint32_t uw = __float_as_uint(w);
-  const auto q = __builtin_amdgcn_permlane16_swap(uw, uw, false, false);
+// Sums over the 4 rows (16-lane groups) of a wave, for the dB and dC terms
+// of two steps at once, in two gfx950 lane swaps (lane layouts checked on the
+// device).  permlane32 swap of (u, v) returns (u's lower half-wave | v's
+// lower) and (u's upper | v's upper): their sum holds u's two half-sums (rows
+// 0+2, 1+3) in the lower half-wave and v's in the upper.  permlane16 swap of
+// (a, b) returns rows (a0, b0, a2, b2) and (a1, b1, a3, b3): their sum is
+// (a0+a1, b0+b1, a2+a3, b2+b3).
+__device__ __forceinline__ float half_sums(float u, float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ float row_sums(float a, float b) {
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
@@ -347,6 +350,11 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
   for (int k = 0; k < KS; ++k) carry[k] = dA[k] = 0.f;
   float dD = 0.f, dbias = 0.f;  // this lane's steps of its channel
   float* prow = &s.part[0][tid][0];
+  static_assert(TT % 2 == 0, "dB, dC row sums pair the steps");
+  // this lane's store of the paired row sums: row r of the wave holds step
+  // T + 1 - (r & 1) (T even) of dB (r < 2) or dC (r >= 2)
+  const int wrow = c % 4;
+  float* red_lane = &s.red[wave][0][0][0] + (1 - (wrow & 1)) * 2 * G * KS + (wrow >> 1) * G * KS + sg * KS;
 
   // Per-lane pointers, set up once and moved one tile per iteration (the
   // loop then needs no strides: fewer live scalar registers).
@@ -448,6 +456,7 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
     asm volatile("" : "+v"(hdt), "+v"(hx));
 
     // reverse through the tile
+    float held[KS];
     for_steps_rev(std::make_integer_sequence<int, TT>{}, [&](auto S) {
 #pragma clang fp contract(off)
       constexpr int T = decltype(S)::value;
@@ -481,16 +490,24 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
           dA[k] = __builtin_fmaf(la_, dt * hp, __builtin_fmaf(l * dc_da, bx, dA[k]));
         }
         carry[k] = la_;
+        // pin the accumulation to this step: left free, the compiler sinks
+        // every step's dA terms past the tile and keeps their operands live
+        asm volatile("" : "+v"(dA[k]));
       }
       s.part[0][tid][T] = dxp;
       s.part[1][tid][T] = dtp;
-      // dB, dC: sum over the wave's 4 channels (rows); every row then holds
-      // the sum and writes it to the same place (no divergent store, which
-      // would keep every step's sums live until after the loop)
+      // dB, dC: sums over the wave's 4 channels (rows), two steps at a time.
+      // Odd step T keeps its half-sums; at step T - 1 the row sums give row 0
+      // dB and row 2 dC of step T, rows 1 and 3 those of step T - 1, and each
+      // lane stores its own (a store in every lane: none is left divergent).
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        s.red[wave][T][0][sg * KS + k] = sum_rows(vB[k]);
-        s.red[wave][T][1][sg * KS + k] = sum_rows(vC[k]);
+        const float u = half_sums(vB[k], vC[k]);
+        if constexpr (T % 2 == 1) {
+          held[k] = u;
+        } else {
+          red_lane[T * 2 * G * KS + k] = row_sums(held[k], u);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     });
