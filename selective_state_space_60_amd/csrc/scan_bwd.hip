@@ -418,16 +418,26 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
     float hh[TT][KS], AA[TT][KS];
     {
       float h[KS];
+      float2 bc_next[KS];  // the next step's (B, C), read one step ahead
 #pragma unroll
-      for (int k = 0; k < KS; ++k) h[k] = h0t[k];
+      for (int k = 0; k < KS; ++k) {
+        h[k] = h0t[k];
+        bc_next[k] = s.bc[0][sg * KS + k];
+      }
       for_steps(std::make_integer_sequence<int, TT>{}, [&](auto S) {
 #pragma clang fp contract(off)
         constexpr int T = decltype(S)::value;
         const float dt = row_bcast<T>(hdt), xv = row_bcast<T>(hx);
+        float2 bc_cur[KS];
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          bc_cur[k] = bc_next[k];
+          if constexpr (T + 1 < TT) bc_next[k] = s.bc[T + 1][sg * KS + k];
+        }
         float yp = 0.f;
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-          const float2 bcv = s.bc[T][sg * KS + k];
+          const float2 bcv = bc_cur[k];
           const float Ab = __builtin_amdgcn_exp2f(dt * la.A2[k]);
           h[k] = __builtin_fmaf(Ab, h[k], cbar<FORM>(Ab, la.a[k], la.iA[k], dt) * (bcv.x * xv));
           hh[T][k] = h[k];
@@ -457,15 +467,24 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
 
     // reverse through the tile
     float held[KS];
+    float2 bc_next[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) bc_next[k] = s.bc[TT - 1][sg * KS + k];
     for_steps_rev(std::make_integer_sequence<int, TT>{}, [&](auto S) {
 #pragma clang fp contract(off)
       constexpr int T = decltype(S)::value;
       const float dt = row_bcast<T>(hdt), xv = row_bcast<T>(hx), gs = row_bcast<T>(g);
       float dxp = 0.f, dtp = 0.f;
       float vB[KS], vC[KS];
+      float2 bc_cur[KS];
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        const float2 bcv = s.bc[T][sg * KS + k];
+        bc_cur[k] = bc_next[k];
+        if constexpr (T > 0) bc_next[k] = s.bc[T - 1][sg * KS + k];
+      }
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const float2 bcv = bc_cur[k];
         const float a = la.a[k];
         const float Ab = AA[T][k];
         const float cb = cbar<FORM>(Ab, a, la.iA[k], dt);
