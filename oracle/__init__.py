@@ -22,6 +22,10 @@ and it shares no code with it.
   (the recomputation-based backward of tildalice.io 역전파 시 재계산 computes
   the same numbers): the forward states of each row, then the adjoint
   recurrence lam_t = C_t g_t + Abar_{t+1} lam_{t+1} backwards in time.
+* ``ssd_bwd`` is the SSD's gradient as the scan's: each channel (h, p) runs
+  the selective recurrence with tied per-head (delta, A, D) and per-group
+  (B, C) parameters, so the scan backward of the untied channels, with the
+  tied copies' gradients added, is its derivative.
 * ``causal_conv1d`` is the Mamba block's per-channel Conv1D of width k with
   k - 1 steps of zero padding cut back to the first L outputs, then SiLU
   (tildalice.io, Mamba 블록 아키텍처 and the SelectiveSSM listing), as a direct
@@ -220,6 +224,62 @@ def selective_scan_bwd(inp: dict, io: str, dy, dy_io: str = None, euler: bool = 
     return out
 
 
+SSD_BWD_MUTATIONS = {1: "head h read from group h % G instead of h / (H / G)",
+                     2: "ddelta taken from the head's first channel only"}
+
+
+def ssd_bwd(inp: dict, io: str, dy, ngroups: int = 1, euler: bool = False, h0=None, dy_io: str = None,
+            mutation: int = 0, nthreads=None) -> dict:
+    """Gradients of sum(dy * y) for (y, _) = ssd(inp, ...), fp64.
+
+    Every channel (h, p) of the SSD runs the selective recurrence with the
+    head's scalar A, its delta and the B, C of its group (obsidian-dorae222
+    "Mamba-2", SSM-Attention 동치성 and SSD 타일링 알고리즘: the chunked form
+    computes that recurrence exactly).  So the SSD is the selective scan of
+    its untied channels, and its gradient is selective_scan_bwd of those
+    channels with the gradients of tied copies added: over p for delta and D,
+    over p and n for A, over the heads of a group for B and C.
+    inp as for ssd; dy (batch, L, H, P) in dy_io (default io).
+    Returns dx (batch, L, H, P), ddelta (batch, L, H), dA (H,), dB, dC
+    (batch, L, G, N), dD (H,) if D, dh0 (batch, H, P, N) if h0.
+    """
+    x, dl, B, C = (_f64(inp.get(k), io) for k in ("x", "delta", "B", "C"))
+    A = np.asarray(inp["A"], np.float32)
+    Dk = None if inp.get("D") is None else np.asarray(inp["D"], np.float32)
+    dyf = _f64(dy, dy_io or io)
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert G == ngroups and H % G == 0 and dl.shape == (batch, L, H) and A.shape == (H,) and dyf.shape == x.shape
+    hpg = H // G
+    out = {"dx": np.zeros((batch, L, H, P)), "ddelta": np.zeros((batch, L, H)), "dA": np.zeros(H),
+           "dB": np.zeros((batch, L, G, N)), "dC": np.zeros((batch, L, G, N))}
+    if Dk is not None:
+        out["dD"] = np.zeros(H)
+    if h0 is not None:
+        out["dh0"] = np.zeros((batch, H, P, N))
+    for g in range(G):
+        heads = np.arange(g * hpg, (g + 1) * hpg)
+        src = heads % G if mutation == 1 else np.full(hpg, g)
+        for k, h in enumerate(heads):
+            # one head at a time: channels p of head h, B and C of its group
+            sub = {"x": x[:, :, h, :], "delta": np.repeat(dl[:, :, h:h + 1], P, axis=2),
+                   "A": np.full((P, N), A[h], np.float32), "B": B[:, :, src[k], :], "C": C[:, :, src[k], :]}
+            if Dk is not None:
+                sub["D"] = np.full(P, Dk[h], np.float32)
+            h0h = None if h0 is None else np.asarray(h0, np.float64)[:, h]
+            r = selective_scan_bwd(sub, "f64", dyf[:, :, h, :], euler=euler, h0=h0h, nthreads=nthreads)
+            out["dx"][:, :, h, :] = r["dx"]
+            out["ddelta"][:, :, h] = r["ddelta"][:, :, 0] if mutation == 2 else r["ddelta"].sum(axis=2)
+            out["dA"][h] = r["dA"].sum()
+            out["dB"][:, :, g, :] += r["dB"]
+            out["dC"][:, :, g, :] += r["dC"]
+            if Dk is not None:
+                out["dD"][h] = r["dD"].sum()
+            if h0 is not None:
+                out["dh0"][:, h] = r["dh0"]
+    return out
+
+
 CONV_MUTATIONS = {1: "taps reversed", 2: "window one step late", 3: "sigmoid in place of SiLU"}
 
 
@@ -249,6 +309,8 @@ def _f64(a, io):
         return None
     if io == "bf16":
         return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if io == "f64":
+        return np.asarray(a, np.float64)
     return np.asarray(a, np.float32).astype(np.float64)
 
 
@@ -272,8 +334,9 @@ def ssd_chunked(inp: dict, io: str, chunk: int, ngroups: int = 1, euler: bool = 
     dl = _f64(inp["delta"], io)
     B = _f64(inp["B"], io)
     C = _f64(inp["C"], io)
-    A = np.asarray(inp["A"], np.float32).astype(np.float64)
-    Dk = None if inp.get("D") is None else np.asarray(inp["D"], np.float32).astype(np.float64)
+    # A and D: fp32 parameters, or fp64 as given (io "f64")
+    A = _f64(inp["A"], "f64" if io == "f64" else "f32")
+    Dk = _f64(inp.get("D"), "f64" if io == "f64" else "f32")
     batch, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     hpg = H // ngroups
