@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 #define SSM_MAX_DIMS 5
 #define SSM_SCAN_MAX_DSTATE 64 /* selective scan: N <= 64 */
 
@@ -224,6 +224,71 @@ typedef struct {
   float* h_last;   /* NULL unless SSM_WANT_HLAST */
 } ssm_ssd_ptrs;
 
+/* ---------------------------------------------------------- SSD backward */
+
+/* Backward of the SSD ("Mamba-2: 상태 공간 기반 시퀀스 모델", obsidian-dorae222,
+ * SSD 타일링 알고리즘, each chunked step differentiated).  Given the forward
+ * inputs and dy = dLoss/dy it writes the gradients of x, delta, A, B, C, D
+ * and h0 (no gradient flows in through the final state).  With A_cum, beta,
+ * S_in as in the forward steps below, decay_ij = exp(A_cum_i - A_cum_j) for
+ * j <= i in a chunk, w_j = exp(A_cum_end - A_cum_j) and, per (batch, head),
+ *   G[c]     = sum_{i in c} exp(A_cum_i) dy_i C_i^T + exp(A_cum_end[c]) G[c+1]
+ *              (G past the last chunk = 0; G[0] = dh0; G[c+1] is the gradient
+ *              of chunk c's own state, dS_loc)
+ *   dC_i     = sum_j decay_ij beta_j (dy_i . x_j) B_j + exp(A_cum_i) S_in^T dy_i
+ *   R_j      = sum_i decay_ij (C_i . B_j) dy_i + w_j dS_loc B_j
+ *   dx_j     = beta_j R_j + D dy_j;   dbeta_j = x_j . R_j
+ *   dB_j     = sum_i decay_ij beta_j (dy_i . x_j) C_i + w_j beta_j dS_loc^T x_j
+ *   dA_cum_i = sum_j W_ij - sum_k W_ki + exp(A_cum_i) C_i . (S_in^T dy_i) - T_i
+ *              with W_ij = decay_ij beta_j (dy_i . x_j)(C_i . B_j) and
+ *              T_i = w_i beta_i x_i . (dS_loc B_i), plus at the chunk end
+ *              sum_j T_j + exp(A_cum_end) <S_in, G[c+1]>
+ *   da       = reverse cumulative sum of dA_cum inside each chunk
+ *   ddelta   = A da + dbeta dbeta/ddelta,  dA = sum (delta da + dbeta dbeta/dA)
+ *   dD       = sum dy . x;  dB, dC summed over the heads of each group.
+ * Tensors (shape, dtype):
+ *   x, delta, A, B, C, D, h0 : as in ssm_ssd_desc (SSM_HAS_D, SSM_HAS_H0)
+ *   dy     : (batch, seqlen, nheads, headdim) BF16, innermost stride 1
+ *   dx     : (batch, seqlen, nheads, headdim) BF16 or F32, innermost stride 1
+ *   ddelta : (batch, seqlen, nheads) F32, innermost stride 1
+ *   dA     : (nheads) F32 contiguous
+ *   dB, dC : (batch, seqlen, ngroups, dstate) F32 contiguous
+ *   dD     : (nheads) F32 contiguous                          if SSM_HAS_D
+ *   dh0    : (batch, nheads, headdim, dstate) F32 contiguous  if SSM_HAS_H0
+ * Flags: SSM_HAS_D, SSM_DISC_EULER, SSM_HAS_H0.  Supported: headdim 64,
+ * dstate 64, chunk in {64, 128, 256}, nheads % ngroups == 0.  Every (batch,
+ * step, head or group) row of x, dy, B, C and dx, and h0 / dh0, must start
+ * 16-byte aligned (SSM_ERR_ALIGN otherwise).  The sums over heads (dB, dC)
+ * and over batch and time (dA, dD) are fixed-order sums of per-workgroup
+ * partial sums, so the results are deterministic.  Outputs may not overlap
+ * inputs or each other.  Workspace: ssm_ssd_bwd_workspace_size bytes
+ * (the recomputed forward intermediates and the partial sums), 256-byte
+ * aligned. */
+typedef struct {
+  int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+  uint32_t flags;
+  ssm_tensor_desc x, delta, A, B, C, D, h0, dy;
+  ssm_tensor_desc dx, ddelta, dA, dB, dC, dD, dh0;
+} ssm_ssd_bwd_desc;
+
+typedef struct {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;   /* NULL unless SSM_HAS_D  */
+  const float* h0;  /* NULL unless SSM_HAS_H0 */
+  const void* dy;
+  void* dx;
+  float* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;        /* NULL unless SSM_HAS_D  */
+  float* dh0;       /* NULL unless SSM_HAS_H0 */
+} ssm_ssd_bwd_ptrs;
+
 /* ---------------------------------------------------------------- decode */
 
 /* One recurrent step (autoregressive decode): the recurrent mode of the
@@ -363,6 +428,13 @@ ssm_status ssm_selective_scan_bwd_workspace_size(const ssm_scan_bwd_desc* d, siz
 /* Backward of the selective scan (definition above ssm_scan_bwd_desc). */
 ssm_status ssm_selective_scan_bwd(const ssm_scan_bwd_desc* d, const ssm_scan_bwd_ptrs* p, void* workspace,
                                   size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes for ssm_ssd_bwd. */
+ssm_status ssm_ssd_bwd_workspace_size(const ssm_ssd_bwd_desc* d, size_t* bytes);
+
+/* Backward of the SSD (definition above ssm_ssd_bwd_desc). */
+ssm_status ssm_ssd_bwd(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_ptrs* p, void* workspace, size_t workspace_bytes,
+                       void* hip_stream);
 
 /* Causal depthwise convolution (+ bias, + SiLU) (definition above
  * ssm_conv_desc).  No workspace. */

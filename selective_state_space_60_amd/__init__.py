@@ -22,14 +22,15 @@ SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_STRIDE, SSM_ERR_ALIG
 SSM_F32, SSM_BF16, SSM_F16 = 0, 1, 2
 SSM_HAS_Z, SSM_HAS_D, SSM_DISC_EULER, SSM_HAS_H0, SSM_WANT_HLAST = 1, 2, 4, 8, 16
 SSM_DELTA_SOFTPLUS, SSM_HAS_DELTA_BIAS, SSM_HAS_BIAS, SSM_SILU = 32, 64, 128, 256
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_DIMS = 5
 
 # Every function include/ssm.h declares.
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_hip_error", "ssm_selective_scan_workspace_size",
            "ssm_selective_scan_fwd", "ssm_ssd_chunk_workspace_size", "ssm_ssd_chunk_fwd", "ssm_ssd_chunk_cumsum",
            "ssm_ssd_chunk_state", "ssm_ssd_state_passing", "ssm_ssd_chunk_scan", "ssm_selective_state_update",
-           "ssm_causal_conv1d_fwd", "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd")
+           "ssm_causal_conv1d_fwd", "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd",
+           "ssm_ssd_bwd_workspace_size", "ssm_ssd_bwd")
 
 
 class TensorDesc(ctypes.Structure):
@@ -43,6 +44,8 @@ _UPD_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "state", "delta_bias")
 _CONV_T = ("x", "weight", "bias", "y")
 _BWD_IN = ("x", "delta", "A", "B", "C", "D", "z", "h0", "delta_bias", "dy")
 _BWD_OUT = ("dx", "ddelta", "dz", "dA", "dB", "dC", "dD", "dh0", "ddelta_bias")
+_SSD_BWD_IN = ("x", "delta", "A", "B", "C", "D", "h0", "dy")
+_SSD_BWD_OUT = ("dx", "ddelta", "dA", "dB", "dC", "dD", "dh0")
 
 
 class ScanDesc(ctypes.Structure):
@@ -91,6 +94,17 @@ class ScanBwdPtrs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _BWD_IN + _BWD_OUT]
 
 
+class SSDBwdDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("flags", ctypes.c_uint32)] + [(n, TensorDesc) for n in
+                                                                         _SSD_BWD_IN + _SSD_BWD_OUT]
+
+
+class SSDBwdPtrs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _SSD_BWD_IN + _SSD_BWD_OUT]
+
+
 class SSMError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -127,6 +141,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_causal_conv1d_fwd.argtypes = [P(ConvDesc), P(ConvPtrs), vp]
         L.ssm_selective_scan_bwd_workspace_size.argtypes = [P(ScanBwdDesc), P(sz)]
         L.ssm_selective_scan_bwd.argtypes = [P(ScanBwdDesc), P(ScanBwdPtrs), vp, sz, vp]
+        L.ssm_ssd_bwd_workspace_size.argtypes = [P(SSDBwdDesc), P(sz)]
+        L.ssm_ssd_bwd.argtypes = [P(SSDBwdDesc), P(SSDBwdPtrs), vp, sz, vp]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = ctypes.c_int
         if L.ssm_abi_version() != ABI_VERSION:
@@ -439,4 +455,42 @@ def selective_scan_bwd(dy, x, delta, A, B, C, D=None, z=None, h0=None, euler=Fal
     ws = _workspace(n.value, dev)
     _check(lib().ssm_selective_scan_bwd(ctypes.byref(d), ctypes.byref(p), _p(ws), n.value, _stream(stream)),
            "ssm_selective_scan_bwd")
+    return {k: v for k, v in out.items() if v is not None}
+
+
+# ----------------------------------------------------------- SSD backward
+
+def ssd_bwd_desc(dy, x, delta, A, B, C, chunk, out: dict, D=None, h0=None, euler=False) -> SSDBwdDesc:
+    d = SSDBwdDesc()
+    d.batch, d.seqlen, d.nheads, d.headdim = x.shape
+    d.ngroups, d.dstate = B.shape[2], B.shape[3]
+    d.chunk = chunk
+    d.flags = (SSM_HAS_D if D is not None else 0) | (SSM_DISC_EULER if euler else 0) | \
+        (SSM_HAS_H0 if h0 is not None else 0)
+    for name, t in list(zip(_SSD_BWD_IN, (x, delta, A, B, C, D, h0, dy))) + [(k, out.get(k)) for k in _SSD_BWD_OUT]:
+        setattr(d, name, tensor_desc(t))
+    return d
+
+
+def ssd_bwd(dy, x, delta, A, B, C, chunk, D=None, h0=None, euler=False, dx_dtype=None, stream=None) -> dict:
+    """Gradients of sum(dy * y) for y = ssd_chunk_fwd(x, delta, A, B, C,
+    chunk, D, h0, euler) (see include/ssm.h).  dy (batch, L, H, P) bf16.
+
+    Returns a dict: dx (dx_dtype, default x's dtype), ddelta (batch, L, H),
+    dA (H,), dB, dC (batch, L, G, N), dD (if D), dh0 (if h0); all but dx fp32."""
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty(x.shape, dtype=dx_dtype or x.dtype, device=dev), "ddelta": f32(batch, L, H),
+           "dA": f32(H), "dB": f32(batch, L, G, N), "dC": f32(batch, L, G, N),
+           "dD": f32(H) if D is not None else None, "dh0": f32(batch, H, P, N) if h0 is not None else None}
+    d = ssd_bwd_desc(dy, x, delta, A, B, C, chunk, out, D, h0, euler)
+    p = SSDBwdPtrs()
+    for name, t in list(zip(_SSD_BWD_IN, (x, delta, A, B, C, D, h0, dy))) + [(k, out[k]) for k in _SSD_BWD_OUT]:
+        setattr(p, name, _p(t))
+    n = ctypes.c_size_t()
+    _check(lib().ssm_ssd_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)), "ssm_ssd_bwd_workspace_size")
+    ws = _workspace(n.value, dev)
+    _check(lib().ssm_ssd_bwd(ctypes.byref(d), ctypes.byref(p), _p(ws), n.value, _stream(stream)), "ssm_ssd_bwd")
     return {k: v for k, v in out.items() if v is not None}

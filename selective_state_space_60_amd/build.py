@@ -8,7 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssm.so")
-SOURCES = ["ssm_abi.cpp", "scan_fwd.hip", "scan_bwd.hip", "ssd_fwd.hip", "update_fwd.hip", "conv_fwd.hip"]
+SOURCES = ["ssm_abi.cpp", "scan_fwd.hip", "scan_bwd.hip", "ssd_fwd.hip", "ssd_bwd.hip", "update_fwd.hip",
+           "conv_fwd.hip"]
 HEADERS = ["ssm_internal.h", os.path.join("..", "..", "include", "ssm.h")]
 
 # Packed fp32 VALU ops are kept out of all device code.

@@ -707,6 +707,11 @@ void launch_io(const ScanBwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
+void launch_fixed_order_sum(const float* src, float* dst, int64_t count, int64_t parts, int64_t stride,
+                            hipStream_t stream) {
+  reduce(src, dst, count, parts, stride, stream);
+}
+
 hipError_t launch_selective_scan_bwd(const ScanBwdParams& p, hipStream_t stream) {
   if (p.io_bf16) launch_io<true>(p, stream);
   else launch_io<false>(p, stream);

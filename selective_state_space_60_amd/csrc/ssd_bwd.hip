@@ -1,0 +1,737 @@
+// Backward of the Mamba-2 SSD chunked form for gfx950 (headdim P = 64,
+// dstate N = 64).
+//
+// What is differentiated ("Mamba-2: 상태 공간 기반 시퀀스 모델",
+// obsidian-dorae222, SSD 타일링 알고리즘; the four forward steps of
+// ssd_fwd.hip).  Per (batch, chunk, head), with decay_ij = exp(A_cum_i -
+// A_cum_j) for j <= i in the chunk, w_j = exp(A_cum_end - A_cum_j), S_in the
+// state entering the chunk and dS_loc the gradient of the chunk's own state:
+//   E_ij = decay_ij beta_j (dy_i . x_j)        M_ij = decay_ij (C_i . B_j)
+//   dC_i = sum_j E_ij B_j + exp(A_cum_i) S_in^T dy_i        (added over the group's heads)
+//   R_j  = sum_i M_ij dy_i + w_j dS_loc B_j
+//   dx_j = beta_j R_j + D dy_j,        dbeta_j = x_j . R_j
+//   dB_j = sum_i E_ij C_i + w_j beta_j dS_loc^T x_j          (added over the group's heads)
+//   dA_cum_i = sum_j W_ij - sum_k W_ki + exp(A_cum_i) C_i . (S_in^T dy_i) - T_i,
+//              W = E o C B^T,  T_i = w_i beta_i x_i . (dS_loc B_i), and at the
+//              chunk end also sum_j T_j + exp(A_cum_end) <S_in, dS_in[c+1]>
+// (W's row and column sums are what the decay exponents collect; they are
+// formed from the fp32 matrix-core tiles, before any bf16 rounding, because
+// dA_cum is a small difference of large terms).  The state gradients run the
+// state passing backwards: dS_in[c] = sum_i exp(A_cum_i) dy_i C_i^T +
+// exp(A_cum_end[c]) dS_in[c+1], dS_loc[c] = dS_in[c+1], dh0 = dS_in[0].
+// Last, da = the reverse cumulative sum of dA_cum inside each chunk, and
+// through a = delta A and beta = expm1(delta A)/A (or delta):
+//   ddelta = A da + dbeta exp(delta A),   dA = sum(delta da + dbeta dbeta/dA).
+//
+// Kernels (after the forward's cumsum and chunk state are recomputed, and
+// its chunk-state kernel has formed sum_i exp(A_cum_i) dy_i C_i^T):
+//   bwd_state_kernel  : the states entering each chunk (fp32, and bf16
+//                       transposed), then the reverse recurrence.
+//   bwd_dc_kernel     : dC and W's row sums -- the forward chunk scan's
+//                       shape with x and B exchanged and dy in place of C.
+//   bwd_dx_kernel     : dx, dbeta, dB and W's column sums -- contractions over
+//                       the later steps i >= j of each column j.
+//   bwd_finish_kernel : reverse cumulative sums, ddelta, partial dA and dD.
+// A workgroup of dc and dx handles the heads of one head block in turn and
+// adds their dC or dB terms in registers; fixed-order reductions add the
+// head blocks' partial sums, so every result is deterministic.
+//
+// Matrix-core layout as in ssd_fwd.hip (v_mfma_f32_16x16x32_bf16): lane l
+// supplies A[l%16][8*(l/16) + i] and B[8*(l/16) + i][l%16] and receives
+// D[4*(l/16) + r][l%16].  A tile computed as D (4 consecutive rows per lane,
+// two tiles for 8) is used as the B operand of the next product with its
+// contraction slots permuted; the matching A operand comes from the LDS
+// transpose read, whose lane (g, m) receives rows 4g + 0..3 (and 16 + 4g +
+// 0..3) of column m.
+#include <hip/hip_runtime.h>
+
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kP = 64, kN = 64, kE = kP * kN;  // headdim, dstate, state entries
+constexpr int kPR = 64 + 4;                    // LDS row pitch (bf16) of staged rows
+constexpr int kNQ = kE / 1024;                 // 1024-entry blocks of one state
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// the 4 bf16 of a uint2, as floats
+__device__ __forceinline__ void unpack4(uint2 v, float (&o)[4]) {
+  o[0] = __uint_as_float(v.x << 16);
+  o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  o[2] = __uint_as_float(v.y << 16);
+  o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+}
+
+// Sum over the 4 rows (16-lane groups) of the wave, in every lane (gfx950
+// lane swaps: permlane32 swap of (v, v) gives v's half-waves, permlane16 swap
+// its neighbouring rows; layouts checked on the device).
+__device__ __forceinline__ float sum_rows(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float w = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t uw = __float_as_uint(w);
+  const auto b = __builtin_amdgcn_permlane16_swap(uw, uw, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// A operand of a product contracting over 32 steps s0 .. s0+31 from rows
+// staged [step][col]: row = column c0 + (lane % 16) of the tile, slots
+// 8*(lane/16) + 0..3 = steps s0 + 4*(lane/16) + 0..3 and slots + 4..7 = steps
+// s0 + 16 + 4*(lane/16) + 0..3 (the D layout of two stacked 16-row tiles).
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t (*rows)[kPR], int s0, int c0, int tr_row, int tr_col) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&rows[s0 + tr_row][c0 + tr_col]);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&rows[s0 + 16 + tr_row][c0 + tr_col]);
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  return as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+}
+
+// Block decode shared by the dc and dx kernels: (b, chunk c, group g, head
+// block hbk); heads h_lo .. h_lo + nh - 1.
+struct HeadBlock {
+  int64_t b, c, g, h_lo;
+  int hbk, nh;
+};
+
+__device__ __forceinline__ HeadBlock head_block(const SSDBwdParams& q) {
+  const SSDParams& p = q.f;
+  HeadBlock r;
+  int64_t bid = blockIdx.x;
+  r.hbk = (int)(bid % q.nhb);
+  bid /= q.nhb;
+  r.g = bid % p.G;
+  bid /= p.G;
+  r.c = bid % p.nchunks;
+  r.b = bid / p.nchunks;
+  const int64_t hpg = p.H / p.G;
+  r.h_lo = r.g * hpg + (int64_t)r.hbk * q.HB;
+  const int64_t left = hpg - (int64_t)r.hbk * q.HB;
+  r.nh = (int)(left < q.HB ? left : q.HB);
+  return r;
+}
+
+// Stage Q rows of 64 bf16 (zero rows at or past L) into rows[Q][kPR].
+template <int Q, int NTH>
+__device__ __forceinline__ void stage_rows(uint16_t (*rows)[kPR], const uint16_t* src, int64_t st, int64_t t0,
+                                           int64_t L) {
+  constexpr int NTX = Q * 8 / NTH;
+  uint4 v[NTX];
+#pragma unroll
+  for (int u = 0; u < NTX; ++u) {
+    const int task = threadIdx.x + NTH * u;
+    const int j = task / 8, cb = (task % 8) * 8;
+    const int64_t tr = t0 + j < L ? t0 + j : L - 1;
+    v[u] = *(const uint4*)(src + tr * st + cb);
+  }
+#pragma unroll
+  for (int u = 0; u < NTX; ++u) {
+    const int task = threadIdx.x + NTH * u;
+    const int j = task / 8, cb = (task % 8) * 8;
+    *(uint4*)&rows[j][cb] = t0 + j < L ? v[u] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// 8 bf16 of row t (zero at or past L): columns c0 .. c0+7
+__device__ __forceinline__ bf16x8 row8(const uint16_t* src, int64_t st, int64_t t, int64_t L, int c0) {
+  const int64_t tr = t < L ? t : L - 1;
+  const uint4 v = *(const uint4*)(src + tr * st + c0);
+  return as_bf16x8(t < L ? v : make_uint4(0, 0, 0, 0));
+}
+
+// 4 bf16 of row t (zero at or past L): columns c0 .. c0+3
+__device__ __forceinline__ uint2 row4(const uint16_t* src, int64_t st, int64_t t, int64_t L, int c0) {
+  const int64_t tr = t < L ? t : L - 1;
+  const uint2 v = *(const uint2*)(src + tr * st + c0);
+  return t < L ? v : make_uint2(0, 0);
+}
+
+// ------------------------------------------------- reverse state passing
+
+// Block = (b, h, 1024 of the 4096 state entries); 4 entries (row p, columns
+// n0 .. n0+3) per thread.  Forward: S_in[c] in fp32 and bf16 transposed.
+// Backward: G = 0; for c = last .. 0: dS_loc[c] = G (bf16, both layouts),
+// partial <S_in[c], G> exp(A_cum_end[c]); G = dS[c] + exp(A_cum_end[c]) G.
+__global__ __launch_bounds__(256) void bwd_state_kernel(SSDBwdParams q) {
+  const SSDParams& p = q.f;
+  __shared__ float red[4];
+  int64_t bid = blockIdx.x;
+  const int qb = (int)(bid % kNQ);
+  bid /= kNQ;
+  const int64_t h = bid % p.H, b = bid / p.H;
+  const int tid = threadIdx.x;
+  const int e0 = qb * 1024 + tid * 4;
+  const int pr = e0 / kN, n0 = e0 % kN;
+  const float* Ac = p.A_cum + (b * p.H + h) * p.Lp;
+  const int64_t cs = p.H * kE;
+  const int64_t base = (b * p.nchunks * p.H + h) * kE;
+  float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (p.h0) S = *(const float4*)(p.h0 + (b * p.H + h) * kE + e0);
+  for (int64_t c = 0; c < p.nchunks; ++c) {
+    const int64_t o = base + c * cs;
+    *(float4*)(q.S32 + o + e0) = S;
+    uint16_t* t = q.SinT + o + pr;
+    t[(n0 + 0) * kP] = f2bf(S.x);
+    t[(n0 + 1) * kP] = f2bf(S.y);
+    t[(n0 + 2) * kP] = f2bf(S.z);
+    t[(n0 + 3) * kP] = f2bf(S.w);
+    const float dec = __builtin_amdgcn_exp2f(Ac[c * p.Q + p.Q - 1] * kLog2e);
+    const float4 sl = *(const float4*)(p.states + o + e0);
+    S.x = __builtin_fmaf(dec, S.x, sl.x);
+    S.y = __builtin_fmaf(dec, S.y, sl.y);
+    S.z = __builtin_fmaf(dec, S.z, sl.z);
+    S.w = __builtin_fmaf(dec, S.w, sl.w);
+  }
+  float4 G = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t c = p.nchunks - 1; c >= 0; --c) {
+    const int64_t o = base + c * cs;
+    *(uint2*)(q.dSl + o + e0) = make_uint2(pack2(G.x, G.y), pack2(G.z, G.w));
+    uint16_t* t = q.dSlT + o + pr;
+    t[(n0 + 0) * kP] = f2bf(G.x);
+    t[(n0 + 1) * kP] = f2bf(G.y);
+    t[(n0 + 2) * kP] = f2bf(G.z);
+    t[(n0 + 3) * kP] = f2bf(G.w);
+    const float4 sc = *(const float4*)(q.S32 + o + e0);
+    float dot = sc.x * G.x + sc.y * G.y + sc.z * G.z + sc.w * G.w;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
+    if (tid % 64 == 0) red[tid / 64] = dot;
+    __syncthreads();
+    const float dec = __builtin_amdgcn_exp2f(Ac[c * p.Q + p.Q - 1] * kLog2e);
+    if (tid == 0) q.pAend[((b * p.H + h) * p.nchunks + c) * kNQ + qb] = dec * (((red[0] + red[1]) + red[2]) + red[3]);
+    __syncthreads();
+    const float4 d = *(const float4*)(q.dS + o + e0);
+    G.x = __builtin_fmaf(dec, G.x, d.x);
+    G.y = __builtin_fmaf(dec, G.y, d.y);
+    G.z = __builtin_fmaf(dec, G.z, d.z);
+    G.w = __builtin_fmaf(dec, G.w, d.w);
+  }
+  if (q.dh0) *(float4*)(q.dh0 + (b * p.H + h) * kE + e0) = G;
+}
+
+// -------------------------------------------------------------- dC pass
+
+// Block = (b, chunk, group, head block), Q/32 waves; wave wv owns the two
+// 16-row strips (rows i) wv and Q/16 - 1 - wv.  Accumulators hold dC^T[n][i]:
+// lane -> n = 16*nt + 4*(l/16) + r, i = 16*strip + l%16.  Per head:
+//   G'^T[j][i] = sum_p x_j[p] dy_i[p]   (A: staged x rows, B: the strip's dy rows)
+//   E^T = G'^T decay_ij beta_j  -> B operand;   dC^T += B^T E^T  (A: transposed B rows)
+//   dC^T[n][i] += exp(A_cum_i) sum_p S_in[p][n] dy_i[p]   (A: S_in^T rows)
+template <int Q>
+__global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
+  constexpr int NTH = 2 * Q, NSTRIP = Q / 16;
+  const SSDParams& p = q.f;
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][kPR];  // x rows of the head: [j][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][kPR];  // B rows of the group: [j][n]
+  __shared__ __attribute__((aligned(16))) float A2[Q];  // A_cum * log2(e)
+  __shared__ __attribute__((aligned(16))) float bj[Q];  // beta
+  __shared__ __attribute__((aligned(16))) float tb[Q];  // exp(A_cum[j|31] - A_cum[j]) beta_j
+  const HeadBlock hb = head_block(q);
+  const int64_t b = hb.b, c = hb.c, g = hb.g;
+  const int tid = threadIdx.x;
+  const int64_t t0 = c * Q;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64), l = tid % 64, lr = l % 16, lq = l / 16;
+  const int kst[2] = {wv, NSTRIP - 1 - wv};
+  const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
+
+  stage_rows<Q, NTH>(Bs, (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g, p.Bs_t, t0, p.L);
+  const uint16_t* Csrc = (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g;
+  bf16x8 cop[2][2];  // B operands: C[i][32*ks + 8*lq .. +7] of the strip's rows
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) cop[s][ks] = row8(Csrc, p.Cs_t, t0 + 16 * kst[s] + lr, p.L, 32 * ks + 8 * lq);
+  f32x4 sum[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) sum[s][nt] = zero4();
+
+  for (int k = 0; k < hb.nh; ++k) {
+    const int64_t h = hb.h_lo + k;
+    const uint16_t* Ysrc = (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h;
+    bf16x8 yop[2][2];  // B operands: dy[i][32*ks + 8*lq .. +7] of the strip's rows
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) yop[s][ks] = row8(Ysrc, q.dys_t, t0 + 16 * kst[s] + lr, p.L, 32 * ks + 8 * lq);
+    const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
+    const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
+    __syncthreads();  // the previous head is done with Xs, A2, bj, tb
+    stage_rows<Q, NTH>(Xs, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
+    for (int t = tid; t < Q; t += NTH) {
+      A2[t] = Ac[t] * kLog2e;
+      bj[t] = be[t];
+    }
+    __syncthreads();
+    for (int t = tid; t < Q; t += NTH) tb[t] = __builtin_amdgcn_exp2f(A2[t | 31] - A2[t]) * bj[t];
+    __syncthreads();
+
+    f32x4 acc[2][4];
+    float rsum[2] = {0.f, 0.f};  // this lane's part of W's row sum
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[s][nt] = zero4();
+    const int jb_last = (16 * kst[1]) / 32;
+    for (int jb = 0; jb <= jb_last; ++jb) {
+      const int j0 = 32 * jb;
+      bf16x8 aB[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) aB[nt] = tr_operand(Bs, j0, 16 * nt, tr_row, tr_col);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int i0 = 16 * kst[s];
+        const int diag = i0 / 32;
+        if (jb > diag) continue;  // wave-uniform
+        const int i = i0 + lr;
+        f32x4 gt[2], cbt[2];
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          f32x4 a = zero4(), cb = zero4();
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            a = mfma(as_bf16x8(*(const uint4*)&Xs[j0 + 16 * jt + lr][32 * ks + 8 * lq]), yop[s][ks], a);
+            cb = mfma(as_bf16x8(*(const uint4*)&Bs[j0 + 16 * jt + lr][32 * ks + 8 * lq]), cop[s][ks], cb);
+          }
+          gt[jt] = a;    // G'^T[j0 + 16*jt + 4*lq + r][i]
+          cbt[jt] = cb;  // (C B^T)^T[j0 + 16*jt + 4*lq + r][i]
+        }
+        float v[8];
+        if (jb < diag) {
+          // exp(A_i - A_j) = exp(A_i - A_m) exp(A_m - A_j), m = j0 + 31
+          const float vi = __builtin_amdgcn_exp2f(A2[i] - A2[j0 + 31]);
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const float4 t4 = *(const float4*)&tb[j0 + 16 * jt + 4 * lq];
+            v[4 * jt + 0] = gt[jt][0] * (t4.x * vi);
+            v[4 * jt + 1] = gt[jt][1] * (t4.y * vi);
+            v[4 * jt + 2] = gt[jt][2] * (t4.z * vi);
+            v[4 * jt + 3] = gt[jt][3] * (t4.w * vi);
+          }
+        } else {
+          const float ai = A2[i];
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const float4 a4 = *(const float4*)&A2[j0 + 16 * jt + 4 * lq];
+            const float4 b4 = *(const float4*)&bj[j0 + 16 * jt + 4 * lq];
+            const float aj[4] = {a4.x, a4.y, a4.z, a4.w};
+            const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = j0 + 16 * jt + 4 * lq + r;
+              const float d = j <= i ? ai - aj[r] : 0.f;
+              const float e = __builtin_amdgcn_exp2f(d);
+              v[4 * jt + r] = j <= i ? gt[jt][r] * (e * bb[r]) : 0.f;
+            }
+          }
+        }
+        const bf16x8 eop = as_bf16x8(make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]),
+                                                pack2(v[6], v[7])));
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[s][nt] = mfma(aB[nt], eop, acc[s][nt]);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) rsum[s] = __builtin_fmaf(v[4 * jt + r], cbt[jt][r], rsum[s]);
+      }
+    }
+    // inter-chunk term; W's row sum and C_i . (inter-chunk dC_i) of this head
+    const uint16_t* Sp = q.SinT + ((b * p.nchunks + c) * p.H + h) * kE;
+    bf16x8 sop[4][2];  // A operands: S_in^T[16*nt + lr][32*ks + 8*lq .. +7]
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) sop[nt][ks] = as_bf16x8(*(const uint4*)(Sp + (16 * nt + lr) * kP + 32 * ks + 8 * lq));
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int il = 16 * kst[s] + lr;
+      const float ei = __builtin_amdgcn_exp2f(A2[il]);
+      float dot = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        f32x4 a = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) a = mfma(sop[nt][ks], yop[s][ks], a);
+        a *= ei;
+        float cv[4];
+        unpack4(row4(Csrc, p.Cs_t, t0 + il, p.L, 16 * nt + 4 * lq), cv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dot = __builtin_fmaf(cv[r], a[r], dot);
+        sum[s][nt] += acc[s][nt] + a;
+      }
+      const float v = sum_rows(dot + rsum[s]);
+      if (lq == 0) q.dAcA[(b * p.H + h) * p.Lp + t0 + il] = v;
+    }
+  }
+  // the head block's dC terms
+  float* dst = q.pdC + ((int64_t)hb.hbk * p.batch + b) * p.L * p.G * kN;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int64_t ti = t0 + 16 * kst[s] + lr;
+    if (ti < p.L)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) *(f32x4*)(dst + (ti * p.G + g) * kN + 16 * nt + 4 * lq) = sum[s][nt];
+  }
+}
+
+// -------------------------------------------------------------- dx pass
+
+// Block as bwd_dc_kernel; strips are now 16 columns j.  Accumulators:
+// RX^T[p][j] (-> R_j) and DB^T[n][j] (-> dB_j), lane -> p or n = 16*t +
+// 4*(l/16) + r, j = 16*strip + l%16.  Per head:
+//   RX^T = w_j dS_loc B_j, DB^T = w_j beta_j dS_loc^T x_j   (A: dS_loc rows / dS_loc^T rows)
+//   for 32-row blocks of i >= j:  CB[i][j], G'[i][j] = dy_i . x_j  (A: staged C / dy rows)
+//     M = CB decay_ij, E = G' decay_ij beta_j -> B operands
+//     RX^T += dy^T M,  DB^T += C^T E   (A: transposed dy / C rows)
+template <int Q>
+__global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
+  constexpr int NTH = 2 * Q, NSTRIP = Q / 16, NIB = Q / 32;
+  const SSDParams& p = q.f;
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[Q][kPR];  // C rows of the group: [i][n]
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[Q][kPR];  // dy rows of the head: [i][p]
+  __shared__ __attribute__((aligned(16))) float A2[Q];
+  __shared__ __attribute__((aligned(16))) float bj[Q];
+  const HeadBlock hb = head_block(q);
+  const int64_t b = hb.b, c = hb.c, g = hb.g;
+  const int tid = threadIdx.x;
+  const int64_t t0 = c * Q;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64), l = tid % 64, lr = l % 16, lq = l / 16;
+  const int kst[2] = {wv, NSTRIP - 1 - wv};
+  const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
+
+  stage_rows<Q, NTH>(Cs, (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g, p.Cs_t, t0, p.L);
+  const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
+  bf16x8 bop[2][2];  // B operands: B[j][32*ks + 8*lq .. +7] of the strip's columns
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) bop[s][ks] = row8(Bsrc, p.Bs_t, t0 + 16 * kst[s] + lr, p.L, 32 * ks + 8 * lq);
+  f32x4 sumB[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) sumB[s][nt] = zero4();
+  const float Dh = p.Dskip ? 1.f : 0.f;  // scaled per head below
+
+  for (int k = 0; k < hb.nh; ++k) {
+    const int64_t h = hb.h_lo + k;
+    const uint16_t* Xsrc = (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h;
+    bf16x8 xop[2][2];  // B operands: x[j][32*ks + 8*lq .. +7]
+    uint2 xE[2][4];    // x[j][16*pt + 4*lq .. +3] for the epilogue
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int64_t tj = t0 + 16 * kst[s] + lr;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) xop[s][ks] = row8(Xsrc, p.xs_t, tj, p.L, 32 * ks + 8 * lq);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) xE[s][pt] = row4(Xsrc, p.xs_t, tj, p.L, 16 * pt + 4 * lq);
+    }
+    const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
+    const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
+    __syncthreads();  // the previous head is done with Ys, A2, bj
+    stage_rows<Q, NTH>(Ys, (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h, q.dys_t, t0, p.L);
+    for (int t = tid; t < Q; t += NTH) {
+      A2[t] = Ac[t] * kLog2e;
+      bj[t] = be[t];
+    }
+    __syncthreads();
+
+    // chunk-state terms
+    f32x4 accX[2][4], accB[2][4];
+    float tj_val[2];
+    float csum[2] = {0.f, 0.f};  // this lane's part of W's column sum
+    {
+      const int64_t so = ((b * p.nchunks + c) * p.H + h) * kE;
+      bf16x8 dsl[4][2], dslT[4][2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dsl[t][ks] = as_bf16x8(*(const uint4*)(q.dSl + so + (16 * t + lr) * kN + 32 * ks + 8 * lq));
+          dslT[t][ks] = as_bf16x8(*(const uint4*)(q.dSlT + so + (16 * t + lr) * kP + 32 * ks + 8 * lq));
+        }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int jl = 16 * kst[s] + lr;
+        const float w = __builtin_amdgcn_exp2f(A2[Q - 1] - A2[jl]);
+        const float wb = w * bj[jl];
+        float tp = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          f32x4 a = zero4();
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) a = mfma(dsl[pt][ks], bop[s][ks], a);  // (dS_loc B_j)[p]
+          float xv[4];
+          unpack4(xE[s][pt], xv);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tp = __builtin_fmaf(xv[r], a[r], tp);
+          accX[s][pt] = a * w;
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          f32x4 a = zero4();
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) a = mfma(dslT[nt][ks], xop[s][ks], a);  // (dS_loc^T x_j)[n]
+          accB[s][nt] = a * wb;
+        }
+        tj_val[s] = sum_rows(tp) * wb;
+      }
+    }
+
+    // intra-chunk terms over the blocks of i at or after the strip
+    for (int ib = (16 * kst[0]) / 32; ib < NIB; ++ib) {
+      const int i0 = 32 * ib;
+      bf16x8 aY[4], aC[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        aY[t] = tr_operand(Ys, i0, 16 * t, tr_row, tr_col);
+        aC[t] = tr_operand(Cs, i0, 16 * t, tr_row, tr_col);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int jl = 16 * kst[s] + lr;
+        const int diag = (16 * kst[s]) / 32;
+        if (ib < diag) continue;  // wave-uniform
+        f32x4 ct[2], gt[2];
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          f32x4 a = zero4(), d = zero4();
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            a = mfma(as_bf16x8(*(const uint4*)&Cs[i0 + 16 * it + lr][32 * ks + 8 * lq]), bop[s][ks], a);
+            d = mfma(as_bf16x8(*(const uint4*)&Ys[i0 + 16 * it + lr][32 * ks + 8 * lq]), xop[s][ks], d);
+          }
+          ct[it] = a;  // CB[i0 + 16*it + 4*lq + r][j]
+          gt[it] = d;  // G'[i0 + 16*it + 4*lq + r][j]
+        }
+        const float aj = A2[jl], bjj = bj[jl];
+        float m[8], e[8];
+        float w_col = 0.f;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const float4 a4 = *(const float4*)&A2[i0 + 16 * it + 4 * lq];
+          const float ai[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 16 * it + 4 * lq + r;
+            const bool ok = ib > diag || i >= jl;
+            const float f = __builtin_amdgcn_exp2f(ok ? ai[r] - aj : 0.f);
+            m[4 * it + r] = ok ? ct[it][r] * f : 0.f;
+            e[4 * it + r] = ok ? gt[it][r] * (f * bjj) : 0.f;
+            w_col = __builtin_fmaf(e[4 * it + r], ct[it][r], w_col);
+          }
+        }
+        csum[s] += w_col;
+        const bf16x8 mop = as_bf16x8(make_uint4(pack2(m[0], m[1]), pack2(m[2], m[3]), pack2(m[4], m[5]),
+                                                pack2(m[6], m[7])));
+        const bf16x8 eop = as_bf16x8(make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]),
+                                                pack2(e[6], e[7])));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          accX[s][t] = mfma(aY[t], mop, accX[s][t]);
+          accB[s][t] = mfma(aC[t], eop, accB[s][t]);
+        }
+      }
+    }
+
+    // dx, dbeta, dy . x; dB terms
+    const float Dk = Dh != 0.f ? p.Dskip[h * p.Ds_h] : 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int jl = 16 * kst[s] + lr;
+      const int64_t tj = t0 + jl;
+      const float bjj = bj[jl];
+      float db = 0.f, dd = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        float xv[4], yv[4], o[4];
+        unpack4(xE[s][pt], xv);
+        unpack4(*(const uint2*)&Ys[jl][16 * pt + 4 * lq], yv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          db = __builtin_fmaf(xv[r], accX[s][pt][r], db);
+          dd = __builtin_fmaf(xv[r], yv[r], dd);
+          o[r] = __builtin_fmaf(bjj, accX[s][pt][r], Dk * yv[r]);
+        }
+        if (tj < p.L) {
+          const int64_t off = b * q.dxs_b + tj * q.dxs_t + h * q.dxs_h + 16 * pt + 4 * lq;
+          if (q.dx_f32) *(float4*)((float*)q.dx + off) = make_float4(o[0], o[1], o[2], o[3]);
+          else *(uint2*)((uint16_t*)q.dx + off) = make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+        }
+      }
+      db = sum_rows(db);
+      dd = sum_rows(dd);
+      const float wc = sum_rows(csum[s]);
+      if (lq == 0) {
+        const int64_t o = (b * p.H + h) * p.Lp + tj;
+        q.dbeta[o] = db;
+        q.Tj[o] = tj_val[s];
+        q.dDj[o] = dd;
+        q.dAcB[o] = -wc - tj_val[s];
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) sumB[s][nt] += accB[s][nt];
+    }
+  }
+  // the head block's dB terms
+  float* dst = q.pdB + ((int64_t)hb.hbk * p.batch + b) * p.L * p.G * kN;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int64_t tj = t0 + 16 * kst[s] + lr;
+    if (tj < p.L)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) *(f32x4*)(dst + (tj * p.G + g) * kN + 16 * nt + 4 * lq) = sumB[s][nt];
+  }
+}
+
+// ----------------------------------------------------------------- finish
+
+// dbeta/dA of beta = expm1(a)/A, a = delta A: delta^2 phi'(a) with
+// phi(a) = expm1(a)/a, phi'(a) = sum_k k a^(k-1)/(k+1)! (series for |a| < 1/4,
+// truncation < 1e-10 relative; (delta e^a - beta)/A elsewhere).
+__device__ __forceinline__ float dbeta_dA(float delta, float A, float a, float ea, float beta) {
+  if (fabsf(a) >= 0.25f) return (delta * ea - beta) / A;
+  float s = 1.f / 45360.f;
+  s = __builtin_fmaf(s, a, 1.f / 5760.f);
+  s = __builtin_fmaf(s, a, 1.f / 840.f);
+  s = __builtin_fmaf(s, a, 1.f / 144.f);
+  s = __builtin_fmaf(s, a, 1.f / 30.f);
+  s = __builtin_fmaf(s, a, 1.f / 8.f);
+  s = __builtin_fmaf(s, a, 1.f / 3.f);
+  s = __builtin_fmaf(s, a, 0.5f);
+  return delta * delta * s;
+}
+
+// Sum over the block (Q threads) in a fixed order, returned in every thread.
+template <int Q>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  __syncthreads();
+  if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < Q / 64; ++w) t += red[w];
+  return t;
+}
+
+// Block = (b, h, chunk), one thread per step of the chunk.
+template <int Q>
+__global__ __launch_bounds__(Q) void bwd_finish_kernel(SSDBwdParams q) {
+  const SSDParams& p = q.f;
+  __shared__ float sc[2][Q];
+  __shared__ float red[Q / 64];
+  int64_t bid = blockIdx.x;
+  const int64_t c = bid % p.nchunks;
+  bid /= p.nchunks;
+  const int64_t h = bid % p.H, b = bid / p.H;
+  const int t = threadIdx.x;
+  const int64_t t0 = c * Q, tg = t0 + t;
+  const bool ok = tg < p.L;
+  const int64_t o = (b * p.H + h) * p.Lp + tg;
+  const float beta = p.beta[o], dbt = q.dbeta[o];
+  float v = q.dAcA[o] + q.dAcB[o];
+  const float tsum = block_sum<Q>(q.Tj[o], red);
+  if (t == Q - 1) {
+    const float* pa = q.pAend + ((b * p.H + h) * p.nchunks + c) * kNQ;
+    float e = 0.f;
+#pragma unroll
+    for (int k = 0; k < kNQ; ++k) e += pa[k];
+    v += tsum + e;
+  }
+  // da_t = sum of v over the steps t .. Q-1 of the chunk (Hillis-Steele, two buffers)
+  int cur = 0;
+  sc[0][t] = v;
+  __syncthreads();
+  for (int off = 1; off < Q; off <<= 1) {
+    const float nv = sc[cur][t] + (t + off < Q ? sc[cur][t + off] : 0.f);
+    sc[cur ^ 1][t] = nv;
+    cur ^= 1;
+    __syncthreads();
+  }
+  const float da = sc[cur][t];
+  const float A = p.A[h * p.As_h];
+  float dAp = 0.f, dDp = 0.f;
+  if (ok) {
+    const float delta = bf2f(((const uint16_t*)p.delta)[b * p.ds_b + tg * p.ds_t + h * p.ds_h]);
+    float dd;
+    if (p.euler) {
+      dd = __builtin_fmaf(A, da, dbt);
+      dAp = delta * da;
+    } else {
+      const float a = delta * A;
+      const float ea = __builtin_amdgcn_exp2f(a * kLog2e);
+      dd = __builtin_fmaf(A, da, dbt * ea);
+      dAp = __builtin_fmaf(delta, da, dbt * dbeta_dA(delta, A, a, ea, beta));
+    }
+    q.ddelta[b * q.dds_b + tg * q.dds_t + h * q.dds_h] = dd;
+    dDp = q.dDj[o];
+  }
+  const float sA = block_sum<Q>(dAp, red);
+  const float sD = block_sum<Q>(dDp, red);
+  if (t == 0) {
+    q.pA[(b * p.nchunks + c) * p.H + h] = sA;
+    q.pD[(b * p.nchunks + c) * p.H + h] = sD;
+  }
+}
+
+template <int Q>
+void launch_q(const SSDBwdParams& q, hipStream_t stream) {
+  const SSDParams& p = q.f;
+  const unsigned nb = (unsigned)(p.batch * p.nchunks * p.G * q.nhb);
+  hipLaunchKernelGGL(bwd_dc_kernel<Q>, dim3(nb), dim3(2 * Q), 0, stream, q);
+  hipLaunchKernelGGL(bwd_dx_kernel<Q>, dim3(nb), dim3(2 * Q), 0, stream, q);
+  hipLaunchKernelGGL(bwd_finish_kernel<Q>, dim3((unsigned)(p.batch * p.H * p.nchunks)), dim3(Q), 0, stream, q);
+}
+
+}  // namespace
+
+hipError_t launch_ssd_bwd(const SSDBwdParams& q, float* dA, float* dB, float* dC, float* dD, hipStream_t stream) {
+  const SSDParams& p = q.f;
+  hipError_t e;
+  // recompute the forward's A_cum, beta and chunk states
+  if ((e = launch_ssd_chunk_cumsum(p, stream)) != hipSuccess) return e;
+  if ((e = launch_ssd_chunk_state(p, stream)) != hipSuccess) return e;
+  // sum_i exp(A_cum_i) dy_i C_i^T: the chunk-state product with dy for x, C for B
+  SSDParams f2 = p;
+  f2.x = q.dy;
+  f2.xs_b = q.dys_b;
+  f2.xs_t = q.dys_t;
+  f2.xs_h = q.dys_h;
+  f2.B = p.C;
+  f2.Bs_b = p.Cs_b;
+  f2.Bs_t = p.Cs_t;
+  f2.Bs_g = p.Cs_g;
+  f2.states = q.dS;
+  f2.state_coef = 1;
+  if ((e = launch_ssd_chunk_state(f2, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_state_kernel, dim3((unsigned)(p.batch * p.H * kNQ)), dim3(256), 0, stream, q);
+  if (p.Q == 64) launch_q<64>(q, stream);
+  else if (p.Q == 128) launch_q<128>(q, stream);
+  else launch_q<256>(q, stream);
+  const int64_t blgn = p.batch * p.L * p.G * kN;
+  launch_fixed_order_sum(q.pdB, dB, blgn, q.nhb, blgn, stream);
+  launch_fixed_order_sum(q.pdC, dC, blgn, q.nhb, blgn, stream);
+  launch_fixed_order_sum(q.pA, dA, p.H, p.batch * p.nchunks, p.H, stream);
+  if (dD) launch_fixed_order_sum(q.pD, dD, p.H, p.batch * p.nchunks, p.H, stream);
+  return hipGetLastError();
+}
+
+}  // namespace ssm

@@ -171,7 +171,8 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t (*rows)[PR], int j0,
 // S_loc[p][n] = sum_j (w_j x_j[p]) B_j[n], w_j = exp(A_cum_end - A_cum_j)
 // beta_j: x rows are staged scaled by w_j, the block's 64 columns of the B
 // rows as they are; wave wv computes p-tile wv % 4 times n-tiles 2*(wv/4) and
-// +1, contracting over the Q steps in slices of 32.
+// +1, contracting over the Q steps in slices of 32.  With state_coef = 1 the
+// weights are w_j = exp(A_cum_j) (the backward passes dy for x and C for B).
 template <int Q, int NB>
 __global__ __launch_bounds__(512) void chunk_state_kernel(SSDParams p) {
   constexpr int NTH = 512;
@@ -203,7 +204,11 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(SSDParams p) {
   const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
   const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
   const float a_end = Ac[Q - 1];
-  for (int t = tid; t < Q; t += NTH) w[t] = __builtin_amdgcn_exp2f((a_end - Ac[t]) * kLog2e) * be[t];
+  if (p.state_coef == 0) {
+    for (int t = tid; t < Q; t += NTH) w[t] = __builtin_amdgcn_exp2f((a_end - Ac[t]) * kLog2e) * be[t];
+  } else {
+    for (int t = tid; t < Q; t += NTH) w[t] = __builtin_amdgcn_exp2f(Ac[t] * kLog2e);
+  }
   __syncthreads();
   // rows at or past L hold zeros (as data, not through w: 0 * inf)
 #pragma unroll

@@ -318,6 +318,112 @@ ssm::SSDParams make_ssd_params(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, con
   return q;
 }
 
+// ---------------------------------------------------------- SSD backward
+
+constexpr uint32_t kSSDBwdFlags = SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0;
+
+struct SSDBwdPlan {
+  SSDPlan f;
+  int HB = 1, nhb = 1;
+  int64_t ws_state = 0, ws_half = 0, ws_aend = 0, ws_step = 0, ws_part = 0, ws_pdb = 0, ws_total = 0;
+};
+
+// The forward problem of a backward descriptor (dx stands in for y: both are
+// (batch, seqlen, nheads, headdim) BF16 or F32 with unit innermost stride).
+ssm_ssd_desc ssd_fwd_of(const ssm_ssd_bwd_desc& d) {
+  ssm_ssd_desc f;
+  std::memset(&f, 0, sizeof(f));
+  f.batch = d.batch; f.seqlen = d.seqlen; f.nheads = d.nheads; f.headdim = d.headdim; f.dstate = d.dstate;
+  f.ngroups = d.ngroups; f.chunk = d.chunk; f.flags = d.flags;
+  f.x = d.x; f.delta = d.delta; f.A = d.A; f.B = d.B; f.C = d.C; f.D = d.D; f.y = d.dx; f.h0 = d.h0;
+  return f;
+}
+
+SSDBwdPlan plan_ssd_bwd(const ssm_ssd_bwd_desc& d) {
+  SSDBwdPlan pl;
+  const ssm_ssd_desc f = ssd_fwd_of(d);
+  pl.f = plan_ssd(f);
+  const int64_t nc = pl.f.nchunks, hpg = d.nheads / d.ngroups;
+  // heads per workgroup of the dC / dx passes: enough workgroups to fill the
+  // chip (about 4 per compute unit), as few partial sums of dB, dC as that allows
+  const int64_t units = d.batch * nc * d.nheads;
+  pl.HB = (int)std::max<int64_t>(1, std::min<int64_t>({8, hpg, units / 1024}));
+  pl.nhb = (int)((hpg + pl.HB - 1) / pl.HB);
+  const int64_t E = d.batch * nc * d.nheads * d.headdim * d.dstate;
+  pl.ws_state = round256(E * 4);
+  pl.ws_half = round256(E * 2);
+  pl.ws_aend = round256(d.batch * d.nheads * nc * (d.headdim * d.dstate / 1024) * 4);
+  pl.ws_step = round256(d.batch * d.nheads * pl.f.Lp * 4);
+  pl.ws_part = round256(d.batch * nc * d.nheads * 4);
+  pl.ws_pdb = round256((int64_t)pl.nhb * d.batch * d.seqlen * d.ngroups * d.dstate * 4);
+  // A_cum, beta | states, dS, S32 | SinT, dSl, dSlT | pAend | dAcA, dAcB, dbeta, Tj, dDj | pA, pD | pdB, pdC
+  pl.ws_total = pl.f.ws_acum + pl.f.ws_beta + 3 * pl.ws_state + 3 * pl.ws_half + pl.ws_aend + 5 * pl.ws_step +
+                2 * pl.ws_part + 2 * pl.ws_pdb;
+  return pl;
+}
+
+ssm_status validate_ssd_bwd_desc(const ssm_ssd_bwd_desc* d) {
+  if (!d) return SSM_ERR_NULL;
+  if (d->flags & ~kSSDBwdFlags) return SSM_ERR_UNSUPPORTED;
+  const ssm_ssd_desc f = ssd_fwd_of(*d);
+  ssm_status s = validate_ssd_desc(&f);
+  if (s) return s;
+  if (d->dstate != 64) return SSM_ERR_UNSUPPORTED;
+  const int64_t blhp[4] = {d->batch, d->seqlen, d->nheads, d->headdim};
+  const int64_t blh[3] = {d->batch, d->seqlen, d->nheads};
+  const int64_t blgn[4] = {d->batch, d->seqlen, d->ngroups, d->dstate};
+  const int64_t h1[1] = {d->nheads};
+  const int64_t bhpn[4] = {d->batch, d->nheads, d->headdim, d->dstate};
+  if ((s = check_tensor(d->dy, 4, blhp, d->dy.dtype == SSM_BF16, true, false))) return s;
+  if ((s = check_tensor(d->ddelta, 3, blh, d->ddelta.dtype == SSM_F32, true, false))) return s;
+  if (!non_overlapping(d->ddelta)) return SSM_ERR_STRIDE;
+  if ((s = check_tensor(d->dA, 1, h1, d->dA.dtype == SSM_F32, false, true))) return s;
+  if ((s = check_tensor(d->dB, 4, blgn, d->dB.dtype == SSM_F32, false, true))) return s;
+  if ((s = check_tensor(d->dC, 4, blgn, d->dC.dtype == SSM_F32, false, true))) return s;
+  if (d->flags & SSM_HAS_D)
+    if ((s = check_tensor(d->dD, 1, h1, d->dD.dtype == SSM_F32, false, true))) return s;
+  if (d->flags & SSM_HAS_H0)
+    if ((s = check_tensor(d->dh0, 4, bhpn, d->dh0.dtype == SSM_F32, false, true))) return s;
+  const SSDBwdPlan pl = plan_ssd_bwd(*d);
+  if (d->batch * pl.f.nchunks * d->ngroups * pl.nhb >= ((int64_t)1 << 31) ||
+      d->batch * d->nheads * pl.f.nchunks * 4 >= ((int64_t)1 << 31))
+    return SSM_ERR_UNSUPPORTED;
+  return SSM_OK;
+}
+
+ssm_status validate_ssd_bwd_ptrs(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_ptrs* p) {
+  if (!p) return SSM_ERR_NULL;
+  const uint32_t f = d->flags;
+  if (!p->x || !p->delta || !p->A || !p->B || !p->C || !p->dy || !p->dx || !p->ddelta || !p->dA || !p->dB ||
+      !p->dC)
+    return SSM_ERR_NULL;
+  if ((f & SSM_HAS_D) && (!p->D || !p->dD)) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_H0) && (!p->h0 || !p->dh0)) return SSM_ERR_NULL;
+  if (!aligned(p->delta, 2) || !aligned(p->A, 4) || !aligned(p->ddelta, 4) || !aligned(p->dA, 4) ||
+      !aligned(p->dB, 4) || !aligned(p->dC, 4) || (p->D && !aligned(p->D, 4)) || (p->dD && !aligned(p->dD, 4)))
+    return SSM_ERR_ALIGN;
+  if (!rows_aligned16(d->x, p->x, 3) || !rows_aligned16(d->dy, p->dy, 3) || !rows_aligned16(d->B, p->B, 3) ||
+      !rows_aligned16(d->C, p->C, 3) || !rows_aligned16(d->dx, p->dx, 3) ||
+      ((f & SSM_HAS_H0) && (!aligned(p->h0, 16) || !aligned(p->dh0, 16))))
+    return SSM_ERR_ALIGN;
+  const Span ins[] = {span_of(d->x, p->x),  span_of(d->delta, p->delta), span_of(d->A, p->A),
+                      span_of(d->B, p->B),  span_of(d->C, p->C),         span_of(d->dy, p->dy),
+                      (f & SSM_HAS_D) ? span_of(d->D, p->D) : Span(),
+                      (f & SSM_HAS_H0) ? span_of(d->h0, p->h0) : Span()};
+  const Span outs[] = {span_of(d->dx, p->dx), span_of(d->ddelta, p->ddelta), span_of(d->dA, p->dA),
+                       span_of(d->dB, p->dB), span_of(d->dC, p->dC),
+                       (f & SSM_HAS_D) ? span_of(d->dD, p->dD) : Span(),
+                       (f & SSM_HAS_H0) ? span_of(d->dh0, p->dh0) : Span()};
+  const int no = sizeof(outs) / sizeof(outs[0]);
+  for (int i = 0; i < no; ++i) {
+    for (const Span& s : ins)
+      if (overlap(outs[i], s)) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < no; ++j)
+      if (overlap(outs[i], outs[j])) return SSM_ERR_ALIAS;
+  }
+  return SSM_OK;
+}
+
 // ---------------------------------------------------------------- decode
 
 ssm_status validate_update(const ssm_update_desc* d, const ssm_update_ptrs* p) {
@@ -770,6 +876,71 @@ ssm_status ssm_selective_scan_bwd(const ssm_scan_bwd_desc* d, const ssm_scan_bwd
   q.euler = (f & SSM_DISC_EULER) ? 1 : 0;
   q.dsoftplus = (f & SSM_DELTA_SOFTPLUS) ? 1 : 0;
   return hip_status(ssm::launch_selective_scan_bwd(q, (hipStream_t)hip_stream));
+}
+
+ssm_status ssm_ssd_bwd_workspace_size(const ssm_ssd_bwd_desc* d, size_t* bytes) {
+  if (!bytes) return SSM_ERR_NULL;
+  ssm_status s = validate_ssd_bwd_desc(d);
+  if (s) return s;
+  *bytes = (size_t)plan_ssd_bwd(*d).ws_total;
+  return SSM_OK;
+}
+
+ssm_status ssm_ssd_bwd(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_ptrs* p, void* workspace, size_t workspace_bytes,
+                       void* hip_stream) {
+  ssm_status s = validate_ssd_bwd_desc(d);
+  if (s) return s;
+  if ((s = validate_ssd_bwd_ptrs(d, p))) return s;
+  const SSDBwdPlan pl = plan_ssd_bwd(*d);
+  if (!workspace || workspace_bytes < (size_t)pl.ws_total) return SSM_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return SSM_ERR_ALIGN;
+  const uint32_t f = d->flags;
+  const ssm_ssd_desc fd = ssd_fwd_of(*d);
+  ssm_ssd_ptrs fp;
+  std::memset(&fp, 0, sizeof(fp));
+  fp.x = p->x; fp.delta = p->delta; fp.A = p->A; fp.B = p->B; fp.C = p->C;
+  fp.D = (f & SSM_HAS_D) ? p->D : nullptr;
+  fp.h0 = (f & SSM_HAS_H0) ? p->h0 : nullptr;
+  ssm::SSDBwdParams q;
+  std::memset(&q, 0, sizeof(q));
+  q.f = make_ssd_params(&fd, &fp, pl.f);
+  q.f.y = nullptr;
+  char* w = (char*)workspace;
+  auto take = [&](int64_t bytes) {
+    char* r = w;
+    w += bytes;
+    return r;
+  };
+  q.f.A_cum = (float*)take(pl.f.ws_acum);
+  q.f.beta = (float*)take(pl.f.ws_beta);
+  q.f.states = (float*)take(pl.ws_state);
+  q.dS = (float*)take(pl.ws_state);
+  q.S32 = (float*)take(pl.ws_state);
+  q.SinT = (uint16_t*)take(pl.ws_half);
+  q.dSl = (uint16_t*)take(pl.ws_half);
+  q.dSlT = (uint16_t*)take(pl.ws_half);
+  q.pAend = (float*)take(pl.ws_aend);
+  q.dAcA = (float*)take(pl.ws_step);
+  q.dAcB = (float*)take(pl.ws_step);
+  q.dbeta = (float*)take(pl.ws_step);
+  q.Tj = (float*)take(pl.ws_step);
+  q.dDj = (float*)take(pl.ws_step);
+  q.pA = (float*)take(pl.ws_part);
+  q.pD = (float*)take(pl.ws_part);
+  q.pdB = (float*)take(pl.ws_pdb);
+  q.pdC = (float*)take(pl.ws_pdb);
+  q.dy = p->dy;
+  q.dys_b = d->dy.stride[0]; q.dys_t = d->dy.stride[1]; q.dys_h = d->dy.stride[2];
+  q.dx = p->dx;
+  q.dxs_b = d->dx.stride[0]; q.dxs_t = d->dx.stride[1]; q.dxs_h = d->dx.stride[2];
+  q.dx_f32 = d->dx.dtype == SSM_F32;
+  q.ddelta = p->ddelta;
+  q.dds_b = d->ddelta.stride[0]; q.dds_t = d->ddelta.stride[1]; q.dds_h = d->ddelta.stride[2];
+  q.dh0 = (f & SSM_HAS_H0) ? p->dh0 : nullptr;
+  q.HB = pl.HB;
+  q.nhb = pl.nhb;
+  return hip_status(ssm::launch_ssd_bwd(q, p->dA, p->dB, p->dC, (f & SSM_HAS_D) ? p->dD : nullptr,
+                                        (hipStream_t)hip_stream));
 }
 
 ssm_status ssm_causal_conv1d_fwd(const ssm_conv_desc* d, const ssm_conv_ptrs* p, void* hip_stream) {

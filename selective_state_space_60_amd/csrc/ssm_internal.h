@@ -151,7 +151,49 @@ struct SSDParams {
   float* beta;    // (batch, H, Lp)
   float* states;  // (batch, nchunks, H, P, N)
   void* S_in;     // (batch, nchunks, H, P, N) bf16
+  // chunk_state weights: 0 = exp(A_cum_end - A_cum_j) beta_j (the chunk's own
+  // state), 1 = exp(A_cum_j) (the backward's sum_i exp(A_cum_i) dy_i C_i^T,
+  // with x <- dy and B <- C)
+  int state_coef;
 };
+
+// SSD backward (P = 64, N = 64).  f holds the forward problem and the
+// recomputed forward intermediates (A_cum, beta, states).
+struct SSDBwdParams {
+  SSDParams f;
+  const void* dy;  // (batch, L, H, P) bf16
+  int64_t dys_b, dys_t, dys_h;
+  void* dx;        // (batch, L, H, P) bf16 or fp32
+  int64_t dxs_b, dxs_t, dxs_h;
+  int dx_f32;
+  float* ddelta;   // (batch, L, H) fp32
+  int64_t dds_b, dds_t, dds_h;
+  float* dh0;      // (batch, H, P, N) or null
+  // workspace
+  float* dS;       // (batch, nchunks, H, P, N): sum_i exp(A_cum_i) dy_i C_i^T
+  float* S32;      // (batch, nchunks, H, P, N): state entering each chunk
+  uint16_t* SinT;  // (batch, nchunks, H, N, P) bf16, the same transposed
+  uint16_t* dSl;   // (batch, nchunks, H, P, N) bf16: gradient of each chunk's own state
+  uint16_t* dSlT;  // (batch, nchunks, H, N, P) bf16, the same transposed
+  float* pAend;    // (batch, H, nchunks, P*N/1024): chunk-end decay gradient, partial sums
+  float* dAcA;     // (batch, H, Lp): row sums of W = E o C B^T, + C_i . (inter-chunk dC_i)
+  float* dAcB;     // (batch, H, Lp): -(column sums of W) - T_j
+  float* dbeta;    // (batch, H, Lp)
+  float* Tj;       // (batch, H, Lp): chunk-state terms of the chunk-end gradient
+  float* dDj;      // (batch, H, Lp): dy_i . x_i
+  float* pA;       // (batch, nchunks, H) partial dA
+  float* pD;       // (batch, nchunks, H) partial dD
+  float* pdB;      // (nhb, batch, L, G, N) partial dB per head block
+  float* pdC;      // (nhb, batch, L, G, N)
+  int HB, nhb;     // heads per workgroup, head blocks per group
+};
+
+hipError_t launch_ssd_bwd(const SSDBwdParams& p, float* dA, float* dB, float* dC, float* dD, hipStream_t stream);
+
+// dst[i] = sum_k src[k * stride + i] over k = 0 .. parts-1 in a fixed order
+// (deterministic partial-sum reduction).
+void launch_fixed_order_sum(const float* src, float* dst, int64_t count, int64_t parts, int64_t stride,
+                            hipStream_t stream);
 
 hipError_t launch_ssd_chunk_cumsum(const SSDParams& p, hipStream_t stream);
 hipError_t launch_ssd_chunk_state(const SSDParams& p, hipStream_t stream);
