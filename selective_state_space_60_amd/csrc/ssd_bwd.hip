@@ -45,6 +45,8 @@
 // 0..3) of column m.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -392,21 +394,30 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
 
 // -------------------------------------------------------------- dx pass
 
-// Block as bwd_dc_kernel; strips are now 16 columns j.  Accumulators:
-// RX^T[p][j] (-> R_j) and DB^T[n][j] (-> dB_j), lane -> p or n = 16*t +
-// 4*(l/16) + r, j = 16*strip + l%16.  Per head:
+// Block as bwd_dc_kernel; strips are now 16 columns j, and a wave works
+// through its two strips one after the other (one strip's accumulators live
+// at a time).  Accumulators: RX^T[p][j] (-> R_j) and DB^T[n][j] (-> dB_j),
+// lane -> p or n = 16*t + 4*(l/16) + r, j = 16*strip + l%16.  Per head:
 //   RX^T = w_j dS_loc B_j, DB^T = w_j beta_j dS_loc^T x_j   (A: dS_loc rows / dS_loc^T rows)
 //   for 32-row blocks of i >= j:  CB[i][j], G'[i][j] = dy_i . x_j  (A: staged C / dy rows)
 //     M = CB decay_ij, E = G' decay_ij beta_j -> B operands
 //     RX^T += dy^T M,  DB^T += C^T E   (A: transposed dy / C rows)
+// Past the strip's own block, decay_ij = U_i v_j with U_i = exp(A_cum_i -
+// A_cum_i0) from a per-head table and v_j = exp(A_cum_i0 - A_cum_j), i0 the
+// block's first row (both factors <= 1: j < i0 <= i); the diagonal block
+// takes exp(A_cum_i - A_cum_j) itself (there the factors could overflow).
 template <int Q>
 __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
   constexpr int NTH = 2 * Q, NSTRIP = Q / 16, NIB = Q / 32;
   const SSDParams& p = q.f;
-  __shared__ __attribute__((aligned(16))) uint16_t Cs[Q][kPR];  // C rows of the group: [i][n]
-  __shared__ __attribute__((aligned(16))) uint16_t Ys[Q][kPR];  // dy rows of the head: [i][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[Q][kPR];   // C rows of the group: [i][n]
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[Q][kPR];   // dy rows of the head: [i][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][kPR];   // x rows of the head: [j][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Sl[kP][kPR];  // dS_loc of the head: [p][n]
+  __shared__ __attribute__((aligned(16))) uint16_t SlT[kN][kPR]; // dS_loc^T: [n][p]
   __shared__ __attribute__((aligned(16))) float A2[Q];
   __shared__ __attribute__((aligned(16))) float bj[Q];
+  __shared__ __attribute__((aligned(16))) float U[Q];            // exp(A_cum_i - A_cum_(i & ~31))
   const HeadBlock hb = head_block(q);
   const int64_t b = hb.b, c = hb.c, g = hb.g;
   const int tid = threadIdx.x;
@@ -417,7 +428,7 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
 
   stage_rows<Q, NTH>(Cs, (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g, p.Cs_t, t0, p.L);
   const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
-  bf16x8 bop[2][2];  // B operands: B[j][32*ks + 8*lq .. +7] of the strip's columns
+  bf16x8 bop[2][2];  // B operands: B[j][32*ks + 8*lq .. +7] of the strips' columns
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -427,87 +438,71 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) sumB[s][nt] = zero4();
-  const float Dh = p.Dskip ? 1.f : 0.f;  // scaled per head below
 
   for (int k = 0; k < hb.nh; ++k) {
     const int64_t h = hb.h_lo + k;
-    const uint16_t* Xsrc = (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h;
-    bf16x8 xop[2][2];  // B operands: x[j][32*ks + 8*lq .. +7]
-    uint2 xE[2][4];    // x[j][16*pt + 4*lq .. +3] for the epilogue
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int64_t tj = t0 + 16 * kst[s] + lr;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) xop[s][ks] = row8(Xsrc, p.xs_t, tj, p.L, 32 * ks + 8 * lq);
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) xE[s][pt] = row4(Xsrc, p.xs_t, tj, p.L, 16 * pt + 4 * lq);
-    }
     const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
     const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
-    __syncthreads();  // the previous head is done with Ys, A2, bj
+    const int64_t so = ((b * p.nchunks + c) * p.H + h) * kE;
+    const float Dk = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
+    __syncthreads();  // the previous head is done with the staged rows and tables
+    // every global read of this head, issued together
     stage_rows<Q, NTH>(Ys, (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h, q.dys_t, t0, p.L);
+    stage_rows<Q, NTH>(Xs, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
+    stage_rows<kP, NTH>(Sl, q.dSl + so, kN, 0, kP);
+    stage_rows<kN, NTH>(SlT, q.dSlT + so, kP, 0, kN);
     for (int t = tid; t < Q; t += NTH) {
       A2[t] = Ac[t] * kLog2e;
       bj[t] = be[t];
     }
     __syncthreads();
+    for (int t = tid; t < Q; t += NTH) U[t] = __builtin_amdgcn_exp2f(A2[t] - A2[t & ~31]);
+    __syncthreads();
 
-    // chunk-state terms
-    f32x4 accX[2][4], accB[2][4];
-    float tj_val[2];
-    float csum[2] = {0.f, 0.f};  // this lane's part of W's column sum
-    {
-      const int64_t so = ((b * p.nchunks + c) * p.H + h) * kE;
-      bf16x8 dsl[4][2], dslT[4][2];
+    auto strip = [&](auto S) {
+      constexpr int s = decltype(S)::value;
+      const int jl = 16 * kst[s] + lr;
+      const int64_t tj = t0 + jl;
+      const int diag = (16 * kst[s]) / 32;
+      bf16x8 xop[2];  // B operands: x[j][32*ks + 8*lq .. +7]
+      uint2 xE[4];    // x[j][16*pt + 4*lq .. +3] for the epilogue
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int ks = 0; ks < 2; ++ks) xop[ks] = as_bf16x8(*(const uint4*)&Xs[jl][32 * ks + 8 * lq]);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          dsl[t][ks] = as_bf16x8(*(const uint4*)(q.dSl + so + (16 * t + lr) * kN + 32 * ks + 8 * lq));
-          dslT[t][ks] = as_bf16x8(*(const uint4*)(q.dSlT + so + (16 * t + lr) * kP + 32 * ks + 8 * lq));
-        }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int jl = 16 * kst[s] + lr;
-        const float w = __builtin_amdgcn_exp2f(A2[Q - 1] - A2[jl]);
-        const float wb = w * bj[jl];
+      for (int pt = 0; pt < 4; ++pt) xE[pt] = *(const uint2*)&Xs[jl][16 * pt + 4 * lq];
+      const float aj = A2[jl], bjj = bj[jl];
+
+      // chunk-state terms
+      f32x4 accX[4], accB[4];
+      float tj_val;
+      {
+        const float w = __builtin_amdgcn_exp2f(A2[Q - 1] - aj);
+        const float wb = w * bjj;
         float tp = 0.f;
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          f32x4 a = zero4();
+        for (int t = 0; t < 4; ++t) {
+          f32x4 a = zero4(), d = zero4();
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) a = mfma(dsl[pt][ks], bop[s][ks], a);  // (dS_loc B_j)[p]
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 dsl = as_bf16x8(*(const uint4*)&Sl[16 * t + lr][32 * ks + 8 * lq]);
+            const bf16x8 dslT = as_bf16x8(*(const uint4*)&SlT[16 * t + lr][32 * ks + 8 * lq]);
+            a = mfma(dsl, bop[s][ks], a);  // (dS_loc B_j)[p]
+            d = mfma(dslT, xop[ks], d);    // (dS_loc^T x_j)[n]
+          }
           float xv[4];
-          unpack4(xE[s][pt], xv);
+          unpack4(xE[t], xv);
 #pragma unroll
           for (int r = 0; r < 4; ++r) tp = __builtin_fmaf(xv[r], a[r], tp);
-          accX[s][pt] = a * w;
+          accX[t] = a * w;
+          accB[t] = d * wb;
         }
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          f32x4 a = zero4();
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) a = mfma(dslT[nt][ks], xop[s][ks], a);  // (dS_loc^T x_j)[n]
-          accB[s][nt] = a * wb;
-        }
-        tj_val[s] = sum_rows(tp) * wb;
+        tj_val = sum_rows(tp) * wb;
       }
-    }
 
-    // intra-chunk terms over the blocks of i at or after the strip
-    for (int ib = (16 * kst[0]) / 32; ib < NIB; ++ib) {
-      const int i0 = 32 * ib;
-      bf16x8 aY[4], aC[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        aY[t] = tr_operand(Ys, i0, 16 * t, tr_row, tr_col);
-        aC[t] = tr_operand(Cs, i0, 16 * t, tr_row, tr_col);
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int jl = 16 * kst[s] + lr;
-        const int diag = (16 * kst[s]) / 32;
-        if (ib < diag) continue;  // wave-uniform
+      // intra-chunk terms over the blocks of i at or after the strip
+      float csum = 0.f;  // this lane's part of W's column sum
+      for (int ib = diag; ib < NIB; ++ib) {
+        const int i0 = 32 * ib;
         f32x4 ct[2], gt[2];
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
@@ -515,59 +510,64 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             a = mfma(as_bf16x8(*(const uint4*)&Cs[i0 + 16 * it + lr][32 * ks + 8 * lq]), bop[s][ks], a);
-            d = mfma(as_bf16x8(*(const uint4*)&Ys[i0 + 16 * it + lr][32 * ks + 8 * lq]), xop[s][ks], d);
+            d = mfma(as_bf16x8(*(const uint4*)&Ys[i0 + 16 * it + lr][32 * ks + 8 * lq]), xop[ks], d);
           }
           ct[it] = a;  // CB[i0 + 16*it + 4*lq + r][j]
           gt[it] = d;  // G'[i0 + 16*it + 4*lq + r][j]
         }
-        const float aj = A2[jl], bjj = bj[jl];
         float m[8], e[8];
-        float w_col = 0.f;
+        if (ib > diag) {
+          const float vj = __builtin_amdgcn_exp2f(A2[i0] - aj), vb = vj * bjj;
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-          const float4 a4 = *(const float4*)&A2[i0 + 16 * it + 4 * lq];
-          const float ai[4] = {a4.x, a4.y, a4.z, a4.w};
+          for (int it = 0; it < 2; ++it) {
+            const float4 u4 = *(const float4*)&U[i0 + 16 * it + 4 * lq];
+            const float u[4] = {u4.x, u4.y, u4.z, u4.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = i0 + 16 * it + 4 * lq + r;
-            const bool ok = ib > diag || i >= jl;
-            const float f = __builtin_amdgcn_exp2f(ok ? ai[r] - aj : 0.f);
-            m[4 * it + r] = ok ? ct[it][r] * f : 0.f;
-            e[4 * it + r] = ok ? gt[it][r] * (f * bjj) : 0.f;
-            w_col = __builtin_fmaf(e[4 * it + r], ct[it][r], w_col);
+            for (int r = 0; r < 4; ++r) {
+              m[4 * it + r] = ct[it][r] * (u[r] * vj);
+              e[4 * it + r] = gt[it][r] * (u[r] * vb);
+              csum = __builtin_fmaf(e[4 * it + r], ct[it][r], csum);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const float4 a4 = *(const float4*)&A2[i0 + 16 * it + 4 * lq];
+            const float ai[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = i0 + 16 * it + 4 * lq + r;
+              const bool ok = i >= jl;
+              const float f = __builtin_amdgcn_exp2f(ok ? ai[r] - aj : 0.f);
+              m[4 * it + r] = ok ? ct[it][r] * f : 0.f;
+              e[4 * it + r] = ok ? gt[it][r] * (f * bjj) : 0.f;
+              csum = __builtin_fmaf(e[4 * it + r], ct[it][r], csum);
+            }
           }
         }
-        csum[s] += w_col;
         const bf16x8 mop = as_bf16x8(make_uint4(pack2(m[0], m[1]), pack2(m[2], m[3]), pack2(m[4], m[5]),
                                                 pack2(m[6], m[7])));
         const bf16x8 eop = as_bf16x8(make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]),
                                                 pack2(e[6], e[7])));
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          accX[s][t] = mfma(aY[t], mop, accX[s][t]);
-          accB[s][t] = mfma(aC[t], eop, accB[s][t]);
+          accX[t] = mfma(tr_operand(Ys, i0, 16 * t, tr_row, tr_col), mop, accX[t]);
+          accB[t] = mfma(tr_operand(Cs, i0, 16 * t, tr_row, tr_col), eop, accB[t]);
         }
       }
-    }
 
-    // dx, dbeta, dy . x; dB terms
-    const float Dk = Dh != 0.f ? p.Dskip[h * p.Ds_h] : 0.f;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int jl = 16 * kst[s] + lr;
-      const int64_t tj = t0 + jl;
-      const float bjj = bj[jl];
+      // dx, dbeta, dy . x, dA_cum terms; dB terms
       float db = 0.f, dd = 0.f;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         float xv[4], yv[4], o[4];
-        unpack4(xE[s][pt], xv);
+        unpack4(xE[pt], xv);
         unpack4(*(const uint2*)&Ys[jl][16 * pt + 4 * lq], yv);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          db = __builtin_fmaf(xv[r], accX[s][pt][r], db);
+          db = __builtin_fmaf(xv[r], accX[pt][r], db);
           dd = __builtin_fmaf(xv[r], yv[r], dd);
-          o[r] = __builtin_fmaf(bjj, accX[s][pt][r], Dk * yv[r]);
+          o[r] = __builtin_fmaf(bjj, accX[pt][r], Dk * yv[r]);
         }
         if (tj < p.L) {
           const int64_t off = b * q.dxs_b + tj * q.dxs_t + h * q.dxs_h + 16 * pt + 4 * lq;
@@ -577,17 +577,20 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
       }
       db = sum_rows(db);
       dd = sum_rows(dd);
-      const float wc = sum_rows(csum[s]);
+      const float wc = sum_rows(csum);
       if (lq == 0) {
         const int64_t o = (b * p.H + h) * p.Lp + tj;
         q.dbeta[o] = db;
-        q.Tj[o] = tj_val[s];
+        q.Tj[o] = tj_val;
         q.dDj[o] = dd;
-        q.dAcB[o] = -wc - tj_val[s];
+        q.dAcB[o] = -wc - tj_val;
       }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) sumB[s][nt] += accB[s][nt];
-    }
+      for (int nt = 0; nt < 4; ++nt) sumB[s][nt] += accB[nt];
+    };
+    strip(std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    strip(std::integral_constant<int, 1>{});
   }
   // the head block's dB terms
   float* dst = q.pdB + ((int64_t)hb.hbk * p.batch + b) * p.L * p.G * kN;
