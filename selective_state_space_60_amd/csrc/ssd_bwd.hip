@@ -165,59 +165,79 @@ __device__ __forceinline__ uint2 row4(const uint16_t* src, int64_t st, int64_t t
 
 // ------------------------------------------------- reverse state passing
 
-// Block = (b, h, 1024 of the 4096 state entries); 4 entries (row p, columns
-// n0 .. n0+3) per thread.  Forward: S_in[c] in fp32 and bf16 transposed.
-// Backward: G = 0; for c = last .. 0: dS_loc[c] = G (bf16, both layouts),
-// partial <S_in[c], G> exp(A_cum_end[c]); G = dS[c] + exp(A_cum_end[c]) G.
+// Block = (b, h, 16 rows p0 .. p0+15 of the 64 x 64 state); thread t holds
+// row p0 + t/16, columns n0 = 4*(t%16) .. +3.  Forward: S_in[c] in fp32 and,
+// through an LDS transpose, bf16 [n][p].  Backward: G = 0; for c = last .. 0:
+// dS_loc[c] = G (bf16, both layouts), partial <S_in[c], G> exp(A_cum_end[c]),
+// G = dS[c] + exp(A_cum_end[c]) G.  The transpose tiles and the partial sums
+// are double-buffered, so each chunk needs one barrier.
 __global__ __launch_bounds__(256) void bwd_state_kernel(SSDBwdParams q) {
   const SSDParams& p = q.f;
-  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint16_t T[2][kN][16 + 4];  // [n][p - p0]
+  __shared__ float red[2][4];
   int64_t bid = blockIdx.x;
   const int qb = (int)(bid % kNQ);
   bid /= kNQ;
   const int64_t h = bid % p.H, b = bid / p.H;
   const int tid = threadIdx.x;
-  const int e0 = qb * 1024 + tid * 4;
-  const int pr = e0 / kN, n0 = e0 % kN;
+  const int p0 = qb * 16, pl = tid / 16, n0 = 4 * (tid % 16);
+  const int e0 = (p0 + pl) * kN + n0;
+  const int tn = tid / 4, tq = 4 * (tid % 4);  // transposed store: row n = tn, p0 + tq .. +3
   const float* Ac = p.A_cum + (b * p.H + h) * p.Lp;
   const int64_t cs = p.H * kE;
   const int64_t base = (b * p.nchunks * p.H + h) * kE;
+  const int64_t nc = p.nchunks;
+  auto put_T = [&](int buf, float4 v) {
+    T[buf][n0 + 0][pl] = f2bf(v.x);
+    T[buf][n0 + 1][pl] = f2bf(v.y);
+    T[buf][n0 + 2][pl] = f2bf(v.z);
+    T[buf][n0 + 3][pl] = f2bf(v.w);
+  };
+  auto store_T = [&](int buf, uint16_t* dst) {
+    *(uint2*)(dst + tn * kP + p0 + tq) = *(const uint2*)&T[buf][tn][tq];
+  };
   float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
   if (p.h0) S = *(const float4*)(p.h0 + (b * p.H + h) * kE + e0);
-  for (int64_t c = 0; c < p.nchunks; ++c) {
+  float4 sl = *(const float4*)(p.states + base + e0);
+  int buf = 0;
+  for (int64_t c = 0; c < nc; ++c) {
     const int64_t o = base + c * cs;
-    *(float4*)(q.S32 + o + e0) = S;
-    uint16_t* t = q.SinT + o + pr;
-    t[(n0 + 0) * kP] = f2bf(S.x);
-    t[(n0 + 1) * kP] = f2bf(S.y);
-    t[(n0 + 2) * kP] = f2bf(S.z);
-    t[(n0 + 3) * kP] = f2bf(S.w);
+    const float4 cur = sl;
+    if (c + 1 < nc) sl = *(const float4*)(p.states + o + cs + e0);
     const float dec = __builtin_amdgcn_exp2f(Ac[c * p.Q + p.Q - 1] * kLog2e);
-    const float4 sl = *(const float4*)(p.states + o + e0);
-    S.x = __builtin_fmaf(dec, S.x, sl.x);
-    S.y = __builtin_fmaf(dec, S.y, sl.y);
-    S.z = __builtin_fmaf(dec, S.z, sl.z);
-    S.w = __builtin_fmaf(dec, S.w, sl.w);
+    *(float4*)(q.S32 + o + e0) = S;
+    put_T(buf, S);
+    __syncthreads();
+    store_T(buf, q.SinT + o);
+    buf ^= 1;
+    S.x = __builtin_fmaf(dec, S.x, cur.x);
+    S.y = __builtin_fmaf(dec, S.y, cur.y);
+    S.z = __builtin_fmaf(dec, S.z, cur.z);
+    S.w = __builtin_fmaf(dec, S.w, cur.w);
   }
   float4 G = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int64_t c = p.nchunks - 1; c >= 0; --c) {
+  float4 dn = *(const float4*)(q.dS + base + (nc - 1) * cs + e0);
+  float4 sn = *(const float4*)(q.S32 + base + (nc - 1) * cs + e0);
+  for (int64_t c = nc - 1; c >= 0; --c) {
     const int64_t o = base + c * cs;
+    const float4 d = dn, sc = sn;
+    if (c > 0) {
+      dn = *(const float4*)(q.dS + o - cs + e0);
+      sn = *(const float4*)(q.S32 + o - cs + e0);
+    }
+    const float dec = __builtin_amdgcn_exp2f(Ac[c * p.Q + p.Q - 1] * kLog2e);
     *(uint2*)(q.dSl + o + e0) = make_uint2(pack2(G.x, G.y), pack2(G.z, G.w));
-    uint16_t* t = q.dSlT + o + pr;
-    t[(n0 + 0) * kP] = f2bf(G.x);
-    t[(n0 + 1) * kP] = f2bf(G.y);
-    t[(n0 + 2) * kP] = f2bf(G.z);
-    t[(n0 + 3) * kP] = f2bf(G.w);
-    const float4 sc = *(const float4*)(q.S32 + o + e0);
+    put_T(buf, G);
     float dot = sc.x * G.x + sc.y * G.y + sc.z * G.z + sc.w * G.w;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
-    if (tid % 64 == 0) red[tid / 64] = dot;
+    if (tid % 64 == 0) red[buf][tid / 64] = dot;
     __syncthreads();
-    const float dec = __builtin_amdgcn_exp2f(Ac[c * p.Q + p.Q - 1] * kLog2e);
-    if (tid == 0) q.pAend[((b * p.H + h) * p.nchunks + c) * kNQ + qb] = dec * (((red[0] + red[1]) + red[2]) + red[3]);
-    __syncthreads();
-    const float4 d = *(const float4*)(q.dS + o + e0);
+    store_T(buf, q.dSlT + o);
+    if (tid == 0)
+      q.pAend[((b * p.H + h) * nc + c) * kNQ + qb] =
+          dec * (((red[buf][0] + red[buf][1]) + red[buf][2]) + red[buf][3]);
+    buf ^= 1;
     G.x = __builtin_fmaf(dec, G.x, d.x);
     G.y = __builtin_fmaf(dec, G.y, d.y);
     G.z = __builtin_fmaf(dec, G.z, d.z);
@@ -238,8 +258,11 @@ template <int Q>
 __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
   constexpr int NTH = 2 * Q, NSTRIP = Q / 16;
   const SSDParams& p = q.f;
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][kPR];  // x rows of the head: [j][p]
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][kPR];  // B rows of the group: [j][n]
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][kPR];   // x rows of the head: [j][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][kPR];   // B rows of the group: [j][n]
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[Q][kPR];   // C rows of the group: [i][n]
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[Q][kPR];   // dy rows of the head: [i][p]
+  __shared__ __attribute__((aligned(16))) uint16_t SsT[kN][kPR]; // S_in^T of the head: [n][p]
   __shared__ __attribute__((aligned(16))) float A2[Q];  // A_cum * log2(e)
   __shared__ __attribute__((aligned(16))) float bj[Q];  // beta
   __shared__ __attribute__((aligned(16))) float tb[Q];  // exp(A_cum[j|31] - A_cum[j]) beta_j
@@ -252,12 +275,7 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
   const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
 
   stage_rows<Q, NTH>(Bs, (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g, p.Bs_t, t0, p.L);
-  const uint16_t* Csrc = (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g;
-  bf16x8 cop[2][2];  // B operands: C[i][32*ks + 8*lq .. +7] of the strip's rows
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) cop[s][ks] = row8(Csrc, p.Cs_t, t0 + 16 * kst[s] + lr, p.L, 32 * ks + 8 * lq);
+  stage_rows<Q, NTH>(Cs, (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g, p.Cs_t, t0, p.L);
   f32x4 sum[2][4];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
@@ -266,16 +284,13 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
 
   for (int k = 0; k < hb.nh; ++k) {
     const int64_t h = hb.h_lo + k;
-    const uint16_t* Ysrc = (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h;
-    bf16x8 yop[2][2];  // B operands: dy[i][32*ks + 8*lq .. +7] of the strip's rows
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) yop[s][ks] = row8(Ysrc, q.dys_t, t0 + 16 * kst[s] + lr, p.L, 32 * ks + 8 * lq);
     const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
     const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
-    __syncthreads();  // the previous head is done with Xs, A2, bj, tb
+    __syncthreads();  // the previous head is done with the staged rows and tables
+    // every global read of this head, issued together
     stage_rows<Q, NTH>(Xs, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
+    stage_rows<Q, NTH>(Ys, (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h, q.dys_t, t0, p.L);
+    stage_rows<kN, NTH>(SsT, q.SinT + ((b * p.nchunks + c) * p.H + h) * kE, kP, 0, kN);
     for (int t = tid; t < Q; t += NTH) {
       A2[t] = Ac[t] * kLog2e;
       bj[t] = be[t];
@@ -283,6 +298,14 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
     __syncthreads();
     for (int t = tid; t < Q; t += NTH) tb[t] = __builtin_amdgcn_exp2f(A2[t | 31] - A2[t]) * bj[t];
     __syncthreads();
+    bf16x8 yop[2][2], cop[2][2];  // B operands: dy[i][32*ks + 8*lq .. +7], C[i][..] of the strips' rows
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        yop[s][ks] = as_bf16x8(*(const uint4*)&Ys[16 * kst[s] + lr][32 * ks + 8 * lq]);
+        cop[s][ks] = as_bf16x8(*(const uint4*)&Cs[16 * kst[s] + lr][32 * ks + 8 * lq]);
+      }
 
     f32x4 acc[2][4];
     float rsum[2] = {0.f, 0.f};  // this lane's part of W's row sum
@@ -354,12 +377,6 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
       }
     }
     // inter-chunk term; W's row sum and C_i . (inter-chunk dC_i) of this head
-    const uint16_t* Sp = q.SinT + ((b * p.nchunks + c) * p.H + h) * kE;
-    bf16x8 sop[4][2];  // A operands: S_in^T[16*nt + lr][32*ks + 8*lq .. +7]
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) sop[nt][ks] = as_bf16x8(*(const uint4*)(Sp + (16 * nt + lr) * kP + 32 * ks + 8 * lq));
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int il = 16 * kst[s] + lr;
@@ -369,10 +386,11 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
       for (int nt = 0; nt < 4; ++nt) {
         f32x4 a = zero4();
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) a = mfma(sop[nt][ks], yop[s][ks], a);
+        for (int ks = 0; ks < 2; ++ks)  // A: S_in^T[16*nt + lr][32*ks + 8*lq .. +7]
+          a = mfma(as_bf16x8(*(const uint4*)&SsT[16 * nt + lr][32 * ks + 8 * lq]), yop[s][ks], a);
         a *= ei;
         float cv[4];
-        unpack4(row4(Csrc, p.Cs_t, t0 + il, p.L, 16 * nt + 4 * lq), cv);
+        unpack4(*(const uint2*)&Cs[il][16 * nt + 4 * lq], cv);
 #pragma unroll
         for (int r = 0; r < 4; ++r) dot = __builtin_fmaf(cv[r], a[r], dot);
         sum[s][nt] += acc[s][nt] + a;
