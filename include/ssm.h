@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 #define SSM_MAX_DIMS 5
 #define SSM_SCAN_MAX_DSTATE 64 /* selective scan: N <= 64 */
 
@@ -86,6 +86,8 @@ typedef struct {
 #define SSM_HAS_DELTA_BIAS 64u /* with SSM_DELTA_SOFTPLUS: add delta_bias first (scan, decode) */
 #define SSM_HAS_BIAS 128u      /* conv: add bias[d]                                   */
 #define SSM_SILU 256u          /* conv: apply SiLU to the output                      */
+#define SSM_WANT_CKPT 512u     /* scan: also write the state before every 16-step tile */
+#define SSM_HAS_CKPT 1024u     /* scan backward: read those states, do not recompute them */
 
 /* ------------------------------------------------------------------ scan */
 
@@ -99,6 +101,10 @@ typedef struct {
  *   h0       : (batch, dim, dstate) F32 contiguous   if SSM_HAS_H0
  *   h_last   : (batch, dim, dstate) F32 contiguous   if SSM_WANT_HLAST
  *   delta_bias: (dim)         F32                if SSM_HAS_DELTA_BIAS, any stride
+ *   ckpt     : (batch, ceil(seqlen/16), dim, dstate) F32 contiguous   if SSM_WANT_CKPT:
+ *              ckpt[b, k] = the state before step 16k (h0 or 0 for k = 0) --
+ *              the checkpoints ssm_selective_scan_bwd takes with SSM_HAS_CKPT,
+ *              so that a training step's backward need not rerun the recurrence
  * io is SSM_F32 or SSM_BF16 and is the same for x, delta, z, B, C.
  * SSM_DELTA_SOFTPLUS: the step size used is softplus(delta + delta_bias[d])
  * (softplus(v) = log(1 + e^v); delta_bias taken as 0 without
@@ -112,7 +118,7 @@ typedef struct {
 typedef struct {
   int64_t batch, seqlen, dim, dstate;
   uint32_t flags;
-  ssm_tensor_desc x, delta, A, B, C, D, z, y, h0, h_last, delta_bias;
+  ssm_tensor_desc x, delta, A, B, C, D, z, y, h0, h_last, delta_bias, ckpt;
 } ssm_scan_desc;
 
 typedef struct {
@@ -127,6 +133,7 @@ typedef struct {
   const float* h0;  /* NULL unless SSM_HAS_H0     */
   float* h_last;    /* NULL unless SSM_WANT_HLAST */
   const float* delta_bias; /* NULL unless SSM_HAS_DELTA_BIAS */
+  float* ckpt;             /* NULL unless SSM_WANT_CKPT      */
 } ssm_scan_ptrs;
 
 /* -------------------------------------------------------- scan backward */
@@ -154,7 +161,11 @@ typedef struct {
  *   dD          : (dim) F32 contiguous  if SSM_HAS_D
  *   dh0         : (batch, dim, dstate) F32 contiguous   if SSM_HAS_H0
  *   ddelta_bias : (dim) F32 contiguous  if SSM_HAS_DELTA_BIAS
- * Flags as in the forward except SSM_WANT_HLAST (not accepted).  The sums
+ *   ckpt        : (batch, ceil(seqlen/16), dim, dstate) F32 contiguous  if SSM_HAS_CKPT:
+ *                 the forward's checkpoints (SSM_WANT_CKPT) of the same inputs;
+ *                 read only; without the flag they are recomputed in the workspace
+ * Flags as in the forward except SSM_WANT_HLAST and SSM_WANT_CKPT (not
+ * accepted), plus SSM_HAS_CKPT.  The sums
  * over channels (dB, dC) and over batch and time (dA, dD, ddelta_bias) are
  * formed from per-workgroup fp32 partial sums added in a fixed order, so the
  * results are deterministic.  Outputs may not overlap inputs or each other.
@@ -165,7 +176,7 @@ typedef struct {
   int64_t batch, seqlen, dim, dstate;
   uint32_t flags;
   ssm_tensor_desc x, delta, A, B, C, D, z, h0, delta_bias, dy;
-  ssm_tensor_desc dx, ddelta, dz, dA, dB, dC, dD, dh0, ddelta_bias;
+  ssm_tensor_desc dx, ddelta, dz, dA, dB, dC, dD, dh0, ddelta_bias, ckpt;
 } ssm_scan_bwd_desc;
 
 typedef struct {
@@ -188,6 +199,7 @@ typedef struct {
   float* dD;               /* NULL unless SSM_HAS_D          */
   float* dh0;              /* NULL unless SSM_HAS_H0         */
   float* ddelta_bias;      /* NULL unless SSM_HAS_DELTA_BIAS */
+  const float* ckpt;       /* NULL unless SSM_HAS_CKPT       */
 } ssm_scan_bwd_ptrs;
 
 /* ------------------------------------------------------------------- SSD */

@@ -22,7 +22,8 @@ SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_STRIDE, SSM_ERR_ALIG
 SSM_F32, SSM_BF16, SSM_F16 = 0, 1, 2
 SSM_HAS_Z, SSM_HAS_D, SSM_DISC_EULER, SSM_HAS_H0, SSM_WANT_HLAST = 1, 2, 4, 8, 16
 SSM_DELTA_SOFTPLUS, SSM_HAS_DELTA_BIAS, SSM_HAS_BIAS, SSM_SILU = 32, 64, 128, 256
-ABI_VERSION = 3
+SSM_WANT_CKPT, SSM_HAS_CKPT = 512, 1024
+ABI_VERSION = 4
 MAX_DIMS = 5
 
 # Every function include/ssm.h declares.
@@ -38,7 +39,7 @@ class TensorDesc(ctypes.Structure):
                 ("stride", ctypes.c_int64 * MAX_DIMS)]
 
 
-_SCAN_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "h0", "h_last", "delta_bias")
+_SCAN_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "h0", "h_last", "delta_bias", "ckpt")
 _SSD_T = ("x", "delta", "A", "B", "C", "D", "y", "h0", "h_last")
 _UPD_T = ("x", "delta", "A", "B", "C", "D", "z", "y", "state", "delta_bias")
 _CONV_T = ("x", "weight", "bias", "y")
@@ -87,11 +88,12 @@ class ConvPtrs(ctypes.Structure):
 
 class ScanBwdDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
-                ("dstate", ctypes.c_int64), ("flags", ctypes.c_uint32)] + [(n, TensorDesc) for n in _BWD_IN + _BWD_OUT]
+                ("dstate", ctypes.c_int64), ("flags", ctypes.c_uint32)] + [(n, TensorDesc) for n in
+                                                                           _BWD_IN + _BWD_OUT + ("ckpt",)]
 
 
 class ScanBwdPtrs(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in _BWD_IN + _BWD_OUT]
+    _fields_ = [(n, ctypes.c_void_p) for n in _BWD_IN + _BWD_OUT + ("ckpt",)]
 
 
 class SSDBwdDesc(ctypes.Structure):
@@ -204,23 +206,31 @@ def _delta_flags(delta_softplus, delta_bias):
 
 
 def scan_desc(x, delta, A, B, C, D=None, z=None, y=None, h0=None, h_last=None, euler=False,
-              delta_softplus=False, delta_bias=None) -> ScanDesc:
+              delta_softplus=False, delta_bias=None, ckpt=None) -> ScanDesc:
     d = ScanDesc()
     d.batch, d.seqlen, d.dim = x.shape
     d.dstate = A.shape[-1]
     d.flags = ((SSM_HAS_Z if z is not None else 0) | (SSM_HAS_D if D is not None else 0) |
                (SSM_DISC_EULER if euler else 0) | (SSM_HAS_H0 if h0 is not None else 0) |
-               (SSM_WANT_HLAST if h_last is not None else 0) | _delta_flags(delta_softplus, delta_bias))
-    for name, t in zip(_SCAN_T, (x, delta, A, B, C, D, z, y, h0, h_last, delta_bias)):
+               (SSM_WANT_HLAST if h_last is not None else 0) | _delta_flags(delta_softplus, delta_bias) |
+               (SSM_WANT_CKPT if ckpt is not None else 0))
+    for name, t in zip(_SCAN_T, (x, delta, A, B, C, D, z, y, h0, h_last, delta_bias, ckpt)):
         setattr(d, name, tensor_desc(t))
     return d
 
 
-def scan_ptrs(x, delta, A, B, C, D=None, z=None, y=None, h0=None, h_last=None, delta_bias=None) -> ScanPtrs:
+def scan_ptrs(x, delta, A, B, C, D=None, z=None, y=None, h0=None, h_last=None, delta_bias=None,
+              ckpt=None) -> ScanPtrs:
     p = ScanPtrs()
-    for name, t in zip(_SCAN_T, (x, delta, A, B, C, D, z, y, h0, h_last, delta_bias)):
+    for name, t in zip(_SCAN_T, (x, delta, A, B, C, D, z, y, h0, h_last, delta_bias, ckpt)):
         setattr(p, name, _p(t))
     return p
+
+
+def scan_ckpt(batch: int, seqlen: int, dim: int, dstate: int, device="cuda"):
+    """An uninitialised checkpoint buffer for selective_scan_fwd(ckpt=...) and
+    selective_scan_bwd(ckpt=...): the state before every 16-step tile."""
+    return torch.empty((batch, (seqlen + 15) // 16, dim, dstate), dtype=torch.float32, device=device)
 
 
 def selective_scan_workspace_size(desc: ScanDesc) -> int:
@@ -231,19 +241,21 @@ def selective_scan_workspace_size(desc: ScanDesc) -> int:
 
 
 def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, euler=False, want_hlast=False,
-                       y_dtype=None, y=None, stream=None, delta_softplus=False, delta_bias=None):
+                       y_dtype=None, y=None, stream=None, delta_softplus=False, delta_bias=None, ckpt=None):
     """y = selective scan of x (see include/ssm.h).  Returns (y, h_last or None).
 
     x, delta, z: (batch, L, dim); B, C: (batch, L, dstate); A: (dim, dstate)
     fp32; D: (dim,) fp32; h0: (batch, dim, dstate) fp32.  x/delta/z/B/C are all
     fp32 or all bf16; y defaults to x's dtype.  delta_softplus: the step size
-    is softplus(delta + delta_bias) (delta_bias (dim,) fp32, optional)."""
+    is softplus(delta + delta_bias) (delta_bias (dim,) fp32, optional).
+    ckpt: optional scan_ckpt(...) buffer, filled with the state before every
+    16-step tile for selective_scan_bwd(ckpt=...)."""
     if y is None:
         y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
     h_last = torch.empty((x.shape[0], x.shape[2], A.shape[-1]), dtype=torch.float32,
                          device=x.device) if want_hlast else None
-    desc = scan_desc(x, delta, A, B, C, D, z, y, h0, h_last, euler, delta_softplus, delta_bias)
-    ptrs = scan_ptrs(x, delta, A, B, C, D, z, y, h0, h_last, delta_bias)
+    desc = scan_desc(x, delta, A, B, C, D, z, y, h0, h_last, euler, delta_softplus, delta_bias, ckpt)
+    ptrs = scan_ptrs(x, delta, A, B, C, D, z, y, h0, h_last, delta_bias, ckpt)
     nbytes = selective_scan_workspace_size(desc)
     ws = _workspace(nbytes, x.device)
     _check(lib().ssm_selective_scan_fwd(ctypes.byref(desc), ctypes.byref(ptrs), _p(ws), nbytes, _stream(stream)),
@@ -422,9 +434,11 @@ def causal_conv1d(x, weight, bias=None, silu=True, y_dtype=None, y=None, stream=
 # ---------------------------------------------------------- scan backward
 
 def selective_scan_bwd(dy, x, delta, A, B, C, D=None, z=None, h0=None, euler=False, delta_softplus=False,
-                       delta_bias=None, grad_dtype=None, stream=None) -> dict:
+                       delta_bias=None, grad_dtype=None, stream=None, ckpt=None) -> dict:
     """Gradients of sum(dy * y) for y = selective_scan_fwd(x, delta, A, B, C,
     D, z, h0, euler, delta_softplus, delta_bias) (see include/ssm.h).
+    ckpt: the forward's checkpoints of the same inputs (selective_scan_fwd(...,
+    ckpt=...)); without them the backward recomputes them.
 
     Returns a dict: dx, ddelta (grad_dtype, default x's dtype), dz (if z), dA
     (dim, dstate), dB, dC (batch, L, dstate), dD (if D), dh0 (if h0),
@@ -444,9 +458,9 @@ def selective_scan_bwd(dy, x, delta, A, B, C, D=None, z=None, h0=None, euler=Fal
     d.batch, d.seqlen, d.dim, d.dstate = batch, L, dim, N
     d.flags = ((SSM_HAS_Z if z is not None else 0) | (SSM_HAS_D if D is not None else 0) |
                (SSM_DISC_EULER if euler else 0) | (SSM_HAS_H0 if h0 is not None else 0) |
-               _delta_flags(delta_softplus, delta_bias))
+               _delta_flags(delta_softplus, delta_bias) | (SSM_HAS_CKPT if ckpt is not None else 0))
     p = ScanBwdPtrs()
-    for name, t in list(zip(_BWD_IN, ins)) + [(k, out[k]) for k in _BWD_OUT]:
+    for name, t in list(zip(_BWD_IN, ins)) + [(k, out[k]) for k in _BWD_OUT] + [("ckpt", ckpt)]:
         setattr(d, name, tensor_desc(t))
         setattr(p, name, _p(t))
     n = ctypes.c_size_t()

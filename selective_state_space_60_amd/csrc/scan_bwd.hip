@@ -16,7 +16,8 @@
 // of a row holds step j's per-channel values (delta, x, z, dy), broadcast to
 // the row with DPP row broadcasts.
 //  1. ckpt_kernel runs the recurrence forward and stores the state before
-//     every tile: 1/16 of the states, the rest is recomputed.
+//     every tile: 1/16 of the states, the rest is recomputed.  (A training
+//     forward can store the same states itself; then this pass is skipped.)
 //  2. bwd_kernel walks the tiles backwards.  Per tile it recomputes the 16
 //     states of each lane from the tile's checkpoint (kept in registers) with
 //     the readout C.h, forms g_t and dz_t, then steps the adjoint back through
@@ -684,10 +685,10 @@ void launch_ks(const ScanBwdParams& p, hipStream_t stream) {
   const int64_t npad = (n_dblk * p.batch + 7) / 8 * 8;  // blocks past the end exit at once
   const dim3 grid((unsigned)npad);
   if (p.euler) {
-    hipLaunchKernelGGL((ckpt_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
+    if (!p.ckpt_given) hipLaunchKernelGGL((ckpt_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
     hipLaunchKernelGGL((bwd_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
   } else {
-    hipLaunchKernelGGL((ckpt_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
+    if (!p.ckpt_given) hipLaunchKernelGGL((ckpt_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
     hipLaunchKernelGGL((bwd_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
   }
   const int64_t bln = p.batch * p.L * p.N;

@@ -483,13 +483,22 @@ __device__ __forceinline__ void finalize_tile(ScanSmem<KS>& s, int buf, const fl
   s.yb[buf][threadIdx.x / G][threadIdx.x % G] = v;
 }
 
-// The walk over the stretch, for one update form.  MODE 0 writes y;
-// MODE 1 only carries the state (from 0) and this lane's share of the sum of
-// delta (the steps it holds).
+// Where a walk stores the state before each of its tiles (the backward's
+// checkpoints): `p` points at the lane's first state of the stretch's first
+// tile, `step` is one tile's stride, `nk` the lane's states below N.
+struct CkptOut {
+  float* p;  // null: no checkpoints
+  int64_t step;
+  int nk;
+};
+
+// The walk over the stretch, for one update form.  MODE 0 writes y (and the
+// checkpoints); MODE 1 only carries the state (from 0) and this lane's share
+// of the sum of delta (the steps it holds).
 template <class L, int KS, int MODE, int FORM>
 __device__ __forceinline__ void walk(ScanSmem<KS>& s, L& ld, const Tiles& tl, float (&h)[KS], const Lane<KS>& ln,
                                      const float (&fA)[G], float Dk, bool want_z, float& sum_dt,
-                                     const DeltaXform& dx) {
+                                     const DeltaXform& dx, const CkptOut& ck) {
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, sg = tid % G;
   float* prow = &s.part[wave][sg][G * (lane / G)];
@@ -515,6 +524,11 @@ __device__ __forceinline__ void walk(ScanSmem<KS>& s, L& ld, const Tiles& tl, fl
   auto body = [&](int it, typename L::Set& rn) {
     const int buf = it & 1;
     const int rows = it < tl.ntiles - 1 ? TT : (it == tl.ntiles - 1 ? tl.last_rows : 0);
+    if (MODE == 0 && ck.p && it < tl.ntiles) {
+#pragma unroll
+      for (int k = 0; k < KS; ++k)  // the g form carries A h
+        if (k < ck.nk) ck.p[it * ck.step + k] = FORM == kFormG ? h[k] * ln.iA[k] : h[k];
+    }
     take_hold<KS, FORM>(s, buf, want_z, hd, dx, sg < rows);
     float4 o[2][2][KS];
     read_block<KS>(s, buf, 0, sg, o[0]);
@@ -668,6 +682,15 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
 #pragma unroll
   for (int n = 0; n < G; ++n) fA[n] = 1.f;
   float sum_dt = 0.f;
+  CkptOut ck;
+  ck.p = nullptr;
+  ck.step = p.D * p.N;
+  ck.nk = 0;
+  if (MODE == 0 && p.ckpt && d_ok) {
+    const int64_t n0 = sg * KS;
+    ck.nk = n0 >= p.N ? 0 : (p.N - n0 < KS ? (int)(p.N - n0) : KS);
+    ck.p = p.ckpt + ((b * ((p.L + TT - 1) / TT) + t_begin / TT) * p.D + d) * p.N + (n0 < p.N ? n0 : 0);
+  }
   DeltaXform dx;
   dx.on = p.dsoftplus != 0;
   dx.bias = (dx.on && p.dbias && d_ok) ? p.dbias[d * p.dbs_d] : 0.f;
@@ -683,15 +706,15 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
     }
 #pragma unroll
     for (int k = 0; k < KS; ++k) h[k] *= Av[k];  // g = A h
-    walk<decltype(ld), KS, MODE, kFormG>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx);
+    walk<decltype(ld), KS, MODE, kFormG>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx, ck);
 #pragma unroll
     for (int k = 0; k < KS; ++k) h[k] *= ln.iA[k];  // h = g / A
   } else if (form == kFormEuler) {
-    walk<decltype(ld), KS, MODE, kFormEuler>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx);
+    walk<decltype(ld), KS, MODE, kFormEuler>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx, ck);
   } else if (form == kFormHZero) {
-    walk<decltype(ld), KS, MODE, kFormHZero>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx);
+    walk<decltype(ld), KS, MODE, kFormHZero>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx, ck);
   } else {
-    walk<decltype(ld), KS, MODE, kFormH>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx);
+    walk<decltype(ld), KS, MODE, kFormH>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx, ck);
   }
 
   if (MODE == 1) {

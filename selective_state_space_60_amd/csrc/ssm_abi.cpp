@@ -15,12 +15,20 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr uint32_t kScanFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_WANT_HLAST |
-                                SSM_DELTA_SOFTPLUS | SSM_HAS_DELTA_BIAS;
+                                SSM_DELTA_SOFTPLUS | SSM_HAS_DELTA_BIAS | SSM_WANT_CKPT;
 constexpr uint32_t kSSDFlags = SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_WANT_HLAST;
 constexpr uint32_t kUpdateFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER | SSM_DELTA_SOFTPLUS | SSM_HAS_DELTA_BIAS;
 constexpr uint32_t kConvFlags = SSM_HAS_BIAS | SSM_SILU;
 constexpr uint32_t kScanBwdFlags = SSM_HAS_Z | SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_DELTA_SOFTPLUS |
-                                   SSM_HAS_DELTA_BIAS;
+                                   SSM_HAS_DELTA_BIAS | SSM_HAS_CKPT;
+
+// Shape of the scan checkpoints: the state before every 16-step tile.
+void ckpt_shape(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t (&sh)[4]) {
+  sh[0] = batch;
+  sh[1] = (seqlen + 15) / 16;
+  sh[2] = dim;
+  sh[3] = dstate;
+}
 constexpr int kSimds = 256 * 4;  // MI355X: 256 compute units x 4 SIMDs
 
 int64_t esize(int32_t dt) { return dt == SSM_BF16 || dt == SSM_F16 ? 2 : 4; }
@@ -147,6 +155,11 @@ ssm_status validate_scan_desc(const ssm_scan_desc* d) {
     if ((s = check_tensor(d->h_last, 3, bdn, d->h_last.dtype == SSM_F32, false, true))) return s;
   if (d->flags & SSM_HAS_DELTA_BIAS)
     if ((s = check_tensor(d->delta_bias, 1, dd, d->delta_bias.dtype == SSM_F32, false, false))) return s;
+  if (d->flags & SSM_WANT_CKPT) {
+    int64_t ck[4];
+    ckpt_shape(d->batch, d->seqlen, d->dim, d->dstate, ck);
+    if ((s = check_tensor(d->ckpt, 4, ck, d->ckpt.dtype == SSM_F32, false, true))) return s;
+  }
   // The kernel addresses one tile of rows (and, for B and C, all N states of
   // a row) with 32-bit byte offsets from the tile's first element.
   const int64_t e = esize(io), ey = esize(d->y.dtype);
@@ -171,6 +184,8 @@ ssm_status validate_scan_ptrs(const ssm_scan_desc* d, const ssm_scan_ptrs* p) {
   if ((f & SSM_WANT_HLAST) && !p->h_last) return SSM_ERR_NULL;
   if ((f & SSM_HAS_DELTA_BIAS) && !p->delta_bias) return SSM_ERR_NULL;
   if ((f & SSM_HAS_DELTA_BIAS) && !aligned(p->delta_bias, 4)) return SSM_ERR_ALIGN;
+  if ((f & SSM_WANT_CKPT) && !p->ckpt) return SSM_ERR_NULL;
+  if ((f & SSM_WANT_CKPT) && !aligned(p->ckpt, 4)) return SSM_ERR_ALIGN;
   const int64_t io = esize(d->x.dtype);
   if (!aligned(p->x, io) || !aligned(p->delta, io) || !aligned(p->B, io) || !aligned(p->C, io) ||
       !aligned(p->A, 4) || !aligned(p->y, esize(d->y.dtype)))
@@ -189,9 +204,10 @@ ssm_status validate_scan_ptrs(const ssm_scan_desc* d, const ssm_scan_ptrs* p) {
                       (f & SSM_HAS_DELTA_BIAS) ? span_of(d->delta_bias, p->delta_bias) : Span()};
   const Span ys = span_of(d->y, p->y);
   const Span hl = (f & SSM_WANT_HLAST) ? span_of(d->h_last, p->h_last) : Span();
+  const Span ck = (f & SSM_WANT_CKPT) ? span_of(d->ckpt, p->ckpt) : Span();
   for (const Span& s : ins)
-    if (overlap(ys, s) || overlap(hl, s)) return SSM_ERR_ALIAS;
-  if (overlap(ys, hl)) return SSM_ERR_ALIAS;
+    if (overlap(ys, s) || overlap(hl, s) || overlap(ck, s)) return SSM_ERR_ALIAS;
+  if (overlap(ys, hl) || overlap(ys, ck) || overlap(hl, ck)) return SSM_ERR_ALIAS;
   return SSM_OK;
 }
 
@@ -495,7 +511,7 @@ BwdPlan plan_bwd(const ssm_scan_bwd_desc& d) {
   BwdPlan pl;
   pl.ntiles = (d.seqlen + 15) / 16;
   pl.n_dblk = (d.dim + 15) / 16;
-  pl.ws_ckpt = round256(d.batch * pl.ntiles * d.dim * d.dstate * 4);
+  pl.ws_ckpt = (d.flags & SSM_HAS_CKPT) ? 0 : round256(d.batch * pl.ntiles * d.dim * d.dstate * 4);
   pl.ws_pdB = round256(pl.n_dblk * d.batch * d.seqlen * d.dstate * 4);
   pl.ws_pdA = round256(d.batch * d.dim * d.dstate * 4);
   pl.ws_pdD = round256(d.batch * d.dim * 4);
@@ -550,6 +566,11 @@ ssm_status validate_bwd_desc(const ssm_scan_bwd_desc* d) {
     if ((s = check_tensor(d->delta_bias, 1, dd, d->delta_bias.dtype == SSM_F32, false, false))) return s;
     if ((s = check_tensor(d->ddelta_bias, 1, dd, d->ddelta_bias.dtype == SSM_F32, false, true))) return s;
   }
+  if (f & SSM_HAS_CKPT) {
+    int64_t ck[4];
+    ckpt_shape(d->batch, d->seqlen, d->dim, d->dstate, ck);
+    if ((s = check_tensor(d->ckpt, 4, ck, d->ckpt.dtype == SSM_F32, false, true))) return s;
+  }
   // The kernels address one 16-step tile of 16 channels (or of all dstate
   // states of B and C) with 32-bit byte offsets.
   const int64_t e = esize(io);
@@ -572,6 +593,8 @@ ssm_status validate_bwd_ptrs(const ssm_scan_bwd_desc* d, const ssm_scan_bwd_ptrs
   if ((f & SSM_HAS_D) && (!p->D || !p->dD)) return SSM_ERR_NULL;
   if ((f & SSM_HAS_H0) && (!p->h0 || !p->dh0)) return SSM_ERR_NULL;
   if ((f & SSM_HAS_DELTA_BIAS) && (!p->delta_bias || !p->ddelta_bias)) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_CKPT) && !p->ckpt) return SSM_ERR_NULL;
+  if ((f & SSM_HAS_CKPT) && !aligned(p->ckpt, 4)) return SSM_ERR_ALIGN;
   const int64_t e = esize(d->x.dtype);
   if (!aligned(p->x, e) || !aligned(p->delta, e) || !aligned(p->B, e) || !aligned(p->C, e) || !aligned(p->A, 4) ||
       !aligned(p->dy, esize(d->dy.dtype)) || !aligned(p->dx, esize(d->dx.dtype)) ||
@@ -590,7 +613,8 @@ ssm_status validate_bwd_ptrs(const ssm_scan_bwd_desc* d, const ssm_scan_bwd_ptrs
                       (f & SSM_HAS_D) ? span_of(d->D, p->D) : Span(),
                       (f & SSM_HAS_Z) ? span_of(d->z, p->z) : Span(),
                       (f & SSM_HAS_H0) ? span_of(d->h0, p->h0) : Span(),
-                      (f & SSM_HAS_DELTA_BIAS) ? span_of(d->delta_bias, p->delta_bias) : Span()};
+                      (f & SSM_HAS_DELTA_BIAS) ? span_of(d->delta_bias, p->delta_bias) : Span(),
+                      (f & SSM_HAS_CKPT) ? span_of(d->ckpt, p->ckpt) : Span()};
   const Span outs[] = {span_of(d->dx, p->dx),
                        span_of(d->ddelta, p->ddelta),
                        span_of(d->dA, p->dA),
@@ -718,6 +742,7 @@ ssm_status ssm_selective_scan_fwd(const ssm_scan_desc* d, const ssm_scan_ptrs* p
   q.dsoftplus = (f & SSM_DELTA_SOFTPLUS) ? 1 : 0;
   q.dbias = (f & SSM_HAS_DELTA_BIAS) ? p->delta_bias : nullptr;
   q.dbs_d = (f & SSM_HAS_DELTA_BIAS) ? d->delta_bias.stride[0] : 0;
+  q.ckpt = (f & SSM_WANT_CKPT) ? p->ckpt : nullptr;
   q.n_seg = pl.n_seg;
   q.seg_len = pl.seg_len;
   if (pl.n_seg > 1) {
@@ -847,7 +872,8 @@ ssm_status ssm_selective_scan_bwd(const ssm_scan_bwd_desc* d, const ssm_scan_bwd
   q.dh0 = (f & SSM_HAS_H0) ? p->dh0 : nullptr;
   q.ddbias = (f & SSM_HAS_DELTA_BIAS) ? p->ddelta_bias : nullptr;
   char* w = (char*)workspace;
-  q.ckpt = (float*)w;
+  q.ckpt = (f & SSM_HAS_CKPT) ? (float*)p->ckpt : (float*)w;  // the given checkpoints are only read
+  q.ckpt_given = (f & SSM_HAS_CKPT) ? 1 : 0;
   q.pdB = (float*)(w + pl.ws_ckpt);
   q.pdC = (float*)(w + pl.ws_ckpt + pl.ws_pdB);
   q.pdA = (float*)(w + pl.ws_ckpt + 2 * pl.ws_pdB);

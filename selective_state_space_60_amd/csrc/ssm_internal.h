@@ -37,6 +37,9 @@ struct ScanParams {
   const float* dbias;
   int64_t dbs_d;
   int dsoftplus;
+  // Optional (batch, ceil(L/16), D, N) fp32: the state before every 16-step
+  // tile, as the backward's checkpoints (null: not written).
+  float* ckpt;
 };
 
 // Tiling of the scan kernels (also used by the host planner).
@@ -93,6 +96,7 @@ struct ScanBwdParams {
   float* ddbias;       // or null
   // workspace
   float* ckpt;         // (batch, ntiles, D, N): state before each 16-step tile
+  int ckpt_given;      // the caller supplied ckpt (the forward's): no checkpoint pass
   float* pdB;          // (n_dblk, batch, L, N): sums over each workgroup's channels
   float* pdC;
   float* pdA;          // (batch, D, N): sums over time

@@ -32,7 +32,7 @@ def test_exports_match_header():
     assert declared == sorted(ssm.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.ssm_abi_version() == ssm.ABI_VERSION == 3
+    assert lib.ssm_abi_version() == ssm.ABI_VERSION == 4
 
 
 def test_status_strings():
@@ -124,6 +124,81 @@ def test_scan_validation(mutate, status):
     d, p = _scan(flags=ALL | ssm.SSM_DELTA_SOFTPLUS | ssm.SSM_HAS_DELTA_BIAS)
     mutate(d, p)
     assert _fwd(d, p) == status
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda d, p: setattr(p, "ckpt", None), ssm.SSM_ERR_NULL),
+    (lambda d, p: d.ckpt.shape.__setitem__(1, 2), ssm.SSM_ERR_SHAPE),   # ceil(16 / 16) = 1 tile
+    (lambda d, p: setattr(d.ckpt, "dtype", 1), ssm.SSM_ERR_DTYPE),
+    (lambda d, p: d.ckpt.stride.__setitem__(2, 8), ssm.SSM_ERR_STRIDE),
+    (lambda d, p: setattr(p, "ckpt", (12 << 36) + 2), ssm.SSM_ERR_ALIGN),
+    (lambda d, p: setattr(p, "ckpt", p.y), ssm.SSM_ERR_ALIAS),
+    (lambda d, p: setattr(p, "ckpt", p.h0), ssm.SSM_ERR_ALIAS),
+    (lambda d, p: setattr(p, "ckpt", p.h_last), ssm.SSM_ERR_ALIAS),
+])
+def test_scan_ckpt_validation(mutate, status):
+    d, p = _scan(flags=ALL | ssm.SSM_WANT_CKPT, ckpt=T((2, 1, 8, 4), ptr=12 << 36))
+    mutate(d, p)
+    assert _fwd(d, p) == status
+
+
+def _scan_bwd(batch=2, L=40, D=8, N=4, io="bf16", flags=0, **over):
+    nt = (L + 15) // 16
+    ts = {"x": T((batch, L, D), io, ptr=1 << 36), "delta": T((batch, L, D), io, ptr=2 << 36),
+          "A": T((D, N), ptr=3 << 36), "B": T((batch, L, N), io, ptr=4 << 36),
+          "C": T((batch, L, N), io, ptr=5 << 36), "D": T((D,), ptr=6 << 36),
+          "z": T((batch, L, D), io, ptr=7 << 36), "h0": T((batch, D, N), ptr=8 << 36),
+          "delta_bias": T((D,), ptr=9 << 36), "dy": T((batch, L, D), io, ptr=10 << 36),
+          "dx": T((batch, L, D), io, ptr=11 << 36), "ddelta": T((batch, L, D), io, ptr=12 << 36),
+          "dz": T((batch, L, D), io, ptr=13 << 36), "dA": T((D, N), ptr=14 << 36),
+          "dB": T((batch, L, N), ptr=15 << 36), "dC": T((batch, L, N), ptr=16 << 36),
+          "dD": T((D,), ptr=17 << 36), "dh0": T((batch, D, N), ptr=18 << 36),
+          "ddelta_bias": T((D,), ptr=19 << 36), "ckpt": T((batch, nt, D, N), ptr=20 << 36)}
+    ts.update(over)
+    d = ssm.ScanBwdDesc()
+    d.batch, d.seqlen, d.dim, d.dstate, d.flags = batch, L, D, N, flags
+    p = ssm.ScanBwdPtrs()
+    for k, t in ts.items():
+        setattr(d, k, _td(t))
+        setattr(p, k, None if t is None or t.ptr is None else t.ptr)
+    return d, p
+
+
+BWD_ALL = (ssm.SSM_HAS_Z | ssm.SSM_HAS_D | ssm.SSM_HAS_H0 | ssm.SSM_DELTA_SOFTPLUS | ssm.SSM_HAS_DELTA_BIAS |
+           ssm.SSM_HAS_CKPT)
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda d, p: setattr(d, "flags", d.flags | ssm.SSM_WANT_HLAST), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: setattr(d, "flags", d.flags | ssm.SSM_WANT_CKPT), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: setattr(d, "dstate", 65), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: setattr(p, "dy", None), ssm.SSM_ERR_NULL),
+    (lambda d, p: setattr(p, "dz", None), ssm.SSM_ERR_NULL),
+    (lambda d, p: setattr(p, "ckpt", None), ssm.SSM_ERR_NULL),
+    (lambda d, p: d.ckpt.shape.__setitem__(1, 2), ssm.SSM_ERR_SHAPE),   # ceil(40 / 16) = 3 tiles
+    (lambda d, p: setattr(d.ckpt, "dtype", 1), ssm.SSM_ERR_DTYPE),
+    (lambda d, p: setattr(d.dA, "dtype", 1), ssm.SSM_ERR_DTYPE),
+    (lambda d, p: d.dB.stride.__setitem__(2, 2), ssm.SSM_ERR_STRIDE),
+    (lambda d, p: setattr(p, "ckpt", (20 << 36) + 2), ssm.SSM_ERR_ALIGN),
+    (lambda d, p: setattr(p, "dx", p.ckpt), ssm.SSM_ERR_ALIAS),
+    (lambda d, p: setattr(p, "dB", p.dC), ssm.SSM_ERR_ALIAS),
+    (lambda d, p: setattr(p, "ddelta", p.delta), ssm.SSM_ERR_ALIAS),
+])
+def test_scan_bwd_validation(mutate, status):
+    d, p = _scan_bwd(flags=BWD_ALL)
+    mutate(d, p)
+    assert ssm.lib().ssm_selective_scan_bwd(ctypes.byref(d), ctypes.byref(p), 30 << 36, 1 << 40, None) == status
+
+
+def test_scan_bwd_workspace_without_checkpoints():
+    # given the forward's checkpoints, the backward keeps none of its own
+    n = ctypes.c_size_t()
+    d, _ = _scan_bwd(batch=4, L=4096, D=5120, N=16, flags=ssm.SSM_HAS_Z | ssm.SSM_HAS_D)
+    assert ssm.lib().ssm_selective_scan_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == ssm.SSM_OK
+    with_ck = n.value
+    d, _ = _scan_bwd(batch=4, L=4096, D=5120, N=16, flags=ssm.SSM_HAS_Z | ssm.SSM_HAS_D | ssm.SSM_HAS_CKPT)
+    assert ssm.lib().ssm_selective_scan_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == ssm.SSM_OK
+    assert with_ck - n.value == 4 * 256 * 5120 * 16 * 4
 
 
 def test_scan_null_descriptor():

@@ -1,0 +1,124 @@
+"""GPU parity of the scan's training checkpoints: ssm_selective_scan_fwd with
+SSM_WANT_CKPT writes the state before every 16-step tile, and
+ssm_selective_scan_bwd with SSM_HAS_CKPT reads them instead of recomputing.
+
+ckpt[b, k] is checked against the oracle's final state of the first 16k
+steps (h0 or 0 for k = 0), fp32 io to rel-L2 1e-5 (bf16 io: the same fp32
+arithmetic on exact inputs, same bar).  The backward from the forward's
+checkpoints is checked against the oracle backward like the recomputing one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+from _gpu import banner, dev_tensor, host_f64, metrics
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import selective_state_space_60_amd as ssm  # noqa: E402
+
+
+def _upload(spec, inp):
+    g = {k: dev_tensor(inp[k], spec.io) for k in ("x", "delta", "B", "C")}
+    g["A"] = dev_tensor(inp["A"], "f32")
+    g["D"] = dev_tensor(inp["D"], "f32") if "D" in inp else None
+    g["z"] = dev_tensor(inp["z"], spec.io) if "z" in inp else None
+    return g
+
+
+def _prefix(inp, t):
+    return {k: (v[:, :t] if k in ("x", "delta", "B", "C", "z") else v) for k, v in inp.items()}
+
+
+def _check_ckpt(spec, seed, tiles, h0=False, softplus=False):
+    banner("scan ckpt %s seed %d" % (spec.name, seed))
+    inp = synth.scan_inputs(spec, seed)
+    g = _upload(spec, inp)
+    h0v = synth.state_input((spec.batch, spec.dim, spec.dstate), seed) if h0 else None
+    db = synth.delta_bias_input(spec.dim, seed) if softplus else None
+    ck = ssm.scan_ckpt(spec.batch, spec.seqlen, spec.dim, spec.dstate)
+    ssm.selective_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
+                           h0=None if h0v is None else torch.from_numpy(h0v).cuda(), euler=spec.euler,
+                           delta_softplus=softplus, delta_bias=None if db is None else torch.from_numpy(db).cuda(),
+                           ckpt=ck)
+    torch.cuda.synchronize()
+    got = host_f64(ck)
+    for k in tiles:
+        if k == 0:
+            ref = np.zeros((spec.batch, spec.dim, spec.dstate)) if h0v is None else h0v.astype(np.float64)
+        else:
+            _, ref = oracle.selective_scan(_prefix(inp, 16 * k), spec.io, euler=spec.euler,
+                                           h0=None if h0v is None else h0v.astype(np.float64),
+                                           delta_softplus=softplus, delta_bias=db)
+        m = metrics(got[:, k], ref)
+        print("tile", k, m, flush=True)
+        assert m["nan"] == 0 and m["rel_l2"] <= 1e-5, (k, m)
+    return inp, g, ck, h0v, db
+
+
+def small(**kw):
+    base = dict(batch=2, seqlen=100, dim=40, dstate=16, io="f32", has_z=True, has_D=True,
+                A=synth.Dist(synth.NEG_EXP_UNIFORM, -1.0, 1.0))
+    base.update(kw)
+    return synth.scan_spec(synth.TINY, **base)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(io="bf16"), dict(dstate=4), dict(dstate=40, dim=24),
+                                dict(euler=True), dict(seqlen=16), dict(seqlen=17)],
+                         ids=lambda kw: "_".join("%s%s" % i for i in sorted(kw.items())) or "base")
+def test_ckpt_values(kw):
+    spec = small(**kw)
+    nt = (spec.seqlen + 15) // 16
+    _check_ckpt(spec, 1, sorted({0, min(1, nt - 1), nt // 2, nt - 1}))
+
+
+def test_ckpt_values_h0_softplus():
+    spec = small(seqlen=70)
+    _check_ckpt(spec, 2, [0, 1, 4], h0=True, softplus=True)
+
+
+def test_ckpt_values_split_sequence():
+    # one workgroup of channels and 4096 steps: the forward splits the
+    # sequence in two segments; the second segment's first checkpoints come
+    # from its rescan
+    spec = small(batch=1, seqlen=4100, dim=16)
+    _check_ckpt(spec, 3, [0, 127, 128, 129, 256])
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(io="bf16"), dict(euler=True), dict(dstate=40, dim=24)],
+                         ids=lambda kw: "_".join("%s%s" % i for i in sorted(kw.items())) or "base")
+def test_bwd_from_forward_ckpt(kw):
+    spec = small(**kw)
+    inp, g, ck, _, _ = _check_ckpt(spec, 4, [0])
+    dy = synth.fill((spec.batch, spec.seqlen, spec.dim), synth.Dist(synth.NORMAL, 0.0, 1.0), "f32", 4, 21)
+    got = ssm.selective_scan_bwd(dev_tensor(dy, "f32"), g["x"], g["delta"], g["A"], g["B"], g["C"], D=g["D"],
+                                 z=g["z"], euler=spec.euler, grad_dtype=torch.float32, ckpt=ck)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(inp, spec.io, dy, "f32", euler=spec.euler)
+    assert set(got) == set(ref)
+    for k in sorted(ref):
+        m = metrics(host_f64(got[k]), ref[k])
+        print(k, m, flush=True)
+        assert m["nan"] == 0 and m["rel_l2"] <= 1e-5, (k, m)
+
+
+def test_bwd_from_forward_ckpt_h0_softplus_bias():
+    spec = small(seqlen=90)
+    inp, g, ck, h0v, db = _check_ckpt(spec, 5, [0], h0=True, softplus=True)
+    dy = synth.fill((spec.batch, spec.seqlen, spec.dim), synth.Dist(synth.NORMAL, 0.0, 1.0), "f32", 5, 21)
+    got = ssm.selective_scan_bwd(dev_tensor(dy, "f32"), g["x"], g["delta"], g["A"], g["B"], g["C"], D=g["D"],
+                                 z=g["z"], h0=torch.from_numpy(h0v).cuda(), delta_softplus=True,
+                                 delta_bias=torch.from_numpy(db).cuda(), grad_dtype=torch.float32, ckpt=ck)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(inp, spec.io, dy, "f32", h0=h0v.astype(np.float64), delta_softplus=True,
+                                    delta_bias=db)
+    for k in sorted(ref):
+        m = metrics(host_f64(got[k]), ref[k])
+        print(k, m, flush=True)
+        assert m["nan"] == 0 and m["rel_l2"] <= 1e-5, (k, m)
