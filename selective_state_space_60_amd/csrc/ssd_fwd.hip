@@ -276,8 +276,12 @@ __global__ __launch_bounds__(256) void state_passing_kernel(SSDParams p) {
 
 // ------------------------------------------------------- s4 chunk scan
 
-// Block = (b, chunk c, head h) with Q/32 waves; wave wv owns the two 16-row
-// strips k = wv and k = Q/16 - 1 - wv, which balances the causal work.
+// Block = (b, chunk c, group g, block of HB heads of g) with Q/32 waves; the
+// heads are taken in turn.  B (staged) and the C operands are the group's, so
+// they are read once per block; the next head's x, S_in, A_cum and beta are
+// loaded into registers while the current head is computed.  Wave wv owns
+// the two 16-row strips k = wv and k = Q/16 - 1 - wv, which balances the
+// causal work.
 // Accumulators hold Y^T[p][i]: lane -> p = 16*mt + 4*(l/16) + r,
 // i = 16*k + l%16.
 //
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(SSDParams p) {
 // four consecutive steps of one p, the contraction slots G'^T's layout needs.
 // beta_j is applied to G' (it multiplies the decay factor of column j).
 template <int Q, int NB>
-__global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
+__global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p, int HB, int nhb) {
   constexpr int NTH = 2 * Q;        // threads
   constexpr int NSTRIP = Q / 16;
   constexpr int N = 64 * NB;        // states
@@ -310,27 +314,49 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
   __shared__ __attribute__((aligned(16))) uint4 Ss[64][8 * NB];
 
   int64_t bid = blockIdx.x;
-  const int64_t h = bid % p.H;
-  bid /= p.H;
+  const int hbk = (int)(bid % nhb);
+  bid /= nhb;
+  const int64_t g = bid % p.G;
+  bid /= p.G;
   const int64_t c = bid % p.nchunks, b = bid / p.nchunks;
-  const int64_t g = h / (p.H / p.G);
+  const int64_t hpg = p.H / p.G, h_lo = g * hpg + (int64_t)hbk * HB;
+  const int nh = (int)(hpg - (int64_t)hbk * HB < HB ? hpg - (int64_t)hbk * HB : HB);
   const int tid = threadIdx.x;
   const int64_t t0 = c * Q;
   // wave index as a scalar, so branches on it are uniform
   const int wv = __builtin_amdgcn_readfirstlane(tid / 64), l = tid % 64, lr = l % 16, lq = l / 16;
   const int kst[2] = {wv, NSTRIP - 1 - wv};
 
-  // --- issue the staging loads and the C operands before using any
-  uint4 rx[NTX], rb[NTB];
-  const uint16_t* Xsrc = (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h;
-  const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
+  // The head-dependent operands of head hh, into registers: x rows, S_in
+  // (512 * NB 16-byte pieces), and for thread t < Q: A_cum[t], A_cum[t | 31], beta[t].
+  constexpr int NS = 512 * NB / NTH;
+  static_assert(NS * NTH == 512 * NB, "whole S_in pieces per thread");
+  uint4 rx[NTX], rs[NS];
+  float ra = 0.f, ra31 = 0.f, rbt = 0.f;
+  auto load_head = [&](int64_t hh) {
+    const uint16_t* Xsrc = (const uint16_t*)p.x + b * p.xs_b + hh * p.xs_h;
 #pragma unroll
-  for (int u = 0; u < NTX; ++u) {
-    const int task = tid + NTH * u;
-    const int j = task / 8, cb = (task % 8) * 8;
-    const int64_t tr = t0 + j < p.L ? t0 + j : p.L - 1;
-    rx[u] = *(const uint4*)(Xsrc + tr * p.xs_t + cb);
-  }
+    for (int u = 0; u < NTX; ++u) {
+      const int task = tid + NTH * u;
+      const int j = task / 8, cb = (task % 8) * 8;
+      const int64_t tr = t0 + j < p.L ? t0 + j : p.L - 1;
+      rx[u] = *(const uint4*)(Xsrc + tr * p.xs_t + cb);
+    }
+    const uint16_t* Sp = (const uint16_t*)p.S_in + ((b * p.nchunks + c) * p.H + hh) * (64 * N);
+#pragma unroll
+    for (int u = 0; u < NS; ++u) rs[u] = *(const uint4*)(Sp + 8 * (tid + NTH * u));
+    if (tid < Q) {
+      const float* Ac = p.A_cum + (b * p.H + hh) * p.Lp + t0;
+      ra = Ac[tid];
+      ra31 = Ac[tid | 31];
+      rbt = p.beta[(b * p.H + hh) * p.Lp + t0 + tid];
+    }
+  };
+
+  // --- issue the group's B rows, the C operands and head h_lo's loads before using any
+  uint4 rb[NTB];
+  const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
+  load_head(h_lo);
 #pragma unroll
   for (int u = 0; u < NTB; ++u) {
     const int task = tid + NTH * u;
@@ -347,29 +373,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) Cop[s][ks] = as_bf16x8(*(const uint4*)(Cb + tr * p.Cs_t + 32 * ks + 8 * lq));
   }
-  // S_in of this (chunk, head): 512 * NB 16-byte pieces
-  constexpr int NS = 512 * NB / NTH;
-  static_assert(NS * NTH == 512 * NB, "whole S_in pieces per thread");
-  const uint16_t* Sp = (const uint16_t*)p.S_in + ((b * p.nchunks + c) * p.H + h) * (64 * N);
-  uint4 rs[NS];
-#pragma unroll
-  for (int u = 0; u < NS; ++u) rs[u] = *(const uint4*)(Sp + 8 * (tid + NTH * u));
-  const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
-  const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
-  for (int t = tid; t < Q; t += NTH) {
-    A2[t] = Ac[t] * kLog2e;
-    bj[t] = be[t];
-  }
-  __syncthreads();
-  for (int t = tid; t < Q; t += NTH) tb[t] = __builtin_amdgcn_exp2f(A2[t | 31] - A2[t]) * bj[t];
   // rows at or past L hold zeros
-#pragma unroll
-  for (int u = 0; u < NTX; ++u) {
-    const int task = tid + NTH * u;
-    const int j = task / 8, cb = (task % 8) * 8;
-    const bool ok = t0 + j < p.L;
-    *(uint4*)&Xs[j][cb] = ok ? rx[u] : make_uint4(0, 0, 0, 0);
-  }
 #pragma unroll
   for (int u = 0; u < NTB; ++u) {
     const int task = tid + NTH * u;
@@ -377,127 +381,146 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p) {
     const bool ok = t0 + j < p.L;
     *(uint4*)&Bs[j][cb] = ok ? rb[u] : make_uint4(0, 0, 0, 0);
   }
-#pragma unroll
-  for (int u = 0; u < NS; ++u) {
-    const int e = tid + NTH * u, row = e / (8 * NB), cq = e % (8 * NB);
-    Ss[row][cq ^ (row % 8)] = rs[u];
-  }
   // C rows past L must not contribute
 #pragma unroll
   for (int s = 0; s < 2; ++s)
     if (t0 + 16 * kst[s] + lr >= p.L)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) Cop[s][ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
-  __syncthreads();
 
-  f32x4 acc[2][4];
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // transpose-read address of this lane: row 4*lq + (lr / 4), values 4*(lr % 4) .. +3 of a 16-wide p block
-  const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
-  // intra-chunk term over 32-step blocks jb up to the later strip's diagonal
-  const int jb_last = (16 * kst[1]) / 32;
-  for (int jb = 0; jb <= jb_last; ++jb) {
-    const int j0 = 32 * jb;
-    // A operands of Y^T += X^T G'^T: rows p, contraction slots in G^T's layout
-    bf16x8 aX[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Xs[j0 + tr_row][16 * mt + tr_col]);
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Xs[j0 + 16 + tr_row][16 * mt + tr_col]);
-      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-      aX[mt] = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+  for (int k = 0; k < nh; ++k) {
+    const int64_t h = h_lo + k;
+    // stage head h from the registers (the previous head's readers are done)
+    if (tid < Q) {
+      A2[tid] = ra * kLog2e;
+      bj[tid] = rbt;
+      tb[tid] = __builtin_amdgcn_exp2f((ra31 - ra) * kLog2e) * rbt;
     }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int i0 = 16 * kst[s];
-      const int diag = i0 / 32;
-      if (jb > diag) continue;  // wave-uniform
-      const int i = i0 + lr;
-      f32x4 gt[2];
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        // A operands of G^T = B_J C_I^T: B rows j0 + 16*jt + lr, read per use
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          a = mfma(as_bf16x8(*(const uint4*)&Bs[j0 + 16 * jt + lr][32 * ks + 8 * lq]), Cop[s][ks], a);
-        gt[jt] = a;  // G^T[j0 + 16*jt + 4*lq + r][i]
+  #pragma unroll
+    for (int u = 0; u < NTX; ++u) {
+      const int task = tid + NTH * u;
+      const int j = task / 8, cb = (task % 8) * 8;
+      const bool ok = t0 + j < p.L;
+      *(uint4*)&Xs[j][cb] = ok ? rx[u] : make_uint4(0, 0, 0, 0);
+    }
+  #pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = tid + NTH * u, row = e / (8 * NB), cq = e % (8 * NB);
+      Ss[row][cq ^ (row % 8)] = rs[u];
+    }
+    __syncthreads();
+    if (k + 1 < nh) load_head(h + 1);  // in flight while head h is computed
+
+    f32x4 acc[2][4];
+  #pragma unroll
+    for (int s = 0; s < 2; ++s)
+  #pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // transpose-read address of this lane: row 4*lq + (lr / 4), values 4*(lr % 4) .. +3 of a 16-wide p block
+    const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
+    // intra-chunk term over 32-step blocks jb up to the later strip's diagonal
+    const int jb_last = (16 * kst[1]) / 32;
+    for (int jb = 0; jb <= jb_last; ++jb) {
+      const int j0 = 32 * jb;
+      // A operands of Y^T += X^T G'^T: rows p, contraction slots in G^T's layout
+      bf16x8 aX[4];
+  #pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Xs[j0 + tr_row][16 * mt + tr_col]);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Xs[j0 + 16 + tr_row][16 * mt + tr_col]);
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        aX[mt] = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
       }
-      float v[8];
-      if (jb < diag) {
-        // every j of the block precedes every row of the strip:
-        // exp(A_i - A_j) = exp(A_i - A_m) exp(A_m - A_j), m = j0 + 31, both <= 1
-        const float vi = __builtin_amdgcn_exp2f(A2[i] - A2[j0 + 31]);
-#pragma unroll
+  #pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int i0 = 16 * kst[s];
+        const int diag = i0 / 32;
+        if (jb > diag) continue;  // wave-uniform
+        const int i = i0 + lr;
+        f32x4 gt[2];
+  #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
-          const float4 t4 = *(const float4*)&tb[j0 + 16 * jt + 4 * lq];
-          v[4 * jt + 0] = gt[jt][0] * (t4.x * vi);
-          v[4 * jt + 1] = gt[jt][1] * (t4.y * vi);
-          v[4 * jt + 2] = gt[jt][2] * (t4.z * vi);
-          v[4 * jt + 3] = gt[jt][3] * (t4.w * vi);
+          // A operands of G^T = B_J C_I^T: B rows j0 + 16*jt + lr, read per use
+          f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            a = mfma(as_bf16x8(*(const uint4*)&Bs[j0 + 16 * jt + lr][32 * ks + 8 * lq]), Cop[s][ks], a);
+          gt[jt] = a;  // G^T[j0 + 16*jt + 4*lq + r][i]
         }
-      } else {
-        const float ai = A2[i];
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          const float4 a4 = *(const float4*)&A2[j0 + 16 * jt + 4 * lq];
-          const float4 b4 = *(const float4*)&bj[j0 + 16 * jt + 4 * lq];
-          const float aj[4] = {a4.x, a4.y, a4.z, a4.w};
-          const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = j0 + 16 * jt + 4 * lq + r;
-            const float d = j <= i ? ai - aj[r] : 0.f;
-            const float e = __builtin_amdgcn_exp2f(d);
-            v[4 * jt + r] = j <= i ? gt[jt][r] * (e * bb[r]) : 0.f;
+        float v[8];
+        if (jb < diag) {
+          // every j of the block precedes every row of the strip:
+          // exp(A_i - A_j) = exp(A_i - A_m) exp(A_m - A_j), m = j0 + 31, both <= 1
+          const float vi = __builtin_amdgcn_exp2f(A2[i] - A2[j0 + 31]);
+  #pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const float4 t4 = *(const float4*)&tb[j0 + 16 * jt + 4 * lq];
+            v[4 * jt + 0] = gt[jt][0] * (t4.x * vi);
+            v[4 * jt + 1] = gt[jt][1] * (t4.y * vi);
+            v[4 * jt + 2] = gt[jt][2] * (t4.z * vi);
+            v[4 * jt + 3] = gt[jt][3] * (t4.w * vi);
+          }
+        } else {
+          const float ai = A2[i];
+  #pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const float4 a4 = *(const float4*)&A2[j0 + 16 * jt + 4 * lq];
+            const float4 b4 = *(const float4*)&bj[j0 + 16 * jt + 4 * lq];
+            const float aj[4] = {a4.x, a4.y, a4.z, a4.w};
+            const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = j0 + 16 * jt + 4 * lq + r;
+              const float d = j <= i ? ai - aj[r] : 0.f;
+              const float e = __builtin_amdgcn_exp2f(d);
+              v[4 * jt + r] = j <= i ? gt[jt][r] * (e * bb[r]) : 0.f;
+            }
           }
         }
+        const bf16x8 bop = as_bf16x8(make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]),
+                                                pack2(v[6], v[7])));
+  #pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[s][mt] = mfma(aX[mt], bop, acc[s][mt]);
       }
-      const bf16x8 bop = as_bf16x8(make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]),
-                                              pack2(v[6], v[7])));
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[s][mt] = mfma(aX[mt], bop, acc[s][mt]);
     }
-  }
-  // inter-chunk term: Y^T[p][i] += exp(A_cum_i) sum_n S_in[p][n] C[i][n]
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int row = 16 * mt + lr;
-    bf16x8 aS[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) aS[ks] = as_bf16x8(Ss[row][(4 * ks + lq) ^ (row % 8)]);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) a = mfma(aS[ks], Cop[s][ks], a);
-      const float ei = __builtin_amdgcn_exp2f(A2[16 * kst[s] + lr]);
-      acc[s][mt] += a * ei;
-    }
-  }
-  // epilogue: + D x (x from the staged rows), store y[i][p0..p0+3]
-  const float Dh = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int il = 16 * kst[s] + lr;
-    const int64_t ti = t0 + il;
-    if (ti >= p.L) continue;
-#pragma unroll
+    // inter-chunk term: Y^T[p][i] += exp(A_cum_i) sum_n S_in[p][n] C[i][n]
+  #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int p0 = 16 * mt + 4 * lq;
-      const uint2 xv = *(const uint2*)&Xs[il][p0];
-      float o[4] = {acc[s][mt][0], acc[s][mt][1], acc[s][mt][2], acc[s][mt][3]};
-      o[0] = __builtin_fmaf(Dh, __uint_as_float(xv.x << 16), o[0]);
-      o[1] = __builtin_fmaf(Dh, __uint_as_float(xv.x & 0xFFFF0000u), o[1]);
-      o[2] = __builtin_fmaf(Dh, __uint_as_float(xv.y << 16), o[2]);
-      o[3] = __builtin_fmaf(Dh, __uint_as_float(xv.y & 0xFFFF0000u), o[3]);
-      const int64_t off = b * p.ys_b + ti * p.ys_t + h * p.ys_h + p0;
-      if (p.y_f32) *(float4*)((float*)p.y + off) = make_float4(o[0], o[1], o[2], o[3]);
-      else *(uint2*)((uint16_t*)p.y + off) = make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+      const int row = 16 * mt + lr;
+      bf16x8 aS[KS];
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) aS[ks] = as_bf16x8(Ss[row][(4 * ks + lq) ^ (row % 8)]);
+  #pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a = mfma(aS[ks], Cop[s][ks], a);
+        const float ei = __builtin_amdgcn_exp2f(A2[16 * kst[s] + lr]);
+        acc[s][mt] += a * ei;
+      }
     }
+    // epilogue: + D x (x from the staged rows), store y[i][p0..p0+3]
+    const float Dh = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
+  #pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int il = 16 * kst[s] + lr;
+      const int64_t ti = t0 + il;
+      if (ti >= p.L) continue;
+  #pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int p0 = 16 * mt + 4 * lq;
+        const uint2 xv = *(const uint2*)&Xs[il][p0];
+        float o[4] = {acc[s][mt][0], acc[s][mt][1], acc[s][mt][2], acc[s][mt][3]};
+        o[0] = __builtin_fmaf(Dh, __uint_as_float(xv.x << 16), o[0]);
+        o[1] = __builtin_fmaf(Dh, __uint_as_float(xv.x & 0xFFFF0000u), o[1]);
+        o[2] = __builtin_fmaf(Dh, __uint_as_float(xv.y << 16), o[2]);
+        o[3] = __builtin_fmaf(Dh, __uint_as_float(xv.y & 0xFFFF0000u), o[3]);
+        const int64_t off = b * p.ys_b + ti * p.ys_t + h * p.ys_h + p0;
+        if (p.y_f32) *(float4*)((float*)p.y + off) = make_float4(o[0], o[1], o[2], o[3]);
+        else *(uint2*)((uint16_t*)p.y + off) = make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+      }
+    }
+    __syncthreads();  // head h's LDS rows are read; the next head may be staged
   }
 }
 
@@ -533,20 +556,28 @@ hipError_t launch_ssd_state_passing(const SSDParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_ssd_chunk_scan(const SSDParams& p, hipStream_t stream) {
-  const unsigned nb = (unsigned)(p.batch * p.nchunks * p.H);
+  // Heads per workgroup: about 1024 workgroups (two rounds at two per CU),
+  // heads of one group only.
+  const int64_t hpg = p.H / p.G;
+  const int64_t units = p.batch * p.nchunks * p.H;
+  int64_t hb = units / 1024;
+  hb = hb < 1 ? 1 : (hb > 8 ? 8 : hb);
+  hb = hb > hpg ? hpg : hb;
+  const int HB = (int)hb, nhb = (int)((hpg + hb - 1) / hb);
+  const unsigned nb = (unsigned)(p.batch * p.nchunks * p.G * nhb);
   // (chunk, states) pairs whose staging fits in LDS; the host rejects chunk
   // 256 with 256 states
   if (p.N == 64) {
-    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 1>), dim3(nb), dim3(128), 0, stream, p);
-    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 1>), dim3(nb), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_scan_kernel<256, 1>), dim3(nb), dim3(512), 0, stream, p);
+    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 1>), dim3(nb), dim3(128), 0, stream, p, HB, nhb);
+    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 1>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
+    else hipLaunchKernelGGL((chunk_scan_kernel<256, 1>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
   } else if (p.N == 128) {
-    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 2>), dim3(nb), dim3(128), 0, stream, p);
-    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 2>), dim3(nb), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_scan_kernel<256, 2>), dim3(nb), dim3(512), 0, stream, p);
+    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 2>), dim3(nb), dim3(128), 0, stream, p, HB, nhb);
+    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 2>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
+    else hipLaunchKernelGGL((chunk_scan_kernel<256, 2>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
   } else {
-    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 4>), dim3(nb), dim3(128), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_scan_kernel<128, 4>), dim3(nb), dim3(256), 0, stream, p);
+    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 4>), dim3(nb), dim3(128), 0, stream, p, HB, nhb);
+    else hipLaunchKernelGGL((chunk_scan_kernel<128, 4>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
   }
   return hipGetLastError();
 }
