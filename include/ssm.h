@@ -267,8 +267,9 @@ typedef struct {
  *   dB, dC : (batch, seqlen, ngroups, dstate) F32 contiguous
  *   dD     : (nheads) F32 contiguous                          if SSM_HAS_D
  *   dh0    : (batch, nheads, headdim, dstate) F32 contiguous  if SSM_HAS_H0
- * Flags: SSM_HAS_D, SSM_DISC_EULER, SSM_HAS_H0.  Supported: headdim 64,
- * dstate 64, chunk in {64, 128, 256}, nheads % ngroups == 0.  Every (batch,
+ * Flags: SSM_HAS_D, SSM_DISC_EULER, SSM_HAS_H0.  Supported: as the forward
+ * (headdim 64, dstate in {64, 128, 256}, chunk in {64, 128, 256} except
+ * dstate 256 with chunk 256, nheads % ngroups == 0).  Every (batch,
  * step, head or group) row of x, dy, B, C and dx, and h0 / dh0, must start
  * 16-byte aligned (SSM_ERR_ALIGN otherwise).  The sums over heads (dB, dC)
  * and over batch and time (dA, dD) are fixed-order sums of per-workgroup

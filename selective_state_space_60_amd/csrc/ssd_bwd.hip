@@ -58,9 +58,9 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kP = 64, kN = 64, kE = kP * kN;  // headdim, dstate, state entries
-constexpr int kPR = 64 + 4;                    // LDS row pitch (bf16) of staged rows
-constexpr int kNQ = kE / 1024;                 // 1024-entry blocks of one state
+constexpr int kP = 64;        // headdim
+constexpr int kN = 64;        // dstate of the fused dx/dB pass; larger states go by 64-wide blocks
+constexpr int kPR = 64 + 4;   // LDS row pitch (bf16) of staged 64-wide rows
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
@@ -104,17 +104,19 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t (*rows)[kPR], int s0
   return as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
 }
 
-// Block decode shared by the dc and dx kernels: (b, chunk c, group g, head
-// block hbk); heads h_lo .. h_lo + nh - 1.
+// Block decode shared by the passes: (b, chunk c, group g, head block hbk,
+// 64-wide block nbk of the states when `nblk` > 1); heads h_lo .. h_lo + nh - 1.
 struct HeadBlock {
   int64_t b, c, g, h_lo;
-  int hbk, nh;
+  int hbk, nh, nbk;
 };
 
-__device__ __forceinline__ HeadBlock head_block(const SSDBwdParams& q) {
+__device__ __forceinline__ HeadBlock head_block(const SSDBwdParams& q, int nblk = 1) {
   const SSDParams& p = q.f;
   HeadBlock r;
   int64_t bid = blockIdx.x;
+  r.nbk = (int)(bid % nblk);
+  bid /= nblk;
   r.hbk = (int)(bid % q.nhb);
   bid /= q.nhb;
   r.g = bid % p.G;
@@ -128,23 +130,25 @@ __device__ __forceinline__ HeadBlock head_block(const SSDBwdParams& q) {
   return r;
 }
 
-// Stage Q rows of 64 bf16 (zero rows at or past L) into rows[Q][kPR].
-template <int Q, int NTH>
-__device__ __forceinline__ void stage_rows(uint16_t (*rows)[kPR], const uint16_t* src, int64_t st, int64_t t0,
+// Stage Q rows of W bf16 (zero rows at or past L) into rows[Q][W + 4].
+template <int Q, int NTH, int W = 64>
+__device__ __forceinline__ void stage_rows(uint16_t (*rows)[W + 4], const uint16_t* src, int64_t st, int64_t t0,
                                            int64_t L) {
-  constexpr int NTX = Q * 8 / NTH;
+  constexpr int PC = W / 8;  // 16-byte pieces per row
+  constexpr int NTX = Q * PC / NTH;
+  static_assert(NTX * NTH == Q * PC, "whole pieces per thread");
   uint4 v[NTX];
 #pragma unroll
   for (int u = 0; u < NTX; ++u) {
     const int task = threadIdx.x + NTH * u;
-    const int j = task / 8, cb = (task % 8) * 8;
+    const int j = task / PC, cb = (task % PC) * 8;
     const int64_t tr = t0 + j < L ? t0 + j : L - 1;
     v[u] = *(const uint4*)(src + tr * st + cb);
   }
 #pragma unroll
   for (int u = 0; u < NTX; ++u) {
     const int task = threadIdx.x + NTH * u;
-    const int j = task / 8, cb = (task % 8) * 8;
+    const int j = task / PC, cb = (task % PC) * 8;
     *(uint4*)&rows[j][cb] = t0 + j < L ? v[u] : make_uint4(0, 0, 0, 0);
   }
 }
@@ -165,39 +169,41 @@ __device__ __forceinline__ uint2 row4(const uint16_t* src, int64_t st, int64_t t
 
 // ------------------------------------------------- reverse state passing
 
-// Block = (b, h, 16 rows p0 .. p0+15 of the 64 x 64 state); thread t holds
-// row p0 + t/16, columns n0 = 4*(t%16) .. +3.  Forward: S_in[c] in fp32 and,
+// Block = (b, h, 16 rows p0 .. p0+15 and 64 columns nc0 .. nc0+63 of the
+// 64 x N state); thread t holds row p0 + t/16, columns nc0 + 4*(t%16) .. +3.  Forward: S_in[c] in fp32 and,
 // through an LDS transpose, bf16 [n][p].  Backward: G = 0; for c = last .. 0:
 // dS_loc[c] = G (bf16, both layouts), partial <S_in[c], G> exp(A_cum_end[c]),
 // G = dS[c] + exp(A_cum_end[c]) G.  The transpose tiles and the partial sums
 // are double-buffered, so each chunk needs one barrier.
 __global__ __launch_bounds__(256) void bwd_state_kernel(SSDBwdParams q) {
   const SSDParams& p = q.f;
-  __shared__ __attribute__((aligned(16))) uint16_t T[2][kN][16 + 4];  // [n][p - p0]
+  __shared__ __attribute__((aligned(16))) uint16_t T[2][64][16 + 4];  // [n - nc0][p - p0]
   __shared__ float red[2][4];
+  const int nblk = (int)(p.N / 64), nq = 4 * nblk;
   int64_t bid = blockIdx.x;
-  const int qb = (int)(bid % kNQ);
-  bid /= kNQ;
+  const int qb = (int)(bid % nq);
+  bid /= nq;
   const int64_t h = bid % p.H, b = bid / p.H;
   const int tid = threadIdx.x;
-  const int p0 = qb * 16, pl = tid / 16, n0 = 4 * (tid % 16);
-  const int e0 = (p0 + pl) * kN + n0;
-  const int tn = tid / 4, tq = 4 * (tid % 4);  // transposed store: row n = tn, p0 + tq .. +3
+  const int p0 = (qb / nblk) * 16, nc0 = 64 * (qb % nblk), pl = tid / 16, nl = 4 * (tid % 16);
+  const int64_t E = kP * p.N;
+  const int e0 = (p0 + pl) * (int)p.N + nc0 + nl;
+  const int tn = tid / 4, tq = 4 * (tid % 4);  // transposed store: row n = nc0 + tn, p0 + tq .. +3
   const float* Ac = p.A_cum + (b * p.H + h) * p.Lp;
-  const int64_t cs = p.H * kE;
-  const int64_t base = (b * p.nchunks * p.H + h) * kE;
+  const int64_t cs = p.H * E;
+  const int64_t base = (b * p.nchunks * p.H + h) * E;
   const int64_t nc = p.nchunks;
   auto put_T = [&](int buf, float4 v) {
-    T[buf][n0 + 0][pl] = f2bf(v.x);
-    T[buf][n0 + 1][pl] = f2bf(v.y);
-    T[buf][n0 + 2][pl] = f2bf(v.z);
-    T[buf][n0 + 3][pl] = f2bf(v.w);
+    T[buf][nl + 0][pl] = f2bf(v.x);
+    T[buf][nl + 1][pl] = f2bf(v.y);
+    T[buf][nl + 2][pl] = f2bf(v.z);
+    T[buf][nl + 3][pl] = f2bf(v.w);
   };
   auto store_T = [&](int buf, uint16_t* dst) {
-    *(uint2*)(dst + tn * kP + p0 + tq) = *(const uint2*)&T[buf][tn][tq];
+    *(uint2*)(dst + (nc0 + tn) * kP + p0 + tq) = *(const uint2*)&T[buf][tn][tq];
   };
   float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (p.h0) S = *(const float4*)(p.h0 + (b * p.H + h) * kE + e0);
+  if (p.h0) S = *(const float4*)(p.h0 + (b * p.H + h) * E + e0);
   float4 sl = *(const float4*)(p.states + base + e0);
   int buf = 0;
   for (int64_t c = 0; c < nc; ++c) {
@@ -235,7 +241,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(SSDBwdParams q) {
     __syncthreads();
     store_T(buf, q.dSlT + o);
     if (tid == 0)
-      q.pAend[((b * p.H + h) * nc + c) * kNQ + qb] =
+      q.pAend[((b * p.H + h) * nc + c) * nq + qb] =
           dec * (((red[buf][0] + red[buf][1]) + red[buf][2]) + red[buf][3]);
     buf ^= 1;
     G.x = __builtin_fmaf(dec, G.x, d.x);
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(SSDBwdParams q) {
     G.z = __builtin_fmaf(dec, G.z, d.z);
     G.w = __builtin_fmaf(dec, G.w, d.w);
   }
-  if (q.dh0) *(float4*)(q.dh0 + (b * p.H + h) * kE + e0) = G;
+  if (q.dh0) *(float4*)(q.dh0 + (b * p.H + h) * E + e0) = G;
 }
 
 // -------------------------------------------------------------- dC pass
@@ -262,20 +268,23 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
   __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][kPR];   // B rows of the group: [j][n]
   __shared__ __attribute__((aligned(16))) uint16_t Cs[Q][kPR];   // C rows of the group: [i][n]
   __shared__ __attribute__((aligned(16))) uint16_t Ys[Q][kPR];   // dy rows of the head: [i][p]
-  __shared__ __attribute__((aligned(16))) uint16_t SsT[kN][kPR]; // S_in^T of the head: [n][p]
+  __shared__ __attribute__((aligned(16))) uint16_t SsT[64][kPR]; // S_in^T of the head: [n][p]
   __shared__ __attribute__((aligned(16))) float A2[Q];  // A_cum * log2(e)
   __shared__ __attribute__((aligned(16))) float bj[Q];  // beta
   __shared__ __attribute__((aligned(16))) float tb[Q];  // exp(A_cum[j|31] - A_cum[j]) beta_j
-  const HeadBlock hb = head_block(q);
+  // one 64-wide block nc0 .. nc0+63 of the states: dC's columns, and partial
+  // sums over those states of C B^T and of C_i . (inter-chunk dC_i)
+  const HeadBlock hb = head_block(q, (int)(q.f.N / 64));
   const int64_t b = hb.b, c = hb.c, g = hb.g;
+  const int64_t N = p.N, nc0 = 64 * hb.nbk, E = kP * N;
   const int tid = threadIdx.x;
   const int64_t t0 = c * Q;
   const int wv = __builtin_amdgcn_readfirstlane(tid / 64), l = tid % 64, lr = l % 16, lq = l / 16;
   const int kst[2] = {wv, NSTRIP - 1 - wv};
   const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
 
-  stage_rows<Q, NTH>(Bs, (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g, p.Bs_t, t0, p.L);
-  stage_rows<Q, NTH>(Cs, (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g, p.Cs_t, t0, p.L);
+  stage_rows<Q, NTH>(Bs, (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g + nc0, p.Bs_t, t0, p.L);
+  stage_rows<Q, NTH>(Cs, (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g + nc0, p.Cs_t, t0, p.L);
   f32x4 sum[2][4];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
@@ -290,7 +299,7 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
     // every global read of this head, issued together
     stage_rows<Q, NTH>(Xs, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
     stage_rows<Q, NTH>(Ys, (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h, q.dys_t, t0, p.L);
-    stage_rows<kN, NTH>(SsT, q.SinT + ((b * p.nchunks + c) * p.H + h) * kE, kP, 0, kN);
+    stage_rows<64, NTH>(SsT, q.SinT + ((b * p.nchunks + c) * p.H + h) * E + nc0 * kP, kP, 0, 64);
     for (int t = tid; t < Q; t += NTH) {
       A2[t] = Ac[t] * kLog2e;
       bj[t] = be[t];
@@ -396,17 +405,17 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
         sum[s][nt] += acc[s][nt] + a;
       }
       const float v = sum_rows(dot + rsum[s]);
-      if (lq == 0) q.dAcA[(b * p.H + h) * p.Lp + t0 + il] = v;
+      if (lq == 0) q.dAcA[((hb.nbk * p.batch + b) * p.H + h) * p.Lp + t0 + il] = v;
     }
   }
   // the head block's dC terms
-  float* dst = q.pdC + ((int64_t)hb.hbk * p.batch + b) * p.L * p.G * kN;
+  float* dst = q.pdC + ((int64_t)hb.hbk * p.batch + b) * p.L * p.G * N;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int64_t ti = t0 + 16 * kst[s] + lr;
     if (ti < p.L)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) *(f32x4*)(dst + (ti * p.G + g) * kN + 16 * nt + 4 * lq) = sum[s][nt];
+      for (int nt = 0; nt < 4; ++nt) *(f32x4*)(dst + (ti * p.G + g) * N + nc0 + 16 * nt + 4 * lq) = sum[s][nt];
   }
 }
 
@@ -461,7 +470,7 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
     const int64_t h = hb.h_lo + k;
     const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
     const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
-    const int64_t so = ((b * p.nchunks + c) * p.H + h) * kE;
+    const int64_t so = ((b * p.nchunks + c) * p.H + h) * (kP * kN);
     const float Dk = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
     __syncthreads();  // the previous head is done with the staged rows and tables
     // every global read of this head, issued together
@@ -621,6 +630,301 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
   }
 }
 
+// ------------------------------------------------- dx and dB, N > 64 states
+
+// dx, dbeta and W's column sums for N = 64 NB states: bwd_dx_kernel without
+// the dB terms (which bwd_db_kernel forms per 64-wide block of the states).
+// C B^T and dS_loc B_j contract over all N states in KS = N/32 slices; C and
+// dS_loc are staged N wide.
+template <int Q, int NB>
+__global__ __launch_bounds__(2 * Q) void bwd_dxn_kernel(SSDBwdParams q) {
+  constexpr int NTH = 2 * Q, NSTRIP = Q / 16, NIB = Q / 32;
+  constexpr int N = 64 * NB, KS = N / 32, PRN = N + 4;
+  const SSDParams& p = q.f;
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[Q][PRN];   // C rows of the group: [i][n]
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[Q][kPR];   // dy rows of the head: [i][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][kPR];   // x rows of the head: [j][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Sl[kP][PRN];  // dS_loc of the head: [p][n]
+  __shared__ __attribute__((aligned(16))) float A2[Q];
+  __shared__ __attribute__((aligned(16))) float bj[Q];
+  __shared__ __attribute__((aligned(16))) float U[Q];            // exp(A_cum_i - A_cum_(i & ~31))
+  const HeadBlock hb = head_block(q);
+  const int64_t b = hb.b, c = hb.c, g = hb.g;
+  const int tid = threadIdx.x;
+  const int64_t t0 = c * Q;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64), l = tid % 64, lr = l % 16, lq = l / 16;
+  const int kst[2] = {wv, NSTRIP - 1 - wv};
+  const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
+
+  stage_rows<Q, NTH, N>(Cs, (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g, p.Cs_t, t0, p.L);
+  const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
+  bf16x8 bop[2][KS];  // B operands: B[j][32*ks + 8*lq .. +7] of the strips' columns
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bop[s][ks] = row8(Bsrc, p.Bs_t, t0 + 16 * kst[s] + lr, p.L, 32 * ks + 8 * lq);
+
+  for (int k = 0; k < hb.nh; ++k) {
+    const int64_t h = hb.h_lo + k;
+    const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
+    const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
+    const int64_t so = ((b * p.nchunks + c) * p.H + h) * (kP * N);
+    const float Dk = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
+    __syncthreads();  // the previous head is done with the staged rows and tables
+    stage_rows<Q, NTH>(Ys, (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h, q.dys_t, t0, p.L);
+    stage_rows<Q, NTH>(Xs, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
+    stage_rows<kP, NTH, N>(Sl, q.dSl + so, N, 0, kP);
+    for (int t = tid; t < Q; t += NTH) {
+      A2[t] = Ac[t] * kLog2e;
+      bj[t] = be[t];
+    }
+    __syncthreads();
+    for (int t = tid; t < Q; t += NTH) U[t] = __builtin_amdgcn_exp2f(A2[t] - A2[t & ~31]);
+    __syncthreads();
+
+    auto strip = [&](auto S) {
+      constexpr int s = decltype(S)::value;
+      const int jl = 16 * kst[s] + lr;
+      const int64_t tj = t0 + jl;
+      const int diag = (16 * kst[s]) / 32;
+      bf16x8 xop[2];
+      uint2 xE[4];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) xop[ks] = as_bf16x8(*(const uint4*)&Xs[jl][32 * ks + 8 * lq]);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) xE[pt] = *(const uint2*)&Xs[jl][16 * pt + 4 * lq];
+      const float aj = A2[jl], bjj = bj[jl];
+
+      // chunk-state term of R_j
+      f32x4 accX[4];
+      float tj_val;
+      {
+        const float w = __builtin_amdgcn_exp2f(A2[Q - 1] - aj);
+        float tp = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          f32x4 a = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            a = mfma(as_bf16x8(*(const uint4*)&Sl[16 * t + lr][32 * ks + 8 * lq]), bop[s][ks], a);
+          float xv[4];
+          unpack4(xE[t], xv);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tp = __builtin_fmaf(xv[r], a[r], tp);
+          accX[t] = a * w;
+        }
+        tj_val = sum_rows(tp) * (w * bjj);
+      }
+
+      float csum = 0.f;  // this lane's part of W's column sum
+      for (int ib = diag; ib < NIB; ++ib) {
+        const int i0 = 32 * ib;
+        f32x4 ct[2], gt[2];
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          f32x4 a = zero4(), d = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            a = mfma(as_bf16x8(*(const uint4*)&Cs[i0 + 16 * it + lr][32 * ks + 8 * lq]), bop[s][ks], a);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            d = mfma(as_bf16x8(*(const uint4*)&Ys[i0 + 16 * it + lr][32 * ks + 8 * lq]), xop[ks], d);
+          ct[it] = a;
+          gt[it] = d;
+        }
+        float m[8];
+        if (ib > diag) {
+          const float vj = __builtin_amdgcn_exp2f(A2[i0] - aj), vb = vj * bjj;
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const float4 u4 = *(const float4*)&U[i0 + 16 * it + 4 * lq];
+            const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              m[4 * it + r] = ct[it][r] * (u[r] * vj);
+              csum = __builtin_fmaf(gt[it][r] * (u[r] * vb), ct[it][r], csum);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const float4 a4 = *(const float4*)&A2[i0 + 16 * it + 4 * lq];
+            const float ai[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = i0 + 16 * it + 4 * lq + r;
+              const bool ok = i >= jl;
+              const float f = __builtin_amdgcn_exp2f(ok ? ai[r] - aj : 0.f);
+              m[4 * it + r] = ok ? ct[it][r] * f : 0.f;
+              csum = __builtin_fmaf(ok ? gt[it][r] * (f * bjj) : 0.f, ct[it][r], csum);
+            }
+          }
+        }
+        const bf16x8 mop = as_bf16x8(make_uint4(pack2(m[0], m[1]), pack2(m[2], m[3]), pack2(m[4], m[5]),
+                                                pack2(m[6], m[7])));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) accX[t] = mfma(tr_operand(Ys, i0, 16 * t, tr_row, tr_col), mop, accX[t]);
+      }
+
+      float db = 0.f, dd = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        float xv[4], yv[4], o[4];
+        unpack4(xE[pt], xv);
+        unpack4(*(const uint2*)&Ys[jl][16 * pt + 4 * lq], yv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          db = __builtin_fmaf(xv[r], accX[pt][r], db);
+          dd = __builtin_fmaf(xv[r], yv[r], dd);
+          o[r] = __builtin_fmaf(bjj, accX[pt][r], Dk * yv[r]);
+        }
+        if (tj < p.L) {
+          const int64_t off = b * q.dxs_b + tj * q.dxs_t + h * q.dxs_h + 16 * pt + 4 * lq;
+          if (q.dx_f32) *(float4*)((float*)q.dx + off) = make_float4(o[0], o[1], o[2], o[3]);
+          else *(uint2*)((uint16_t*)q.dx + off) = make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+        }
+      }
+      db = sum_rows(db);
+      dd = sum_rows(dd);
+      const float wc = sum_rows(csum);
+      if (lq == 0) {
+        const int64_t o = (b * p.H + h) * p.Lp + tj;
+        q.dbeta[o] = db;
+        q.Tj[o] = tj_val;
+        q.dDj[o] = dd;
+        q.dAcB[o] = -wc - tj_val;
+      }
+    };
+    strip(std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    strip(std::integral_constant<int, 1>{});
+  }
+}
+
+// dB for one 64-wide block nc0 .. nc0+63 of N > 64 states: per head,
+// DB^T = w_j beta_j dS_loc^T x_j (A: the block's rows of dS_loc^T), then for
+// the 32-row blocks of i >= j, G'[i][j] = dy_i . x_j, E = G' decay_ij beta_j
+// (decay as in bwd_dx_kernel) and DB^T += C^T E (A: transposed C rows of the
+// block); added over the block's heads.
+template <int Q>
+__global__ __launch_bounds__(2 * Q) void bwd_db_kernel(SSDBwdParams q) {
+  constexpr int NTH = 2 * Q, NSTRIP = Q / 16, NIB = Q / 32;
+  const SSDParams& p = q.f;
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[Q][kPR];    // the block's columns of C: [i][n]
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[Q][kPR];    // dy rows of the head
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][kPR];    // x rows of the head
+  __shared__ __attribute__((aligned(16))) uint16_t SlT[64][kPR];  // the block's rows of dS_loc^T: [n][p]
+  __shared__ __attribute__((aligned(16))) float A2[Q];
+  __shared__ __attribute__((aligned(16))) float bj[Q];
+  __shared__ __attribute__((aligned(16))) float U[Q];
+  const HeadBlock hb = head_block(q, (int)(q.f.N / 64));
+  const int64_t b = hb.b, c = hb.c, g = hb.g;
+  const int64_t N = p.N, nc0 = 64 * hb.nbk;
+  const int tid = threadIdx.x;
+  const int64_t t0 = c * Q;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64), l = tid % 64, lr = l % 16, lq = l / 16;
+  const int kst[2] = {wv, NSTRIP - 1 - wv};
+  const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
+
+  stage_rows<Q, NTH>(Cs, (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g + nc0, p.Cs_t, t0, p.L);
+  f32x4 sumB[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) sumB[s][nt] = zero4();
+
+  for (int k = 0; k < hb.nh; ++k) {
+    const int64_t h = hb.h_lo + k;
+    const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
+    const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
+    const int64_t so = ((b * p.nchunks + c) * p.H + h) * (kP * N);
+    __syncthreads();
+    stage_rows<Q, NTH>(Ys, (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h, q.dys_t, t0, p.L);
+    stage_rows<Q, NTH>(Xs, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
+    stage_rows<64, NTH>(SlT, q.dSlT + so + nc0 * kP, kP, 0, 64);
+    for (int t = tid; t < Q; t += NTH) {
+      A2[t] = Ac[t] * kLog2e;
+      bj[t] = be[t];
+    }
+    __syncthreads();
+    for (int t = tid; t < Q; t += NTH) U[t] = __builtin_amdgcn_exp2f(A2[t] - A2[t & ~31]);
+    __syncthreads();
+
+    auto strip = [&](auto S) {
+      constexpr int s = decltype(S)::value;
+      const int jl = 16 * kst[s] + lr;
+      const int diag = (16 * kst[s]) / 32;
+      bf16x8 xop[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) xop[ks] = as_bf16x8(*(const uint4*)&Xs[jl][32 * ks + 8 * lq]);
+      const float aj = A2[jl], bjj = bj[jl];
+      const float wb = __builtin_amdgcn_exp2f(A2[Q - 1] - aj) * bjj;
+      f32x4 accB[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f32x4 d = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          d = mfma(as_bf16x8(*(const uint4*)&SlT[16 * t + lr][32 * ks + 8 * lq]), xop[ks], d);
+        accB[t] = d * wb;
+      }
+      for (int ib = diag; ib < NIB; ++ib) {
+        const int i0 = 32 * ib;
+        f32x4 gt[2];
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          f32x4 d = zero4();
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            d = mfma(as_bf16x8(*(const uint4*)&Ys[i0 + 16 * it + lr][32 * ks + 8 * lq]), xop[ks], d);
+          gt[it] = d;
+        }
+        float e[8];
+        if (ib > diag) {
+          const float vb = __builtin_amdgcn_exp2f(A2[i0] - aj) * bjj;
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const float4 u4 = *(const float4*)&U[i0 + 16 * it + 4 * lq];
+            const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e[4 * it + r] = gt[it][r] * (u[r] * vb);
+          }
+        } else {
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const float4 a4 = *(const float4*)&A2[i0 + 16 * it + 4 * lq];
+            const float ai[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = i0 + 16 * it + 4 * lq + r;
+              const bool ok = i >= jl;
+              const float f = __builtin_amdgcn_exp2f(ok ? ai[r] - aj : 0.f);
+              e[4 * it + r] = ok ? gt[it][r] * (f * bjj) : 0.f;
+            }
+          }
+        }
+        const bf16x8 eop = as_bf16x8(make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]),
+                                                pack2(e[6], e[7])));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) accB[t] = mfma(tr_operand(Cs, i0, 16 * t, tr_row, tr_col), eop, accB[t]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) sumB[s][nt] += accB[nt];
+    };
+    strip(std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    strip(std::integral_constant<int, 1>{});
+  }
+  float* dst = q.pdB + ((int64_t)hb.hbk * p.batch + b) * p.L * p.G * N;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int64_t tj = t0 + 16 * kst[s] + lr;
+    if (tj < p.L)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) *(f32x4*)(dst + (tj * p.G + g) * N + nc0 + 16 * nt + 4 * lq) = sumB[s][nt];
+  }
+}
+
 // ----------------------------------------------------------------- finish
 
 // dbeta/dA of beta = expm1(a)/A, a = delta A: delta^2 phi'(a) with
@@ -668,13 +972,14 @@ __global__ __launch_bounds__(Q) void bwd_finish_kernel(SSDBwdParams q) {
   const bool ok = tg < p.L;
   const int64_t o = (b * p.H + h) * p.Lp + tg;
   const float beta = p.beta[o], dbt = q.dbeta[o];
-  float v = q.dAcA[o] + q.dAcB[o];
+  const int nblk = (int)(p.N / 64), nq = 4 * nblk;
+  float v = q.dAcB[o];
+  for (int k = 0; k < nblk; ++k) v += q.dAcA[k * p.batch * p.H * p.Lp + o];
   const float tsum = block_sum<Q>(q.Tj[o], red);
   if (t == Q - 1) {
-    const float* pa = q.pAend + ((b * p.H + h) * p.nchunks + c) * kNQ;
+    const float* pa = q.pAend + ((b * p.H + h) * p.nchunks + c) * nq;
     float e = 0.f;
-#pragma unroll
-    for (int k = 0; k < kNQ; ++k) e += pa[k];
+    for (int k = 0; k < nq; ++k) e += pa[k];
     v += tsum + e;
   }
   // da_t = sum of v over the steps t .. Q-1 of the chunk (Hillis-Steele, two buffers)
@@ -716,9 +1021,16 @@ __global__ __launch_bounds__(Q) void bwd_finish_kernel(SSDBwdParams q) {
 template <int Q>
 void launch_q(const SSDBwdParams& q, hipStream_t stream) {
   const SSDParams& p = q.f;
+  const int nblk = (int)(p.N / 64);
   const unsigned nb = (unsigned)(p.batch * p.nchunks * p.G * q.nhb);
-  hipLaunchKernelGGL(bwd_dc_kernel<Q>, dim3(nb), dim3(2 * Q), 0, stream, q);
-  hipLaunchKernelGGL(bwd_dx_kernel<Q>, dim3(nb), dim3(2 * Q), 0, stream, q);
+  hipLaunchKernelGGL(bwd_dc_kernel<Q>, dim3(nb * nblk), dim3(2 * Q), 0, stream, q);
+  if (nblk == 1) {
+    hipLaunchKernelGGL(bwd_dx_kernel<Q>, dim3(nb), dim3(2 * Q), 0, stream, q);
+  } else {
+    if (nblk == 2) hipLaunchKernelGGL((bwd_dxn_kernel<Q, 2>), dim3(nb), dim3(2 * Q), 0, stream, q);
+    else if constexpr (Q <= 128) hipLaunchKernelGGL((bwd_dxn_kernel<Q, 4>), dim3(nb), dim3(2 * Q), 0, stream, q);
+    hipLaunchKernelGGL(bwd_db_kernel<Q>, dim3(nb * nblk), dim3(2 * Q), 0, stream, q);
+  }
   hipLaunchKernelGGL(bwd_finish_kernel<Q>, dim3((unsigned)(p.batch * p.H * p.nchunks)), dim3(Q), 0, stream, q);
 }
 
@@ -743,11 +1055,11 @@ hipError_t launch_ssd_bwd(const SSDBwdParams& q, float* dA, float* dB, float* dC
   f2.states = q.dS;
   f2.state_coef = 1;
   if ((e = launch_ssd_chunk_state(f2, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_state_kernel, dim3((unsigned)(p.batch * p.H * kNQ)), dim3(256), 0, stream, q);
+  hipLaunchKernelGGL(bwd_state_kernel, dim3((unsigned)(p.batch * p.H * 4 * (p.N / 64))), dim3(256), 0, stream, q);
   if (p.Q == 64) launch_q<64>(q, stream);
   else if (p.Q == 128) launch_q<128>(q, stream);
   else launch_q<256>(q, stream);
-  const int64_t blgn = p.batch * p.L * p.G * kN;
+  const int64_t blgn = p.batch * p.L * p.G * p.N;
   launch_fixed_order_sum(q.pdB, dB, blgn, q.nhb, blgn, stream);
   launch_fixed_order_sum(q.pdC, dC, blgn, q.nhb, blgn, stream);
   launch_fixed_order_sum(q.pA, dA, p.H, p.batch * p.nchunks, p.H, stream);

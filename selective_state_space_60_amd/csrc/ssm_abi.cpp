@@ -341,7 +341,7 @@ constexpr uint32_t kSSDBwdFlags = SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0;
 struct SSDBwdPlan {
   SSDPlan f;
   int HB = 1, nhb = 1;
-  int64_t ws_state = 0, ws_half = 0, ws_aend = 0, ws_step = 0, ws_part = 0, ws_pdb = 0, ws_total = 0;
+  int64_t ws_state = 0, ws_half = 0, ws_aend = 0, ws_step = 0, ws_acA = 0, ws_part = 0, ws_pdb = 0, ws_total = 0;
 };
 
 // The forward problem of a backward descriptor (dx stands in for y: both are
@@ -370,10 +370,12 @@ SSDBwdPlan plan_ssd_bwd(const ssm_ssd_bwd_desc& d) {
   pl.ws_half = round256(E * 2);
   pl.ws_aend = round256(d.batch * d.nheads * nc * (d.headdim * d.dstate / 1024) * 4);
   pl.ws_step = round256(d.batch * d.nheads * pl.f.Lp * 4);
+  pl.ws_acA = round256((d.dstate / 64) * d.batch * d.nheads * pl.f.Lp * 4);  // one per 64-wide block of the states
   pl.ws_part = round256(d.batch * nc * d.nheads * 4);
   pl.ws_pdb = round256((int64_t)pl.nhb * d.batch * d.seqlen * d.ngroups * d.dstate * 4);
-  // A_cum, beta | states, dS, S32 | SinT, dSl, dSlT | pAend | dAcA, dAcB, dbeta, Tj, dDj | pA, pD | pdB, pdC
-  pl.ws_total = pl.f.ws_acum + pl.f.ws_beta + 3 * pl.ws_state + 3 * pl.ws_half + pl.ws_aend + 5 * pl.ws_step +
+  // A_cum, beta | states, dS, S32 | SinT, dSl, dSlT | pAend | dAcA | dAcB, dbeta, Tj, dDj | pA, pD | pdB, pdC
+  pl.ws_total = pl.f.ws_acum + pl.f.ws_beta + 3 * pl.ws_state + 3 * pl.ws_half + pl.ws_aend + pl.ws_acA +
+                4 * pl.ws_step +
                 2 * pl.ws_part + 2 * pl.ws_pdb;
   return pl;
 }
@@ -384,7 +386,6 @@ ssm_status validate_ssd_bwd_desc(const ssm_ssd_bwd_desc* d) {
   const ssm_ssd_desc f = ssd_fwd_of(*d);
   ssm_status s = validate_ssd_desc(&f);
   if (s) return s;
-  if (d->dstate != 64) return SSM_ERR_UNSUPPORTED;
   const int64_t blhp[4] = {d->batch, d->seqlen, d->nheads, d->headdim};
   const int64_t blh[3] = {d->batch, d->seqlen, d->nheads};
   const int64_t blgn[4] = {d->batch, d->seqlen, d->ngroups, d->dstate};
@@ -946,7 +947,7 @@ ssm_status ssm_ssd_bwd(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_ptrs* p, voi
   q.dSl = (uint16_t*)take(pl.ws_half);
   q.dSlT = (uint16_t*)take(pl.ws_half);
   q.pAend = (float*)take(pl.ws_aend);
-  q.dAcA = (float*)take(pl.ws_step);
+  q.dAcA = (float*)take(pl.ws_acA);
   q.dAcB = (float*)take(pl.ws_step);
   q.dbeta = (float*)take(pl.ws_step);
   q.Tj = (float*)take(pl.ws_step);

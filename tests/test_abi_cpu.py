@@ -309,8 +309,11 @@ def test_ssd_bwd_validation(mutate, status):
 
 
 def test_ssd_bwd_dstate_limit():
-    # 128 states are accepted by the forward, not (yet) by the backward
-    d, p = _ssd_bwd(N=128)
+    # as in the forward: 96 states are not a supported size, 256 states not with chunk 256
+    d, p = _ssd_bwd(N=96)
+    assert ssm.lib().ssm_ssd_bwd(ctypes.byref(d), ctypes.byref(p), 16 << 36, 1 << 40, None) == \
+        ssm.SSM_ERR_UNSUPPORTED
+    d, p = _ssd_bwd(N=256, Q=256)
     assert ssm.lib().ssm_ssd_bwd(ctypes.byref(d), ctypes.byref(p), 16 << 36, 1 << 40, None) == \
         ssm.SSM_ERR_UNSUPPORTED
 

@@ -1,7 +1,8 @@
 """GPU parity of ssm_ssd_bwd (the SSD backward on bf16 matrix cores) against
 the fp64 oracle backward (oracle.ssd_bwd).
 
-Inputs and dy are bf16 (exact in the oracle); the kernels round the
+Inputs and dy are bf16 (exact in the oracle), with 64, 128 and 256 states;
+the kernels round the
 intermediate matrices E, M, the chunk-entry states and their gradients to
 bf16 as matrix-core operands and accumulate in fp32, so every gradient is
 held to the bf16 bar rel-L2 <= 2e-2.
@@ -71,6 +72,25 @@ def test_ssd_bwd_chunks_and_ragged_lengths(chunk, seqlen):
                          ids=lambda kw: "_".join("%s%s" % i for i in sorted(kw.items())))
 def test_ssd_bwd_flags_and_heads(kw):
     _check(small(**kw), 3)
+
+
+@pytest.mark.parametrize("kw", [dict(dstate=128, chunk=64), dict(dstate=128, chunk=128), dict(dstate=128, chunk=256),
+                                dict(dstate=256, chunk=64), dict(dstate=256, chunk=128),
+                                dict(dstate=128, chunk=128, seqlen=1000, ngroups=2),
+                                dict(dstate=256, chunk=64, seqlen=77, nheads=3)],
+                         ids=lambda kw: "_".join("%s%s" % i for i in sorted(kw.items())))
+def test_ssd_bwd_larger_states(kw):
+    _check(small(**kw), 7)
+
+
+def test_ssd_bwd_larger_states_h0():
+    _check(small(dstate=128, chunk=128), 8, h0=True, dx_dtype=torch.float32)
+
+
+def test_ssd_bwd_2_7b_n128_batch1():
+    """The 2.7B-shaped layer with 128 states (chunk 128), one sequence of 4096
+    steps, 80 heads: every gradient against the oracle."""
+    _check(synth.ssd_spec(synth.SSD2_7B, batch=1, dstate=128, chunk=128), 9)
 
 
 def test_ssd_bwd_h0_and_f32_dx():
