@@ -60,7 +60,8 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kP = 64;        // headdim
 constexpr int kN = 64;        // dstate of the fused dx/dB pass; larger states go by 64-wide blocks
-constexpr int kPR = 64 + 4;   // LDS row pitch (bf16) of staged 64-wide rows
+constexpr int kPad = 4;       // LDS row padding (bf16) of staged rows
+constexpr int kPR = 64 + kPad;  // LDS row pitch (bf16) of staged 64-wide rows
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
@@ -130,9 +131,9 @@ __device__ __forceinline__ HeadBlock head_block(const SSDBwdParams& q, int nblk 
   return r;
 }
 
-// Stage Q rows of W bf16 (zero rows at or past L) into rows[Q][W + 4].
+// Stage Q rows of W bf16 (zero rows at or past L) into rows[Q][W + kPad].
 template <int Q, int NTH, int W = 64>
-__device__ __forceinline__ void stage_rows(uint16_t (*rows)[W + 4], const uint16_t* src, int64_t st, int64_t t0,
+__device__ __forceinline__ void stage_rows(uint16_t (*rows)[W + kPad], const uint16_t* src, int64_t st, int64_t t0,
                                            int64_t L) {
   constexpr int PC = W / 8;  // 16-byte pieces per row
   constexpr int NTX = Q * PC / NTH;
@@ -639,7 +640,7 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
 template <int Q, int NB>
 __global__ __launch_bounds__(2 * Q) void bwd_dxn_kernel(SSDBwdParams q) {
   constexpr int NTH = 2 * Q, NSTRIP = Q / 16, NIB = Q / 32;
-  constexpr int N = 64 * NB, KS = N / 32, PRN = N + 4;
+  constexpr int N = 64 * NB, KS = N / 32, PRN = N + kPad;
   const SSDParams& p = q.f;
   __shared__ __attribute__((aligned(16))) uint16_t Cs[Q][PRN];   // C rows of the group: [i][n]
   __shared__ __attribute__((aligned(16))) uint16_t Ys[Q][kPR];   // dy rows of the head: [i][p]
