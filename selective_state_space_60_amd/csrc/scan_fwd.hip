@@ -256,10 +256,12 @@ struct VecLoader {
   bool used[kSlots];     // the slot holds a piece
   uint32_t voff[kSlots];  // byte offset of this lane's 4 elements in the piece
   // Where the slot's 4 elements go in LDS: element i of tile buffer `buf` at
-  // dst[j] + buf * dbuf[j] + i * dpitch[j] (floats); elements i >= nok[j]
-  // (states past N) are staged as zeros.
+  // dst[j] + buf * dbuf[j] + i * dpitch[j] (floats).  A lane whose 4 states
+  // lie past N (N % 4 == 0 on this path, so a piece is all in or all out)
+  // stores nothing: those rows of B and C are cleared once (clear_rows).
   float* dst[kSlots];
-  int dbuf[kSlots], dpitch[kSlots], nok[kSlots];
+  int dbuf[kSlots], dpitch[kSlots];
+  bool st_ok[kSlots];
   Span y;
   uint32_t oy;
   bool y_ok;  // this lane's 4 channels exist
@@ -293,23 +295,38 @@ struct VecLoader {
     }
   }
 
-  __device__ __forceinline__ void stage(ScanSmem<KS>& s, const Tiles& tl, int buf, int it, const Set& st) const {
-    const bool ok = tl.row_ok(it, r);
+  // Rows past the stretch need no mask: their loads lie past the descriptor
+  // range of the stretch's last tile (or of a tile past it) and return zeros.
+  // (A mask per element costs a lane mask per element and slot, more than
+  // the scalar registers hold.)
+  __device__ __forceinline__ void stage(ScanSmem<KS>& s, const Tiles&, int buf, int, const Set& st) const {
 #pragma unroll
     for (int j = 0; j < kSlots; ++j) {
-      if (!used[j]) continue;
+      if (!used[j] || !st_ok[j]) continue;
       float e[4];
       unpack(st.v[j], e);
       float* d = dst[j] + buf * dbuf[j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d[i * dpitch[j]] = ok && i < nok[j] ? e[i] : 0.f;
+      for (int i = 0; i < 4; ++i) d[i * dpitch[j]] = e[i];
+    }
+  }
+
+  // Zeros into the B and C rows of states n_states .. G*KS-1 of both tile
+  // buffers (never staged); ordered before their first read by the barrier
+  // that follows the first stage.
+  __device__ __forceinline__ static void clear_rows(ScanSmem<KS>& s, int n_states) {
+    const int n0 = n_states < G * KS ? n_states : G * KS;
+    const int per_buf = (G * KS - n0) * TP;
+    for (int i = threadIdx.x; i < 2 * per_buf; i += NT) {
+      const int b = i / per_buf, k = i % per_buf;
+      s.bc[b][n0 + k / TP][k % TP] = make_float2(0.f, 0.f);
     }
   }
 
   // Set slot j up for piece `kd` (see VecLoader); `s` gives the LDS layout.
   __device__ __forceinline__ void place(ScanSmem<KS>& s, int j, int kd, int n_states) {
     used[j] = kd < kPieces;
-    nok[j] = 4;
+    st_ok[j] = true;
     if (kd == 0 || kd == 1) {
       dst[j] = kd == 0 ? &s.hx[0][4 * q][r].y : &s.hx[0][4 * q][r].x;
       dpitch[j] = 2 * HP;
@@ -326,7 +343,7 @@ struct VecLoader {
       dpitch[j] = 2 * TP;
       dbuf[j] = 2 * G * KS * TP;
       const int left = n_states - n0;
-      nok[j] = left < 0 ? 0 : (left > 4 ? 4 : left);
+      st_ok[j] = left >= 4;
     }
   }
 
@@ -618,8 +635,9 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   // of rows at a time.  The last tile's range ends at its last row's last
   // element (channel D-1 or state N-1 of the span): lanes of rows past the
   // stretch, or of channels / states past the end of the tensor's last row,
-  // read zeros.  (Rows past the stretch inside the tensor may also be read;
-  // the loaders stage them as zeros.)
+  // read zeros.  (With rows that overlap in memory, rows past the stretch
+  // can lie inside that range: the element loader, which such layouts take,
+  // stages them as zeros.)
   const int rows_last = tl.last_rows;
   typename std::conditional<VEC, VecLoader<BF16, KS>, ElemLoader<BF16, KS>>::type ld;
   if constexpr (VEC) {
@@ -647,6 +665,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
                      rows_last, MODE == 0);
     ld.oy = (uint32_t)((ld.r * p.ys_t + 4 * ld.q) * yesz);
     ld.y_ok = d0 + 4 * ld.q < p.D;
+    ld.clear_rows(s, (int)p.N);
   } else {
     ld.t = tid / G;
     ld.ch_ok = d0 + sg < p.D;
@@ -793,8 +812,11 @@ hipError_t launch_selective_scan(const ScanParams& p, hipStream_t stream) {
   bool vec = p.D % 4 == 0 && p.N % 4 == 0 && al(p.x, 4 * e) && al(p.delta, 4 * e) && al(p.y, 4 * ye) &&
              al(p.B, 4 * e) && al(p.C, 4 * e) && p.xs_b % 4 == 0 && p.xs_t % 4 == 0 && p.ds_b % 4 == 0 &&
              p.ds_t % 4 == 0 && p.ys_b % 4 == 0 && p.ys_t % 4 == 0 && p.Bs_n == 1 && p.Cs_n == 1 &&
-             p.Bs_b % 4 == 0 && p.Bs_t % 4 == 0 && p.Cs_b % 4 == 0 && p.Cs_t % 4 == 0;
-  if (p.flags & kHasZ) vec = vec && al(p.z, 4 * e) && p.zs_b % 4 == 0 && p.zs_t % 4 == 0;
+             p.Bs_b % 4 == 0 && p.Bs_t % 4 == 0 && p.Cs_b % 4 == 0 && p.Cs_t % 4 == 0 &&
+             // rows apart by at least their width: the last tile's descriptor
+             // range then ends before any row past the stretch
+             p.xs_t >= p.D && p.ds_t >= p.D && p.ys_t >= p.D && p.Bs_t >= p.N && p.Cs_t >= p.N;
+  if (p.flags & kHasZ) vec = vec && al(p.z, 4 * e) && p.zs_b % 4 == 0 && p.zs_t % 4 == 0 && p.zs_t >= p.D;
   if (p.io_bf16) return vec ? launch_io<true, true>(p, stream) : launch_io<true, false>(p, stream);
   return vec ? launch_io<false, true>(p, stream) : launch_io<false, false>(p, stream);
 }
