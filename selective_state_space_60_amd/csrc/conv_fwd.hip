@@ -62,6 +62,16 @@ __device__ __forceinline__ float elem(const Row<BF16, V>& r, int v) {
   }
 }
 
+// Two floats to a bf16 pair (a in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 (converting each float alone and merging the halves
+// takes four instructions).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 template <bool BF16, bool YF32, int V>
 __device__ __forceinline__ void store_row(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&o)[V]) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -76,10 +86,8 @@ __device__ __forceinline__ void store_row(__amdgpu_buffer_rsrc_t r, uint32_t off
   } else {
     if constexpr (V == 4) {
       u32x2 w;
-      w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[0]) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[1]) << 16);
-      w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[2]) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[3]) << 16);
+      w[0] = pack2(o[0], o[1]);
+      w[1] = pack2(o[2], o[3]);
       __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)off, 0, 0);
     } else {
       __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)o[0]), r, (int)off, 0, 0);

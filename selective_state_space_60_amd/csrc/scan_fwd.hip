@@ -146,6 +146,16 @@ __device__ __forceinline__ Span make_span(const void* base, int64_t off, int64_t
   return sp;
 }
 
+// Two floats to a bf16 pair (a in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 (converting each float alone and merging the halves
+// takes four instructions).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 template <bool BF16>
 __device__ __forceinline__ float raw2f(uint32_t v) {
   if constexpr (BF16) return __uint_as_float(v << 16);
@@ -362,10 +372,8 @@ struct VecLoader {
           __builtin_amdgcn_raw_buffer_store_b128(w, rsrc(y, 0xFFFFFFFFu), (int)oy, 0, 0);
         } else {
           u32x2 w;
-          w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
-                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
-          w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
-                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+          w.x = pack2(v[0], v[1]);
+          w.y = pack2(v[2], v[3]);
           __builtin_amdgcn_raw_buffer_store_b64(w, rsrc(y, 0xFFFFFFFFu), (int)oy, 0, 0);
         }
       }
