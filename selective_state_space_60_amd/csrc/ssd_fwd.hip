@@ -282,12 +282,15 @@ __global__ __launch_bounds__(256) void state_passing_kernel(SSDParams p) {
 
 // ------------------------------------------------------- s4 chunk scan
 
-// Block = (b, chunk c, group g, block of HB heads of g) with Q/32 waves; the
-// heads are taken in turn.  B (staged) and the C operands are the group's, so
-// they are read once per block; the next head's x, S_in, A_cum and beta are
-// loaded into registers while the current head is computed.  Wave wv owns
-// the two 16-row strips k = wv and k = Q/16 - 1 - wv, which balances the
-// causal work.
+// Block = (b, chunk c, group g, block of HB heads of g) with Q/16 waves, one
+// per 16-row strip; the heads are taken in turn.  B (staged) and the C
+// operands are the group's, so they are read once per block; the next head's
+// x, S_in, A_cum and beta are loaded into registers while the current head is
+// computed.  Strips k and Q/16 - 1 - k together hold the same causal work:
+// wave wv < Q/32 owns strip wv and wave wv >= Q/32 strip 3Q/32 - 1 - wv, so
+// the waves a SIMD runs (wv, wv + 4, ...) hold whole pairs.  (Two strips per
+// wave need twice the accumulator and operand registers, which halves the
+// waves a SIMD holds: slower at every size measured.)
 // Accumulators hold Y^T[p][i]: lane -> p = 16*mt + 4*(l/16) + r,
 // i = 16*k + l%16.
 //
@@ -300,8 +303,8 @@ __global__ __launch_bounds__(256) void state_passing_kernel(SSDParams p) {
 // four consecutive steps of one p, the contraction slots G'^T's layout needs.
 // beta_j is applied to G' (it multiplies the decay factor of column j).
 template <int Q, int NB>
-__global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p, int HB, int nhb) {
-  constexpr int NTH = 2 * Q;        // threads
+__global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, int nhb) {
+  constexpr int NTH = 4 * Q;        // threads
   constexpr int NSTRIP = Q / 16;
   constexpr int N = 64 * NB;        // states
   constexpr int KS = N / 32;        // 32-wide contraction slices over the states
@@ -331,12 +334,15 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
   const int64_t t0 = c * Q;
   // wave index as a scalar, so branches on it are uniform
   const int wv = __builtin_amdgcn_readfirstlane(tid / 64), l = tid % 64, lr = l % 16, lq = l / 16;
-  const int kst[2] = {wv, NSTRIP - 1 - wv};
+  const int kst = wv < NSTRIP / 2 ? wv : NSTRIP + NSTRIP / 2 - 1 - wv;  // this wave's strip
+  const int i0 = 16 * kst, i = i0 + lr;                                  // its rows; this lane's row
 
   // The head-dependent operands of head hh, into registers: x rows, S_in
   // (512 * NB 16-byte pieces), and for thread t < Q: A_cum[t], A_cum[t | 31], beta[t].
-  constexpr int NS = 512 * NB / NTH;
-  static_assert(NS * NTH == 512 * NB, "whole S_in pieces per thread");
+  constexpr int NS = (512 * NB + NTH - 1) / NTH;
+  static_assert(NS * NTH == 512 * NB || NS == 1, "whole S_in pieces per thread, or at most one");
+  constexpr bool kSomeIdle = NS * NTH != 512 * NB;      // more threads than S_in pieces
+  const bool s_ok = !kSomeIdle || tid < 512 * NB;       // this thread holds S_in pieces
   uint4 rx[NTX], rs[NS];
   float ra = 0.f, ra31 = 0.f, rbt = 0.f;
   auto load_head = [&](int64_t hh) {
@@ -350,7 +356,8 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
     }
     const uint16_t* Sp = (const uint16_t*)p.S_in + ((b * p.nchunks + c) * p.H + hh) * (64 * N);
 #pragma unroll
-    for (int u = 0; u < NS; ++u) rs[u] = *(const uint4*)(Sp + 8 * (tid + NTH * u));
+    for (int u = 0; u < NS; ++u)
+      if (!kSomeIdle || s_ok) rs[u] = *(const uint4*)(Sp + 8 * (tid + NTH * u));
     if (tid < Q) {
       const float* Ac = p.A_cum + (b * p.H + hh) * p.Lp + t0;
       ra = Ac[tid];
@@ -370,14 +377,13 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
     const int64_t tr = t0 + j < p.L ? t0 + j : p.L - 1;
     rb[u] = *(const uint4*)(Bsrc + tr * p.Bs_t + cb);
   }
-  bf16x8 Cop[2][KS];  // C operand of each strip: C[i][32*ks + 8*lq .. +7]
+  bf16x8 Cop[KS];  // C operand of the strip: C[i][32*ks + 8*lq .. +7]
   const uint16_t* Cb = (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int64_t ti = t0 + 16 * kst[s] + lr;
+  const int64_t ti = t0 + i;
+  {
     const int64_t tr = ti < p.L ? ti : p.L - 1;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) Cop[s][ks] = as_bf16x8(*(const uint4*)(Cb + tr * p.Cs_t + 32 * ks + 8 * lq));
+    for (int ks = 0; ks < KS; ++ks) Cop[ks] = as_bf16x8(*(const uint4*)(Cb + tr * p.Cs_t + 32 * ks + 8 * lq));
   }
   // rows at or past L hold zeros
 #pragma unroll
@@ -388,11 +394,9 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
     *(uint4*)&Bs[j][cb] = ok ? rb[u] : make_uint4(0, 0, 0, 0);
   }
   // C rows past L must not contribute
+  if (ti >= p.L)
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
-    if (t0 + 16 * kst[s] + lr >= p.L)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Cop[s][ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    for (int ks = 0; ks < KS; ++ks) Cop[ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
 
   for (int k = 0; k < nh; ++k) {
     const int64_t h = h_lo + k;
@@ -412,21 +416,28 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
   #pragma unroll
     for (int u = 0; u < NS; ++u) {
       const int e = tid + NTH * u, row = e / (8 * NB), cq = e % (8 * NB);
-      Ss[row][cq ^ (row % 8)] = rs[u];
+      if (!kSomeIdle || s_ok) Ss[row][cq ^ (row % 8)] = rs[u];
     }
     __syncthreads();
     if (k + 1 < nh) load_head(h + 1);  // in flight while head h is computed
 
-    f32x4 acc[2][4];
+    // inter-chunk term first, from a zero accumulator (no zeroing of the
+    // accumulators): Y^T[p][i] = exp(A_cum_i) sum_n S_in[p][n] C[i][n]
+    f32x4 acc[4];
+    const float ei = __builtin_amdgcn_exp2f(A2[i]);
   #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int mt = 0; mt < 4; ++mt) {
+      const int row = 16 * mt + lr;
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) a = mfma(as_bf16x8(Ss[row][(4 * ks + lq) ^ (row % 8)]), Cop[ks], a);
+      acc[mt] = a * ei;
+    }
     // transpose-read address of this lane: row 4*lq + (lr / 4), values 4*(lr % 4) .. +3 of a 16-wide p block
     const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
-    // intra-chunk term over 32-step blocks jb up to the later strip's diagonal
-    const int jb_last = (16 * kst[1]) / 32;
-    for (int jb = 0; jb <= jb_last; ++jb) {
+    // intra-chunk term over 32-step blocks jb up to the strip's diagonal
+    const int diag = i0 / 32;
+    for (int jb = 0; jb <= diag; ++jb) {
       const int j0 = 32 * jb;
       // A operands of Y^T += X^T G'^T: rows p, contraction slots in G^T's layout
       bf16x8 aX[4];
@@ -437,12 +448,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
         const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
         aX[mt] = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
       }
-  #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int i0 = 16 * kst[s];
-        const int diag = i0 / 32;
-        if (jb > diag) continue;  // wave-uniform
-        const int i = i0 + lr;
+      {
         f32x4 gt[2];
   #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
@@ -450,7 +456,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
           f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            a = mfma(as_bf16x8(*(const uint4*)&Bs[j0 + 16 * jt + lr][32 * ks + 8 * lq]), Cop[s][ks], a);
+            a = mfma(as_bf16x8(*(const uint4*)&Bs[j0 + 16 * jt + lr][32 * ks + 8 * lq]), Cop[ks], a);
           gt[jt] = a;  // G^T[j0 + 16*jt + 4*lq + r][i]
         }
         float v[8];
@@ -486,37 +492,17 @@ __global__ __launch_bounds__(2 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
         const bf16x8 bop = as_bf16x8(make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]),
                                                 pack2(v[6], v[7])));
   #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[s][mt] = mfma(aX[mt], bop, acc[s][mt]);
-      }
-    }
-    // inter-chunk term: Y^T[p][i] += exp(A_cum_i) sum_n S_in[p][n] C[i][n]
-  #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int row = 16 * mt + lr;
-      bf16x8 aS[KS];
-  #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) aS[ks] = as_bf16x8(Ss[row][(4 * ks + lq) ^ (row % 8)]);
-  #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a = mfma(aS[ks], Cop[s][ks], a);
-        const float ei = __builtin_amdgcn_exp2f(A2[16 * kst[s] + lr]);
-        acc[s][mt] += a * ei;
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(aX[mt], bop, acc[mt]);
       }
     }
     // epilogue: + D x (x from the staged rows), store y[i][p0..p0+3]
     const float Dh = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
-  #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int il = 16 * kst[s] + lr;
-      const int64_t ti = t0 + il;
-      if (ti >= p.L) continue;
+    if (ti < p.L) {
   #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int p0 = 16 * mt + 4 * lq;
-        const uint2 xv = *(const uint2*)&Xs[il][p0];
-        float o[4] = {acc[s][mt][0], acc[s][mt][1], acc[s][mt][2], acc[s][mt][3]};
+        const uint2 xv = *(const uint2*)&Xs[i][p0];
+        float o[4] = {acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]};
         o[0] = __builtin_fmaf(Dh, __uint_as_float(xv.x << 16), o[0]);
         o[1] = __builtin_fmaf(Dh, __uint_as_float(xv.x & 0xFFFF0000u), o[1]);
         o[2] = __builtin_fmaf(Dh, __uint_as_float(xv.y << 16), o[2]);
@@ -562,8 +548,7 @@ hipError_t launch_ssd_state_passing(const SSDParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_ssd_chunk_scan(const SSDParams& p, hipStream_t stream) {
-  // Heads per workgroup: about 1024 workgroups (two rounds at two per CU),
-  // heads of one group only.
+  // Heads per workgroup: about 1024 workgroups, heads of one group only.
   const int64_t hpg = p.H / p.G;
   const int64_t units = p.batch * p.nchunks * p.H;
   int64_t hb = units / 1024;
@@ -574,16 +559,16 @@ hipError_t launch_ssd_chunk_scan(const SSDParams& p, hipStream_t stream) {
   // (chunk, states) pairs whose staging fits in LDS; the host rejects chunk
   // 256 with 256 states
   if (p.N == 64) {
-    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 1>), dim3(nb), dim3(128), 0, stream, p, HB, nhb);
-    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 1>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
-    else hipLaunchKernelGGL((chunk_scan_kernel<256, 1>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
+    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 1>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
+    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 1>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
+    else hipLaunchKernelGGL((chunk_scan_kernel<256, 1>), dim3(nb), dim3(1024), 0, stream, p, HB, nhb);
   } else if (p.N == 128) {
-    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 2>), dim3(nb), dim3(128), 0, stream, p, HB, nhb);
-    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 2>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
-    else hipLaunchKernelGGL((chunk_scan_kernel<256, 2>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
+    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 2>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
+    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 2>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
+    else hipLaunchKernelGGL((chunk_scan_kernel<256, 2>), dim3(nb), dim3(1024), 0, stream, p, HB, nhb);
   } else {
-    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 4>), dim3(nb), dim3(128), 0, stream, p, HB, nhb);
-    else hipLaunchKernelGGL((chunk_scan_kernel<128, 4>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
+    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 4>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
+    else hipLaunchKernelGGL((chunk_scan_kernel<128, 4>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
   }
   return hipGetLastError();
 }
