@@ -173,80 +173,114 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t (*rows)[PR], int j0,
   return as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
 }
 
-// Block = (b, chunk c, head h, 64-wide block nbk of the N states), 8 waves.
+// Block = (b, chunk c, group g, block of HB heads of g, 64-wide block nbk
+// of the N states), 8 waves; the heads are taken in turn.
 // S_loc[p][n] = sum_j (w_j x_j[p]) B_j[n], w_j = exp(A_cum_end - A_cum_j)
-// beta_j: x rows are staged scaled by w_j, the block's 64 columns of the B
-// rows as they are; wave wv computes p-tile wv % 4 times n-tiles 2*(wv/4) and
-// +1, contracting over the Q steps in slices of 32.  With state_coef = 1 the
+// beta_j: x rows are staged scaled by w_j, the block's 64 columns of the
+// group's B rows as they are (once per block); wave wv computes p-tile wv % 4
+// times n-tiles 2*(wv/4) and +1, contracting over the Q steps in slices of
+// 32.  The next head's x rows, A_cum and beta are loaded into registers while
+// the current head is contracted and stored.  With state_coef = 1 the
 // weights are w_j = exp(A_cum_j) (the backward passes dy for x and C for B).
 template <int Q, int NB>
-__global__ __launch_bounds__(512) void chunk_state_kernel(SSDParams p) {
+__global__ __launch_bounds__(512) void chunk_state_kernel(SSDParams p, int HB, int nhb) {
   constexpr int NTH = 512;
   constexpr int PR = 64 + 4;        // row pitch (bf16)
   constexpr int NTX = Q * 8 / NTH;  // (row, 8 values) pieces of x and of B per thread
+  constexpr int N = 64 * NB;
   __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][PR];  // w_j x_j rows
   __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][PR];  // B rows
   __shared__ float w[Q];
-  int bid = (int)blockIdx.x;
-  const int nbk = bid % NB;
+  int64_t bid = blockIdx.x;
+  const int nbk = (int)(bid % NB);
   bid /= NB;
-  const int64_t h = bid % (int)p.H;
-  bid /= (int)p.H;
-  const int64_t c = bid % (int)p.nchunks, b = bid / (int)p.nchunks;
-  const int64_t g = h / (p.H / p.G);
+  const int hbk = (int)(bid % nhb);
+  bid /= nhb;
+  const int64_t g = bid % p.G;
+  bid /= p.G;
+  const int64_t c = bid % p.nchunks, b = bid / p.nchunks;
+  const int64_t hpg = p.H / p.G, h_lo = g * hpg + (int64_t)hbk * HB;
+  const int nh = (int)(hpg - (int64_t)hbk * HB < HB ? hpg - (int64_t)hbk * HB : HB);
   const int tid = threadIdx.x;
   const int64_t t0 = c * Q;
-  uint4 rx[NTX], rb[NTX];
-  const uint16_t* Xsrc = (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h;
+
+  // head hh's x rows, and for thread t < Q: A_cum[t], beta[t] (and A_cum at the chunk's end)
+  uint4 rx[NTX];
+  float ra = 0.f, rbe = 0.f, rend = 0.f;
+  auto load_head = [&](int64_t hh) {
+    const uint16_t* Xsrc = (const uint16_t*)p.x + b * p.xs_b + hh * p.xs_h;
+#pragma unroll
+    for (int u = 0; u < NTX; ++u) {
+      const int task = tid + NTH * u;
+      const int j = task / 8, cb = (task % 8) * 8;
+      const int64_t tr = t0 + j < p.L ? t0 + j : p.L - 1;
+      rx[u] = *(const uint4*)(Xsrc + tr * p.xs_t + cb);
+    }
+    const float* Ac = p.A_cum + (b * p.H + hh) * p.Lp + t0;
+    rend = Ac[Q - 1];
+    if (tid < Q) {
+      ra = Ac[tid];
+      rbe = p.beta[(b * p.H + hh) * p.Lp + t0 + tid];
+    }
+  };
+
+  uint4 rb[NTX];
   const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g + 64 * nbk;
+  load_head(h_lo);
 #pragma unroll
   for (int u = 0; u < NTX; ++u) {
     const int task = tid + NTH * u;
     const int j = task / 8, cb = (task % 8) * 8;
     const int64_t tr = t0 + j < p.L ? t0 + j : p.L - 1;
-    rx[u] = *(const uint4*)(Xsrc + tr * p.xs_t + cb);
     rb[u] = *(const uint4*)(Bsrc + tr * p.Bs_t + cb);
   }
-  const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
-  const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
-  const float a_end = Ac[Q - 1];
-  if (p.state_coef == 0) {
-    for (int t = tid; t < Q; t += NTH) w[t] = __builtin_amdgcn_exp2f((a_end - Ac[t]) * kLog2e) * be[t];
-  } else {
-    for (int t = tid; t < Q; t += NTH) w[t] = __builtin_amdgcn_exp2f(Ac[t] * kLog2e);
-  }
-  __syncthreads();
   // rows at or past L hold zeros (as data, not through w: 0 * inf)
 #pragma unroll
   for (int u = 0; u < NTX; ++u) {
     const int task = tid + NTH * u;
     const int j = task / 8, cb = (task % 8) * 8;
-    const bool ok = t0 + j < p.L;
-    const float wj = w[j];
-    const uint32_t v[4] = {rx[u].x, rx[u].y, rx[u].z, rx[u].w};
-    uint32_t o[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      o[k] = ok ? pack2(__uint_as_float(v[k] << 16) * wj, __uint_as_float(v[k] & 0xFFFF0000u) * wj) : 0u;
-    *(uint4*)&Xs[j][cb] = make_uint4(o[0], o[1], o[2], o[3]);
-    *(uint4*)&Bs[j][cb] = ok ? rb[u] : make_uint4(0, 0, 0, 0);
+    *(uint4*)&Bs[j][cb] = t0 + j < p.L ? rb[u] : make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();
+
   const int wv = __builtin_amdgcn_readfirstlane(tid / 64), l = tid % 64, lr = l % 16, lq = l / 16;
   const int pt = wv % 4, nt0 = 2 * (wv / 4);
-  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int k = 0; k < nh; ++k) {
+    const int64_t h = h_lo + k;
+    if (tid < Q)
+      w[tid] = p.state_coef == 0 ? __builtin_amdgcn_exp2f((rend - ra) * kLog2e) * rbe
+                                 : __builtin_amdgcn_exp2f(ra * kLog2e);
+    __syncthreads();  // w is written; the previous head's readers of Xs are done
 #pragma unroll
-  for (int ks = 0; ks < Q / 32; ++ks) {
-    const bf16x8 a = tr_operand<PR>(Xs, 32 * ks, 16 * pt, lr, lq);
+    for (int u = 0; u < NTX; ++u) {
+      const int task = tid + NTH * u;
+      const int j = task / 8, cb = (task % 8) * 8;
+      const bool ok = t0 + j < p.L;
+      const float wj = w[j];
+      const uint32_t v[4] = {rx[u].x, rx[u].y, rx[u].z, rx[u].w};
+      uint32_t o[4];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) acc[k] = mfma(a, tr_operand<PR>(Bs, 32 * ks, 16 * (nt0 + k), lr, lq), acc[k]);
+      for (int e = 0; e < 4; ++e)
+        o[e] = ok ? pack2(__uint_as_float(v[e] << 16) * wj, __uint_as_float(v[e] & 0xFFFF0000u) * wj) : 0u;
+      *(uint4*)&Xs[j][cb] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    __syncthreads();
+    if (k + 1 < nh) load_head(h + 1);  // in flight while head h is contracted
+
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < Q / 32; ++ks) {
+      const bf16x8 a = tr_operand<PR>(Xs, 32 * ks, 16 * pt, lr, lq);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        acc[kk] = mfma(a, tr_operand<PR>(Bs, 32 * ks, 16 * (nt0 + kk), lr, lq), acc[kk]);
+    }
+    float* dst = p.states + (((b * p.nchunks + c) * p.H + h) * 64) * N + 64 * nbk;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(16 * pt + 4 * lq + r) * N + 16 * (nt0 + kk) + lr] = acc[kk][r];
+    __syncthreads();  // w and Xs may be rewritten
   }
-  constexpr int N = 64 * NB;
-  float* dst = p.states + (((b * p.nchunks + c) * p.H + h) * 64) * N + 64 * nbk;
-#pragma unroll
-  for (int k = 0; k < 2; ++k)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(16 * pt + 4 * lq + r) * N + 16 * (nt0 + k) + lr] = acc[k][r];
 }
 
 // ---------------------------------------------------- s3 state passing
@@ -528,10 +562,18 @@ hipError_t launch_ssd_chunk_cumsum(const SSDParams& p, hipStream_t stream) {
 
 template <int NB>
 void launch_state_nb(const SSDParams& p, hipStream_t stream) {
-  const unsigned nb = (unsigned)(p.batch * p.nchunks * p.H * NB);
-  if (p.Q == 64) hipLaunchKernelGGL((chunk_state_kernel<64, NB>), dim3(nb), dim3(512), 0, stream, p);
-  else if (p.Q == 128) hipLaunchKernelGGL((chunk_state_kernel<128, NB>), dim3(nb), dim3(512), 0, stream, p);
-  else hipLaunchKernelGGL((chunk_state_kernel<256, NB>), dim3(nb), dim3(512), 0, stream, p);
+  // Heads per workgroup: one round of workgroups (the LDS holds two per CU at
+  // chunk 256, four below), heads of one group only.
+  const int64_t hpg = p.H / p.G;
+  const int64_t units = p.batch * p.nchunks * p.H * NB;
+  const int64_t slots = 256 * (p.Q == 256 ? 2 : 4);
+  int64_t hb = (units + slots - 1) / slots;
+  hb = hb < 1 ? 1 : (hb > hpg ? hpg : hb);
+  const int HB = (int)hb, nhb = (int)((hpg + hb - 1) / hb);
+  const unsigned nb = (unsigned)(p.batch * p.nchunks * p.G * nhb * NB);
+  if (p.Q == 64) hipLaunchKernelGGL((chunk_state_kernel<64, NB>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
+  else if (p.Q == 128) hipLaunchKernelGGL((chunk_state_kernel<128, NB>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
+  else hipLaunchKernelGGL((chunk_state_kernel<256, NB>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
 }
 
 hipError_t launch_ssd_chunk_state(const SSDParams& p, hipStream_t stream) {
