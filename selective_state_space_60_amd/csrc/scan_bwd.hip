@@ -139,7 +139,8 @@ struct LaneA {
 // the values its lane holds -- and KS (B, C) pairs for the shared staging.
 template <int KS>
 struct Fetch {
-  float x, dr, z, gy;
+  float x, dr, z;
+  uint32_t gy;  // dy as loaded: fp32 bits, or bf16 bits in the low half (converted where it is used)
   float B[KS], C[KS];
 };
 
@@ -207,11 +208,18 @@ __device__ __forceinline__ Fetch<KS> fetch(const ScanBwdParams& p, LanePtrs<KS>&
   Fetch<KS> f;
   f.x = lload<BF16>(w.x, ok);
   f.dr = lload<BF16>(w.dr, ok);
+  // No conversion behind a branch on p.z or p.dy_f32: converting there makes
+  // the compiler wait for these loads (and all before them) at once, while
+  // they are meant to be in flight for a whole tile.
   if constexpr (FULL) {
-    f.z = p.z ? lload<BF16>(w.z, ok) : 0.f;
-    f.gy = p.dy_f32 ? lload<false>(w.gy, ok) : lload<true>(w.gy, ok);
+    f.z = lload<BF16>(w.z, ok);  // without z, w.z reads x's element (unused)
+    const char* a = ok ? w.gy.p : w.gy.safe;
+    f.gy = p.dy_f32 ? *(const uint32_t*)a : (uint32_t)*(const uint16_t*)a;
   }
-  if (!ok) f.x = f.dr = f.z = f.gy = 0.f;
+  if (!ok) {
+    f.x = f.dr = f.z = 0.f;
+    f.gy = 0u;
+  }
   w.x.p += dir * w.x.step;
   w.dr.p += dir * w.dr.step;
   w.z.p += dir * w.z.step;
@@ -405,7 +413,7 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
     put_bc<KS>(s.bc, cur);
     float dv;
     float hdt = step_size(p, cur.dr, bias, j_ok, dv), hx = cur.x;
-    const float zj = cur.z, gyj = cur.gy;
+    const float zj = cur.z, gyj = __uint_as_float(p.dy_f32 ? cur.gy : cur.gy << 16);
     float h0t[KS];
 #pragma unroll
     for (int k = 0; k < KS; ++k) h0t[k] = h0n[k];
