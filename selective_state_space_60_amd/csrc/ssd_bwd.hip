@@ -160,6 +160,34 @@ __device__ __forceinline__ void stage_rows(uint16_t (*rows)[W + kPad], const uin
   }
 }
 
+// stage_rows in two halves: load() issues the global reads into registers,
+// store() writes them to LDS later (zero rows at or past L), so the reads of
+// the next head can be in flight while the current one is computed.
+template <int QR, int NTH, int W = 64>
+struct RowsInFlight {
+  static constexpr int PC = W / 8;  // 16-byte pieces per row
+  static constexpr int NTX = QR * PC / NTH;
+  static_assert(NTX * NTH == QR * PC, "whole pieces per thread");
+  uint4 v[NTX];
+  __device__ __forceinline__ void load(const uint16_t* src, int64_t st, int64_t t0, int64_t L) {
+#pragma unroll
+    for (int u = 0; u < NTX; ++u) {
+      const int task = threadIdx.x + NTH * u;
+      const int j = task / PC, cb = (task % PC) * 8;
+      const int64_t tr = t0 + j < L ? t0 + j : L - 1;
+      v[u] = *(const uint4*)(src + tr * st + cb);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t (*rows)[W + kPad], int64_t t0, int64_t L) const {
+#pragma unroll
+    for (int u = 0; u < NTX; ++u) {
+      const int task = threadIdx.x + NTH * u;
+      const int j = task / PC, cb = (task % PC) * 8;
+      *(uint4*)&rows[j][cb] = t0 + j < L ? v[u] : make_uint4(0, 0, 0, 0);
+    }
+  }
+};
+
 // 8 bf16 of row t (zero at or past L): columns c0 .. c0+7
 __device__ __forceinline__ bf16x8 row8(const uint16_t* src, int64_t st, int64_t t, int64_t L, int c0) {
   const int64_t tr = t < L ? t : L - 1;
@@ -298,20 +326,38 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) sum[s][nt] = zero4();
 
+  // The head's x, dy and S_in^T rows, A_cum and beta.  At chunk 256 (one
+  // workgroup per CU: nothing else would run while they load) the next
+  // head's are in flight while the current head is computed; below, the
+  // registers they take would halve the workgroups per CU, and they are
+  // loaded when the head starts.
+  constexpr bool kAhead = Q == 256;
+  RowsInFlight<Q, NTH> nx, ny;
+  RowsInFlight<64, NTH> ns;
+  float na = 0.f, nbe = 0.f;
+  auto load_head = [&](int64_t hh) {
+    nx.load((const uint16_t*)p.x + b * p.xs_b + hh * p.xs_h, p.xs_t, t0, p.L);
+    ny.load((const uint16_t*)q.dy + b * q.dys_b + hh * q.dys_h, q.dys_t, t0, p.L);
+    ns.load(q.SinT + ((b * p.nchunks + c) * p.H + hh) * E + nc0 * kP, kP, 0, 64);
+    if (tid < Q) {
+      na = p.A_cum[(b * p.H + hh) * p.Lp + t0 + tid];
+      nbe = p.beta[(b * p.H + hh) * p.Lp + t0 + tid];
+    }
+  };
+  if (kAhead) load_head(hb.h_lo);
   for (int k = 0; k < hb.nh; ++k) {
     const int64_t h = hb.h_lo + k;
-    const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
-    const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
     __syncthreads();  // the previous head is done with the staged rows and tables
-    // every global read of this head, issued together
-    stage_rows<Q, NTH>(Xs, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
-    stage_rows<Q, NTH>(Ys, (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h, q.dys_t, t0, p.L);
-    stage_rows<64, NTH>(SsT, q.SinT + ((b * p.nchunks + c) * p.H + h) * E + nc0 * kP, kP, 0, 64);
-    for (int t = tid; t < Q; t += NTH) {
-      A2[t] = Ac[t] * kLog2e;
-      bj[t] = be[t];
+    if (!kAhead) load_head(h);
+    nx.store(Xs, t0, p.L);
+    ny.store(Ys, t0, p.L);
+    ns.store(SsT, 0, 64);
+    if (tid < Q) {
+      A2[tid] = na * kLog2e;
+      bj[tid] = nbe;
     }
     __syncthreads();
+    if (kAhead && k + 1 < hb.nh) load_head(h + 1);
     for (int t = tid; t < Q; t += NTH) tb[t] = __builtin_amdgcn_exp2f(A2[t | 31] - A2[t]) * bj[t];
     __syncthreads();
     bf16x8 yop[2][2], cop[2][2];  // B operands: dy[i][32*ks + 8*lq .. +7], C[i][..] of the strips' rows
