@@ -562,7 +562,10 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
       const int i = tid + r * NT;
       const int j = i / (2 * G * KS), q = (i / (G * KS)) % 2, n = i % (G * KS);
       const float v = s.red[0][j][q][n] + s.red[1][j][q][n] + s.red[2][j][q][n] + s.red[3][j][q][n];
-      if (t0 + red_j[r] < L && red_n_ok[r]) *pred[r] = v;
+      // written once, read back only by the reduction kernel: non-temporal,
+      // so these 2 KB per tile do not displace the input lines that the
+      // neighbouring workgroups share in L2
+      if (t0 + red_j[r] < L && red_n_ok[r]) __builtin_nontemporal_store(v, pred[r]);
       pred[r] -= red_step;
     }
     pdx -= sdx;
