@@ -80,7 +80,7 @@ __device__ __forceinline__ float expm1_acc(float a) {
 }
 
 template <int Q>
-__global__ __launch_bounds__(256) void chunk_cumsum_kernel(SSDParams p) {
+__global__ __launch_bounds__(256) void chunk_cumsum_kernel(SSDParams p, int nblocks, int nblocks_padded) {
   constexpr int RUN = Q / 16;                  // steps per thread in the scan phase
   constexpr int NLD = Q * kCumHeads / 256;     // delta loads per thread
   __shared__ float sa[kCumHeads][Q + 1];
@@ -88,7 +88,11 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(SSDParams p) {
   __shared__ float spart[kCumHeads][17];
   __shared__ float sA[kCumHeads], srA[kCumHeads];
   const int nhb = (int)((p.H + kCumHeads - 1) / kCumHeads);
-  int bid = (int)blockIdx.x;
+  // The hardware deals consecutive block ids round-robin over the 8 XCDs;
+  // this order puts the blocks of one (batch, chunk), which read disjoint
+  // 32-byte pieces of the same delta rows, on one XCD and so one L2.
+  int bid = (int)((blockIdx.x & 7) * (nblocks_padded >> 3) + (blockIdx.x >> 3));
+  if (bid >= nblocks) return;
   const int hb = bid % nhb;
   bid /= nhb;
   const int c = bid % (int)p.nchunks, b = bid / (int)p.nchunks;
@@ -553,10 +557,11 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
 }  // namespace
 
 hipError_t launch_ssd_chunk_cumsum(const SSDParams& p, hipStream_t stream) {
-  const unsigned nb = (unsigned)(p.batch * p.nchunks * ((p.H + kCumHeads - 1) / kCumHeads));
-  if (p.Q == 64) hipLaunchKernelGGL(chunk_cumsum_kernel<64>, dim3(nb), dim3(256), 0, stream, p);
-  else if (p.Q == 128) hipLaunchKernelGGL(chunk_cumsum_kernel<128>, dim3(nb), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(chunk_cumsum_kernel<256>, dim3(nb), dim3(256), 0, stream, p);
+  const int nb = (int)(p.batch * p.nchunks * ((p.H + kCumHeads - 1) / kCumHeads));
+  const int npad = (nb + 7) / 8 * 8;  // blocks past nb exit at once
+  if (p.Q == 64) hipLaunchKernelGGL(chunk_cumsum_kernel<64>, dim3(npad), dim3(256), 0, stream, p, nb, npad);
+  else if (p.Q == 128) hipLaunchKernelGGL(chunk_cumsum_kernel<128>, dim3(npad), dim3(256), 0, stream, p, nb, npad);
+  else hipLaunchKernelGGL(chunk_cumsum_kernel<256>, dim3(npad), dim3(256), 0, stream, p, nb, npad);
   return hipGetLastError();
 }
 
