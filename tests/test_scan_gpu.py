@@ -159,6 +159,28 @@ def test_broadcast_A_and_strided_inputs():
     assert_close(host_f64(y), yr, "f32", "strided")
 
 
+def test_overlapping_rows_take_the_element_loader():
+    """B and C as views whose rows overlap in memory (row stride 8 < N = 16),
+    with a partial last tile: rows past the stretch lie inside the last tile's
+    descriptor range there, so such layouts must not take the vector loader
+    (which relies on that range to read them as zeros)."""
+    banner("scan overlapping rows")
+    spec = synth.scan_spec(synth.TINY, batch=2, seqlen=70, dim=24, dstate=16, has_z=True)
+    inp = synth.scan_inputs(spec, 11)
+    g = _upload(spec, inp)
+    views = {}
+    for k in ("B", "C"):
+        base = torch.from_numpy(synth.fill((2, 70 * 8 + 8), synth.Dist(synth.NORMAL, 0.0, 1.0), "f32", 11,
+                                           31 if k == "B" else 32)).cuda()
+        v = torch.as_strided(base, (2, 70, 16), (base.stride(0), 8, 1))
+        views[k] = v
+        inp[k] = v.cpu().numpy().astype(np.float32).copy()  # the values the view holds, for the oracle
+    y, _ = ssm.selective_scan_fwd(g["x"], g["delta"], g["A"], views["B"], views["C"], D=g["D"], z=g["z"])
+    torch.cuda.synchronize()
+    yr, _ = oracle.selective_scan(inp, "f32")
+    assert_close(host_f64(y), yr, "f32", "overlapping rows")
+
+
 def test_zero_A_limit():
     """A = 0 entries take the limit Bbar = delta * B."""
     spec = synth.scan_spec(synth.TINY, batch=1, seqlen=70, dim=20, dstate=8, has_z=False)
