@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 #define SSM_MAX_DIMS 5
 #define SSM_SCAN_MAX_DSTATE 64 /* selective scan: N <= 64 */
 
@@ -88,6 +88,7 @@ typedef struct {
 #define SSM_SILU 256u          /* conv: apply SiLU to the output                      */
 #define SSM_WANT_CKPT 512u     /* scan: also write the state before every 16-step tile */
 #define SSM_HAS_CKPT 1024u     /* scan backward: read those states, do not recompute them */
+#define SSM_HAS_SSD_FWD 2048u  /* SSD backward: read the forward's A_cum, beta and chunk states */
 
 /* ------------------------------------------------------------------ scan */
 
@@ -267,7 +268,7 @@ typedef struct {
  *   dB, dC : (batch, seqlen, ngroups, dstate) F32 contiguous
  *   dD     : (nheads) F32 contiguous                          if SSM_HAS_D
  *   dh0    : (batch, nheads, headdim, dstate) F32 contiguous  if SSM_HAS_H0
- * Flags: SSM_HAS_D, SSM_DISC_EULER, SSM_HAS_H0.  Supported: as the forward
+ * Flags: SSM_HAS_D, SSM_DISC_EULER, SSM_HAS_H0, SSM_HAS_SSD_FWD.  Supported: as the forward
  * (headdim 64, dstate in {64, 128, 256}, chunk in {64, 128, 256} except
  * dstate 256 with chunk 256, nheads % ngroups == 0).  Every (batch,
  * step, head or group) row of x, dy, B, C and dx, and h0 / dh0, must start
@@ -276,7 +277,12 @@ typedef struct {
  * partial sums, so the results are deterministic.  Outputs may not overlap
  * inputs or each other.  Workspace: ssm_ssd_bwd_workspace_size bytes
  * (the recomputed forward intermediates and the partial sums), 256-byte
- * aligned. */
+ * aligned.
+ * With SSM_HAS_SSD_FWD the caller passes A_cum, beta and states as written
+ * by ssm_ssd_chunk_cumsum and ssm_ssd_chunk_state on the same inputs (layouts
+ * below ssm_ssd_chunk_fwd; contiguous, 16-byte aligned, read only): the
+ * backward then skips those two steps, and its workspace drops their space.
+ * A training step that ran the four forward steps keeps them for this. */
 typedef struct {
   int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
   uint32_t flags;
@@ -300,6 +306,9 @@ typedef struct {
   float* dC;
   float* dD;        /* NULL unless SSM_HAS_D  */
   float* dh0;       /* NULL unless SSM_HAS_H0 */
+  const float* A_cum;  /* NULL unless SSM_HAS_SSD_FWD */
+  const float* beta;   /* NULL unless SSM_HAS_SSD_FWD */
+  const float* states; /* NULL unless SSM_HAS_SSD_FWD */
 } ssm_ssd_bwd_ptrs;
 
 /* ---------------------------------------------------------------- decode */

@@ -22,8 +22,8 @@ SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_STRIDE, SSM_ERR_ALIG
 SSM_F32, SSM_BF16, SSM_F16 = 0, 1, 2
 SSM_HAS_Z, SSM_HAS_D, SSM_DISC_EULER, SSM_HAS_H0, SSM_WANT_HLAST = 1, 2, 4, 8, 16
 SSM_DELTA_SOFTPLUS, SSM_HAS_DELTA_BIAS, SSM_HAS_BIAS, SSM_SILU = 32, 64, 128, 256
-SSM_WANT_CKPT, SSM_HAS_CKPT = 512, 1024
-ABI_VERSION = 4
+SSM_WANT_CKPT, SSM_HAS_CKPT, SSM_HAS_SSD_FWD = 512, 1024, 2048
+ABI_VERSION = 5
 MAX_DIMS = 5
 
 # Every function include/ssm.h declares.
@@ -47,6 +47,7 @@ _BWD_IN = ("x", "delta", "A", "B", "C", "D", "z", "h0", "delta_bias", "dy")
 _BWD_OUT = ("dx", "ddelta", "dz", "dA", "dB", "dC", "dD", "dh0", "ddelta_bias")
 _SSD_BWD_IN = ("x", "delta", "A", "B", "C", "D", "h0", "dy")
 _SSD_BWD_OUT = ("dx", "ddelta", "dA", "dB", "dC", "dD", "dh0")
+_SSD_FWD_SAVED = ("A_cum", "beta", "states")   # the forward's intermediates the backward can take
 
 
 class ScanDesc(ctypes.Structure):
@@ -104,7 +105,7 @@ class SSDBwdDesc(ctypes.Structure):
 
 
 class SSDBwdPtrs(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in _SSD_BWD_IN + _SSD_BWD_OUT]
+    _fields_ = [(n, ctypes.c_void_p) for n in _SSD_BWD_IN + _SSD_BWD_OUT + _SSD_FWD_SAVED]
 
 
 class SSMError(RuntimeError):
@@ -363,6 +364,20 @@ def ssd_chunk_scan(x, delta, A, B, C, chunk, A_cum, beta, S_in, D=None, euler=Fa
     return y
 
 
+def ssd_chunk_fwd_train(x, delta, A, B, C, chunk, D=None, h0=None, euler=False, want_hlast=False, y_dtype=None,
+                        stream=None):
+    """SSD forward by its four steps, keeping what ssd_bwd(..., fwd=saved)
+    takes instead of recomputing it.  Returns (y, h_last or None, saved) with
+    saved = {"A_cum", "beta", "states"}."""
+    A_cum, beta = ssd_chunk_cumsum(x, delta, A, B, C, chunk, euler=euler, stream=stream)
+    states = ssd_chunk_state(x, delta, A, B, C, chunk, A_cum, beta, euler=euler, stream=stream)
+    S_in, h_last = ssd_state_passing(x, delta, A, B, C, chunk, A_cum, states, h0=h0, want_hlast=want_hlast,
+                                     euler=euler, stream=stream)
+    y = ssd_chunk_scan(x, delta, A, B, C, chunk, A_cum, beta, S_in, D=D, euler=euler, y_dtype=y_dtype,
+                       stream=stream)
+    return y, h_last, {"A_cum": A_cum, "beta": beta, "states": states}
+
+
 # ------------------------------------------------------------------ decode
 
 def update_desc(x, delta, A, B, C, state, D=None, z=None, y=None, euler=False, delta_softplus=False,
@@ -474,21 +489,25 @@ def selective_scan_bwd(dy, x, delta, A, B, C, D=None, z=None, h0=None, euler=Fal
 
 # ----------------------------------------------------------- SSD backward
 
-def ssd_bwd_desc(dy, x, delta, A, B, C, chunk, out: dict, D=None, h0=None, euler=False) -> SSDBwdDesc:
+def ssd_bwd_desc(dy, x, delta, A, B, C, chunk, out: dict, D=None, h0=None, euler=False,
+                 has_fwd=False) -> SSDBwdDesc:
     d = SSDBwdDesc()
     d.batch, d.seqlen, d.nheads, d.headdim = x.shape
     d.ngroups, d.dstate = B.shape[2], B.shape[3]
     d.chunk = chunk
     d.flags = (SSM_HAS_D if D is not None else 0) | (SSM_DISC_EULER if euler else 0) | \
-        (SSM_HAS_H0 if h0 is not None else 0)
+        (SSM_HAS_H0 if h0 is not None else 0) | (SSM_HAS_SSD_FWD if has_fwd else 0)
     for name, t in list(zip(_SSD_BWD_IN, (x, delta, A, B, C, D, h0, dy))) + [(k, out.get(k)) for k in _SSD_BWD_OUT]:
         setattr(d, name, tensor_desc(t))
     return d
 
 
-def ssd_bwd(dy, x, delta, A, B, C, chunk, D=None, h0=None, euler=False, dx_dtype=None, stream=None) -> dict:
+def ssd_bwd(dy, x, delta, A, B, C, chunk, D=None, h0=None, euler=False, dx_dtype=None, fwd=None,
+            stream=None) -> dict:
     """Gradients of sum(dy * y) for y = ssd_chunk_fwd(x, delta, A, B, C,
     chunk, D, h0, euler) (see include/ssm.h).  dy (batch, L, H, P) bf16.
+    fwd: the `saved` dict of ssd_chunk_fwd_train on the same inputs, whose
+    A_cum, beta and chunk states are then read instead of recomputed.
 
     Returns a dict: dx (dx_dtype, default x's dtype), ddelta (batch, L, H),
     dA (H,), dB, dC (batch, L, G, N), dD (if D), dh0 (if h0); all but dx fp32."""
@@ -499,10 +518,19 @@ def ssd_bwd(dy, x, delta, A, B, C, chunk, D=None, h0=None, euler=False, dx_dtype
     out = {"dx": torch.empty(x.shape, dtype=dx_dtype or x.dtype, device=dev), "ddelta": f32(batch, L, H),
            "dA": f32(H), "dB": f32(batch, L, G, N), "dC": f32(batch, L, G, N),
            "dD": f32(H) if D is not None else None, "dh0": f32(batch, H, P, N) if h0 is not None else None}
-    d = ssd_bwd_desc(dy, x, delta, A, B, C, chunk, out, D, h0, euler)
+    d = ssd_bwd_desc(dy, x, delta, A, B, C, chunk, out, D, h0, euler, has_fwd=fwd is not None)
     p = SSDBwdPtrs()
     for name, t in list(zip(_SSD_BWD_IN, (x, delta, A, B, C, D, h0, dy))) + [(k, out[k]) for k in _SSD_BWD_OUT]:
         setattr(p, name, _p(t))
+    if fwd is not None:
+        # the library sees bare pointers here, so the shapes are checked on this side
+        _, _, _, _, nc, Lp = _ssd_shapes(x, B, chunk)
+        want = {"A_cum": (batch, H, Lp), "beta": (batch, H, Lp), "states": (batch, nc, H, P, N)}
+        for k in _SSD_FWD_SAVED:
+            t = fwd[k]
+            if tuple(t.shape) != want[k] or t.dtype != torch.float32 or not t.is_contiguous() or t.device != dev:
+                raise ValueError(f"ssd_bwd: fwd[{k!r}] must be a contiguous fp32 {want[k]} tensor on {dev}")
+            setattr(p, k, _p(t))
     n = ctypes.c_size_t()
     _check(lib().ssm_ssd_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)), "ssm_ssd_bwd_workspace_size")
     ws = _workspace(n.value, dev)

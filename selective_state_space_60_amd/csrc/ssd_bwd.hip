@@ -23,8 +23,9 @@
 // through a = delta A and beta = expm1(delta A)/A (or delta):
 //   ddelta = A da + dbeta exp(delta A),   dA = sum(delta da + dbeta dbeta/dA).
 //
-// Kernels (after the forward's cumsum and chunk state are recomputed, and
-// its chunk-state kernel has formed sum_i exp(A_cum_i) dy_i C_i^T):
+// Kernels (given the forward's cumsum and chunk states, recomputed by the
+// caller or kept from the forward, and after the forward's chunk-state kernel
+// has formed sum_i exp(A_cum_i) dy_i C_i^T):
 //   bwd_state_kernel  : the states entering each chunk (fp32, and bf16
 //                       transposed), then the reverse recurrence.
 //   bwd_dc_kernel     : dC and W's row sums -- the forward chunk scan's
@@ -193,13 +194,6 @@ __device__ __forceinline__ bf16x8 row8(const uint16_t* src, int64_t st, int64_t 
   const int64_t tr = t < L ? t : L - 1;
   const uint4 v = *(const uint4*)(src + tr * st + c0);
   return as_bf16x8(t < L ? v : make_uint4(0, 0, 0, 0));
-}
-
-// 4 bf16 of row t (zero at or past L): columns c0 .. c0+3
-__device__ __forceinline__ uint2 row4(const uint16_t* src, int64_t st, int64_t t, int64_t L, int c0) {
-  const int64_t tr = t < L ? t : L - 1;
-  const uint2 v = *(const uint2*)(src + tr * st + c0);
-  return t < L ? v : make_uint2(0, 0);
 }
 
 // ------------------------------------------------- reverse state passing
@@ -1090,11 +1084,9 @@ void launch_q(const SSDBwdParams& q, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_ssd_bwd(const SSDBwdParams& q, float* dA, float* dB, float* dC, float* dD, hipStream_t stream) {
+  // q.f holds the forward's A_cum, beta and chunk states (recomputed or kept)
   const SSDParams& p = q.f;
   hipError_t e;
-  // recompute the forward's A_cum, beta and chunk states
-  if ((e = launch_ssd_chunk_cumsum(p, stream)) != hipSuccess) return e;
-  if ((e = launch_ssd_chunk_state(p, stream)) != hipSuccess) return e;
   // sum_i exp(A_cum_i) dy_i C_i^T: the chunk-state product with dy for x, C for B
   SSDParams f2 = p;
   f2.x = q.dy;

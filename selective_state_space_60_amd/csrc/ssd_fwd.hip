@@ -42,7 +42,6 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 // Two floats to a bf16 pair (a in the low half), round to nearest even: one
 // v_cvt_pk_bf16_f32 (converting each float alone and merging the halves
 // takes four instructions).

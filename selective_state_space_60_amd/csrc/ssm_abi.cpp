@@ -49,6 +49,16 @@ Span span_of(const ssm_tensor_desc& t, const void* ptr) {
   return s;
 }
 
+// The bytes [ptr, ptr + bytes) of a plain contiguous buffer.
+Span span_bytes(const void* ptr, int64_t bytes) {
+  Span s;
+  if (!ptr) return s;
+  s.lo = (uintptr_t)ptr;
+  s.hi = s.lo + (uintptr_t)bytes;
+  s.valid = true;
+  return s;
+}
+
 bool overlap(const Span& a, const Span& b) { return a.valid && b.valid && a.lo < b.hi && b.lo < a.hi; }
 
 // Shape, dtype and stride checks of one tensor.
@@ -336,12 +346,13 @@ ssm::SSDParams make_ssd_params(const ssm_ssd_desc* d, const ssm_ssd_ptrs* p, con
 
 // ---------------------------------------------------------- SSD backward
 
-constexpr uint32_t kSSDBwdFlags = SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0;
+constexpr uint32_t kSSDBwdFlags = SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_HAS_SSD_FWD;
 
 struct SSDBwdPlan {
   SSDPlan f;
   int HB = 1, nhb = 1;
   int64_t ws_state = 0, ws_half = 0, ws_aend = 0, ws_step = 0, ws_acA = 0, ws_part = 0, ws_pdb = 0, ws_total = 0;
+  bool own_fwd = true;  // A_cum, beta and states are recomputed into the workspace
 };
 
 // The forward problem of a backward descriptor (dx stands in for y: both are
@@ -350,7 +361,7 @@ ssm_ssd_desc ssd_fwd_of(const ssm_ssd_bwd_desc& d) {
   ssm_ssd_desc f;
   std::memset(&f, 0, sizeof(f));
   f.batch = d.batch; f.seqlen = d.seqlen; f.nheads = d.nheads; f.headdim = d.headdim; f.dstate = d.dstate;
-  f.ngroups = d.ngroups; f.chunk = d.chunk; f.flags = d.flags;
+  f.ngroups = d.ngroups; f.chunk = d.chunk; f.flags = d.flags & ~SSM_HAS_SSD_FWD;
   f.x = d.x; f.delta = d.delta; f.A = d.A; f.B = d.B; f.C = d.C; f.D = d.D; f.y = d.dx; f.h0 = d.h0;
   return f;
 }
@@ -373,10 +384,11 @@ SSDBwdPlan plan_ssd_bwd(const ssm_ssd_bwd_desc& d) {
   pl.ws_acA = round256((d.dstate / 64) * d.batch * d.nheads * pl.f.Lp * 4);  // one per 64-wide block of the states
   pl.ws_part = round256(d.batch * nc * d.nheads * 4);
   pl.ws_pdb = round256((int64_t)pl.nhb * d.batch * d.seqlen * d.ngroups * d.dstate * 4);
-  // A_cum, beta | states, dS, S32 | SinT, dSl, dSlT | pAend | dAcA | dAcB, dbeta, Tj, dDj | pA, pD | pdB, pdC
-  pl.ws_total = pl.f.ws_acum + pl.f.ws_beta + 3 * pl.ws_state + 3 * pl.ws_half + pl.ws_aend + pl.ws_acA +
-                4 * pl.ws_step +
-                2 * pl.ws_part + 2 * pl.ws_pdb;
+  // A_cum, beta | states, dS, S32 | SinT, dSl, dSlT | pAend | dAcA | dAcB, dbeta, Tj, dDj | pA, pD | pdB, pdC;
+  // with SSM_HAS_SSD_FWD the caller's A_cum, beta and states take the place of the first three
+  pl.own_fwd = !(d.flags & SSM_HAS_SSD_FWD);
+  pl.ws_total = (pl.own_fwd ? pl.f.ws_acum + pl.f.ws_beta + pl.ws_state : 0) + 2 * pl.ws_state + 3 * pl.ws_half +
+                pl.ws_aend + pl.ws_acA + 4 * pl.ws_step + 2 * pl.ws_part + 2 * pl.ws_pdb;
   return pl;
 }
 
@@ -416,6 +428,9 @@ ssm_status validate_ssd_bwd_ptrs(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_pt
     return SSM_ERR_NULL;
   if ((f & SSM_HAS_D) && (!p->D || !p->dD)) return SSM_ERR_NULL;
   if ((f & SSM_HAS_H0) && (!p->h0 || !p->dh0)) return SSM_ERR_NULL;
+  const bool fwd = f & SSM_HAS_SSD_FWD;
+  if (fwd && (!p->A_cum || !p->beta || !p->states)) return SSM_ERR_NULL;
+  if (fwd && (!aligned(p->A_cum, 16) || !aligned(p->beta, 16) || !aligned(p->states, 16))) return SSM_ERR_ALIGN;
   if (!aligned(p->delta, 2) || !aligned(p->A, 4) || !aligned(p->ddelta, 4) || !aligned(p->dA, 4) ||
       !aligned(p->dB, 4) || !aligned(p->dC, 4) || (p->D && !aligned(p->D, 4)) || (p->dD && !aligned(p->dD, 4)))
     return SSM_ERR_ALIGN;
@@ -423,10 +438,17 @@ ssm_status validate_ssd_bwd_ptrs(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_pt
       !rows_aligned16(d->C, p->C, 3) || !rows_aligned16(d->dx, p->dx, 3) ||
       ((f & SSM_HAS_H0) && (!aligned(p->h0, 16) || !aligned(p->dh0, 16))))
     return SSM_ERR_ALIGN;
+  // sizes of the forward's intermediates: (batch, nheads, Lp) and (batch, nchunks, nheads, headdim, dstate) F32
+  const int64_t nc = (d->seqlen + d->chunk - 1) / d->chunk;
+  const int64_t acum_bytes = d->batch * d->nheads * nc * d->chunk * 4;
+  const int64_t state_bytes = d->batch * nc * d->nheads * d->headdim * d->dstate * 4;
   const Span ins[] = {span_of(d->x, p->x),  span_of(d->delta, p->delta), span_of(d->A, p->A),
                       span_of(d->B, p->B),  span_of(d->C, p->C),         span_of(d->dy, p->dy),
                       (f & SSM_HAS_D) ? span_of(d->D, p->D) : Span(),
-                      (f & SSM_HAS_H0) ? span_of(d->h0, p->h0) : Span()};
+                      (f & SSM_HAS_H0) ? span_of(d->h0, p->h0) : Span(),
+                      fwd ? span_bytes(p->A_cum, acum_bytes) : Span(),
+                      fwd ? span_bytes(p->beta, acum_bytes) : Span(),
+                      fwd ? span_bytes(p->states, state_bytes) : Span()};
   const Span outs[] = {span_of(d->dx, p->dx), span_of(d->ddelta, p->ddelta), span_of(d->dA, p->dA),
                        span_of(d->dB, p->dB), span_of(d->dC, p->dC),
                        (f & SSM_HAS_D) ? span_of(d->dD, p->dD) : Span(),
@@ -938,9 +960,15 @@ ssm_status ssm_ssd_bwd(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_ptrs* p, voi
     w += bytes;
     return r;
   };
-  q.f.A_cum = (float*)take(pl.f.ws_acum);
-  q.f.beta = (float*)take(pl.f.ws_beta);
-  q.f.states = (float*)take(pl.ws_state);
+  if (pl.own_fwd) {
+    q.f.A_cum = (float*)take(pl.f.ws_acum);
+    q.f.beta = (float*)take(pl.f.ws_beta);
+    q.f.states = (float*)take(pl.ws_state);
+  } else {  // read only by the backward's kernels
+    q.f.A_cum = const_cast<float*>(p->A_cum);
+    q.f.beta = const_cast<float*>(p->beta);
+    q.f.states = const_cast<float*>(p->states);
+  }
   q.dS = (float*)take(pl.ws_state);
   q.S32 = (float*)take(pl.ws_state);
   q.SinT = (uint16_t*)take(pl.ws_half);
@@ -966,6 +994,12 @@ ssm_status ssm_ssd_bwd(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_ptrs* p, voi
   q.dh0 = (f & SSM_HAS_H0) ? p->dh0 : nullptr;
   q.HB = pl.HB;
   q.nhb = pl.nhb;
+  const hipStream_t st = (hipStream_t)hip_stream;
+  if (pl.own_fwd) {  // recompute the forward's A_cum, beta and chunk states
+    hipError_t e = ssm::launch_ssd_chunk_cumsum(q.f, st);
+    if (e == hipSuccess) e = ssm::launch_ssd_chunk_state(q.f, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
   return hip_status(ssm::launch_ssd_bwd(q, p->dA, p->dB, p->dC, (f & SSM_HAS_D) ? p->dD : nullptr,
                                         (hipStream_t)hip_stream));
 }

@@ -32,7 +32,7 @@ def test_exports_match_header():
     assert declared == sorted(ssm.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.ssm_abi_version() == ssm.ABI_VERSION == 4
+    assert lib.ssm_abi_version() == ssm.ABI_VERSION == 5
 
 
 def test_status_strings():
@@ -308,6 +308,34 @@ def test_ssd_bwd_validation(mutate, status):
     assert ssm.lib().ssm_ssd_bwd(ctypes.byref(d), ctypes.byref(p), 16 << 36, 1 << 40, None) == status
 
 
+# batch 1, L 100, 4 heads, chunk 64: A_cum, beta (1, 4, 128) fp32; states (1, 2, 4, 64, 64) fp32
+_FWD = {"A_cum": 17 << 36, "beta": 18 << 36, "states": 19 << 36}
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda d, p: setattr(p, "A_cum", None), ssm.SSM_ERR_NULL),
+    (lambda d, p: setattr(p, "states", None), ssm.SSM_ERR_NULL),
+    (lambda d, p: setattr(p, "beta", p.beta + 4), ssm.SSM_ERR_ALIGN),
+    (lambda d, p: setattr(p, "states", p.states + 8), ssm.SSM_ERR_ALIGN),
+    # each buffer's extent: A_cum is 1 * 4 * 128 * 4 = 2048 bytes, states 2 * 4 * 4096 * 4 bytes
+    (lambda d, p: setattr(p, "dA", p.A_cum + 2032), ssm.SSM_ERR_ALIAS),
+    (lambda d, p: setattr(p, "dA", p.A_cum + 2048), ssm.SSM_OK),
+    (lambda d, p: setattr(p, "dh0", p.states + 2 * 4 * 4096 * 4 - 16), ssm.SSM_ERR_ALIAS),
+    (lambda d, p: setattr(p, "ddelta", p.beta), ssm.SSM_ERR_ALIAS),
+])
+def test_ssd_bwd_fwd_validation(mutate, status):
+    d, p = _ssd_bwd(flags=ssm.SSM_HAS_D | ssm.SSM_HAS_H0 | ssm.SSM_HAS_SSD_FWD)
+    for k, v in _FWD.items():
+        setattr(p, k, v)
+    mutate(d, p)
+    if status == ssm.SSM_OK:   # valid: stop before any launch with a too-small workspace
+        status = ssm.SSM_ERR_WORKSPACE
+        n = 256
+    else:
+        n = 1 << 40
+    assert ssm.lib().ssm_ssd_bwd(ctypes.byref(d), ctypes.byref(p), 16 << 36, n, None) == status
+
+
 def test_ssd_bwd_dstate_limit():
     # as in the forward: 96 states are not a supported size, 256 states not with chunk 256
     d, p = _ssd_bwd(N=96)
@@ -331,6 +359,11 @@ def test_ssd_bwd_workspace():
     assert n.value == want
     assert ssm.lib().ssm_ssd_bwd(ctypes.byref(d), ctypes.byref(p), 16 << 36, n.value - 1, None) == \
         ssm.SSM_ERR_WORKSPACE
+    # with the forward's A_cum, beta and states given, their space is not taken
+    d.flags |= ssm.SSM_HAS_SSD_FWD
+    m = ctypes.c_size_t()
+    assert ssm.lib().ssm_ssd_bwd_workspace_size(ctypes.byref(d), ctypes.byref(m)) == ssm.SSM_OK
+    assert n.value - m.value == 2 * 4 * 80 * 4096 * 4 + 4 * nc * 80 * E * 4
 
 
 def test_ssd_workspace_size():

@@ -26,8 +26,8 @@ import selective_state_space_60_amd as ssm  # noqa: E402
 REL = 2e-2
 
 
-def _check(spec, seed=0, h0=False, dx_dtype=None, patch=None):
-    banner("ssd bwd %s seed %d h0%d" % (spec.name, seed, h0))
+def _check(spec, seed=0, h0=False, dx_dtype=None, patch=None, from_fwd=False):
+    banner("ssd bwd %s seed %d h0%d fwd%d" % (spec.name, seed, h0, from_fwd))
     inp = synth.ssd_inputs(spec, seed)
     if patch:
         patch(inp)
@@ -37,8 +37,13 @@ def _check(spec, seed=0, h0=False, dx_dtype=None, patch=None):
     g = {k: dev_tensor(inp[k], "bf16") for k in ("x", "delta", "B", "C")}
     A = dev_tensor(inp["A"], "f32")
     Dk = dev_tensor(inp["D"], "f32") if "D" in inp else None
+    h0d = None if h0v is None else torch.from_numpy(h0v).cuda()
+    saved = None
+    if from_fwd:   # the backward reads the forward's A_cum, beta and chunk states
+        _, _, saved = ssm.ssd_chunk_fwd_train(g["x"], g["delta"], A, g["B"], g["C"], spec.chunk, D=Dk, h0=h0d,
+                                              euler=spec.euler)
     got = ssm.ssd_bwd(dev_tensor(dy, "bf16"), g["x"], g["delta"], A, g["B"], g["C"], spec.chunk, D=Dk,
-                      h0=None if h0v is None else torch.from_numpy(h0v).cuda(), euler=spec.euler, dx_dtype=dx_dtype)
+                      h0=h0d, euler=spec.euler, dx_dtype=dx_dtype, fwd=saved)
     torch.cuda.synchronize()
     ref = oracle.ssd_bwd(inp, "bf16", dy, ngroups=spec.ngroups, euler=spec.euler,
                          h0=None if h0v is None else h0v.astype(np.float64))
@@ -123,3 +128,56 @@ def test_ssd_bwd_2_7b_full():
     """The 2.7B-shaped layer (batch 4, L 4096, 80 heads x 64, N 64, chunk
     256): every gradient against the oracle at full size."""
     _check(synth.SSD2_7B, 0)
+
+
+@pytest.mark.parametrize("kw,h0", [(dict(), True), (dict(seqlen=1000, chunk=256), False),
+                                   (dict(ngroups=2, euler=True, chunk=128), False),
+                                   (dict(dstate=128, chunk=128, seqlen=200), True),
+                                   (dict(dstate=256, chunk=64, seqlen=130), False)])
+def test_ssd_bwd_from_forward_intermediates(kw, h0):
+    """With the forward's A_cum, beta and chunk states passed in
+    (SSM_HAS_SSD_FWD): every gradient against the oracle, and equal bit for
+    bit to the backward that recomputes them (the same kernels on the same
+    values)."""
+    spec = small(**kw)
+    got = _check(spec, 7, h0=h0, from_fwd=True)
+    ref = _check(spec, 7, h0=h0)
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), k
+
+
+def test_ssd_forward_by_steps_keeps_intermediates():
+    """ssd_chunk_fwd_train runs the four steps: its y and h_last equal the
+    one-call forward's, and its kept A_cum, beta and states are the steps'
+    own outputs."""
+    spec = small(seqlen=333, chunk=128)
+    banner("ssd fwd train %s" % spec.name)
+    inp = synth.ssd_inputs(spec, 8)
+    g = {k: dev_tensor(inp[k], "bf16") for k in ("x", "delta", "B", "C")}
+    A, Dk = dev_tensor(inp["A"], "f32"), dev_tensor(inp["D"], "f32")
+    h0 = torch.from_numpy(synth.state_input((spec.batch, spec.nheads, spec.headdim, spec.dstate), 8)).cuda()
+    y, hl, saved = ssm.ssd_chunk_fwd_train(g["x"], g["delta"], A, g["B"], g["C"], spec.chunk, D=Dk, h0=h0,
+                                           want_hlast=True)
+    y1, hl1 = ssm.ssd_chunk_fwd(g["x"], g["delta"], A, g["B"], g["C"], spec.chunk, D=Dk, h0=h0, want_hlast=True)
+    A_cum, beta = ssm.ssd_chunk_cumsum(g["x"], g["delta"], A, g["B"], g["C"], spec.chunk)
+    states = ssm.ssd_chunk_state(g["x"], g["delta"], A, g["B"], g["C"], spec.chunk, A_cum, beta)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y1) and torch.equal(hl, hl1)
+    L = spec.seqlen
+    nc = -(-L // spec.chunk)
+    assert torch.equal(saved["states"], states)
+    # A_cum and beta are specified for the first seqlen steps of each row
+    for k, v in (("A_cum", A_cum), ("beta", beta)):
+        assert torch.equal(saved[k][..., :L], v[..., :L]), k
+    assert saved["A_cum"].shape == (spec.batch, spec.nheads, nc * spec.chunk)
+
+
+def test_ssd_bwd_fwd_shape_checked():
+    spec = small()
+    inp = synth.ssd_inputs(spec, 9)
+    g = {k: dev_tensor(inp[k], "bf16") for k in ("x", "delta", "B", "C")}
+    A = dev_tensor(inp["A"], "f32")
+    _, _, saved = ssm.ssd_chunk_fwd_train(g["x"], g["delta"], A, g["B"], g["C"], spec.chunk)
+    saved["states"] = saved["states"][:, :-1]   # one chunk short
+    with pytest.raises(ValueError):
+        ssm.ssd_bwd(g["x"], g["x"], g["delta"], A, g["B"], g["C"], spec.chunk, fwd=saved)
