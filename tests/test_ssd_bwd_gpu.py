@@ -181,3 +181,25 @@ def test_ssd_bwd_fwd_shape_checked():
     saved["states"] = saved["states"][:, :-1]   # one chunk short
     with pytest.raises(ValueError):
         ssm.ssd_bwd(g["x"], g["x"], g["delta"], A, g["B"], g["C"], spec.chunk, fwd=saved)
+
+
+def test_ssd_bwd_from_forward_2_7b_full_equals_recompute():
+    """At the 2.7B-shaped layer's full size, in the configuration the bench
+    times: the backward reading the forward's intermediates equals, bit for
+    bit, the recomputing backward (whose gradients the full-size oracle test
+    above checks)."""
+    spec = synth.SSD2_7B
+    banner("ssd bwd from fwd %s" % spec.name)
+    inp = synth.ssd_inputs(spec, 0)
+    dy = dev_tensor(synth.fill((spec.batch, spec.seqlen, spec.nheads, spec.headdim),
+                               synth.Dist(synth.NORMAL, 0.0, 1.0), "bf16", 0, 21), "bf16")
+    g = {k: dev_tensor(inp[k], "bf16") for k in ("x", "delta", "B", "C")}
+    A, Dk = dev_tensor(inp["A"], "f32"), dev_tensor(inp["D"], "f32")
+    del inp
+    _, _, saved = ssm.ssd_chunk_fwd_train(g["x"], g["delta"], A, g["B"], g["C"], spec.chunk, D=Dk)
+    a = ssm.ssd_bwd(dy, g["x"], g["delta"], A, g["B"], g["C"], spec.chunk, D=Dk, fwd=saved)
+    b = ssm.ssd_bwd(dy, g["x"], g["delta"], A, g["B"], g["C"], spec.chunk, D=Dk)
+    torch.cuda.synchronize()
+    assert set(a) == set(b)
+    for k in b:
+        assert torch.equal(a[k], b[k]), k
