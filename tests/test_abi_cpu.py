@@ -464,3 +464,20 @@ def test_conv_validation(mutate, status):
 def test_conv_null_descriptor():
     d, p = _conv()
     assert ssm.lib().ssm_causal_conv1d_fwd(None, ctypes.byref(p), None) == ssm.SSM_ERR_NULL
+
+
+@pytest.mark.parametrize("key,bad", [("A_cum", lambda t: t[..., :-1]), ("beta", lambda t: t.double()),
+                                     ("states", lambda t: t.transpose(3, 4))])
+def test_ssd_bwd_fwd_buffers_checked_by_the_binding(key, bad):
+    # the library sees bare pointers for the forward's intermediates, so the
+    # binding checks their shape, dtype and layout before any call
+    torch = _torch
+    batch, L, H, P, N, Q = 1, 100, 4, 64, 64, 64
+    bf = lambda *s: torch.zeros(s, dtype=torch.bfloat16)
+    x, dy, delta, B, C = bf(batch, L, H, P), bf(batch, L, H, P), bf(batch, L, H), bf(batch, L, 1, N), bf(batch, L, 1, N)
+    A = torch.zeros(H)
+    fwd = {"A_cum": torch.zeros(batch, H, 128), "beta": torch.zeros(batch, H, 128),
+           "states": torch.zeros(batch, 2, H, P, N)}
+    fwd[key] = bad(fwd[key])
+    with pytest.raises(ValueError, match=key):
+        ssm.ssd_bwd(dy, x, delta, A, B, C, Q, fwd=fwd)
