@@ -38,7 +38,9 @@
  *  - Errors: every entry point returns an ssm_status.  All checks except
  *    SSM_ERR_HIP happen on the host before any HIP call, so a rejected call
  *    has no side effects.  Values are never inspected: NaN/Inf propagate.
- *  - Thread safety: no mutable global state; calls may come from any thread.
+ *  - Thread safety: no mutable global state; calls may come from any thread
+ *    (except ssm_selective_scan_fwd_noalloc, whose device scratch is shared by
+ *    all calls on one GPU).
  */
 #ifndef SSM_H
 #define SSM_H
@@ -405,6 +407,26 @@ ssm_status ssm_selective_scan_workspace_size(const ssm_scan_desc* d, size_t* byt
  * overwritten.  Outputs: y, and h_last if SSM_WANT_HLAST. */
 ssm_status ssm_selective_scan_fwd(const ssm_scan_desc* d, const ssm_scan_ptrs* p, void* workspace,
                                   size_t workspace_bytes, void* hip_stream);
+
+/* Largest workspace (bytes) ssm_selective_scan_fwd_noalloc can serve. */
+#define SSM_SCAN_STATIC_SCRATCH_BYTES ((size_t)4 << 20)
+
+/* ssm_selective_scan_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace taken from a
+ * static device array of SSM_SCAN_STATIC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on until the process ends.  The caller still passes
+ * every input and output.  Never allocates or frees.
+ *  - Returns SSM_ERR_WORKSPACE, before any HIP call, when the workspace that
+ *    ssm_selective_scan_workspace_size reports for `d` exceeds
+ *    SSM_SCAN_STATIC_SCRATCH_BYTES (long, narrow problems whose sequence is
+ *    cut into many segments); other errors as ssm_selective_scan_fwd.
+ *  - The first call on a device looks up the array's device address (one
+ *    hipGetSymbolAddress, with that device current).
+ *  - Every call on a GPU shares that GPU's array: calls that overlap on one
+ *    GPU (different streams, or threads) race and must be serialised by the
+ *    caller.  Nothing in the array needs clearing between calls. */
+ssm_status ssm_selective_scan_fwd_noalloc(const ssm_scan_desc* d, const ssm_scan_ptrs* p, void* hip_stream);
 
 /* Bytes of device workspace ssm_ssd_chunk_fwd needs for `d`. */
 ssm_status ssm_ssd_chunk_workspace_size(const ssm_ssd_desc* d, size_t* bytes);

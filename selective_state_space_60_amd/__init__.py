@@ -31,7 +31,7 @@ EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_hip_error", "ssm_se
            "ssm_selective_scan_fwd", "ssm_ssd_chunk_workspace_size", "ssm_ssd_chunk_fwd", "ssm_ssd_chunk_cumsum",
            "ssm_ssd_chunk_state", "ssm_ssd_state_passing", "ssm_ssd_chunk_scan", "ssm_selective_state_update",
            "ssm_causal_conv1d_fwd", "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd",
-           "ssm_ssd_bwd_workspace_size", "ssm_ssd_bwd")
+           "ssm_ssd_bwd_workspace_size", "ssm_ssd_bwd", "ssm_selective_scan_fwd_noalloc")
 
 
 class TensorDesc(ctypes.Structure):
@@ -134,6 +134,7 @@ def lib() -> ctypes.CDLL:
         L.ssm_last_hip_error.restype = ctypes.c_int
         L.ssm_selective_scan_workspace_size.argtypes = [P(ScanDesc), P(sz)]
         L.ssm_selective_scan_fwd.argtypes = [P(ScanDesc), P(ScanPtrs), vp, sz, vp]
+        L.ssm_selective_scan_fwd_noalloc.argtypes = [P(ScanDesc), P(ScanPtrs), vp]
         L.ssm_ssd_chunk_workspace_size.argtypes = [P(SSDDesc), P(sz)]
         L.ssm_ssd_chunk_fwd.argtypes = [P(SSDDesc), P(SSDPtrs), vp, sz, vp]
         L.ssm_ssd_chunk_cumsum.argtypes = [P(SSDDesc), P(SSDPtrs), vp, vp, vp]
@@ -261,6 +262,26 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, euler=False, 
     ws = _workspace(nbytes, x.device)
     _check(lib().ssm_selective_scan_fwd(ctypes.byref(desc), ctypes.byref(ptrs), _p(ws), nbytes, _stream(stream)),
            "ssm_selective_scan_fwd")
+    return y, h_last
+
+
+SCAN_STATIC_SCRATCH_BYTES = 4 << 20  # SSM_SCAN_STATIC_SCRATCH_BYTES
+
+
+def selective_scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, h0=None, euler=False, want_hlast=False,
+                               y_dtype=None, y=None, stream=None, delta_softplus=False, delta_bias=None, ckpt=None):
+    """selective_scan_fwd through ssm_selective_scan_fwd_noalloc: no workspace
+    is allocated; the library's static device scratch serves as one (calls on
+    one GPU must not overlap).  Pass y (and h_last through want_hlast=False)
+    preallocated to keep the call free of allocations."""
+    if y is None:
+        y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
+    h_last = torch.empty((x.shape[0], x.shape[2], A.shape[-1]), dtype=torch.float32,
+                         device=x.device) if want_hlast else None
+    desc = scan_desc(x, delta, A, B, C, D, z, y, h0, h_last, euler, delta_softplus, delta_bias, ckpt)
+    ptrs = scan_ptrs(x, delta, A, B, C, D, z, y, h0, h_last, delta_bias, ckpt)
+    _check(lib().ssm_selective_scan_fwd_noalloc(ctypes.byref(desc), ctypes.byref(ptrs), _stream(stream)),
+           "ssm_selective_scan_fwd_noalloc")
     return y, h_last
 
 

@@ -57,6 +57,8 @@
 //    writes y.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -810,6 +812,33 @@ hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Workspace of the allocation-free entry point: one copy per GPU, alive until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// the device array: kernels are given the address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[kScanStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null: not looked up yet)
+}  // namespace
+
+hipError_t scan_static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_selective_scan(const ScanParams& p, hipStream_t stream) {
   // Tile pieces load 4 consecutive elements per lane: every row of x, delta,

@@ -701,6 +701,45 @@ ssm_status hip_status(hipError_t e) {
   return SSM_ERR_HIP;
 }
 
+// Fills the kernel parameters of a validated scan and launches it; the
+// workspace (pl.ws_total bytes, 256-byte aligned) is the caller's or the
+// static scratch.
+ssm_status launch_scan_fwd(const ssm_scan_desc* d, const ssm_scan_ptrs* p, const ScanPlan& pl, void* workspace,
+                           void* hip_stream) {
+  ssm::ScanParams q;
+  std::memset(&q, 0, sizeof(q));
+  const uint32_t f = d->flags;
+  q.x = p->x; q.delta = p->delta; q.z = (f & SSM_HAS_Z) ? p->z : nullptr; q.y = p->y;
+  q.B = p->B; q.C = p->C; q.A = p->A; q.Dskip = (f & SSM_HAS_D) ? p->D : nullptr;
+  q.h0 = (f & SSM_HAS_H0) ? p->h0 : nullptr;
+  q.h_last = (f & SSM_WANT_HLAST) ? p->h_last : nullptr;
+  q.batch = d->batch; q.L = d->seqlen; q.D = d->dim; q.N = d->dstate;
+  q.xs_b = d->x.stride[0]; q.xs_t = d->x.stride[1];
+  q.ds_b = d->delta.stride[0]; q.ds_t = d->delta.stride[1];
+  if (f & SSM_HAS_Z) { q.zs_b = d->z.stride[0]; q.zs_t = d->z.stride[1]; }
+  q.ys_b = d->y.stride[0]; q.ys_t = d->y.stride[1];
+  q.Bs_b = d->B.stride[0]; q.Bs_t = d->B.stride[1]; q.Bs_n = d->B.stride[2];
+  q.Cs_b = d->C.stride[0]; q.Cs_t = d->C.stride[1]; q.Cs_n = d->C.stride[2];
+  q.As_d = d->A.stride[0]; q.As_n = d->A.stride[1];
+  q.Ds_d = (f & SSM_HAS_D) ? d->D.stride[0] : 0;
+  q.flags = f;
+  q.io_bf16 = d->x.dtype == SSM_BF16;
+  q.y_f32 = d->y.dtype == SSM_F32;
+  q.dsoftplus = (f & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+  q.dbias = (f & SSM_HAS_DELTA_BIAS) ? p->delta_bias : nullptr;
+  q.dbs_d = (f & SSM_HAS_DELTA_BIAS) ? d->delta_bias.stride[0] : 0;
+  q.ckpt = (f & SSM_WANT_CKPT) ? p->ckpt : nullptr;
+  q.n_seg = pl.n_seg;
+  q.seg_len = pl.seg_len;
+  if (pl.n_seg > 1) {
+    char* w = (char*)workspace;
+    q.agg_H = (float*)w;
+    q.agg_S = (float*)(w + pl.ws_H);
+    q.h_in = (float*)(w + pl.ws_H + pl.ws_S);
+  }
+  return hip_status(ssm::launch_selective_scan(q, (hipStream_t)hip_stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -743,38 +782,22 @@ ssm_status ssm_selective_scan_fwd(const ssm_scan_desc* d, const ssm_scan_ptrs* p
     if (!workspace || workspace_bytes < (size_t)pl.ws_total) return SSM_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SSM_ERR_ALIGN;
   }
-  ssm::ScanParams q;
-  std::memset(&q, 0, sizeof(q));
-  const uint32_t f = d->flags;
-  q.x = p->x; q.delta = p->delta; q.z = (f & SSM_HAS_Z) ? p->z : nullptr; q.y = p->y;
-  q.B = p->B; q.C = p->C; q.A = p->A; q.Dskip = (f & SSM_HAS_D) ? p->D : nullptr;
-  q.h0 = (f & SSM_HAS_H0) ? p->h0 : nullptr;
-  q.h_last = (f & SSM_WANT_HLAST) ? p->h_last : nullptr;
-  q.batch = d->batch; q.L = d->seqlen; q.D = d->dim; q.N = d->dstate;
-  q.xs_b = d->x.stride[0]; q.xs_t = d->x.stride[1];
-  q.ds_b = d->delta.stride[0]; q.ds_t = d->delta.stride[1];
-  if (f & SSM_HAS_Z) { q.zs_b = d->z.stride[0]; q.zs_t = d->z.stride[1]; }
-  q.ys_b = d->y.stride[0]; q.ys_t = d->y.stride[1];
-  q.Bs_b = d->B.stride[0]; q.Bs_t = d->B.stride[1]; q.Bs_n = d->B.stride[2];
-  q.Cs_b = d->C.stride[0]; q.Cs_t = d->C.stride[1]; q.Cs_n = d->C.stride[2];
-  q.As_d = d->A.stride[0]; q.As_n = d->A.stride[1];
-  q.Ds_d = (f & SSM_HAS_D) ? d->D.stride[0] : 0;
-  q.flags = f;
-  q.io_bf16 = d->x.dtype == SSM_BF16;
-  q.y_f32 = d->y.dtype == SSM_F32;
-  q.dsoftplus = (f & SSM_DELTA_SOFTPLUS) ? 1 : 0;
-  q.dbias = (f & SSM_HAS_DELTA_BIAS) ? p->delta_bias : nullptr;
-  q.dbs_d = (f & SSM_HAS_DELTA_BIAS) ? d->delta_bias.stride[0] : 0;
-  q.ckpt = (f & SSM_WANT_CKPT) ? p->ckpt : nullptr;
-  q.n_seg = pl.n_seg;
-  q.seg_len = pl.seg_len;
-  if (pl.n_seg > 1) {
-    char* w = (char*)workspace;
-    q.agg_H = (float*)w;
-    q.agg_S = (float*)(w + pl.ws_H);
-    q.h_in = (float*)(w + pl.ws_H + pl.ws_S);
+  return launch_scan_fwd(d, p, pl, workspace, hip_stream);
+}
+
+ssm_status ssm_selective_scan_fwd_noalloc(const ssm_scan_desc* d, const ssm_scan_ptrs* p, void* hip_stream) {
+  ssm_status s = validate_scan_desc(d);
+  if (s) return s;
+  if ((s = validate_scan_ptrs(d, p))) return s;
+  const ScanPlan pl = plan_scan(*d);
+  static_assert(SSM_SCAN_STATIC_SCRATCH_BYTES == ssm::kScanStaticScratchBytes, "scratch size");
+  if ((size_t)pl.ws_total > SSM_SCAN_STATIC_SCRATCH_BYTES) return SSM_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (pl.ws_total > 0) {
+    hipError_t e = ssm::scan_static_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e);
   }
-  return hip_status(ssm::launch_selective_scan(q, (hipStream_t)hip_stream));
+  return launch_scan_fwd(d, p, pl, ws, hip_stream);
 }
 
 ssm_status ssm_ssd_chunk_workspace_size(const ssm_ssd_desc* d, size_t* bytes) {

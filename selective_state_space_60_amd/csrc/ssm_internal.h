@@ -50,6 +50,11 @@ constexpr int kScanThreads = kScanLanesPerChannel * kScanChannelsPerBlock;
 
 hipError_t launch_selective_scan(const ScanParams& p, hipStream_t stream);
 
+// Device address of the current device's static scan scratch (the workspace
+// of the allocation-free scan entry point), looked up once per device.
+constexpr size_t kScanStaticScratchBytes = (size_t)4 << 20;
+hipError_t scan_static_scratch(void** ptr);
+
 // ------------------------------------------------------------------- decode
 struct UpdateParams {
   const void* x;      // (batch, D)
