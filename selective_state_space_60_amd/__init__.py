@@ -389,14 +389,15 @@ def ssd_chunk_fwd_train(x, delta, A, B, C, chunk, D=None, h0=None, euler=False, 
                         stream=None):
     """SSD forward by its four steps, keeping what ssd_bwd(..., fwd=saved)
     takes instead of recomputing it.  Returns (y, h_last or None, saved) with
-    saved = {"A_cum", "beta", "states"}."""
+    saved = {"A_cum", "beta", "states", "chunk", "euler"} (the last two let
+    ssd_bwd refuse a backward of another chunk size or discretisation)."""
     A_cum, beta = ssd_chunk_cumsum(x, delta, A, B, C, chunk, euler=euler, stream=stream)
     states = ssd_chunk_state(x, delta, A, B, C, chunk, A_cum, beta, euler=euler, stream=stream)
     S_in, h_last = ssd_state_passing(x, delta, A, B, C, chunk, A_cum, states, h0=h0, want_hlast=want_hlast,
                                      euler=euler, stream=stream)
     y = ssd_chunk_scan(x, delta, A, B, C, chunk, A_cum, beta, S_in, D=D, euler=euler, y_dtype=y_dtype,
                        stream=stream)
-    return y, h_last, {"A_cum": A_cum, "beta": beta, "states": states}
+    return y, h_last, {"A_cum": A_cum, "beta": beta, "states": states, "chunk": chunk, "euler": bool(euler)}
 
 
 # ------------------------------------------------------------------ decode
@@ -544,6 +545,10 @@ def ssd_bwd(dy, x, delta, A, B, C, chunk, D=None, h0=None, euler=False, dx_dtype
     for name, t in list(zip(_SSD_BWD_IN, (x, delta, A, B, C, D, h0, dy))) + [(k, out[k]) for k in _SSD_BWD_OUT]:
         setattr(p, name, _p(t))
     if fwd is not None:
+        # intermediates of another chunk size or discretisation would give wrong gradients
+        for k, v in (("chunk", chunk), ("euler", bool(euler))):
+            if k in fwd and fwd[k] != v:
+                raise ValueError(f"ssd_bwd: fwd was computed with {k}={fwd[k]!r}, this backward has {k}={v!r}")
         # the library sees bare pointers here, so the shapes are checked on this side
         _, _, _, _, nc, Lp = _ssd_shapes(x, B, chunk)
         want = {"A_cum": (batch, H, Lp), "beta": (batch, H, Lp), "states": (batch, nc, H, P, N)}

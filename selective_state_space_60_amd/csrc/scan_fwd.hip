@@ -49,12 +49,18 @@
 //    workgroup barrier; the results go through LDS to the stores of the next
 //    tile.
 //  * When batch x channels cannot fill the GPU (long, narrow problems), the
-//    sequence is cut into segments: (1) each segment but the last is scanned
-//    from h = 0 for its end state and its sum of delta, (2) a small kernel
-//    chains those into the state entering each segment (the associative
-//    combine of (Abar, Bbar x) pairs -- tildalice.io, 병렬 스캔 -- at segment
-//    granularity), (3) every segment is scanned from its entering state and
-//    writes y.
+//    sequence is cut into segments: (1) every segment is scanned from h = 0
+//    (the first from h0) and writes y, and each but the last also its end
+//    state and its sum of delta; (2) a small kernel chains those into the
+//    state entering each segment (the associative combine of (Abar, Bbar x)
+//    pairs -- tildalice.io, 병렬 스캔 -- at segment granularity); (3) each
+//    later segment is scanned again from its entering state, next to a twin
+//    of the first pass's states from zero.  The two differ by the entering
+//    state times the running product of Abar, which decays; once every state
+//    equals its twin bit for bit (checked at the end of each tile), the rest
+//    of the first pass's output is exactly what the rescan would write, and
+//    the rescan stops.  A decaying model rescans a short prefix of each
+//    segment; with no decay the rescan runs to the segment's end.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -434,13 +440,23 @@ __device__ __forceinline__ void take_hold(const ScanSmem<KS>& s, int buf, bool w
   hd.z = want_z ? s.hz[buf][tid / G][tid % G] : 0.f;
 }
 
+// One state update of the form FORM with the step's factors.
+template <int FORM>
+__device__ __forceinline__ float update(float h, float Ab, float q, float c) {
+  if constexpr (FORM == kFormG) return __builtin_fmaf(Ab, h + q, -q);
+  else if constexpr (FORM == kFormEuler) return __builtin_fmaf(Ab, h, q);
+  else return __builtin_fmaf(Ab, h, c * q);
+}
+
 // One step (step T of the tile) of one lane's KS states; returns the lane's
 // partial readout.  delta and x come from lane T of the row.  No implicit
 // fusing of multiplies into adds here: that would turn the broadcast
-// multiplies into fmas, which cannot take the DPP operand.
-template <int KS, int FORM, bool READOUT, int T>
-__device__ __forceinline__ float step(float (&h)[KS], const Lane<KS>& ln, const Hold& hd, const float4 (&bc)[KS],
-                                      bool hi) {
+// multiplies into fmas, which cannot take the DPP operand.  With TWIN, a
+// second set of states h2 takes the same step (same factors, same
+// operations, so the same roundings), and only h is read out.
+template <int KS, int FORM, bool TWIN, int T>
+__device__ __forceinline__ float step(float (&h)[KS], float (&h2)[KS], const Lane<KS>& ln, const Hold& hd,
+                                      const float4 (&bc)[KS], bool hi) {
 #pragma clang fp contract(off)
   float yp = 0.f;
 #pragma unroll
@@ -449,18 +465,16 @@ __device__ __forceinline__ float step(float (&h)[KS], const Lane<KS>& ln, const 
     const float Cv = hi ? bc[k].w : bc[k].y;
     const float Ab = __builtin_amdgcn_exp2f(row_bcast<T>(hd.dt) * ln.A2[k]);
     const float q = row_bcast<T>(hd.xs) * Bv;  // B*x (B*delta*x in the Euler form)
-    if constexpr (FORM == kFormG) {
-      h[k] = __builtin_fmaf(Ab, h[k] + q, -q);
-    } else if constexpr (FORM == kFormEuler) {
-      h[k] = __builtin_fmaf(Ab, h[k], q);
-    } else {
+    float c = 0.f;
+    if constexpr (FORM == kFormH || FORM == kFormHZero) {
       // (Abar - 1)/A as Abar*(1/A) - 1/A with one rounding; with A == 0 the
       // factor is 0 and ez*delta supplies the limit delta.
-      float c = __builtin_fmaf(Ab, ln.iA[k], -ln.iA[k]);
+      c = __builtin_fmaf(Ab, ln.iA[k], -ln.iA[k]);
       if constexpr (FORM == kFormHZero) c = __builtin_fmaf(ln.ez[k], row_bcast<T>(hd.dt), c);
-      h[k] = __builtin_fmaf(Ab, h[k], c * q);
     }
-    if constexpr (READOUT) yp = k == 0 ? Cv * h[k] : __builtin_fmaf(Cv, h[k], yp);
+    h[k] = update<FORM>(h[k], Ab, q, c);
+    if constexpr (TWIN) h2[k] = update<FORM>(h2[k], Ab, q, c);
+    yp = k == 0 ? Cv * h[k] : __builtin_fmaf(Cv, h[k], yp);
   }
   return yp;
 }
@@ -476,19 +490,20 @@ __device__ __forceinline__ void read_block(const ScanSmem<KS>& s, int buf, int t
 
 // Blocks BLK.. of one tile: operands of block BLK+1 are read while block BLK
 // is scanned.  prow: this lane's row of partials (column 16*channel).
-template <int KS, int FORM, bool READOUT, int BLK>
+template <int KS, int FORM, bool TWIN, int BLK>
 __device__ __forceinline__ void scan_blocks(const ScanSmem<KS>& s, float* prow, int buf, int sg, float (&h)[KS],
-                                            const Lane<KS>& ln, const Hold& hd, float4 (&o)[2][2][KS]) {
+                                            float (&h2)[KS], const Lane<KS>& ln, const Hold& hd,
+                                            float4 (&o)[2][2][KS]) {
   if constexpr (BLK < TT / UB) {
     if constexpr (BLK + 1 < TT / UB) read_block<KS>(s, buf, (BLK + 1) * UB, sg, o[(BLK + 1) & 1]);
     const float4(&c)[2][KS] = o[BLK & 1];
     float yp[UB];
-    yp[0] = step<KS, FORM, READOUT, UB * BLK + 0>(h, ln, hd, c[0], false);
-    yp[1] = step<KS, FORM, READOUT, UB * BLK + 1>(h, ln, hd, c[0], true);
-    yp[2] = step<KS, FORM, READOUT, UB * BLK + 2>(h, ln, hd, c[1], false);
-    yp[3] = step<KS, FORM, READOUT, UB * BLK + 3>(h, ln, hd, c[1], true);
-    if (READOUT) *(float4*)&prow[UB * BLK] = make_float4(yp[0], yp[1], yp[2], yp[3]);
-    scan_blocks<KS, FORM, READOUT, BLK + 1>(s, prow, buf, sg, h, ln, hd, o);
+    yp[0] = step<KS, FORM, TWIN, UB * BLK + 0>(h, h2, ln, hd, c[0], false);
+    yp[1] = step<KS, FORM, TWIN, UB * BLK + 1>(h, h2, ln, hd, c[0], true);
+    yp[2] = step<KS, FORM, TWIN, UB * BLK + 2>(h, h2, ln, hd, c[1], false);
+    yp[3] = step<KS, FORM, TWIN, UB * BLK + 3>(h, h2, ln, hd, c[1], true);
+    *(float4*)&prow[UB * BLK] = make_float4(yp[0], yp[1], yp[2], yp[3]);
+    scan_blocks<KS, FORM, TWIN, BLK + 1>(s, prow, buf, sg, h, h2, ln, hd, o);
   }
 }
 
@@ -519,12 +534,16 @@ struct CkptOut {
   int nk;
 };
 
-// The walk over the stretch, for one update form.  MODE 0 writes y (and the
-// checkpoints); MODE 1 only carries the state (from 0) and this lane's share
-// of the sum of delta (the steps it holds).
+// The walk over the stretch, for one update form; writes y and the
+// checkpoints.  MODE 0 also sums this lane's share of delta (the steps it
+// holds).  MODE 2 carries a twin of the states, h2, started where the first
+// pass over the stretch started (zero), and ends the walk after the first
+// tile at whose end every state of the workgroup equals its twin bit for bit:
+// from there on, the first pass's states, y and checkpoints are exactly the
+// ones this walk would produce.  Returns whether the walk ended that way.
 template <class L, int KS, int MODE, int FORM>
-__device__ __forceinline__ void walk(ScanSmem<KS>& s, L& ld, const Tiles& tl, float (&h)[KS], const Lane<KS>& ln,
-                                     const float (&fA)[G], float Dk, bool want_z, float& sum_dt,
+__device__ __forceinline__ bool walk(ScanSmem<KS>& s, L& ld, const Tiles& tl, float (&h)[KS], float (&h2)[KS],
+                                     const Lane<KS>& ln, const float (&fA)[G], float Dk, bool want_z, float& sum_dt,
                                      const DeltaXform& dx, const CkptOut& ck) {
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, sg = tid % G;
@@ -547,11 +566,12 @@ __device__ __forceinline__ void walk(ScanSmem<KS>& s, L& ld, const Tiles& tl, fl
   // One tile: take this lane's step, scan, finalize into yb, store the
   // previous tile's y, stage tile it+1 (held in rn) and refill rn.  Loads
   // are issued whatever `it` (past the stretch they read nothing): a branch
-  // around them would make the compiler wait for them at once.
-  auto body = [&](int it, typename L::Set& rn) {
+  // around them would make the compiler wait for them at once.  Returns
+  // (MODE 2) whether the states and their twins now agree.
+  auto body = [&](int it, typename L::Set& rn) -> bool {
     const int buf = it & 1;
     const int rows = it < tl.ntiles - 1 ? TT : (it == tl.ntiles - 1 ? tl.last_rows : 0);
-    if (MODE == 0 && ck.p && it < tl.ntiles) {
+    if (ck.p && it < tl.ntiles) {
 #pragma unroll
       for (int k = 0; k < KS; ++k)  // the g form carries A h
         if (k < ck.nk) ck.p[it * ck.step + k] = FORM == kFormG ? h[k] * ln.iA[k] : h[k];
@@ -559,32 +579,47 @@ __device__ __forceinline__ void walk(ScanSmem<KS>& s, L& ld, const Tiles& tl, fl
     take_hold<KS, FORM>(s, buf, want_z, hd, dx, sg < rows);
     float4 o[2][2][KS];
     read_block<KS>(s, buf, 0, sg, o[0]);
-    scan_blocks<KS, FORM, MODE == 0, 0>(s, prow, buf, sg, h, ln, hd, o);
-    if (MODE == 0) {
-      finalize_tile<KS, FORM>(s, buf, pcol, fA, Dk, hd, want_z);
-      if (it > 0) ld.store_y(s, tl, buf ^ 1, it - 1);
-    } else {
-      sum_dt += hd.dt;
-    }
+    scan_blocks<KS, FORM, MODE == 2, 0>(s, prow, buf, sg, h, h2, ln, hd, o);
+    finalize_tile<KS, FORM>(s, buf, pcol, fA, Dk, hd, want_z);
+    if (it > 0) ld.store_y(s, tl, buf ^ 1, it - 1);
+    if (MODE == 0) sum_dt += hd.dt;
     if (it + 1 < nrun) ld.stage(s, tl, buf ^ 1, it + 1, rn);
     ld.load(tl, it + 1 + L::kDepth, rn);
-    __syncthreads();
+    if constexpr (MODE == 2) {
+      bool same = true;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) same = same && (__float_as_uint(h[k]) == __float_as_uint(h2[k]));
+      return __syncthreads_and(same) != 0;
+    } else {
+      __syncthreads();
+      return false;
+    }
   };
+  int last = nrun - 1;
+  bool met = false;
   if constexpr (L::kDepth == 2) {
     for (int it = 0; it < nrun; it += 2) {
-      body(it, rb);
-      body(it + 1, ra);
+      if (body(it, rb)) { last = it; met = true; break; }
+      if (body(it + 1, ra)) { last = it + 1; met = true; break; }
     }
   } else {
-    for (int it = 0; it < nrun; ++it) body(it, ra);
+    for (int it = 0; it < nrun; ++it)
+      if (body(it, ra)) { last = it; met = true; break; }
   }
-  if (MODE == 0) ld.store_y(s, tl, (nrun - 1) & 1, nrun - 1);
+  ld.store_y(s, tl, last & 1, last);
+  return met;
 }
 
-// MODE 0: write y (and h_last / start from h_in).  MODE 1: segment aggregates.
+// MODE 0: scan the stretch and write y (and h_last, the checkpoints).  With
+// the sequence split, every segment starts from zero (segment 0 from h0) and
+// each segment but the last writes its aggregate (end state, sum of delta).
+// MODE 2 (split only; segments 1..n_seg-1): rescan a segment from the state
+// entering it, next to a twin started from zero, until the two agree.
+// (The fp32 single-state first pass is held to five waves per SIMD, the
+// occupancy the planner's segment count assumes.)
 template <bool BF16, bool VEC, int KS, int MODE>
-__global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, int64_t nseg_run,
-                                                  int64_t nblocks_padded) {
+__global__ __launch_bounds__(NT, (!BF16 && KS == 1 && MODE == 0) ? 5 : 1) void scan_kernel(
+    ScanParams p, int64_t n_dblk, int64_t nseg_run, int64_t nblocks_padded) {
   __shared__ ScanSmem<KS> s;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;  // wave: uniform (SGPR)
@@ -593,12 +628,12 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   const int64_t lb = logical_block(nblocks_padded);
   if (lb >= n_dblk * nseg_run * p.batch) return;
   const int64_t dblk = lb % n_dblk;
-  const int64_t seg = (lb / n_dblk) % nseg_run;
+  const int64_t seg = (MODE == 2 ? 1 : 0) + (lb / n_dblk) % nseg_run;
   const int64_t b = lb / (n_dblk * nseg_run);
   const int64_t d0 = dblk * CH;
   const int64_t d = d0 + chb;  // this lane's channel (scan and finalize)
   const bool d_ok = d < p.D;
-  const bool want_z = MODE == 0 && (p.flags & kHasZ);
+  const bool want_z = (p.flags & kHasZ) != 0;
   const int64_t esz = BF16 ? 2 : 4;
   const int64_t yesz = (p.y_f32 || !BF16) ? 4 : 2;
 
@@ -610,7 +645,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
 
   // Per-lane constants of this lane's KS states.
   Lane<KS> ln;
-  float Av[KS], h[KS];
+  float Av[KS], h[KS], h2[KS];
   int zero_A = 0;
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
@@ -623,11 +658,12 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
     ln.iA[k] = a != 0.f ? 1.f / a : 0.f;
     ln.ez[k] = a == 0.f ? 1.f : 0.f;
     h[k] = 0.f;
+    h2[k] = 0.f;
   }
-  if (MODE == 0) {
+  {
     const float* src = nullptr;
-    if (p.n_seg > 1) src = p.h_in + ((b * p.n_seg + seg) * p.D) * p.N;
-    else if (p.flags & kHasH0) src = p.h0 + (b * p.D) * p.N;
+    if (MODE == 2) src = p.h_in + ((b * p.n_seg + seg) * p.D) * p.N;
+    else if (seg == 0 && (p.flags & kHasH0)) src = p.h0 + (b * p.D) * p.N;
     if (src && d_ok) {
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
@@ -639,7 +675,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   const bool any_zero_A = __syncthreads_or(zero_A) != 0;
 
   float Dk = 0.f;
-  if (MODE == 0 && (p.flags & kHasD) && d_ok) Dk = p.Dskip[d * p.Ds_d];
+  if ((p.flags & kHasD) && d_ok) Dk = p.Dskip[d * p.Ds_d];
 
   // Streams: each starts at row t_begin of batch row b and advances one tile
   // of rows at a time.  The last tile's range ends at its last row's last
@@ -671,8 +707,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
       ld.sp[j] = make_span(base, b * sb + t_begin * st + col0, st, 1, width, esz, rows_last, live);
       ld.voff[j] = (uint32_t)((ld.r * st + 4 * ld.q) * esz);
     }
-    ld.y = make_span(MODE == 0 ? p.y : p.x, b * p.ys_b + t_begin * p.ys_t + d0, p.ys_t, 1, p.D - d0, yesz,
-                     rows_last, MODE == 0);
+    ld.y = make_span(p.y, b * p.ys_b + t_begin * p.ys_t + d0, p.ys_t, 1, p.D - d0, yesz, rows_last, true);
     ld.oy = (uint32_t)((ld.r * p.ys_t + 4 * ld.q) * yesz);
     ld.y_ok = d0 + 4 * ld.q < p.D;
     ld.clear_rows(s, (int)p.N);
@@ -686,8 +721,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
                      want_z);
     ld.B = make_span(p.B, b * p.Bs_b + t_begin * p.Bs_t, p.Bs_t, p.Bs_n, p.N, esz, rows_last, true);
     ld.C = make_span(p.C, b * p.Cs_b + t_begin * p.Cs_t, p.Cs_t, p.Cs_n, p.N, esz, rows_last, true);
-    ld.y = make_span(MODE == 0 ? p.y : p.x, b * p.ys_b + t_begin * p.ys_t + d0, p.ys_t, 1, p.D - d0, yesz,
-                     rows_last, MODE == 0);
+    ld.y = make_span(p.y, b * p.ys_b + t_begin * p.ys_t + d0, p.ys_t, 1, p.D - d0, yesz, rows_last, true);
     ld.ox = (uint32_t)((ld.t * p.xs_t + sg) * esz);
     ld.odl = (uint32_t)((ld.t * p.ds_t + sg) * esz);
     ld.oz = (uint32_t)((ld.t * p.zs_t + sg) * esz);
@@ -715,7 +749,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   ck.p = nullptr;
   ck.step = p.D * p.N;
   ck.nk = 0;
-  if (MODE == 0 && p.ckpt && d_ok) {
+  if (p.ckpt && d_ok) {
     const int64_t n0 = sg * KS;
     ck.nk = n0 >= p.N ? 0 : (p.N - n0 < KS ? (int)(p.N - n0) : KS);
     ck.p = p.ckpt + ((b * ((p.L + TT - 1) / TT) + t_begin / TT) * p.D + d) * p.N + (n0 < p.N ? n0 : 0);
@@ -723,44 +757,45 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   DeltaXform dx;
   dx.on = p.dsoftplus != 0;
   dx.bias = (dx.on && p.dbias && d_ok) ? p.dbias[d * p.dbs_d] : 0.f;
+  bool met = false;
   if (KS == 1 && form == kFormG) {
     // g form: the finalize weighs the partial of state n by 1/A of the lane's channel.
-    if (MODE == 0) {
 #pragma unroll
-      for (int n = 0; n < G; ++n) {
-        float a = -1.f;
-        if (d_ok && n < p.N) a = p.A[d * p.As_d + n * p.As_n];
-        fA[n] = 1.f / a;
-      }
+    for (int n = 0; n < G; ++n) {
+      float a = -1.f;
+      if (d_ok && n < p.N) a = p.A[d * p.As_d + n * p.As_n];
+      fA[n] = 1.f / a;
     }
 #pragma unroll
-    for (int k = 0; k < KS; ++k) h[k] *= Av[k];  // g = A h
-    walk<decltype(ld), KS, MODE, kFormG>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx, ck);
+    for (int k = 0; k < KS; ++k) h[k] *= Av[k];  // g = A h (the twin starts at 0)
+    met = walk<decltype(ld), KS, MODE, kFormG>(s, ld, tl, h, h2, ln, fA, Dk, want_z, sum_dt, dx, ck);
 #pragma unroll
     for (int k = 0; k < KS; ++k) h[k] *= ln.iA[k];  // h = g / A
   } else if (form == kFormEuler) {
-    walk<decltype(ld), KS, MODE, kFormEuler>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx, ck);
+    met = walk<decltype(ld), KS, MODE, kFormEuler>(s, ld, tl, h, h2, ln, fA, Dk, want_z, sum_dt, dx, ck);
   } else if (form == kFormHZero) {
-    walk<decltype(ld), KS, MODE, kFormHZero>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx, ck);
+    met = walk<decltype(ld), KS, MODE, kFormHZero>(s, ld, tl, h, h2, ln, fA, Dk, want_z, sum_dt, dx, ck);
   } else {
-    walk<decltype(ld), KS, MODE, kFormH>(s, ld, tl, h, ln, fA, Dk, want_z, sum_dt, dx, ck);
+    met = walk<decltype(ld), KS, MODE, kFormH>(s, ld, tl, h, h2, ln, fA, Dk, want_z, sum_dt, dx, ck);
   }
 
-  if (MODE == 1) {
+  const bool split = p.n_seg > 1;
+  if (MODE == 0 && split) {
     // the row's 16 lanes each summed the steps they hold
 #pragma unroll
     for (int m = 1; m < G; m <<= 1) sum_dt += __shfl_xor(sum_dt, m, G);
   }
   if (!d_ok) return;
-  if (MODE == 0) {
-    if (seg == p.n_seg - 1 && (p.flags & kWantHLast)) {
+  // h_last: the last segment's end state.  A MODE 2 walk that met its twin
+  // leaves the first pass's (equal) one in place.
+  if (seg == p.n_seg - 1 && (p.flags & kWantHLast) && !met) {
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const int n = sg * KS + k;
-        if (n < p.N) p.h_last[(b * p.D + d) * p.N + n] = h[k];
-      }
+    for (int k = 0; k < KS; ++k) {
+      const int n = sg * KS + k;
+      if (n < p.N) p.h_last[(b * p.D + d) * p.N + n] = h[k];
     }
-  } else {
+  }
+  if (MODE == 0 && split && seg < p.n_seg - 1) {
     float* H = p.agg_H + ((b * (p.n_seg - 1) + seg) * p.D + d) * p.N;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
@@ -771,19 +806,21 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanParams p, int64_t n_dblk, 
   }
 }
 
-// Chain segment aggregates: h_in[0] = h0 or 0; h_in[s+1] = exp(A*S_s) h_in[s] + H_s.
+// States entering segments 1..n_seg-1 from the first pass's aggregates
+// (segment 0's includes h0):  h_in[1] = H_0;  h_in[s+1] = exp(A*S_s) h_in[s] + H_s.
 __global__ __launch_bounds__(256) void scan_combine_kernel(ScanParams p) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over batch*D*N
   if (i >= p.batch * p.D * p.N) return;
   const int64_t n = i % p.N, d = (i / p.N) % p.D, b = i / (p.N * p.D);
   const float a2 = p.A[d * p.As_d + n * p.As_n] * kLog2e;
-  float h = (p.flags & kHasH0) ? p.h0[i] : 0.f;
-  p.h_in[((b * p.n_seg + 0) * p.D + d) * p.N + n] = h;
-  for (int s = 0; s + 1 < p.n_seg; ++s) {
-    const float S = p.agg_S[(b * (p.n_seg - 1) + s) * p.D + d];
-    const float H = p.agg_H[((b * (p.n_seg - 1) + s) * p.D + d) * p.N + n];
-    h = __builtin_fmaf(__builtin_amdgcn_exp2f(a2 * S), h, H);
-    p.h_in[((b * p.n_seg + s + 1) * p.D + d) * p.N + n] = h;
+  float h = p.agg_H[((b * (p.n_seg - 1) + 0) * p.D + d) * p.N + n];
+  for (int s = 1; s < p.n_seg; ++s) {
+    p.h_in[((b * p.n_seg + s) * p.D + d) * p.N + n] = h;
+    if (s + 1 < p.n_seg) {
+      const float S = p.agg_S[(b * (p.n_seg - 1) + s) * p.D + d];
+      const float H = p.agg_H[((b * (p.n_seg - 1) + s) * p.D + d) * p.N + n];
+      h = __builtin_fmaf(__builtin_amdgcn_exp2f(a2 * S), h, H);
+    }
   }
 }
 
@@ -791,16 +828,18 @@ template <bool BF16, bool VEC, int KS>
 hipError_t launch_ks(const ScanParams& p, hipStream_t stream) {
   const int64_t n_dblk = (p.D + CH - 1) / CH;
   auto padded = [](int64_t n) { return (n + 7) / 8 * 8; };
-  if (p.n_seg > 1) {
-    const int64_t nb = n_dblk * (p.n_seg - 1) * p.batch;
-    hipLaunchKernelGGL((scan_kernel<BF16, VEC, KS, 1>), dim3((unsigned)padded(nb)), dim3(NT), 0, stream, p, n_dblk,
-                       (int64_t)(p.n_seg - 1), padded(nb));
-    const int64_t ncomb = p.batch * p.D * p.N;
-    hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((ncomb + 255) / 256)), dim3(256), 0, stream, p);
-  }
+  // pass 1: every segment from zero (segment 0 from h0)
   const int64_t nb = n_dblk * p.n_seg * p.batch;
   hipLaunchKernelGGL((scan_kernel<BF16, VEC, KS, 0>), dim3((unsigned)padded(nb)), dim3(NT), 0, stream, p, n_dblk,
                      (int64_t)p.n_seg, padded(nb));
+  if (p.n_seg > 1) {
+    // the states entering the segments, then each segment's correction
+    const int64_t ncomb = p.batch * p.D * p.N;
+    hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((ncomb + 255) / 256)), dim3(256), 0, stream, p);
+    const int64_t nb2 = n_dblk * (p.n_seg - 1) * p.batch;
+    hipLaunchKernelGGL((scan_kernel<BF16, VEC, KS, 2>), dim3((unsigned)padded(nb2)), dim3(NT), 0, stream, p,
+                       n_dblk, (int64_t)(p.n_seg - 1), padded(nb2));
+  }
   return hipGetLastError();
 }
 

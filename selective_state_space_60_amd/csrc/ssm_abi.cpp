@@ -420,7 +420,9 @@ ssm_status validate_ssd_bwd_desc(const ssm_ssd_bwd_desc* d) {
   return SSM_OK;
 }
 
-ssm_status validate_ssd_bwd_ptrs(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_ptrs* p) {
+// `ws`: the workspace the call will write (invalid span: none given); it may
+// not overlap any input, output or the forward's intermediates.
+ssm_status validate_ssd_bwd_ptrs(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_ptrs* p, Span ws = Span()) {
   if (!p) return SSM_ERR_NULL;
   const uint32_t f = d->flags;
   if (!p->x || !p->delta || !p->A || !p->B || !p->C || !p->dy || !p->dx || !p->ddelta || !p->dA || !p->dB ||
@@ -459,7 +461,10 @@ ssm_status validate_ssd_bwd_ptrs(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_pt
       if (overlap(outs[i], s)) return SSM_ERR_ALIAS;
     for (int j = i + 1; j < no; ++j)
       if (overlap(outs[i], outs[j])) return SSM_ERR_ALIAS;
+    if (overlap(outs[i], ws)) return SSM_ERR_ALIAS;
   }
+  for (const Span& s : ins)
+    if (overlap(ws, s)) return SSM_ERR_ALIAS;
   return SSM_OK;
 }
 
@@ -962,8 +967,8 @@ ssm_status ssm_ssd_bwd(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_ptrs* p, voi
                        void* hip_stream) {
   ssm_status s = validate_ssd_bwd_desc(d);
   if (s) return s;
-  if ((s = validate_ssd_bwd_ptrs(d, p))) return s;
   const SSDBwdPlan pl = plan_ssd_bwd(*d);
+  if ((s = validate_ssd_bwd_ptrs(d, p, span_bytes(workspace, pl.ws_total)))) return s;
   if (!workspace || workspace_bytes < (size_t)pl.ws_total) return SSM_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return SSM_ERR_ALIGN;
   const uint32_t f = d->flags;

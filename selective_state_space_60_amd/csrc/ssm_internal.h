@@ -29,9 +29,9 @@ struct ScanParams {
   // Sequence split: segment s covers [s*seg_len, min(L, (s+1)*seg_len)).
   int n_seg;
   int64_t seg_len;
-  float* agg_H;  // (batch, n_seg-1, D, N): end state of segment s scanned from 0
+  float* agg_H;  // (batch, n_seg-1, D, N): end state of segment s in the first pass (from 0; segment 0 from h0)
   float* agg_S;  // (batch, n_seg-1, D): sum of delta over segment s
-  float* h_in;   // (batch, n_seg, D, N): state entering segment s
+  float* h_in;   // (batch, n_seg, D, N): state entering segment s (s >= 1)
   // Step-size transform: delta <- softplus(delta + dbias[d * dbs_d]) when
   // dsoftplus (dbias may be null: bias 0).
   const float* dbias;

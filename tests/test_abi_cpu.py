@@ -481,3 +481,29 @@ def test_ssd_bwd_fwd_buffers_checked_by_the_binding(key, bad):
     fwd[key] = bad(fwd[key])
     with pytest.raises(ValueError, match=key):
         ssm.ssd_bwd(dy, x, delta, A, B, C, Q, fwd=fwd)
+
+
+@pytest.mark.parametrize("where", ["A_cum", "states", "dx", "x"])
+def test_ssd_bwd_workspace_may_not_overlap(where):
+    # the backward writes its workspace: it may not overlap an input, an
+    # output or the forward's intermediates it reads
+    d, p = _ssd_bwd(flags=ssm.SSM_HAS_D | ssm.SSM_HAS_H0 | ssm.SSM_HAS_SSD_FWD)
+    for k, v in _FWD.items():
+        setattr(p, k, v)
+    ws = getattr(p, where) + 256
+    assert ssm.lib().ssm_ssd_bwd(ctypes.byref(d), ctypes.byref(p), ws, 1 << 40, None) == ssm.SSM_ERR_ALIAS
+
+
+@pytest.mark.parametrize("key,value", [("chunk", 128), ("euler", True)])
+def test_ssd_bwd_refuses_intermediates_of_another_forward(key, value):
+    # ssd_chunk_fwd_train records the chunk size and the discretisation of
+    # its intermediates; a backward with others would compute wrong gradients
+    torch = _torch
+    batch, L, H, P, N, Q = 1, 100, 4, 64, 64, 64
+    bf = lambda *s: torch.zeros(s, dtype=torch.bfloat16)
+    x, dy, delta, B, C = bf(batch, L, H, P), bf(batch, L, H, P), bf(batch, L, H), bf(batch, L, 1, N), bf(batch, L, 1, N)
+    fwd = {"A_cum": torch.zeros(batch, H, 128), "beta": torch.zeros(batch, H, 128),
+           "states": torch.zeros(batch, 2, H, P, N), "chunk": Q, "euler": False}
+    fwd[key] = value
+    with pytest.raises(ValueError, match=key):
+        ssm.ssd_bwd(dy, x, delta, torch.zeros(H), B, C, Q, fwd=fwd)

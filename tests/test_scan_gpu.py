@@ -278,3 +278,35 @@ def test_delta_softplus_sequence_split():
     yr, hr = oracle.selective_scan(inp, "f32", delta_softplus=True, delta_bias=db)
     assert_close(host_f64(y), yr, "f32", "softplus split y")
     assert_close(host_f64(hl), hr, "f32", "softplus split h_last")
+
+
+@pytest.mark.parametrize("variant", ["zero_A", "euler", "bf16_y_f32"])
+def test_sequence_split_variants(variant):
+    """The split path's rescan stops once every state equals its zero-started
+    twin.  With a zero entry of A (no decay of that state) it never does and
+    runs to the end of every segment; the Euler form and bf16 inputs take
+    their own update forms and loaders.  All against the oracle at the fp32
+    bar (fp32 y)."""
+    kw = dict(batch=1, seqlen=9000, dim=40, has_z=True, has_D=True)
+    if variant == "euler":
+        kw["euler"] = True
+    if variant == "bf16_y_f32":
+        kw["io"] = "bf16"
+    spec = synth.scan_spec(synth.LONG1M, **kw)
+    inp = synth.scan_inputs(spec, 21)
+    if variant == "zero_A":
+        inp["A"][:, 3] = 0.0      # state 3 of every channel: the limit delta*B, no decay
+        # that state sums 9000 inputs without decay, and fp32 rounding of a
+        # sum grows with its size: x / 4 (exact) keeps |y| near 16, so the
+        # absolute bar measures the path, not the growth of the sum
+        inp["x"] *= 0.25
+    banner("scan split %s" % variant)
+    h0 = synth.state_input((1, 40, 16), 21)
+    g = _upload(spec, inp)
+    y, hl = ssm.selective_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
+                                   h0=torch.from_numpy(h0).cuda(), euler=spec.euler, want_hlast=True,
+                                   y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yr, hr = oracle.selective_scan(inp, spec.io, euler=spec.euler, h0=h0.astype(np.float64))
+    assert_close(host_f64(y), yr, "f32", "split %s y" % variant)
+    assert_close(host_f64(hl), hr, "f32", "split %s h_last" % variant)
