@@ -11,7 +11,7 @@ import pytest
 import oracle
 import synth
 
-from _gpu import assert_close, banner, dev_tensor, host_f64, metrics
+from _gpu import BF16_REGRESSION, assert_close, assert_tiles, banner, dev_tensor, host_f64, metrics
 
 pytestmark = pytest.mark.gpu
 
@@ -67,13 +67,38 @@ def test_tiny_f32():
     _check(synth.TINY)
 
 
+def _check_full(spec, seed):
+    """The spec bar (inside _check), then the regression bars: the whole
+    output and every (batch, 256-step, 256-channel) tile."""
+    y = _check(spec, seed)
+    inp = synth.scan_inputs(spec, seed)
+    yr, _ = oracle.selective_scan(inp, spec.io)
+    yh = host_f64(y)
+    m = metrics(yh, yr)
+    assert m["rel_l2"] <= BF16_REGRESSION["scan"], m
+    assert_tiles(yh, yr, (1, 256, 256), 1e-2, spec.name + " y")
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_mamba130m_bf16_full(seed):
-    _check(synth.MAMBA130M, seed)
+    _check_full(synth.MAMBA130M, seed)
 
 
 def test_mamba2_8b_bf16_full():
-    _check(synth.MAMBA2_8B, 0)
+    _check_full(synth.MAMBA2_8B, 0)
+
+
+def test_mamba2_8b_fp32_output_full():
+    """The whole Mamba-2.8B layer from its exact bf16 inputs with fp32 y: the
+    state and arithmetic are fp32, so y meets the fp32 bar (rel-L2 <= 1e-5,
+    max-abs <= 1e-4) against the fp64 oracle on the same stored inputs."""
+    spec = synth.MAMBA2_8B
+    inp = synth.scan_inputs(spec, 0)
+    banner("scan %s fp32 y" % spec.name)
+    y, hl = _run(spec, inp, want_hlast=True, y_dtype=torch.float32)
+    yr, hr = oracle.selective_scan(inp, spec.io)
+    assert_close(host_f64(y), yr, "f32", spec.name + " fp32 y")
+    assert_close(host_f64(hl), hr, "f32", spec.name + " fp32 y: h_last")
 
 
 def test_long1m_f32_sampled_rows():

@@ -13,7 +13,7 @@ import pytest
 import oracle
 import synth
 
-from _gpu import assert_close, banner, dev_tensor, host_f64, metrics
+from _gpu import BF16_REGRESSION, assert_close, assert_tiles, banner, dev_tensor, host_f64, metrics
 
 pytestmark = pytest.mark.gpu
 
@@ -68,8 +68,16 @@ def small(**kw):
 
 def test_ssd_2_7b_full():
     """The 2.7B-shaped layer (batch 4, L 4096, 80 heads x 64, N 64, chunk 256)
-    against the expanded recurrence, every output."""
-    _check(synth.SSD2_7B, 0)
+    against the expanded recurrence, every output: the bf16 bar, then the
+    regression bars on the whole output and on every (batch, chunk, head)
+    tile."""
+    s = synth.SSD2_7B
+    y = _check(s, 0)
+    yr, _ = oracle.ssd(synth.ssd_inputs(s, 0), "bf16", ngroups=s.ngroups)
+    yh = host_f64(y)
+    m = metrics(yh, yr)
+    assert m["rel_l2"] <= BF16_REGRESSION["ssd"], m
+    assert_tiles(yh, yr, (1, s.chunk, 1, s.headdim), 2e-2, s.name + " y")
 
 
 @pytest.mark.parametrize("chunk", [64, 128, 256])
