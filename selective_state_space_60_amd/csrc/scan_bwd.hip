@@ -345,7 +345,7 @@ __global__ __launch_bounds__(NT) void ckpt_kernel(ScanBwdParams p, int64_t n_dbl
 
 template <bool BF16, int KS, int FORM>
 __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p, int64_t b, int64_t dblk,
-                                         const LaneA<KS>& la) {
+                                         int64_t seg, const LaneA<KS>& la) {
   const int tid = threadIdx.x, c = tid / G, sg = tid % G;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int64_t d0 = dblk * CH, d = d0 + c;
@@ -354,9 +354,18 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
   const float Dk = (p.Dskip && d_ok) ? p.Dskip[d * p.Ds_d] : 0.f;
   const float bias = (p.dbias && d_ok) ? p.dbias[d * p.dbs_d] : 0.f;
   const int ntiles = (int)((p.L + TT - 1) / TT);
+  // this workgroup's tiles: its segment's (the whole sequence unless split)
+  const int64_t t_begin = seg * p.seg_len;
+  const int64_t t_end = p.n_seg > 1 && t_begin + p.seg_len < p.L ? t_begin + p.seg_len : p.L;
+  const int it_lo = (int)(t_begin / TT), it_hi = (int)((t_end - 1) / TT);
   float carry[KS], dA[KS];
 #pragma unroll
-  for (int k = 0; k < KS; ++k) carry[k] = dA[k] = 0.f;
+  for (int k = 0; k < KS; ++k) {
+    const int n = sg * KS + k;
+    // the adjoint carried in from the later segments (zero for the last)
+    carry[k] = (p.n_seg > 1 && d_ok && n < p.N) ? p.cin[((b * p.n_seg + seg) * p.D + d) * p.N + n] : 0.f;
+    dA[k] = 0.f;
+  }
   float dD = 0.f, dbias = 0.f;  // this lane's steps of its channel
   float* prow = &s.part[0][tid][0];
   static_assert(TT % 2 == 0, "dB, dC row sums pair the steps");
@@ -368,12 +377,12 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
   // Per-lane pointers, set up once and moved one tile per iteration (the
   // loop then needs no strides: fewer live scalar registers).
   const int64_t dd = d_ok ? d : 0;
-  const float* ckp = p.ckpt + ((b * ntiles + (ntiles - 1)) * p.D + dd) * p.N;  // tile ntiles-1
+  const float* ckp = p.ckpt + ((b * ntiles + it_hi) * p.D + dd) * p.N;  // tile it_hi
   const int64_t ck_step = p.D * p.N;
   const int64_t e_dx = p.dx_f32 ? 4 : 2, e_dd = p.dd_f32 ? 4 : 2, e_dz = p.dz_f32 ? 4 : 2;
-  char* pdx = (char*)p.dx + (b * p.dxs_b + ((int64_t)(ntiles - 1) * TT + sg) * p.dxs_t + dd) * e_dx;
-  char* pdd = (char*)p.ddelta + (b * p.dds_b + ((int64_t)(ntiles - 1) * TT + sg) * p.dds_t + dd) * e_dd;
-  char* pdz = p.dz ? (char*)p.dz + (b * p.dzs_b + ((int64_t)(ntiles - 1) * TT + sg) * p.dzs_t + dd) * e_dz : nullptr;
+  char* pdx = (char*)p.dx + (b * p.dxs_b + ((int64_t)it_hi * TT + sg) * p.dxs_t + dd) * e_dx;
+  char* pdd = (char*)p.ddelta + (b * p.dds_b + ((int64_t)it_hi * TT + sg) * p.dds_t + dd) * e_dd;
+  char* pdz = p.dz ? (char*)p.dz + (b * p.dzs_b + ((int64_t)it_hi * TT + sg) * p.dzs_t + dd) * e_dz : nullptr;
   const int64_t sdx = TT * p.dxs_t * e_dx, sdd = TT * p.dds_t * e_dd, sdz = TT * p.dzs_t * e_dz;
   const bool dx_f32 = p.dx_f32, dd_f32 = p.dd_f32, dz_f32 = p.dz_f32;
   // dB, dC partials: element (j, q, n) of a tile per thread (2 * KS of them)
@@ -389,7 +398,7 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
     const int j = i / (2 * G * KS), q = (i / (G * KS)) % 2, n = i % (G * KS);
     red_j[r] = j;
     red_n_ok[r] = n < p.N;
-    pred[r] = (q == 0 ? p.pdB : p.pdC) + ((dblk * p.batch + b) * p.L + (int64_t)(ntiles - 1) * TT + j) * p.N +
+    pred[r] = (q == 0 ? p.pdB : p.pdC) + ((dblk * p.batch + b) * p.L + (int64_t)it_hi * TT + j) * p.N +
               (n < p.N ? n : 0);
   }
   const int64_t L = p.L;
@@ -403,11 +412,11 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
       h[k] = ok ? v : 0.f;
     }
   };
-  LanePtrs<KS> w = lane_ptrs<BF16, KS>(p, b, d0, ntiles - 1);
-  Fetch<KS> cur = fetch<BF16, KS, true>(p, w, d0, ntiles - 1, -1);
+  LanePtrs<KS> w = lane_ptrs<BF16, KS>(p, b, d0, it_hi);
+  Fetch<KS> cur = fetch<BF16, KS, true>(p, w, d0, it_hi, -1);
   float h0n[KS];
   ckpt_of(h0n);
-  for (int it = ntiles - 1; it >= 0; --it) {
+  for (int it = it_hi; it >= it_lo; --it) {
     const int64_t t0 = (int64_t)it * TT;
     const bool j_ok = d_ok && t0 + sg < L;
     put_bc<KS>(s.bc, cur);
@@ -418,8 +427,10 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
 #pragma unroll
     for (int k = 0; k < KS; ++k) h0t[k] = h0n[k];
     __syncthreads();
-    // the previous tile's inputs are in flight during this tile
-    cur = fetch<BF16, KS, true>(p, w, d0, it - 1, -1);  // before the first tile: masked
+    // the previous tile's inputs are in flight during this tile (before the
+    // first tile of the sequence: masked; before a later segment's first
+    // tile: read, unused)
+    cur = fetch<BF16, KS, true>(p, w, d0, it - 1, -1);
     if (it > 0) ckp -= ck_step;
     ckpt_of(h0n);
 
@@ -573,14 +584,15 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
     if (pdz) pdz -= sdz;
     __syncthreads();
   }
-  // per-channel and per-state sums of this batch row
+  // per-channel and per-state sums of this batch row (and segment)
+  const int64_t bs = b * p.n_seg + seg;
   if (d_ok) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       const int n = sg * KS + k;
       if (n < p.N) {
-        p.pdA[(b * p.D + d) * p.N + n] = dA[k];
-        if (p.dh0) p.dh0[(b * p.D + d) * p.N + n] = carry[k];
+        p.pdA[(bs * p.D + d) * p.N + n] = dA[k];
+        if (p.dh0 && seg == 0) p.dh0[(b * p.D + d) * p.N + n] = carry[k];
       }
     }
   }
@@ -591,25 +603,123 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
     dbias += __shfl_xor(dbias, m, G);
   }
   if (sg == 0 && d_ok) {
-    if (p.pdD) p.pdD[b * p.D + d] = dD;
-    if (p.pdbias) p.pdbias[b * p.D + d] = dbias;
+    if (p.pdD) p.pdD[bs * p.D + d] = dD;
+    if (p.pdbias) p.pdbias[bs * p.D + d] = dbias;
+  }
+}
+
+template <bool BF16, int KS, bool EULER>
+__device__ __forceinline__ void bwd_block(BwdSmem<KS>& s, const ScanBwdParams& p, int64_t n_dblk,
+                                          int64_t nblocks_padded) {
+  const int tid = threadIdx.x;
+  const int64_t lb = logical_block(nblocks_padded);
+  if (lb >= n_dblk * p.n_seg * p.batch) return;
+  const int64_t dblk = lb % n_dblk, seg = (lb / n_dblk) % p.n_seg, b = lb / (n_dblk * p.n_seg);
+  int zero_a;
+  const LaneA<KS> la = lane_a<BF16, KS>(p, dblk * CH + tid / G, tid % G, zero_a);
+  if constexpr (EULER) {
+    bwd_walk<BF16, KS, kEuler>(s, p, b, dblk, seg, la);
+  } else {
+    if (__syncthreads_or(zero_a)) bwd_walk<BF16, KS, kZohZero>(s, p, b, dblk, seg, la);
+    else bwd_walk<BF16, KS, kZoh>(s, p, b, dblk, seg, la);
   }
 }
 
 template <bool BF16, int KS, bool EULER>
 __global__ __launch_bounds__(NT) void bwd_kernel(ScanBwdParams p, int64_t n_dblk, int64_t nblocks_padded) {
   __shared__ BwdSmem<KS> s;
-  const int tid = threadIdx.x;
+  bwd_block<BF16, KS, EULER>(s, p, n_dblk, nblocks_padded);
+}
+
+// One state per lane: capped at 168 VGPRs, three waves per SIMD (at 169 the
+// 8-register allocation granule leaves room for two).
+template <bool BF16, bool EULER>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_num_vgpr(168))) void bwd_kernel_1(ScanBwdParams p,
+                                                                                        int64_t n_dblk,
+                                                                                        int64_t nblocks_padded) {
+  __shared__ BwdSmem<1> s;
+  bwd_block<BF16, 1, EULER>(s, p, n_dblk, nblocks_padded);
+}
+
+// ------------------------------------------------- sequence split: carries
+
+// The adjoint recurrence alone, lam_t = C_t g_t + Abar_{t+1} lam_{t+1}, over
+// segment s = 1 + (its index) from a zero carry: it needs no state, so it is
+// a few operations per state and step.  Writes the carry out of the
+// segment's first step, Abar lam (cH), and the segment's sum of delta (cS).
+template <bool BF16, int KS>
+__global__ __launch_bounds__(NT) void bwd_carry_kernel(ScanBwdParams p, int64_t n_dblk, int64_t nblocks_padded) {
+  __shared__ float Cs[TT][G * KS];
+  const int tid = threadIdx.x, c = tid / G, sg = tid % G;
   const int64_t lb = logical_block(nblocks_padded);
-  if (lb >= n_dblk * p.batch) return;
-  const int64_t dblk = lb % n_dblk, b = lb / n_dblk;
+  if (lb >= n_dblk * (p.n_seg - 1) * p.batch) return;
+  const int64_t dblk = lb % n_dblk, seg = 1 + (lb / n_dblk) % (p.n_seg - 1), b = lb / (n_dblk * (p.n_seg - 1));
+  const int64_t d0 = dblk * CH, d = d0 + c;
+  const bool d_ok = d < p.D;
+  const bool has_z = p.z != nullptr;
+  const float bias = (p.dbias && d_ok) ? p.dbias[d * p.dbs_d] : 0.f;
   int zero_a;
-  const LaneA<KS> la = lane_a<BF16, KS>(p, dblk * CH + tid / G, tid % G, zero_a);
-  if constexpr (EULER) {
-    bwd_walk<BF16, KS, kEuler>(s, p, b, dblk, la);
-  } else {
-    if (__syncthreads_or(zero_a)) bwd_walk<BF16, KS, kZohZero>(s, p, b, dblk, la);
-    else bwd_walk<BF16, KS, kZoh>(s, p, b, dblk, la);
+  const LaneA<KS> la = lane_a<BF16, KS>(p, d, sg, zero_a);
+  const int64_t t_begin = seg * p.seg_len;
+  const int64_t t_end = t_begin + p.seg_len < p.L ? t_begin + p.seg_len : p.L;
+  const int it_lo = (int)(t_begin / TT), it_hi = (int)((t_end - 1) / TT);
+  float carry[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) carry[k] = 0.f;
+  float sum_dt = 0.f;
+  LanePtrs<KS> w = lane_ptrs<BF16, KS>(p, b, d0, it_hi);
+  Fetch<KS> cur = fetch<BF16, KS, true>(p, w, d0, it_hi, -1);
+  for (int it = it_hi; it >= it_lo; --it) {
+    const bool j_ok = d_ok && (int64_t)it * TT + sg < p.L;
+#pragma unroll
+    for (int r = 0; r < KS; ++r) {
+      const int i = tid + r * NT;
+      Cs[i / (G * KS)][i % (G * KS)] = cur.C[r];
+    }
+    float dv;
+    const float hdt = step_size(p, cur.dr, bias, j_ok, dv);
+    const float zj = cur.z, gyj = __uint_as_float(p.dy_f32 ? cur.gy : cur.gy << 16);
+    const float g = has_z ? gyj * zj * sigmoid_f32(zj) : gyj;
+    sum_dt += hdt;
+    __syncthreads();
+    cur = fetch<BF16, KS, true>(p, w, d0, it - 1, -1);  // before the segment: read, unused
+    for_steps_rev(std::make_integer_sequence<int, TT>{}, [&](auto S) {
+#pragma clang fp contract(off)
+      constexpr int T = decltype(S)::value;
+      const float dt = row_bcast<T>(hdt), gs = row_bcast<T>(g);
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const float Ab = __builtin_amdgcn_exp2f(dt * la.A2[k]);
+        carry[k] = Ab * __builtin_fmaf(Cs[T][sg * KS + k], gs, carry[k]);
+      }
+    });
+    __syncthreads();
+  }
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) sum_dt += __shfl_xor(sum_dt, m, G);
+  if (!d_ok) return;
+  const int64_t bs = b * p.n_seg + seg;
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const int n = sg * KS + k;
+    if (n < p.N) p.cH[(bs * p.D + d) * p.N + n] = carry[k];
+  }
+  if (sg == 0) p.cS[bs * p.D + d] = sum_dt;
+}
+
+// The carry into each segment's last step, from the last segment back:
+// cin[n_seg-1] = 0;  cin[s-1] = cH[s] + exp(A * cS[s]) cin[s].
+__global__ __launch_bounds__(256) void bwd_combine_kernel(ScanBwdParams p) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over batch*D*N
+  if (i >= p.batch * p.D * p.N) return;
+  const int64_t n = i % p.N, d = (i / p.N) % p.D, b = i / (p.N * p.D);
+  const float a2 = p.A[d * p.As_d + n * p.As_n] * kLog2e;
+  float c = 0.f;
+  p.cin[((b * p.n_seg + p.n_seg - 1) * p.D + d) * p.N + n] = 0.f;
+  for (int64_t sgm = p.n_seg - 1; sgm >= 1; --sgm) {
+    const int64_t bs = b * p.n_seg + sgm;
+    c = __builtin_fmaf(__builtin_amdgcn_exp2f(a2 * p.cS[bs * p.D + d]), c, p.cH[(bs * p.D + d) * p.N + n]);
+    p.cin[((bs - 1) * p.D + d) * p.N + n] = c;
   }
 }
 
@@ -693,21 +803,37 @@ void reduce(const float* src, float* dst, int64_t count, int64_t parts, int64_t 
 template <bool BF16, int KS>
 void launch_ks(const ScanBwdParams& p, hipStream_t stream) {
   const int64_t n_dblk = (p.D + CH - 1) / CH;
-  const int64_t npad = (n_dblk * p.batch + 7) / 8 * 8;  // blocks past the end exit at once
+  auto pad8 = [](int64_t n) { return (n + 7) / 8 * 8; };  // blocks past the end exit at once
+  const int64_t npad = pad8(n_dblk * p.batch);
   const dim3 grid((unsigned)npad);
-  if (p.euler) {
-    if (!p.ckpt_given) hipLaunchKernelGGL((ckpt_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
-    hipLaunchKernelGGL((bwd_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
+  // unsplit, the checkpoint pass (the split path's checkpoints come from the
+  // forward's split kernels, run by the caller)
+  if (!p.ckpt_given) {
+    if (p.euler) hipLaunchKernelGGL((ckpt_kernel<BF16, KS, true>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
+    else hipLaunchKernelGGL((ckpt_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
+  }
+  if (p.n_seg > 1) {
+    const int64_t nc = pad8(n_dblk * (p.n_seg - 1) * p.batch);
+    hipLaunchKernelGGL((bwd_carry_kernel<BF16, KS>), dim3((unsigned)nc), dim3(NT), 0, stream, p, n_dblk, nc);
+    const int64_t ncomb = p.batch * p.D * p.N;
+    hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((ncomb + 255) / 256)), dim3(256), 0, stream, p);
+  }
+  const int64_t nb = pad8(n_dblk * p.n_seg * p.batch);
+  const dim3 gb((unsigned)nb);
+  if constexpr (KS == 1) {
+    if (p.euler) hipLaunchKernelGGL((bwd_kernel_1<BF16, true>), gb, dim3(NT), 0, stream, p, n_dblk, nb);
+    else hipLaunchKernelGGL((bwd_kernel_1<BF16, false>), gb, dim3(NT), 0, stream, p, n_dblk, nb);
   } else {
-    if (!p.ckpt_given) hipLaunchKernelGGL((ckpt_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
-    hipLaunchKernelGGL((bwd_kernel<BF16, KS, false>), grid, dim3(NT), 0, stream, p, n_dblk, npad);
+    if (p.euler) hipLaunchKernelGGL((bwd_kernel<BF16, KS, true>), gb, dim3(NT), 0, stream, p, n_dblk, nb);
+    else hipLaunchKernelGGL((bwd_kernel<BF16, KS, false>), gb, dim3(NT), 0, stream, p, n_dblk, nb);
   }
   const int64_t bln = p.batch * p.L * p.N;
+  const int64_t nbs = p.batch * p.n_seg;  // parts of the per-row sums: batch rows x segments
   reduce(p.pdB, p.dB, bln, n_dblk, bln, stream);
   reduce(p.pdC, p.dC, bln, n_dblk, bln, stream);
-  reduce(p.pdA, p.dA, p.D * p.N, p.batch, p.D * p.N, stream);
-  if (p.dD) reduce(p.pdD, p.dD, p.D, p.batch, p.D, stream);
-  if (p.ddbias) reduce(p.pdbias, p.ddbias, p.D, p.batch, p.D, stream);
+  reduce(p.pdA, p.dA, p.D * p.N, nbs, p.D * p.N, stream);
+  if (p.dD) reduce(p.pdD, p.dD, p.D, nbs, p.D, stream);
+  if (p.ddbias) reduce(p.pdbias, p.ddbias, p.D, nbs, p.D, stream);
 }
 
 template <bool BF16>

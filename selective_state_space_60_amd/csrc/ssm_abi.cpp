@@ -109,29 +109,39 @@ struct ScanPlan {
   int64_t ws_H = 0, ws_S = 0, ws_hin = 0, ws_total = 0;
 };
 
-// Split the sequence only when batch x channels cannot give every SIMD work.
-ScanPlan plan_scan(const ssm_scan_desc& d) {
-  ScanPlan pl;
-  const int64_t blocks = d.batch * ((d.dim + ssm::kScanChannelsPerBlock - 1) / ssm::kScanChannelsPerBlock);
+// Segments of a sequence split: only when batch x channels cannot give every
+// SIMD a wave, into about `target` waves per SIMD, segments at least 2048
+// steps long and a whole number of 16-step tiles.
+void split_seq(int64_t batch, int64_t seqlen, int64_t dim, int64_t target, int& n_seg_out, int64_t& seg_len_out) {
+  const int64_t blocks = batch * ((dim + ssm::kScanChannelsPerBlock - 1) / ssm::kScanChannelsPerBlock);
   const int64_t waves = blocks * (ssm::kScanThreads / 64);
   int64_t n_seg = 1;
   if (waves < kSimds) {
-    n_seg = std::max<int64_t>(1, (5 * kSimds + waves / 2) / waves);
-    n_seg = std::min<int64_t>(n_seg, std::max<int64_t>(1, d.seqlen / 2048));
+    n_seg = std::max<int64_t>(1, (target * kSimds + waves / 2) / waves);
+    n_seg = std::min<int64_t>(n_seg, std::max<int64_t>(1, seqlen / 2048));
   }
-  int64_t seg_len = (d.seqlen + n_seg - 1) / n_seg;
+  int64_t seg_len = (seqlen + n_seg - 1) / n_seg;
   seg_len = (seg_len + ssm::kScanTileSteps - 1) / ssm::kScanTileSteps * ssm::kScanTileSteps;
-  n_seg = (d.seqlen + seg_len - 1) / seg_len;
-  pl.n_seg = (int)n_seg;
-  pl.seg_len = seg_len;
+  n_seg_out = (int)((seqlen + seg_len - 1) / seg_len);
+  seg_len_out = seg_len;
+}
+
+// The forward's split targets five waves per SIMD (its first pass runs at
+// five).
+ScanPlan plan_scan_dims(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  ScanPlan pl;
+  split_seq(batch, seqlen, dim, 5, pl.n_seg, pl.seg_len);
+  const int64_t n_seg = pl.n_seg;
   if (n_seg > 1) {
-    pl.ws_H = round256(d.batch * (n_seg - 1) * d.dim * d.dstate * 4);
-    pl.ws_S = round256(d.batch * (n_seg - 1) * d.dim * 4);
-    pl.ws_hin = round256(d.batch * n_seg * d.dim * d.dstate * 4);
+    pl.ws_H = round256(batch * (n_seg - 1) * dim * dstate * 4);
+    pl.ws_S = round256(batch * (n_seg - 1) * dim * 4);
+    pl.ws_hin = round256(batch * n_seg * dim * dstate * 4);
   }
   pl.ws_total = pl.ws_H + pl.ws_S + pl.ws_hin;
   return pl;
 }
+
+ScanPlan plan_scan(const ssm_scan_desc& d) { return plan_scan_dims(d.batch, d.seqlen, d.dim, d.dstate); }
 
 ssm_status validate_scan_desc(const ssm_scan_desc* d) {
   if (!d) return SSM_ERR_NULL;
@@ -530,20 +540,39 @@ ssm_status validate_update(const ssm_update_desc* d, const ssm_update_ptrs* p) {
 
 // --------------------------------------------------------- scan backward
 
+// Workspace of the backward, in this order: checkpoints (unless given), the
+// per-channel-block partials of dB and dC, the per-(batch row, segment)
+// partials of dA, dD and dbias, and with the sequence split the segment
+// carries cH, cS, cin.  When the split backward computes its own
+// checkpoints, the forward's split aggregates (agg_H, agg_S, h_in, which fit)
+// reuse the carry buffers: the forward is done with them before the carry
+// pass starts.
 struct BwdPlan {
   int64_t ntiles = 0, n_dblk = 0;
-  int64_t ws_ckpt = 0, ws_pdB = 0, ws_pdA = 0, ws_pdD = 0, ws_total = 0;
+  int n_seg = 1;
+  int64_t seg_len = 0;
+  ScanPlan fwd;  // the split forward that writes the checkpoints (fwd.n_seg > 1)
+  int64_t ws_ckpt = 0, ws_pdB = 0, ws_pdA = 0, ws_pdD = 0, ws_cH = 0, ws_cS = 0, ws_total = 0;
 };
 
 BwdPlan plan_bwd(const ssm_scan_bwd_desc& d) {
   BwdPlan pl;
   pl.ntiles = (d.seqlen + 15) / 16;
   pl.n_dblk = (d.dim + 15) / 16;
+  // the backward's walk holds three waves per SIMD
+  split_seq(d.batch, d.seqlen, d.dim, 3, pl.n_seg, pl.seg_len);
+  const int64_t ns = pl.n_seg;
+  if (ns > 1 && !(d.flags & SSM_HAS_CKPT)) pl.fwd = plan_scan_dims(d.batch, d.seqlen, d.dim, d.dstate);
   pl.ws_ckpt = (d.flags & SSM_HAS_CKPT) ? 0 : round256(d.batch * pl.ntiles * d.dim * d.dstate * 4);
   pl.ws_pdB = round256(pl.n_dblk * d.batch * d.seqlen * d.dstate * 4);
-  pl.ws_pdA = round256(d.batch * d.dim * d.dstate * 4);
-  pl.ws_pdD = round256(d.batch * d.dim * 4);
-  pl.ws_total = pl.ws_ckpt + 2 * pl.ws_pdB + pl.ws_pdA + 2 * pl.ws_pdD;
+  pl.ws_pdA = round256(d.batch * ns * d.dim * d.dstate * 4);
+  pl.ws_pdD = round256(d.batch * ns * d.dim * 4);
+  if (ns > 1) {
+    // cH and cin are (batch, n_seg, D, N) like pdA, cS (batch, n_seg, D) like pdD
+    pl.ws_cH = std::max(pl.ws_pdA, std::max(pl.fwd.ws_H, pl.fwd.ws_hin));
+    pl.ws_cS = std::max(pl.ws_pdD, pl.fwd.ws_S);
+  }
+  pl.ws_total = pl.ws_ckpt + 2 * pl.ws_pdB + pl.ws_pdA + 2 * pl.ws_pdD + 2 * pl.ws_cH + pl.ws_cS;
   return pl;
 }
 
@@ -952,7 +981,43 @@ ssm_status ssm_selective_scan_bwd(const ssm_scan_bwd_desc* d, const ssm_scan_bwd
   q.dd_f32 = d->ddelta.dtype == SSM_F32;
   q.euler = (f & SSM_DISC_EULER) ? 1 : 0;
   q.dsoftplus = (f & SSM_DELTA_SOFTPLUS) ? 1 : 0;
-  return hip_status(ssm::launch_selective_scan_bwd(q, (hipStream_t)hip_stream));
+  q.n_seg = pl.n_seg;
+  q.seg_len = pl.seg_len;
+  hipStream_t st = (hipStream_t)hip_stream;
+  if (pl.n_seg > 1) {
+    char* c = w + pl.ws_ckpt + 2 * pl.ws_pdB + pl.ws_pdA + 2 * pl.ws_pdD;
+    q.cH = (float*)c;
+    q.cin = (float*)(c + pl.ws_cH);
+    q.cS = (float*)(c + 2 * pl.ws_cH);
+    if (!q.ckpt_given) {
+      // The checkpoints from the forward's split kernels, y not written.
+      ssm::ScanParams fq;
+      std::memset(&fq, 0, sizeof(fq));
+      fq.x = q.x; fq.delta = q.delta; fq.B = q.B; fq.C = q.C; fq.A = q.A; fq.h0 = q.h0;
+      fq.batch = q.batch; fq.L = q.L; fq.D = q.D; fq.N = q.N;
+      fq.xs_b = q.xs_b; fq.xs_t = q.xs_t; fq.ds_b = q.ds_b; fq.ds_t = q.ds_t;
+      fq.ys_b = q.xs_b; fq.ys_t = q.xs_t;  // no y: strides that pass the layout checks
+      fq.Bs_b = q.Bs_b; fq.Bs_t = q.Bs_t; fq.Bs_n = q.Bs_n;
+      fq.Cs_b = q.Cs_b; fq.Cs_t = q.Cs_t; fq.Cs_n = q.Cs_n;
+      fq.As_d = q.As_d; fq.As_n = q.As_n;
+      fq.flags = f & (SSM_DISC_EULER | SSM_HAS_H0);
+      fq.io_bf16 = q.io_bf16;
+      fq.y_f32 = 1;
+      fq.dbias = q.dbias; fq.dbs_d = q.dbs_d; fq.dsoftplus = q.dsoftplus;
+      fq.ckpt = q.ckpt;
+      fq.n_seg = pl.fwd.n_seg;
+      fq.seg_len = pl.fwd.seg_len;
+      if (fq.n_seg > 1) {
+        fq.agg_H = q.cH;
+        fq.agg_S = q.cS;
+        fq.h_in = q.cin;
+      }
+      hipError_t e = ssm::launch_selective_scan(fq, st);
+      if (e != hipSuccess) return hip_status(e);
+      q.ckpt_given = 1;
+    }
+  }
+  return hip_status(ssm::launch_selective_scan_bwd(q, st));
 }
 
 ssm_status ssm_ssd_bwd_workspace_size(const ssm_ssd_bwd_desc* d, size_t* bytes) {

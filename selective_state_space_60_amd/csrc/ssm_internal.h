@@ -104,9 +104,18 @@ struct ScanBwdParams {
   int ckpt_given;      // the caller supplied ckpt (the forward's): no checkpoint pass
   float* pdB;          // (n_dblk, batch, L, N): sums over each workgroup's channels
   float* pdC;
-  float* pdA;          // (batch, D, N): sums over time
-  float* pdD;          // (batch, D)
-  float* pdbias;       // (batch, D)
+  float* pdA;          // (batch, n_seg, D, N): sums over each segment's time
+  float* pdD;          // (batch, n_seg, D)
+  float* pdbias;       // (batch, n_seg, D)
+  // Sequence split (n_seg > 1 when batch x channels cannot fill the GPU):
+  // segment s covers [s*seg_len, min(L, (s+1)*seg_len)), seg_len a multiple
+  // of 16.  The adjoint carried into each segment's last step comes from a
+  // pass that runs the adjoint recurrence alone over every later segment.
+  int n_seg;
+  int64_t seg_len;
+  float* cH;           // (batch, n_seg, D, N): carry out of segment s (s >= 1) from a zero carry in
+  float* cS;           // (batch, n_seg, D): sum of delta over segment s
+  float* cin;          // (batch, n_seg, D, N): carry into segment s at its last step
   int64_t batch, L, D, N;
   int64_t xs_b, xs_t, ds_b, ds_t, zs_b, zs_t, gs_b, gs_t;  // x, delta, z, dy
   int64_t dxs_b, dxs_t, dds_b, dds_t, dzs_b, dzs_t;        // dx, ddelta, dz

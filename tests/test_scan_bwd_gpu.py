@@ -114,3 +114,50 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for k in r1:
         assert torch.equal(r1[k], r2[k]), k
+
+
+# Sequence split: one batch row of few channels cannot fill the chip, so the
+# backward cuts the sequence into segments of at least 2048 steps: a carry
+# pass gives each later segment's adjoint aggregate, a combine chains them
+# right to left, and every segment is then walked from its true carry; the
+# checkpoints come from the split forward (y not written).  9000 steps make
+# four segments with a ragged last tile, 40000 steps nineteen.
+@pytest.mark.parametrize("kw", [dict(), dict(io="bf16"), dict(euler=True), dict(dstate=20), dict(dstate=64, dim=24),
+                                dict(has_z=False, has_D=False), dict(seqlen=40000, dim=17)],
+                         ids=lambda kw: "_".join("%s%s" % i for i in sorted(kw.items())) or "base")
+def test_bwd_split_sequence(kw):
+    base = dict(batch=1, seqlen=9000, dim=40)
+    base.update(kw)
+    _check(small(**base), 9)
+
+
+def test_bwd_split_sequence_h0_softplus_bias():
+    spec = small(batch=1, seqlen=9000, dim=40, delta=synth.Dist(synth.NORMAL, 0.0, 1.0))
+    _check(spec, 10, h0=True, softplus=True, bias=True)
+
+
+def test_bwd_split_sequence_zero_A():
+    def patch(inp):
+        inp["A"][3, :] = 0.0
+        inp["A"][7, 2] = 0.0
+    # A = 0 makes Abar = 1: the carries cross segments undamped; small x
+    # keeps the states in the range where fp32 sums meet the bar
+    def patch_all(inp):
+        patch(inp)
+        inp["x"] *= 0.25
+    _check(small(batch=1, seqlen=9000, dim=40, dstate=8), 11, patch=patch_all)
+
+
+def test_bwd_split_sequence_two_rows_deterministic():
+    spec = small(batch=2, seqlen=9000, dim=16)
+    _check(spec, 12)
+    inp = synth.scan_inputs(spec, 12)
+    g = {k: dev_tensor(inp[k], "f32") for k in ("x", "delta", "B", "C", "z")}
+    A, Dk = dev_tensor(inp["A"], "f32"), dev_tensor(inp["D"], "f32")
+    dy = torch.randn(g["x"].shape, device="cuda", generator=torch.Generator("cuda").manual_seed(1))
+    banner("scan bwd split determinism")
+    r1 = ssm.selective_scan_bwd(dy, g["x"], g["delta"], A, g["B"], g["C"], D=Dk, z=g["z"])
+    r2 = ssm.selective_scan_bwd(dy, g["x"], g["delta"], A, g["B"], g["C"], D=Dk, z=g["z"])
+    torch.cuda.synchronize()
+    for k in r1:
+        assert torch.equal(r1[k], r2[k]), k

@@ -122,3 +122,19 @@ def test_bwd_from_forward_ckpt_h0_softplus_bias():
         m = metrics(host_f64(got[k]), ref[k])
         print(k, m, flush=True)
         assert m["nan"] == 0 and m["rel_l2"] <= 1e-5, (k, m)
+
+
+def test_bwd_split_from_forward_ckpt():
+    # both split: the forward writes the checkpoints (its rescan fixes the
+    # later segments' first ones), the backward reads them
+    spec = small(batch=1, seqlen=9000, dim=40)
+    inp, g, ck, h0v, _ = _check_ckpt(spec, 6, [0, 128, 200, 562], h0=True)
+    dy = synth.fill((spec.batch, spec.seqlen, spec.dim), synth.Dist(synth.NORMAL, 0.0, 1.0), "f32", 6, 21)
+    got = ssm.selective_scan_bwd(dev_tensor(dy, "f32"), g["x"], g["delta"], g["A"], g["B"], g["C"], D=g["D"],
+                                 z=g["z"], h0=torch.from_numpy(h0v).cuda(), grad_dtype=torch.float32, ckpt=ck)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(inp, spec.io, dy, "f32", h0=h0v.astype(np.float64))
+    for k in sorted(ref):
+        m = metrics(host_f64(got[k]), ref[k])
+        print(k, m, flush=True)
+        assert m["nan"] == 0 and m["rel_l2"] <= 1e-5, (k, m)
