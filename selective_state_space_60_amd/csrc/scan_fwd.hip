@@ -245,9 +245,9 @@ struct ElemLoader {
     const float v = s.yb[buf][c][t];
     if (tl.row_ok(it, t) && ch_ok) {
       if (y_f32 || !BF16)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc(y, y.full_range), (int)oy, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc(y, 0xFFFFFFFFu), (int)oy, 0, 0);
       else
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rsrc(y, y.full_range),
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rsrc(y, 0xFFFFFFFFu),
                                               (int)oy, 0, 0);
     }
     advance(y);
@@ -377,12 +377,12 @@ struct VecLoader {
           w.y = __float_as_uint(v[1]);
           w.z = __float_as_uint(v[2]);
           w.w = __float_as_uint(v[3]);
-          __builtin_amdgcn_raw_buffer_store_b128(w, rsrc(y, y.full_range), (int)oy, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(w, rsrc(y, 0xFFFFFFFFu), (int)oy, 0, 0);
         } else {
           u32x2 w;
           w.x = pack2(v[0], v[1]);
           w.y = pack2(v[2], v[3]);
-          __builtin_amdgcn_raw_buffer_store_b64(w, rsrc(y, y.full_range), (int)oy, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(w, rsrc(y, 0xFFFFFFFFu), (int)oy, 0, 0);
         }
       }
     }
@@ -707,9 +707,7 @@ __global__ __launch_bounds__(NT, (!BF16 && KS == 1 && MODE == 0) ? 5 : 1) void s
       ld.sp[j] = make_span(base, b * sb + t_begin * st + col0, st, 1, width, esz, rows_last, live);
       ld.voff[j] = (uint32_t)((ld.r * st + 4 * ld.q) * esz);
     }
-    // y == null (the backward's checkpoints only): a zero range drops the stores
-    ld.y = make_span(p.y ? p.y : p.x, b * p.ys_b + t_begin * p.ys_t + d0, p.ys_t, 1, p.D - d0, yesz, rows_last,
-                     p.y != nullptr);
+    ld.y = make_span(p.y, b * p.ys_b + t_begin * p.ys_t + d0, p.ys_t, 1, p.D - d0, yesz, rows_last, true);
     ld.oy = (uint32_t)((ld.r * p.ys_t + 4 * ld.q) * yesz);
     ld.y_ok = d0 + 4 * ld.q < p.D;
     ld.clear_rows(s, (int)p.N);
@@ -723,8 +721,7 @@ __global__ __launch_bounds__(NT, (!BF16 && KS == 1 && MODE == 0) ? 5 : 1) void s
                      want_z);
     ld.B = make_span(p.B, b * p.Bs_b + t_begin * p.Bs_t, p.Bs_t, p.Bs_n, p.N, esz, rows_last, true);
     ld.C = make_span(p.C, b * p.Cs_b + t_begin * p.Cs_t, p.Cs_t, p.Cs_n, p.N, esz, rows_last, true);
-    ld.y = make_span(p.y ? p.y : p.x, b * p.ys_b + t_begin * p.ys_t + d0, p.ys_t, 1, p.D - d0, yesz, rows_last,
-                     p.y != nullptr);
+    ld.y = make_span(p.y, b * p.ys_b + t_begin * p.ys_t + d0, p.ys_t, 1, p.D - d0, yesz, rows_last, true);
     ld.ox = (uint32_t)((ld.t * p.xs_t + sg) * esz);
     ld.odl = (uint32_t)((ld.t * p.ds_t + sg) * esz);
     ld.oz = (uint32_t)((ld.t * p.zs_t + sg) * esz);
@@ -894,7 +891,9 @@ hipError_t launch_selective_scan(const ScanParams& p, hipStream_t stream) {
              p.Bs_b % 4 == 0 && p.Bs_t % 4 == 0 && p.Cs_b % 4 == 0 && p.Cs_t % 4 == 0 &&
              // rows apart by at least their width: the last tile's descriptor
              // range then ends before any row past the stretch
-             p.xs_t >= p.D && p.ds_t >= p.D && p.ys_t >= p.D && p.Bs_t >= p.N && p.Cs_t >= p.N;
+             p.xs_t >= p.D && p.ds_t >= p.D && p.Bs_t >= p.N && p.Cs_t >= p.N &&
+             // (y strides 0: one scratch row takes every store, y not wanted)
+             (p.ys_t >= p.D || (p.ys_t == 0 && p.ys_b == 0));
   if (p.flags & kHasZ) vec = vec && al(p.z, 4 * e) && p.zs_b % 4 == 0 && p.zs_t % 4 == 0 && p.zs_t >= p.D;
   if (p.io_bf16) return vec ? launch_io<true, true>(p, stream) : launch_io<true, false>(p, stream);
   return vec ? launch_io<false, true>(p, stream) : launch_io<false, false>(p, stream);

@@ -552,7 +552,7 @@ struct BwdPlan {
   int n_seg = 1;
   int64_t seg_len = 0;
   ScanPlan fwd;  // the split forward that writes the checkpoints (fwd.n_seg > 1)
-  int64_t ws_ckpt = 0, ws_pdB = 0, ws_pdA = 0, ws_pdD = 0, ws_cH = 0, ws_cS = 0, ws_total = 0;
+  int64_t ws_ckpt = 0, ws_pdB = 0, ws_pdA = 0, ws_pdD = 0, ws_cH = 0, ws_cS = 0, ws_yrow = 0, ws_total = 0;
 };
 
 BwdPlan plan_bwd(const ssm_scan_bwd_desc& d) {
@@ -562,7 +562,10 @@ BwdPlan plan_bwd(const ssm_scan_bwd_desc& d) {
   // the backward's walk holds three waves per SIMD
   split_seq(d.batch, d.seqlen, d.dim, 3, pl.n_seg, pl.seg_len);
   const int64_t ns = pl.n_seg;
-  if (ns > 1 && !(d.flags & SSM_HAS_CKPT)) pl.fwd = plan_scan_dims(d.batch, d.seqlen, d.dim, d.dstate);
+  if (ns > 1 && !(d.flags & SSM_HAS_CKPT)) {
+    pl.fwd = plan_scan_dims(d.batch, d.seqlen, d.dim, d.dstate);
+    pl.ws_yrow = round256(d.dim * 4);  // the checkpoint forward's y: one fp32 row, overwritten
+  }
   pl.ws_ckpt = (d.flags & SSM_HAS_CKPT) ? 0 : round256(d.batch * pl.ntiles * d.dim * d.dstate * 4);
   pl.ws_pdB = round256(pl.n_dblk * d.batch * d.seqlen * d.dstate * 4);
   pl.ws_pdA = round256(d.batch * ns * d.dim * d.dstate * 4);
@@ -572,7 +575,7 @@ BwdPlan plan_bwd(const ssm_scan_bwd_desc& d) {
     pl.ws_cH = std::max(pl.ws_pdA, std::max(pl.fwd.ws_H, pl.fwd.ws_hin));
     pl.ws_cS = std::max(pl.ws_pdD, pl.fwd.ws_S);
   }
-  pl.ws_total = pl.ws_ckpt + 2 * pl.ws_pdB + pl.ws_pdA + 2 * pl.ws_pdD + 2 * pl.ws_cH + pl.ws_cS;
+  pl.ws_total = pl.ws_ckpt + 2 * pl.ws_pdB + pl.ws_pdA + 2 * pl.ws_pdD + 2 * pl.ws_cH + pl.ws_cS + pl.ws_yrow;
   return pl;
 }
 
@@ -990,13 +993,15 @@ ssm_status ssm_selective_scan_bwd(const ssm_scan_bwd_desc* d, const ssm_scan_bwd
     q.cin = (float*)(c + pl.ws_cH);
     q.cS = (float*)(c + 2 * pl.ws_cH);
     if (!q.ckpt_given) {
-      // The checkpoints from the forward's split kernels, y not written.
+      // The checkpoints from the forward's split kernels; y goes to a
+      // scratch row (strides 0) and is not used.
       ssm::ScanParams fq;
       std::memset(&fq, 0, sizeof(fq));
       fq.x = q.x; fq.delta = q.delta; fq.B = q.B; fq.C = q.C; fq.A = q.A; fq.h0 = q.h0;
       fq.batch = q.batch; fq.L = q.L; fq.D = q.D; fq.N = q.N;
       fq.xs_b = q.xs_b; fq.xs_t = q.xs_t; fq.ds_b = q.ds_b; fq.ds_t = q.ds_t;
-      fq.ys_b = q.xs_b; fq.ys_t = q.xs_t;  // no y: strides that pass the layout checks
+      fq.y = c + 2 * pl.ws_cH + pl.ws_cS;
+      fq.ys_b = 0; fq.ys_t = 0;
       fq.Bs_b = q.Bs_b; fq.Bs_t = q.Bs_t; fq.Bs_n = q.Bs_n;
       fq.Cs_b = q.Cs_b; fq.Cs_t = q.Cs_t; fq.Cs_n = q.Cs_n;
       fq.As_d = q.As_d; fq.As_n = q.As_n;

@@ -20,7 +20,9 @@ struct ScanParams {
   const float* h0;
   float* h_last;
   int64_t batch, L, D, N;
-  int64_t xs_b, xs_t, ds_b, ds_t, zs_b, zs_t, ys_b, ys_t;  // element strides
+  // element strides; ys_b = ys_t = 0 makes y one scratch row of D elements
+  // that every store lands in (when only the checkpoints are wanted)
+  int64_t xs_b, xs_t, ds_b, ds_t, zs_b, zs_t, ys_b, ys_t;
   int64_t Bs_b, Bs_t, Bs_n, Cs_b, Cs_t, Cs_n;
   int64_t As_d, As_n, Ds_d;
   uint32_t flags;
