@@ -29,6 +29,8 @@
 // contraction slots permuted the same way in both operands.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -593,28 +595,60 @@ hipError_t launch_ssd_state_passing(const SSDParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_ssd_chunk_scan(const SSDParams& p, hipStream_t stream) {
-  // Heads per workgroup: about 1024 workgroups, heads of one group only.
+// Workgroups of chunk_scan<Q, NB> (4Q threads) resident on the whole device,
+// looked up once per device (256, one per compute unit, if the lookup fails).
+constexpr int kSlotDevices = 64;
+
+template <int Q, int NB>
+int64_t chunk_scan_slots() {
+  static std::atomic<int> cache[kSlotDevices];  // 0: not looked up yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSlotDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int ncu = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&chunk_scan_kernel<Q, NB>),
+                                                     4 * Q, 0) != hipSuccess ||
+        ncu <= 0 || per_cu <= 0) {
+      (void)hipGetLastError();
+      return 256;
+    }
+    v = ncu * per_cu;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+template <int Q, int NB>
+void launch_scan_q(const SSDParams& p, hipStream_t stream) {
+  // heads of one group per workgroup, as many as keep the rounds of
+  // workgroups few (at chunk 256 and N = 64: 20 heads, one round of 256)
   const int64_t hpg = p.H / p.G;
-  const int64_t units = p.batch * p.nchunks * p.H;
-  int64_t hb = units / 1024;
-  hb = hb < 1 ? 1 : (hb > 8 ? 8 : hb);
-  hb = hb > hpg ? hpg : hb;
-  const int HB = (int)hb, nhb = (int)((hpg + hb - 1) / hb);
-  const unsigned nb = (unsigned)(p.batch * p.nchunks * p.G * nhb);
+  const int64_t base = p.batch * p.nchunks * p.G;
+  const int HB = ssd_heads_per_block(hpg, base, chunk_scan_slots<Q, NB>());
+  const int nhb = (int)((hpg + HB - 1) / HB);
+  const unsigned nb = (unsigned)(base * nhb);
+  hipLaunchKernelGGL((chunk_scan_kernel<Q, NB>), dim3(nb), dim3(4 * Q), 0, stream, p, HB, nhb);
+}
+
+hipError_t launch_ssd_chunk_scan(const SSDParams& p, hipStream_t stream) {
   // (chunk, states) pairs whose staging fits in LDS; the host rejects chunk
   // 256 with 256 states
   if (p.N == 64) {
-    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 1>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
-    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 1>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
-    else hipLaunchKernelGGL((chunk_scan_kernel<256, 1>), dim3(nb), dim3(1024), 0, stream, p, HB, nhb);
+    if (p.Q == 64) launch_scan_q<64, 1>(p, stream);
+    else if (p.Q == 128) launch_scan_q<128, 1>(p, stream);
+    else launch_scan_q<256, 1>(p, stream);
   } else if (p.N == 128) {
-    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 2>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
-    else if (p.Q == 128) hipLaunchKernelGGL((chunk_scan_kernel<128, 2>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
-    else hipLaunchKernelGGL((chunk_scan_kernel<256, 2>), dim3(nb), dim3(1024), 0, stream, p, HB, nhb);
+    if (p.Q == 64) launch_scan_q<64, 2>(p, stream);
+    else if (p.Q == 128) launch_scan_q<128, 2>(p, stream);
+    else launch_scan_q<256, 2>(p, stream);
   } else {
-    if (p.Q == 64) hipLaunchKernelGGL((chunk_scan_kernel<64, 4>), dim3(nb), dim3(256), 0, stream, p, HB, nhb);
-    else hipLaunchKernelGGL((chunk_scan_kernel<128, 4>), dim3(nb), dim3(512), 0, stream, p, HB, nhb);
+    if (p.Q == 64) launch_scan_q<64, 4>(p, stream);
+    else launch_scan_q<128, 4>(p, stream);
   }
   return hipGetLastError();
 }

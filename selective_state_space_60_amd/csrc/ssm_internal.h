@@ -215,6 +215,26 @@ hipError_t launch_ssd_bwd(const SSDBwdParams& p, float* dA, float* dB, float* dC
 void launch_fixed_order_sum(const float* src, float* dst, int64_t count, int64_t parts, int64_t stride,
                             hipStream_t stream);
 
+// Heads per workgroup for the SSD kernels whose workgroup takes a block of one
+// group's heads in turn (chunk_scan, and the backward's dC and dx passes):
+// the count that minimises (rounds of workgroups) x (heads + 1), where `base`
+// workgroups share each head block (batch x chunks x groups), `slots`
+// workgroups are resident at once, and one head's time stands for a
+// workgroup's set-up (staging B and C, its first head's loads, which nothing
+// overlaps).  Ties go to fewer workgroups.
+inline int ssd_heads_per_block(int64_t hpg, int64_t base, int64_t slots) {
+  int64_t best = 1, best_cost = -1;
+  for (int64_t hb = 1; hb <= hpg; ++hb) {
+    const int64_t nhb = (hpg + hb - 1) / hb;
+    const int64_t cost = ((base * nhb + slots - 1) / slots) * (hb + 1);
+    if (best_cost < 0 || cost <= best_cost) {
+      best_cost = cost;
+      best = hb;
+    }
+  }
+  return (int)best;
+}
+
 hipError_t launch_ssd_chunk_cumsum(const SSDParams& p, hipStream_t stream);
 hipError_t launch_ssd_chunk_state(const SSDParams& p, hipStream_t stream);
 hipError_t launch_ssd_state_passing(const SSDParams& p, hipStream_t stream);

@@ -351,8 +351,11 @@ def test_ssd_bwd_workspace():
     n = ctypes.c_size_t()
     assert ssm.lib().ssm_ssd_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == ssm.SSM_OK
     nc, E = 16, 64 * 64
-    HB = 5  # 4 * 16 * 80 units / 1024 per workgroup, at most 8
-    nhb = 16
+    # chunk 256, 64 states: heads per workgroup that give the fewest rounds of
+    # one workgroup per compute unit x (heads + 1): 20, so 4 head blocks and
+    # 4 * 16 * 4 = 256 workgroups, one round
+    HB = 20
+    nhb = 4
     want = (2 * 4 * 80 * 4096 * 4 + 3 * 4 * nc * 80 * E * 4 + 3 * 4 * nc * 80 * E * 2 + 4 * 80 * nc * 4 * 4 +
             5 * 4 * 80 * 4096 * 4 + 2 * 4 * nc * 80 * 4 + 2 * nhb * 4 * 4096 * 64 * 4)
     assert HB * nhb == 80
