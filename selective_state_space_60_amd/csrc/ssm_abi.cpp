@@ -381,16 +381,11 @@ SSDBwdPlan plan_ssd_bwd(const ssm_ssd_bwd_desc& d) {
   const ssm_ssd_desc f = ssd_fwd_of(d);
   pl.f = plan_ssd(f);
   const int64_t nc = pl.f.nchunks, hpg = d.nheads / d.ngroups;
-  // heads per workgroup of the dC / dx passes.  At chunk 256 with 64 states
-  // both run one workgroup per compute unit: as few rounds of workgroups as
-  // the heads allow (ssd_heads_per_block; 20 heads and one round at the 2.7B
-  // layer).  Otherwise enough workgroups to fill the chip (about 4 per
-  // compute unit), as few partial sums of dB, dC as that allows.
-  const int64_t units = d.batch * nc * d.nheads;
-  if (d.chunk == 256 && d.dstate == 64)
-    pl.HB = ssm::ssd_heads_per_block(hpg, d.batch * nc * d.ngroups, kSimds / 4);
-  else
-    pl.HB = (int)std::max<int64_t>(1, std::min<int64_t>({8, hpg, units / 1024}));
+  // heads per workgroup of the dC / dx passes: as few rounds of workgroups
+  // as the heads allow (ssd_heads_per_block), counted for the dx pass, which
+  // sets the time and runs one workgroup per compute unit (20 heads and one
+  // round at the 2.7B layer with chunk 256; 40 at chunk 128)
+  pl.HB = ssm::ssd_heads_per_block(hpg, d.batch * nc * d.ngroups, kSimds / 4);
   pl.nhb = (int)((hpg + pl.HB - 1) / pl.HB);
   const int64_t E = d.batch * nc * d.nheads * d.headdim * d.dstate;
   pl.ws_state = round256(E * 4);
