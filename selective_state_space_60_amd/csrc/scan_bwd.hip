@@ -56,17 +56,6 @@ __device__ __forceinline__ float ld(const void* p, int64_t i) {
   else return ((const float*)p)[i];
 }
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two floats to a bf16 pair (a in the low half), round to nearest even as
-// st() does: one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  const f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
 __device__ __forceinline__ void st(void* p, int64_t i, float v, bool f32) {
   if (f32) ((float*)p)[i] = v;
   else ((__bf16*)p)[i] = (__bf16)v;
@@ -133,7 +122,6 @@ struct BwdSmem {
   float2 bc[TT][G * KS];
   float part[2][NT][TP];          // per-lane partial sums over states, by step
   float red[4][TT][2][G * KS];    // per-wave sums of dB, dC over the wave's 4 channels
-  float out[3][TT][CH];           // the tile's dx, ddelta, dz: [step][channel]
 };
 
 template <int KS>
@@ -397,22 +385,6 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
   char* pdz = p.dz ? (char*)p.dz + (b * p.dzs_b + ((int64_t)it_hi * TT + sg) * p.dzs_t + dd) * e_dz : nullptr;
   const int64_t sdx = TT * p.dxs_t * e_dx, sdd = TT * p.dds_t * e_dd, sdz = TT * p.dzs_t * e_dz;
   const bool dx_f32 = p.dx_f32, dd_f32 = p.dd_f32, dz_f32 = p.dz_f32;
-  // Vector stores of the tile's outputs: wave w < 3 stores output w (dx,
-  // ddelta, dz), lane l step l / 4, channels d0 + 4 (l % 4) .. + 3.
-  const bool out_vec = p.out_vec != 0, red_vec = p.red_vec != 0;
-  const int vo_r = (tid % 64) / 4, vo_q = tid % 4;
-  const bool vo_ok = (wave == 0 || wave == 1 || (wave == 2 && p.dz)) && d0 + 4 * vo_q < p.D;
-  const bool vo_f32 = wave == 0 ? dx_f32 : (wave == 1 ? dd_f32 : dz_f32);
-  const int64_t vo_e = vo_f32 ? 4 : 2;
-  char* vo_p = nullptr;
-  int64_t vo_step = 0;
-  if (vo_ok) {
-    const int64_t vs_b = wave == 0 ? p.dxs_b : (wave == 1 ? p.dds_b : p.dzs_b);
-    const int64_t vs_t = wave == 0 ? p.dxs_t : (wave == 1 ? p.dds_t : p.dzs_t);
-    char* vbase = (char*)(wave == 0 ? p.dx : (wave == 1 ? p.ddelta : p.dz));
-    vo_p = vbase + (b * vs_b + ((int64_t)it_hi * TT + vo_r) * vs_t + d0 + 4 * vo_q) * vo_e;
-    vo_step = TT * vs_t * vo_e;
-  }
   // dB, dC partials: element (j, q, n) of a tile per thread (2 * KS of them)
   constexpr int RED = TT * 2 * G * KS / NT;
   static_assert(RED * NT == TT * 2 * G * KS, "whole tiles of dB, dC partials");
@@ -506,8 +478,7 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
       const float sgm = sigmoid_f32(zj);
       g = gyj * zj * sgm;
       const float dz = gyj * o * sgm * __builtin_fmaf(zj, 1.f - sgm, 1.f);
-      if (out_vec) s.out[2][sg][c] = dz;
-      else if (j_ok) st(pdz, 0, dz, dz_f32);
+      if (j_ok) st(pdz, 0, dz, dz_f32);
     }
     dD = __builtin_fmaf(g, hx, dD);
     // the reverse recomputes its per-step values instead of keeping the
@@ -591,56 +562,22 @@ __device__ __forceinline__ void bwd_walk(BwdSmem<KS>& s, const ScanBwdParams& p,
       dts *= sigmoid_f32(dv);
       if (j_ok) dbias += dts;
     }
-    if (out_vec) {
-      s.out[0][sg][c] = dxs;
-      s.out[1][sg][c] = dts;
-    } else if (j_ok) {
+    if (j_ok) {
       st(pdx, 0, dxs, dx_f32);
       st(pdd, 0, dts, dd_f32);
     }
     __syncthreads();
-    // dx, ddelta, dz of the tile, 4 channels of one step per lane: wave 0
-    // stores dx, wave 1 ddelta, wave 2 dz (a lane storing one 2-byte value
-    // per output had made each store instruction touch 16 rows)
-    if (out_vec && vo_ok && t0 + vo_r < L) {
-      const float4 v = *(const float4*)&s.out[wave][vo_r][4 * vo_q];
-      if (vo_f32) {
-        *(float4*)vo_p = v;
-      } else {
-        uint2 w;
-        w.x = pack2(v.x, v.y);
-        w.y = pack2(v.z, v.w);
-        *(uint2*)vo_p = w;
-      }
-    }
-    vo_p -= vo_step;
     // dB, dC of the tile: sum over the 4 waves, store the workgroup's partial
-    // (written once, read back only by the reduction kernel: non-temporal, so
-    // these 2 KB per tile do not displace the input lines that the
-    // neighbouring workgroups share in L2)
-    if (red_vec) {
-      for (int i = tid; i < TT * 2 * G * KS / 4; i += NT) {
-        const int j = i / (2 * G * KS / 4), q = (i / (G * KS / 4)) % 2, n = (i % (G * KS / 4)) * 4;
-        const float4 a0 = *(const float4*)&s.red[0][j][q][n], a1 = *(const float4*)&s.red[1][j][q][n];
-        const float4 a2 = *(const float4*)&s.red[2][j][q][n], a3 = *(const float4*)&s.red[3][j][q][n];
-        f32x4 v;
-        v[0] = a0.x + a1.x + a2.x + a3.x;
-        v[1] = a0.y + a1.y + a2.y + a3.y;
-        v[2] = a0.z + a1.z + a2.z + a3.z;
-        v[3] = a0.w + a1.w + a2.w + a3.w;
-        if (t0 + j < L && n < N)
-          __builtin_nontemporal_store(
-              v, (f32x4*)((q == 0 ? p.pdB : p.pdC) + ((dblk * p.batch + b) * L + t0 + j) * p.N + n));
-      }
-    } else {
 #pragma unroll
-      for (int r = 0; r < RED; ++r) {
-        const int i = tid + r * NT;
-        const int j = i / (2 * G * KS), q = (i / (G * KS)) % 2, n = i % (G * KS);
-        const float v = s.red[0][j][q][n] + s.red[1][j][q][n] + s.red[2][j][q][n] + s.red[3][j][q][n];
-        if (t0 + red_j[r] < L && red_n_ok[r]) __builtin_nontemporal_store(v, pred[r]);
-        pred[r] -= red_step;
-      }
+    for (int r = 0; r < RED; ++r) {
+      const int i = tid + r * NT;
+      const int j = i / (2 * G * KS), q = (i / (G * KS)) % 2, n = i % (G * KS);
+      const float v = s.red[0][j][q][n] + s.red[1][j][q][n] + s.red[2][j][q][n] + s.red[3][j][q][n];
+      // written once, read back only by the reduction kernel: non-temporal,
+      // so these 2 KB per tile do not displace the input lines that the
+      // neighbouring workgroups share in L2
+      if (t0 + red_j[r] < L && red_n_ok[r]) __builtin_nontemporal_store(v, pred[r]);
+      pred[r] -= red_step;
     }
     pdx -= sdx;
     pdd -= sdd;
@@ -913,15 +850,7 @@ void launch_fixed_order_sum(const float* src, float* dst, int64_t count, int64_t
   reduce(src, dst, count, parts, stride, stream);
 }
 
-hipError_t launch_selective_scan_bwd(const ScanBwdParams& p_in, hipStream_t stream) {
-  ScanBwdParams p = p_in;
-  auto row_al = [](const void* q, int64_t b, int64_t t, bool f32) {
-    const int64_t e = f32 ? 4 : 2;
-    return q == nullptr || (((uintptr_t)q % (uintptr_t)(4 * e)) == 0 && b % 4 == 0 && t % 4 == 0);
-  };
-  p.out_vec = p.D % 4 == 0 && row_al(p.dx, p.dxs_b, p.dxs_t, p.dx_f32) && row_al(p.ddelta, p.dds_b, p.dds_t, p.dd_f32) &&
-              row_al(p.dz, p.dzs_b, p.dzs_t, p.dz_f32);
-  p.red_vec = p.N % 4 == 0;  // the partial buffers are the workspace's, 256-byte aligned
+hipError_t launch_selective_scan_bwd(const ScanBwdParams& p, hipStream_t stream) {
   if (p.io_bf16) launch_io<true>(p, stream);
   else launch_io<false>(p, stream);
   return hipGetLastError();

@@ -127,10 +127,6 @@ struct ScanBwdParams {
   int dy_f32;     // dy fp32 (1) or io (0)
   int dx_f32, dd_f32, dz_f32;
   int euler, dsoftplus;
-  // set by the launcher: dx, ddelta, dz rows start 4-element aligned (a
-  // tile's values go out 4 channels per lane); N % 4 == 0 (the dB, dC
-  // partial sums go out 4 states per lane)
-  int out_vec, red_vec;
 };
 
 hipError_t launch_selective_scan_bwd(const ScanBwdParams& p, hipStream_t stream);
