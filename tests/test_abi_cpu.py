@@ -369,6 +369,32 @@ def test_ssd_bwd_workspace():
     assert n.value - m.value == 2 * 4 * 80 * 4096 * 4 + 4 * nc * 80 * E * 4
 
 
+@pytest.mark.parametrize("batch,L,H,Q,nhb", [
+    (4, 4096, 80, 256, 4),   # 64 (batch, chunk) pairs: 20 heads per workgroup, 256 workgroups
+    (4, 4096, 80, 128, 2),   # 128 pairs: 40 heads, 256 workgroups
+    (1, 4096, 80, 256, 16),  # 16 pairs: 5 heads, 256 workgroups
+    (1, 300, 8, 64, 8),      # 5 pairs: one head per workgroup (one round either way)
+])
+def test_ssd_bwd_head_blocks(batch, L, H, Q, nhb):
+    # the dB, dC partial sums (two fp32 (nhb, batch, L, G, N) buffers, the last
+    # part of the workspace) count the head blocks the planner chose: the head
+    # count that minimises (rounds of 256 workgroups) x (heads + 1)
+    d, _ = _ssd_bwd(batch=batch, L=L, H=H, Q=Q)
+    n = ctypes.c_size_t()
+    assert ssm.lib().ssm_ssd_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == ssm.SSM_OK
+    part = 4 * batch * L * 64  # one head block's dB (or dC) partial sums
+    r256 = lambda v: (v + 255) // 256 * 256
+    rest = n.value - 2 * r256(nhb * part)
+    # the rest of the workspace does not depend on the head blocks
+    nc = (L + Q - 1) // Q
+    E = 64 * 64
+    Lp = nc * Q
+    want_rest = (2 * r256(batch * H * Lp * 4) + 3 * r256(batch * nc * H * E * 4) + 3 * r256(batch * nc * H * E * 2) +
+                 r256(batch * H * nc * 4 * 4) + r256(batch * H * Lp * 4) + 4 * r256(batch * H * Lp * 4) +
+                 2 * r256(batch * nc * H * 4))
+    assert rest == want_rest, (rest, want_rest)
+
+
 def test_ssd_workspace_size():
     d, p = _ssd(batch=4, L=4096, H=80, Q=256)
     n = ssm.ssd_chunk_workspace_size(d)
