@@ -60,6 +60,33 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// fp16 pairs (a in the low half), round to nearest even, and back to floats
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2h(float a, float b) {
+  const f16x2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ f32x2_t unpack2h(uint32_t v) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2, v), f32x2_t);
+}
+
+// largest magnitude of 8 bf16 values
+__device__ __forceinline__ float max_abs8(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xFFFF0000u))));
+  return m;
+}
+
+// maximum over the wave's 64 lanes, in every lane
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
 // ------------------------------------------------------------ s1 cumsum
 
 constexpr int kCumHeads = 16;  // heads per block; 16 threads per head
@@ -360,6 +387,20 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
   // stored at chunk q ^ (p % 8) so the inter-chunk reads (16 rows, one chunk)
   // spread over the banks.
   __shared__ __attribute__((aligned(16))) uint4 Ss[64][8 * NB];
+  // C B^T is the group's, the same for every head: at chunk 256 (one
+  // workgroup per CU) each wave forms its strip's tiles of it once, before
+  // the heads, and keeps them in LDS -- 1 KB per (strip, 32-step block),
+  // read back by the lanes that wrote them.  Per head and block that
+  // replaces 4 matrix-core products and 4 KB of B operand reads by one 1 KB
+  // read.  Strip s holds blocks 0 .. s/2, from slot goff(s).  The tiles are
+  // stored as fp16 times a power of two chosen from N max|B| max|C| (so no
+  // tile can overflow): one rounding at fp16's 11 bits, where bf16 storage
+  // would have added a second rounding at 8 bits before the decay.
+  constexpr int NPAIR = (NSTRIP / 2) * (NSTRIP / 2 + 1);
+  constexpr bool GPRE = Q == 256 && (sizeof(uint16_t) * Q * (PR + PRB) + 3 * 4 * Q + 16 * 64 * 8 * NB +
+                                     1024 * NPAIR) <= 160 * 1024;
+  __shared__ __attribute__((aligned(16))) uint4 Gs[GPRE ? NPAIR * 64 : 1];
+  __shared__ float wmaxB[NTH / 64];  // max |B| of each wave's staged pieces
 
   int64_t bid = blockIdx.x;
   const int hbk = (int)(bid % nhb);
@@ -425,17 +466,59 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
     for (int ks = 0; ks < KS; ++ks) Cop[ks] = as_bf16x8(*(const uint4*)(Cb + tr * p.Cs_t + 32 * ks + 8 * lq));
   }
   // rows at or past L hold zeros
+  float mB = 0.f;
 #pragma unroll
   for (int u = 0; u < NTB; ++u) {
     const int task = tid + NTH * u;
     const int j = task / (8 * NB), cb = (task % (8 * NB)) * 8;
     const bool ok = t0 + j < p.L;
-    *(uint4*)&Bs[j][cb] = ok ? rb[u] : make_uint4(0, 0, 0, 0);
+    const uint4 v = ok ? rb[u] : make_uint4(0, 0, 0, 0);
+    *(uint4*)&Bs[j][cb] = v;
+    if constexpr (GPRE) mB = fmaxf(mB, max_abs8(v));
   }
   // C rows past L must not contribute
   if (ti >= p.L)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) Cop[ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  // G^T = B_J C_I^T for the strip's blocks: G^T[j0 + 16*jt + 4*lq + r][i]
+  auto form_gt = [&](int j0, f32x4 (&gt)[2]) {
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        a = mfma(as_bf16x8(*(const uint4*)&Bs[j0 + 16 * jt + lr][32 * ks + 8 * lq]), Cop[ks], a);
+      gt[jt] = a;
+    }
+  };
+  const int goff = (kst % 2 == 0) ? (kst / 2) * (kst / 2 + 1) : ((kst + 1) / 2) * ((kst + 1) / 2);
+  float g_unscale = 1.f;  // 2^-k, the inverse of the stored tiles' scale
+  if constexpr (GPRE) {
+    mB = wave_max(mB);
+    if (l == 0) wmaxB[wv] = mB;
+    float mC = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) mC = fmaxf(mC, max_abs8(__builtin_bit_cast(uint4, Cop[ks])));
+    mC = wave_max(mC);
+    __syncthreads();  // the B rows and the wave maxima are staged
+#pragma unroll
+    for (int w = 0; w < NTH / 64; ++w) mB = fmaxf(mB, wmaxB[w]);
+    // |G| <= N max|B| max|C| < 2^e; scaled by 2^(14 - e) every tile is below
+    // 2^14 (fp16 holds up to 65504)
+    const float bound = (float)N * mB * mC;
+    int e = bound > 0.f ? __builtin_amdgcn_frexp_expf(bound) : 0;
+    e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    const float g_scale = __builtin_ldexpf(1.f, 14 - e);
+    g_unscale = __builtin_ldexpf(1.f, e - 14);
+    for (int jb = 0; jb <= i0 / 32; ++jb) {
+      f32x4 gt[2];
+      form_gt(32 * jb, gt);
+      Gs[(goff + jb) * 64 + l] = make_uint4(pack2h(gt[0][0] * g_scale, gt[0][1] * g_scale),
+                                            pack2h(gt[0][2] * g_scale, gt[0][3] * g_scale),
+                                            pack2h(gt[1][0] * g_scale, gt[1][1] * g_scale),
+                                            pack2h(gt[1][2] * g_scale, gt[1][3] * g_scale));
+    }
+  }
 
   for (int k = 0; k < nh; ++k) {
     const int64_t h = h_lo + k;
@@ -489,20 +572,20 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
       }
       {
         f32x4 gt[2];
-  #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          // A operands of G^T = B_J C_I^T: B rows j0 + 16*jt + lr, read per use
-          f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            a = mfma(as_bf16x8(*(const uint4*)&Bs[j0 + 16 * jt + lr][32 * ks + 8 * lq]), Cop[ks], a);
-          gt[jt] = a;  // G^T[j0 + 16*jt + 4*lq + r][i]
+        if constexpr (GPRE) {
+          // the stored tile (still scaled: g_unscale goes into the decay factors)
+          const uint4 q4 = Gs[(goff + jb) * 64 + l];
+          const f32x2_t g0 = unpack2h(q4.x), g1 = unpack2h(q4.y), g2 = unpack2h(q4.z), g3 = unpack2h(q4.w);
+          gt[0] = f32x4{g0.x, g0.y, g1.x, g1.y};
+          gt[1] = f32x4{g2.x, g2.y, g3.x, g3.y};
+        } else {
+          form_gt(j0, gt);  // B rows j0 + 16*jt + lr, read per use
         }
         float v[8];
         if (jb < diag) {
           // every j of the block precedes every row of the strip:
           // exp(A_i - A_j) = exp(A_i - A_m) exp(A_m - A_j), m = j0 + 31, both <= 1
-          const float vi = __builtin_amdgcn_exp2f(A2[i] - A2[j0 + 31]);
+          const float vi = __builtin_amdgcn_exp2f(A2[i] - A2[j0 + 31]) * g_unscale;
   #pragma unroll
           for (int jt = 0; jt < 2; ++jt) {
             const float4 t4 = *(const float4*)&tb[j0 + 16 * jt + 4 * lq];
@@ -518,7 +601,7 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
             const float4 a4 = *(const float4*)&A2[j0 + 16 * jt + 4 * lq];
             const float4 b4 = *(const float4*)&bj[j0 + 16 * jt + 4 * lq];
             const float aj[4] = {a4.x, a4.y, a4.z, a4.w};
-            const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+            const float bb[4] = {b4.x * g_unscale, b4.y * g_unscale, b4.z * g_unscale, b4.w * g_unscale};
   #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int j = j0 + 16 * jt + 4 * lq + r;
