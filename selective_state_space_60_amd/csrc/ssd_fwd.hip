@@ -387,19 +387,25 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
   // stored at chunk q ^ (p % 8) so the inter-chunk reads (16 rows, one chunk)
   // spread over the banks.
   __shared__ __attribute__((aligned(16))) uint4 Ss[64][8 * NB];
-  // C B^T is the group's, the same for every head: at chunk 256 (one
-  // workgroup per CU) each wave forms its strip's tiles of it once, before
-  // the heads, and keeps them in LDS -- 1 KB per (strip, 32-step block),
-  // read back by the lanes that wrote them.  Per head and block that
-  // replaces 4 matrix-core products and 4 KB of B operand reads by one 1 KB
-  // read.  Strip s holds blocks 0 .. s/2, from slot goff(s).  The tiles are
-  // stored as fp16 times a power of two chosen from N max|B| max|C| (so no
-  // tile can overflow): one rounding at fp16's 11 bits, where bf16 storage
-  // would have added a second rounding at 8 bits before the decay.
+  // C B^T is the group's, the same for every head, yet the head loop would
+  // form it per head and block (for N states, 2N/32 of the block's
+  // matrix-core products and 2N/32 KB of B operand reads per wave).  So each
+  // wave forms its strip's tiles once, before the heads, and keeps them in
+  // LDS -- 1 KB per (strip, 32-step block), read back by the lanes that
+  // wrote them; strip s holds blocks 0 .. s/2 from slot goff(s).  At chunk
+  // 256 with N = 64 the tiles get their own 72 KB (the workgroup is alone on
+  // its CU); at chunk 128 and below they are written over the staged B rows,
+  // which they fit in and which nothing reads afterwards (chunk 256 with
+  // N = 128 has room for neither and forms them per head).  The tiles are
+  // stored as fp16 times a power of two chosen from N max|B| max|C| (so none
+  // can overflow): one rounding at fp16's 11 bits, where bf16 storage would
+  // add a second rounding at 8 bits before the decay.
   constexpr int NPAIR = (NSTRIP / 2) * (NSTRIP / 2 + 1);
-  constexpr bool GPRE = Q == 256 && (sizeof(uint16_t) * Q * (PR + PRB) + 3 * 4 * Q + 16 * 64 * 8 * NB +
+  constexpr bool GSEP = Q == 256 && (sizeof(uint16_t) * Q * (PR + PRB) + 3 * 4 * Q + 16 * 64 * 8 * NB +
                                      1024 * NPAIR) <= 160 * 1024;
-  __shared__ __attribute__((aligned(16))) uint4 Gs[GPRE ? NPAIR * 64 : 1];
+  constexpr bool GALIAS = !GSEP && Q <= 128 && 1024 * NPAIR <= sizeof(uint16_t) * Q * PRB;
+  constexpr bool GPRE = GSEP || GALIAS;
+  __shared__ __attribute__((aligned(16))) uint4 Gsep[GSEP ? NPAIR * 64 : 1];
   __shared__ float wmaxB[NTH / 64];  // max |B| of each wave's staged pieces
 
   int64_t bid = blockIdx.x;
@@ -510,13 +516,25 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
     e = e < -100 ? -100 : (e > 100 ? 100 : e);
     const float g_scale = __builtin_ldexpf(1.f, 14 - e);
     g_unscale = __builtin_ldexpf(1.f, e - 14);
-    for (int jb = 0; jb <= i0 / 32; ++jb) {
+    auto tile = [&](int jb) {
       f32x4 gt[2];
       form_gt(32 * jb, gt);
-      Gs[(goff + jb) * 64 + l] = make_uint4(pack2h(gt[0][0] * g_scale, gt[0][1] * g_scale),
-                                            pack2h(gt[0][2] * g_scale, gt[0][3] * g_scale),
-                                            pack2h(gt[1][0] * g_scale, gt[1][1] * g_scale),
-                                            pack2h(gt[1][2] * g_scale, gt[1][3] * g_scale));
+      return make_uint4(pack2h(gt[0][0] * g_scale, gt[0][1] * g_scale), pack2h(gt[0][2] * g_scale, gt[0][3] * g_scale),
+                        pack2h(gt[1][0] * g_scale, gt[1][1] * g_scale), pack2h(gt[1][2] * g_scale, gt[1][3] * g_scale));
+    };
+    if constexpr (GSEP) {
+      for (int jb = 0; jb <= i0 / 32; ++jb) Gsep[(goff + jb) * 64 + l] = tile(jb);
+    } else {
+      // all tiles into registers, then over the B rows once every wave has read them
+      constexpr int MAXB = NSTRIP / 2;  // blocks of the last strip
+      uint4 gq[MAXB];
+#pragma unroll
+      for (int jb = 0; jb < MAXB; ++jb)
+        if (jb <= i0 / 32) gq[jb] = tile(jb);
+      __syncthreads();
+#pragma unroll
+      for (int jb = 0; jb < MAXB; ++jb)
+        if (jb <= i0 / 32) ((uint4*)&Bs[0][0])[(goff + jb) * 64 + l] = gq[jb];
     }
   }
 
@@ -574,7 +592,9 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
         f32x4 gt[2];
         if constexpr (GPRE) {
           // the stored tile (still scaled: g_unscale goes into the decay factors)
-          const uint4 q4 = Gs[(goff + jb) * 64 + l];
+          uint4 q4;
+          if constexpr (GSEP) q4 = Gsep[(goff + jb) * 64 + l];
+          else q4 = ((const uint4*)&Bs[0][0])[(goff + jb) * 64 + l];
           const f32x2_t g0 = unpack2h(q4.x), g1 = unpack2h(q4.y), g2 = unpack2h(q4.z), g3 = unpack2h(q4.w);
           gt[0] = f32x4{g0.x, g0.y, g1.x, g1.y};
           gt[1] = f32x4{g2.x, g2.y, g3.x, g3.y};
