@@ -281,6 +281,105 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(SSDBwdParams q) {
   if (q.dh0) *(float4*)(q.dh0 + (b * p.H + h) * E + e0) = G;
 }
 
+// bwd_state_kernel with the entering states kept in registers, for up to
+// NCMAX chunks: the fp32 copy of them that the backward sweep needs (for
+// <S_in[c], G>) then never goes to memory and back -- a third of the pass's
+// traffic.  Block as there (16 rows, 64 columns), 512 threads of 2 values;
+// the loops are unrolled over NCMAX register slots, slot k holding chunk
+// k - (NCMAX - nchunks), so every slot is a fixed register, and the loads
+// run PD chunks ahead.
+template <int NCMAX>
+__global__ __launch_bounds__(512) void bwd_state_reg_kernel(SSDBwdParams q) {
+  constexpr int PD = 4, NW = 8;
+  const SSDParams& p = q.f;
+  __shared__ __attribute__((aligned(16))) uint16_t T[2][64][16 + 4];  // [n - nc0][p - p0]
+  __shared__ float red[2][NW];
+  const int nblk = (int)(p.N / 64), nq = 4 * nblk;
+  int64_t bid = blockIdx.x;
+  const int qb = (int)(bid % nq);
+  bid /= nq;
+  const int64_t h = bid % p.H, b = bid / p.H;
+  const int tid = threadIdx.x, wv = tid / 64;
+  const int p0 = (qb / nblk) * 16, nc0 = 64 * (qb % nblk), pl = tid / 32, nl = 2 * (tid % 32);
+  const int64_t E = kP * p.N;
+  const int e0 = (p0 + pl) * (int)p.N + nc0 + nl;
+  const int tn = tid / 8, tq = 2 * (tid % 8);  // transposed store: row n = nc0 + tn, p0 + tq, +1
+  const float* Ac = p.A_cum + (b * p.H + h) * p.Lp;
+  const int64_t cs = p.H * E;
+  const int64_t base = (b * p.nchunks * p.H + h) * E;
+  const int nc = (int)p.nchunks, off = NCMAX - nc;  // slot k: chunk k - off
+  auto put_T = [&](int buf, float2 v) {
+    T[buf][nl][pl] = f2bf(v.x);
+    T[buf][nl + 1][pl] = f2bf(v.y);
+  };
+  auto store_T = [&](int buf, uint16_t* dst) {
+    *(uint32_t*)(dst + (nc0 + tn) * kP + p0 + tq) = *(const uint32_t*)&T[buf][tn][tq];
+  };
+  float2 S = make_float2(0.f, 0.f);
+  if (p.h0) S = *(const float2*)(p.h0 + (b * p.H + h) * E + e0);
+  float2 Sh[NCMAX], ld[NCMAX];  // history; loads in flight
+  float ae[NCMAX];              // A_cum at the chunk ends
+#pragma unroll
+  for (int k = 0; k < PD; ++k) {
+    const int c = k - off;
+    if (c >= 0) {
+      ld[k] = *(const float2*)(p.states + base + c * cs + e0);
+      ae[k] = Ac[c * p.Q + p.Q - 1];
+    }
+  }
+  int buf = 0;
+#pragma unroll
+  for (int k = 0; k < NCMAX; ++k) {
+    const int c = k - off;
+    // slot k + PD (chunk c + PD < nchunks), also in the slots before the
+    // first chunk: that is how the first PD chunks' slots get theirs
+    if (k + PD < NCMAX && c + PD >= 0) {
+      ld[k + PD] = *(const float2*)(p.states + base + (c + PD) * cs + e0);
+      ae[k + PD] = Ac[(c + PD) * p.Q + p.Q - 1];
+    }
+    if (c >= 0) {
+      const float dec = __builtin_amdgcn_exp2f(ae[k] * kLog2e);
+      Sh[k] = S;
+      put_T(buf, S);
+      __syncthreads();
+      store_T(buf, q.SinT + base + c * cs);
+      buf ^= 1;
+      S.x = __builtin_fmaf(dec, S.x, ld[k].x);
+      S.y = __builtin_fmaf(dec, S.y, ld[k].y);
+    }
+  }
+  float2 G = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int k = NCMAX - 1; k >= NCMAX - PD; --k)
+    if (k - off >= 0) ld[k] = *(const float2*)(q.dS + base + (k - off) * cs + e0);
+#pragma unroll
+  for (int k = NCMAX - 1; k >= 0; --k) {
+    const int c = k - off;
+    if (c >= 0) {
+      if (k - PD >= 0 && c - PD >= 0) ld[k - PD] = *(const float2*)(q.dS + base + (c - PD) * cs + e0);
+      const float dec = __builtin_amdgcn_exp2f(Ac[c * p.Q + p.Q - 1] * kLog2e);
+      *(uint32_t*)(q.dSl + base + c * cs + e0) = pack2(G.x, G.y);
+      put_T(buf, G);
+      float dot = Sh[k].x * G.x + Sh[k].y * G.y;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
+      if (tid % 64 == 0) red[buf][wv] = dot;
+      __syncthreads();
+      store_T(buf, q.dSlT + base + c * cs);
+      if (tid == 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) t += red[buf][w];
+        q.pAend[((b * p.H + h) * nc + c) * nq + qb] = dec * t;
+      }
+      buf ^= 1;
+      G.x = __builtin_fmaf(dec, G.x, ld[k].x);
+      G.y = __builtin_fmaf(dec, G.y, ld[k].y);
+    }
+  }
+  if (q.dh0) *(float2*)(q.dh0 + (b * p.H + h) * E + e0) = G;
+}
+
 // -------------------------------------------------------------- dC pass
 
 // Block = (b, chunk, group, head block), Q/32 waves; wave wv owns the two
@@ -1100,7 +1199,12 @@ hipError_t launch_ssd_bwd(const SSDBwdParams& q, float* dA, float* dB, float* dC
   f2.states = q.dS;
   f2.state_coef = 1;
   if ((e = launch_ssd_chunk_state(f2, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_state_kernel, dim3((unsigned)(p.batch * p.H * 4 * (p.N / 64))), dim3(256), 0, stream, q);
+  {
+    const dim3 grid((unsigned)(p.batch * p.H * 4 * (p.N / 64)));
+    if (p.nchunks <= 16) hipLaunchKernelGGL(bwd_state_reg_kernel<16>, grid, dim3(512), 0, stream, q);
+    else if (p.nchunks <= 32) hipLaunchKernelGGL(bwd_state_reg_kernel<32>, grid, dim3(512), 0, stream, q);
+    else hipLaunchKernelGGL(bwd_state_kernel, grid, dim3(256), 0, stream, q);
+  }
   if (p.Q == 64) launch_q<64>(q, stream);
   else if (p.Q == 128) launch_q<128>(q, stream);
   else launch_q<256>(q, stream);
