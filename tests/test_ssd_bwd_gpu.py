@@ -203,3 +203,12 @@ def test_ssd_bwd_from_forward_2_7b_full_equals_recompute():
     assert set(a) == set(b)
     for k in b:
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("seqlen", [1024, 1040, 2048, 2100])
+def test_ssd_bwd_state_pass_chunk_counts(seqlen):
+    """Chunk counts on both sides of the state pass's register-history limits
+    (16 and 32 chunks kept in registers, more by the kernel that keeps them
+    in memory): 16, 17, 32 and 33 chunks of 64 steps, with h0 (dh0 is the
+    gradient carried out of the first chunk)."""
+    _check(small(batch=1, nheads=2, seqlen=seqlen, chunk=64), 10, h0=True)

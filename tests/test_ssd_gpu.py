@@ -187,3 +187,35 @@ def test_larger_states_steps():
     assert_close(host_f64(S_in), ref["S_in"], "bf16", "chunk-entry states N256")
     assert_close(host_f64(hl), ref["h_last"], "bf16", "h_last N256")
     assert_close(host_f64(y), ref["y"], "bf16", "y N256")
+
+
+def _scale_bf16(bits, k):
+    """bf16 bit patterns times 2**k (exact: the exponent field moves by k;
+    zeros stay zero)."""
+    b = np.asarray(bits, np.uint16).astype(np.int32)
+    e = (b >> 7) & 0xFF
+    assert np.all((e == 0) | ((e + k > 0) & (e + k < 255))), "scaled out of the normal range"
+    return np.where(e == 0, b, b + (k << 7)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kb,kc", [(10, 9), (-20, -20)])
+@pytest.mark.parametrize("kw", [dict(chunk=256), dict(chunk=128, dstate=128), dict(chunk=64)],
+                         ids=lambda kw: "_".join("%s%s" % i for i in sorted(kw.items())))
+def test_magnitudes_of_B_and_C(kw, kb, kc):
+    """B and C times powers of two far from 1: y (no D skip) scales by exactly
+    2**(kb + kc) and h_last by 2**kb, bit for bit -- every step is
+    scale-equivariant, including chunk_scan's fp16 copy of C B^T, whose own
+    power-of-two scale follows max|B| max|C| (no tile may overflow fp16 or
+    fall into its subnormals) -- and y still meets the oracle."""
+    spec = small(seqlen=600, has_D=False, **kw)
+    inp = synth.ssd_inputs(spec, 11)
+    y0, h0_ = _run(spec, inp)
+    inp2 = dict(inp)
+    inp2["B"] = _scale_bf16(inp["B"], kb)
+    inp2["C"] = _scale_bf16(inp["C"], kc)
+    banner("ssd magnitudes %s kb %d kc %d" % (spec.name, kb, kc))
+    y1, h1 = _run(spec, inp2)
+    assert torch.equal(y1.float(), y0.float() * 2.0 ** (kb + kc))
+    assert torch.equal(h1, h0_ * 2.0 ** kb)
+    yr, _ = oracle.ssd(inp2, "bf16", ngroups=spec.ngroups)
+    assert_close(host_f64(y1), yr, "bf16", spec.name + " y, scaled B and C")
