@@ -138,10 +138,18 @@ __device__ __forceinline__ HeadBlock head_block(const SSDBwdParams& q, int nblk 
   return r;
 }
 
+// The transposed state tiles S_in^T and dS_loc^T of one (batch, chunk, head)
+// are laid out [p / 8][n][p % 8]: 8 consecutive p of one n are 16 contiguous
+// bytes (a row piece for the passes that stage them), and the state pass,
+// which writes 8 rows of p for 64 n at a time, writes whole cache lines.
+__device__ __forceinline__ int64_t tile_T(int64_t n, int p, int64_t N) { return ((p >> 3) * N + n) * 8 + (p & 7); }
+
 // Stage Q rows of W bf16 (zero rows at or past L) into rows[Q][W + kPad].
+// Row j's 8 columns from 8c are at src + j st + 8c cm (cm = 1: row-major;
+// the transposed state tiles below take cm = N).
 template <int Q, int NTH, int W = 64>
 __device__ __forceinline__ void stage_rows(uint16_t (*rows)[W + kPad], const uint16_t* src, int64_t st, int64_t t0,
-                                           int64_t L) {
+                                           int64_t L, int64_t cm = 1) {
   constexpr int PC = W / 8;  // 16-byte pieces per row
   constexpr int NTX = Q * PC / NTH;
   static_assert(NTX * NTH == Q * PC, "whole pieces per thread");
@@ -151,7 +159,7 @@ __device__ __forceinline__ void stage_rows(uint16_t (*rows)[W + kPad], const uin
     const int task = threadIdx.x + NTH * u;
     const int j = task / PC, cb = (task % PC) * 8;
     const int64_t tr = t0 + j < L ? t0 + j : L - 1;
-    v[u] = *(const uint4*)(src + tr * st + cb);
+    v[u] = *(const uint4*)(src + tr * st + cb * cm);
   }
 #pragma unroll
   for (int u = 0; u < NTX; ++u) {
@@ -170,13 +178,13 @@ struct RowsInFlight {
   static constexpr int NTX = QR * PC / NTH;
   static_assert(NTX * NTH == QR * PC, "whole pieces per thread");
   uint4 v[NTX];
-  __device__ __forceinline__ void load(const uint16_t* src, int64_t st, int64_t t0, int64_t L) {
+  __device__ __forceinline__ void load(const uint16_t* src, int64_t st, int64_t t0, int64_t L, int64_t cm = 1) {
 #pragma unroll
     for (int u = 0; u < NTX; ++u) {
       const int task = threadIdx.x + NTH * u;
       const int j = task / PC, cb = (task % PC) * 8;
       const int64_t tr = t0 + j < L ? t0 + j : L - 1;
-      v[u] = *(const uint4*)(src + tr * st + cb);
+      v[u] = *(const uint4*)(src + tr * st + cb * cm);
     }
   }
   __device__ __forceinline__ void store(uint16_t (*rows)[W + kPad], int64_t t0, int64_t L) const {
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(SSDBwdParams q) {
   const SSDParams& p = q.f;
   __shared__ __attribute__((aligned(16))) uint16_t T[2][64][16 + 4];  // [n - nc0][p - p0]
   __shared__ float red[2][4];
-  const int nblk = (int)(p.N / 64), nq = 4 * nblk;
+  const int nblk = (int)(p.N / 64), nq = q.aend_parts;  // 4 per 64-wide block of the states
   int64_t bid = blockIdx.x;
   const int qb = (int)(bid % nq);
   bid /= nq;
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(SSDBwdParams q) {
     T[buf][nl + 3][pl] = f2bf(v.w);
   };
   auto store_T = [&](int buf, uint16_t* dst) {
-    *(uint2*)(dst + (nc0 + tn) * kP + p0 + tq) = *(const uint2*)&T[buf][tn][tq];
+    *(uint2*)(dst + tile_T(nc0 + tn, p0 + tq, p.N)) = *(const uint2*)&T[buf][tn][tq];
   };
   float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
   if (p.h0) S = *(const float4*)(p.h0 + (b * p.H + h) * E + e0);
@@ -281,103 +289,182 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(SSDBwdParams q) {
   if (q.dh0) *(float4*)(q.dh0 + (b * p.H + h) * E + e0) = G;
 }
 
-// bwd_state_kernel with the entering states kept in registers, for up to
-// NCMAX chunks: the fp32 copy of them that the backward sweep needs (for
-// <S_in[c], G>) then never goes to memory and back -- a third of the pass's
-// traffic.  Block as there (16 rows, 64 columns), 512 threads of 2 values;
-// the loops are unrolled over NCMAX register slots, slot k holding chunk
-// k - (NCMAX - nchunks), so every slot is a fixed register, and the loads
-// run PD chunks ahead.
-template <int NCMAX>
-__global__ __launch_bounds__(512) void bwd_state_reg_kernel(SSDBwdParams q) {
-  constexpr int PD = 4, NW = 8;
+// The reverse state passing with the chunks in parallel: both recurrences,
+// S_in[c+1] = d_c S_in[c] + S_loc[c] and G[c] = d_c G[c+1] + dS[c] (d_c the
+// chunk-end decay), are affine maps composed along the chunks, so a row of
+// 16 lanes takes 16 chunks at once and composes their (d, .) pairs with a
+// 4-step shift-and-combine (DPP row shifts) instead of walking the chunks
+// with a barrier each; groups of 16 chunks follow one another with the
+// carry broadcast from the row's last (first) lane.  Block = (b, h, 8 rows
+// p0 .. p0+7, 64 columns nc0 .. nc0+63 of the 64 x N state), 512 threads
+// (two workgroups share a CU, so one's loads overlap the other's work):
+// wave w takes row p0 + w, its 16-lane row r the columns nc0 + 16r .. +15
+// (16 values per lane) and lane j of the row chunk 16 g + j of group g.  The
+// entering states of each group stay in registers for the backward sweep;
+// up to NG groups (16 NG chunks).
+template <int NG>
+__global__ __launch_bounds__(512) void bwd_state_scan_kernel(SSDBwdParams q) {
+  constexpr int NW = 8;  // waves: rows of the state
   const SSDParams& p = q.f;
-  __shared__ __attribute__((aligned(16))) uint16_t T[2][64][16 + 4];  // [n - nc0][p - p0]
-  __shared__ float red[2][NW];
-  const int nblk = (int)(p.N / 64), nq = 4 * nblk;
+  // The transposed tile of 16 chunks: T[j JS + (n - nc0) PT + (p - p0)] bf16.
+  // A lane writes one p of 16 n; with a 5-word row pitch and a chunk stride
+  // of 321 words, the 64 lanes of a write land on 32 distinct banks.
+  constexpr int PT = NW + 2, JS = 64 * PT + 2;
+  __shared__ __attribute__((aligned(16))) uint16_t T[16 * JS];
+  __shared__ float red[NW][16];  // [wave][chunk j]
+  const int nblk = (int)(p.N / 64), nq = q.aend_parts;  // 8 per 64-wide block of the states
   int64_t bid = blockIdx.x;
   const int qb = (int)(bid % nq);
   bid /= nq;
   const int64_t h = bid % p.H, b = bid / p.H;
-  const int tid = threadIdx.x, wv = tid / 64;
-  const int p0 = (qb / nblk) * 16, nc0 = 64 * (qb % nblk), pl = tid / 32, nl = 2 * (tid % 32);
+  const int tid = threadIdx.x, w = tid / 64, l = tid % 64, r = l / 16, j = l % 16;
+  const int p0 = (qb / nblk) * NW, nc0 = 64 * (qb % nblk);
   const int64_t E = kP * p.N;
-  const int e0 = (p0 + pl) * (int)p.N + nc0 + nl;
-  const int tn = tid / 8, tq = 2 * (tid % 8);  // transposed store: row n = nc0 + tn, p0 + tq, +1
-  const float* Ac = p.A_cum + (b * p.H + h) * p.Lp;
+  const int e0 = (p0 + w) * (int)p.N + nc0 + 16 * r;  // this lane's 16 elements
   const int64_t cs = p.H * E;
-  const int64_t base = (b * p.nchunks * p.H + h) * E;
-  const int nc = (int)p.nchunks, off = NCMAX - nc;  // slot k: chunk k - off
-  auto put_T = [&](int buf, float2 v) {
-    T[buf][nl][pl] = f2bf(v.x);
-    T[buf][nl + 1][pl] = f2bf(v.y);
+  const int64_t base = (b * p.nchunks * p.H + h) * E;  // chunk 0 of (b, h)
+  const int nc = (int)p.nchunks;
+  const float* Ac = p.A_cum + (b * p.H + h) * p.Lp;
+
+  auto ld16 = [&](const float* src, float (&v)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 t = *(const float4*)(src + 4 * i);
+      v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
   };
-  auto store_T = [&](int buf, uint16_t* dst) {
-    *(uint32_t*)(dst + (nc0 + tn) * kP + p0 + tq) = *(const uint32_t*)&T[buf][tn][tq];
+  // shift by k lanes within the row from below (UP) or above, with `id` where there is no source
+  auto shr = [](float v, float id, auto K) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id), __builtin_bit_cast(int, v),
+                                                                 0x110 + decltype(K)::value, 0xF, 0xF, false));
   };
-  float2 S = make_float2(0.f, 0.f);
-  if (p.h0) S = *(const float2*)(p.h0 + (b * p.H + h) * E + e0);
-  float2 Sh[NCMAX], ld[NCMAX];  // history; loads in flight
-  float ae[NCMAX];              // A_cum at the chunk ends
+  auto shl = [](float v, float id, auto K) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id), __builtin_bit_cast(int, v),
+                                                                 0x100 + decltype(K)::value, 0xF, 0xF, false));
+  };
+  // (a, v) <- (a, v) o (a', v') from k lanes below (forward) or above (backward): v = a v' + v, a = a a'
+  auto combine = [&](float& a, float (&v)[16], auto K, bool up) {
+    float a2 = up ? shr(a, 1.f, K) : shl(a, 1.f, K);
 #pragma unroll
-  for (int k = 0; k < PD; ++k) {
-    const int c = k - off;
-    if (c >= 0) {
-      ld[k] = *(const float2*)(p.states + base + c * cs + e0);
-      ae[k] = Ac[c * p.Q + p.Q - 1];
+    for (int i = 0; i < 16; ++i) {
+      const float v2 = up ? shr(v[i], 0.f, K) : shl(v[i], 0.f, K);
+      v[i] = __builtin_fmaf(a, v2, v[i]);
     }
-  }
-  int buf = 0;
+    a *= a2;
+  };
+  // the transposed bf16 tile of 16 chunks: T[j][n][p], stored as rows of 8 p (16 bytes)
+  auto put_T = [&](const float (&v)[16]) {
 #pragma unroll
-  for (int k = 0; k < NCMAX; ++k) {
-    const int c = k - off;
-    // slot k + PD (chunk c + PD < nchunks), also in the slots before the
-    // first chunk: that is how the first PD chunks' slots get theirs
-    if (k + PD < NCMAX && c + PD >= 0) {
-      ld[k + PD] = *(const float2*)(p.states + base + (c + PD) * cs + e0);
-      ae[k + PD] = Ac[(c + PD) * p.Q + p.Q - 1];
-    }
-    if (c >= 0) {
-      const float dec = __builtin_amdgcn_exp2f(ae[k] * kLog2e);
-      Sh[k] = S;
-      put_T(buf, S);
-      __syncthreads();
-      store_T(buf, q.SinT + base + c * cs);
-      buf ^= 1;
-      S.x = __builtin_fmaf(dec, S.x, ld[k].x);
-      S.y = __builtin_fmaf(dec, S.y, ld[k].y);
-    }
-  }
-  float2 G = make_float2(0.f, 0.f);
+    for (int i = 0; i < 16; ++i) T[j * JS + (16 * r + i) * PT + w] = f2bf(v[i]);
+  };
+  auto store_T = [&](uint16_t* dstT, int g) {
 #pragma unroll
-  for (int k = NCMAX - 1; k >= NCMAX - PD; --k)
-    if (k - off >= 0) ld[k] = *(const float2*)(q.dS + base + (k - off) * cs + e0);
-#pragma unroll
-  for (int k = NCMAX - 1; k >= 0; --k) {
-    const int c = k - off;
-    if (c >= 0) {
-      if (k - PD >= 0 && c - PD >= 0) ld[k - PD] = *(const float2*)(q.dS + base + (c - PD) * cs + e0);
-      const float dec = __builtin_amdgcn_exp2f(Ac[c * p.Q + p.Q - 1] * kLog2e);
-      *(uint32_t*)(q.dSl + base + c * cs + e0) = pack2(G.x, G.y);
-      put_T(buf, G);
-      float dot = Sh[k].x * G.x + Sh[k].y * G.y;
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
-      if (tid % 64 == 0) red[buf][wv] = dot;
-      __syncthreads();
-      store_T(buf, q.dSlT + base + c * cs);
-      if (tid == 0) {
-        float t = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) t += red[buf][w];
-        q.pAend[((b * p.H + h) * nc + c) * nq + qb] = dec * t;
+    for (int half = 0; half < 2; ++half) {
+      const int jj = tid / 64 + NW * half, n = tid % 64, c = 16 * g + jj;  // one 16-byte row per thread and half
+      if (c < nc) {
+        const uint32_t* src = (const uint32_t*)&T[jj * JS + n * PT];
+        *(uint4*)(dstT + base + c * cs + tile_T(nc0 + n, p0, p.N)) = make_uint4(src[0], src[1], src[2], src[3]);
       }
-      buf ^= 1;
-      G.x = __builtin_fmaf(dec, G.x, ld[k].x);
-      G.y = __builtin_fmaf(dec, G.y, ld[k].y);
     }
+  };
+
+  // chunk 16 g + j of group g (the last chunk where there is none: read, unused)
+  auto chunk_of = [&](int g) { return 16 * g + j < nc ? 16 * g + j : nc - 1; };
+  float S0[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) S0[i] = 0.f;
+  if (p.h0) ld16(p.h0 + (b * p.H + h) * E + e0, S0);
+  // the next group's inputs are in flight while a group is combined (and
+  // the last group's dS during the forward's last group)
+  float nxt[16];
+  ld16(p.states + base + chunk_of(0) * cs + e0, nxt);
+  float hist[NG][16], dg[NG];
+  const int ng = (nc + 15) / 16;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (g >= ng) break;
+    const int c = 16 * g + j;
+    const bool ok = c < nc;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = ok ? nxt[i] : 0.f;
+    if (g + 1 < ng) ld16(p.states + base + chunk_of(g + 1) * cs + e0, nxt);
+    else ld16(q.dS + base + chunk_of(g) * cs + e0, nxt);
+    const float d = ok ? __builtin_amdgcn_exp2f(Ac[chunk_of(g) * p.Q + p.Q - 1] * kLog2e) : 1.f;
+    dg[g] = d;
+    float a = d;
+    combine(a, v, std::integral_constant<int, 1>{}, true);
+    combine(a, v, std::integral_constant<int, 2>{}, true);
+    combine(a, v, std::integral_constant<int, 4>{}, true);
+    combine(a, v, std::integral_constant<int, 8>{}, true);
+    // S_in[c + 1] = a S0 + v; S_in[c] from the lane below (S0 in lane 0)
+    float sn[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sn[i] = __builtin_fmaf(a, S0[i], v[i]);
+      hist[g][i] = shr(sn[i], S0[i], std::integral_constant<int, 1>{});
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S0[i] = __shfl(sn[i], 16 * r + 15, 64);  // the next group's entering state
+    put_T(hist[g]);
+    __syncthreads();
+    store_T(q.SinT, g);
+    __syncthreads();
   }
-  if (q.dh0) *(float2*)(q.dh0 + (b * p.H + h) * E + e0) = G;
+
+  float Gc[16];  // G[16 (g + 1)]: the carry into the group from the right
+#pragma unroll
+  for (int i = 0; i < 16; ++i) Gc[i] = 0.f;
+#pragma unroll
+  for (int g = NG - 1; g >= 0; --g) {
+    if (g >= ng) continue;
+    const int c = 16 * g + j;
+    const bool ok = c < nc;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = ok ? nxt[i] : 0.f;
+    if (g > 0) ld16(q.dS + base + chunk_of(g - 1) * cs + e0, nxt);
+    const float d = dg[g];
+    float a = d;
+    combine(a, v, std::integral_constant<int, 1>{}, false);
+    combine(a, v, std::integral_constant<int, 2>{}, false);
+    combine(a, v, std::integral_constant<int, 4>{}, false);
+    combine(a, v, std::integral_constant<int, 8>{}, false);
+    // G[c] = a Gc + v; G[c + 1] from the lane above (Gc in lane 15)
+    float gcur[16], gn[16];
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      gcur[i] = __builtin_fmaf(a, Gc[i], v[i]);
+      gn[i] = shl(gcur[i], Gc[i], std::integral_constant<int, 1>{});
+      dot = __builtin_fmaf(hist[g][i], gn[i], dot);
+    }
+    // dS_loc[c] = G[c + 1], in both layouts
+    if (ok) {
+      uint4* dst = (uint4*)(q.dSl + base + c * cs + e0);
+      dst[0] = make_uint4(pack2(gn[0], gn[1]), pack2(gn[2], gn[3]), pack2(gn[4], gn[5]), pack2(gn[6], gn[7]));
+      dst[1] = make_uint4(pack2(gn[8], gn[9]), pack2(gn[10], gn[11]), pack2(gn[12], gn[13]), pack2(gn[14], gn[15]));
+    }
+    put_T(gn);
+    dot = sum_rows(dot);  // over the wave's four rows: chunk j's share of row p0 + w
+    if (r == 0) red[w][j] = dot;
+    __syncthreads();
+    store_T(q.dSlT, g);
+    if (tid < 16 && 16 * g + tid < nc) {
+      float t = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) t += red[ww][tid];
+      q.pAend[((b * p.H + h) * nc + 16 * g + tid) * nq + qb] = dg[g] * t;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Gc[i] = __shfl(gcur[i], 16 * r, 64);  // G[16 g], the carry further left
+    __syncthreads();
+  }
+  if (q.dh0 && j == 0) {
+    float* dst = q.dh0 + (b * p.H + h) * E + e0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(float4*)(dst + 4 * i) = make_float4(Gc[4 * i], Gc[4 * i + 1], Gc[4 * i + 2], Gc[4 * i + 3]);
+  }
 }
 
 // -------------------------------------------------------------- dC pass
@@ -431,7 +518,7 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
   auto load_head = [&](int64_t hh) {
     nx.load((const uint16_t*)p.x + b * p.xs_b + hh * p.xs_h, p.xs_t, t0, p.L);
     ny.load((const uint16_t*)q.dy + b * q.dys_b + hh * q.dys_h, q.dys_t, t0, p.L);
-    ns.load(q.SinT + ((b * p.nchunks + c) * p.H + hh) * E + nc0 * kP, kP, 0, 64);
+    ns.load(q.SinT + ((b * p.nchunks + c) * p.H + hh) * E + tile_T(nc0, 0, N), 8, 0, 64, N);
     if (tid < Q) {
       na = p.A_cum[(b * p.H + hh) * p.Lp + t0 + tid];
       nbe = p.beta[(b * p.H + hh) * p.Lp + t0 + tid];
@@ -623,7 +710,7 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
     stage_rows<Q, NTH>(Ys, (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h, q.dys_t, t0, p.L);
     stage_rows<Q, NTH>(Xs, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
     stage_rows<kP, NTH>(Sl, q.dSl + so, kN, 0, kP);
-    stage_rows<kN, NTH>(SlT, q.dSlT + so, kP, 0, kN);
+    stage_rows<kN, NTH>(SlT, q.dSlT + so, 8, 0, kN, kN);
     for (int t = tid; t < Q; t += NTH) {
       A2[t] = Ac[t] * kLog2e;
       bj[t] = be[t];
@@ -987,7 +1074,7 @@ __global__ __launch_bounds__(2 * Q) void bwd_db_kernel(SSDBwdParams q) {
     __syncthreads();
     stage_rows<Q, NTH>(Ys, (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h, q.dys_t, t0, p.L);
     stage_rows<Q, NTH>(Xs, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
-    stage_rows<64, NTH>(SlT, q.dSlT + so + nc0 * kP, kP, 0, 64);
+    stage_rows<64, NTH>(SlT, q.dSlT + so + tile_T(nc0, 0, p.N), 8, 0, 64, p.N);
     for (int t = tid; t < Q; t += NTH) {
       A2[t] = Ac[t] * kLog2e;
       bj[t] = be[t];
@@ -1118,7 +1205,7 @@ __global__ __launch_bounds__(Q) void bwd_finish_kernel(SSDBwdParams q) {
   const bool ok = tg < p.L;
   const int64_t o = (b * p.H + h) * p.Lp + tg;
   const float beta = p.beta[o], dbt = q.dbeta[o];
-  const int nblk = (int)(p.N / 64), nq = 4 * nblk;
+  const int nblk = (int)(p.N / 64), nq = q.aend_parts;
   float v = q.dAcB[o];
   for (int k = 0; k < nblk; ++k) v += q.dAcA[k * p.batch * p.H * p.Lp + o];
   const float tsum = block_sum<Q>(q.Tj[o], red);
@@ -1200,9 +1287,9 @@ hipError_t launch_ssd_bwd(const SSDBwdParams& q, float* dA, float* dB, float* dC
   f2.state_coef = 1;
   if ((e = launch_ssd_chunk_state(f2, stream)) != hipSuccess) return e;
   {
-    const dim3 grid((unsigned)(p.batch * p.H * 4 * (p.N / 64)));
-    if (p.nchunks <= 16) hipLaunchKernelGGL(bwd_state_reg_kernel<16>, grid, dim3(512), 0, stream, q);
-    else if (p.nchunks <= 32) hipLaunchKernelGGL(bwd_state_reg_kernel<32>, grid, dim3(512), 0, stream, q);
+    const dim3 grid((unsigned)(p.batch * p.H * q.aend_parts));  // one workgroup per partial sum
+    if (p.nchunks <= 16) hipLaunchKernelGGL(bwd_state_scan_kernel<1>, grid, dim3(512), 0, stream, q);
+    else if (p.nchunks <= 32) hipLaunchKernelGGL(bwd_state_scan_kernel<2>, grid, dim3(512), 0, stream, q);
     else hipLaunchKernelGGL(bwd_state_kernel, grid, dim3(256), 0, stream, q);
   }
   if (p.Q == 64) launch_q<64>(q, stream);

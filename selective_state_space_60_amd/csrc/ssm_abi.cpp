@@ -390,7 +390,7 @@ SSDBwdPlan plan_ssd_bwd(const ssm_ssd_bwd_desc& d) {
   const int64_t E = d.batch * nc * d.nheads * d.headdim * d.dstate;
   pl.ws_state = round256(E * 4);
   pl.ws_half = round256(E * 2);
-  pl.ws_aend = round256(d.batch * d.nheads * nc * (d.headdim * d.dstate / 1024) * 4);
+  pl.ws_aend = round256(d.batch * d.nheads * nc * ((64 / ssm::ssd_bwd_state_rows(nc)) * (d.dstate / 64)) * 4);
   pl.ws_step = round256(d.batch * d.nheads * pl.f.Lp * 4);
   pl.ws_acA = round256((d.dstate / 64) * d.batch * d.nheads * pl.f.Lp * 4);  // one per 64-wide block of the states
   pl.ws_part = round256(d.batch * nc * d.nheads * 4);
@@ -1093,6 +1093,7 @@ ssm_status ssm_ssd_bwd(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_ptrs* p, voi
   q.dh0 = (f & SSM_HAS_H0) ? p->dh0 : nullptr;
   q.HB = pl.HB;
   q.nhb = pl.nhb;
+  q.aend_parts = (64 / ssm::ssd_bwd_state_rows(q.f.nchunks)) * (int)(d->dstate / 64);
   const hipStream_t st = (hipStream_t)hip_stream;
   if (pl.own_fwd) {  // recompute the forward's A_cum, beta and chunk states
     hipError_t e = ssm::launch_ssd_chunk_cumsum(q.f, st);

@@ -192,10 +192,11 @@ struct SSDBwdParams {
   // workspace
   float* dS;       // (batch, nchunks, H, P, N): sum_i exp(A_cum_i) dy_i C_i^T
   float* S32;      // (batch, nchunks, H, P, N): state entering each chunk
-  uint16_t* SinT;  // (batch, nchunks, H, N, P) bf16, the same transposed
+  uint16_t* SinT;  // (batch, nchunks, H) tiles of N x P bf16, the same transposed: [p / 8][n][p % 8]
   uint16_t* dSl;   // (batch, nchunks, H, P, N) bf16: gradient of each chunk's own state
-  uint16_t* dSlT;  // (batch, nchunks, H, N, P) bf16, the same transposed
-  float* pAend;    // (batch, H, nchunks, P*N/1024): chunk-end decay gradient, partial sums
+  uint16_t* dSlT;  // (batch, nchunks, H) tiles of N x P bf16, the same transposed: [p / 8][n][p % 8]
+  float* pAend;    // (batch, H, nchunks, aend_parts): chunk-end decay gradient, partial sums
+  int aend_parts;  // partial sums per (batch, head, chunk): one per workgroup of the state pass
   float* dAcA;     // (batch, H, Lp): row sums of W = E o C B^T, + C_i . (inter-chunk dC_i)
   float* dAcB;     // (batch, H, Lp): -(column sums of W) - T_j
   float* dbeta;    // (batch, H, Lp)
@@ -234,6 +235,12 @@ inline int ssd_heads_per_block(int64_t hpg, int64_t base, int64_t slots) {
   }
   return (int)best;
 }
+
+// Rows of the 64 x N state per workgroup of the SSD backward's state pass:
+// 8 for the chunk-parallel kernel (up to 32 chunks), 16 for the one that
+// walks the chunks.  The pass writes (64 / rows) (N / 64) partial sums of the
+// chunk-end decay gradient per (batch, head, chunk).
+inline int ssd_bwd_state_rows(int64_t nchunks) { return nchunks <= 32 ? 8 : 16; }
 
 hipError_t launch_ssd_chunk_cumsum(const SSDParams& p, hipStream_t stream);
 hipError_t launch_ssd_chunk_state(const SSDParams& p, hipStream_t stream);
