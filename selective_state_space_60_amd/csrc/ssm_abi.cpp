@@ -361,7 +361,8 @@ constexpr uint32_t kSSDBwdFlags = SSM_HAS_D | SSM_DISC_EULER | SSM_HAS_H0 | SSM_
 struct SSDBwdPlan {
   SSDPlan f;
   int HB = 1, nhb = 1;
-  int64_t ws_state = 0, ws_half = 0, ws_aend = 0, ws_step = 0, ws_acA = 0, ws_part = 0, ws_pdb = 0, ws_total = 0;
+  int64_t ws_state = 0, ws_s32 = 0, ws_half = 0, ws_aend = 0, ws_step = 0, ws_acA = 0, ws_part = 0, ws_pdb = 0,
+          ws_total = 0;
   bool own_fwd = true;  // A_cum, beta and states are recomputed into the workspace
 };
 
@@ -389,6 +390,9 @@ SSDBwdPlan plan_ssd_bwd(const ssm_ssd_bwd_desc& d) {
   pl.nhb = (int)((hpg + pl.HB - 1) / pl.HB);
   const int64_t E = d.batch * nc * d.nheads * d.headdim * d.dstate;
   pl.ws_state = round256(E * 4);
+  // the entering states in fp32 for the state pass's backward sweep: kept in
+  // registers when the chunk-parallel kernel runs (up to 32 chunks)
+  pl.ws_s32 = nc <= 32 ? 0 : pl.ws_state;
   pl.ws_half = round256(E * 2);
   pl.ws_aend = round256(d.batch * d.nheads * nc * ((64 / ssm::ssd_bwd_state_rows(nc)) * (d.dstate / 64)) * 4);
   pl.ws_step = round256(d.batch * d.nheads * pl.f.Lp * 4);
@@ -398,7 +402,7 @@ SSDBwdPlan plan_ssd_bwd(const ssm_ssd_bwd_desc& d) {
   // A_cum, beta | states, dS, S32 | SinT, dSl, dSlT | pAend | dAcA | dAcB, dbeta, Tj, dDj | pA, pD | pdB, pdC;
   // with SSM_HAS_SSD_FWD the caller's A_cum, beta and states take the place of the first three
   pl.own_fwd = !(d.flags & SSM_HAS_SSD_FWD);
-  pl.ws_total = (pl.own_fwd ? pl.f.ws_acum + pl.f.ws_beta + pl.ws_state : 0) + 2 * pl.ws_state + 3 * pl.ws_half +
+  pl.ws_total = (pl.own_fwd ? pl.f.ws_acum + pl.f.ws_beta + pl.ws_state : 0) + pl.ws_state + pl.ws_s32 + 3 * pl.ws_half +
                 pl.ws_aend + pl.ws_acA + 4 * pl.ws_step + 2 * pl.ws_part + 2 * pl.ws_pdb;
   return pl;
 }
@@ -1069,7 +1073,7 @@ ssm_status ssm_ssd_bwd(const ssm_ssd_bwd_desc* d, const ssm_ssd_bwd_ptrs* p, voi
     q.f.states = const_cast<float*>(p->states);
   }
   q.dS = (float*)take(pl.ws_state);
-  q.S32 = (float*)take(pl.ws_state);
+  q.S32 = pl.ws_s32 ? (float*)take(pl.ws_s32) : nullptr;
   q.SinT = (uint16_t*)take(pl.ws_half);
   q.dSl = (uint16_t*)take(pl.ws_half);
   q.dSlT = (uint16_t*)take(pl.ws_half);

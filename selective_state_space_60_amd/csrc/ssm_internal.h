@@ -191,7 +191,7 @@ struct SSDBwdParams {
   float* dh0;      // (batch, H, P, N) or null
   // workspace
   float* dS;       // (batch, nchunks, H, P, N): sum_i exp(A_cum_i) dy_i C_i^T
-  float* S32;      // (batch, nchunks, H, P, N): state entering each chunk
+  float* S32;      // (batch, nchunks, H, P, N): state entering each chunk (more than 32 chunks; else null)
   uint16_t* SinT;  // (batch, nchunks, H) tiles of N x P bf16, the same transposed: [p / 8][n][p % 8]
   uint16_t* dSl;   // (batch, nchunks, H, P, N) bf16: gradient of each chunk's own state
   uint16_t* dSlT;  // (batch, nchunks, H) tiles of N x P bf16, the same transposed: [p / 8][n][p % 8]
