@@ -274,7 +274,9 @@ typedef struct {
  * (headdim 64, dstate in {64, 128, 256}, chunk in {64, 128, 256} except
  * dstate 256 with chunk 256, nheads % ngroups == 0).  Every (batch,
  * step, head or group) row of x, dy, B, C and dx, and h0 / dh0, must start
- * 16-byte aligned (SSM_ERR_ALIGN otherwise).  The sums over heads (dB, dC)
+ * 16-byte aligned (SSM_ERR_ALIGN otherwise), and chunk x the step stride of
+ * x and of dy must stay below 2^30 elements (SSM_ERR_UNSUPPORTED otherwise).
+ * The sums over heads (dB, dC)
  * and over batch and time (dA, dD) are fixed-order sums of per-workgroup
  * partial sums, so the results are deterministic.  Outputs may not overlap
  * inputs or each other.  Workspace: ssm_ssd_bwd_workspace_size bytes

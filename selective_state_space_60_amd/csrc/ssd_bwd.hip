@@ -654,11 +654,62 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
 
 // -------------------------------------------------------------- dx pass
 
+// Tiles of 128-byte rows (64 bf16) with no padding: the 16-byte piece c of row
+// r sits in slot c ^ swz(r) of the row, so that the row reads, transposed reads
+// and 8-byte reads below each touch every bank evenly.  Such tiles are filled
+// by direct global-to-LDS loads (global_load_lds_dwordx4: one wave instruction
+// writes 1 KB, lane i the 16 bytes at i * 16), which need no registers: the
+// next head's rows can be in flight while the current head is computed.
+typedef __attribute__((address_space(3))) void lds_void;
+// (a function of r % 16 only, so rows 16 apart are swizzled alike)
+__device__ __forceinline__ int swz(int r) { return (r & 6) | ((r >> 3) & 1); }
+// byte offset of bf16 column col (a multiple of 4) of row r
+__device__ __forceinline__ int sw_off(int r, int col) { return r * 128 + 16 * ((col >> 3) ^ swz(r)) + 2 * (col & 7); }
+
+// Direct loads of 8 rows of a swizzled tile: lane i fills slot i % 8 of row
+// r = r0 + i / 8, i.e. the piece c = (i % 8) ^ swz(r) of its source row.
+// dma_off is the lane's byte offset from the source's first row t_base (its
+// row t clamped to L - 1; rows at or past L are zeroed separately), with 8
+// columns from 8c at + 8c cm elements; it is the same for every head, so it
+// is formed once (32-bit: the ABI checks the strides).
+__device__ __forceinline__ uint32_t dma_off(int r, int64_t t, int64_t t_base, int64_t L, int64_t st, int64_t cm = 1) {
+  const int lane = threadIdx.x % 64;
+  const int c = (lane % 8) ^ swz(r);
+  const int64_t tc = t < L ? t : L - 1;
+  return (uint32_t)(tc - t_base) * (uint32_t)st * 2u + (uint32_t)c * (uint32_t)cm * 16u;
+}
+__device__ __forceinline__ void dma_rows8(uint8_t* tile, int r0, const void* base, uint32_t off) {
+  __builtin_amdgcn_global_load_lds((const void*)((const uint8_t*)base + off), (lds_void*)(tile + r0 * 128), 16, 0, 0);
+}
+
+// Reads of a swizzled tile of SZ bytes (a power of two).  The offset is
+// masked to the tile, which costs nothing in range but lets the compiler see
+// that the read stays inside the tile, so it does not wait for direct loads
+// into other tiles that are still in flight.
+template <int SZ>
+__device__ __forceinline__ const uint8_t* sw_at(const uint8_t* tile, int r, int col) {
+  static_assert((SZ & (SZ - 1)) == 0, "power-of-two tile");
+  return tile + ((uint32_t)sw_off(r, col) & (uint32_t)(SZ - 1));
+}
+// A operand as tr_operand, from a swizzled tile
+template <int SZ>
+__device__ __forceinline__ bf16x8 tr_operand_sw(const uint8_t* tile, int s0, int c0, int tr_row, int tr_col) {
+  const int r = s0 + tr_row, c = c0 + tr_col;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)sw_at<SZ>(tile, r, c));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)sw_at<SZ>(tile, r + 16, c));
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  return as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+}
+template <int SZ>
+__device__ __forceinline__ uint4 ld16_sw(const uint8_t* tile, int r, int col) { return *(const uint4*)sw_at<SZ>(tile, r, col); }
+template <int SZ>
+__device__ __forceinline__ uint2 ld8_sw(const uint8_t* tile, int r, int col) { return *(const uint2*)sw_at<SZ>(tile, r, col); }
+
 // Block as bwd_dc_kernel; strips are now 16 columns j, and a wave works
 // through its two strips one after the other (one strip's accumulators live
 // at a time).  Accumulators: RX^T[p][j] (-> R_j) and DB^T[n][j] (-> dB_j),
 // lane -> p or n = 16*t + 4*(l/16) + r, j = 16*strip + l%16.  Per head:
-//   RX^T = w_j dS_loc B_j, DB^T = w_j beta_j dS_loc^T x_j   (A: dS_loc rows / dS_loc^T rows)
+//   RX^T = w_j dS_loc B_j, DB^T = w_j beta_j dS_loc^T x_j   (A: dS_loc rows / transposed reads of them)
 //   for 32-row blocks of i >= j:  CB[i][j], G'[i][j] = dy_i . x_j  (A: staged C / dy rows)
 //     M = CB decay_ij, E = G' decay_ij beta_j -> B operands
 //     RX^T += dy^T M,  DB^T += C^T E   (A: transposed dy / C rows)
@@ -666,25 +717,114 @@ __global__ __launch_bounds__(2 * Q) void bwd_dc_kernel(SSDBwdParams q) {
 // A_cum_i0) from a per-head table and v_j = exp(A_cum_i0 - A_cum_j), i0 the
 // block's first row (both factors <= 1: j < i0 <= i); the diagonal block
 // takes exp(A_cum_i - A_cum_j) itself (there the factors could overflow).
+// Staging: C once per workgroup.  The next head's dy and dS_loc go by direct
+// loads into the other half of double-buffered tiles, and its A_cum and beta
+// into registers, when a head starts; its tables are formed into the other
+// half when the head ends.  The x rows of a strip are read only by the wave
+// that owns it, which loads the next head's as soon as it holds the current
+// ones in registers.  So a head needs one barrier, whose fence waits for the
+// direct loads.  Heads alternate between the two halves in code (not by an
+// index): the compiler then sees that the loads in flight never alias the
+// tiles being read.
 template <int Q>
 __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
-  constexpr int NTH = 2 * Q, NSTRIP = Q / 16, NIB = Q / 32;
+  constexpr int NTH = 2 * Q, NW = NTH / 64, NSTRIP = Q / 16, NIB = Q / 32;
+  constexpr int YSZ = Q * 128, XSZ = Q * 64, SSZ = kP * 128;  // tile bytes
+  constexpr int YR = Q / NW;  // dy rows each wave loads
+  static_assert(kP == 64 && kN == 64, "128-byte tile rows");
   const SSDParams& p = q.f;
-  __shared__ __attribute__((aligned(16))) uint16_t Cs[Q][kPR];   // C rows of the group: [i][n]
-  __shared__ __attribute__((aligned(16))) uint16_t Ys[Q][kPR];   // dy rows of the head: [i][p]
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][kPR];   // x rows of the head: [j][p]
-  __shared__ __attribute__((aligned(16))) uint16_t Sl[kP][kPR];  // dS_loc of the head: [p][n]
-  __shared__ __attribute__((aligned(16))) uint16_t SlT[kN][kPR]; // dS_loc^T: [n][p]
-  __shared__ __attribute__((aligned(16))) float A2[Q];
-  __shared__ __attribute__((aligned(16))) float bj[Q];
-  __shared__ __attribute__((aligned(16))) float U[Q];            // exp(A_cum_i - A_cum_(i & ~31))
+  // (the largest alignment puts C at the start of LDS, where its reads take immediate offsets)
+  __shared__ __attribute__((aligned(2048))) uint16_t Cs[Q][kPR];   // C rows of the group: [i][n]
+  __shared__ __attribute__((aligned(1024))) uint8_t Ys0[YSZ];       // dy rows of a head: [i][p], swizzled
+  __shared__ __attribute__((aligned(1024))) uint8_t Ys1[YSZ];
+  __shared__ __attribute__((aligned(1024))) uint8_t XsA[XSZ];       // x rows of the first strips (wave w: strip w)
+  __shared__ __attribute__((aligned(1024))) uint8_t XsB[XSZ];       // and of the second (wave w: strip NSTRIP-1-w)
+  __shared__ __attribute__((aligned(1024))) uint8_t Sl0[SSZ];       // dS_loc of a head: [p][n], swizzled
+  __shared__ __attribute__((aligned(1024))) uint8_t Sl1[SSZ];
+  // per-head tables, two halves: A_cum * log2(e), beta, exp(A_cum_i - A_cum_(i & ~31))
+  __shared__ __attribute__((aligned(2048))) float Tb[2][3][Q];
   const HeadBlock hb = head_block(q);
   const int64_t b = hb.b, c = hb.c, g = hb.g;
   const int tid = threadIdx.x;
   const int64_t t0 = c * Q;
   const int wv = __builtin_amdgcn_readfirstlane(tid / 64), l = tid % 64, lr = l % 16, lq = l / 16;
   const int kst[2] = {wv, NSTRIP - 1 - wv};
-  const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
+  const int nvalid = (int)(p.L - t0 < Q ? p.L - t0 : Q);  // rows of the chunk inside the sequence
+
+  // direct loads of head h's dy and dS_loc into half BF, and of x rows:
+  // the lanes' offsets, formed once
+  uint32_t yoff[YR / 8], soff[8 / NW], xoff[2][2];
+#pragma unroll
+  for (int u = 0; u < YR / 8; ++u) {
+    const int r = YR * wv + 8 * u + l / 8;
+    yoff[u] = dma_off(r, t0 + r, t0, p.L, q.dys_t);
+  }
+#pragma unroll
+  for (int u = 0; u < 8 / NW; ++u) {
+    const int r = 8 * ((8 / NW) * wv + u) + l / 8;
+    soff[u] = dma_off(r, r, 0, kP, kN);
+  }
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) xoff[st][v] = dma_off(16 * wv + 8 * v + l / 8, t0 + 16 * kst[st] + 8 * v + l / 8, t0, p.L, p.xs_t);
+  auto load_rows = [&](int64_t h, auto BFc) {
+    constexpr int BF = decltype(BFc)::value;
+    uint8_t* ys = BF ? Ys1 : Ys0;
+    uint8_t* sl = BF ? Sl1 : Sl0;
+    const uint16_t* dy = (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h + t0 * q.dys_t;
+#pragma unroll
+    for (int u = 0; u < YR / 8; ++u) dma_rows8(ys, YR * wv + 8 * u, dy, yoff[u]);
+    const uint16_t* dsl = q.dSl + ((b * p.nchunks + c) * p.H + h) * (kP * kN);
+#pragma unroll
+    for (int u = 0; u < 8 / NW; ++u) dma_rows8(sl, 8 * ((8 / NW) * wv + u), dsl, soff[u]);
+  };
+  // the x rows of this wave's strip S of head h
+  auto load_x = [&](int64_t h, auto Sc) {
+    constexpr int S = decltype(Sc)::value;
+    const uint16_t* x = (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h + t0 * p.xs_t;
+    uint8_t* xs = S ? XsB : XsA;
+    dma_rows8(xs, 16 * wv, x, xoff[S][0]);
+    dma_rows8(xs, 16 * wv + 8, x, xoff[S][1]);
+  };
+  // A_cum_t, A_cum_(t & ~31) and beta_t of head h (thread t < Q), and D_h
+  float na = 0.f, na0 = 0.f, nbe = 0.f, nD = 0.f;
+  auto load_ab = [&](int64_t h) {
+    nD = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
+    if (tid < Q) {
+      const int64_t o = (b * p.H + h) * p.Lp + t0;
+      na = p.A_cum[o + tid];
+      na0 = p.A_cum[o + (tid & ~31)];
+      nbe = p.beta[o + tid];
+    }
+  };
+  auto put_tables = [&](auto BFc) {
+    constexpr int BF = decltype(BFc)::value;
+    if (tid < Q) {
+      const float a = na * kLog2e;
+      Tb[BF][0][tid] = a;
+      Tb[BF][1][tid] = nbe;
+      Tb[BF][2][tid] = __builtin_amdgcn_exp2f(a - na0 * kLog2e);
+    }
+  };
+  // In a chunk past the sequence's end the dy and x rows there are zero:
+  // each wave clears the ones it loaded, once they have landed.
+  auto clear_tail = [&](auto BFc) {
+    constexpr int BF = decltype(BFc)::value;
+    if (nvalid < Q) {
+      __builtin_amdgcn_s_waitcnt(0);
+      uint8_t* ys = BF ? Ys1 : Ys0;
+      for (int e = l; e < YR * 8; e += 64) {
+        const int r = YR * wv + e / 8;
+        if (r >= nvalid) *(uint4*)(ys + r * 128 + 16 * (e % 8)) = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        for (int e = l; e < 16 * 8; e += 64)
+          if (16 * kst[st] + e / 8 >= nvalid)
+            *(uint4*)((st ? XsB : XsA) + (16 * wv + e / 8) * 128 + 16 * (e % 8)) = make_uint4(0, 0, 0, 0);
+    }
+  };
 
   stage_rows<Q, NTH>(Cs, (const uint16_t*)p.C + b * p.Cs_b + g * p.Cs_g, p.Cs_t, t0, p.L);
   const uint16_t* Bsrc = (const uint16_t*)p.B + b * p.Bs_b + g * p.Bs_g;
@@ -698,38 +838,56 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) sumB[s][nt] = zero4();
+  load_rows(hb.h_lo, std::integral_constant<int, 0>{});
+  load_x(hb.h_lo, std::integral_constant<int, 0>{});
+  load_x(hb.h_lo, std::integral_constant<int, 1>{});
+  load_ab(hb.h_lo);
+  put_tables(std::integral_constant<int, 0>{});
+  clear_tail(std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);  // the first head's loads (nothing else is in flight yet)
 
-  for (int k = 0; k < hb.nh; ++k) {
+  auto head = [&](int k, auto BFc) {
+    constexpr int BF = decltype(BFc)::value;
     const int64_t h = hb.h_lo + k;
-    const float* Ac = p.A_cum + (b * p.H + h) * p.Lp + t0;
-    const float* be = p.beta + (b * p.H + h) * p.Lp + t0;
-    const int64_t so = ((b * p.nchunks + c) * p.H + h) * (kP * kN);
-    const float Dk = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
-    __syncthreads();  // the previous head is done with the staged rows and tables
-    // every global read of this head, issued together
-    stage_rows<Q, NTH>(Ys, (const uint16_t*)q.dy + b * q.dys_b + h * q.dys_h, q.dys_t, t0, p.L);
-    stage_rows<Q, NTH>(Xs, (const uint16_t*)p.x + b * p.xs_b + h * p.xs_h, p.xs_t, t0, p.L);
-    stage_rows<kP, NTH>(Sl, q.dSl + so, kN, 0, kP);
-    stage_rows<kN, NTH>(SlT, q.dSlT + so, 8, 0, kN, kN);
-    for (int t = tid; t < Q; t += NTH) {
-      A2[t] = Ac[t] * kLog2e;
-      bj[t] = be[t];
+    const uint8_t* Ys = BF ? Ys1 : Ys0;
+    const uint8_t* Sl = BF ? Sl1 : Sl0;
+    const float* A2 = Tb[BF][0];
+    const float* bj = Tb[BF][1];
+    const float* U = Tb[BF][2];
+    const bool more = k + 1 < hb.nh;
+    const float Dk = nD;
+    // this head's rows and tables are in place (the fence waits for the
+    // direct loads), and the previous head is done with the other half
+    __syncthreads();
+    if (more) {
+      load_rows(h + 1, std::integral_constant<int, 1 - BF>{});
+      load_ab(h + 1);
     }
-    __syncthreads();
-    for (int t = tid; t < Q; t += NTH) U[t] = __builtin_amdgcn_exp2f(A2[t] - A2[t & ~31]);
-    __syncthreads();
 
     auto strip = [&](auto S) {
       constexpr int s = decltype(S)::value;
+      // the lane's indices, opaque to the compiler, so that the addresses made
+      // from them are formed per strip rather than held over every head
+      int lane = l;
+      asm volatile("" : "+v"(lane));
+      const int lr = lane % 16, lq = lane / 16;
+      const int tr_row = 4 * lq + lr / 4, tr_col = 4 * (lr % 4);
+      const uint8_t* Xs = s ? XsB : XsA;
+      const int xr = 16 * wv + lr;  // the lane's row in Xs
       const int jl = 16 * kst[s] + lr;
       const int64_t tj = t0 + jl;
       const int diag = (16 * kst[s]) / 32;
       bf16x8 xop[2];  // B operands: x[j][32*ks + 8*lq .. +7]
-      uint2 xE[4];    // x[j][16*pt + 4*lq .. +3] for the epilogue
+      uint2 xE[4];    // x[j][16*pt + 4*lq .. +3]
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) xop[ks] = as_bf16x8(*(const uint4*)&Xs[jl][32 * ks + 8 * lq]);
+      for (int ks = 0; ks < 2; ++ks) xop[ks] = as_bf16x8(ld16_sw<XSZ>(Xs, xr, 32 * ks + 8 * lq));
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) xE[pt] = *(const uint2*)&Xs[jl][16 * pt + 4 * lq];
+      for (int pt = 0; pt < 4; ++pt) xE[pt] = ld8_sw<XSZ>(Xs, xr, 16 * pt + 4 * lq);
+      if (more) {
+        // the rows are in registers: the next head's may land
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        load_x(h + 1, S);
+      }
       const float aj = A2[jl], bjj = bj[jl];
 
       // chunk-state terms
@@ -744,10 +902,13 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
           f32x4 a = zero4(), d = zero4();
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 dsl = as_bf16x8(*(const uint4*)&Sl[16 * t + lr][32 * ks + 8 * lq]);
-            const bf16x8 dslT = as_bf16x8(*(const uint4*)&SlT[16 * t + lr][32 * ks + 8 * lq]);
-            a = mfma(dsl, bop[s][ks], a);  // (dS_loc B_j)[p]
-            d = mfma(dslT, xop[ks], d);    // (dS_loc^T x_j)[n]
+            // (dS_loc^T x_j): the transposed read takes p in the order
+            // 32ks + 4lq + 0..3, 32ks + 16 + 4lq + 0..3, so x goes in that order
+            const uint2 x0 = xE[2 * ks], x1 = xE[2 * ks + 1];
+            const bf16x8 dsl = as_bf16x8(ld16_sw<SSZ>(Sl, 16 * t + lr, 32 * ks + 8 * lq));
+            const bf16x8 dslT = tr_operand_sw<SSZ>(Sl, 32 * ks, 16 * t, tr_row, tr_col);
+            a = mfma(dsl, bop[s][ks], a);                                    // (dS_loc B_j)[p]
+            d = mfma(dslT, as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), d);  // (dS_loc^T x_j)[n]
           }
           float xv[4];
           unpack4(xE[t], xv);
@@ -759,10 +920,19 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
         tj_val = sum_rows(tp) * wb;
       }
 
-      // intra-chunk terms over the blocks of i at or after the strip
+      // intra-chunk terms over the blocks of i at or after the strip.  The
+      // swizzle depends on the row mod 16 only, so a dy read at row i0 + r
+      // (r < 16) is at (i0 * 128) | (the lane's offset for row r), the second
+      // 16 rows 2048 bytes on (offsets below 2048, in range of the tile).
+      uint32_t yrow[2], ytr[4];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) yrow[ks] = (uint32_t)sw_off(lr, 32 * ks + 8 * lq) & 2047u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ytr[t] = (uint32_t)sw_off(tr_row, 16 * t + tr_col) & 2047u;
       float csum = 0.f;  // this lane's part of W's column sum
       for (int ib = diag; ib < NIB; ++ib) {
         const int i0 = 32 * ib;
+        const uint32_t yb = ((uint32_t)i0 * 128u) & (uint32_t)(YSZ - 1);
         f32x4 ct[2], gt[2];
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
@@ -770,7 +940,7 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             a = mfma(as_bf16x8(*(const uint4*)&Cs[i0 + 16 * it + lr][32 * ks + 8 * lq]), bop[s][ks], a);
-            d = mfma(as_bf16x8(*(const uint4*)&Ys[i0 + 16 * it + lr][32 * ks + 8 * lq]), xop[ks], d);
+            d = mfma(as_bf16x8(*(const uint4*)(Ys + (yb | yrow[ks]) + 2048 * it)), xop[ks], d);
           }
           ct[it] = a;  // CB[i0 + 16*it + 4*lq + r][j]
           gt[it] = d;  // G'[i0 + 16*it + 4*lq + r][j]
@@ -811,8 +981,23 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
                                                 pack2(e[6], e[7])));
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          accX[t] = mfma(tr_operand(Ys, i0, 16 * t, tr_row, tr_col), mop, accX[t]);
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Ys + (yb | ytr[t])));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Ys + (yb | ytr[t]) + 2048));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          accX[t] = mfma(as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y)), mop, accX[t]);
           accB[t] = mfma(tr_operand(Cs, i0, 16 * t, tr_row, tr_col), eop, accB[t]);
+        }
+      }
+
+      if (s == 1) {
+        // Every load of this head has long landed: waiting for them here,
+        // before the last stores, leaves the barrier that ends the head only
+        // those stores in flight (which it does not wait for).  Then the
+        // next head's tables.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        if (more) {
+          put_tables(std::integral_constant<int, 1 - BF>{});
+          clear_tail(std::integral_constant<int, 1 - BF>{});
         }
       }
 
@@ -822,7 +1007,7 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
       for (int pt = 0; pt < 4; ++pt) {
         float xv[4], yv[4], o[4];
         unpack4(xE[pt], xv);
-        unpack4(*(const uint2*)&Ys[jl][16 * pt + 4 * lq], yv);
+        unpack4(ld8_sw<YSZ>(Ys, jl, 16 * pt + 4 * lq), yv);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           db = __builtin_fmaf(xv[r], accX[pt][r], db);
@@ -851,6 +1036,10 @@ __global__ __launch_bounds__(2 * Q) void bwd_dx_kernel(SSDBwdParams q) {
     strip(std::integral_constant<int, 0>{});
     __builtin_amdgcn_sched_barrier(0);
     strip(std::integral_constant<int, 1>{});
+  };
+  for (int k = 0; k < hb.nh; k += 2) {
+    head(k, std::integral_constant<int, 0>{});
+    if (k + 1 < hb.nh) head(k + 1, std::integral_constant<int, 1>{});
   }
   // the head block's dB terms
   float* dst = q.pdB + ((int64_t)hb.hbk * p.batch + b) * p.L * p.G * kN;

@@ -432,6 +432,10 @@ ssm_status validate_ssd_bwd_desc(const ssm_ssd_bwd_desc* d) {
   if (d->batch * pl.f.nchunks * d->ngroups * pl.nhb >= ((int64_t)1 << 31) ||
       d->batch * d->nheads * pl.f.nchunks * 4 >= ((int64_t)1 << 31))
     return SSM_ERR_UNSUPPORTED;
+  // The dx pass loads a chunk's rows of x and dy with 32-bit byte offsets
+  // from the chunk's first row.
+  if (d->chunk * d->x.stride[1] * 2 >= ((int64_t)1 << 31) || d->chunk * d->dy.stride[1] * 2 >= ((int64_t)1 << 31))
+    return SSM_ERR_UNSUPPORTED;
   return SSM_OK;
 }
 

@@ -301,11 +301,18 @@ def _ssd_bwd(batch=1, L=100, H=4, P=64, N=64, G=1, Q=64, flags=0, **over):
     (lambda d, p: setattr(p, "dC", p.dB), ssm.SSM_ERR_ALIAS),
     (lambda d, p: setattr(p, "dh0", p.dh0 + 4), ssm.SSM_ERR_ALIGN),
     (lambda d, p: setattr(p, "dx", p.dx + 2), ssm.SSM_ERR_ALIGN),
+    # chunk rows of x and dy are addressed with 32-bit byte offsets
+    (lambda d, p: (d.x.stride.__setitem__(1, 1 << 24), d.x.stride.__setitem__(0, 1 << 32)), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: (d.dy.stride.__setitem__(1, 1 << 24), d.dy.stride.__setitem__(0, 1 << 32)), ssm.SSM_ERR_UNSUPPORTED),
+    (lambda d, p: (d.dy.stride.__setitem__(1, 1 << 20), d.dy.stride.__setitem__(0, 1 << 28)), ssm.SSM_OK),
 ])
 def test_ssd_bwd_validation(mutate, status):
     d, p = _ssd_bwd(flags=ssm.SSM_HAS_D | ssm.SSM_HAS_H0)
     mutate(d, p)
-    assert ssm.lib().ssm_ssd_bwd(ctypes.byref(d), ctypes.byref(p), 16 << 36, 1 << 40, None) == status
+    n = 1 << 40
+    if status == ssm.SSM_OK:   # valid: stop before any launch with a too-small workspace
+        status, n = ssm.SSM_ERR_WORKSPACE, 256
+    assert ssm.lib().ssm_ssd_bwd(ctypes.byref(d), ctypes.byref(p), 16 << 36, n, None) == status
 
 
 # batch 1, L 100, 4 heads, chunk 64: A_cum, beta (1, 4, 128) fp32; states (1, 2, 4, 64, 64) fp32
