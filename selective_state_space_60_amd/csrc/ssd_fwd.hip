@@ -378,15 +378,6 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
   constexpr int PRB = N + 4;        // row pitch (bf16) of the staged B rows
   constexpr int NTX = Q * 8 / NTH;  // (row, 8 values) pieces of x per thread
   constexpr int NTB = NTX * NB;     // pieces of B per thread
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[Q][PR];   // x rows: [j][p]
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[Q][PRB];  // B rows: [j][n]
-  __shared__ float A2[Q];                                     // A_cum * log2(e)
-  __shared__ float tb[Q];                                     // exp(A_cum[j|31] - A_cum[j]) * beta_j
-  __shared__ float bj[Q];                                     // beta
-  // S_in (64 x N bf16), row p in N/8 chunks of 8 values; chunk q of row p is
-  // stored at chunk q ^ (p % 8) so the inter-chunk reads (16 rows, one chunk)
-  // spread over the banks.
-  __shared__ __attribute__((aligned(16))) uint4 Ss[64][8 * NB];
   // C B^T is the group's, the same for every head, yet the head loop would
   // form it per head and block (for N states, 2N/32 of the block's
   // matrix-core products and 2N/32 KB of B operand reads per wave).  So each
@@ -405,8 +396,32 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
                                      1024 * NPAIR) <= 160 * 1024;
   constexpr bool GALIAS = !GSEP && Q <= 128 && 1024 * NPAIR <= sizeof(uint16_t) * Q * PRB;
   constexpr bool GPRE = GSEP || GALIAS;
-  __shared__ __attribute__((aligned(16))) uint4 Gsep[GSEP ? NPAIR * 64 : 1];
-  __shared__ float wmaxB[NTH / 64];  // max |B| of each wave's staged pieces
+  // One LDS object, so the member order is the address order: the arrays the
+  // block loop reads at run-time row offsets (x rows, the decay columns) come
+  // first, below 64 KB, where a read's 16-bit immediate offset reaches every
+  // constant part of its address and no per-read address add is needed.
+  struct alignas(16) Smem {
+    alignas(16) uint16_t Xs[Q][PR];  // x rows: [j][p]
+    float A2[Q];                     // A_cum * log2(e)
+    float tb[Q];                     // exp(A_cum[j|31] - A_cum[j]) * beta_j
+    float bj[Q];                     // beta
+    // S_in (64 x N bf16), row p in N/8 chunks of 8 values; chunk q of row p
+    // is stored at chunk q ^ (p % 8) so the inter-chunk reads (16 rows, one
+    // chunk) spread over the banks.
+    uint4 Ss[64][8 * NB];
+    alignas(16) uint16_t Bs[Q][PRB];  // B rows: [j][n]
+    float wmaxB[NTH / 64];            // max |B| of each wave's staged pieces
+    uint4 Gsep[GSEP ? NPAIR * 64 : 1];
+  };
+  __shared__ Smem sm;
+  auto& Xs = sm.Xs;
+  auto& Bs = sm.Bs;
+  auto& A2 = sm.A2;
+  auto& tb = sm.tb;
+  auto& bj = sm.bj;
+  auto& Ss = sm.Ss;
+  auto& Gsep = sm.Gsep;
+  auto& wmaxB = sm.wmaxB;
 
   int64_t bid = blockIdx.x;
   const int hbk = (int)(bid % nhb);
@@ -430,8 +445,11 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
   constexpr bool kSomeIdle = NS * NTH != 512 * NB;      // more threads than S_in pieces
   const bool s_ok = !kSomeIdle || tid < 512 * NB;       // this thread holds S_in pieces
   uint4 rx[NTX], rs[NS];
-  float ra = 0.f, ra31 = 0.f, rbt = 0.f;
+  float ra = 0.f, ra31 = 0.f, rbt = 0.f, rD = 0.f;
   auto load_head = [&](int64_t hh) {
+    // D of the head with its other loads: a load of its own in the epilogue
+    // would wait for every load and store then in flight
+    rD = p.Dskip ? p.Dskip[hh * p.Ds_h] : 0.f;
     const uint16_t* Xsrc = (const uint16_t*)p.x + b * p.xs_b + hh * p.xs_h;
 #pragma unroll
     for (int u = 0; u < NTX; ++u) {
@@ -540,6 +558,7 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
 
   for (int k = 0; k < nh; ++k) {
     const int64_t h = h_lo + k;
+    const float hD = rD;  // head h's D (rD is refilled with the next head's below)
     // stage head h from the registers (the previous head's readers are done)
     if (tid < Q) {
       A2[tid] = ra * kLog2e;
@@ -638,7 +657,7 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
       }
     }
     // epilogue: + D x (x from the staged rows), store y[i][p0..p0+3]
-    const float Dh = p.Dskip ? p.Dskip[h * p.Ds_h] : 0.f;
+    const float Dh = hD;
     if (ti < p.L) {
   #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
