@@ -68,7 +68,7 @@ def test_tiny_f32():
 
 
 def _check_full(spec, seed):
-    """The spec bar (inside _check), then the regression bars: the whole
+    """The bf16 accuracy bar (inside _check), then the regression bars: the whole
     output and every (batch, 256-step, 256-channel) tile."""
     y = _check(spec, seed)
     inp = synth.scan_inputs(spec, seed)
