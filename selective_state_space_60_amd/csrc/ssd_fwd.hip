@@ -656,9 +656,35 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
         for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(aX[mt], bop, acc[mt]);
       }
     }
-    // epilogue: + D x (x from the staged rows), store y[i][p0..p0+3]
+    // epilogue: + D x (x from the staged rows), and the store of y's rows
     const float Dh = hD;
-    if (ti < p.L) {
+    if (!p.y_f32) {
+      // bf16 y: lane row lq holds p = 16 mt + 4 lq .. +3 of row i for every
+      // mt; a lane swap between rows 2k and 2k+1 (v_permlane16_swap) of the
+      // packed values of blocks (0, 1) and (2, 3) gives each lane 8
+      // consecutive values, p = 32 u + 16 (lq & 1) + 8 (lq >> 1) .. +7, so
+      // each of its two stores writes 16 bytes and a wave's store covers 64
+      // contiguous bytes of each of its 16 rows (four 8-byte stores per lane,
+      // 32-byte runs, had left the L2 to merge four pieces of every line).
+      uint32_t w[4][2];
+  #pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint2 xv = *(const uint2*)&Xs[i][16 * mt + 4 * lq];
+        const float o0 = __builtin_fmaf(Dh, __uint_as_float(xv.x << 16), acc[mt][0]);
+        const float o1 = __builtin_fmaf(Dh, __uint_as_float(xv.x & 0xFFFF0000u), acc[mt][1]);
+        const float o2 = __builtin_fmaf(Dh, __uint_as_float(xv.y << 16), acc[mt][2]);
+        const float o3 = __builtin_fmaf(Dh, __uint_as_float(xv.y & 0xFFFF0000u), acc[mt][3]);
+        w[mt][0] = pack2(o0, o1);
+        w[mt][1] = pack2(o2, o3);
+      }
+  #pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const auto lo = __builtin_amdgcn_permlane16_swap(w[2 * u][0], w[2 * u + 1][0], false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(w[2 * u][1], w[2 * u + 1][1], false, false);
+        const int64_t off = b * p.ys_b + ti * p.ys_t + h * p.ys_h + 32 * u + 16 * (lq & 1) + 8 * (lq >> 1);
+        if (ti < p.L) *(uint4*)((uint16_t*)p.y + off) = make_uint4(lo[0], hi[0], lo[1], hi[1]);
+      }
+    } else if (ti < p.L) {
   #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int p0 = 16 * mt + 4 * lq;
@@ -669,8 +695,7 @@ __global__ __launch_bounds__(4 * Q) void chunk_scan_kernel(SSDParams p, int HB, 
         o[2] = __builtin_fmaf(Dh, __uint_as_float(xv.y << 16), o[2]);
         o[3] = __builtin_fmaf(Dh, __uint_as_float(xv.y & 0xFFFF0000u), o[3]);
         const int64_t off = b * p.ys_b + ti * p.ys_t + h * p.ys_h + p0;
-        if (p.y_f32) *(float4*)((float*)p.y + off) = make_float4(o[0], o[1], o[2], o[3]);
-        else *(uint2*)((uint16_t*)p.y + off) = make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+        *(float4*)((float*)p.y + off) = make_float4(o[0], o[1], o[2], o[3]);  // fp32 y: 16 bytes a lane
       }
     }
     __syncthreads();  // head h's LDS rows are read; the next head may be staged
