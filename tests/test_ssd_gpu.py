@@ -161,6 +161,28 @@ def test_strided_heads_view():
     assert_close(host_f64(y), yr, "bf16", "ssd strided")
 
 
+@pytest.mark.parametrize("chunk,y_dtype", [(64, None), (128, None), (256, None), (256, torch.float32)])
+def test_strided_y_view_keeps_its_neighbours(chunk, y_dtype):
+    """y as a view into a wider (batch, L, H+2, P) buffer filled with a
+    sentinel, the sequence ending inside a chunk: the outputs (bf16 rows are
+    stored 16 bytes a lane after lane swaps) land in the view, and the heads
+    on either side and the rows after L keep the sentinel."""
+    spec = small(seqlen=301, chunk=chunk)
+    inp = synth.ssd_inputs(spec, 11)
+    g = _upload(inp)
+    H = spec.nheads
+    dt = y_dtype or torch.bfloat16
+    wide = torch.full((2, 303, H + 2, 64), 7.0, dtype=dt, device="cuda")
+    yv = wide[:, :301, 1:H + 1]
+    banner("ssd strided y chunk %d %s" % (chunk, dt))
+    y, _ = ssm.ssd_chunk_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], spec.chunk, D=g["D"], y=yv)
+    torch.cuda.synchronize()
+    yr, _ = oracle.ssd(inp, "bf16")
+    assert_close(host_f64(yv), yr, "bf16", "ssd strided y")
+    assert bool((wide[:, :, 0] == 7.0).all()) and bool((wide[:, :, H + 1] == 7.0).all())
+    assert bool((wide[:, 301:] == 7.0).all())
+
+
 @pytest.mark.parametrize("dstate,chunk", [(128, 64), (128, 128), (128, 256), (256, 64), (256, 128)])
 def test_larger_states(dstate, chunk):
     """N = 128 and 256 states (every supported chunk size), ragged length,
