@@ -317,7 +317,7 @@ struct VecLoader {
   // range of the stretch's last tile (or of a tile past it) and return zeros.
   // (A mask per element costs a lane mask per element and slot, more than
   // the scalar registers hold.)
-  __device__ __forceinline__ void stage(ScanSmem<KS>& s, const Tiles&, int buf, int, const Set& st) const {
+  __device__ __forceinline__ void stage(ScanSmem<KS>&, const Tiles&, int buf, int, const Set& st) const {
 #pragma unroll
     for (int j = 0; j < kSlots; ++j) {
       if (!used[j] || !st_ok[j]) continue;
